@@ -1,0 +1,393 @@
+"""CPU oracle of one decode step over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import or call anything in oracle/. The
+product path (the HIP library and its binding) never does, and shares no
+code with it: the only common module is fixtures/, which draws the seeded
+inputs and holds none of the step's arithmetic.
+
+What it computes. The megakernel page ("Inside the megakernel serving
+engine for North Mini Code", introduction) states that the megakernel is
+ordinary tiled GEMMs and ordinary paged attention restructured into one
+persistent kernel; section "What is a Megakernel?" states that it runs the
+entire forward pass. The step is therefore the plain decoder step, written
+here op by op in the order the step takes them, per sequence (batch rows
+are independent; the Kinetic book, "Adding a weight format or a kernel",
+requires each batch row to equal the single-row result):
+
+  x = E[token]
+  per layer: u = rmsnorm(x); q,k,v = W_qkv u; rotate q,k at position p;
+             append bf16(k), bf16(v); o = softmax(q K^T / sqrt(d)) V per
+             query head (grouped-query); x += W_o o; u = rmsnorm(x);
+             dense:  x += W_down (silu(W_gate u) * W_up u)
+             MoE:    pi = softmax(W_r u); top-k of pi; renormalised weights;
+                     x += sum_j w_j W_down,j (silu(W_gate,j u) * W_up,j u)
+  z = rmsnorm(x); logits = W_lm z; next = argmax(logits)
+
+Readings where the pages are silent (each listed in the design notes):
+RMSNorm gains are 1.0; rotary uses the half-split ("NeoX") layout with
+theta_i = theta^(-2i/d) and cos/sin computed in fp64, rounded to fp32;
+the new token sits at position p = number of cached tokens and attends to
+itself through its bf16-rounded k and v; score scale 1/sqrt(d); GQA maps
+query head h to kv head h // (Hq/Hkv); the router takes a softmax over all
+experts, keeps the top k (ties to the lower index) and renormalises over
+them; argmax ties go to the lower index; the LM head is untied.
+
+Precision. The benchmark spec fixes fp32 math on bf16 weights: `dt` defaults
+to torch.float32; torch.float64 is a cross-check mode. Weights are the
+same bf16 bits as the GPU's, widened exactly. Decisions (top-k, argmax)
+are taken in the working precision.
+
+Library primitives used as steps: matrix-vector products (torch.mv), the
+stable sort (torch.sort(stable=True)) and torch.argmax (first maximum).
+"""
+import math
+from collections import deque
+
+import torch
+
+
+# ---------------------------------------------------------------- elementary ops
+
+def widen(w, dt):
+    """bf16 tensor -> working precision (exact)."""
+    return w.to(dt)
+
+
+def to_bf16(x):
+    """Round to bf16, nearest-even, through fp32 (the storage precision of KV)."""
+    return x.to(torch.float32).to(torch.bfloat16)
+
+
+def rmsnorm(x, g, eps):
+    """x / sqrt(mean(x^2) + eps) * g."""
+    dt = x.dtype
+    return x / torch.sqrt((x * x).mean() + eps) * widen(g, dt)
+
+
+def matvec(w, u):
+    """y = W u for W bf16 [rows][cols] (row-major [out][in])."""
+    return torch.mv(widen(w, u.dtype), u)
+
+
+def rope_cos_sin(theta, d, pos):
+    """cos/sin of pos * theta^(-2i/d), i < d/2, in fp64, rounded to fp32."""
+    i = torch.arange(d // 2, dtype=torch.float64)
+    ang = float(pos) * torch.pow(torch.tensor(float(theta), dtype=torch.float64), -2.0 * i / d)
+    return torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)
+
+
+def rope(v, cos, sin):
+    """Rotate rows of v [n][d] by pairs (i, i + d/2): (a, b) -> (a c - b s, b c + a s)."""
+    d = v.shape[-1]
+    c, s = cos.to(v.dtype), sin.to(v.dtype)
+    a, b = v[..., : d // 2], v[..., d // 2:]
+    return torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+
+
+def softmax(s):
+    """exp(s - max s) / sum exp(s - max s) along the last axis."""
+    e = torch.exp(s - s.max(dim=-1, keepdim=True).values)
+    return e / e.sum(dim=-1, keepdim=True)
+
+
+def attention(q, K, V):
+    """Plain softmax attention of queries q [n][d] over K, V [T][d] (bf16 or float)."""
+    dt = q.dtype
+    d = q.shape[-1]
+    s = (q @ widen(K, dt).T) / math.sqrt(d)
+    return softmax(s) @ widen(V, dt)
+
+
+def gather_pages(pool, page_row, n_tok, pt):
+    """Contiguous [n_tok][d] view of a paged store pool [n_pages][pt][d] through page_row."""
+    n_pg = (n_tok + pt - 1) // pt
+    rows = [pool[int(page_row[j])] for j in range(n_pg)]
+    return torch.cat(rows, dim=0)[:n_tok]
+
+
+def attention_paged(q, pool_k, pool_v, page_row, n_tok, pt):
+    """Paged attention: gather K, V through the page table, then attend."""
+    return attention(q, gather_pages(pool_k, page_row, n_tok, pt),
+                     gather_pages(pool_v, page_row, n_tok, pt))
+
+
+def attention_partial(q, K, V):
+    """Unnormalised partial over one key range: (o = sum_j e^{s_j - m} v_j, m, l)."""
+    dt = q.dtype
+    d = q.shape[-1]
+    s = (q @ widen(K, dt).T) / math.sqrt(d)
+    m = s.max(dim=-1).values
+    e = torch.exp(s - m[:, None])
+    return e @ widen(V, dt), m, e.sum(dim=-1)
+
+
+def merge_partials(parts):
+    """Log-sum-exp merge of partials (o, m, l) over disjoint key ranges, in list order."""
+    M = torch.stack([m for _, m, _ in parts]).max(dim=0).values
+    o = torch.zeros_like(parts[0][0])
+    L = torch.zeros_like(parts[0][1])
+    for oi, mi, li in parts:
+        c = torch.exp(mi - M)
+        o = o + c[:, None] * oi
+        L = L + c * li
+    return o / L[:, None]
+
+
+def topk(p, k):
+    """Indices of the k largest entries, descending, ties to the lower index."""
+    _, idx = torch.sort(-p, stable=True)
+    return idx[:k]
+
+
+def route(r, k, norm_topk=True):
+    """pi = softmax(r); ids = top-k of pi; w = pi[ids] (/ sum pi[ids] if norm_topk)."""
+    pi = softmax(r)
+    ids = topk(pi, k)
+    w = pi[ids]
+    if norm_topk:
+        w = w / w.sum()
+    return ids, w
+
+
+def silu(z):
+    return z / (1.0 + torch.exp(-z))
+
+
+def swiglu(wg, wu, u):
+    """silu(W_gate u) * (W_up u)."""
+    return silu(matvec(wg, u)) * matvec(wu, u)
+
+
+def argmax(v):
+    """Index of the largest entry, ties to the lower index."""
+    return int(torch.argmax(v))
+
+
+# ---------------------------------------------------------------- KV state
+
+class OracleKV:
+    """Contiguous bf16 KV per (layer, sequence, kv head), with a length per sequence."""
+
+    def __init__(self, m, ctx, cap_extra, kv_src=None):
+        L, Hkv, d = m["n_layers"], m["n_kv_heads"], m["head_dim"]
+        self.m = m
+        self.len = list(ctx)
+        self.K, self.V = {}, {}
+        for b, c in enumerate(ctx):
+            cap = c + cap_extra
+            for l in range(L):
+                for g in range(Hkv):
+                    K = torch.zeros(cap, d, dtype=torch.bfloat16)
+                    V = torch.zeros(cap, d, dtype=torch.bfloat16)
+                    if kv_src is not None and c > 0:
+                        K[:c] = kv_src.k(l, b, g, c)
+                        V[:c] = kv_src.v(l, b, g, c)
+                    self.K[l, b, g] = K
+                    self.V[l, b, g] = V
+
+    def append(self, l, b, g, k, v):
+        p = self.len[b]
+        self.K[l, b, g][p] = k
+        self.V[l, b, g][p] = v
+
+    def keys(self, l, b, g, n):
+        return self.K[l, b, g][:n]
+
+    def values(self, l, b, g, n):
+        return self.V[l, b, g][:n]
+
+
+# ---------------------------------------------------------------- the step
+
+def decode_step(m, W, kv, tokens, dt=torch.float32):
+    """One decode step for every sequence b: token tokens[b] at position kv.len[b].
+
+    Returns a dict with per-sequence lists: next (int), logits [V],
+    x_attn[l] / x_ffn[l] (hidden after each residual), topk_ids[l],
+    topk_w[l], router_logits[l], k_new[l] / v_new[l] (bf16 [Hkv][d]).
+    The KV state gains one token per sequence.
+    """
+    L, H, Hq, Hkv, d = m["n_layers"], m["hidden"], m["n_q_heads"], m["n_kv_heads"], m["head_dim"]
+    hg = Hq // Hkv
+    eps = m["rms_eps"]
+    moe = m["n_experts"] > 0
+    out = {k: [] for k in ("next", "logits", "x_attn", "x_ffn", "topk_ids", "topk_w",
+                           "router_logits", "k_new", "v_new")}
+    for b, tok in enumerate(tokens):
+        pos = kv.len[b]
+        cos, sin = rope_cos_sin(m["rope_theta"], d, pos)
+        x = widen(W.embed_row(int(tok)), dt)
+        xa, xf, ids_l, w_l, r_l, kn_l, vn_l = [], [], [], [], [], [], []
+        for l in range(L):
+            u = rmsnorm(x, W.attn_norm(l), eps)
+            qkv = matvec(W.wqkv(l), u)
+            q = rope(qkv[: Hq * d].view(Hq, d), cos, sin)
+            k = rope(qkv[Hq * d: (Hq + Hkv) * d].view(Hkv, d), cos, sin)
+            v = qkv[(Hq + Hkv) * d:].view(Hkv, d)
+            kb, vb = to_bf16(k), to_bf16(v)
+            for g in range(Hkv):
+                kv.append(l, b, g, kb[g], vb[g])
+            kn_l.append(kb)
+            vn_l.append(vb)
+            o = torch.empty(Hq, d, dtype=dt)
+            for g in range(Hkv):
+                o[g * hg:(g + 1) * hg] = attention(q[g * hg:(g + 1) * hg],
+                                                   kv.keys(l, b, g, pos + 1),
+                                                   kv.values(l, b, g, pos + 1))
+            x = x + matvec(W.wo(l), o.reshape(-1))
+            xa.append(x.clone())
+            u = rmsnorm(x, W.ffn_norm(l), eps)
+            if moe:
+                r = matvec(W.router(l), u)
+                ids, wts = route(r, m["top_k"], bool(m["norm_topk"]))
+                y = torch.zeros(H, dtype=dt)
+                for j in range(m["top_k"]):
+                    e = int(ids[j])
+                    y = y + wts[j] * matvec(W.down(l, e), swiglu(W.gate(l, e), W.up(l, e), u))
+                x = x + y
+                ids_l.append(ids.clone())
+                w_l.append(wts.clone())
+                r_l.append(r.clone())
+            else:
+                x = x + matvec(W.down(l), swiglu(W.gate(l), W.up(l), u))
+            xf.append(x.clone())
+        z = rmsnorm(x, W.final_norm(), eps)
+        logits = matvec(W.lm_head(), z)
+        out["next"].append(argmax(logits))
+        out["logits"].append(logits)
+        out["x_attn"].append(xa)
+        out["x_ffn"].append(xf)
+        out["topk_ids"].append(ids_l)
+        out["topk_w"].append(w_l)
+        out["router_logits"].append(r_l)
+        out["k_new"].append(kn_l)
+        out["v_new"].append(vn_l)
+    for b in range(len(tokens)):
+        kv.len[b] += 1
+    return out
+
+
+# ---------------------------------------------------------------- speed-of-light
+
+def step_bytes(m, ctx, distinct_experts=None):
+    """Algorithmic HBM bytes of one step: (weights, kv_read, kv_write).
+
+    Weights read once per step: per layer W_qkv, W_o, router and the experts
+    actually selected (distinct per layer, all batch rows together), plus the
+    LM head, one embedding row per sequence and the norm gains. KV: every
+    cached token of every layer and kv head is read (including the new one),
+    and the new token's K and V are written.
+    """
+    L, H, Hq, Hkv, d = m["n_layers"], m["hidden"], m["n_q_heads"], m["n_kv_heads"], m["head_dim"]
+    B = len(ctx)
+    w = L * (H * (Hq + 2 * Hkv) * d + Hq * d * H)
+    if m["n_experts"]:
+        w += L * H * m["n_experts"]
+        if distinct_experts is None:
+            distinct_experts = [min(m["n_experts"], B * m["top_k"])] * L
+        w += sum(distinct_experts) * 3 * H * m["expert_ffn"]
+    else:
+        w += L * 3 * H * m["ffn_dim"]
+    w += m["vocab"] * H + B * H + (2 * L + 1) * H
+    per_tok = L * 2 * Hkv * d * 2
+    kv_read = sum((c + 1) * per_tok for c in ctx)
+    kv_write = B * per_tok
+    return 2 * w, kv_read, kv_write
+
+
+def param_counts(m):
+    """(total, active) parameter counts; the LM head is untied."""
+    L, H, Hq, Hkv, d = m["n_layers"], m["hidden"], m["n_q_heads"], m["n_kv_heads"], m["head_dim"]
+    attn = H * (Hq + 2 * Hkv) * d + Hq * d * H + 2 * H
+    if m["n_experts"]:
+        ffn_all = H * m["n_experts"] + m["n_experts"] * 3 * H * m["expert_ffn"]
+        ffn_act = H * m["n_experts"] + m["top_k"] * 3 * H * m["expert_ffn"]
+    else:
+        ffn_all = ffn_act = 3 * H * m["ffn_dim"]
+    emb = 2 * m["vocab"] * H + H
+    return L * (attn + ffn_all) + emb, L * (attn + ffn_act) + emb
+
+
+def speed_of_light(bytes_per_step, bandwidth):
+    """Tokens per second per sequence at a given bandwidth: bandwidth / bytes."""
+    return bandwidth / bytes_per_step
+
+
+# ---------------------------------------------------------------- pool model
+
+class PoolModel:
+    """Plain model of the page/slot pool.
+
+    The free list is a deque holding the initial page order; a lease of a
+    sequence's worst case takes ceil(tokens / page_tokens) pages from the
+    front, all or nothing (kern page, "The runtime": a request leases the
+    pages its worst case needs and a state slot, all or nothing); a release
+    appends the sequence's pages, in its page order, to the back. Slots are
+    the lowest free index.
+    """
+
+    def __init__(self, order, page_tokens, n_slots):
+        self.free = deque(int(p) for p in order)
+        self.pt = page_tokens
+        self.slots_free = list(range(n_slots))
+        self.pages = {}
+        self.slot = {}
+
+    def lease(self, seq, tokens):
+        need = -(-tokens // self.pt)
+        if seq in self.pages or need > len(self.free) or not self.slots_free:
+            return False
+        self.pages[seq] = [self.free.popleft() for _ in range(need)]
+        self.slots_free.sort()
+        self.slot[seq] = self.slots_free.pop(0)
+        return True
+
+    def extend(self, seq, tokens):
+        need = -(-tokens // self.pt) - len(self.pages[seq])
+        if need > len(self.free):
+            return False
+        self.pages[seq] += [self.free.popleft() for _ in range(max(0, need))]
+        return True
+
+    def release(self, seq):
+        self.free.extend(self.pages.pop(seq))
+        self.slots_free.append(self.slot.pop(seq))
+
+    def page_table(self, seqs, max_pages):
+        t = [[-1] * max_pages for _ in seqs]
+        for i, s in enumerate(seqs):
+            for j, p in enumerate(self.pages[s][:max_pages]):
+                t[i][j] = p
+        return t
+
+
+# ---------------------------------------------------------------- work enumeration
+
+def work_sets(m, ctx_bound):
+    """What one step must produce, op by op, as sets the plan must cover exactly once.
+
+    Keys: ("qkv", l) rows of W_qkv; ("attn", l) triples (b, kv head, page) for
+    the pages that can hold tokens below each sequence's bound; ("comb", l)
+    pairs (b, q head); ("o", l) rows; ("router", l) rows; ("gateup", l)
+    (b, slot, row) for MoE or rows for dense; ("down", l) rows; ("lm",) rows.
+    """
+    L, H, Hq, Hkv, d = m["n_layers"], m["hidden"], m["n_q_heads"], m["n_kv_heads"], m["head_dim"]
+    pt = m["page_tokens"]
+    B = len(ctx_bound)
+    S = {}
+    for l in range(L):
+        S["qkv", l] = set(range((Hq + 2 * Hkv) * d))
+        S["attn", l] = {(b, g, p) for b in range(B) for g in range(Hkv)
+                        for p in range(-(-ctx_bound[b] // pt))}
+        S["comb", l] = {(b, h) for b in range(B) for h in range(Hq)}
+        S["o", l] = set(range(H))
+        if m["n_experts"]:
+            S["router", l] = set(range(m["n_experts"]))
+            S["gateup", l] = {(b, j, f) for b in range(B) for j in range(m["top_k"])
+                              for f in range(m["expert_ffn"])}
+        else:
+            S["gateup", l] = set(range(m["ffn_dim"]))
+        S["down", l] = set(range(H))
+    S["lm", ] = set(range(m["vocab"]))
+    return S
