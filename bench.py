@@ -1,0 +1,210 @@
+"""Decode throughput of the persistent megakernel on one GPU.
+
+A step is one decode step of the whole batch (every layer, the LM head and
+the greedy argmax) in ONE persistent-kernel launch. Default workload: the
+48-layer MoE (hidden 2048, 32/4 heads of 128, 128 experts top-8 of width
+768, vocab 151936) at batch 1 with 8192 prior tokens in 16-token pages,
+seeded random-init bf16 weights and KV, all resident in HBM before timing.
+
+Prints ONE JSON line: tok/s, ms per step, the megakernel's achieved HBM
+bandwidth over the step's algorithmic bytes (weights actually read + KV
+read and written) against the 8 TB/s peak, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s at batch 1 & 32; achieved HBM GB/s as % of speed-of-light"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="moe48_b1_8k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-steps", type=int, default=3,
+                    help="oracle steps in the CPU baseline sample (0: skip)")
+    ap.add_argument("--n-cu", type=int, default=0)
+    ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM counter bytes per launch measured by rocprofv3 --pmc")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every GPU box here has one GPU); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decode_megakernel_persistent_amd as mk
+    from fixtures.session import gpu_session, spec
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    total_steps = a.warmup + a.steps
+    w = spec(a.workload, a.seed, steps=total_steps)
+    m, B = w["model"], w["batch"]
+    L = m["n_layers"]
+    moe = m["n_experts"] > 0
+    K = m["top_k"] if moe else 1
+    print(f"[bench] setting up {a.workload}: B={B} ctx={w['ctx'] if B <= 4 else '...'} "
+          f"steps={a.steps} warmup={a.warmup}", file=sys.stderr, flush=True)
+    dec, pool, W = gpu_session(w, a.seed, device=dev, n_cu=a.n_cu, attn_split_pages=a.split_pages)
+    ctx0 = torch.tensor(w["ctx"], dtype=torch.int32, device=dev)
+    tok0 = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
+    toks = [tok0.clone(), torch.empty(B, dtype=torch.int32, device=dev)]
+    ids = torch.full((a.steps, L, B, K), -1, dtype=torch.int32, device=dev)
+
+    # warm-up, then restore the pre-warm-up state (lengths and first tokens)
+    for s in range(a.warmup):
+        dec.step(toks[s % 2], toks[(s + 1) % 2])
+    torch.cuda.synchronize()
+    dec.check_status()
+    dec.seq_lens.copy_(ctx0)
+    toks[0].copy_(tok0)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(a.steps):
+        ti, to = toks[s % 2], toks[(s + 1) % 2]
+        dec.step(ti, to, topk_ids=ids[s] if moe else None)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec.check_status()
+    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(a.steps)]
+    ms_total = ev[0].elapsed_time(ev[a.steps])
+    ms_step = ms_total / a.steps
+
+    # algorithmic bytes: weights read (distinct experts per layer from the step's
+    # own top-k ids) + KV read (every cached token incl. the new one) + KV written
+    ids_h = ids.cpu() if moe else None
+    desc = mk.model_desc(m)
+    tot_bytes = 0.0
+    wsum = ksum = 0.0
+    for s in range(a.steps):
+        lens = [c + s for c in w["ctx"]]
+        distinct = [len(set(ids_h[s, l].reshape(-1).tolist())) for l in range(L)] if moe else None
+        wb, kr, kw = mk.mk_step_bytes(desc, lens, distinct)
+        tot_bytes += wb + kr + kw
+        wsum += wb
+        ksum += kr + kw
+    bytes_step = tot_bytes / a.steps
+    achieved_gbs = tot_bytes / (ms_total * 1e-3) / 1e9
+    tok_s = B * a.steps / (ms_total * 1e-3)
+    sol_tok_s = B * HBM_PEAK_GBS * 1e9 / bytes_step
+
+    traffic = None
+    if os.path.exists(a.traffic_json):
+        try:
+            tj = json.load(open(a.traffic_json))
+            ent = tj.get(a.workload)
+            if ent and ent.get("kernel_hash") == mk_kernel_hash():
+                traffic = ent.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if a.cpu_steps > 0:
+        cpu = cpu_baseline(w, a, dec, tok0)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded random-init bf16 weights N(0,0.02), KV N(0,1), shuffled pages",
+        "config": {"workload": a.workload, "batch": B,
+                   "context": w["ctx"] if B == 1 else [min(w["ctx"]), max(w["ctx"])],
+                   "layers": L, "hidden": m["hidden"], "experts": m["n_experts"],
+                   "top_k": m["top_k"], "vocab": m["vocab"], "page_tokens": m["page_tokens"],
+                   "n_cu": mk.mk_plan_n_cu(dec.plan), "tasks": mk.mk_plan_n_tasks(dec.plan)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "bytes_per_step": {"weights": wsum / a.steps, "kv": ksum / a.steps, "total": bytes_step},
+        "sol_tok_s": round(sol_tok_s, 1),
+        "frac_of_sol": round(tok_s / sol_tok_s, 4),
+        "step_ms": {"median": round(statistics.median(per), 4),
+                    "p10": round(sorted(per)[len(per) // 10], 4),
+                    "p90": round(sorted(per)[(9 * len(per)) // 10], 4)},
+        "host_wall_s": round(wall, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    mk.mk_pool_free(pool)
+    dec.close()
+
+
+def mk_kernel_hash():
+    """Hash of the kernel sources; counter figures are used only while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_megakernel_persistent_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, a, dec, tok0):
+    """The oracle on the host cores, on a bounded sample of the same workload.
+
+    Sample: the first a.cpu_steps decode steps from the workload's starting
+    state (same context, same first token), each run once untimed to
+    materialise the weights it touches in host memory and once timed.
+    """
+    import torch
+    import oracle as O
+    from fixtures.session import oracle_inputs
+    m = w["model"]
+    B = w["batch"]
+    n = a.cpu_steps
+    W, kv_warm = oracle_inputs(dict(w, steps=n), a.seed, cache=True)
+    _, kv = oracle_inputs(dict(w, steps=n), a.seed, cache=True)
+    times = []
+    t_in = [int(t) for t in tok0.cpu().tolist()]
+    for s in range(n):
+        O.decode_step(m, W, kv_warm, t_in)          # untimed: materialises this step's weights
+        t0 = time.perf_counter()
+        r = O.decode_step(m, W, kv, t_in)
+        times.append(time.perf_counter() - t0)
+        t_in = r["next"]
+        if sum(times) > 60:
+            break
+    dt = sum(times) / len(times)
+    return {"value": round(B / dt, 4), "unit": "tok/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(times)} decode step(s) of {a.workload} from its starting context, "
+                      f"weights resident in host memory (materialised in an untimed pass), "
+                      f"mean {dt:.3f} s per step"}
+
+
+if __name__ == "__main__":
+    main()

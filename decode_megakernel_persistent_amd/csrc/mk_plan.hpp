@@ -1,0 +1,42 @@
+// Host-side plan object (opaque mk_plan_t of include/mk.h).
+#pragma once
+#include <string>
+#include <vector>
+
+#include "mk.h"
+#include "mk_internal.hpp"
+
+struct mk_plan {
+  mk_model_desc m;
+  int32_t B = 0, max_pages = 0, bound = 0, n_cu = 0;
+  std::vector<int32_t> seq_lens, page_table;
+
+  // derived shape
+  int32_t HG = 0, QKV_ROWS = 0, F = 0, n_pairs_g = 0;
+
+  std::vector<std::vector<mk::Task>> lists;  // per compute unit, in execution order
+  std::vector<int32_t> stage_of_task;        // parallel to the flattened lists
+  std::vector<uint32_t> targets;             // per counter: producers per epoch
+  std::vector<std::string> ctr_name;
+
+  // counter ids
+  std::vector<int32_t> c_qkv, c_attn;  // [L][Hkv]
+  std::vector<int32_t> c_comb, c_o, c_router, c_gateup, c_down;  // [L]
+  int32_t c_lm = -1;
+
+  int32_t S_max = 0;                // attention splits per (b, g), max over b
+  std::vector<int32_t> n_split;     // per b
+  int32_t n_lm = 0, n_stages = 0;
+
+  // workspace layout: base offset (bytes) and per-layer stride (bytes) per MK_BUF_*
+  size_t ws_off[8] = {}, ws_stride[8] = {}, ws_layer_bytes[8] = {};
+  size_t ws_total = 0;
+
+  std::vector<uint8_t> image;  // device image
+  size_t n_tasks = 0;
+};
+
+namespace mkh {
+void set_error(const std::string& s);
+mk_status fail(mk_status st, const std::string& s);
+}  // namespace mkh

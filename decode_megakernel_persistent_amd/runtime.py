@@ -1,0 +1,133 @@
+"""Device-memory plumbing around the C ABI: a planned batch ready to step.
+
+PyTorch provides device memory and the stream; every computation of the
+decode step runs in libmk.so's kernels, and the plan, page bookkeeping and
+rotary tables come from the library's host code. Nothing here computes any
+part of the step.
+"""
+import ctypes
+
+import numpy as np
+import torch
+
+from . import (
+    MK_BUF_ACT, MK_BUF_O, MK_BUF_Q, MK_BUF_RLOG, MK_BUF_XATTN, MK_BUF_XFFN,
+    MkError, MK_OK, mk_decode_step, mk_io, mk_kv, mk_kv_pool_elems, mk_plan, mk_plan_buffer,
+    mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_upload,
+    mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_step_status, mk_weights,
+    model_desc,
+)
+
+EPOCH_LIMIT = 65535  # counters end a step at epoch * target; target <= 65535
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def rope_tables(model, n_pos, device):
+    """Rotary cos/sin tables [n_pos][head_dim/2] from the library, moved to the device."""
+    h = model["head_dim"] // 2
+    c = np.empty(n_pos * h, dtype=np.float32)
+    s = np.empty(n_pos * h, dtype=np.float32)
+    mk_rope_table(model["rope_theta"], model["head_dim"], n_pos, c.ctypes.data, s.ctypes.data)
+    return (torch.from_numpy(c).view(n_pos, h).to(device), torch.from_numpy(s).view(n_pos, h).to(device))
+
+
+def alloc_kv_pool(model, n_pages, device, zero=True):
+    desc = model_desc(model)
+    n = mk_kv_pool_elems(desc, n_pages)
+    mk = torch.zeros if zero else torch.empty
+    return mk(n, dtype=torch.bfloat16, device=device)
+
+
+class Decoder:
+    """A plan for one batch shape plus every device buffer a step needs.
+
+    model: dict with the mk_model_desc field names. weights: dict of device
+    bf16 tensors (fixtures.device.weights layout). pool: bf16 KV pool tensor.
+    seq_lens: host ints (tokens cached per sequence). page_table: host
+    [batch][max_pages] ints. bound: the plan stays valid while every
+    sequence's length + 1 <= bound.
+    """
+
+    def __init__(self, model, weights, pool, n_pages, seq_lens, page_table, max_pages, bound,
+                 n_cu=0, attn_split_pages=0, device="cuda"):
+        self.m = dict(model)
+        self.device = torch.device(device)
+        self.B = len(seq_lens)
+        self.desc = model_desc(self.m)
+        flat = [int(v) for row in page_table for v in row]
+        self.plan = mk_plan(self.desc, seq_lens, flat, max_pages, bound, n_cu, attn_split_pages)
+        self.bound = bound
+        dev = self.device
+        self.plan_buf = torch.empty(mk_plan_device_bytes(self.plan), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(mk_plan_workspace_bytes(self.plan), dtype=torch.uint8, device=dev)
+        self.ctr = torch.zeros(mk_plan_counter_bytes(self.plan) // 4, dtype=torch.int32, device=dev)
+        self.status = torch.zeros(4, dtype=torch.int32, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        mk_plan_upload(self.plan, self.plan_buf.data_ptr(), self.plan_buf.numel(), stream)
+        self.page_table = torch.tensor(flat, dtype=torch.int32, device=dev).view(self.B, max_pages)
+        self.seq_lens = torch.tensor([int(v) for v in seq_lens], dtype=torch.int32, device=dev)
+        self.rope_cos, self.rope_sin = rope_tables(self.m, bound, dev)
+        self.pool = pool
+        self.W = weights
+        self.epoch = 0
+        self._w = mk_weights(*[_ptr(weights.get(k)) for k, _ in mk_weights._fields_])
+        self._kv = mk_kv(pool.data_ptr(), n_pages, self.page_table.data_ptr(),
+                         self.seq_lens.data_ptr(), self.rope_cos.data_ptr(),
+                         self.rope_sin.data_ptr(), bound)
+        self._bufs = mk_step_buffers(self.plan_buf.data_ptr(), self.plan_buf.numel(),
+                                     self.ws.data_ptr(), self.ws.numel(), self.ctr.data_ptr(),
+                                     self.ctr.numel() * 4, self.status.data_ptr())
+
+    def close(self):
+        if self.plan:
+            mk_plan_free(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def step(self, tokens_in, tokens_out, topk_ids=None, topk_w=None, logits=None, timeout_ms=0):
+        """Enqueue one decode step on the current stream (asynchronous)."""
+        if self.epoch >= EPOCH_LIMIT:
+            self.ctr.zero_()
+            self.epoch = 0
+        self.epoch += 1
+        io = mk_io(_ptr(tokens_in), _ptr(tokens_out), _ptr(topk_ids), _ptr(topk_w), _ptr(logits))
+        mk_decode_step(self.plan, self._w, self._kv, io, self._bufs, self.epoch, timeout_ms,
+                       torch.cuda.current_stream(self.device).cuda_stream)
+
+    def check_status(self):
+        """Synchronise and raise MkError if the device recorded a failure."""
+        h = self.status.cpu().tolist()
+        st, msg = mk_step_status([v & 0xFFFFFFFF for v in h])
+        if st != MK_OK:
+            raise MkError(st, msg)
+
+    def buffer(self, which, layer, dtype=torch.float32):
+        """Workspace sub-buffer (MK_BUF_*) of one layer as a device tensor view."""
+        off, nb = mk_plan_buffer(self.plan, which, layer)
+        return self.ws[off:off + nb].view(dtype)
+
+    def hidden_after_attn(self, layer):
+        return self.buffer(MK_BUF_XATTN, layer).view(self.B, self.m["hidden"])
+
+    def hidden_after_ffn(self, layer):
+        return self.buffer(MK_BUF_XFFN, layer).view(self.B, self.m["hidden"])
+
+    def router_logits(self, layer):
+        return self.buffer(MK_BUF_RLOG, layer).view(self.B, -1)
+
+    def queries(self, layer):
+        return self.buffer(MK_BUF_Q, layer).view(self.B, self.m["n_q_heads"], self.m["head_dim"])
+
+    def attn_out(self, layer):
+        return self.buffer(MK_BUF_O, layer).view(self.B, self.m["n_q_heads"], self.m["head_dim"])
+
+    def ffn_act(self, layer):
+        return self.buffer(MK_BUF_ACT, layer)

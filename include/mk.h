@@ -1,0 +1,229 @@
+/* mk.h -- C ABI of a persistent decode megakernel for MI355X (gfx950).
+ *
+ * One decode step of a decoder-only LLM over a paged KV cache runs as ONE
+ * persistent kernel: one workgroup per compute unit, each walking its own
+ * host-built task list in device memory, each task one tile of one
+ * operation; dependencies are counters in device memory that a task
+ * increments when it finishes and that its consumers spin on before they
+ * read (megakernel page, "Inside the megakernel serving engine for North
+ * Mini Code", section "What is a Megakernel?" and the caption of Image 2).
+ *
+ * Conventions
+ *  - Ownership: the library never allocates device memory. The caller owns
+ *    every device buffer (sizes come from mk_plan_*_bytes). Plans and pools
+ *    are host objects owned by the library and freed with *_free.
+ *  - Errors: every call returns an mk_status; on failure mk_last_error()
+ *    gives a message for the calling thread (Kinetic book, "Python, C and
+ *    Rust": NULL or -1 on failure plus a per-thread last-error string).
+ *    Calls validate before they launch; a batch, context or page outside a
+ *    plan's declared bounds is MK_EBOUNDS (kern page, "The manifest": a call
+ *    outside declared bounds is rejected before it launches).
+ *  - Asynchrony: mk_decode_step only enqueues work on the caller's HIP
+ *    stream. Device-side failures (a dependency wait that exceeded its
+ *    deadline, a context past the plan's bound) are written to the status
+ *    words, which the caller reads after its next synchronisation and
+ *    decodes with mk_step_status.
+ *  - Threads: a plan is immutable once built and may be used from several
+ *    threads; a pool is single-threaded.
+ *  - Determinism: the same inputs give the same plan bytes and the same
+ *    output bits (kern page, "The harness": running twice and diffing is a
+ *    test).
+ *
+ * Data formats (all device pointers unless stated otherwise)
+ *  - Weights: bf16, logical row-major [out][in] matrices, stacked over
+ *    layers (and experts) as documented in mk_weights.
+ *  - Activations between tasks: fp32, in the caller's workspace.
+ *  - KV pool: bf16 pages of page_tokens (= 16) tokens holding every layer.
+ *    For physical page p, layer l, kv head g, the block of 2*16*d elements
+ *    starting at element p*page_stride + l*layer_stride + g*(2*16*d) holds
+ *    K as [slot][dim] (16*d elements) followed by V as [dim][slot] (16*d
+ *    elements), where layer_stride = Hkv*2*16*d and page_stride =
+ *    L*layer_stride. Token t of sequence b is in page page_table[b][t/16],
+ *    slot t%16.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1
+
+typedef enum mk_status {
+  MK_OK = 0,
+  MK_EINVAL = -1,       /* bad argument, NULL pointer, inconsistent sizes */
+  MK_ENOMEM = -2,       /* pool exhausted; pool state unchanged */
+  MK_EBOUNDS = -3,      /* batch / context / page outside the plan's bounds */
+  MK_EDEVICE = -4,      /* a HIP runtime call failed */
+  MK_ETIMEOUT = -5,     /* a device dependency wait passed its deadline */
+  MK_ESTATE = -6,       /* object in the wrong state (e.g. sequence not leased) */
+  MK_EUNSUPPORTED = -7  /* shape outside what the kernels implement */
+} mk_status;
+
+/* Model shape. Dense FFN if n_experts == 0 (uses ffn_dim), MoE otherwise. */
+typedef struct mk_model_desc {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim;
+  int32_t ffn_dim;                       /* dense SwiGLU width; 0 for MoE */
+  int32_t n_experts, top_k, expert_ffn;  /* MoE; 0 for dense */
+  int32_t norm_topk;                     /* 1: renormalise the top-k softmax weights */
+  int32_t vocab, page_tokens;            /* page_tokens must be 16 */
+  float rms_eps, rope_theta;
+} mk_model_desc;
+
+/* One step's batch. Host pointers; copied by mk_plan. */
+typedef struct mk_batch_desc {
+  int32_t batch;
+  int32_t max_pages;           /* columns of the page table */
+  const int32_t* seq_lens;     /* [batch] tokens already cached (= position of the new token) */
+  const int32_t* page_table;   /* [batch][max_pages] physical page ids, -1 = none */
+  int32_t max_ctx_bound;       /* the plan stays valid while every seq_len + 1 <= bound;
+                                  every sequence must have ceil(bound/16) pages mapped */
+} mk_batch_desc;
+
+typedef struct mk_plan_opts {
+  int32_t n_cu;                /* workgroups = task lists (0: the current device's CU count) */
+  int32_t attn_split_pages;    /* pages per attention task (0: automatic) */
+  int32_t flags;               /* reserved, 0 */
+} mk_plan_opts;
+
+typedef struct mk_plan mk_plan_t;   /* opaque host object */
+typedef struct mk_pool mk_pool_t;   /* opaque host object */
+
+/* Device pointers to bf16 weights (logical row-major layouts). */
+typedef struct mk_weights {
+  const void* embed;       /* [vocab][hidden] */
+  const void* attn_norm;   /* [L][hidden] */
+  const void* w_qkv;       /* [L][(Hq + 2 Hkv) d][hidden]: rows q (head-major), k, v */
+  const void* w_o;         /* [L][hidden][Hq d] */
+  const void* ffn_norm;    /* [L][hidden] */
+  const void* router;      /* [L][E][hidden] (MoE) or NULL */
+  const void* gate;        /* [L][E][F][hidden] (MoE) or [L][ffn][hidden] */
+  const void* up;          /* same shape as gate */
+  const void* down;        /* [L][E][hidden][F] (MoE) or [L][hidden][ffn] */
+  const void* final_norm;  /* [hidden] */
+  const void* lm_head;     /* [vocab][hidden] (untied) */
+} mk_weights;
+
+/* KV cache and positions. */
+typedef struct mk_kv {
+  void* pool;                /* bf16 KV pool, format above */
+  int64_t n_pages;           /* pages in the pool */
+  const int32_t* page_table; /* device [batch][max_pages] (same shape as the plan's) */
+  int32_t* seq_lens;         /* device [batch]; incremented by one when the step completes */
+  const float* rope_cos;     /* device [n_rope_pos][head_dim/2] (see mk_rope_table) */
+  const float* rope_sin;     /* device [n_rope_pos][head_dim/2] */
+  int32_t n_rope_pos;        /* positions covered by the tables (>= max_ctx_bound) */
+} mk_kv;
+
+/* Per-step inputs and outputs. */
+typedef struct mk_io {
+  const int32_t* tokens_in;  /* device [batch] */
+  int32_t* tokens_out;       /* device [batch] greedy next tokens; may alias nothing else */
+  int32_t* topk_ids;         /* device [L][batch][top_k] or NULL */
+  float* topk_w;             /* device [L][batch][top_k] or NULL */
+  float* logits;             /* device [batch][vocab] or NULL */
+} mk_io;
+
+/* Caller-owned device buffers of a plan. */
+typedef struct mk_step_buffers {
+  const void* plan; size_t plan_bytes;      /* image uploaded by mk_plan_upload */
+  void* workspace; size_t workspace_bytes;  /* activations; no initialisation needed */
+  uint32_t* counters; size_t counter_bytes; /* zeroed once before epoch 1 */
+  uint32_t* status;                         /* 4 words, zeroed once */
+} mk_step_buffers;
+
+/* ---- library ---- */
+int32_t mk_abi_version(void);
+const char* mk_last_error(void);
+/* Compute units of the current HIP device. */
+mk_status mk_device_cu_count(int32_t* n_cu);
+
+/* ---- model-level helpers (host only) ---- */
+/* Rotary tables: angle(p, i) = p * theta^(-2i/d) for p < n_pos, i < d/2, computed
+ * in fp64 and rounded to fp32. Host outputs of n_pos*d/2 floats each. */
+mk_status mk_rope_table(float theta, int32_t head_dim, int32_t n_pos, float* cos_out,
+                        float* sin_out);
+/* Elements (bf16) of a KV pool of n_pages pages. */
+int64_t mk_kv_pool_elems(const mk_model_desc* m, int64_t n_pages);
+/* Algorithmic bytes of one step: weights read once (selected experts only:
+ * distinct_experts[l] per layer, or NULL for min(E, batch*top_k)), one embedding
+ * row per sequence, KV read (every cached token incl. the new one) and written. */
+mk_status mk_step_bytes(const mk_model_desc* m, int32_t batch, const int32_t* seq_lens,
+                        const int32_t* distinct_experts, double* weight_bytes,
+                        double* kv_read_bytes, double* kv_write_bytes);
+
+/* ---- plan (host; no device is touched except by mk_plan_upload) ---- */
+/* Build the task lists, counters and workspace layout for one batch shape
+ * (megakernel page, caption of Image 2: the host decomposes the step into
+ * tasks of one tile of one operation each and deals them round-robin over
+ * the compute units). */
+mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* b, const mk_plan_opts* o,
+                  mk_plan_t** out);
+/* Coverage (every output row / KV page exactly once), counter targets equal
+ * producer counts, per-list stage order. MK_OK or MK_EINVAL with a message. */
+mk_status mk_plan_validate(const mk_plan_t* p);
+/* Execute the lists on n_cu virtual compute units under seeded random
+ * interleavings, n_runs times; fails (MK_ESTATE) on a read before its
+ * producers finished or on a deadlock (message names the blocked tasks). */
+mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t n_runs);
+size_t mk_plan_device_bytes(const mk_plan_t* p);
+size_t mk_plan_workspace_bytes(const mk_plan_t* p);
+size_t mk_plan_counter_bytes(const mk_plan_t* p);
+int32_t mk_plan_n_tasks(const mk_plan_t* p);
+int32_t mk_plan_n_counters(const mk_plan_t* p);
+int32_t mk_plan_n_cu(const mk_plan_t* p);
+/* The device image (the bytes mk_plan_upload copies) into a host buffer. */
+mk_status mk_plan_export(const mk_plan_t* p, void* host_buf, size_t bytes);
+mk_status mk_plan_upload(const mk_plan_t* p, void* d_plan, size_t bytes, void* hip_stream);
+/* Workspace sub-buffer `which` (MK_BUF_*) of layer `layer`: byte offset and size. */
+enum { MK_BUF_XATTN = 0, MK_BUF_XFFN = 1, MK_BUF_Q = 2, MK_BUF_PART = 3, MK_BUF_O = 4,
+       MK_BUF_RLOG = 5, MK_BUF_ACT = 6, MK_BUF_LMPART = 7 };
+mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t layer, size_t* offset,
+                         size_t* bytes);
+/* The plan's per-epoch counter targets, [n_counters] (host). */
+mk_status mk_plan_counter_targets(const mk_plan_t* p, uint32_t* out, int32_t n);
+void mk_plan_free(mk_plan_t* p);
+
+/* ---- one decode step (asynchronous on hip_stream) ----
+ * epoch: 1 for the first step after the counters were zeroed, +1 per step
+ * (every counter ends a step at epoch x its target; keep epoch x 65535 < 2^32).
+ * tokens_in -> tokens_out: greedy argmax of the LM head (ties to the lower id).
+ * On completion every seq_lens[b] has grown by one: the new token's K and V
+ * sit at position seq_lens[b] (old value) of its sequence. timeout_ms bounds
+ * every dependency wait (0: 2000 ms); on expiry the kernel records
+ * MK_ETIMEOUT in the status words and every workgroup exits. */
+mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv,
+                         const mk_io* io, const mk_step_buffers* bufs, uint32_t epoch,
+                         uint32_t timeout_ms, void* hip_stream);
+/* Decode a host copy of the 4 status words: MK_OK, MK_ETIMEOUT (word 1: task
+ * index, word 2: counter, word 3: value seen) or MK_EBOUNDS (context past the
+ * plan bound). Sets mk_last_error. */
+mk_status mk_step_status(const uint32_t* h_status);
+
+/* ---- page/slot pool (pure host; kern page, "The runtime") ----
+ * n_pages pages of page_tokens tokens, n_slots sequence slots. The free list
+ * starts in initial_order (a permutation of [0, n_pages); NULL = ascending).
+ * A lease takes ceil(tokens/page_tokens) pages from the front of the free list
+ * and the lowest free slot, all or nothing; a release appends the sequence's
+ * pages, in its page order, to the back. */
+mk_status mk_pool_create(int32_t n_pages, int32_t page_tokens, int32_t n_slots,
+                         const int32_t* initial_order, mk_pool_t** out);
+mk_status mk_pool_lease(mk_pool_t* p, int64_t seq_id, int32_t worst_case_tokens,
+                        int32_t* slot_out);
+mk_status mk_pool_extend(mk_pool_t* p, int64_t seq_id, int32_t worst_case_tokens);
+mk_status mk_pool_release(mk_pool_t* p, int64_t seq_id);
+/* out[i][j] = page j of seq_ids[i], -1 past its pages (host [n][max_pages]). */
+mk_status mk_pool_page_table(const mk_pool_t* p, const int64_t* seq_ids, int32_t n,
+                             int32_t max_pages, int32_t* out);
+int32_t mk_pool_free_pages(const mk_pool_t* p);
+int32_t mk_pool_seq_pages(const mk_pool_t* p, int64_t seq_id);
+void mk_pool_free(mk_pool_t* p);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */
