@@ -64,7 +64,8 @@ class mk_io(ctypes.Structure):
 
 class mk_step_buffers(ctypes.Structure):
     _fields_ = [("plan", _vp), ("plan_bytes", _sz), ("workspace", _vp), ("workspace_bytes", _sz),
-                ("counters", _vp), ("counter_bytes", _sz), ("status", _vp)]
+                ("counters", _vp), ("counter_bytes", _sz), ("status", _vp),
+                ("trace", _vp), ("trace_bytes", _sz)]
 
 
 _P = ctypes.POINTER

@@ -42,6 +42,7 @@ struct Smem {
   int route_ids[16];
   float route_w[16];
   int flag;
+  uint64_t tw[4];  // trace: (begin, end) of the routing wait and of the data wait
 };
 
 // ------------------------------------------------------------------ block GEMV
@@ -250,7 +251,7 @@ __device__ __forceinline__ bool task_qkv(const KArgs& a, const Task& t, uint32_t
   };
   float u[CPL * 8];
   auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
     const float* xf;
     const uint16_t* xb;
     layer_input(a, l, &xf, &xb);
@@ -340,7 +341,7 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
   const bool preB = cnt > 1 && pB < cur;
   if (preA) load(k0, v0, pA);
   if (preB) load(k1, v1, pB);
-  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
   if (cnt > 0 && !preA) load(k0, v0, pA);
   if (cnt > 1 && !preB) load(k1, v1, pB);
 
@@ -477,7 +478,7 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
 
 __device__ __forceinline__ bool task_comb(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
   const int l = t.layer, b = t.a0, h = t.a1, S = t.a3, D = a.D, PS = D + 4;
-  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
   const float* base = a.part + (size_t)l * a.s_part + (size_t)(b * a.Hq + h) * a.S_max * PS;
   float* ms = s.aux;          // [S]
   float* ls = s.aux + 1024;   // [S]
@@ -517,7 +518,7 @@ __device__ __forceinline__ bool task_o(const KArgs& a, const Task& t, uint32_t t
   auto rowptr = [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * K); };
   float u[CPL * 8];
   auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
     load_slice<CPL>(a, a.o + (size_t)l * a.s_o, nullptr, nullptr, K, TC, u, s.aux);
     return true;
   };
@@ -541,7 +542,7 @@ __device__ __forceinline__ bool task_router(const KArgs& a, const Task& t, uint3
   auto rowptr = [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); };
   float u[CPL * 8];
   auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
     load_slice<CPL>(a, a.xa + (size_t)l * a.s_x, nullptr, a.ffn_norm + (size_t)l * H, H, TC, u, s.aux);
     return true;
   };
@@ -559,7 +560,7 @@ __device__ __forceinline__ bool task_gateup(const KArgs& a, const Task& t, uint3
   const int TC = task_tc(t);
   int e = 0;
   if (!a.dense) {
-    if (!wg_wait(a, t.wait_a, t.cnt_a, ti, &s.flag)) return false;
+    if (!wg_wait(a, t.wait_a, t.cnt_a, ti, &s.flag, s.tw)) return false;
     route(a, l, s);
     e = s.route_ids[slot];
     if ((t.flags & TF_WRITE_TOPK) && threadIdx.x < a.K) {
@@ -574,7 +575,7 @@ __device__ __forceinline__ bool task_gateup(const KArgs& a, const Task& t, uint3
   };
   float u[CPL * 8];
   auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
     load_slice<CPL>(a, a.xa + (size_t)l * a.s_x, nullptr, a.ffn_norm + (size_t)l * H, H, TC, u, s.aux);
     return true;
   };
@@ -595,7 +596,7 @@ __device__ __forceinline__ bool task_down(const KArgs& a, const Task& t, uint32_
   const int nj = n * KK;
   const int TC = task_tc(t);
   if (!a.dense) {
-    if (!wg_wait(a, t.wait_a, t.cnt_a, ti, &s.flag)) return false;
+    if (!wg_wait(a, t.wait_a, t.cnt_a, ti, &s.flag, s.tw)) return false;
     route(a, l, s);
   } else if (threadIdx.x == 0) {
     s.route_ids[0] = 0;
@@ -610,7 +611,7 @@ __device__ __forceinline__ bool task_down(const KArgs& a, const Task& t, uint32_
   const int my_slot = (threadIdx.x / TC) % KK;  // NT/TC is a multiple of KK
   float u[CPL * 8];
   auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
     load_slice<CPL>(a, a.act + (size_t)l * a.s_act + (size_t)my_slot * F, nullptr, nullptr, F, TC,
                     u, s.aux);
     return true;
@@ -632,7 +633,7 @@ __device__ __forceinline__ bool task_lm(const KArgs& a, const Task& t, uint32_t 
   auto rowptr = [&](int j) { return (const uint4*)(a.lm + (size_t)(r0 + j) * H); };
   float u[CPL * 8];
   auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
     load_slice<CPL>(a, a.xf + (size_t)(a.L - 1) * a.s_x, nullptr, a.final_norm, H, TC, u, s.aux);
     return true;
   };
@@ -665,7 +666,7 @@ __device__ __forceinline__ bool task_lm(const KArgs& a, const Task& t, uint32_t 
 }
 
 __device__ __forceinline__ bool task_final(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag)) return false;
+  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
   float bv = NEG_INF;
   int bi = 0x7fffffff;
   for (int q = threadIdx.x; q < t.a0; q += NT) {
@@ -710,6 +711,11 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
   const uint32_t beg = off[blockIdx.x], end = off[blockIdx.x + 1];
   for (uint32_t ti = beg; ti < end; ++ti) {
     const Task t = tasks[ti];
+    uint64_t t_start = 0;
+    if (a.trace && threadIdx.x == 0) {
+      t_start = __builtin_amdgcn_s_memrealtime();
+      s.tw[0] = s.tw[1] = s.tw[2] = s.tw[3] = 0;
+    }
     bool ok = true;
     switch (t.op) {
       case OP_QKV: ok = MK_CPL_DISPATCH(task_qkv, a.H); break;
@@ -724,7 +730,17 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
       default: break;
     }
     if (!ok) return;
+    uint64_t t_body = 0;
+    if (a.trace && threadIdx.x == 0) t_body = __builtin_amdgcn_s_memrealtime();
     wg_signal(a, t.signal);
+    if (a.trace && threadIdx.x == 0) {
+      uint64_t* tr = a.trace + (size_t)ti * TRACE_WORDS;
+      tr[0] = t_start;
+      tr[1] = s.tw[0]; tr[2] = s.tw[1]; tr[3] = s.tw[2]; tr[4] = s.tw[3];
+      tr[5] = t_body;
+      tr[6] = __builtin_amdgcn_s_memrealtime();
+      tr[7] = ((uint64_t)blockIdx.x << 32) | ((uint64_t)t.op << 16) | t.layer;
+    }
   }
 }
 
@@ -828,6 +844,11 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
   a.S_max = p->S_max; a.n_lm = p->n_lm;
   a.plan = (const uint32_t*)bu->plan; a.ctr = bu->counters; a.status = bu->status; a.epoch = epoch;
   a.timeout_ticks = (uint64_t)(timeout_ms ? timeout_ms : 2000) * 100000ull;
+  if (bu->trace) {
+    if (bu->trace_bytes < p->n_tasks * mk::TRACE_WORDS * sizeof(uint64_t))
+      return fail(MK_EINVAL, "mk_decode_step: trace buffer smaller than 64 bytes per task");
+    a.trace = bu->trace;
+  }
 
   void* args[] = {&a};
   hipError_t e = hipLaunchCooperativeKernel((const void*)mk::dev::megakernel, dim3(p->n_cu),

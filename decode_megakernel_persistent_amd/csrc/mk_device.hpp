@@ -81,10 +81,11 @@ __device__ __forceinline__ void raise_status(const KArgs& a, uint32_t code, uint
 // stay in flight. Returns false (uniformly) if the step was aborted: this
 // wait passed its deadline, or another workgroup recorded a failure.
 __device__ __forceinline__ bool wg_wait(const KArgs& a, uint16_t ci, uint16_t cnt, uint32_t task,
-                                        int* sflag) {
+                                        int* sflag, uint64_t* tw) {
   if (ci == NO_CTR) return true;
   const uint32_t target = a.epoch * (uint32_t)cnt;
   if (threadIdx.x < 64) {
+    if (a.trace && threadIdx.x == 0) tw[0] = __builtin_amdgcn_s_memrealtime();
     const uint32_t* c = a.ctr + (size_t)ci * CTR_STRIDE;
     int ok = 1;
     uint32_t v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -110,7 +111,10 @@ __device__ __forceinline__ bool wg_wait(const KArgs& a, uint16_t ci, uint16_t cn
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     wait_vm();
-    if (threadIdx.x == 0) *sflag = ok;
+    if (threadIdx.x == 0) {
+      *sflag = ok;
+      if (a.trace) tw[1] = __builtin_amdgcn_s_memrealtime();
+    }
   }
   __syncthreads();
   return *sflag != 0;

@@ -58,6 +58,11 @@ constexpr int CTR_STRIDE = 16;  // u32 words between counters (one 64-byte line 
 constexpr int NT = 512;         // threads per workgroup (8 wave64)
 constexpr int NWAVE = NT / 64;
 
+// Per-task trace record (u64 words, constant 100 MHz clock): task start,
+// routing wait begin/end, data wait begin/end (0 where the task has no such
+// wait), body end, signal end, and (cu << 32 | op << 16 | layer).
+constexpr int TRACE_WORDS = 8;
+
 // Status words written by the device on failure.
 enum DevStatus : uint32_t { DS_OK = 0, DS_TIMEOUT = 1, DS_BOUNDS = 2 };
 
@@ -126,6 +131,7 @@ struct KArgs {
   uint32_t* status;
   uint32_t epoch;
   uint64_t timeout_ticks;  // of the 100 MHz constant clock
+  uint64_t* trace;         // NULL, or TRACE_WORDS per task (see mk_step_buffers.trace)
 };
 
 }  // namespace mk

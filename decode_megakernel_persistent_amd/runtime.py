@@ -13,12 +13,13 @@ import torch
 from . import (
     MK_BUF_ACT, MK_BUF_O, MK_BUF_Q, MK_BUF_RLOG, MK_BUF_XATTN, MK_BUF_XFFN,
     MkError, MK_OK, mk_decode_step, mk_io, mk_kv, mk_kv_pool_elems, mk_plan, mk_plan_buffer,
-    mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_upload,
+    mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks, mk_plan_upload,
     mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_step_status, mk_weights,
     model_desc,
 )
 
 EPOCH_LIMIT = 65535  # counters end a step at epoch * target; target <= 65535
+TRACE_WORDS = 8     # u64 per task in the optional trace buffer
 
 
 def _ptr(t):
@@ -52,7 +53,7 @@ class Decoder:
     """
 
     def __init__(self, model, weights, pool, n_pages, seq_lens, page_table, max_pages, bound,
-                 n_cu=0, attn_split_pages=0, device="cuda"):
+                 n_cu=0, attn_split_pages=0, device="cuda", trace=False):
         self.m = dict(model)
         self.device = torch.device(device)
         self.B = len(seq_lens)
@@ -77,9 +78,15 @@ class Decoder:
         self._kv = mk_kv(pool.data_ptr(), n_pages, self.page_table.data_ptr(),
                          self.seq_lens.data_ptr(), self.rope_cos.data_ptr(),
                          self.rope_sin.data_ptr(), bound)
+        self.trace = None
+        if trace:
+            n = mk_plan_n_tasks(self.plan) * TRACE_WORDS
+            self.trace = torch.zeros(n, dtype=torch.int64, device=dev)
         self._bufs = mk_step_buffers(self.plan_buf.data_ptr(), self.plan_buf.numel(),
                                      self.ws.data_ptr(), self.ws.numel(), self.ctr.data_ptr(),
-                                     self.ctr.numel() * 4, self.status.data_ptr())
+                                     self.ctr.numel() * 4, self.status.data_ptr(),
+                                     _ptr(self.trace),
+                                     0 if self.trace is None else self.trace.numel() * 8)
 
     def close(self):
         if self.plan:

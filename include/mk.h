@@ -134,6 +134,13 @@ typedef struct mk_step_buffers {
   void* workspace; size_t workspace_bytes;  /* activations; no initialisation needed */
   uint32_t* counters; size_t counter_bytes; /* zeroed once before epoch 1 */
   uint32_t* status;                         /* 4 words, zeroed once */
+  uint64_t* trace; size_t trace_bytes;      /* NULL (no tracing), or 8 u64 per task
+                                               (64 * mk_plan_n_tasks bytes), indexed by
+                                               the task's position in the plan image:
+                                               start, routing-wait begin/end, data-wait
+                                               begin/end (0 = no such wait), body end,
+                                               signal end (ticks of the 100 MHz constant
+                                               clock), then cu << 32 | op << 16 | layer */
 } mk_step_buffers;
 
 /* ---- library ---- */

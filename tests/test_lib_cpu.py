@@ -1,0 +1,259 @@
+"""The C-ABI library on the host (no GPU): exports, pool, planner, helpers.
+
+- every function include/mk.h declares is exported by libmk.so;
+- the page/slot pool gives the same page tables as the oracle's plain deque
+  model under a seeded random sequence of leases, extensions and releases;
+- the exported plan image, decoded here from its documented record format,
+  covers exactly the oracle's work enumeration (every output row, every
+  (sequence, kv head, page), every (sequence, query head)) once, and every
+  counter's target equals the number of tasks that signal it;
+- plans validate, simulate without deadlock under random interleavings,
+  and are byte-identical when built twice;
+- calls outside the declared bounds fail before anything launches.
+"""
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import decode_megakernel_persistent_amd as mk
+import oracle as O
+from fixtures.session import lease_pages, spec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Task record (32 bytes): u8 op, u8 flags, u16 layer, u16 wait_a, u16 wait_b,
+# u16 cnt_a, u16 cnt_b, u16 signal, u16 aux, i32 a0, a1, a2, a3.
+TASK = np.dtype([("op", "u1"), ("flags", "u1"), ("layer", "<u2"), ("wait_a", "<u2"),
+                 ("wait_b", "<u2"), ("cnt_a", "<u2"), ("cnt_b", "<u2"), ("signal", "<u2"),
+                 ("aux", "<u2"), ("a0", "<i4"), ("a1", "<i4"), ("a2", "<i4"), ("a3", "<i4")])
+OP_QKV, OP_ATTN, OP_COMB, OP_O, OP_ROUTER, OP_GATEUP, OP_DOWN, OP_LM, OP_FINAL = range(1, 10)
+NO_CTR = 0xFFFF
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 25
+    for n in names:
+        assert hasattr(mk._lib, n), f"libmk.so does not export {n}"
+        assert n in mk.EXPORTED, f"binding does not wrap {n}"
+    assert mk.mk_abi_version() == 1
+
+
+def test_pool_matches_oracle_model():
+    rng = random.Random(5)
+    n_pages, n_slots, pt = 300, 6, 16
+    order = list(range(n_pages))
+    rng.shuffle(order)
+    pool = mk.mk_pool_create(n_pages, pt, n_slots, order)
+    model = O.PoolModel(order, pt, n_slots)
+    live = {}
+    for it in range(400):
+        op = rng.random()
+        if op < 0.45:
+            seq = rng.randrange(1000)
+            tokens = rng.randrange(0, 700)
+            ok = model.lease(seq, tokens)
+            try:
+                slot = mk.mk_pool_lease(pool, seq, tokens)
+                assert ok and slot == model.slot[seq]
+                live[seq] = tokens
+            except mk.MkError as e:
+                assert not ok
+                assert e.status in (mk.MK_ENOMEM, mk.MK_ESTATE)
+        elif op < 0.75 and live:
+            seq = rng.choice(sorted(live))
+            tokens = live[seq] + rng.randrange(0, 200)
+            ok = model.extend(seq, tokens)
+            try:
+                mk.mk_pool_extend(pool, seq, tokens)
+                assert ok
+                live[seq] = tokens
+            except mk.MkError as e:
+                assert not ok and e.status == mk.MK_ENOMEM
+        elif live:
+            seq = rng.choice(sorted(live))
+            model.release(seq)
+            mk.mk_pool_release(pool, seq)
+            del live[seq]
+        assert mk.mk_pool_free_pages(pool) == len(model.free)
+        if live:
+            seqs = sorted(live)
+            mp = max(len(model.pages[s]) for s in seqs) + 1
+            assert mk.mk_pool_page_table(pool, seqs, mp) == model.page_table(seqs, mp)
+    mk.mk_pool_free(pool)
+
+
+def test_pool_lease_is_all_or_nothing():
+    pool = mk.mk_pool_create(10, 16, 4, None)
+    mk.mk_pool_lease(pool, 1, 100)                       # 7 pages
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_pool_lease(pool, 2, 16 * 4)                # 4 > 3 free
+    assert e.value.status == mk.MK_ENOMEM
+    assert mk.mk_pool_free_pages(pool) == 3 and mk.mk_pool_seq_pages(pool, 2) == -1
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_pool_lease(pool, 1, 1)
+    assert e.value.status == mk.MK_ESTATE
+    with pytest.raises(mk.MkError):
+        mk.mk_pool_create(4, 16, 1, [0, 1, 1, 2])        # not a permutation
+    mk.mk_pool_free(pool)
+
+
+def decode_plan(img):
+    hdr = np.frombuffer(img, dtype="<u4", count=16)
+    assert hdr[0] == 0x31504B4D
+    n_cu, n_tasks, n_ctr, off = int(hdr[1]), int(hdr[2]), int(hdr[3]), int(hdr[4])
+    cu_off = np.frombuffer(img, dtype="<u4", count=n_cu + 1, offset=64)
+    tasks = np.frombuffer(img, dtype=TASK, count=n_tasks, offset=off)
+    assert cu_off[0] == 0 and cu_off[-1] == n_tasks and np.all(np.diff(cu_off.astype(np.int64)) >= 0)
+    return n_cu, n_ctr, cu_off, tasks
+
+
+def qkv_rows(p, g, m):
+    """Rows of W_qkv covered by rotary pair p of kv group g: group g owns the
+    q rows of its query heads, then its k head, then its v head; pair p covers
+    dims i and i + d/2 of one head."""
+    d, Hq, Hkv = m["head_dim"], m["n_q_heads"], m["n_kv_heads"]
+    hg = Hq // Hkv
+    h2 = d // 2
+    if p < hg * h2:
+        head, i = g * hg + p // h2, p % h2
+        row = head * d + i
+    elif p < hg * h2 + h2:
+        i = p - hg * h2
+        row = Hq * d + g * d + i
+    else:
+        i = p - hg * h2 - h2
+        row = (Hq + Hkv) * d + g * d + i
+    return row, row + h2
+
+
+def plan_coverage(tasks, m):
+    S = {}
+
+    def add(key, items):
+        S.setdefault(key, []).extend(items)
+
+    for t in tasks:
+        op, l = int(t["op"]), int(t["layer"])
+        a0, a1, a2, a3, aux = int(t["a0"]), int(t["a1"]), int(t["a2"]), int(t["a3"]), int(t["aux"])
+        if op == OP_QKV:
+            add(("qkv", l), [r for p in range(a1, a1 + a2) for r in qkv_rows(p, a0, m)])
+        elif op == OP_ATTN:
+            add(("attn", l), [(a0, a1, p) for p in range(a2, a2 + a3)])
+        elif op == OP_COMB:
+            add(("comb", l), [(a0, h) for h in range(a1, a1 + a2)])
+        elif op == OP_O:
+            add(("o", l), list(range(a1, a1 + a2)))
+        elif op == OP_ROUTER:
+            add(("router", l), list(range(a1, a1 + a2)))
+        elif op == OP_GATEUP:
+            add(("gateup", l), list(range(a1, a1 + a2)) if a0 < 0 else
+                [(a0, aux, f) for f in range(a1, a1 + a2)])
+        elif op == OP_DOWN:
+            add(("down", l), list(range(a1, a1 + a2)))
+        elif op == OP_LM:
+            add(("lm",), list(range(a1, a1 + a2)))
+    return S
+
+
+def build_plan(name, n_cu=256, **over):
+    w = spec(name, 0, **over)
+    pool, rows, max_pages = lease_pages(w, 0)
+    bound = max(w["ctx"]) + w["steps"]
+    p = mk.mk_plan(mk.model_desc(w["model"]), w["ctx"], [v for r in rows for v in r], max_pages,
+                   bound, n_cu=n_cu)
+    return w, pool, p, bound
+
+
+@pytest.mark.parametrize("name,n_cu", [("tiny_dense", 256), ("tiny_dense", 7), ("small_moe", 256),
+                                       ("small_moe", 64), ("moe48_b1_8k", 256)])
+def test_plan_covers_the_oracle_work_exactly_once(name, n_cu):
+    w, pool, p, bound = build_plan(name, n_cu)
+    try:
+        img = mk.mk_plan_export(p)
+        n_cu2, n_ctr, cu_off, tasks = decode_plan(img)
+        assert n_cu2 == n_cu and mk.mk_plan_n_tasks(p) == len(tasks)
+        got = plan_coverage(tasks, w["model"])
+        want = O.work_sets(w["model"], [bound] * w["batch"])
+        assert set(got) == set(want)
+        for k, items in got.items():
+            assert len(items) == len(set(items)), f"{k}: covered more than once"
+            assert set(items) == want[k], f"{k}: coverage differs from the oracle's work"
+        # counter targets = number of tasks signalling each counter; waits carry the target
+        tg = np.array(mk.mk_plan_counter_targets(p), dtype=np.int64)
+        sig = tasks["signal"][tasks["signal"] != NO_CTR].astype(np.int64)
+        assert np.array_equal(np.bincount(sig, minlength=n_ctr), tg)
+        for wf, cf in (("wait_a", "cnt_a"), ("wait_b", "cnt_b")):
+            m_ = tasks[wf] != NO_CTR
+            assert np.array_equal(tasks[cf][m_].astype(np.int64), tg[tasks[wf][m_].astype(np.int64)])
+        mk.mk_plan_validate(p)
+        mk.mk_plan_simulate(p, 11, 3)
+    finally:
+        mk.mk_plan_free(p)
+        mk.mk_pool_free(pool)
+
+
+def test_plan_is_deterministic():
+    w, pool, p1, bound = build_plan("small_moe")
+    _, pool2, p2, _ = build_plan("small_moe")
+    assert mk.mk_plan_export(p1) == mk.mk_plan_export(p2)
+    for q in (p1, p2):
+        mk.mk_plan_free(q)
+    mk.mk_pool_free(pool)
+    mk.mk_pool_free(pool2)
+
+
+def test_plan_rejects_out_of_bounds():
+    w = spec("tiny_dense", 0)
+    desc = mk.model_desc(w["model"])
+    pt = [0] * 8
+    with pytest.raises(mk.MkError) as e:                     # 128 + 1 > bound 100
+        mk.mk_plan(desc, [128], list(range(8)) + [0] * 0, 8, 100, n_cu=16)
+    assert e.value.status == mk.MK_EBOUNDS
+    with pytest.raises(mk.MkError) as e:                     # bound needs 9 pages, table has 8
+        mk.mk_plan(desc, [128], list(range(8)), 8, 129, n_cu=16)
+    assert e.value.status == mk.MK_EBOUNDS
+    with pytest.raises(mk.MkError) as e:                     # unmapped page below the bound
+        mk.mk_plan(desc, [10], [0, -1] + pt[2:], 8, 128, n_cu=16)
+    assert e.value.status == mk.MK_EBOUNDS
+    bad = dict(w["model"], page_tokens=32)
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan(mk.model_desc(bad), [10], list(range(8)), 8, 64, n_cu=16)
+    assert e.value.status == mk.MK_EUNSUPPORTED
+
+
+def test_step_status_decoding():
+    assert mk.mk_step_status([0, 0, 0, 0])[0] == mk.MK_OK
+    st, msg = mk.mk_step_status([1, 17, 3, 42])
+    assert st == mk.MK_ETIMEOUT and "task 17" in msg and "counter 3" in msg
+    assert mk.mk_step_status([2, 5, 0, 0])[0] == mk.MK_EBOUNDS
+
+
+def test_step_bytes_match_oracle():
+    for name in ("tiny_dense", "small_moe", "moe48_b1_8k"):
+        m = spec(name, 0)["model"]
+        for ctx in ([0], [128], [8192], [100, 5000]):
+            a = mk.mk_step_bytes(mk.model_desc(m), ctx)
+            b = O.step_bytes(m, ctx)
+            assert a == pytest.approx(b, rel=1e-12)
+
+
+def test_rope_table_matches_oracle():
+    import torch
+    n = 300
+    c = np.empty(n * 64, dtype=np.float32)
+    s = np.empty(n * 64, dtype=np.float32)
+    mk.mk_rope_table(1e4, 128, n, c.ctypes.data, s.ctypes.data)
+    for p in (0, 1, 17, 299):
+        oc, os_ = O.rope_cos_sin(1e4, 128, p)
+        assert np.array_equal(c.reshape(n, 64)[p], oc.numpy())
+        assert np.array_equal(s.reshape(n, 64)[p], os_.numpy())
