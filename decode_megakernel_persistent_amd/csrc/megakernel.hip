@@ -2,21 +2,31 @@
 //
 // One workgroup of 512 threads per compute unit walks its own task list
 // (megakernel page, "What is a Megakernel?": one resident block per
-// processor, work read from a task list in global memory, dependencies as
-// counters in global memory that finished tasks increment and waiting tasks
-// spin on). Every task first issues the loads that do not depend on other
-// tasks (weights, KV of earlier steps), then waits for its producers, then
-// computes, stores and signals.
+// processor, work read from a task list in global memory, tasks that wait
+// for exactly the producers they read). Every task first issues the loads
+// that depend on no other task (weights, KV pages of earlier steps) into
+// registers, then waits for its inputs, then computes and publishes.
+//
+// Synchronisation. Activations pass between tasks as tagged words (epoch in
+// the high half, fp32 bits in the low half) written with device-coherent
+// stores; a consumer spins on the words themselves until they carry the
+// step's epoch. On MI355X each XCD has its own L2, and a counter handoff
+// that releases with an L2 writeback and acquires with an L2 invalidate costs
+// several microseconds per dependency stage; a tagged word needs neither,
+// because the value and its completion mark travel in one coherent access.
+// Each task also adds one to its completion counter (spread over 8 lines),
+// so that a finished step leaves every counter at steps x producers.
 //
 // Task bodies:
 //  - projections (QKV, O, router, expert gate/up, expert down, LM head) are
-//    block GEMVs streaming 16-byte bf16 chunks per thread with fp32
-//    accumulation and wave reductions; RMSNorm is recomputed as a prologue
-//    by every consumer tile; RoPE + KV append, residual adds, SwiGLU, the
-//    weighted expert combine and the local argmax are epilogues;
+//    GEMVs: each lane group of 64 (or 32) lanes holds whole rows as 16-byte
+//    bf16 chunks, accumulates in fp32 and reduces with DPP row operations;
+//    RMSNorm is recomputed by every consumer tile from the gathered vector;
+//    RoPE + KV append, residual adds, SwiGLU, the weighted expert combine and
+//    the local argmax are epilogues;
 //  - paged attention splits use MFMA 16x16x16 bf16 tiles on 16-token pages
-//    (queries and probabilities carried as bf16 hi + lo pairs), with an
-//    online softmax across pages and a log-sum-exp merge across waves;
+//    (queries and probabilities carried as bf16 hi + lo pairs), an online
+//    softmax across pages and a log-sum-exp merge across waves;
 //  - the split combine is a log-sum-exp merge in fixed split order.
 #include <hip/hip_runtime.h>
 
@@ -32,265 +42,329 @@
 namespace mk {
 namespace dev {
 
-constexpr int SMEM_MAIN = GEMV_LDS_FLOATS;   // per-row partial sums, attention merge
-constexpr int SMEM_AUX = 4096;               // small reductions, routing, combine weights
-constexpr float NEG_INF = -__builtin_inff();
+constexpr int LDS_VEC = 8192;
+
+constexpr int STAGE_CHUNKS = 12;  // 1 KB wave chunks per wave in the staging area (96 KB)
 
 struct Smem {
-  float main[SMEM_MAIN];
-  float aux[SMEM_AUX];
-  int route_ids[16];
+  float vec[LDS_VEC];  // gathered input vector(s), normalised in place
+  union {
+    uint4 stage[NWAVE * STAGE_CHUNKS * 64];  // expert: down-projection rows (direct-to-LDS loads)
+    float att[NWAVE * STAGE_CHUNKS * 256];   // attention: per-wave partials; combine: split words
+  };
+  float out[2048];     // per-row dot products
+  float res[2048];     // residual rows
+  float red[64];       // block reductions
   float route_w[16];
-  int flag;
-  uint64_t tw[4];  // trace: (begin, end) of the routing wait and of the data wait
+  int route_ids[16];
+  int fail;
+  uint64_t tw[4];      // trace: (begin, end) of the routing wait and of the data wait
 };
 
-// ------------------------------------------------------------------ block GEMV
+struct Ctx {
+  const KArgs& a;
+  Smem& s;
+  uint64_t t0;
+  uint32_t ti;
+};
 
-// Threads per row of a GEMV task, carried in the task record (high nibble of
-// flags = log2 TC) so that index math derived from it is recomputed per task.
-__device__ __forceinline__ int task_tc(const Task& t) { return 1 << (t.flags >> 4); }
-
-// Jobs j < nj are rows; thread (rg = tid / TC, tc = tid % TC) takes jobs
-// rg + k*TR, reading CPL 16-byte chunks (chunk index tc + c*TC) of each row and
-// dotting them with its slice u[CPL*8] of the input vector. Rows move through
-// two register batches of NR rows; both batches are issued before `ready`
-// (the dependency wait, which also fills u). The reduced dot of job j is
-// sum_s part[s*nj + j] over s < max(1, TC/64) after the final barrier.
-template <int CPL, int NR, class RowFn, class ReadyFn>
-__device__ __forceinline__ bool gemv_block(int nj, int TC, const RowFn& rowptr,
-                                           const ReadyFn& ready, float* part, float* u) {
-  const int tid = threadIdx.x;
-  const int TR = NT / TC;
-  const int rg = tid / TC, tc = tid % TC;
-  const int my = rg < nj ? (nj - rg + TR - 1) / TR : 0;
-  const int nb = (my + NR - 1) / NR;
-  uint4 wa[NR][CPL], wb[NR][CPL];
-  auto issue = [&](uint4 (&w)[NR][CPL], int bi) {
+// Gather tagged words into LDS: dst[i] = value of word i for i < n, where
+// word i sits at src1 + i for i < n1 and at src2 + (i - n1) after that; MAXW
+// words per thread per batch. which: 0 = routing wait, 1 = data wait (trace
+// slots), -1 = untraced. Uniform result.
+template <int MAXW>
+__device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, const uint64_t* src2, int n,
+                                        float* dst, int which) {
+  const KArgs& a = c.a;
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
+  bool ok = true;
+  for (int base = 0; base < n && ok; base += MAXW * NT) {
+    const int t = tid();
+    float v[MAXW];
+    ok = read_words<MAXW>(a, [&](int k) -> const uint64_t* {
+      const int i = base + t + k * NT;
+      return i < n1 ? src1 + i : (i < n ? src2 + (i - n1) : nullptr);
+    }, v, c.t0, c.ti);
+    if (ok) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int k = bi * NR + r;
-      if (k < my) {
-        const uint4* p = rowptr(rg + k * TR);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) w[r][c] = ld_nt(p + tc + c * TC);
+      for (int k = 0; k < MAXW; ++k) {
+        const int i = base + t + k * NT;
+        if (i < n) dst[i] = v[k];
       }
-    }
-  };
-  auto consume = [&](uint4 (&w)[NR][CPL], int bi) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int k = bi * NR + r;
-      if (k < my) {
-        float s = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) s += dot8(w[r][c], u + c * 8);
-        const int j = rg + k * TR;
-        if (TC >= 64) {
-          s = wave_sum(s);
-          if ((tid & 63) == 0) part[(tc >> 6) * nj + j] = s;
-        } else {
-          s = group_sum(s, 32);
-          if ((tid & 31) == 0) part[j] = s;
-        }
-      }
-    }
-  };
-  issue(wa, 0);
-  issue(wb, 1);
-  if (!ready()) return false;
-  for (int bi = 0; bi < nb; bi += 2) {
-    consume(wa, bi);
-    issue(wa, bi + 2);
-    if (bi + 1 < nb) {
-      consume(wb, bi + 1);
-      issue(wb, bi + 3);
     }
   }
+  if (!ok) c.s.fail = 1;
   __syncthreads();
-  return true;
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
+  return c.s.fail == 0;
+}
+template <int MAXW>
+__device__ __forceinline__ bool gather(Ctx& c, const uint64_t* src, int n, float* dst, int which) {
+  return gather2<MAXW>(c, src, n, src, n, dst, which);
 }
 
-__device__ __forceinline__ float job_sum(const float* part, int nj, int TC, int j) {
-  float s = part[j];
-  for (int q = 1; q < TC / 64; ++q) s += part[q * nj + j];
-  return s;
-}
-
-// Load this thread's slice of a K-vector (fp32 or bf16 source), optionally
-// RMS-normalised with gains `gain`: u = x / sqrt(mean(x^2) + eps) * gain.
-template <int CPL>
-__device__ __forceinline__ void load_slice(const KArgs& a, const float* xf, const uint16_t* xb,
-                                           const uint16_t* gain, int K, int TC, float* u,
-                                           float* red8) {
-  const int tc = threadIdx.x % TC;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int col = (tc + c * TC) * 8;
-    if (xf) {
-      const float4 p0 = *(const float4*)(xf + col);
-      const float4 p1 = *(const float4*)(xf + col + 4);
-      u[c * 8 + 0] = p0.x; u[c * 8 + 1] = p0.y; u[c * 8 + 2] = p0.z; u[c * 8 + 3] = p0.w;
-      u[c * 8 + 4] = p1.x; u[c * 8 + 5] = p1.y; u[c * 8 + 6] = p1.z; u[c * 8 + 7] = p1.w;
-    } else {
-      const uint4 w = *(const uint4*)(xb + col);
-      u[c * 8 + 0] = bf_lo(w.x); u[c * 8 + 1] = bf_hi(w.x);
-      u[c * 8 + 2] = bf_lo(w.y); u[c * 8 + 3] = bf_hi(w.y);
-      u[c * 8 + 4] = bf_lo(w.z); u[c * 8 + 5] = bf_hi(w.z);
-      u[c * 8 + 6] = bf_lo(w.w); u[c * 8 + 7] = bf_hi(w.w);
-    }
-  }
-  if (!gain) return;
+// In-place RMSNorm of LDS v[0..K): v = v / sqrt(mean(v^2) + eps) * g.
+// Fixed summation order (strided per thread, then waves in order).
+__device__ __forceinline__ void rmsnorm_lds(Ctx& c, float* v, int K, const uint16_t* g) {
   float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < CPL * 8; ++i) ss = fmaf(u[i], u[i], ss);
+  for (int i = tid(); i < K; i += NT) ss = fmaf(v[i], v[i], ss);
   ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = ss;
+  if ((tid() & 63) == 0) c.s.red[tid() >> 6] = ss;
   __syncthreads();
   float tot = 0.f;
 #pragma unroll
-  for (int w = 0; w < NWAVE; ++w) tot += red8[w];
-  tot *= (float)TC / (float)NT;  // every row group holds a full copy of the columns
-  const float rs = 1.0f / sqrtf(tot / (float)K + a.eps);
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int col = (tc + c * TC) * 8;
-    const uint4 g = *(const uint4*)(gain + col);
-    const float gv[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y),
-                         bf_lo(g.z), bf_hi(g.z), bf_lo(g.w), bf_hi(g.w)};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) u[c * 8 + i] = u[c * 8 + i] * rs * gv[i];
-  }
+  for (int w = 0; w < NWAVE; ++w) tot += c.s.red[w];
+  const float rs = 1.0f / sqrtf(tot / (float)K + c.a.eps);
+  for (int i = tid(); i < K; i += NT) v[i] = v[i] * rs * bf2f(g[i]);
+  __syncthreads();
 }
 
-// Hidden state entering layer l (batch row 0): the embedding row for l = 0.
-__device__ __forceinline__ void layer_input(const KArgs& a, int l, const float** xf,
-                                            const uint16_t** xb) {
-  if (l == 0) {
-    int tok = a.tok_in[0];
-    if (tok < 0 || tok >= a.V) {  // an id outside the vocabulary reads row 0 and is reported
-      if (threadIdx.x == 0) raise_status(a, DS_BOUNDS, 0xFFFFFFFFu, (uint32_t)tok, 0u);
-      tok = 0;
-    }
-    *xf = nullptr;
-    *xb = a.embed + (size_t)tok * a.H;
-  } else {
-    *xf = a.xf + (size_t)(l - 1) * a.s_x;
-    *xb = nullptr;
+// ------------------------------------------------------------------ GEMV tiles
+
+// A tile of R rows of K = TC*CPL*8 bf16 elements held in registers: lane
+// group lg (TC lanes) holds rows lg, lg + G, ... (G lane groups), each as
+// CPL 16-byte chunks per lane (chunk index tc + c*TC). Loads are issued by
+// issue() before the task waits; dots() reduces each row against the LDS
+// vector and writes out[row].
+template <int CPL, int RPW>
+struct Tile {
+  uint4 w[RPW][CPL];
+  int nr, lg, tc, G, TC;
+
+  template <class RowPtr>
+  __device__ __forceinline__ void issue(int R, int tc_width, const RowPtr& rowptr) {
+    TC = tc_width;
+    G = NT / TC;
+    lg = tid() / TC;
+    tc = tid() % TC;
+    nr = lg < R ? (R - lg + G - 1) / G : 0;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      if (r < nr) {
+        const uint4* p = rowptr(lg + r * G);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) w[r][c] = ld_nt(p + tc + c * TC);
+      }
   }
+  __device__ __forceinline__ void dots(const float* u, float* out) {
+    float acc[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float4* up = (const float4*)(u + (tc + c * TC) * 8);
+      const float4 p0 = up[0], p1 = up[1];
+      const float uc[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        if (r < nr) acc[r] = dot8(w[r][c], uc, acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      if (r < nr) {
+        const float s = group_sum(acc[r], TC);
+        if (tc == 0) out[lg + r * G] = s;
+      }
+  }
+};
+
+// A tile like Tile, but its 16-byte chunks go straight from global memory to
+// LDS (direct-to-LDS loads, no registers): wave w's chunk c of row slot r is
+// one 1 KB block at stage[((w * RPW + r) * CPL + c) * 64 + lane], written and
+// later read by the same lane. The caller waits for the loads (vmcnt) before
+// dots().
+template <int CPL, int RPW>
+struct StageTile {
+  int nr, lg, tc, G, TC, w;
+
+  template <class RowPtr>
+  __device__ __forceinline__ void issue(int R, int tc_width, const RowPtr& rowptr, uint4* stage) {
+    TC = tc_width;
+    G = NT / TC;
+    lg = tid() / TC;
+    tc = tid() % TC;
+    w = __builtin_amdgcn_readfirstlane(tid() >> 6);
+    nr = lg < R ? (R - lg + G - 1) / G : 0;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      if (r < nr) {
+        const uint4* p = rowptr(lg + r * G);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          __builtin_amdgcn_global_load_lds((const void*)(p + tc + c * TC),
+                                           (__attribute__((address_space(3))) void*)(stage + ((w * RPW + r) * CPL + c) * 64),
+                                           16, 0, 0);
+      }
+  }
+  __device__ __forceinline__ void dots(const uint4* stage, const float* u, float* out) {
+    const int lane = tid() & 63;
+    float acc[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float4* up = (const float4*)(u + (tc + c * TC) * 8);
+      const float4 p0 = up[0], p1 = up[1];
+      const float uc[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        if (r < nr) acc[r] = dot8(stage[((w * RPW + r) * CPL + c) * 64 + lane], uc, acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      if (r < nr) {
+        const float s = group_sum(acc[r], TC);
+        if (tc == 0) out[lg + r * G] = s;
+      }
+  }
+};
+
+// Token id of sequence b, checked against the vocabulary.
+__device__ __forceinline__ int token_row(const KArgs& a, int b) {
+  int tok = a.tok_in[b];
+  if (tok < 0 || tok >= a.V) {  // an id outside the vocabulary reads row 0 and is reported
+    if (tid() == 0) raise_status(a, DS_BOUNDS, 0xFFFFFFFFu, (uint32_t)tok, 0u);
+    tok = 0;
+  }
+  return tok;
+}
+
+// Hidden state entering layer l of sequence b into LDS dst: the embedding
+// row for l = 0 (bf16, no wait), else the tagged output of layer l - 1.
+__device__ __forceinline__ bool layer_input(Ctx& c, int l, int b, float* dst) {
+  const KArgs& a = c.a;
+  if (l == 0) {
+    const uint16_t* e = a.embed + (size_t)token_row(a, b) * a.H;
+    for (int i = tid(); i < a.H; i += NT) dst[i] = bf2f(e[i]);
+    __syncthreads();
+    return true;
+  }
+  return gather<4>(c, a.x + (size_t)(l - 1) * a.s_x + (size_t)b * a.H, a.H, dst, 1);
+}
+
+// Residual value of row r entering layer l (read once the layer's inputs are known complete).
+__device__ __forceinline__ float resid(Ctx& c, int l, int b, int r, bool* fail) {
+  const KArgs& a = c.a;
+  if (l == 0) return bf2f(a.embed[(size_t)token_row(a, b) * a.H + r]);
+  return get_tagged(a, a.x + (size_t)(l - 1) * a.s_x + (size_t)b * a.H + r, c.t0, c.ti, fail);
 }
 
 // ------------------------------------------------------------------ routing
 
-// softmax over the E router logits of layer l, top-k (ties to the lower
-// index), weights renormalised over the selection when norm_topk. Wave 0
-// computes; the result is in s.route_ids / s.route_w after the barrier.
-__device__ __forceinline__ void route(const KArgs& a, int l, Smem& s) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const float* r = a.rlog + (size_t)l * a.s_rlog;
-    float v[4];
-    float mx = NEG_INF;
+// softmax over the E router logits in r (LDS), top-k (ties to the lower
+// index), weights renormalised over the selection when norm_topk. Thread e
+// owns expert e; its rank is the number of experts with a larger
+// probability, or an equal one and a lower index, so the k selected experts
+// land in rank order without a serial selection loop. The result is in
+// s.route_ids / s.route_w after the final barrier.
+__device__ __forceinline__ void route(Ctx& c, const float* r) {
+  const KArgs& a = c.a;
+  Smem& s = c.s;
+  const int t = tid(), E = a.E;
+  float* p = s.out + 1024;  // [E]
+  const float v = t < E ? r[t] : NEG_INF;
+  float m = wave_max(v);
+  if ((t & 63) == 0) s.red[t >> 6] = m;
+  __syncthreads();
+  float M = s.red[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = e < a.E ? r[e] : NEG_INF;
-      mx = fmaxf(mx, v[i]);
+  for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, s.red[w]);
+  const float ex = t < E ? expf(v - M) : 0.f;
+  const float sm = wave_sum(ex);
+  __syncthreads();
+  if ((t & 63) == 0) s.red[t >> 6] = sm;
+  __syncthreads();
+  float S = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) S += s.red[w];
+  const float pe = ex / S;
+  if (t < E) p[t] = pe;
+  __syncthreads();
+  if (t < E) {
+    int rank = 0;
+    for (int e = 0; e < E; ++e) {
+      const float q = p[e];
+      rank += (q > pe || (q == pe && e < t)) ? 1 : 0;
     }
-    mx = wave_max(mx);
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = (lane + 64 * i) < a.E ? expf(v[i] - mx) : 0.f;
-      sum += v[i];
+    if (rank < a.K) {
+      s.route_ids[rank] = t;
+      s.route_w[rank] = pe;
     }
-    sum = wave_sum(sum);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = (lane + 64 * i) < a.E ? v[i] / sum : NEG_INF;
-    float wsum = 0.f;
-    for (int j = 0; j < a.K; ++j) {
-      float bv = NEG_INF;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (p[i] > bv) { bv = p[i]; bi = lane + 64 * i; }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (lane == 0) { s.route_ids[j] = bi; s.route_w[j] = bv; }
-      wsum += bv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == bi) p[i] = NEG_INF;
-    }
-    if (lane == 0 && a.norm_topk)
-      for (int j = 0; j < a.K; ++j) s.route_w[j] = s.route_w[j] / wsum;
   }
   __syncthreads();
+  if (t == 0 && a.norm_topk) {
+    float wsum = 0.f;
+    for (int j = 0; j < a.K; ++j) wsum += s.route_w[j];
+    for (int j = 0; j < a.K; ++j) s.route_w[j] = s.route_w[j] / wsum;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ bool routing(Ctx& c, int l, int b) {
+  const KArgs& a = c.a;
+  if (!gather<1>(c, a.rlog + (size_t)l * a.s_rlog + (size_t)b * a.E, a.E, c.s.out, 0)) return false;
+  route(c, c.s.out);
+  return true;
 }
 
 // ------------------------------------------------------------------ tasks
 
 template <int CPL>
-__device__ __forceinline__ bool task_qkv(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  constexpr int NR = CPL == 1 ? 8 : (CPL == 2 ? 4 : (CPL == 3 ? 3 : 2));
+__device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
+  constexpr int RPW = 24 / CPL < GEMV_RPW_MAX ? 24 / CPL : GEMV_RPW_MAX;
+  const KArgs& a = c.a;
   const int l = t.layer, g = t.a0, p0 = t.a1, np = t.a2, nj = 2 * np;
   const int H = a.H, D = a.D;
   const int QR = (a.Hq + 2 * a.Hkv) * D;
-  const int TC = task_tc(t);
   const uint16_t* W = a.wqkv + (size_t)l * QR * H;
-  auto rowptr = [&](int j) {
+  Tile<CPL, RPW> tile;
+  tile.issue(nj, (H / 8) / CPL, [&](int j) {
     int head, i, row;
     qkv_pair(p0 + (j >> 1), g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
-    row += (j & 1) * (D / 2);
-    return (const uint4*)(W + (size_t)row * H);
-  };
-  float u[CPL * 8];
-  auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
-    const float* xf;
-    const uint16_t* xb;
-    layer_input(a, l, &xf, &xb);
-    load_slice<CPL>(a, xf, xb, a.attn_norm + (size_t)l * H, H, TC, u, s.aux);
-    return true;
-  };
-  if (!gemv_block<CPL, NR>(nj, TC, rowptr, ready, s.main, u)) return false;
+    return (const uint4*)(W + (size_t)(row + (j & 1) * (D / 2)) * H);
+  });
+  if (!layer_input(c, l, 0, c.s.vec)) return false;
+  rmsnorm_lds(c, c.s.vec, H, a.attn_norm + (size_t)l * H);
+  tile.dots(c.s.vec, c.s.out);
+  __syncthreads();
   const int pos = a.seq_lens[0];
   const bool in_bounds = pos >= 0 && pos + 1 <= a.bound && pos < a.n_rope;
   int32_t phys = -1;
   if (in_bounds) phys = a.page_table[pos >> 4];
   const bool page_ok = in_bounds && phys >= 0 && phys < a.n_pages;
-  if (!page_ok && threadIdx.x == 0) raise_status(a, DS_BOUNDS, ti, (uint32_t)pos, (uint32_t)phys);
-  for (int q = threadIdx.x; q < np; q += NT) {
-    const float y0 = job_sum(s.main, nj, TC, 2 * q), y1 = job_sum(s.main, nj, TC, 2 * q + 1);
+  if (!page_ok && tid() == 0) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)pos, (uint32_t)phys);
+  for (int q = tid(); q < np; q += NT) {
+    const float y0 = c.s.out[2 * q], y1 = c.s.out[2 * q + 1];
     int head, i, row;
     const int sec = qkv_pair(p0 + q, g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
-    if (!page_ok) continue;
+    const int pc = page_ok ? pos : 0;
     float r0 = y0, r1 = y1;
     if (sec < 2) {
-      const float c = a.rope_cos[(size_t)pos * (D / 2) + i];
-      const float sn = a.rope_sin[(size_t)pos * (D / 2) + i];
-      r0 = y0 * c - y1 * sn;
-      r1 = y1 * c + y0 * sn;
+      const float cs = a.rope_cos[(size_t)pc * (D / 2) + i];
+      const float sn = a.rope_sin[(size_t)pc * (D / 2) + i];
+      r0 = y0 * cs - y1 * sn;
+      r1 = y1 * cs + y0 * sn;
     }
     if (sec == 0) {
-      float* qd = a.q + (size_t)l * a.s_q + (size_t)head * D;
-      qd[i] = r0;
-      qd[i + D / 2] = r1;
+      uint64_t* qd = a.q + (size_t)l * a.s_q + (size_t)head * D;
+      st_tagged(qd + i, r0, a.epoch);
+      st_tagged(qd + i + D / 2, r1, a.epoch);
     } else {
-      uint16_t* base = a.pool + (size_t)phys * a.page_stride + (size_t)l * a.layer_stride +
-                       (size_t)g * 2 * 16 * D;
-      const int slot = pos & 15;
-      if (sec == 1) {
-        base[slot * D + i] = (uint16_t)f2bf(r0);
-        base[slot * D + i + D / 2] = (uint16_t)f2bf(r1);
-      } else {
-        base[16 * D + i * 16 + slot] = (uint16_t)f2bf(r0);
-        base[16 * D + (i + D / 2) * 16 + slot] = (uint16_t)f2bf(r1);
+      const uint32_t b0 = f2bf(r0), b1 = f2bf(r1);
+      uint64_t* kn = a.kvn + (size_t)l * a.s_kvn + ((size_t)g * 2 + (sec - 1)) * D;
+      st_tagged(kn + i, __uint_as_float(b0), a.epoch);
+      st_tagged(kn + i + D / 2, __uint_as_float(b1), a.epoch);
+      if (page_ok) {
+        uint16_t* base = a.pool + (size_t)phys * a.page_stride + (size_t)l * a.layer_stride +
+                         (size_t)g * 2 * 16 * D;
+        const int slot = pos & 15;
+        if (sec == 1) {
+          base[slot * D + i] = (uint16_t)b0;
+          base[slot * D + i + D / 2] = (uint16_t)b1;
+        } else {
+          base[16 * D + i * 16 + slot] = (uint16_t)b0;
+          base[16 * D + (i + D / 2) * 16 + slot] = (uint16_t)b1;
+        }
       }
     }
   }
@@ -298,21 +372,23 @@ __device__ __forceinline__ bool task_qkv(const KArgs& a, const Task& t, uint32_t
 }
 
 template <int D>
-__device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
+__device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   constexpr int KQ = D / 4;     // dims of one lane group in the QK product
   constexpr int NK4 = D / 32;   // 16-byte K loads per lane per page
   constexpr int NB = D / 16;    // 16-dim blocks of the PV product
   constexpr int NS = D / 16;    // MFMA k-steps of the QK product
+  const KArgs& a = c.a;
+  Smem& s = c.s;
   const int l = t.layer, b = t.a0, g = t.a1, pg0 = t.a2, npg = t.a3, split = t.aux;
   const int HG = a.HG;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = tid() & 63, w = tid() >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
   const int pos = a.seq_lens[b];
   const int n_tok = min(pos + 1, a.bound);
   const int pg_lim = min(pg0 + npg, (n_tok + 15) >> 4);
   const int first = pg0 + w;
   const int cnt = first < pg_lim ? (pg_lim - first + NWAVE - 1) / NWAVE : 0;
-  const int cur = pos >> 4;
+  const int cur = pos >> 4, ns = pos & 15;
   const uint16_t* lbase = a.pool + (size_t)l * a.layer_stride + (size_t)g * 2 * 16 * D;
   const int32_t* prow = a.page_table + (size_t)b * a.max_pages;
   uint4 k0[NK4], k1[NK4];
@@ -336,14 +412,15 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) vv[nb] = ld_nt2((const uint2*)(vp + nb * 256));
   };
-  const int pA = first, pB = first + NWAVE;
-  const bool preA = cnt > 0 && pA < cur;
-  const bool preB = cnt > 1 && pB < cur;
-  if (preA) load(k0, v0, pA);
-  if (preB) load(k1, v1, pB);
-  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
-  if (cnt > 0 && !preA) load(k0, v0, pA);
-  if (cnt > 1 && !preB) load(k1, v1, pB);
+  if (cnt > 0) load(k0, v0, first);
+  if (cnt > 1) load(k1, v1, first + NWAVE);
+
+  // inputs: the group's queries and the new token's K and V (bf16 bits), one batch
+  float* qv = s.vec;                 // [HG][D]
+  float* kvnew = s.vec + HG * D;     // [2][D]
+  const uint64_t* qsrc = a.q + (size_t)l * a.s_q + ((size_t)b * a.Hq + (size_t)g * HG) * D;
+  const uint64_t* ksrc = a.kvn + (size_t)l * a.s_kvn + ((size_t)b * a.Hkv + g) * 2 * D;
+  if (!gather2<3>(c, qsrc, HG * D, ksrc, HG * D + 2 * D, qv, 1)) return false;
 
   // query operand: column r16 < 8 carries bf16(q) of head r16, column
   // r16 >= 8 the bf16 residual q - bf16(q) of head r16 - 8
@@ -352,7 +429,7 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
   v4s qop[NS];
   {
     const bool valid = hh < HG;
-    const float* qp = a.q + (size_t)l * a.s_q + (size_t)(g * HG + (valid ? hh : 0)) * D + kq * KQ;
+    const float* qp = qv + (valid ? hh : 0) * D + kq * KQ;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const float4 x = valid ? *(const float4*)(qp + 4 * st) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -360,7 +437,7 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t hi = f2bf(xs[j]);
-        const uint32_t v = lo_part ? f2bf(xs[j] - bf2f((uint16_t)hi)) : hi;
+        const uint32_t v = lo_part ? f2bf(xs[j] - bf2f(hi)) : hi;
         qop[st][j] = (short)v;
       }
     }
@@ -370,12 +447,35 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
   const float scale = a.attn_scale;
-  auto compute = [&](const uint4 (&kk)[NK4], const uint2 (&vv)[NB], int pg) {
+  auto compute = [&](uint4 (&kk)[NK4], uint2 (&vv)[NB], int pg) {
+    if (pg == cur) {
+      // the new token's slot: its K and V come from this step's QKV tasks
+      if (r16 == ns) {
+#pragma unroll
+        for (int i = 0; i < NK4; ++i) {
+          const float* kn = kvnew + kq * KQ + 8 * i;
+          kk[i] = make_uint4(__float_as_uint(kn[0]) | (__float_as_uint(kn[1]) << 16),
+                             __float_as_uint(kn[2]) | (__float_as_uint(kn[3]) << 16),
+                             __float_as_uint(kn[4]) | (__float_as_uint(kn[5]) << 16),
+                             __float_as_uint(kn[6]) | (__float_as_uint(kn[7]) << 16));
+        }
+      }
+      if (kq == (ns >> 2)) {
+        const int e = ns & 3;
+        const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        const int sh = (e & 1) ? 16 : 0;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t vb = __float_as_uint(kvnew[D + nb * 16 + r16]) << sh;
+          const uint32_t x = vv[nb].x, y = vv[nb].y;
+          vv[nb] = e < 2 ? make_uint2((x & keep) | vb, y) : make_uint2(x, (y & keep) | vb);
+        }
+      }
+    }
     v4f S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const uint4 kv = kk[st >> 1];
-      typedef unsigned u2v __attribute__((ext_vector_type(2)));
       const u2v pr = (st & 1) ? u2v{kv.z, kv.w} : u2v{kv.x, kv.y};
       S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, pr), qop[st], S, 0, 0, 0);
     }
@@ -402,7 +502,7 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t hi = f2bf(pj[j]);
-      P[j] = (short)(lo_part ? f2bf(pj[j] - bf2f((uint16_t)hi)) : hi);
+      P[j] = (short)(lo_part ? f2bf(pj[j] - bf2f(hi)) : hi);
     }
     float aj[4];
 #pragma unroll
@@ -433,11 +533,11 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
       if (i + 3 < cnt) load(k1, v1, first + (i + 3) * NWAVE);
     }
   }
-  if (bad && lane == 0) raise_status(a, DS_BOUNDS, ti, (uint32_t)b, 0xFFFFFFFFu);
+  if (bad && lane == 0) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)b, 0xFFFFFFFFu);
   // merge hi/lo rows and publish this wave's partial in LDS
-  float* Ow = s.main;                     // [NWAVE][HG][D]
-  float* mw = s.aux;                      // [NWAVE][8]
-  float* lw = s.aux + NWAVE * 8;          // [NWAVE][8]
+  float* Ow = s.att;                      // [NWAVE][HG][D]
+  float* mw = s.red;                      // [NWAVE][8]
+  float* lw = s.out;                      // [NWAVE][8]
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -451,8 +551,10 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
     lw[w * 8 + lane] = l_run;
   }
   __syncthreads();
-  const int PS = D + 4;
-  for (int idx = threadIdx.x; idx < HG * D; idx += NT) {
+  const int PS = D + 2;
+  uint64_t* dst0 = a.part + (size_t)l * a.s_part +
+                   (((size_t)b * a.Hkv + g) * a.S_max + split) * HG * PS;
+  for (int idx = tid(); idx < HG * D; idx += NT) {
     const int head = idx / D, dim = idx % D;
     float M = NEG_INF;
 #pragma unroll
@@ -465,183 +567,276 @@ __device__ __forceinline__ bool task_attn(const KArgs& a, const Task& t, uint32_
       oo += e * Ow[(q * HG + head) * D + dim];
       LL += e * lw[q * 8 + head];
     }
-    float* dst = a.part + (size_t)l * a.s_part +
-                 ((size_t)(b * a.Hq + g * HG + head) * a.S_max + split) * PS;
-    dst[dim] = oo;
+    uint64_t* dst = dst0 + (size_t)head * PS;
+    st_tagged(dst + dim, oo, a.epoch);
     if (dim == 0) {
-      dst[D] = M;
-      dst[D + 1] = LL;
+      st_tagged(dst + D, M, a.epoch);
+      st_tagged(dst + D + 1, LL, a.epoch);
     }
   }
   return true;
 }
 
-__device__ __forceinline__ bool task_comb(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  const int l = t.layer, b = t.a0, h = t.a1, S = t.a3, D = a.D, PS = D + 4;
-  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
-  const float* base = a.part + (size_t)l * a.s_part + (size_t)(b * a.Hq + h) * a.S_max * PS;
-  float* ms = s.aux;          // [S]
-  float* ls = s.aux + 1024;   // [S]
-  float* cs = s.aux + 2048;   // [S]
-  for (int q = threadIdx.x; q < S; q += NT) {
-    ms[q] = base[(size_t)q * PS + D];
-    ls[q] = base[(size_t)q * PS + D + 1];
+__device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
+  const KArgs& a = c.a;
+  Smem& s = c.s;
+  const int l = t.layer, b = t.a0, h = t.a1, d0 = t.a2, nd = t.a3, S = t.aux, D = a.D;
+  const int HG = a.HG, g = h / HG, hh = h % HG, PS = D + 2;
+  const uint64_t* base = a.part + (size_t)l * a.s_part + ((size_t)b * a.Hkv + g) * a.S_max * HG * PS +
+                         (size_t)hh * PS;
+  const size_t sstride = (size_t)HG * PS;
+  // every split's dims d0 .. d0+nd, max and sum in one batch: word i of split
+  // q = i / (nd + 2), j = i % (nd + 2) -> att[i] (j < nd: value, nd: max, nd+1: sum)
+  const int W = nd + 2, n = S * W;
+  float* sw = s.att;
+  if (a.trace && tid() == 0) s.tw[2] = now();
+  bool ok = true;
+  for (int bs = 0; bs < n && ok; bs += 4 * NT) {
+    const int t = tid();
+    float v[4];
+    ok = read_words<4>(a, [&](int k) -> const uint64_t* {
+      const int i = bs + t + k * NT;
+      if (i >= n) return nullptr;
+      const int q = i / W, j = i - q * W;
+      return base + q * sstride + (j < nd ? d0 + j : D + (j - nd));
+    }, v, c.t0, c.ti);
+    if (ok) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = bs + t + k * NT;
+        if (i < n) sw[i] = v[k];
+      }
+    }
+  }
+  if (!ok) s.fail = 1;
+  __syncthreads();
+  if (a.trace && tid() == 0) s.tw[3] = now();
+  if (s.fail) return false;
+  float* cs = s.out;  // [S] merge weights
+  if (tid() < 64) {
+    const int lane = tid();
+    float M = NEG_INF;
+    for (int q = lane; q < S; q += 64) M = fmaxf(M, sw[q * W + nd]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int q = lane; q < S; q += 64) {
+      const float mq = sw[q * W + nd];
+      L += mq == NEG_INF ? 0.f : expf(mq - M) * sw[q * W + nd + 1];
+    }
+    L = wave_sum(L);
+    for (int q = lane; q < S; q += 64) {
+      const float mq = sw[q * W + nd];
+      cs[q] = (mq == NEG_INF || L == 0.f) ? 0.f : expf(mq - M) / L;
+    }
   }
   __syncthreads();
-  float M = NEG_INF;
-  for (int q = 0; q < S; ++q) M = fmaxf(M, ms[q]);
-  float L = 0.f;
-  for (int q = 0; q < S; ++q) L += ms[q] == NEG_INF ? 0.f : expf(ms[q] - M) * ls[q];
-  for (int q = threadIdx.x; q < S; q += NT)
-    cs[q] = (ms[q] == NEG_INF || L == 0.f) ? 0.f : expf(ms[q] - M) / L;
-  __syncthreads();
-  const int G = NT / D, sg = threadIdx.x / D, dim = threadIdx.x % D;
+  const int NG = NT / nd, sg = tid() / nd, dim = tid() % nd;
   float acc = 0.f;
-  for (int q = sg; q < S; q += G) acc += cs[q] * base[(size_t)q * PS + dim];
-  s.main[sg * D + dim] = acc;
+  if (sg < NG)
+    for (int q = sg; q < S; q += NG) acc += cs[q] * sw[q * W + dim];
+  float* red = s.out + 1024;
+  if (sg < NG) red[sg * nd + dim] = acc;
   __syncthreads();
-  if (threadIdx.x < D) {
+  if (tid() < nd) {
     float o = 0.f;
-    for (int q = 0; q < G; ++q) o += s.main[q * D + threadIdx.x];
-    a.o[(size_t)l * a.s_o + (size_t)b * a.Hq * D + (size_t)h * D + threadIdx.x] = o;
+    for (int q = 0; q < NG; ++q) o += red[q * nd + tid()];
+    st_tagged(a.o + (size_t)l * a.s_o + ((size_t)b * a.Hq + h) * D + d0 + tid(), o, a.epoch);
   }
   return true;
 }
 
 template <int CPL>
-__device__ __forceinline__ bool task_o(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  constexpr int NR = CPL == 1 ? 8 : (CPL == 2 ? 4 : (CPL == 3 ? 3 : 2));
+__device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
+  constexpr int RPW = 24 / CPL < GEMV_RPW_MAX ? 24 / CPL : GEMV_RPW_MAX;
+  const KArgs& a = c.a;
   const int l = t.layer, r0 = t.a1, n = t.a2;
   const int H = a.H, K = a.Hq * a.D;
-  const int TC = task_tc(t);
   const uint16_t* W = a.wo + (size_t)l * H * K;
-  auto rowptr = [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * K); };
-  float u[CPL * 8];
-  auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
-    load_slice<CPL>(a, a.o + (size_t)l * a.s_o, nullptr, nullptr, K, TC, u, s.aux);
-    return true;
-  };
-  if (!gemv_block<CPL, NR>(n, TC, rowptr, ready, s.main, u)) return false;
-  const float* xf;
-  const uint16_t* xb;
-  layer_input(a, l, &xf, &xb);
-  for (int j = threadIdx.x; j < n; j += NT) {
-    const float x = xf ? xf[r0 + j] : bf2f(xb[r0 + j]);
-    a.xa[(size_t)l * a.s_x + r0 + j] = x + job_sum(s.main, n, TC, j);
+  Tile<CPL, RPW> tile;
+  tile.issue(n, (K / 8) / CPL, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * K); });
+  // residual rows (layer input, complete once o is): loaded ahead of the wait
+  const int th = tid();
+  uint64_t rw = 0;
+  if (th < n) {
+    if (l == 0) rw = tag_word(bf2f(a.embed[(size_t)token_row(a, 0) * a.H + r0 + th]), a.epoch);
+    else rw = ld_tagged(a.x + (size_t)(l - 1) * a.s_x + r0 + th);
   }
-  return true;
+  if (!gather<8>(c, a.o + (size_t)l * a.s_o, K, c.s.vec, 1)) return false;
+  tile.dots(c.s.vec, c.s.out);
+  __syncthreads();
+  bool fail = false;
+  if (th < n) {
+    const float x = tag_is(rw, a.epoch) ? tag_value(rw) : resid(c, l, 0, r0 + th, &fail);
+    st_tagged(a.xa + (size_t)l * a.s_x + r0 + th, x + c.s.out[th], a.epoch);
+  }
+  for (int j = th + NT; j < n; j += NT) {
+    const float x = resid(c, l, 0, r0 + j, &fail);
+    st_tagged(a.xa + (size_t)l * a.s_x + r0 + j, x + c.s.out[j], a.epoch);
+  }
+  return !fail;
 }
 
 template <int CPL>
-__device__ __forceinline__ bool task_router(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  constexpr int NR = CPL == 1 ? 8 : (CPL == 2 ? 4 : (CPL == 3 ? 3 : 2));
+__device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
+  constexpr int RPW = 24 / CPL < GEMV_RPW_MAX ? 24 / CPL : GEMV_RPW_MAX;
+  const KArgs& a = c.a;
   const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H;
-  const int TC = task_tc(t);
   const uint16_t* W = a.router + (size_t)l * a.E * H;
-  auto rowptr = [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); };
-  float u[CPL * 8];
-  auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
-    load_slice<CPL>(a, a.xa + (size_t)l * a.s_x, nullptr, a.ffn_norm + (size_t)l * H, H, TC, u, s.aux);
-    return true;
-  };
-  if (!gemv_block<CPL, NR>(n, TC, rowptr, ready, s.main, u)) return false;
-  for (int j = threadIdx.x; j < n; j += NT)
-    a.rlog[(size_t)l * a.s_rlog + r0 + j] = job_sum(s.main, n, TC, j);
+  Tile<CPL, RPW> tile;
+  tile.issue(n, (H / 8) / CPL, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
+  if (!gather<4>(c, a.xa + (size_t)l * a.s_x, H, c.s.vec, 1)) return false;
+  rmsnorm_lds(c, c.s.vec, H, a.ffn_norm + (size_t)l * H);
+  tile.dots(c.s.vec, c.s.out);
+  __syncthreads();
+  for (int j = tid(); j < n; j += NT)
+    st_tagged(a.rlog + (size_t)l * a.s_rlog + r0 + j, c.s.out[j], a.epoch);
   return true;
 }
 
-template <int CPL>
-__device__ __forceinline__ bool task_gateup(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  constexpr int NR = CPL == 1 ? 8 : (CPL == 2 ? 4 : (CPL == 3 ? 3 : 2));
-  const int l = t.layer, slot = t.aux, f0 = t.a1, n = t.a2, nj = 2 * n;
-  const int H = a.H, F = a.F, EE = a.dense ? 1 : a.E;
-  const int TC = task_tc(t);
-  int e = 0;
+// Expert task: route (every expert task computes the same top-k), stream the
+// gate/up rows of its slot's expert into registers, SwiGLU them against the
+// normalised hidden state and publish the activations; meanwhile the rows of
+// the down projection stream into LDS; then read every slot's activations and
+// finish its hidden rows: x = x_attn + sum_j w_j * W_down[e_j] a_j (fixed j
+// order). Dense FFN: one slot, expert 0, weight 1.
+template <int CH, int CF>
+__device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
+  constexpr int RPW_G = 24 / CH < GEMV_RPW_MAX ? 24 / CH : GEMV_RPW_MAX;
+  constexpr int RPW_D = STAGE_CHUNKS / CF < GEMV_RPW_MAX ? STAGE_CHUNKS / CF : GEMV_RPW_MAX;
+  const KArgs& a = c.a;
+  Smem& s = c.s;
+  const int l = t.layer, b = t.a0, slot = t.aux, f0 = t.a1, nf = t.a2;
+  const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
+  const int H = a.H, F = a.F, KK = a.dense ? 1 : a.K, EE = a.dense ? 1 : a.E;
+  const int TCH = (H / 8) / CH, TCF = (F / 8) / CF;
   if (!a.dense) {
-    if (!wg_wait(a, t.wait_a, t.cnt_a, ti, &s.flag, s.tw)) return false;
-    route(a, l, s);
-    e = s.route_ids[slot];
-    if ((t.flags & TF_WRITE_TOPK) && threadIdx.x < a.K) {
-      if (a.topk_ids) a.topk_ids[(size_t)l * a.K + threadIdx.x] = s.route_ids[threadIdx.x];
-      if (a.topk_w) a.topk_w[(size_t)l * a.K + threadIdx.x] = s.route_w[threadIdx.x];
+    if (!routing(c, l, b)) return false;
+    if ((t.flags & TF_WRITE_TOPK) && tid() < a.K) {
+      if (a.topk_ids) a.topk_ids[(size_t)l * a.K + tid()] = s.route_ids[tid()];
+      if (a.topk_w) a.topk_w[(size_t)l * a.K + tid()] = s.route_w[tid()];
     }
+  } else {
+    if (tid() == 0) {
+      s.route_ids[0] = 0;
+      s.route_w[0] = 1.f;
+    }
+    __syncthreads();
   }
+  const int e = s.route_ids[slot];
   const uint16_t* Wg = a.gate + ((size_t)l * EE + e) * F * H;
   const uint16_t* Wu = a.up + ((size_t)l * EE + e) * F * H;
-  auto rowptr = [&](int j) {
-    return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + (j >> 1)) * H);
-  };
-  float u[CPL * 8];
-  auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
-    load_slice<CPL>(a, a.xa + (size_t)l * a.s_x, nullptr, a.ffn_norm + (size_t)l * H, H, TC, u, s.aux);
-    return true;
-  };
-  if (!gemv_block<CPL, NR>(nj, TC, rowptr, ready, s.main, u)) return false;
-  float* act = a.act + (size_t)l * a.s_act + (size_t)slot * F;
-  for (int q = threadIdx.x; q < n; q += NT) {
-    const float yg = job_sum(s.main, nj, TC, 2 * q), yu = job_sum(s.main, nj, TC, 2 * q + 1);
-    act[f0 + q] = yg / (1.0f + expf(-yg)) * yu;
-  }
-  return true;
-}
-
-template <int CPL>
-__device__ __forceinline__ bool task_down(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  constexpr int NR = CPL == 1 ? 8 : (CPL == 2 ? 4 : (CPL == 3 ? 3 : 2));
-  const int l = t.layer, r0 = t.a1, n = t.a2;
-  const int H = a.H, F = a.F, KK = a.dense ? 1 : a.K, EE = a.dense ? 1 : a.E;
-  const int nj = n * KK;
-  const int TC = task_tc(t);
-  if (!a.dense) {
-    if (!wg_wait(a, t.wait_a, t.cnt_a, ti, &s.flag, s.tw)) return false;
-    route(a, l, s);
-  } else if (threadIdx.x == 0) {
-    s.route_ids[0] = 0;
-    s.route_w[0] = 1.f;
-  }
-  if (a.dense) __syncthreads();
   const uint16_t* Wd = a.down + (size_t)l * EE * H * F;
-  auto rowptr = [&](int j) {
-    const int e = s.route_ids[j % KK];
-    return (const uint4*)(Wd + ((size_t)e * H + r0 + j / KK) * F);
-  };
-  const int my_slot = (threadIdx.x / TC) % KK;  // NT/TC is a multiple of KK
-  float u[CPL * 8];
-  auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
-    load_slice<CPL>(a, a.act + (size_t)l * a.s_act + (size_t)my_slot * F, nullptr, nullptr, F, TC,
-                    u, s.aux);
-    return true;
-  };
-  if (!gemv_block<CPL, NR>(nj, TC, rowptr, ready, s.main, u)) return false;
-  for (int q = threadIdx.x; q < n; q += NT) {
-    float y = 0.f;
-    for (int j = 0; j < KK; ++j) y += s.route_w[j] * job_sum(s.main, nj, TC, q * KK + j);
-    a.xf[(size_t)l * a.s_x + r0 + q] = a.xa[(size_t)l * a.s_x + r0 + q] + y;
+  const uint64_t* xa = a.xa + (size_t)l * a.s_x + (size_t)b * H;
+  // gate/up part, in register tiles of capg FFN rows (one tile in the usual plan)
+  const int capg = (NT / TCH) * RPW_G / 2;
+  bool have_x = false;
+  for (int fc = 0; fc < nf; fc += capg) {
+    const int nfc = min(capg, nf - fc);
+    Tile<CH, RPW_G> gu;
+    gu.issue(2 * nfc, TCH, [&](int j) {
+      return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + fc + (j >> 1)) * H);
+    });
+    if (!have_x) {
+      if (!gather<4>(c, xa, H, s.vec, 1)) return false;
+      for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
+      rmsnorm_lds(c, s.vec, H, a.ffn_norm + (size_t)l * H);
+      have_x = true;
+    }
+    gu.dots(s.vec, s.out);
+    __syncthreads();
+    uint64_t* act = a.act + (size_t)l * a.s_act + ((size_t)b * KK + slot) * F + f0 + fc;
+    for (int q = tid(); q < nfc; q += NT) {
+      const float yg = s.out[2 * q], yu = s.out[2 * q + 1];
+      st_tagged(act + q, yg / (1.0f + expf(-yg)) * yu, a.epoch);
+    }
+    __syncthreads();
+  }
+  if (nr == 0) return true;
+  if (!have_x) {
+    if (!gather<4>(c, xa, H, s.vec, 1)) return false;
+    for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
+    __syncthreads();
+  }
+  // down part: job j = (hidden row j / KK, slot j % KK); a lane group's slot
+  // is fixed because the number of lane groups is a multiple of KK
+  const int capd = (NT / TCF) * RPW_D / KK;
+  for (int rc = 0; rc < nr; rc += capd) {
+    const int nrc = min(capd, nr - rc);
+    StageTile<CF, RPW_D> dn;
+    dn.issue(nrc * KK, TCF, [&](int j) {
+      return (const uint4*)(Wd + ((size_t)s.route_ids[j % KK] * H + r0 + rc + j / KK) * F);
+    }, s.stage);
+    if (rc == 0 && !gather<12>(c, a.act + (size_t)l * a.s_act + (size_t)b * KK * F, KK * F, s.vec, 1))
+      return false;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct-to-LDS loads
+    dn.dots(s.stage, s.vec + (size_t)(dn.lg % KK) * F, s.out);
+    __syncthreads();
+    for (int q = tid(); q < nrc; q += NT) {
+      float y = 0.f;
+      for (int j = 0; j < KK; ++j) y += s.route_w[j] * s.out[q * KK + j];
+      st_tagged(a.x + (size_t)l * a.s_x + (size_t)b * H + r0 + rc + q, s.res[rc + q] + y, a.epoch);
+    }
+    __syncthreads();
   }
   return true;
 }
 
+// LM head tile: rows stream through registers in double-buffered batches of
+// LM_BATCH rows per lane group; every lane group walks the same number of
+// batches (rows past the tile's end re-read its last row and are ignored), so
+// the loop issues its loads unconditionally.
 template <int CPL>
-__device__ __forceinline__ bool task_lm(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  constexpr int NR = CPL == 1 ? 8 : (CPL == 2 ? 4 : (CPL == 3 ? 3 : 2));
+__device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
+  const KArgs& a = c.a;
+  Smem& s = c.s;
   const int r0 = t.a1, n = t.a2, H = a.H;
-  const int TC = task_tc(t);
-  auto rowptr = [&](int j) { return (const uint4*)(a.lm + (size_t)(r0 + j) * H); };
-  float u[CPL * 8];
-  auto ready = [&]() -> bool {
-    if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
-    load_slice<CPL>(a, a.xf + (size_t)(a.L - 1) * a.s_x, nullptr, a.final_norm, H, TC, u, s.aux);
-    return true;
+  const int TC = (H / 8) / CPL, G = NT / TC;
+  const int lg = tid() / TC, tc = tid() % TC;
+  const int per = (n + G - 1) / G;                       // rows per lane group
+  int nb = (per + LM_BATCH - 1) / LM_BATCH;
+  nb = nb < 2 ? 2 : nb + (nb & 1);                       // even, >= 2
+  uint4 A[LM_BATCH][CPL], Bf[LM_BATCH][CPL];
+  auto row_of = [&](int bi, int r) { return min(lg + (bi * LM_BATCH + r) * G, n - 1); };
+  auto issue = [&](uint4 (&w)[LM_BATCH][CPL], int bi) {
+#pragma unroll
+    for (int r = 0; r < LM_BATCH; ++r) {
+      const uint4* p = (const uint4*)(a.lm + (size_t)(r0 + row_of(bi, r)) * H);
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) w[r][cc] = ld_nt(p + tc + cc * TC);
+    }
   };
-  if (!gemv_block<CPL, NR>(n, TC, rowptr, ready, s.main, u)) return false;
+  float uu[CPL * 8];
+  auto consume = [&](uint4 (&w)[LM_BATCH][CPL], int bi) {
+#pragma unroll
+    for (int r = 0; r < LM_BATCH; ++r) {
+      float sum = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) sum = dot8(w[r][cc], uu + cc * 8, sum);
+      sum = group_sum(sum, TC);
+      if (tc == 0) s.out[row_of(bi, r)] = sum;
+    }
+  };
+  issue(A, 0);
+  issue(Bf, 1);
+  if (!gather<4>(c, a.x + (size_t)(a.L - 1) * a.s_x, H, s.vec, 1)) return false;
+  rmsnorm_lds(c, s.vec, H, a.final_norm);
+#pragma unroll
+  for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) uu[cc * 8 + e] = s.vec[(tc + cc * TC) * 8 + e];
+  for (int bi = 0; bi + 2 < nb; bi += 2) {
+    consume(A, bi);
+    issue(A, bi + 2);
+    consume(Bf, bi + 1);
+    issue(Bf, bi + 3);
+  }
+  consume(A, nb - 2);
+  consume(Bf, nb - 1);
+  __syncthreads();
   float bv = NEG_INF;
   int bi = 0x7fffffff;
-  for (int j = threadIdx.x; j < n; j += NT) {
-    const float y = job_sum(s.main, n, TC, j);
+  for (int j = tid(); j < n; j += NT) {
+    const float y = s.out[j];
     if (a.logits) a.logits[r0 + j] = y;
     if (y > bv) { bv = y; bi = r0 + j; }
   }
@@ -651,27 +846,29 @@ __device__ __forceinline__ bool task_lm(const KArgs& a, const Task& t, uint32_t 
     const int oi = __shfl_xor(bi, o, 64);
     if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
   }
-  float* rv = s.aux;
-  int* ri = (int*)(s.aux + NWAVE);
-  if ((threadIdx.x & 63) == 0) { rv[threadIdx.x >> 6] = bv; ri[threadIdx.x >> 6] = bi; }
+  float* rv = s.red;
+  int* ri = (int*)(s.red + NWAVE);
+  if ((tid() & 63) == 0) { rv[tid() >> 6] = bv; ri[tid() >> 6] = bi; }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     for (int q = 1; q < NWAVE; ++q)
       if (rv[q] > bv || (rv[q] == bv && ri[q] < bi)) { bv = rv[q]; bi = ri[q]; }
-    // the wave-0 value of bv/bi is already folded in (lane 0 holds the wave result)
-    a.lmpart[(size_t)t.a3 * 2] = __float_as_uint(bv);
-    a.lmpart[(size_t)t.a3 * 2 + 1] = (uint32_t)bi;
+    st_tagged(a.lmpart + (size_t)t.a3 * 2, bv, a.epoch);
+    st_tagged(a.lmpart + (size_t)t.a3 * 2 + 1, __int_as_float(bi), a.epoch);
   }
   return true;
 }
 
-__device__ __forceinline__ bool task_final(const KArgs& a, const Task& t, uint32_t ti, Smem& s) {
-  if (!wg_wait(a, t.wait_b, t.cnt_b, ti, &s.flag, s.tw + 2)) return false;
+__device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
+  const KArgs& a = c.a;
+  Smem& s = c.s;
+  const int n = t.a0;
+  if (!gather<2>(c, a.lmpart, 2 * n, s.vec, 1)) return false;
   float bv = NEG_INF;
   int bi = 0x7fffffff;
-  for (int q = threadIdx.x; q < t.a0; q += NT) {
-    const float v = __uint_as_float(a.lmpart[(size_t)q * 2]);
-    const int i = (int)a.lmpart[(size_t)q * 2 + 1];
+  for (int q = tid(); q < n; q += NT) {
+    const float v = s.vec[2 * q];
+    const int i = __float_as_int(s.vec[2 * q + 1]);
     if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
   }
 #pragma unroll
@@ -680,11 +877,11 @@ __device__ __forceinline__ bool task_final(const KArgs& a, const Task& t, uint32
     const int oi = __shfl_xor(bi, o, 64);
     if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
   }
-  float* rv = s.aux;
-  int* ri = (int*)(s.aux + NWAVE);
-  if ((threadIdx.x & 63) == 0) { rv[threadIdx.x >> 6] = bv; ri[threadIdx.x >> 6] = bi; }
+  float* rv = s.red;
+  int* ri = (int*)(s.red + NWAVE);
+  if ((tid() & 63) == 0) { rv[tid() >> 6] = bv; ri[tid() >> 6] = bi; }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     for (int q = 1; q < NWAVE; ++q)
       if (rv[q] > bv || (rv[q] == bv && ri[q] < bi)) { bv = rv[q]; bi = ri[q]; }
     a.tok_out[0] = bi;
@@ -693,54 +890,61 @@ __device__ __forceinline__ bool task_final(const KArgs& a, const Task& t, uint32
   return true;
 }
 
-#define MK_CPL_DISPATCH(fn, K)                                  \
-  [&]() -> bool {                                               \
-    switch ((K) / (8 * task_tc(t))) {                           \
-      case 1: return fn<1>(a, t, ti, s);                        \
-      case 2: return fn<2>(a, t, ti, s);                        \
-      case 3: return fn<3>(a, t, ti, s);                        \
-      default: return fn<4>(a, t, ti, s);                       \
-    }                                                           \
-  }()
-
+// One kernel per shape class: CH, CO, CF are the 16-byte chunks per lane of
+// the GEMVs over the hidden size, the attention output (query heads x head
+// dim) and the FFN width; HD is the head dim. Each variant contains only the
+// task bodies its shapes use, so registers are allocated for them alone.
+template <int CH, int CO, int CF, int HD>
 __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
   __shared__ Smem s;
   const uint32_t* hdr = a.plan;
   const uint32_t* off = hdr + PLAN_HDR_WORDS;
   const Task* tasks = (const Task*)((const char*)a.plan + hdr[H_TASK_OFF_BYTES]);
   const uint32_t beg = off[blockIdx.x], end = off[blockIdx.x + 1];
+  if (tid() == 0) s.fail = 0;
+  __syncthreads();
   for (uint32_t ti = beg; ti < end; ++ti) {
     const Task t = tasks[ti];
-    uint64_t t_start = 0;
-    if (a.trace && threadIdx.x == 0) {
-      t_start = __builtin_amdgcn_s_memrealtime();
-      s.tw[0] = s.tw[1] = s.tw[2] = s.tw[3] = 0;
-    }
+    Ctx c{a, s, now(), ti};
+    if (a.trace && tid() == 0) s.tw[0] = s.tw[1] = s.tw[2] = s.tw[3] = 0;
     bool ok = true;
     switch (t.op) {
-      case OP_QKV: ok = MK_CPL_DISPATCH(task_qkv, a.H); break;
-      case OP_ATTN: ok = a.D == 128 ? task_attn<128>(a, t, ti, s) : task_attn<64>(a, t, ti, s); break;
-      case OP_COMB: ok = task_comb(a, t, ti, s); break;
-      case OP_O: ok = MK_CPL_DISPATCH(task_o, a.Hq * a.D); break;
-      case OP_ROUTER: ok = MK_CPL_DISPATCH(task_router, a.H); break;
-      case OP_GATEUP: ok = MK_CPL_DISPATCH(task_gateup, a.H); break;
-      case OP_DOWN: ok = MK_CPL_DISPATCH(task_down, a.F); break;
-      case OP_LM: ok = MK_CPL_DISPATCH(task_lm, a.H); break;
-      case OP_FINAL: ok = task_final(a, t, ti, s); break;
+      case OP_QKV: ok = task_qkv<CH>(c, t); break;
+      case OP_ATTN: ok = task_attn<HD>(c, t); break;
+      case OP_COMB: ok = task_comb(c, t); break;
+      case OP_O: ok = task_o<CO>(c, t); break;
+      case OP_ROUTER: ok = task_router<CH>(c, t); break;
+      case OP_EXPERT: ok = task_expert<CH, CF>(c, t); break;
+      case OP_LM: ok = task_lm<CH>(c, t); break;
+      case OP_FINAL: ok = task_final(c, t); break;
       default: break;
     }
-    if (!ok) return;
-    uint64_t t_body = 0;
-    if (a.trace && threadIdx.x == 0) t_body = __builtin_amdgcn_s_memrealtime();
-    wg_signal(a, t.signal);
-    if (a.trace && threadIdx.x == 0) {
-      uint64_t* tr = a.trace + (size_t)ti * TRACE_WORDS;
-      tr[0] = t_start;
-      tr[1] = s.tw[0]; tr[2] = s.tw[1]; tr[3] = s.tw[2]; tr[4] = s.tw[3];
-      tr[5] = t_body;
-      tr[6] = __builtin_amdgcn_s_memrealtime();
-      tr[7] = ((uint64_t)blockIdx.x << 32) | ((uint64_t)t.op << 16) | t.layer;
+    if (!ok) return;  // uniform: the failure was recorded in the status words
+    const uint64_t t_body = (a.trace && tid() == 0) ? now() : 0;
+    __syncthreads();  // LDS is reused by the next task
+    if (tid() == 0) {
+      if (t.signal != NO_CTR)
+        __hip_atomic_fetch_add(a.ctr + ((size_t)t.signal * CTR_LINES + blockIdx.x % CTR_LINES) * CTR_STRIDE,
+                               1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.trace) {
+        uint64_t* tr = a.trace + (size_t)ti * TRACE_WORDS;
+        tr[0] = c.t0;
+        tr[1] = s.tw[0]; tr[2] = s.tw[1]; tr[3] = s.tw[2]; tr[4] = s.tw[3];
+        tr[5] = t_body;
+        tr[6] = now();
+        tr[7] = ((uint64_t)blockIdx.x << 32) | ((uint64_t)t.op << 16) | t.layer;
+      }
     }
+  }
+}
+
+// Kernel variants, indexed by mk::kernel_class (see mk_internal.hpp).
+const void* kernel_for(int cls) {
+  switch (cls) {
+    case 0: return (const void*)megakernel<1, 1, 1, 64>;    // hidden 256, 4x64 heads, FFN 512
+    case 1: return (const void*)megakernel<2, 2, 1, 64>;    // hidden 1024, 16x64 heads, FFN 512
+    case 2: return (const void*)megakernel<4, 8, 3, 128>;   // hidden 2048, 32x128 heads, FFN 768
+    default: return nullptr;
   }
 }
 
@@ -783,11 +987,11 @@ extern "C" mk_status mk_step_status(const uint32_t* h) {
   switch (h[0]) {
     case mk::DS_OK: return MK_OK;
     case mk::DS_TIMEOUT:
-      return fail(MK_ETIMEOUT, "device wait timed out: task " + std::to_string(h[1]) + " counter " +
-                                   std::to_string(h[2]) + " value " + std::to_string(h[3]));
+      return fail(MK_ETIMEOUT, "device wait timed out: task " + std::to_string(h[1]) + " buffer word " +
+                                   std::to_string(h[2]) + " tag seen " + std::to_string(h[3]));
     case mk::DS_BOUNDS:
       return fail(MK_EBOUNDS, "device bounds check failed: task " + std::to_string(h[1]) +
-                                  " (position or page outside the plan/pool)");
+                                  " (token, position or page outside the plan/pool)");
     default:
       return fail(MK_EDEVICE, "unknown device status " + std::to_string(h[0]));
   }
@@ -810,10 +1014,9 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
   if (!io->tokens_in || !io->tokens_out) return fail(MK_EINVAL, "mk_decode_step: missing token buffers");
   if (!bu->plan || bu->plan_bytes < p->image.size() || !bu->workspace ||
       bu->workspace_bytes < p->ws_total || !bu->counters ||
-      bu->counter_bytes < p->targets.size() * mk::CTR_STRIDE * 4 || !bu->status)
+      bu->counter_bytes < p->targets.size() * mk::CTR_LINES * mk::CTR_STRIDE * 4 || !bu->status)
     return fail(MK_EINVAL, "mk_decode_step: step buffers missing or too small");
-  if (epoch == 0 || (uint64_t)epoch * 65535ull >= (1ull << 32))
-    return fail(MK_EBOUNDS, "mk_decode_step: epoch outside [1, 65536)");
+  if (epoch == 0) return fail(MK_EINVAL, "mk_decode_step: epoch must be >= 1");
 
   mk::KArgs a;
   std::memset(&a, 0, sizeof a);
@@ -834,13 +1037,14 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
   a.tok_in = io->tokens_in; a.tok_out = io->tokens_out; a.topk_ids = io->topk_ids;
   a.topk_w = io->topk_w; a.logits = io->logits;
   char* ws = (char*)bu->workspace;
-  a.xa = (float*)(ws + p->ws_off[MK_BUF_XATTN]); a.xf = (float*)(ws + p->ws_off[MK_BUF_XFFN]);
-  a.q = (float*)(ws + p->ws_off[MK_BUF_Q]); a.part = (float*)(ws + p->ws_off[MK_BUF_PART]);
-  a.o = (float*)(ws + p->ws_off[MK_BUF_O]); a.rlog = (float*)(ws + p->ws_off[MK_BUF_RLOG]);
-  a.act = (float*)(ws + p->ws_off[MK_BUF_ACT]); a.lmpart = (uint32_t*)(ws + p->ws_off[MK_BUF_LMPART]);
-  a.s_x = (int64_t)(p->ws_stride[MK_BUF_XATTN] / 4); a.s_q = (int64_t)(p->ws_stride[MK_BUF_Q] / 4);
-  a.s_part = (int64_t)(p->ws_stride[MK_BUF_PART] / 4); a.s_o = (int64_t)(p->ws_stride[MK_BUF_O] / 4);
-  a.s_rlog = (int64_t)(p->ws_stride[MK_BUF_RLOG] / 4); a.s_act = (int64_t)(p->ws_stride[MK_BUF_ACT] / 4);
+  auto buf = [&](int which) { return (uint64_t*)(ws + p->ws_off[which]); };
+  auto words = [&](int which) { return (int64_t)(p->ws_stride[which] / 8); };
+  a.x = buf(MK_BUF_XFFN); a.xa = buf(MK_BUF_XATTN); a.q = buf(MK_BUF_Q); a.kvn = buf(MK_BUF_KVN);
+  a.part = buf(MK_BUF_PART); a.o = buf(MK_BUF_O); a.rlog = buf(MK_BUF_RLOG); a.act = buf(MK_BUF_ACT);
+  a.lmpart = buf(MK_BUF_LMPART);
+  a.s_x = words(MK_BUF_XFFN); a.s_q = words(MK_BUF_Q); a.s_kvn = words(MK_BUF_KVN);
+  a.s_part = words(MK_BUF_PART); a.s_o = words(MK_BUF_O); a.s_rlog = words(MK_BUF_RLOG);
+  a.s_act = words(MK_BUF_ACT);
   a.S_max = p->S_max; a.n_lm = p->n_lm;
   a.plan = (const uint32_t*)bu->plan; a.ctr = bu->counters; a.status = bu->status; a.epoch = epoch;
   a.timeout_ticks = (uint64_t)(timeout_ms ? timeout_ms : 2000) * 100000ull;
@@ -850,9 +1054,11 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
     a.trace = bu->trace;
   }
 
+  const void* kern = mk::dev::kernel_for(p->kernel_class);
+  if (!kern) return fail(MK_EUNSUPPORTED, "mk_decode_step: no kernel variant for this model shape");
   void* args[] = {&a};
-  hipError_t e = hipLaunchCooperativeKernel((const void*)mk::dev::megakernel, dim3(p->n_cu),
-                                            dim3(mk::NT), args, 0, (hipStream_t)stream);
+  hipError_t e = hipLaunchCooperativeKernel(kern, dim3(p->n_cu), dim3(mk::NT), args, 0,
+                                            (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel(megakernel)");
   return MK_OK;
 }

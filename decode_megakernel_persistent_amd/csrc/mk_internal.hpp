@@ -1,7 +1,8 @@
 // Internal formats shared by the host planner and the device megakernel:
-// the 32-byte task record, the plan image in device memory and the kernel
-// argument block. Not part of the public ABI (include/mk.h), except that the
-// task record layout is documented for mk_plan_export consumers.
+// the 32-byte task record, the plan image in device memory, the tagged
+// activation word and the kernel argument block. Not part of the public ABI
+// (include/mk.h), except that the task record layout is documented for
+// mk_plan_export consumers.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -20,28 +21,32 @@ enum Op : uint8_t {
   OP_NONE = 0,
   OP_QKV = 1,     // a0 = kv group g, a1 = first rotary pair, a2 = pairs
   OP_ATTN = 2,    // a0 = b, a1 = g, a2 = first page, a3 = pages; aux = split index
-  OP_COMB = 3,    // a0 = b, a1 = q head, a2 = heads (1), a3 = splits of (b, g)
+  OP_COMB = 3,    // a0 = b, a1 = query head, a2 = first dim, a3 = dims; aux = splits of (b, g)
   OP_O = 4,       // a1 = first row, a2 = rows
   OP_ROUTER = 5,  // a1 = first expert row, a2 = rows
-  OP_GATEUP = 6,  // a0 = b (MoE) or -1 (dense, all rows), aux = slot j, a1 = first row, a2 = rows
-  OP_DOWN = 7,    // a1 = first row, a2 = rows
+  OP_EXPERT = 6,  // gate/up part: a0 = b, aux = expert slot j, a1 = first FFN row, a2 = FFN
+                  // rows (may be 0); down part: a3 = first hidden row << 16 | hidden rows
+                  // (may be 0), over every slot of sequence 0
+                  // (7 is unused)
   OP_LM = 8,      // a1 = first row, a2 = rows, a3 = index of this LM tile
   OP_FINAL = 9,   // a0 = LM tiles
   OP_COUNT = 10
 };
 
-// flags: bit 0 TF_WRITE_TOPK; bits 4-7 log2 of the GEMV threads per row (TC).
 enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1 };
 
 constexpr uint16_t NO_CTR = 0xFFFF;
 
+// wait_a / wait_b name the producer classes a task depends on (wait_a: the
+// routing decision, wait_b: the data) with their per-step producer counts;
+// signal is the completion counter the task increments. The device waits on
+// the tagged data itself (see TaggedWord); the counters record completions.
 struct Task {
   uint8_t op, flags;
   uint16_t layer;
-  uint16_t wait_a, wait_b;  // counter indices (NO_CTR: none); wait_a gates address
-                            // computation (routing), wait_b gates the data
-  uint16_t cnt_a, cnt_b;    // per-epoch producer counts of wait_a / wait_b
-  uint16_t signal;          // counter incremented on completion (NO_CTR: none)
+  uint16_t wait_a, wait_b;
+  uint16_t cnt_a, cnt_b;
+  uint16_t signal;
   uint16_t aux;
   int32_t a0, a1, a2, a3;
 };
@@ -49,36 +54,58 @@ static_assert(sizeof(Task) == 32, "task record is 32 bytes");
 
 // Plan image: u32 header[PLAN_HDR_WORDS], u32 cu_off[n_cu + 1] (task index
 // ranges per list), padding to 32 B, Task tasks[n_tasks] (lists back to back).
-constexpr uint32_t PLAN_MAGIC = 0x31504B4Du;  // "MKP1"
+constexpr uint32_t PLAN_MAGIC = 0x32504B4Du;  // "MKP2"
 constexpr int PLAN_HDR_WORDS = 16;
 enum PlanHdr { H_MAGIC = 0, H_NCU = 1, H_NTASKS = 2, H_NCTR = 3, H_TASK_OFF_BYTES = 4,
                H_STAGES = 5 };
 
-constexpr int CTR_STRIDE = 16;  // u32 words between counters (one 64-byte line each)
+// Completion counters: counter c is CTR_LINES sub-counters, one 64-byte line
+// each; a task on compute unit cu increments sub-counter cu % CTR_LINES.
+constexpr int CTR_LINES = 8;
+constexpr int CTR_STRIDE = 16;  // u32 words per line
 constexpr int NT = 512;         // threads per workgroup (8 wave64)
 constexpr int NWAVE = NT / 64;
 
 // Per-task trace record (u64 words, constant 100 MHz clock): task start,
 // routing wait begin/end, data wait begin/end (0 where the task has no such
-// wait), body end, signal end, and (cu << 32 | op << 16 | layer).
+// wait), body end, task end, and (cu << 32 | op << 16 | layer).
 constexpr int TRACE_WORDS = 8;
 
 // Status words written by the device on failure.
 enum DevStatus : uint32_t { DS_OK = 0, DS_TIMEOUT = 1, DS_BOUNDS = 2 };
 
-// Thread mapping of a block GEMV over rows of K bf16 elements: each row is
-// read as K/8 16-byte chunks by TC threads (a power of two in [32, NT]),
-// CPL chunks per thread. Returns false when K has no such mapping.
+// Tagged word: every activation passed between tasks is a 64-bit word
+// (epoch << 32 | fp32 bits) written with one device-coherent store. A
+// consumer spins on the word until its tag equals the current step's epoch:
+// the tag is the word's own completion counter, so the value and its
+// readiness arrive in the same access. Buffers start zeroed and epochs start
+// at 1, so a stale word never carries the current tag.
+MK_HD inline uint64_t tag_word(float v, uint32_t epoch) {
+  union { float f; uint32_t u; } c;
+  c.f = v;
+  return ((uint64_t)epoch << 32) | c.u;
+}
+
+// GEMV mapping of a reduction width K (bf16 elements): a lane group of TC
+// lanes (64 or 32) covers a row as K/8 16-byte chunks, CPL chunks per lane.
 MK_HD inline bool gemv_map(int K, int* tc, int* cpl) {
   if (K <= 0 || K % 8) return false;
-  int chunks = K / 8;
-  for (int c = 1; c <= 4; ++c) {
-    if (chunks % c) continue;
-    int t = chunks / c;
-    if (t >= 32 && t <= NT && (t & (t - 1)) == 0) { *tc = t; *cpl = c; return true; }
-  }
-  return false;
+  const int chunks = K / 8;
+  int t = 0;
+  if (chunks % 64 == 0) t = 64;
+  else if (chunks % 32 == 0) t = 32;
+  else return false;
+  const int c = chunks / t;
+  if (!(c == 1 || c == 2 || c == 3 || c == 4 || c == 6 || c == 8)) return false;
+  *tc = t;
+  *cpl = c;
+  return true;
 }
+// Lane groups of a workgroup for lane-group width tc.
+MK_HD inline int gemv_groups(int tc) { return NWAVE * (64 / tc); }
+// Most 16-byte chunks a lane may hold for a prefetched GEMV tile.
+constexpr int GEMV_REG_CHUNKS = 24;
+constexpr int GEMV_RPW_MAX = 8;   // rows per lane group of a prefetched tile
 
 // Rows of W_qkv are taken by kv group and rotary pair: group g owns the q
 // rows of its HG query heads, then its k head, then its v head; pair p of the
@@ -96,8 +123,19 @@ MK_HD inline int qkv_pair(int p, int g, int HG, int D, int Hq, int Hkv, int* hea
   *head = g; *i = p; *row = (Hq + Hkv) * D + g * D + p; return 2;
 }
 
-// Floats of LDS available to one task's per-row partial sums.
-constexpr int GEMV_LDS_FLOATS = 8192;
+// Kernel variants: the megakernel is compiled once per shape class, given by
+// the 16-byte chunks per lane of the GEMVs over the hidden size (ch), the
+// attention output (co) and the FFN width (cf), and the head dim. Returns the
+// class index, or -1 when no variant is compiled for the shape.
+MK_HD inline int kernel_class(int ch, int co, int cf, int head_dim) {
+  if (ch == 1 && co == 1 && cf == 1 && head_dim == 64) return 0;
+  if (ch == 2 && co == 2 && cf == 1 && head_dim == 64) return 1;
+  if (ch == 4 && co == 8 && cf == 3 && head_dim == 128) return 2;
+  return -1;
+}
+
+// LM-head tiles stream their rows in batches of LM_BATCH rows per lane group.
+constexpr int LM_BATCH = 2;
 
 struct KArgs {
   // shape
@@ -120,10 +158,13 @@ struct KArgs {
   int32_t* topk_ids;
   float* topk_w;
   float* logits;
-  // workspace (fp32 unless noted) and per-layer strides in elements
-  float *xa, *xf, *q, *part, *o, *rlog, *act;
-  uint32_t* lmpart;  // [n_lm][B][2] (value bits, index)
-  int64_t s_x, s_q, s_part, s_o, s_rlog, s_act;
+  // tagged activation buffers and their per-layer strides (words):
+  //  x [L][B][H] layer outputs, xa [L][B][H] after attention, q [L][B][Hq][D],
+  //  kvn [L][B][Hkv][2][D] new K and V (bf16 bits), part [L][B][Hkv][S_max][HG][D+2]
+  //  split partials (o, m, l), o [L][B][Hq][D], rlog [L][B][E], act [L][B][K][F],
+  //  lmpart [n_lm][B][2] (value, index)
+  uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart;
+  int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act;
   int32_t S_max, n_lm;
   // plan and sync
   const uint32_t* plan;
@@ -131,7 +172,7 @@ struct KArgs {
   uint32_t* status;
   uint32_t epoch;
   uint64_t timeout_ticks;  // of the 100 MHz constant clock
-  uint64_t* trace;         // NULL, or TRACE_WORDS per task (see mk_step_buffers.trace)
+  uint64_t* trace;         // NULL, or TRACE_WORDS per task
 };
 
 }  // namespace mk

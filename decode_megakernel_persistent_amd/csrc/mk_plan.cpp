@@ -7,17 +7,21 @@
 // The decomposition follows the megakernel page ("What is a Megakernel?" and
 // the caption of Image 2): every operation of the step is cut into tiles, one
 // task per tile; the host deals the tasks round-robin over the compute units
-// so each unit gets its own list in device memory; counters express which
-// producers a task waits for. Stages, in order, per layer:
+// so each unit gets its own list in device memory; every task names the
+// producer classes it waits for and the completion counter it increments.
+// Stages, in order, per layer:
 //   QKV (per kv group: q, k, v rows of the group, rotary epilogue, KV append)
 //   ATTN (per sequence, kv group and page range: split-KV partials)
-//   COMB (per sequence and query head: log-sum-exp merge of the splits)
+//   COMB (per sequence, query head and dim range: log-sum-exp merge)
 //   O    (rows of W_o, residual)
 //   ROUTER (MoE: rows of W_router)
-//   GATEUP (MoE: per sequence, expert slot and row range; dense: row range)
-//   DOWN (rows of W_down, weighted combine over slots, residual)
+//   EXPERT (at most one per unit: a gate/up tile of one expert slot with
+//           SwiGLU, then a down tile of hidden rows over every slot with the
+//           weighted combine and residual; the down part reads the
+//           activations of every expert task of the layer)
 // then LM (rows of the LM head, local argmax) and FINAL (argmax merge).
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <map>
 #include <numeric>
@@ -61,12 +65,15 @@ Task mk_task(uint8_t op, int layer) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int rows_cap(int K, int B, int mult) {
+// Most rows one GEMV tile over reduction width K can hold in registers.
+int rows_max(int K) {
   int tc = 0, cpl = 0;
-  mk::gemv_map(K, &tc, &cpl);
-  int per = std::max(1, tc / 64) * std::max(1, B) * std::max(1, mult);
-  return std::max(1, mk::GEMV_LDS_FLOATS / per);
+  if (!mk::gemv_map(K, &tc, &cpl)) return 0;
+  int rpw = std::min(mk::GEMV_RPW_MAX, mk::GEMV_REG_CHUNKS / cpl);
+  return mk::gemv_groups(tc) * rpw;
 }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace
 
@@ -91,17 +98,35 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   for (int K : {H, Hq * D, F})
     if (!mk::gemv_map(K, &tc, &cpl))
       return fail(MK_EUNSUPPORTED, "mk_plan: reduction width " + std::to_string(K) +
-                                       " has no GEMV mapping (need a multiple of 256)");
+                                       " has no GEMV mapping (need K/8 a multiple of 32 with "
+                                       "K/8/lanes in {1,2,3,4,6,8})");
   {
     int tcf = 64, cplf = 1;
     mk::gemv_map(F, &tcf, &cplf);
     int kk = moe ? m->top_k : 1;
-    if ((mk::NT / tcf) % kk)
-      return fail(MK_EUNSUPPORTED, "mk_plan: down-projection mapping needs top_k to divide " +
-                                       std::to_string(mk::NT / tcf));
+    if (mk::gemv_groups(tcf) % kk)
+      return fail(MK_EUNSUPPORTED, "mk_plan: down-projection lane groups (" +
+                                       std::to_string(mk::gemv_groups(tcf)) + ") not a multiple of top_k");
+    if (rows_max(F) < kk)
+      return fail(MK_EUNSUPPORTED, "mk_plan: down-projection tile cannot hold top_k rows");
+  }
+  if ((size_t)H > 8192 || (size_t)Hq * D > 8192 || (size_t)(moe ? m->top_k : 1) * F > 8192)
+    return fail(MK_EUNSUPPORTED, "mk_plan: an input vector exceeds the 8192-float LDS staging area");
+  int kclass = -1;
+  {
+    int t1, ch, co, cf;
+    mk::gemv_map(H, &t1, &ch);
+    mk::gemv_map(Hq * D, &t1, &co);
+    mk::gemv_map(F, &t1, &cf);
+    kclass = mk::kernel_class(ch, co, cf, D);
+    if (kclass < 0)
+      return fail(MK_EUNSUPPORTED, "mk_plan: no compiled kernel variant for hidden " + std::to_string(H) +
+                                       ", heads x dim " + std::to_string(Hq * D) + ", FFN " +
+                                       std::to_string(F) + ", head dim " + std::to_string(D));
   }
   const int B = bd->batch;
   if (B != 1) return fail(MK_EUNSUPPORTED, "mk_plan: only batch 1 is implemented by the kernels");
+  if (m->page_tokens != 16) return fail(MK_EUNSUPPORTED, "mk_plan: page_tokens must be 16");
   if (!bd->seq_lens || !bd->page_table || bd->max_pages <= 0)
     return fail(MK_EINVAL, "mk_plan: seq_lens / page_table / max_pages missing");
   const int bound = bd->max_ctx_bound;
@@ -132,6 +157,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   p->n_cu = n_cu;
   p->seq_lens.assign(bd->seq_lens, bd->seq_lens + B);
   p->page_table.assign(bd->page_table, bd->page_table + (int64_t)B * bd->max_pages);
+  p->kernel_class = kclass;
   p->HG = Hq / Hkv;
   p->QKV_ROWS = (Hq + 2 * Hkv) * D;
   p->F = F;
@@ -144,13 +170,13 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     return (int32_t)p->targets.size() - 1;
   };
   for (int l = 0; l < L; ++l) {
-    for (int g = 0; g < Hkv; ++g) p->c_qkv.push_back(new_ctr("qkv[" + std::to_string(l) + "][" + std::to_string(g) + "]"));
-    for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + std::to_string(l) + "][" + std::to_string(g) + "]"));
-    p->c_comb.push_back(new_ctr("comb[" + std::to_string(l) + "]"));
-    p->c_o.push_back(new_ctr("o[" + std::to_string(l) + "]"));
-    p->c_router.push_back(moe ? new_ctr("router[" + std::to_string(l) + "]") : -1);
-    p->c_gateup.push_back(new_ctr("gateup[" + std::to_string(l) + "]"));
-    p->c_down.push_back(new_ctr("down[" + std::to_string(l) + "]"));
+    const std::string ls = std::to_string(l);
+    for (int g = 0; g < Hkv; ++g) p->c_qkv.push_back(new_ctr("qkv[" + ls + "][" + std::to_string(g) + "]"));
+    for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + ls + "][" + std::to_string(g) + "]"));
+    p->c_comb.push_back(new_ctr("comb[" + ls + "]"));
+    p->c_o.push_back(new_ctr("o[" + ls + "]"));
+    p->c_router.push_back(moe ? new_ctr("router[" + ls + "]") : -1);
+    p->c_expert.push_back(new_ctr("expert[" + ls + "]"));
   }
   p->c_lm = new_ctr("lm");
   if (p->targets.size() >= mk::NO_CTR) {
@@ -165,6 +191,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   p->n_split.assign(B, 0);
   for (int b = 0; b < B; ++b) p->n_split[b] = (pg_bound + pps - 1) / pps;
   p->S_max = *std::max_element(p->n_split.begin(), p->n_split.end());
+  p->comb_dim_tasks = std::max(1, std::min(D / 8, n_cu / std::max(1, B * Hq)));
 
   std::vector<std::vector<Task>> stages;
   auto ctr16 = [](int c) { return c < 0 ? mk::NO_CTR : (uint16_t)c; };
@@ -173,14 +200,14 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     {
       std::vector<Task> st;
       int per_g = std::max(1, n_cu / Hkv);
-      int cap_pairs = std::max(1, rows_cap(H, B, 1) / 2);
-      per_g = std::max(per_g, (p->n_pairs_g + cap_pairs - 1) / cap_pairs);
+      const int cap_pairs = std::max(1, rows_max(H) / 2);
+      per_g = std::max(per_g, ceil_div(p->n_pairs_g, cap_pairs));
       for (int g = 0; g < Hkv; ++g)
-        for (auto [s, c] : split_even(p->n_pairs_g, per_g)) {
+        for (auto [s0, c] : split_even(p->n_pairs_g, per_g)) {
           Task t = mk_task(mk::OP_QKV, l);
-          t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_down[l - 1]);
+          t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_expert[l - 1]);
           t.signal = ctr16(p->c_qkv[l * Hkv + g]);
-          t.a0 = g; t.a1 = s; t.a2 = c;
+          t.a0 = g; t.a1 = s0; t.a2 = c;
           st.push_back(t);
         }
       stages.push_back(st);
@@ -191,115 +218,112 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       for (int b = 0; b < B; ++b)
         for (int g = 0; g < Hkv; ++g) {
           int si = 0;
-          for (auto [s, c] : split_even(pg_bound, p->n_split[b])) {
+          for (auto [s0, c] : split_even(pg_bound, p->n_split[b])) {
             Task t = mk_task(mk::OP_ATTN, l);
             t.wait_b = ctr16(p->c_qkv[l * Hkv + g]);
             t.signal = ctr16(p->c_attn[l * Hkv + g]);
-            t.a0 = b; t.a1 = g; t.a2 = s; t.a3 = c; t.aux = (uint16_t)si++;
+            t.a0 = b; t.a1 = g; t.a2 = s0; t.a3 = c; t.aux = (uint16_t)si++;
             st.push_back(t);
           }
         }
       stages.push_back(st);
     }
-    // COMB: one query head of one sequence per task
+    // COMB: one query head of one sequence, a range of its dims, per task
     {
       std::vector<Task> st;
       for (int b = 0; b < B; ++b)
-        for (int h = 0; h < Hq; ++h) {
-          Task t = mk_task(mk::OP_COMB, l);
-          t.wait_b = ctr16(p->c_attn[l * Hkv + h / HG]);
-          t.signal = ctr16(p->c_comb[l]);
-          t.a0 = b; t.a1 = h; t.a2 = 1; t.a3 = p->n_split[b];
-          st.push_back(t);
-        }
+        for (int h = 0; h < Hq; ++h)
+          for (auto [d0, nd] : split_even(D, p->comb_dim_tasks)) {
+            Task t = mk_task(mk::OP_COMB, l);
+            t.wait_b = ctr16(p->c_attn[l * Hkv + h / HG]);
+            t.signal = ctr16(p->c_comb[l]);
+            t.a0 = b; t.a1 = h; t.a2 = d0; t.a3 = nd; t.aux = (uint16_t)p->n_split[b];
+            st.push_back(t);
+          }
       stages.push_back(st);
     }
     // O
     {
       std::vector<Task> st;
-      int nt = std::max(n_cu, (H + rows_cap(Hq * D, B, 1) - 1) / rows_cap(Hq * D, B, 1));
-      for (auto [s, c] : split_even(H, nt)) {
+      int nt = std::max(n_cu, ceil_div(H, rows_max(Hq * D)));
+      for (auto [s0, c] : split_even(H, nt)) {
         Task t = mk_task(mk::OP_O, l);
         t.wait_b = ctr16(p->c_comb[l]);
         t.signal = ctr16(p->c_o[l]);
-        t.a1 = s; t.a2 = c;
+        t.a1 = s0; t.a2 = c;
         st.push_back(t);
       }
       stages.push_back(st);
     }
     if (moe) {
       std::vector<Task> st;
-      for (auto [s, c] : split_even(m->n_experts, std::max(1, n_cu / 4))) {
+      int nt = std::max(std::min(n_cu, ceil_div(m->n_experts, 8)), ceil_div(m->n_experts, rows_max(H)));
+      for (auto [s0, c] : split_even(m->n_experts, nt)) {
         Task t = mk_task(mk::OP_ROUTER, l);
         t.wait_b = ctr16(p->c_o[l]);
         t.signal = ctr16(p->c_router[l]);
-        t.a1 = s; t.a2 = c;
+        t.a1 = s0; t.a2 = c;
         st.push_back(t);
       }
       stages.push_back(st);
     }
-    // GATEUP
+    // EXPERT: at most one per compute unit. Task i takes gate/up tile i (an
+    // expert slot of one sequence and a range of FFN rows) and down tile i (a
+    // range of hidden rows over every slot); its down part reads the
+    // activations of every expert task of the layer.
     {
-      std::vector<Task> st;
-      int cap = std::max(1, rows_cap(H, moe ? 1 : B, 2));
+      std::vector<std::array<int, 4>> gu;  // (b, slot, f0, nf)
       if (moe) {
-        int per = std::max(1, n_cu / (B * K));
-        per = std::max(per, (F + cap - 1) / cap);
+        const int per = std::max(1, n_cu / (B * K));
         for (int b = 0; b < B; ++b)
-          for (int j = 0; j < K; ++j) {
-            bool first = true;
-            for (auto [s, c] : split_even(F, per)) {
-              Task t = mk_task(mk::OP_GATEUP, l);
-              t.wait_a = ctr16(p->c_router[l]);
-              t.signal = ctr16(p->c_gateup[l]);
-              t.a0 = b; t.aux = (uint16_t)j; t.a1 = s; t.a2 = c;
-              if (first && j == 0) t.flags |= mk::TF_WRITE_TOPK;
-              first = false;
-              st.push_back(t);
-            }
-          }
+          for (int j = 0; j < K; ++j)
+            for (auto [s0, c] : split_even(F, per)) gu.push_back({b, j, s0, c});
       } else {
-        int per = std::max(n_cu, (F + cap - 1) / cap);
-        for (auto [s, c] : split_even(F, per)) {
-          Task t = mk_task(mk::OP_GATEUP, l);
-          t.wait_b = ctr16(p->c_o[l]);
-          t.signal = ctr16(p->c_gateup[l]);
-          t.a0 = -1; t.a1 = s; t.a2 = c;
-          st.push_back(t);
-        }
+        for (auto [s0, c] : split_even(F, n_cu)) gu.push_back({0, 0, s0, c});
       }
-      stages.push_back(st);
-    }
-    // DOWN
-    {
+      std::vector<std::pair<int, int>> dn = split_even(H, n_cu);
+      const size_t n = std::max(gu.size(), dn.size());
+      if (n > (size_t)n_cu) {
+        delete p;
+        return fail(MK_EUNSUPPORTED, "mk_plan: more expert tiles than compute units");
+      }
       std::vector<Task> st;
-      int cap = rows_cap(F, B, K);
-      int nt = std::max(n_cu, (H + cap - 1) / cap);
-      for (auto [s, c] : split_even(H, nt)) {
-        Task t = mk_task(mk::OP_DOWN, l);
+      for (size_t i = 0; i < n; ++i) {
+        Task t = mk_task(mk::OP_EXPERT, l);
         t.wait_a = moe ? ctr16(p->c_router[l]) : mk::NO_CTR;
-        t.wait_b = ctr16(p->c_gateup[l]);
-        t.signal = ctr16(p->c_down[l]);
-        t.a1 = s; t.a2 = c;
+        t.wait_b = ctr16(p->c_o[l]);
+        t.signal = ctr16(p->c_expert[l]);
+        if (i < gu.size()) {
+          t.a0 = gu[i][0]; t.aux = (uint16_t)gu[i][1]; t.a1 = gu[i][2]; t.a2 = gu[i][3];
+          if (moe && gu[i][1] == 0 && gu[i][2] == 0) t.flags |= mk::TF_WRITE_TOPK;
+        }
+        if (i < dn.size()) t.a3 = (dn[i].first << 16) | dn[i].second;
         st.push_back(t);
       }
       stages.push_back(st);
     }
   }
-  // LM head and final argmax merge
+  // LM head (rows per tile a multiple of the streaming batch) and the final argmax merge
   {
     std::vector<Task> st;
-    int cap = std::min(1024, rows_cap(H, B, 1));
-    int nt = std::max(n_cu, (m->vocab + cap - 1) / cap);
+    int tch = 64, cplh = 1;
+    mk::gemv_map(H, &tch, &cplh);
+    const int quantum = mk::gemv_groups(tch) * mk::LM_BATCH * 2;
+    int rows = ceil_div(ceil_div(m->vocab, n_cu), quantum) * quantum;
+    rows = std::min(rows, 2048 / quantum * quantum);
     int i = 0;
-    for (auto [s, c] : split_even(m->vocab, nt)) {
+    for (int s0 = 0; s0 < m->vocab; s0 += rows) {
       Task t = mk_task(mk::OP_LM, 0);
-      t.wait_b = ctr16(p->c_down[L - 1]);
+      t.wait_b = ctr16(p->c_expert[L - 1]);
       t.signal = ctr16(p->c_lm);
-      t.a1 = s; t.a2 = c; t.a3 = i++;
+      t.a1 = s0; t.a2 = std::min(rows, m->vocab - s0); t.a3 = i++;
       st.push_back(t);
     }
     p->n_lm = i;
+    if (p->n_lm > 4096) {
+      delete p;
+      return fail(MK_EUNSUPPORTED, "mk_plan: more than 4096 LM-head tiles");
+    }
     stages.push_back(st);
     Task f = mk_task(mk::OP_FINAL, 0);
     f.wait_b = ctr16(p->c_lm);
@@ -307,24 +331,6 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     stages.push_back({f});
   }
   p->n_stages = (int)stages.size();
-
-  // GEMV thread mapping per task kind (log2 TC in the high nibble of flags)
-  auto lg = [](int v) { int r = 0; while ((1 << r) < v) ++r; return r; };
-  for (auto& st : stages)
-    for (auto& t : st) {
-      int K = 0;
-      switch (t.op) {
-        case mk::OP_QKV: case mk::OP_ROUTER: case mk::OP_GATEUP: case mk::OP_LM: K = H; break;
-        case mk::OP_O: K = Hq * D; break;
-        case mk::OP_DOWN: K = F; break;
-        default: break;
-      }
-      if (K) {
-        int tcK = 0, cplK = 0;
-        mk::gemv_map(K, &tcK, &cplK);
-        t.flags = (uint8_t)((t.flags & 0x0F) | (lg(tcK) << 4));
-      }
-    }
 
   // producer counts -> targets, then the per-epoch counts carried by the waits
   for (auto& st : stages)
@@ -345,42 +351,45 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   p->lists.assign(n_cu, {});
   std::vector<std::vector<int>> stage_lists(n_cu);
   int cursor = 0;
-  for (int s = 0; s < (int)stages.size(); ++s) {
-    for (size_t i = 0; i < stages[s].size(); ++i) {
+  for (int s0 = 0; s0 < (int)stages.size(); ++s0) {
+    for (size_t i = 0; i < stages[s0].size(); ++i) {
       int cu = (cursor + (int)i) % n_cu;
-      p->lists[cu].push_back(stages[s][i]);
-      stage_lists[cu].push_back(s);
+      p->lists[cu].push_back(stages[s0][i]);
+      stage_lists[cu].push_back(s0);
     }
-    cursor = (cursor + (int)stages[s].size()) % n_cu;
+    cursor = (cursor + (int)stages[s0].size()) % n_cu;
   }
   p->stage_of_task.clear();
   for (int cu = 0; cu < n_cu; ++cu)
-    for (int s : stage_lists[cu]) p->stage_of_task.push_back(s);
+    for (int s0 : stage_lists[cu]) p->stage_of_task.push_back(s0);
   p->n_tasks = p->stage_of_task.size();
 
-  // workspace layout
+  // workspace layout: tagged words (8 bytes), per layer
   {
-    const int PS = D + 4;
-    size_t per_layer[8] = {
-        (size_t)B * H * 4,                       // XATTN
-        (size_t)B * H * 4,                       // XFFN
-        (size_t)B * Hq * D * 4,                  // Q
-        (size_t)B * Hq * p->S_max * PS * 4,      // PART
-        (size_t)B * Hq * D * 4,                  // O
-        moe ? (size_t)B * m->n_experts * 4 : 0,  // RLOG
-        (size_t)B * K * F * 4,                   // ACT
-        0};
+    const int PS = D + 2;
+    size_t per_layer[9] = {
+        (size_t)B * H,                                    // XATTN
+        (size_t)B * H,                                    // XFFN
+        (size_t)B * Hq * D,                               // Q
+        (size_t)B * Hkv * p->S_max * HG * PS,             // PART
+        (size_t)B * Hq * D,                               // O
+        moe ? (size_t)B * m->n_experts : 0,               // RLOG
+        (size_t)B * K * F,                                // ACT
+        0,                                                // LMPART (not per layer)
+        (size_t)B * Hkv * 2 * D};                         // KVN
     size_t off = 0;
-    for (int i = 0; i < 7; ++i) {
+    for (int i = 0; i < 9; ++i) {
       p->ws_off[i] = off;
-      p->ws_stride[i] = per_layer[i];
-      p->ws_layer_bytes[i] = per_layer[i];
-      off = align256(off + per_layer[i] * L);
+      if (i == MK_BUF_LMPART) {
+        p->ws_stride[i] = 0;
+        p->ws_layer_bytes[i] = (size_t)p->n_lm * B * 2 * 8;
+        off = align256(off + p->ws_layer_bytes[i]);
+      } else {
+        p->ws_stride[i] = per_layer[i] * 8;
+        p->ws_layer_bytes[i] = per_layer[i] * 8;
+        off = align256(off + per_layer[i] * 8 * L);
+      }
     }
-    p->ws_off[7] = off;
-    p->ws_stride[7] = 0;
-    p->ws_layer_bytes[7] = (size_t)p->n_lm * B * 8;
-    off = align256(off + p->ws_layer_bytes[7]);
     p->ws_total = off;
   }
 
@@ -413,41 +422,47 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
 
 namespace {
 
-struct Cover {
-  std::string what;
-  std::vector<int64_t> items;
-};
-
 // Expand the outputs a task produces into integer keys per (op, layer).
 void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::string, int64_t>>& out) {
   const auto& m = p->m;
   const int D = m.head_dim, Hkv = m.n_kv_heads, Hq = m.n_q_heads;
-  std::string key = std::to_string(t.op) + ":" + std::to_string(t.layer);
+  const std::string ls = ":" + std::to_string(t.layer);
   switch (t.op) {
     case mk::OP_QKV:
       for (int q = t.a1; q < t.a1 + t.a2; ++q) {
         int head, i, row;
         mk::qkv_pair(q, t.a0, p->HG, D, Hq, Hkv, &head, &i, &row);
-        out.push_back({key, row});
-        out.push_back({key, row + D / 2});
+        out.push_back({"qkv" + ls, row});
+        out.push_back({"qkv" + ls, row + D / 2});
       }
       break;
     case mk::OP_ATTN:
       for (int pg = t.a2; pg < t.a2 + t.a3; ++pg)
-        out.push_back({key, ((int64_t)t.a0 * Hkv + t.a1) * 1000000 + pg});
+        out.push_back({"attn" + ls, ((int64_t)t.a0 * Hkv + t.a1) * 1000000 + pg});
       break;
     case mk::OP_COMB:
-      for (int h = t.a1; h < t.a1 + t.a2; ++h) out.push_back({key, (int64_t)t.a0 * Hq + h});
+      for (int d = t.a2; d < t.a2 + t.a3; ++d)
+        out.push_back({"comb" + ls, ((int64_t)t.a0 * Hq + t.a1) * 1024 + d});
       break;
-    case mk::OP_GATEUP:
+    case mk::OP_EXPERT: {
+      const bool moe = m.n_experts > 0;
       for (int f = t.a1; f < t.a1 + t.a2; ++f)
-        out.push_back({key, t.a0 < 0 ? f : ((int64_t)t.a0 * 64 + t.aux) * 1000000 + f});
+        out.push_back({"gateup" + ls, moe ? ((int64_t)t.a0 * 64 + t.aux) * 1000000 + f : f});
+      const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
+      for (int r = r0; r < r0 + nr; ++r) out.push_back({"down" + ls, r});
       break;
-    case mk::OP_O: case mk::OP_ROUTER: case mk::OP_DOWN: case mk::OP_LM:
-      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({key, r});
+    }
+    case mk::OP_O:
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"o" + ls, r});
+      break;
+    case mk::OP_ROUTER:
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"router" + ls, r});
+      break;
+    case mk::OP_LM:
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"lm", r});
       break;
     case mk::OP_FINAL:
-      out.push_back({key, 0});
+      out.push_back({"final", 0});
       break;
   }
 }
@@ -462,26 +477,27 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
   // expected output sets
   std::map<std::string, std::set<int64_t>> want;
   for (int l = 0; l < L; ++l) {
-    auto k = [&](int op) { return std::to_string(op) + ":" + std::to_string(l); };
-    for (int r = 0; r < p->QKV_ROWS; ++r) want[k(mk::OP_QKV)].insert(r);
+    const std::string ls = ":" + std::to_string(l);
+    for (int r = 0; r < p->QKV_ROWS; ++r) want["qkv" + ls].insert(r);
     for (int b = 0; b < B; ++b)
       for (int g = 0; g < m.n_kv_heads; ++g)
         for (int pg = 0; pg < (p->bound + 15) / 16; ++pg)
-          want[k(mk::OP_ATTN)].insert(((int64_t)b * m.n_kv_heads + g) * 1000000 + pg);
+          want["attn" + ls].insert(((int64_t)b * m.n_kv_heads + g) * 1000000 + pg);
     for (int b = 0; b < B; ++b)
-      for (int h = 0; h < m.n_q_heads; ++h) want[k(mk::OP_COMB)].insert((int64_t)b * m.n_q_heads + h);
-    for (int r = 0; r < m.hidden; ++r) want[k(mk::OP_O)].insert(r), want[k(mk::OP_DOWN)].insert(r);
+      for (int h = 0; h < m.n_q_heads; ++h)
+        for (int d = 0; d < m.head_dim; ++d) want["comb" + ls].insert(((int64_t)b * m.n_q_heads + h) * 1024 + d);
+    for (int r = 0; r < m.hidden; ++r) want["o" + ls].insert(r), want["down" + ls].insert(r);
     if (moe) {
-      for (int r = 0; r < m.n_experts; ++r) want[k(mk::OP_ROUTER)].insert(r);
+      for (int r = 0; r < m.n_experts; ++r) want["router" + ls].insert(r);
       for (int b = 0; b < B; ++b)
         for (int j = 0; j < m.top_k; ++j)
-          for (int f = 0; f < p->F; ++f) want[k(mk::OP_GATEUP)].insert(((int64_t)b * 64 + j) * 1000000 + f);
+          for (int f = 0; f < p->F; ++f) want["gateup" + ls].insert(((int64_t)b * 64 + j) * 1000000 + f);
     } else {
-      for (int f = 0; f < p->F; ++f) want[k(mk::OP_GATEUP)].insert(f);
+      for (int f = 0; f < p->F; ++f) want["gateup" + ls].insert(f);
     }
   }
-  for (int r = 0; r < m.vocab; ++r) want[std::to_string(mk::OP_LM) + ":0"].insert(r);
-  want[std::to_string(mk::OP_FINAL) + ":0"].insert(0);
+  for (int r = 0; r < m.vocab; ++r) want["lm"].insert(r);
+  want["final"].insert(0);
 
   std::map<std::string, std::multiset<int64_t>> got;
   std::vector<uint32_t> producers(p->targets.size(), 0);
@@ -489,10 +505,14 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
   size_t k = 0;
   for (int cu = 0; cu < p->n_cu; ++cu) {
     int last = -1;
+    std::set<int> expert_layers;
     for (auto& t : p->lists[cu]) {
       int st = p->stage_of_task[k++];
       if (st < last) return fail(MK_EINVAL, "validate: list of unit " + std::to_string(cu) + " is not in stage order");
       last = st;
+      if (t.op == mk::OP_EXPERT && !expert_layers.insert(t.layer).second)
+        return fail(MK_EINVAL, "validate: unit " + std::to_string(cu) + " holds two expert tasks of layer " +
+                                   std::to_string(t.layer) + " (their down parts would wait on each other)");
       std::vector<std::pair<std::string, int64_t>> outs;
       task_outputs(p, t, outs);
       for (auto& [key, v] : outs) got[key].insert(v);
@@ -505,10 +525,10 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
       }
     }
   }
-  for (auto& [key, s] : want) {
+  for (auto& [key, s0] : want) {
     auto it = got.find(key);
     if (it == got.end()) return fail(MK_EINVAL, "validate: no task covers " + key);
-    if (it->second.size() != s.size() || std::set<int64_t>(it->second.begin(), it->second.end()) != s)
+    if (it->second.size() != s0.size() || std::set<int64_t>(it->second.begin(), it->second.end()) != s0)
       return fail(MK_EINVAL, "validate: outputs of " + key + " not covered exactly once");
   }
   if (got.size() != want.size()) return fail(MK_EINVAL, "validate: tasks of an unexpected kind");
@@ -531,6 +551,11 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
 
 // ------------------------------------------------------------------ simulation
 
+// Runs the per-unit lists on n_cu virtual units under seeded random
+// interleavings. A task may start when its waits are satisfied; an expert
+// task first publishes its activations (gate/up part) and then waits until
+// every expert task of its layer has published before it completes (down
+// part). Every task's reads are checked against the completed producers.
 extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t n_runs) {
   if (!p || n_runs <= 0) return fail(MK_EINVAL, "mk_plan_simulate: bad args");
   const auto& m = p->m;
@@ -538,9 +563,9 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
   const bool moe = m.n_experts > 0;
   std::mt19937_64 rng(seed);
   std::vector<uint64_t> ctr(p->targets.size(), 0);
-  // per-epoch completion counts by (op, layer, group) for the data-readiness check
   auto slot = [&](int op, int l, int g) { return ((size_t)op * (L + 1) + l) * (Hkv + 1) + g; };
-  std::vector<uint32_t> total((mk::OP_COUNT + 1) * (L + 1) * (Hkv + 1), 0);
+  const size_t n_slots = (mk::OP_COUNT + 1) * (L + 1) * (Hkv + 1);
+  std::vector<uint32_t> total(n_slots, 0);
   for (int cu = 0; cu < p->n_cu; ++cu)
     for (auto& t : p->lists[cu]) {
       total[slot(t.op, t.layer, Hkv)]++;
@@ -548,10 +573,12 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
     }
   for (int run = 0; run < n_runs; ++run) {
     const uint64_t epoch = (uint64_t)run + 1;
-    std::vector<uint32_t> done(total.size(), 0);
+    std::vector<uint32_t> done(n_slots, 0);
+    std::vector<uint32_t> published(L, 0);      // expert gate/up parts finished per layer
     std::vector<size_t> head(p->n_cu, 0);
+    std::vector<char> phase(p->n_cu, 0);        // expert task at the head: 1 = published
     auto all_done = [&](int op, int l, int g) { return done[slot(op, l, g)] == total[slot(op, l, g)]; };
-    auto ready = [&](const Task& t) {
+    auto waits_ok = [&](const Task& t) {
       if (t.wait_a != mk::NO_CTR && ctr[t.wait_a] < epoch * t.cnt_a) return false;
       if (t.wait_b != mk::NO_CTR && ctr[t.wait_b] < epoch * t.cnt_b) return false;
       return true;
@@ -560,14 +587,13 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
     auto inputs_ok = [&](const Task& t) -> bool {
       int l = t.layer;
       switch (t.op) {
-        case mk::OP_QKV: return l == 0 || all_done(mk::OP_DOWN, l - 1, Hkv);
+        case mk::OP_QKV: return l == 0 || all_done(mk::OP_EXPERT, l - 1, Hkv);
         case mk::OP_ATTN: return all_done(mk::OP_QKV, l, t.a1);
         case mk::OP_COMB: return all_done(mk::OP_ATTN, l, t.a1 / HG);
         case mk::OP_O: return all_done(mk::OP_COMB, l, Hkv);
         case mk::OP_ROUTER: return all_done(mk::OP_O, l, Hkv);
-        case mk::OP_GATEUP: return all_done(mk::OP_O, l, Hkv) && (!moe || all_done(mk::OP_ROUTER, l, Hkv));
-        case mk::OP_DOWN: return all_done(mk::OP_GATEUP, l, Hkv) && all_done(mk::OP_O, l, Hkv);
-        case mk::OP_LM: return all_done(mk::OP_DOWN, L - 1, Hkv);
+        case mk::OP_EXPERT: return all_done(mk::OP_O, l, Hkv) && (!moe || all_done(mk::OP_ROUTER, l, Hkv));
+        case mk::OP_LM: return all_done(mk::OP_EXPERT, L - 1, Hkv);
         case mk::OP_FINAL: return all_done(mk::OP_LM, 0, Hkv);
       }
       return false;
@@ -576,8 +602,15 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
     std::vector<int> runnable;
     while (remaining) {
       runnable.clear();
-      for (int cu = 0; cu < p->n_cu; ++cu)
-        if (head[cu] < p->lists[cu].size() && ready(p->lists[cu][head[cu]])) runnable.push_back(cu);
+      for (int cu = 0; cu < p->n_cu; ++cu) {
+        if (head[cu] >= p->lists[cu].size()) continue;
+        const Task& t = p->lists[cu][head[cu]];
+        if (t.op == mk::OP_EXPERT && phase[cu] == 1) {
+          if (published[t.layer] == total[slot(mk::OP_EXPERT, t.layer, Hkv)]) runnable.push_back(cu);
+        } else if (waits_ok(t)) {
+          runnable.push_back(cu);
+        }
+      }
       if (runnable.empty()) {
         std::string msg = "simulate: deadlock in epoch " + std::to_string(epoch) + "; blocked:";
         int shown = 0;
@@ -591,15 +624,24 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
           }
         return fail(MK_ESTATE, msg);
       }
-      // run a random prefix of runnable units, one task each, in random order
+      // advance a random subset of runnable units by one event each, in random order
       std::shuffle(runnable.begin(), runnable.end(), rng);
       size_t n = 1 + rng() % runnable.size();
       for (size_t i = 0; i < n; ++i) {
         int cu = runnable[i];
         const Task& t = p->lists[cu][head[cu]];
-        if (!inputs_ok(t))
+        if (t.op == mk::OP_EXPERT && phase[cu] == 0) {
+          if (!inputs_ok(t))
+            return fail(MK_ESTATE, "simulate: expert layer " + std::to_string(t.layer) +
+                                       " ran before its producers finished");
+          phase[cu] = 1;
+          published[t.layer]++;
+          continue;
+        }
+        if (t.op != mk::OP_EXPERT && !inputs_ok(t))
           return fail(MK_ESTATE, "simulate: op " + std::to_string(t.op) + " layer " +
                                      std::to_string(t.layer) + " ran before its producers finished");
+        phase[cu] = 0;
         head[cu]++;
         remaining--;
         done[slot(t.op, t.layer, Hkv)]++;
@@ -620,7 +662,7 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
 extern "C" size_t mk_plan_device_bytes(const mk_plan_t* p) { return p ? p->image.size() : 0; }
 extern "C" size_t mk_plan_workspace_bytes(const mk_plan_t* p) { return p ? p->ws_total : 0; }
 extern "C" size_t mk_plan_counter_bytes(const mk_plan_t* p) {
-  return p ? p->targets.size() * mk::CTR_STRIDE * 4 : 0;
+  return p ? p->targets.size() * mk::CTR_LINES * mk::CTR_STRIDE * 4 : 0;
 }
 extern "C" int32_t mk_plan_n_tasks(const mk_plan_t* p) { return p ? (int32_t)p->n_tasks : -1; }
 extern "C" int32_t mk_plan_n_counters(const mk_plan_t* p) { return p ? (int32_t)p->targets.size() : -1; }
@@ -635,9 +677,10 @@ extern "C" mk_status mk_plan_export(const mk_plan_t* p, void* buf, size_t bytes)
 
 extern "C" mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t layer, size_t* off,
                                     size_t* bytes) {
-  if (!p || !off || !bytes || which < 0 || which > 7) return fail(MK_EINVAL, "mk_plan_buffer: bad args");
-  if (which < 7 && (layer < 0 || layer >= p->m.n_layers)) return fail(MK_EINVAL, "mk_plan_buffer: bad layer");
-  *off = p->ws_off[which] + (which < 7 ? (size_t)layer * p->ws_stride[which] : 0);
+  if (!p || !off || !bytes || which < 0 || which > 8) return fail(MK_EINVAL, "mk_plan_buffer: bad args");
+  const bool per_layer = which != MK_BUF_LMPART;
+  if (per_layer && (layer < 0 || layer >= p->m.n_layers)) return fail(MK_EINVAL, "mk_plan_buffer: bad layer");
+  *off = p->ws_off[which] + (per_layer ? (size_t)layer * p->ws_stride[which] : 0);
   *bytes = p->ws_layer_bytes[which];
   return MK_OK;
 }

@@ -21,20 +21,24 @@ struct mk_plan {
 
   // counter ids
   std::vector<int32_t> c_qkv, c_attn;  // [L][Hkv]
-  std::vector<int32_t> c_comb, c_o, c_router, c_gateup, c_down;  // [L]
+  std::vector<int32_t> c_comb, c_o, c_router, c_expert;  // [L]
   int32_t c_lm = -1;
 
   int32_t S_max = 0;                // attention splits per (b, g), max over b
+  int32_t comb_dim_tasks = 1;       // combine tasks per (b, query head)
+  int32_t kernel_class = -1;        // compiled kernel variant for this shape
   std::vector<int32_t> n_split;     // per b
   int32_t n_lm = 0, n_stages = 0;
 
   // workspace layout: base offset (bytes) and per-layer stride (bytes) per MK_BUF_*
-  size_t ws_off[8] = {}, ws_stride[8] = {}, ws_layer_bytes[8] = {};
+  size_t ws_off[9] = {}, ws_stride[9] = {}, ws_layer_bytes[9] = {};
   size_t ws_total = 0;
 
   std::vector<uint8_t> image;  // device image
   size_t n_tasks = 0;
 };
+
+inline int mk_buf_lmpart() { return MK_BUF_LMPART; }
 
 namespace mkh {
 void set_error(const std::string& s);

@@ -11,15 +11,15 @@ import numpy as np
 import torch
 
 from . import (
-    MK_BUF_ACT, MK_BUF_O, MK_BUF_Q, MK_BUF_RLOG, MK_BUF_XATTN, MK_BUF_XFFN,
+    MK_BUF_O, MK_BUF_Q, MK_BUF_RLOG, MK_BUF_XATTN, MK_BUF_XFFN,
     MkError, MK_OK, mk_decode_step, mk_io, mk_kv, mk_kv_pool_elems, mk_plan, mk_plan_buffer,
     mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks, mk_plan_upload,
     mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_step_status, mk_weights,
     model_desc,
 )
 
-EPOCH_LIMIT = 65535  # counters end a step at epoch * target; target <= 65535
 TRACE_WORDS = 8     # u64 per task in the optional trace buffer
+CTR_LINES = 8       # sub-counters (64-byte lines) per completion counter
 
 
 def _ptr(t):
@@ -63,7 +63,8 @@ class Decoder:
         self.bound = bound
         dev = self.device
         self.plan_buf = torch.empty(mk_plan_device_bytes(self.plan), dtype=torch.uint8, device=dev)
-        self.ws = torch.empty(mk_plan_workspace_bytes(self.plan), dtype=torch.uint8, device=dev)
+        # tagged activation words: zero-filled once, then every step uses a larger epoch
+        self.ws = torch.zeros(mk_plan_workspace_bytes(self.plan), dtype=torch.uint8, device=dev)
         self.ctr = torch.zeros(mk_plan_counter_bytes(self.plan) // 4, dtype=torch.int32, device=dev)
         self.status = torch.zeros(4, dtype=torch.int32, device=dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
@@ -101,9 +102,6 @@ class Decoder:
 
     def step(self, tokens_in, tokens_out, topk_ids=None, topk_w=None, logits=None, timeout_ms=0):
         """Enqueue one decode step on the current stream (asynchronous)."""
-        if self.epoch >= EPOCH_LIMIT:
-            self.ctr.zero_()
-            self.epoch = 0
         self.epoch += 1
         io = mk_io(_ptr(tokens_in), _ptr(tokens_out), _ptr(topk_ids), _ptr(topk_w), _ptr(logits))
         mk_decode_step(self.plan, self._w, self._kv, io, self._bufs, self.epoch, timeout_ms,
@@ -116,25 +114,40 @@ class Decoder:
         if st != MK_OK:
             raise MkError(st, msg)
 
-    def buffer(self, which, layer, dtype=torch.float32):
-        """Workspace sub-buffer (MK_BUF_*) of one layer as a device tensor view."""
+    def counters(self):
+        """Completion counts per counter (sum of its lines), as a host int64 tensor."""
+        c = self.ctr.view(-1, CTR_LINES, 16)[:, :, 0].to(torch.int64)
+        return c.sum(dim=1).cpu()
+
+    def buffer(self, which, layer=0):
+        """Workspace sub-buffer (MK_BUF_*) of one layer: its tagged u64 words (device view)."""
         off, nb = mk_plan_buffer(self.plan, which, layer)
-        return self.ws[off:off + nb].view(dtype)
+        return self.ws[off:off + nb].view(torch.int64)
+
+    def values(self, which, layer=0):
+        """(values fp32, tags int64) of a tagged sub-buffer, on the host."""
+        w = self.buffer(which, layer).cpu()
+        vals = (w & 0xFFFFFFFF).to(torch.int32).view(torch.float32)
+        tags = (w >> 32) & 0xFFFFFFFF
+        return vals, tags
+
+    def _current(self, which, layer, shape):
+        v, t = self.values(which, layer)
+        if not bool((t == self.epoch).all()):
+            raise RuntimeError(f"buffer {which} layer {layer} holds words of another step")
+        return v.view(*shape)
 
     def hidden_after_attn(self, layer):
-        return self.buffer(MK_BUF_XATTN, layer).view(self.B, self.m["hidden"])
+        return self._current(MK_BUF_XATTN, layer, (self.B, self.m["hidden"]))
 
     def hidden_after_ffn(self, layer):
-        return self.buffer(MK_BUF_XFFN, layer).view(self.B, self.m["hidden"])
+        return self._current(MK_BUF_XFFN, layer, (self.B, self.m["hidden"]))
 
     def router_logits(self, layer):
-        return self.buffer(MK_BUF_RLOG, layer).view(self.B, -1)
+        return self._current(MK_BUF_RLOG, layer, (self.B, self.m["n_experts"]))
 
     def queries(self, layer):
-        return self.buffer(MK_BUF_Q, layer).view(self.B, self.m["n_q_heads"], self.m["head_dim"])
+        return self._current(MK_BUF_Q, layer, (self.B, self.m["n_q_heads"], self.m["head_dim"]))
 
     def attn_out(self, layer):
-        return self.buffer(MK_BUF_O, layer).view(self.B, self.m["n_q_heads"], self.m["head_dim"])
-
-    def ffn_act(self, layer):
-        return self.buffer(MK_BUF_ACT, layer)
+        return self._current(MK_BUF_O, layer, (self.B, self.m["n_q_heads"], self.m["head_dim"]))

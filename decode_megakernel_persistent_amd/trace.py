@@ -8,7 +8,7 @@ it into per-operation time splits and a per-stage timeline.
 """
 import numpy as np
 
-OPS = {1: "qkv", 2: "attn", 3: "comb", 4: "o", 5: "router", 6: "gateup", 7: "down", 8: "lm",
+OPS = {1: "qkv", 2: "attn", 3: "comb", 4: "o", 5: "router", 6: "expert", 8: "lm",
        9: "final"}
 TICK_US = 0.01  # 100 MHz
 

@@ -131,8 +131,12 @@ typedef struct mk_io {
 /* Caller-owned device buffers of a plan. */
 typedef struct mk_step_buffers {
   const void* plan; size_t plan_bytes;      /* image uploaded by mk_plan_upload */
-  void* workspace; size_t workspace_bytes;  /* activations; no initialisation needed */
-  uint32_t* counters; size_t counter_bytes; /* zeroed once before epoch 1 */
+  void* workspace; size_t workspace_bytes;  /* tagged activations: zero-filled before the
+                                               first step; thereafter every step on this
+                                               workspace uses a larger epoch */
+  uint32_t* counters; size_t counter_bytes; /* completion counters, 8 sub-counters of one
+                                               64-byte line each per counter; each step adds
+                                               the counter's target to the sum of its lines */
   uint32_t* status;                         /* 4 words, zeroed once */
   uint64_t* trace; size_t trace_bytes;      /* NULL (no tracing), or 8 u64 per task
                                                (64 * mk_plan_n_tasks bytes), indexed by
@@ -186,9 +190,18 @@ int32_t mk_plan_n_cu(const mk_plan_t* p);
 /* The device image (the bytes mk_plan_upload copies) into a host buffer. */
 mk_status mk_plan_export(const mk_plan_t* p, void* host_buf, size_t bytes);
 mk_status mk_plan_upload(const mk_plan_t* p, void* d_plan, size_t bytes, void* hip_stream);
-/* Workspace sub-buffer `which` (MK_BUF_*) of layer `layer`: byte offset and size. */
+/* Workspace sub-buffer `which` (MK_BUF_*) of layer `layer` (ignored for
+ * MK_BUF_LMPART): byte offset and size. Every workspace buffer holds tagged
+ * words: u64 = (epoch << 32) | fp32 bits of the value, written by the step
+ * of that epoch (KVN holds bf16 bits in the low 16 bits of the value; LMPART
+ * holds (value, index) pairs per LM-head tile). Per layer:
+ *   XATTN [B][H] hidden after the attention residual, XFFN [B][H] layer output,
+ *   Q [B][Hq][d] rotated queries, KVN [B][Hkv][2][d] the new token's K and V,
+ *   PART [B][Hkv][splits][Hq/Hkv][d+2] attention split partials (o, max, sum),
+ *   O [B][Hq][d] combined attention, RLOG [B][E] router logits,
+ *   ACT [B][top_k][F] SwiGLU activations. */
 enum { MK_BUF_XATTN = 0, MK_BUF_XFFN = 1, MK_BUF_Q = 2, MK_BUF_PART = 3, MK_BUF_O = 4,
-       MK_BUF_RLOG = 5, MK_BUF_ACT = 6, MK_BUF_LMPART = 7 };
+       MK_BUF_RLOG = 5, MK_BUF_ACT = 6, MK_BUF_LMPART = 7, MK_BUF_KVN = 8 };
 mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t layer, size_t* offset,
                          size_t* bytes);
 /* The plan's per-epoch counter targets, [n_counters] (host). */
@@ -196,8 +209,9 @@ mk_status mk_plan_counter_targets(const mk_plan_t* p, uint32_t* out, int32_t n);
 void mk_plan_free(mk_plan_t* p);
 
 /* ---- one decode step (asynchronous on hip_stream) ----
- * epoch: 1 for the first step after the counters were zeroed, +1 per step
- * (every counter ends a step at epoch x its target; keep epoch x 65535 < 2^32).
+ * epoch: the tag of this step's activations; >= 1 and larger than every epoch
+ * used before on the same workspace since it was zero-filled (steps on one
+ * workspace run in stream order; a step never reads a word of another epoch).
  * tokens_in -> tokens_out: greedy argmax of the LM head (ties to the lower id).
  * On completion every seq_lens[b] has grown by one: the new token's K and V
  * sit at position seq_lens[b] (old value) of its sequence. timeout_ms bounds

@@ -369,7 +369,8 @@ def work_sets(m, ctx_bound):
 
     Keys: ("qkv", l) rows of W_qkv; ("attn", l) triples (b, kv head, page) for
     the pages that can hold tokens below each sequence's bound; ("comb", l)
-    pairs (b, q head); ("o", l) rows; ("router", l) rows; ("gateup", l)
+    elements (b, q head, dim) of the merged attention output; ("o", l) rows;
+    ("router", l) rows; ("gateup", l)
     (b, slot, row) for MoE or rows for dense; ("down", l) rows; ("lm",) rows.
     """
     L, H, Hq, Hkv, d = m["n_layers"], m["hidden"], m["n_q_heads"], m["n_kv_heads"], m["head_dim"]
@@ -380,7 +381,7 @@ def work_sets(m, ctx_bound):
         S["qkv", l] = set(range((Hq + 2 * Hkv) * d))
         S["attn", l] = {(b, g, p) for b in range(B) for g in range(Hkv)
                         for p in range(-(-ctx_bound[b] // pt))}
-        S["comb", l] = {(b, h) for b in range(B) for h in range(Hq)}
+        S["comb", l] = {(b, h, i) for b in range(B) for h in range(Hq) for i in range(d)}
         S["o", l] = set(range(H))
         if m["n_experts"]:
             S["router", l] = set(range(m["n_experts"]))

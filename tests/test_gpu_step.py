@@ -108,8 +108,7 @@ def run_step_parity(name, seed=0, **over):
     # counters: every counter at epoch x producers; sequence lengths advanced
     import decode_megakernel_persistent_amd as mk
     tg = torch.tensor(mk.mk_plan_counter_targets(dec.plan), dtype=torch.int64)
-    ctr = dec.ctr.view(-1, 16)[:, 0].cpu().to(torch.int64)
-    assert torch.equal(ctr, tg * dec.epoch)
+    assert torch.equal(dec.counters(), tg * dec.epoch)
     assert dec.seq_lens.cpu().tolist() == [c + 1 for c in w["ctx"]]
     mk.mk_pool_free(pool)
     dec.close()

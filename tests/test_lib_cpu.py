@@ -29,7 +29,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TASK = np.dtype([("op", "u1"), ("flags", "u1"), ("layer", "<u2"), ("wait_a", "<u2"),
                  ("wait_b", "<u2"), ("cnt_a", "<u2"), ("cnt_b", "<u2"), ("signal", "<u2"),
                  ("aux", "<u2"), ("a0", "<i4"), ("a1", "<i4"), ("a2", "<i4"), ("a3", "<i4")])
-OP_QKV, OP_ATTN, OP_COMB, OP_O, OP_ROUTER, OP_GATEUP, OP_DOWN, OP_LM, OP_FINAL = range(1, 10)
+OP_QKV, OP_ATTN, OP_COMB, OP_O, OP_ROUTER, OP_EXPERT = range(1, 7)
+OP_LM, OP_FINAL = 8, 9
 NO_CTR = 0xFFFF
 
 
@@ -109,7 +110,7 @@ def test_pool_lease_is_all_or_nothing():
 
 def decode_plan(img):
     hdr = np.frombuffer(img, dtype="<u4", count=16)
-    assert hdr[0] == 0x31504B4D
+    assert hdr[0] == 0x32504B4D
     n_cu, n_tasks, n_ctr, off = int(hdr[1]), int(hdr[2]), int(hdr[3]), int(hdr[4])
     cu_off = np.frombuffer(img, dtype="<u4", count=n_cu + 1, offset=64)
     tasks = np.frombuffer(img, dtype=TASK, count=n_tasks, offset=off)
@@ -150,16 +151,16 @@ def plan_coverage(tasks, m):
         elif op == OP_ATTN:
             add(("attn", l), [(a0, a1, p) for p in range(a2, a2 + a3)])
         elif op == OP_COMB:
-            add(("comb", l), [(a0, h) for h in range(a1, a1 + a2)])
+            add(("comb", l), [(a0, a1, i) for i in range(a2, a2 + a3)])
         elif op == OP_O:
             add(("o", l), list(range(a1, a1 + a2)))
         elif op == OP_ROUTER:
             add(("router", l), list(range(a1, a1 + a2)))
-        elif op == OP_GATEUP:
-            add(("gateup", l), list(range(a1, a1 + a2)) if a0 < 0 else
-                [(a0, aux, f) for f in range(a1, a1 + a2)])
-        elif op == OP_DOWN:
-            add(("down", l), list(range(a1, a1 + a2)))
+        elif op == OP_EXPERT:
+            # gate/up part: (b, slot, FFN row) for MoE, FFN row for a dense FFN;
+            # down part: hidden rows a3 >> 16 .. + (a3 & 0xFFFF)
+            add(("gateup", l), [(a0, aux, f) if m["n_experts"] else f for f in range(a1, a1 + a2)])
+            add(("down", l), list(range(a3 >> 16, (a3 >> 16) + (a3 & 0xFFFF))))
         elif op == OP_LM:
             add(("lm",), list(range(a1, a1 + a2)))
     return S
@@ -195,6 +196,11 @@ def test_plan_covers_the_oracle_work_exactly_once(name, n_cu):
         for wf, cf in (("wait_a", "cnt_a"), ("wait_b", "cnt_b")):
             m_ = tasks[wf] != NO_CTR
             assert np.array_equal(tasks[cf][m_].astype(np.int64), tg[tasks[wf][m_].astype(np.int64)])
+        # at most one expert task per compute unit and layer (their down parts wait on each other)
+        for cu in range(n_cu):
+            lt = tasks[int(cu_off[cu]):int(cu_off[cu + 1])]
+            ex = lt["layer"][lt["op"] == OP_EXPERT]
+            assert len(ex) == len(set(ex.tolist()))
         mk.mk_plan_validate(p)
         mk.mk_plan_simulate(p, 11, 3)
     finally:
@@ -234,7 +240,7 @@ def test_plan_rejects_out_of_bounds():
 def test_step_status_decoding():
     assert mk.mk_step_status([0, 0, 0, 0])[0] == mk.MK_OK
     st, msg = mk.mk_step_status([1, 17, 3, 42])
-    assert st == mk.MK_ETIMEOUT and "task 17" in msg and "counter 3" in msg
+    assert st == mk.MK_ETIMEOUT and "task 17" in msg and "word 3" in msg and "tag seen 42" in msg
     assert mk.mk_step_status([2, 5, 0, 0])[0] == mk.MK_EBOUNDS
 
 
