@@ -59,6 +59,7 @@ struct Smem {
   int route_ids[16];
   int fail;
   uint64_t tw[4];      // trace: (begin, end) of the routing wait and of the data wait
+  uint64_t mk[TRACE_MARKS];  // trace: body-specific marks
 };
 
 struct Ctx {
@@ -67,6 +68,11 @@ struct Ctx {
   uint64_t t0;
   uint32_t ti;
 };
+
+// Trace mark i of the current task (no-op without a trace buffer).
+__device__ __forceinline__ void mark(Ctx& c, int i) {
+  if (c.a.trace && tid() == 0) c.s.mk[i] = now();
+}
 
 // Gather tagged words into LDS: dst[i] = value of word i for i < n, where
 // word i sits at src1 + i for i < n1 and at src2 + (i - n1) after that; MAXW
@@ -94,7 +100,7 @@ __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, co
     }
   }
   if (!ok) c.s.fail = 1;
-  __syncthreads();
+  lds_barrier();
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
   return c.s.fail == 0;
 }
@@ -103,20 +109,60 @@ __device__ __forceinline__ bool gather(Ctx& c, const uint64_t* src, int n, float
   return gather2<MAXW>(c, src, n, src, n, dst, which);
 }
 
-// In-place RMSNorm of LDS v[0..K): v = v / sqrt(mean(v^2) + eps) * g.
-// Fixed summation order (strided per thread, then waves in order).
-__device__ __forceinline__ void rmsnorm_lds(Ctx& c, float* v, int K, const uint16_t* g) {
+// Norm gains of chunk tid (elements 8*tid .. 8*tid+7) of a vector of K <=
+// 8*NT elements, loaded ahead of a task's wait.
+struct Gains {
+  uint4 g;
+  __device__ __forceinline__ void load(const uint16_t* src, int K) {
+    g = tid() < K / 8 ? *(const uint4*)(src + 8 * tid()) : make_uint4(0, 0, 0, 0);
+  }
+};
+
+// A GEMV input vector in LDS is stored in split form: chunk c (elements
+// 8c .. 8c+7) holds 4 words of hi bf16 pairs then 4 words of lo bf16 pairs
+// (split8) in place of its 8 floats. pack_lds converts fp32 v[0..K) in place;
+// rmsnorm_pack first normalises: v = v / sqrt(mean(v^2) + eps) * g (fixed
+// summation order: per chunk, then waves in order).
+__device__ __forceinline__ void pack_lds(Ctx& c, float* v, int K) {
+  for (int ch = tid(); ch < K / 8; ch += NT) {
+    float x[8];
+    *(float4*)x = *(const float4*)(v + 8 * ch);
+    *(float4*)(x + 4) = *(const float4*)(v + 8 * ch + 4);
+    uint4 hi, lo;
+    split8(x, hi, lo);
+    *(uint4*)(v + 8 * ch) = hi;
+    *(uint4*)(v + 8 * ch + 4) = lo;
+  }
+  lds_barrier();
+}
+
+__device__ __forceinline__ void rmsnorm_pack(Ctx& c, float* v, int K, const Gains& gn) {
+  const int t = tid();
+  float x[8];
   float ss = 0.f;
-  for (int i = tid(); i < K; i += NT) ss = fmaf(v[i], v[i], ss);
+  if (t < K / 8) {
+    *(float4*)x = *(const float4*)(v + 8 * t);
+    *(float4*)(x + 4) = *(const float4*)(v + 8 * t + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+  }
   ss = wave_sum(ss);
-  if ((tid() & 63) == 0) c.s.red[tid() >> 6] = ss;
-  __syncthreads();
+  if ((t & 63) == 0) c.s.red[t >> 6] = ss;
+  lds_barrier();
   float tot = 0.f;
 #pragma unroll
   for (int w = 0; w < NWAVE; ++w) tot += c.s.red[w];
   const float rs = 1.0f / sqrtf(tot / (float)K + c.a.eps);
-  for (int i = tid(); i < K; i += NT) v[i] = v[i] * rs * bf2f(g[i]);
-  __syncthreads();
+  if (t < K / 8) {
+    const uint32_t gw[4] = {gn.g.x, gn.g.y, gn.g.z, gn.g.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * rs * ((e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1]));
+    uint4 hi, lo;
+    split8(x, hi, lo);
+    *(uint4*)(v + 8 * t) = hi;
+    *(uint4*)(v + 8 * t + 4) = lo;
+  }
+  lds_barrier();
 }
 
 // ------------------------------------------------------------------ GEMV tiles
@@ -126,18 +172,18 @@ __device__ __forceinline__ void rmsnorm_lds(Ctx& c, float* v, int K, const uint1
 // CPL 16-byte chunks per lane (chunk index tc + c*TC). Loads are issued by
 // issue() before the task waits; dots() reduces each row against the LDS
 // vector and writes out[row].
-template <int CPL, int RPW>
+template <int CPL, int RPW, int TC>
 struct Tile {
+  static constexpr int G = NT / TC;
   uint4 w[RPW][CPL];
-  int nr, lg, tc, G, TC;
+  int nr, lg, tc;
 
   template <class RowPtr>
-  __device__ __forceinline__ void issue(int R, int tc_width, const RowPtr& rowptr) {
-    TC = tc_width;
-    G = NT / TC;
+  __device__ __forceinline__ void issue(int R, const RowPtr& rowptr) {
     lg = tid() / TC;
     tc = tid() % TC;
     nr = lg < R ? (R - lg + G - 1) / G : 0;
+    if (TC == 64) nr = __builtin_amdgcn_readfirstlane(nr);  // one lane group per wave
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       if (r < nr) {
@@ -146,24 +192,24 @@ struct Tile {
         for (int c = 0; c < CPL; ++c) w[r][c] = ld_nt(p + tc + c * TC);
       }
   }
+  // u: split-form input vector (see pack_lds)
   __device__ __forceinline__ void dots(const float* u, float* out) {
     float acc[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const float4* up = (const float4*)(u + (tc + c * TC) * 8);
-      const float4 p0 = up[0], p1 = up[1];
-      const float uc[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      const uint4* up = (const uint4*)(u + (tc + c * TC) * 8);
+      const uint4 uh = up[0], ul = up[1];
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
-        if (r < nr) acc[r] = dot8(w[r][c], uc, acc[r]);
+        if (r < nr) acc[r] = dot8h(w[r][c], uh, ul, acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       if (r < nr) {
-        const float s = group_sum(acc[r], TC);
-        if (tc == 0) out[lg + r * G] = s;
+        const float s = group_sum_last<TC>(acc[r]);
+        if (tc == TC - 1) out[lg + r * G] = s;
       }
   }
 };
@@ -173,18 +219,18 @@ struct Tile {
 // one 1 KB block at stage[((w * RPW + r) * CPL + c) * 64 + lane], written and
 // later read by the same lane. The caller waits for the loads (vmcnt) before
 // dots().
-template <int CPL, int RPW>
+template <int CPL, int RPW, int TC>
 struct StageTile {
-  int nr, lg, tc, G, TC, w;
+  static constexpr int G = NT / TC;
+  int nr, lg, tc, w;
 
   template <class RowPtr>
-  __device__ __forceinline__ void issue(int R, int tc_width, const RowPtr& rowptr, uint4* stage) {
-    TC = tc_width;
-    G = NT / TC;
+  __device__ __forceinline__ void issue(int R, const RowPtr& rowptr, uint4* stage) {
     lg = tid() / TC;
     tc = tid() % TC;
     w = __builtin_amdgcn_readfirstlane(tid() >> 6);
     nr = lg < R ? (R - lg + G - 1) / G : 0;
+    if (TC == 64) nr = __builtin_amdgcn_readfirstlane(nr);
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       if (r < nr) {
@@ -203,18 +249,17 @@ struct StageTile {
     for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const float4* up = (const float4*)(u + (tc + c * TC) * 8);
-      const float4 p0 = up[0], p1 = up[1];
-      const float uc[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      const uint4* up = (const uint4*)(u + (tc + c * TC) * 8);
+      const uint4 uh = up[0], ul = up[1];
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
-        if (r < nr) acc[r] = dot8(stage[((w * RPW + r) * CPL + c) * 64 + lane], uc, acc[r]);
+        if (r < nr) acc[r] = dot8h(stage[((w * RPW + r) * CPL + c) * 64 + lane], uh, ul, acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       if (r < nr) {
-        const float s = group_sum(acc[r], TC);
-        if (tc == 0) out[lg + r * G] = s;
+        const float s = group_sum_last<TC>(acc[r]);
+        if (tc == TC - 1) out[lg + r * G] = s;
       }
   }
 };
@@ -236,7 +281,7 @@ __device__ __forceinline__ bool layer_input(Ctx& c, int l, int b, float* dst) {
   if (l == 0) {
     const uint16_t* e = a.embed + (size_t)token_row(a, b) * a.H;
     for (int i = tid(); i < a.H; i += NT) dst[i] = bf2f(e[i]);
-    __syncthreads();
+    lds_barrier();
     return true;
   }
   return gather<4>(c, a.x + (size_t)(l - 1) * a.s_x + (size_t)b * a.H, a.H, dst, 1);
@@ -265,21 +310,21 @@ __device__ __forceinline__ void route(Ctx& c, const float* r) {
   const float v = t < E ? r[t] : NEG_INF;
   float m = wave_max(v);
   if ((t & 63) == 0) s.red[t >> 6] = m;
-  __syncthreads();
+  lds_barrier();
   float M = s.red[0];
 #pragma unroll
   for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, s.red[w]);
   const float ex = t < E ? expf(v - M) : 0.f;
   const float sm = wave_sum(ex);
-  __syncthreads();
+  lds_barrier();
   if ((t & 63) == 0) s.red[t >> 6] = sm;
-  __syncthreads();
+  lds_barrier();
   float S = 0.f;
 #pragma unroll
   for (int w = 0; w < NWAVE; ++w) S += s.red[w];
   const float pe = ex / S;
   if (t < E) p[t] = pe;
-  __syncthreads();
+  lds_barrier();
   if (t < E) {
     int rank = 0;
     for (int e = 0; e < E; ++e) {
@@ -291,13 +336,13 @@ __device__ __forceinline__ void route(Ctx& c, const float* r) {
       s.route_w[rank] = pe;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (t == 0 && a.norm_topk) {
     float wsum = 0.f;
     for (int j = 0; j < a.K; ++j) wsum += s.route_w[j];
     for (int j = 0; j < a.K; ++j) s.route_w[j] = s.route_w[j] / wsum;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 __device__ __forceinline__ bool routing(Ctx& c, int l, int b) {
@@ -309,39 +354,50 @@ __device__ __forceinline__ bool routing(Ctx& c, int l, int b) {
 
 // ------------------------------------------------------------------ tasks
 
-template <int CPL>
+template <int CPL, int TC>
 __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
-  constexpr int RPW = 24 / CPL < GEMV_RPW_MAX ? 24 / CPL : GEMV_RPW_MAX;
+  constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
   const KArgs& a = c.a;
   const int l = t.layer, g = t.a0, p0 = t.a1, np = t.a2, nj = 2 * np;
   const int H = a.H, D = a.D;
   const int QR = (a.Hq + 2 * a.Hkv) * D;
   const uint16_t* W = a.wqkv + (size_t)l * QR * H;
-  Tile<CPL, RPW> tile;
-  tile.issue(nj, (H / 8) / CPL, [&](int j) {
+  Tile<CPL, RPW, TC> tile;
+  tile.issue(nj, [&](int j) {
     int head, i, row;
     qkv_pair(p0 + (j >> 1), g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
     return (const uint4*)(W + (size_t)(row + (j & 1) * (D / 2)) * H);
   });
-  if (!layer_input(c, l, 0, c.s.vec)) return false;
-  rmsnorm_lds(c, c.s.vec, H, a.attn_norm + (size_t)l * H);
-  tile.dots(c.s.vec, c.s.out);
-  __syncthreads();
+  Gains gn;
+  gn.load(a.attn_norm + (size_t)l * H, H);
+  // the step's position, its page and rotation: independent of other tasks, loaded ahead
   const int pos = a.seq_lens[0];
   const bool in_bounds = pos >= 0 && pos + 1 <= a.bound && pos < a.n_rope;
-  int32_t phys = -1;
-  if (in_bounds) phys = a.page_table[pos >> 4];
+  const int pc = in_bounds ? pos : 0;
+  const int32_t phys = a.page_table[pc >> 4];
+  const int q_me = tid();
+  float cs = 1.f, sn = 0.f;
+  int head = 0, i = 0, row = 0, sec = 2;
+  if (q_me < np) {
+    sec = qkv_pair(p0 + q_me, g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
+    if (sec < 2) {
+      cs = a.rope_cos[(size_t)pc * (D / 2) + i];
+      sn = a.rope_sin[(size_t)pc * (D / 2) + i];
+    }
+  }
+  if (!layer_input(c, l, 0, c.s.vec)) return false;
+  mark(c, 0);
+  rmsnorm_pack(c, c.s.vec, H, gn);
+  mark(c, 1);
+  tile.dots(c.s.vec, c.s.out);
+  lds_barrier();
+  mark(c, 2);
   const bool page_ok = in_bounds && phys >= 0 && phys < a.n_pages;
   if (!page_ok && tid() == 0) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)pos, (uint32_t)phys);
-  for (int q = tid(); q < np; q += NT) {
-    const float y0 = c.s.out[2 * q], y1 = c.s.out[2 * q + 1];
-    int head, i, row;
-    const int sec = qkv_pair(p0 + q, g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
-    const int pc = page_ok ? pos : 0;
+  if (q_me < np) {  // np <= NT: one rotary pair per thread
+    const float y0 = c.s.out[2 * q_me], y1 = c.s.out[2 * q_me + 1];
     float r0 = y0, r1 = y1;
     if (sec < 2) {
-      const float cs = a.rope_cos[(size_t)pc * (D / 2) + i];
-      const float sn = a.rope_sin[(size_t)pc * (D / 2) + i];
       r0 = y0 * cs - y1 * sn;
       r1 = y1 * cs + y0 * sn;
     }
@@ -383,19 +439,22 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   const int HG = a.HG;
   const int lane = tid() & 63, w = tid() >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
+  const int32_t* prow = a.page_table + (size_t)b * a.max_pages;
+  // this wave's first two page ids, read together with the position (the
+  // plan maps every page below its bound)
+  const int first = pg0 + w;
+  const int32_t ph0 = first < pg0 + npg ? prow[first] : -1;
+  const int32_t ph1 = first + NWAVE < pg0 + npg ? prow[first + NWAVE] : -1;
   const int pos = a.seq_lens[b];
   const int n_tok = min(pos + 1, a.bound);
   const int pg_lim = min(pg0 + npg, (n_tok + 15) >> 4);
-  const int first = pg0 + w;
   const int cnt = first < pg_lim ? (pg_lim - first + NWAVE - 1) / NWAVE : 0;
   const int cur = pos >> 4, ns = pos & 15;
   const uint16_t* lbase = a.pool + (size_t)l * a.layer_stride + (size_t)g * 2 * 16 * D;
-  const int32_t* prow = a.page_table + (size_t)b * a.max_pages;
   uint4 k0[NK4], k1[NK4];
   uint2 v0[NB], v1[NB];
   bool bad = false;
-  auto load = [&](uint4 (&kk)[NK4], uint2 (&vv)[NB], int pg) {
-    const int32_t phys = prow[pg];
+  auto load = [&](uint4 (&kk)[NK4], uint2 (&vv)[NB], int pg, int32_t phys) {
     if (phys < 0 || phys >= a.n_pages) {
       bad = true;
 #pragma unroll
@@ -412,15 +471,17 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) vv[nb] = ld_nt2((const uint2*)(vp + nb * 256));
   };
-  if (cnt > 0) load(k0, v0, first);
-  if (cnt > 1) load(k1, v1, first + NWAVE);
+  if (cnt > 0) load(k0, v0, first, ph0);
+  if (cnt > 1) load(k1, v1, first + NWAVE, ph1);
 
   // inputs: the group's queries and the new token's K and V (bf16 bits), one batch
   float* qv = s.vec;                 // [HG][D]
   float* kvnew = s.vec + HG * D;     // [2][D]
   const uint64_t* qsrc = a.q + (size_t)l * a.s_q + ((size_t)b * a.Hq + (size_t)g * HG) * D;
   const uint64_t* ksrc = a.kvn + (size_t)l * a.s_kvn + ((size_t)b * a.Hkv + g) * 2 * D;
+  mark(c, 0);
   if (!gather2<3>(c, qsrc, HG * D, ksrc, HG * D + 2 * D, qv, 1)) return false;
+  mark(c, 1);
 
   // query operand: column r16 < 8 carries bf16(q) of head r16, column
   // r16 >= 8 the bf16 residual q - bf16(q) of head r16 - 8
@@ -525,14 +586,16 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, __builtin_bit_cast(v4s, vm), acc[nb], 0, 0, 0);
     }
   };
-  for (int i = 0; i < cnt; i += 2) {
+  // page i of this wave is in (k0, v0), page i + 1 in flight in (k1, v1)
+  for (int i = 0; i < cnt; ++i) {
     compute(k0, v0, first + i * NWAVE);
-    if (i + 2 < cnt) load(k0, v0, first + (i + 2) * NWAVE);
-    if (i + 1 < cnt) {
-      compute(k1, v1, first + (i + 1) * NWAVE);
-      if (i + 3 < cnt) load(k1, v1, first + (i + 3) * NWAVE);
-    }
+#pragma unroll
+    for (int q = 0; q < NK4; ++q) k0[q] = k1[q];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) v0[q] = v1[q];
+    if (i + 2 < cnt) load(k1, v1, first + (i + 2) * NWAVE, prow[first + (i + 2) * NWAVE]);
   }
+  mark(c, 2);
   if (bad && lane == 0) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)b, 0xFFFFFFFFu);
   // merge hi/lo rows and publish this wave's partial in LDS
   float* Ow = s.att;                      // [NWAVE][HG][D]
@@ -550,28 +613,41 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     mw[w * 8 + lane] = m_run;
     lw[w * 8 + lane] = l_run;
   }
-  __syncthreads();
+  lds_barrier();
+  mark(c, 3);
+  // per-head merge scales over the waves: ew[q][head] = exp(m_q - M), M = max_q m_q
+  float* ew = s.out + 64;  // [NWAVE][8]
+  float* mm = s.out + 128; // [8] (M, then L)
+  if (tid() < 8) {
+    const int head = tid();
+    float M = NEG_INF;
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) M = fmaxf(M, mw[q * 8 + head]);
+    float LL = 0.f;
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) {
+      const float m = mw[q * 8 + head];
+      const float e = m == NEG_INF ? 0.f : expf(m - M);
+      ew[q * 8 + head] = e;
+      LL += e * lw[q * 8 + head];
+    }
+    mm[head] = M;
+    mm[8 + head] = LL;
+  }
+  lds_barrier();
   const int PS = D + 2;
   uint64_t* dst0 = a.part + (size_t)l * a.s_part +
                    (((size_t)b * a.Hkv + g) * a.S_max + split) * HG * PS;
   for (int idx = tid(); idx < HG * D; idx += NT) {
     const int head = idx / D, dim = idx % D;
-    float M = NEG_INF;
+    float oo = 0.f;
 #pragma unroll
-    for (int q = 0; q < NWAVE; ++q) M = fmaxf(M, mw[q * 8 + head]);
-    float oo = 0.f, LL = 0.f;
-#pragma unroll
-    for (int q = 0; q < NWAVE; ++q) {
-      const float m = mw[q * 8 + head];
-      const float e = m == NEG_INF ? 0.f : expf(m - M);
-      oo += e * Ow[(q * HG + head) * D + dim];
-      LL += e * lw[q * 8 + head];
-    }
+    for (int q = 0; q < NWAVE; ++q) oo += ew[q * 8 + head] * Ow[(q * HG + head) * D + dim];
     uint64_t* dst = dst0 + (size_t)head * PS;
     st_tagged(dst + dim, oo, a.epoch);
     if (dim == 0) {
-      st_tagged(dst + D, M, a.epoch);
-      st_tagged(dst + D + 1, LL, a.epoch);
+      st_tagged(dst + D, mm[head], a.epoch);
+      st_tagged(dst + D + 1, mm[8 + head], a.epoch);
     }
   }
   return true;
@@ -609,7 +685,7 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
     }
   }
   if (!ok) s.fail = 1;
-  __syncthreads();
+  lds_barrier();
   if (a.trace && tid() == 0) s.tw[3] = now();
   if (s.fail) return false;
   float* cs = s.out;  // [S] merge weights
@@ -629,14 +705,14 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
       cs[q] = (mq == NEG_INF || L == 0.f) ? 0.f : expf(mq - M) / L;
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int NG = NT / nd, sg = tid() / nd, dim = tid() % nd;
   float acc = 0.f;
   if (sg < NG)
     for (int q = sg; q < S; q += NG) acc += cs[q] * sw[q * W + dim];
   float* red = s.out + 1024;
   if (sg < NG) red[sg * nd + dim] = acc;
-  __syncthreads();
+  lds_barrier();
   if (tid() < nd) {
     float o = 0.f;
     for (int q = 0; q < NG; ++q) o += red[q * nd + tid()];
@@ -645,15 +721,15 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   return true;
 }
 
-template <int CPL>
+template <int CPL, int TC>
 __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
-  constexpr int RPW = 24 / CPL < GEMV_RPW_MAX ? 24 / CPL : GEMV_RPW_MAX;
+  constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
   const KArgs& a = c.a;
   const int l = t.layer, r0 = t.a1, n = t.a2;
   const int H = a.H, K = a.Hq * a.D;
   const uint16_t* W = a.wo + (size_t)l * H * K;
-  Tile<CPL, RPW> tile;
-  tile.issue(n, (K / 8) / CPL, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * K); });
+  Tile<CPL, RPW, TC> tile;
+  tile.issue(n, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * K); });
   // residual rows (layer input, complete once o is): loaded ahead of the wait
   const int th = tid();
   uint64_t rw = 0;
@@ -662,8 +738,9 @@ __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
     else rw = ld_tagged(a.x + (size_t)(l - 1) * a.s_x + r0 + th);
   }
   if (!gather<8>(c, a.o + (size_t)l * a.s_o, K, c.s.vec, 1)) return false;
+  pack_lds(c, c.s.vec, K);
   tile.dots(c.s.vec, c.s.out);
-  __syncthreads();
+  lds_barrier();
   bool fail = false;
   if (th < n) {
     const float x = tag_is(rw, a.epoch) ? tag_value(rw) : resid(c, l, 0, r0 + th, &fail);
@@ -676,18 +753,20 @@ __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
   return !fail;
 }
 
-template <int CPL>
+template <int CPL, int TC>
 __device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
-  constexpr int RPW = 24 / CPL < GEMV_RPW_MAX ? 24 / CPL : GEMV_RPW_MAX;
+  constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
   const KArgs& a = c.a;
   const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H;
   const uint16_t* W = a.router + (size_t)l * a.E * H;
-  Tile<CPL, RPW> tile;
-  tile.issue(n, (H / 8) / CPL, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
+  Tile<CPL, RPW, TC> tile;
+  tile.issue(n, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
+  Gains gn;
+  gn.load(a.ffn_norm + (size_t)l * H, H);
   if (!gather<4>(c, a.xa + (size_t)l * a.s_x, H, c.s.vec, 1)) return false;
-  rmsnorm_lds(c, c.s.vec, H, a.ffn_norm + (size_t)l * H);
+  rmsnorm_pack(c, c.s.vec, H, gn);
   tile.dots(c.s.vec, c.s.out);
-  __syncthreads();
+  lds_barrier();
   for (int j = tid(); j < n; j += NT)
     st_tagged(a.rlog + (size_t)l * a.s_rlog + r0 + j, c.s.out[j], a.epoch);
   return true;
@@ -699,18 +778,25 @@ __device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
 // the down projection stream into LDS; then read every slot's activations and
 // finish its hidden rows: x = x_attn + sum_j w_j * W_down[e_j] a_j (fixed j
 // order). Dense FFN: one slot, expert 0, weight 1.
-template <int CH, int CF>
+template <int CH, int TCH, int CF, int TCF>
 __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
-  constexpr int RPW_G = 24 / CH < GEMV_RPW_MAX ? 24 / CH : GEMV_RPW_MAX;
+  constexpr int RPW_G = GEMV_REG_CHUNKS / CH < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CH : GEMV_RPW_MAX;
   constexpr int RPW_D = STAGE_CHUNKS / CF < GEMV_RPW_MAX ? STAGE_CHUNKS / CF : GEMV_RPW_MAX;
   const KArgs& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, slot = t.aux, f0 = t.a1, nf = t.a2;
   const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
   const int H = a.H, F = a.F, KK = a.dense ? 1 : a.K, EE = a.dense ? 1 : a.E;
-  const int TCH = (H / 8) / CH, TCF = (F / 8) / CF;
+  Gains gn;
+  gn.load(a.ffn_norm + (size_t)l * H, H);
+  const uint64_t* xa = a.xa + (size_t)l * a.s_x + (size_t)b * H;
+  // the router logits and the normalised hidden state in one batch: s.vec =
+  // [x_attn (H) | logits (E)]
+  float* lg_ = s.vec + H;
   if (!a.dense) {
-    if (!routing(c, l, b)) return false;
+    if (!gather2<5>(c, xa, H, a.rlog + (size_t)l * a.s_rlog + (size_t)b * a.E, H + a.E, s.vec, 0))
+      return false;
+    route(c, lg_);
     if ((t.flags & TF_WRITE_TOPK) && tid() < a.K) {
       if (a.topk_ids) a.topk_ids[(size_t)l * a.K + tid()] = s.route_ids[tid()];
       if (a.topk_w) a.topk_w[(size_t)l * a.K + tid()] = s.route_w[tid()];
@@ -720,63 +806,74 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
       s.route_ids[0] = 0;
       s.route_w[0] = 1.f;
     }
-    __syncthreads();
+    if (!gather<4>(c, xa, H, s.vec, 0)) return false;
   }
+  mark(c, 0);
+  for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
+  rmsnorm_pack(c, s.vec, H, gn);  // before the weight loads: the gains are not waited behind them
   const int e = s.route_ids[slot];
   const uint16_t* Wg = a.gate + ((size_t)l * EE + e) * F * H;
   const uint16_t* Wu = a.up + ((size_t)l * EE + e) * F * H;
   const uint16_t* Wd = a.down + (size_t)l * EE * H * F;
-  const uint64_t* xa = a.xa + (size_t)l * a.s_x + (size_t)b * H;
-  // gate/up part, in register tiles of capg FFN rows (one tile in the usual plan)
-  const int capg = (NT / TCH) * RPW_G / 2;
-  bool have_x = false;
+  const int capg = (NT / TCH) * RPW_G / 2;   // FFN rows per register tile
+  const int capd = (NT / TCF) * RPW_D / KK;  // hidden rows per staged tile
+  // In the usual plan each part is one tile: the gate/up rows go to registers
+  // and the down rows to LDS back to back, so the down rows stream while the
+  // gate/up rows are used; the dots wait only for the loads they read.
+  Tile<CH, RPW_G, TCH> gu;
+  StageTile<CF, RPW_D, TCF> dn;
+  const bool one_g = nf <= capg, one_d = nr <= capd;
+  if (nf > 0)
+    gu.issue(2 * min(nf, capg), [&](int j) {
+      return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + (j >> 1)) * H);
+    });
+  if (one_g && one_d && nr > 0)
+    dn.issue(nr * KK, [&](int j) {
+      return (const uint4*)(Wd + ((size_t)s.route_ids[j % KK] * H + r0 + j / KK) * F);
+    }, s.stage);
+  mark(c, 1);
   for (int fc = 0; fc < nf; fc += capg) {
     const int nfc = min(capg, nf - fc);
-    Tile<CH, RPW_G> gu;
-    gu.issue(2 * nfc, TCH, [&](int j) {
-      return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + fc + (j >> 1)) * H);
-    });
-    if (!have_x) {
-      if (!gather<4>(c, xa, H, s.vec, 1)) return false;
-      for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
-      rmsnorm_lds(c, s.vec, H, a.ffn_norm + (size_t)l * H);
-      have_x = true;
-    }
+    if (fc > 0)
+      gu.issue(2 * nfc, [&](int j) {
+        return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + fc + (j >> 1)) * H);
+      });
     gu.dots(s.vec, s.out);
-    __syncthreads();
+    lds_barrier();
+    mark(c, 3);
     uint64_t* act = a.act + (size_t)l * a.s_act + ((size_t)b * KK + slot) * F + f0 + fc;
     for (int q = tid(); q < nfc; q += NT) {
       const float yg = s.out[2 * q], yu = s.out[2 * q + 1];
       st_tagged(act + q, yg / (1.0f + expf(-yg)) * yu, a.epoch);
     }
-    __syncthreads();
+    lds_barrier();
   }
+  mark(c, 4);
   if (nr == 0) return true;
-  if (!have_x) {
-    if (!gather<4>(c, xa, H, s.vec, 1)) return false;
-    for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
-    __syncthreads();
-  }
   // down part: job j = (hidden row j / KK, slot j % KK); a lane group's slot
   // is fixed because the number of lane groups is a multiple of KK
-  const int capd = (NT / TCF) * RPW_D / KK;
   for (int rc = 0; rc < nr; rc += capd) {
     const int nrc = min(capd, nr - rc);
-    StageTile<CF, RPW_D> dn;
-    dn.issue(nrc * KK, TCF, [&](int j) {
-      return (const uint4*)(Wd + ((size_t)s.route_ids[j % KK] * H + r0 + rc + j / KK) * F);
-    }, s.stage);
-    if (rc == 0 && !gather<12>(c, a.act + (size_t)l * a.s_act + (size_t)b * KK * F, KK * F, s.vec, 1))
-      return false;
+    if (!(one_g && one_d))
+      dn.issue(nrc * KK, [&](int j) {
+        return (const uint4*)(Wd + ((size_t)s.route_ids[j % KK] * H + r0 + rc + j / KK) * F);
+      }, s.stage);
+    if (rc == 0) {
+      if (!gather<12>(c, a.act + (size_t)l * a.s_act + (size_t)b * KK * F, KK * F, s.vec, 1)) return false;
+      pack_lds(c, s.vec, KK * F);
+    }
+    mark(c, 5);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct-to-LDS loads
+    mark(c, 6);
     dn.dots(s.stage, s.vec + (size_t)(dn.lg % KK) * F, s.out);
-    __syncthreads();
+    lds_barrier();
+    mark(c, 7);
     for (int q = tid(); q < nrc; q += NT) {
       float y = 0.f;
       for (int j = 0; j < KK; ++j) y += s.route_w[j] * s.out[q * KK + j];
       st_tagged(a.x + (size_t)l * a.s_x + (size_t)b * H + r0 + rc + q, s.res[rc + q] + y, a.epoch);
     }
-    __syncthreads();
+    lds_barrier();
   }
   return true;
 }
@@ -785,16 +882,16 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
 // LM_BATCH rows per lane group; every lane group walks the same number of
 // batches (rows past the tile's end re-read its last row and are ignored), so
 // the loop issues its loads unconditionally.
-template <int CPL>
+template <int CPL, int TC>
 __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
+  constexpr int G = NT / TC;
   const KArgs& a = c.a;
   Smem& s = c.s;
   const int r0 = t.a1, n = t.a2, H = a.H;
-  const int TC = (H / 8) / CPL, G = NT / TC;
   const int lg = tid() / TC, tc = tid() % TC;
   const int per = (n + G - 1) / G;                       // rows per lane group
   int nb = (per + LM_BATCH - 1) / LM_BATCH;
-  nb = nb < 2 ? 2 : nb + (nb & 1);                       // even, >= 2
+  nb = nb < 2 ? 2 : nb;                                  // >= 2 (two batches are issued up front)
   uint4 A[LM_BATCH][CPL], Bf[LM_BATCH][CPL];
   auto row_of = [&](int bi, int r) { return min(lg + (bi * LM_BATCH + r) * G, n - 1); };
   auto issue = [&](uint4 (&w)[LM_BATCH][CPL], int bi) {
@@ -805,34 +902,35 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
       for (int cc = 0; cc < CPL; ++cc) w[r][cc] = ld_nt(p + tc + cc * TC);
     }
   };
-  float uu[CPL * 8];
-  auto consume = [&](uint4 (&w)[LM_BATCH][CPL], int bi) {
+  issue(A, 0);
+  issue(Bf, 1);
+  Gains gn;
+  gn.load(a.final_norm, H);
+  if (!gather<4>(c, a.x + (size_t)(a.L - 1) * a.s_x, H, s.vec, 1)) return false;
+  rmsnorm_pack(c, s.vec, H, gn);
+  uint4 uh[CPL], ul[CPL];
+#pragma unroll
+  for (int cc = 0; cc < CPL; ++cc) {
+    uh[cc] = ((const uint4*)(s.vec + (tc + cc * TC) * 8))[0];
+    ul[cc] = ((const uint4*)(s.vec + (tc + cc * TC) * 8))[1];
+  }
+  // batch bi is in A; batch bi + 1 is in flight in Bf
+  for (int bi = 0; bi < nb; ++bi) {
 #pragma unroll
     for (int r = 0; r < LM_BATCH; ++r) {
       float sum = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) sum = dot8(w[r][cc], uu + cc * 8, sum);
-      sum = group_sum(sum, TC);
-      if (tc == 0) s.out[row_of(bi, r)] = sum;
+      for (int cc = 0; cc < CPL; ++cc) sum = dot8h(A[r][cc], uh[cc], ul[cc], sum);
+      sum = group_sum_last<TC>(sum);
+      if (tc == TC - 1) s.out[row_of(bi, r)] = sum;
     }
-  };
-  issue(A, 0);
-  issue(Bf, 1);
-  if (!gather<4>(c, a.x + (size_t)(a.L - 1) * a.s_x, H, s.vec, 1)) return false;
-  rmsnorm_lds(c, s.vec, H, a.final_norm);
 #pragma unroll
-  for (int cc = 0; cc < CPL; ++cc)
+    for (int r = 0; r < LM_BATCH; ++r)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) uu[cc * 8 + e] = s.vec[(tc + cc * TC) * 8 + e];
-  for (int bi = 0; bi + 2 < nb; bi += 2) {
-    consume(A, bi);
-    issue(A, bi + 2);
-    consume(Bf, bi + 1);
-    issue(Bf, bi + 3);
+      for (int cc = 0; cc < CPL; ++cc) A[r][cc] = Bf[r][cc];
+    if (bi + 2 < nb) issue(Bf, bi + 2);
   }
-  consume(A, nb - 2);
-  consume(Bf, nb - 1);
-  __syncthreads();
+  lds_barrier();
   float bv = NEG_INF;
   int bi = 0x7fffffff;
   for (int j = tid(); j < n; j += NT) {
@@ -849,7 +947,7 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
   float* rv = s.red;
   int* ri = (int*)(s.red + NWAVE);
   if ((tid() & 63) == 0) { rv[tid() >> 6] = bv; ri[tid() >> 6] = bi; }
-  __syncthreads();
+  lds_barrier();
   if (tid() == 0) {
     for (int q = 1; q < NWAVE; ++q)
       if (rv[q] > bv || (rv[q] == bv && ri[q] < bi)) { bv = rv[q]; bi = ri[q]; }
@@ -880,7 +978,7 @@ __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
   float* rv = s.red;
   int* ri = (int*)(s.red + NWAVE);
   if ((tid() & 63) == 0) { rv[tid() >> 6] = bv; ri[tid() >> 6] = bi; }
-  __syncthreads();
+  lds_barrier();
   if (tid() == 0) {
     for (int q = 1; q < NWAVE; ++q)
       if (rv[q] > bv || (rv[q] == bv && ri[q] < bi)) { bv = rv[q]; bi = ri[q]; }
@@ -892,9 +990,10 @@ __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
 
 // One kernel per shape class: CH, CO, CF are the 16-byte chunks per lane of
 // the GEMVs over the hidden size, the attention output (query heads x head
-// dim) and the FFN width; HD is the head dim. Each variant contains only the
+// dim) and the FFN width, TCH, TCO, TCF their lane-group widths; HD is the
+// head dim. Each variant contains only the
 // task bodies its shapes use, so registers are allocated for them alone.
-template <int CH, int CO, int CF, int HD>
+template <int CH, int TCH, int CO, int TCO, int CF, int TCF, int HD>
 __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
   __shared__ Smem s;
   const uint32_t* hdr = a.plan;
@@ -902,26 +1001,29 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
   const Task* tasks = (const Task*)((const char*)a.plan + hdr[H_TASK_OFF_BYTES]);
   const uint32_t beg = off[blockIdx.x], end = off[blockIdx.x + 1];
   if (tid() == 0) s.fail = 0;
-  __syncthreads();
+  lds_barrier();
   for (uint32_t ti = beg; ti < end; ++ti) {
     const Task t = tasks[ti];
     Ctx c{a, s, now(), ti};
-    if (a.trace && tid() == 0) s.tw[0] = s.tw[1] = s.tw[2] = s.tw[3] = 0;
+    if (a.trace && tid() == 0) {
+      s.tw[0] = s.tw[1] = s.tw[2] = s.tw[3] = 0;
+      for (int i = 0; i < TRACE_MARKS; ++i) s.mk[i] = 0;
+    }
     bool ok = true;
     switch (t.op) {
-      case OP_QKV: ok = task_qkv<CH>(c, t); break;
+      case OP_QKV: ok = task_qkv<CH, TCH>(c, t); break;
       case OP_ATTN: ok = task_attn<HD>(c, t); break;
       case OP_COMB: ok = task_comb(c, t); break;
-      case OP_O: ok = task_o<CO>(c, t); break;
-      case OP_ROUTER: ok = task_router<CH>(c, t); break;
-      case OP_EXPERT: ok = task_expert<CH, CF>(c, t); break;
-      case OP_LM: ok = task_lm<CH>(c, t); break;
+      case OP_O: ok = task_o<CO, TCO>(c, t); break;
+      case OP_ROUTER: ok = task_router<CH, TCH>(c, t); break;
+      case OP_EXPERT: ok = task_expert<CH, TCH, CF, TCF>(c, t); break;
+      case OP_LM: ok = task_lm<CH, TCH>(c, t); break;
       case OP_FINAL: ok = task_final(c, t); break;
       default: break;
     }
     if (!ok) return;  // uniform: the failure was recorded in the status words
     const uint64_t t_body = (a.trace && tid() == 0) ? now() : 0;
-    __syncthreads();  // LDS is reused by the next task
+    lds_barrier();  // LDS is reused by the next task
     if (tid() == 0) {
       if (t.signal != NO_CTR)
         __hip_atomic_fetch_add(a.ctr + ((size_t)t.signal * CTR_LINES + blockIdx.x % CTR_LINES) * CTR_STRIDE,
@@ -933,6 +1035,7 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
         tr[5] = t_body;
         tr[6] = now();
         tr[7] = ((uint64_t)blockIdx.x << 32) | ((uint64_t)t.op << 16) | t.layer;
+        for (int i = 0; i < TRACE_MARKS; ++i) tr[8 + i] = s.mk[i];
       }
     }
   }
@@ -941,9 +1044,9 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
 // Kernel variants, indexed by mk::kernel_class (see mk_internal.hpp).
 const void* kernel_for(int cls) {
   switch (cls) {
-    case 0: return (const void*)megakernel<1, 1, 1, 64>;    // hidden 256, 4x64 heads, FFN 512
-    case 1: return (const void*)megakernel<2, 2, 1, 64>;    // hidden 1024, 16x64 heads, FFN 512
-    case 2: return (const void*)megakernel<4, 8, 3, 128>;   // hidden 2048, 32x128 heads, FFN 768
+    case 0: return (const void*)megakernel<1, 32, 1, 32, 1, 64, 64>;   // hidden 256, 4x64 heads, FFN 512
+    case 1: return (const void*)megakernel<2, 64, 2, 64, 1, 64, 64>;   // hidden 1024, 16x64 heads, FFN 512
+    case 2: return (const void*)megakernel<4, 64, 8, 64, 3, 32, 128>;  // hidden 2048, 32x128 heads, FFN 768
     default: return nullptr;
   }
 }
@@ -1050,7 +1153,7 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
   a.timeout_ticks = (uint64_t)(timeout_ms ? timeout_ms : 2000) * 100000ull;
   if (bu->trace) {
     if (bu->trace_bytes < p->n_tasks * mk::TRACE_WORDS * sizeof(uint64_t))
-      return fail(MK_EINVAL, "mk_decode_step: trace buffer smaller than 64 bytes per task");
+      return fail(MK_EINVAL, "mk_decode_step: trace buffer smaller than 128 bytes per task");
     a.trace = bu->trace;
   }
 

@@ -27,6 +27,15 @@ __device__ __forceinline__ int tid() {
 
 __device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
 
+// Workgroup barrier for LDS traffic only. Waves of a workgroup share data
+// through LDS alone (global data between tasks is synchronised by its tags),
+// so a wave need only finish its own LDS accesses before the barrier. A full
+// __syncthreads() would also wait for every outstanding global load, including
+// weight and direct-to-LDS prefetches that are meant to stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // streaming (non-temporal) loads for data read once per step
 __device__ __forceinline__ uint4 ld_nt(const uint4* p) {
   const u4v v = __builtin_nontemporal_load((const u4v*)p);
@@ -59,9 +68,37 @@ __device__ __forceinline__ float dot8(const uint4 w, const float* u, float s) {
   return s;
 }
 
-template <int CTRL>
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Dot of 8 bf16 weights (one 16-byte chunk) with 8 activations given as a
+// hi/lo bf16 split (uh = bf16(u), ul = bf16(u - uh), two per 32-bit word in
+// element order): each bf16 x bf16 product is exact in fp32 and u - uh - ul is
+// below 2^-18 |u|, so this equals an fp32 dot to within fp32 accumulation.
+__device__ __forceinline__ float dot8h(const uint4 w, const uint4 uh, const uint4 ul, float s) {
+#define MK_DOT2(a, b) s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), s, false)
+  MK_DOT2(w.x, uh.x); MK_DOT2(w.x, ul.x);
+  MK_DOT2(w.y, uh.y); MK_DOT2(w.y, ul.y);
+  MK_DOT2(w.z, uh.z); MK_DOT2(w.z, ul.z);
+  MK_DOT2(w.w, uh.w); MK_DOT2(w.w, ul.w);
+#undef MK_DOT2
+  return s;
+}
+
+// hi/lo bf16 split of 8 floats: words (hi of u[2j] | hi of u[2j+1] << 16), then lo.
+__device__ __forceinline__ void split8(const float* u, uint4& hi, uint4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f2bf(u[e]);
+    l[e] = f2bf(u[e] - bf2f(h[e]));
+  }
+  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
 }
 // Sum over each row of 16 lanes; every lane of the row gets the sum.
 __device__ __forceinline__ float row16_sum(float v) {
@@ -71,14 +108,20 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x140>(v);  // row_mirror
   return v;
 }
-// Sum over aligned groups of `width` (32 or 64) lanes; every lane gets its group's sum.
-__device__ __forceinline__ float group_sum(float v, int width) {
+// Sum over aligned groups of TC (32 or 64) lanes, all in DPP (no LDS
+// crossbar): the group's sum is valid in its last lane (tc == TC - 1).
+template <int TC>
+__device__ __forceinline__ float group_sum_last(float v) {
   v = row16_sum(v);
-  v += __shfl_xor(v, 16, 64);
-  if (width == 64) v += __shfl_xor(v, 32, 64);
+  v += dpp<0x142, 0xA>(v);                    // row_bcast:15 into rows 1 and 3
+  if (TC == 64) v += dpp<0x143, 0xC>(v);      // row_bcast:31 into rows 2 and 3
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
+// Sum over the wave, returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  const float s = group_sum_last<64>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -134,9 +177,8 @@ __device__ __forceinline__ float get_tagged(const KArgs& a, const uint64_t* p, u
 
 // Read up to MAXW tagged words of this thread, word k at addr(k) (nullptr:
 // none), into out[k]. All loads are in flight together; while some words are
-// stale the thread spins on its first stale word alone (one load per round)
-// and then re-reads the stale set as one batch, so a consumer that starts
-// early adds little traffic and one that starts late pays one round trip.
+// stale the thread re-reads the stale set (again all in flight) after a short
+// sleep, so a word is seen within one round trip of its store landing.
 // Returns false on deadline or another workgroup's failure.
 template <int MAXW, class Addr>
 __device__ __forceinline__ bool read_words(const KArgs& a, const Addr& addr, float* out, uint64_t t0,
@@ -153,34 +195,22 @@ __device__ __forceinline__ bool read_words(const KArgs& a, const Addr& addr, flo
   for (int k = 0; k < MAXW; ++k) stale |= tag_is(w[k], ep) ? 0u : (1u << k);
   uint32_t it = 0;
   while (stale) {
-    // spin on the first stale word
-#pragma unroll
-    for (int k = 0; k < MAXW; ++k) {
-      if (stale & (1u << k)) {
-        const uint64_t* p = addr(k);
-        while (true) {
-          __builtin_amdgcn_s_sleep(1);
-          w[k] = ld_tagged(p);
-          if (tag_is(w[k], ep)) break;
-          if ((++it & 63u) == 0u) {
-            if (aborted(a)) return false;
-            if (now() - t0 > a.timeout_ticks) {
-              raise_status(a, DS_TIMEOUT, task, (uint32_t)(p - a.x), (uint32_t)(w[k] >> 32));
-              return false;
-            }
-          }
-        }
-        stale &= ~(1u << k);
-        break;
-      }
-    }
-    // then re-read the rest of the stale set together
+    // re-read the whole stale set each round, all loads in flight together
+    __builtin_amdgcn_s_sleep(2);
 #pragma unroll
     for (int k = 0; k < MAXW; ++k)
       if (stale & (1u << k)) w[k] = ld_tagged(addr(k));
 #pragma unroll
     for (int k = 0; k < MAXW; ++k)
       if ((stale & (1u << k)) && tag_is(w[k], ep)) stale &= ~(1u << k);
+    if (stale && (++it & 31u) == 0u) {
+      if (aborted(a)) return false;
+      if (now() - t0 > a.timeout_ticks) {
+        const int k = __builtin_ctz(stale);
+        raise_status(a, DS_TIMEOUT, task, (uint32_t)k, 0xFFFFFFFFu);
+        return false;
+      }
+    }
   }
 #pragma unroll
   for (int k = 0; k < MAXW; ++k) out[k] = tag_value(w[k]);

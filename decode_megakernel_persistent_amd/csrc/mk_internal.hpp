@@ -68,8 +68,10 @@ constexpr int NWAVE = NT / 64;
 
 // Per-task trace record (u64 words, constant 100 MHz clock): task start,
 // routing wait begin/end, data wait begin/end (0 where the task has no such
-// wait), body end, task end, and (cu << 32 | op << 16 | layer).
-constexpr int TRACE_WORDS = 8;
+// wait), body end, task end, (cu << 32 | op << 16 | layer), then 8 marks a
+// task body may set at points of its own (0 = unset).
+constexpr int TRACE_WORDS = 16;
+constexpr int TRACE_MARKS = 8;
 
 // Status words written by the device on failure.
 enum DevStatus : uint32_t { DS_OK = 0, DS_TIMEOUT = 1, DS_BOUNDS = 2 };
@@ -104,7 +106,7 @@ MK_HD inline bool gemv_map(int K, int* tc, int* cpl) {
 // Lane groups of a workgroup for lane-group width tc.
 MK_HD inline int gemv_groups(int tc) { return NWAVE * (64 / tc); }
 // Most 16-byte chunks a lane may hold for a prefetched GEMV tile.
-constexpr int GEMV_REG_CHUNKS = 24;
+constexpr int GEMV_REG_CHUNKS = 28;
 constexpr int GEMV_RPW_MAX = 8;   // rows per lane group of a prefetched tile
 
 // Rows of W_qkv are taken by kv group and rotary pair: group g owns the q
@@ -124,13 +126,17 @@ MK_HD inline int qkv_pair(int p, int g, int HG, int D, int Hq, int Hkv, int* hea
 }
 
 // Kernel variants: the megakernel is compiled once per shape class, given by
-// the 16-byte chunks per lane of the GEMVs over the hidden size (ch), the
-// attention output (co) and the FFN width (cf), and the head dim. Returns the
-// class index, or -1 when no variant is compiled for the shape.
-MK_HD inline int kernel_class(int ch, int co, int cf, int head_dim) {
-  if (ch == 1 && co == 1 && cf == 1 && head_dim == 64) return 0;
-  if (ch == 2 && co == 2 && cf == 1 && head_dim == 64) return 1;
-  if (ch == 4 && co == 8 && cf == 3 && head_dim == 128) return 2;
+// the GEMV mappings (lane-group width, 16-byte chunks per lane) of the
+// hidden size, the attention output (query heads x head dim) and the FFN
+// width, and the head dim. Returns the class index, or -1 when no variant is
+// compiled for the shape.
+MK_HD inline int kernel_class(int hidden, int attn_out, int ffn, int head_dim) {
+  int th, ch, to, co, tf, cf;
+  if (!gemv_map(hidden, &th, &ch) || !gemv_map(attn_out, &to, &co) || !gemv_map(ffn, &tf, &cf))
+    return -1;
+  if (th == 32 && ch == 1 && to == 32 && co == 1 && tf == 64 && cf == 1 && head_dim == 64) return 0;
+  if (th == 64 && ch == 2 && to == 64 && co == 2 && tf == 64 && cf == 1 && head_dim == 64) return 1;
+  if (th == 64 && ch == 4 && to == 64 && co == 8 && tf == 32 && cf == 3 && head_dim == 128) return 2;
   return -1;
 }
 

@@ -114,11 +114,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     return fail(MK_EUNSUPPORTED, "mk_plan: an input vector exceeds the 8192-float LDS staging area");
   int kclass = -1;
   {
-    int t1, ch, co, cf;
-    mk::gemv_map(H, &t1, &ch);
-    mk::gemv_map(Hq * D, &t1, &co);
-    mk::gemv_map(F, &t1, &cf);
-    kclass = mk::kernel_class(ch, co, cf, D);
+    kclass = mk::kernel_class(H, Hq * D, F, D);
     if (kclass < 0)
       return fail(MK_EUNSUPPORTED, "mk_plan: no compiled kernel variant for hidden " + std::to_string(H) +
                                        ", heads x dim " + std::to_string(Hq * D) + ", FFN " +
@@ -255,9 +251,11 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       }
       stages.push_back(st);
     }
+    int n_router = 0;
     if (moe) {
       std::vector<Task> st;
       int nt = std::max(std::min(n_cu, ceil_div(m->n_experts, 8)), ceil_div(m->n_experts, rows_max(H)));
+      n_router = nt;
       for (auto [s0, c] : split_even(m->n_experts, nt)) {
         Task t = mk_task(mk::OP_ROUTER, l);
         t.wait_b = ctr16(p->c_o[l]);
@@ -270,11 +268,17 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     // EXPERT: at most one per compute unit. Task i takes gate/up tile i (an
     // expert slot of one sequence and a range of FFN rows) and down tile i (a
     // range of hidden rows over every slot); its down part reads the
-    // activations of every expert task of the layer.
+    // activations of every expert task of the layer. The gate/up tiles avoid
+    // the units that just ran a router task (the expert tasks are dealt right
+    // after the router tasks, so the last n_router expert tasks land on those
+    // units): they would start their weight stream late and hold up every
+    // unit's down part, whereas a down part alone waits for the activations
+    // anyway.
     {
       std::vector<std::array<int, 4>> gu;  // (b, slot, f0, nf)
+      const int gu_units = n_cu - n_router >= B * K ? n_cu - n_router : n_cu;
       if (moe) {
-        const int per = std::max(1, n_cu / (B * K));
+        const int per = std::max(1, gu_units / (B * K));
         for (int b = 0; b < B; ++b)
           for (int j = 0; j < K; ++j)
             for (auto [s0, c] : split_even(F, per)) gu.push_back({b, j, s0, c});

@@ -18,7 +18,7 @@ from . import (
     model_desc,
 )
 
-TRACE_WORDS = 8     # u64 per task in the optional trace buffer
+TRACE_WORDS = 16    # u64 per task in the optional trace buffer
 CTR_LINES = 8       # sub-counters (64-byte lines) per completion counter
 
 

@@ -1,9 +1,10 @@
 """Decode the optional per-task trace of a decode step.
 
-The trace buffer (mk_step_buffers.trace) holds 8 u64 words per task, in
+The trace buffer (mk_step_buffers.trace) holds 16 u64 words per task, in
 plan-image order: task start, routing-wait begin/end, data-wait begin/end
-(0 where the task has no such wait), body end, signal end (ticks of the
-100 MHz constant clock) and cu << 32 | op << 16 | layer. This module turns
+(0 where the task has no such wait), body end, task end (ticks of the
+100 MHz constant clock), cu << 32 | op << 16 | layer, then 8 marks set by
+the task body at points of its own (0 = unset). This module turns
 it into per-operation time splits and a per-stage timeline.
 """
 import numpy as np
@@ -15,7 +16,7 @@ TICK_US = 0.01  # 100 MHz
 
 def decode(raw):
     """raw: int64 tensor/array of n_tasks * 8 words -> dict of numpy columns (us, relative)."""
-    a = np.asarray(raw.cpu() if hasattr(raw, "cpu") else raw).view(np.uint64).reshape(-1, 8)
+    a = np.asarray(raw.cpu() if hasattr(raw, "cpu") else raw).view(np.uint64).reshape(-1, 16)
     t0 = a[:, 0].astype(np.float64)
     base = t0[t0 > 0].min()
     rel = lambda c: np.where(a[:, c] > 0, (a[:, c].astype(np.float64) - base) * TICK_US, np.nan)
@@ -26,6 +27,7 @@ def decode(raw):
         "cu": (meta >> np.uint64(32)).astype(np.int64),
         "op": ((meta >> np.uint64(16)) & np.uint64(0xFFFF)).astype(np.int64),
         "layer": (meta & np.uint64(0xFFFF)).astype(np.int64),
+        "marks": [rel(8 + i) for i in range(8)],
     }
 
 

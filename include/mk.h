@@ -138,13 +138,14 @@ typedef struct mk_step_buffers {
                                                64-byte line each per counter; each step adds
                                                the counter's target to the sum of its lines */
   uint32_t* status;                         /* 4 words, zeroed once */
-  uint64_t* trace; size_t trace_bytes;      /* NULL (no tracing), or 8 u64 per task
-                                               (64 * mk_plan_n_tasks bytes), indexed by
+  uint64_t* trace; size_t trace_bytes;      /* NULL (no tracing), or 16 u64 per task
+                                               (128 * mk_plan_n_tasks bytes), indexed by
                                                the task's position in the plan image:
                                                start, routing-wait begin/end, data-wait
                                                begin/end (0 = no such wait), body end,
-                                               signal end (ticks of the 100 MHz constant
-                                               clock), then cu << 32 | op << 16 | layer */
+                                               task end (ticks of the 100 MHz constant
+                                               clock), cu << 32 | op << 16 | layer, then
+                                               8 marks set inside the task body */
 } mk_step_buffers;
 
 /* ---- library ---- */
