@@ -24,6 +24,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode tok/s at batch 1 & 32; achieved HBM GB/s as % of speed-of-light"
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 1 << 30      # stream-copy probe: bytes copied per launch
 
 
 def parse():
@@ -57,6 +58,7 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    copy_gbs = stream_copy_probe(torch, mk, dev)
     total_steps = a.warmup + a.steps
     w = spec(a.workload, a.seed, steps=total_steps)
     m, B = w["model"], w["batch"]
@@ -118,7 +120,7 @@ def main():
         try:
             tj = json.load(open(a.traffic_json))
             ent = tj.get(a.workload)
-            if ent and ent.get("kernel_hash") == mk_kernel_hash():
+            if ent and ent.get("kernel_hash") == mk.kernel_hash():
                 traffic = ent.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -149,6 +151,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "bytes_per_step": {"weights": wsum / a.steps, "kv": ksum / a.steps, "total": bytes_step},
+        "stream_copy": {"gbs": round(copy_gbs, 1), "bytes_per_launch": 2 * COPY_BYTES,
+                        "frac_of_copy": round(achieved_gbs / copy_gbs, 4)},
         "sol_tok_s": round(sol_tok_s, 1),
         "frac_of_sol": round(tok_s / sol_tok_s, 4),
         "step_ms": {"median": round(statistics.median(per), 4),
@@ -162,15 +166,25 @@ def main():
     dec.close()
 
 
-def mk_kernel_hash():
-    """Hash of the kernel sources; counter figures are used only while it matches."""
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "decode_megakernel_persistent_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
+def stream_copy_probe(torch, mk, dev, reps=5):
+    """Achievable streaming bandwidth: mk_stream_copy of COPY_BYTES (read and
+    written once each) timed with HIP events on the launch stream. The same
+    launches are the known-size kernel that calibrates rocprofv3 byte counters."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        mk.mk_stream_copy(dst.data_ptr(), src.data_ptr(), COPY_BYTES, stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        mk.mk_stream_copy(dst.data_ptr(), src.data_ptr(), COPY_BYTES, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(w, a, dec, tok0):

@@ -73,6 +73,7 @@ _SIGS = {
     "mk_abi_version": (_i32, []),
     "mk_last_error": (ctypes.c_char_p, []),
     "mk_device_cu_count": (_i32, [_P(_i32)]),
+    "mk_stream_copy": (_i32, [_vp, _vp, _sz, _vp]),
     "mk_rope_table": (_i32, [_f32, _i32, _i32, _vp, _vp]),
     "mk_kv_pool_elems": (_i64, [_P(mk_model_desc), _i64]),
     "mk_step_bytes": (_i32, [_P(mk_model_desc), _i32, _P(_i32), _P(_i32), _P(ctypes.c_double),
@@ -129,6 +130,10 @@ def mk_device_cu_count():
     n = _i32()
     _check(_lib.mk_device_cu_count(ctypes.byref(n)))
     return n.value
+
+
+def mk_stream_copy(dst_ptr, src_ptr, nbytes, stream_ptr):
+    _check(_lib.mk_stream_copy(dst_ptr, src_ptr, nbytes, stream_ptr))
 
 
 def model_desc(m):
@@ -277,3 +282,16 @@ def mk_pool_seq_pages(pool, seq_id):
 
 def mk_pool_free(pool):
     _lib.mk_pool_free(pool)
+
+
+def kernel_hash():
+    """Hash of the device sources (csrc/*.hip, *.hpp): hardware-counter figures
+    recorded for one kernel build are valid only while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]

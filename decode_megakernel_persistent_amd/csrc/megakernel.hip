@@ -30,6 +30,7 @@
 //  - the split combine is a log-sum-exp merge in fixed split order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -1041,6 +1042,19 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
   }
 }
 
+
+// Streaming copy with the 16-byte non-temporal loads the task bodies use for
+// weights: the bandwidth probe behind the roofline's achievable ceiling and
+// the known-size kernel that calibrates hardware byte counters.
+__global__ __launch_bounds__(256) void mk_stream_copy_kernel(uint4* __restrict__ dst,
+                                                             const uint4* __restrict__ src, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint4 v = ld_nt(src + i);
+    __builtin_nontemporal_store(u4v{v.x, v.y, v.z, v.w}, (u4v*)(dst + i));
+  }
+}
+
 // Kernel variants, indexed by mk::kernel_class (see mk_internal.hpp).
 const void* kernel_for(int cls) {
   switch (cls) {
@@ -1071,6 +1085,24 @@ extern "C" mk_status mk_device_cu_count(int32_t* n_cu) {
   e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   *n_cu = v;
+  return MK_OK;
+}
+
+extern "C" mk_status mk_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src) return fail(MK_EINVAL, "mk_stream_copy: NULL pointer");
+  if (bytes % 16 || ((uintptr_t)dst | (uintptr_t)src) % 16)
+    return fail(MK_EINVAL, "mk_stream_copy: bytes and both pointers must be multiples of 16");
+  if (bytes == 0) return MK_OK;
+  const size_t n = bytes / 16;
+  int32_t cus = 0;
+  mk_status st = mk_device_cu_count(&cus);
+  if (st != MK_OK) return st;
+  const size_t want = (n + 255) / 256;
+  const unsigned grid = (unsigned)std::min<size_t>(want, (size_t)cus * 16);
+  hipLaunchKernelGGL(mk::dev::mk_stream_copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     (uint4*)dst, (const uint4*)src, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "mk_stream_copy launch");
   return MK_OK;
 }
 

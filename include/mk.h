@@ -153,6 +153,11 @@ int32_t mk_abi_version(void);
 const char* mk_last_error(void);
 /* Compute units of the current HIP device. */
 mk_status mk_device_cu_count(int32_t* n_cu);
+/* Device-to-device copy of `bytes` (a multiple of 16; both pointers 16-byte
+ * aligned) with 16-byte non-temporal loads and stores, enqueued on `stream`.
+ * A bandwidth probe and the known-size kernel that calibrates hardware byte
+ * counters; dst and src must not overlap. MK_EINVAL on a bad size/alignment. */
+mk_status mk_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 /* ---- model-level helpers (host only) ---- */
 /* Rotary tables: angle(p, i) = p * theta^(-2i/d) for p < n_pos, i < d/2, computed
