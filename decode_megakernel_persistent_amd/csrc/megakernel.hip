@@ -64,7 +64,7 @@ struct Smem {
 };
 
 struct Ctx {
-  const KArgs& a;
+  KAC& a;
   Smem& s;
   uint64_t t0;
   uint32_t ti;
@@ -82,7 +82,7 @@ __device__ __forceinline__ void mark(Ctx& c, int i) {
 template <int MAXW>
 __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, const uint64_t* src2, int n,
                                         float* dst, int which) {
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
   bool ok = true;
   for (int base = 0; base < n && ok; base += MAXW * NT) {
@@ -238,9 +238,7 @@ struct StageTile {
         const uint4* p = rowptr(lg + r * G);
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
-          __builtin_amdgcn_global_load_lds((const void*)(p + tc + c * TC),
-                                           (__attribute__((address_space(3))) void*)(stage + ((w * RPW + r) * CPL + c) * 64),
-                                           16, 0, 0);
+          dma16(p + tc + c * TC, lds_addr(stage + ((w * RPW + r) * CPL + c) * 64));
       }
   }
   __device__ __forceinline__ void dots(const uint4* stage, const float* u, float* out) {
@@ -266,7 +264,7 @@ struct StageTile {
 };
 
 // Token id of sequence b, checked against the vocabulary.
-__device__ __forceinline__ int token_row(const KArgs& a, int b) {
+__device__ __forceinline__ int token_row(KAC& a, int b) {
   int tok = a.tok_in[b];
   if (tok < 0 || tok >= a.V) {  // an id outside the vocabulary reads row 0 and is reported
     if (tid() == 0) raise_status(a, DS_BOUNDS, 0xFFFFFFFFu, (uint32_t)tok, 0u);
@@ -275,10 +273,18 @@ __device__ __forceinline__ int token_row(const KArgs& a, int b) {
   return tok;
 }
 
+// Running argmax with ties to the lower index, without branches (a
+// short-circuit condition here compiles to divergent branches per element).
+__device__ __forceinline__ void argmax_merge(float v, int i, float& bv, int& bi) {
+  const bool take = (int)(v > bv) | ((int)(v == bv) & (int)(i < bi));
+  bv = take ? v : bv;
+  bi = take ? i : bi;
+}
+
 // Hidden state entering layer l of sequence b into LDS dst: the embedding
 // row for l = 0 (bf16, no wait), else the tagged output of layer l - 1.
 __device__ __forceinline__ bool layer_input(Ctx& c, int l, int b, float* dst) {
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   if (l == 0) {
     const uint16_t* e = a.embed + (size_t)token_row(a, b) * a.H;
     for (int i = tid(); i < a.H; i += NT) dst[i] = bf2f(e[i]);
@@ -290,77 +296,110 @@ __device__ __forceinline__ bool layer_input(Ctx& c, int l, int b, float* dst) {
 
 // Residual value of row r entering layer l (read once the layer's inputs are known complete).
 __device__ __forceinline__ float resid(Ctx& c, int l, int b, int r, bool* fail) {
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   if (l == 0) return bf2f(a.embed[(size_t)token_row(a, b) * a.H + r]);
   return get_tagged(a, a.x + (size_t)(l - 1) * a.s_x + (size_t)b * a.H + r, c.t0, c.ti, fail);
 }
 
 // ------------------------------------------------------------------ routing
 
-// softmax over the E router logits in r (LDS), top-k (ties to the lower
-// index), weights renormalised over the selection when norm_topk. Thread e
-// owns expert e; its rank is the number of experts with a larger
+// softmax over the E router logits in r (LDS), then top-k with ties to the
+// lower index: the rank of expert e is the number of experts with a larger
 // probability, or an equal one and a lower index, so the k selected experts
 // land in rank order without a serial selection loop. The result is in
-// s.route_ids / s.route_w after the final barrier.
+// s.route_ids / s.route_w (selected probabilities, not yet renormalised: see
+// route_div) after the final barrier.
 __device__ __forceinline__ void route(Ctx& c, const float* r) {
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   Smem& s = c.s;
   const int t = tid(), E = a.E;
-  float* p = s.out + 1024;  // [E]
-  const float v = t < E ? r[t] : NEG_INF;
-  float m = wave_max(v);
-  if ((t & 63) == 0) s.red[t >> 6] = m;
-  lds_barrier();
-  float M = s.red[0];
+  const int E32 = (E + 31) & ~31;
+  uint64_t* keys = (uint64_t*)(s.out + 1024);  // [E32] (padding keys 0 rank below all)
+  float* prob = s.out + 1536;                  // [E]
+  int* partial = (int*)(s.out + 512);          // [parts][E32] (parts * E32 <= 512)
+  // softmax in wave 0 (E <= 256: four logits per lane), no block reductions
+  if (t < 64) {
+    float v[4], ex[4];
+    float m = NEG_INF;
 #pragma unroll
-  for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, s.red[w]);
-  const float ex = t < E ? expf(v - M) : 0.f;
-  const float sm = wave_sum(ex);
-  lds_barrier();
-  if ((t & 63) == 0) s.red[t >> 6] = sm;
-  lds_barrier();
-  float S = 0.f;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) S += s.red[w];
-  const float pe = ex / S;
-  if (t < E) p[t] = pe;
-  lds_barrier();
-  if (t < E) {
-    int rank = 0;
-    for (int e = 0; e < E; ++e) {
-      const float q = p[e];
-      rank += (q > pe || (q == pe && e < t)) ? 1 : 0;
+    for (int i = 0; i < 4; ++i) {
+      const int e = t + 64 * i;
+      v[i] = e < E ? r[e] : NEG_INF;
+      m = fmaxf(m, v[i]);
     }
-    if (rank < a.K) {
-      s.route_ids[rank] = t;
-      s.route_w[rank] = pe;
+    const float M = wave_max_dpp(m);
+    float sl = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ex[i] = t + 64 * i < E ? expf(v[i] - M) : 0.f;
+      sl += ex[i];
+    }
+    const float S = wave_sum(sl);
+    // Rank key of an expert: its probability's bits above its inverted index
+    // (non-negative floats order as their bit patterns; on equal
+    // probabilities the lower index ranks first). Keys are unique.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = t + 64 * i;
+      const float pe = ex[i] / S;
+      if (e < E) prob[e] = pe;
+      if (e < E32) keys[e] = e < E ? ((uint64_t)__float_as_uint(pe) << 32) | (uint32_t)(0xFFFF - e) : 0ull;
     }
   }
   lds_barrier();
-  if (t == 0 && a.norm_topk) {
-    float wsum = 0.f;
-    for (int j = 0; j < a.K; ++j) wsum += s.route_w[j];
-    for (int j = 0; j < a.K; ++j) s.route_w[j] = s.route_w[j] / wsum;
+  // rank = number of keys ahead; thread t counts part t / E32 of the keys for
+  // expert t % E32, then the parts are summed
+  const int parts = E32 <= 128 ? 4 : 2;
+  const int chunk = E32 / parts;  // a multiple of 8
+  {
+    const int te = t % E32, part = t / E32;
+    if (part < parts) {
+      const uint64_t mine = keys[te];
+      int cnt = 0;
+#pragma unroll 2
+      for (int e = part * chunk; e < (part + 1) * chunk; e += 8) {
+        uint4 q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = *(const uint4*)(keys + e + 2 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cnt += ((((uint64_t)q[i].y << 32) | q[i].x) > mine) ? 1 : 0;
+          cnt += ((((uint64_t)q[i].w << 32) | q[i].z) > mine) ? 1 : 0;
+        }
+      }
+      partial[part * E32 + te] = cnt;
+    }
+  }
+  lds_barrier();
+  if (t < E) {
+    int rank = 0;
+    for (int q = 0; q < parts; ++q) rank += partial[q * E32 + t];
+    if (rank < a.K) {
+      s.route_ids[rank] = t;
+      s.route_w[rank] = prob[t];
+    }
   }
   lds_barrier();
 }
 
-__device__ __forceinline__ bool routing(Ctx& c, int l, int b) {
-  const KArgs& a = c.a;
-  if (!gather<1>(c, a.rlog + (size_t)l * a.s_rlog + (size_t)b * a.E, a.E, c.s.out, 0)) return false;
-  route(c, c.s.out);
-  return true;
+// Divisor of the routing weights: the sum of the selected probabilities (in
+// slot order) when they are renormalised over the selection, else 1.
+__device__ __forceinline__ float route_div(KAC& a, const Smem& s) {
+  if (!a.norm_topk) return 1.f;
+  float w = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w += i < a.K ? s.route_w[i] : 0.f;
+  return w;
 }
 
 // ------------------------------------------------------------------ tasks
 
-template <int CPL, int TC>
+template <int CPL, int TC, int D>
 __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
   constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   const int l = t.layer, g = t.a0, p0 = t.a1, np = t.a2, nj = 2 * np;
-  const int H = a.H, D = a.D;
+  const int H = a.H;
   const int QR = (a.Hq + 2 * a.Hkv) * D;
   const uint16_t* W = a.wqkv + (size_t)l * QR * H;
   Tile<CPL, RPW, TC> tile;
@@ -434,7 +473,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   constexpr int NK4 = D / 32;   // 16-byte K loads per lane per page
   constexpr int NB = D / 16;    // 16-dim blocks of the PV product
   constexpr int NS = D / 16;    // MFMA k-steps of the QK product
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, g = t.a1, pg0 = t.a2, npg = t.a3, split = t.aux;
   const int HG = a.HG;
@@ -655,7 +694,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
 }
 
 __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, h = t.a1, d0 = t.a2, nd = t.a3, S = t.aux, D = a.D;
   const int HG = a.HG, g = h / HG, hh = h % HG, PS = D + 2;
@@ -671,12 +710,14 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   for (int bs = 0; bs < n && ok; bs += 4 * NT) {
     const int t = tid();
     float v[4];
-    ok = read_words<4>(a, [&](int k) -> const uint64_t* {
+    const uint64_t* ptr[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
       const int i = bs + t + k * NT;
-      if (i >= n) return nullptr;
       const int q = i / W, j = i - q * W;
-      return base + q * sstride + (j < nd ? d0 + j : D + (j - nd));
-    }, v, c.t0, c.ti);
+      ptr[k] = i < n ? base + q * sstride + (j < nd ? d0 + j : D + (j - nd)) : nullptr;
+    }
+    ok = read_words<4>(a, [&](int k) -> const uint64_t* { return ptr[k]; }, v, c.t0, c.ti);
     if (ok) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -716,6 +757,7 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   lds_barrier();
   if (tid() < nd) {
     float o = 0.f;
+#pragma unroll 16
     for (int q = 0; q < NG; ++q) o += red[q * nd + tid()];
     st_tagged(a.o + (size_t)l * a.s_o + ((size_t)b * a.Hq + h) * D + d0 + tid(), o, a.epoch);
   }
@@ -725,7 +767,7 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
 template <int CPL, int TC>
 __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
   constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   const int l = t.layer, r0 = t.a1, n = t.a2;
   const int H = a.H, K = a.Hq * a.D;
   const uint16_t* W = a.wo + (size_t)l * H * K;
@@ -757,7 +799,7 @@ __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
 template <int CPL, int TC>
 __device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
   constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H;
   const uint16_t* W = a.router + (size_t)l * a.E * H;
   Tile<CPL, RPW, TC> tile;
@@ -783,7 +825,7 @@ template <int CH, int TCH, int CF, int TCF>
 __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
   constexpr int RPW_G = GEMV_REG_CHUNKS / CH < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CH : GEMV_RPW_MAX;
   constexpr int RPW_D = STAGE_CHUNKS / CF < GEMV_RPW_MAX ? STAGE_CHUNKS / CF : GEMV_RPW_MAX;
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, slot = t.aux, f0 = t.a1, nf = t.a2;
   const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
@@ -800,7 +842,7 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
     route(c, lg_);
     if ((t.flags & TF_WRITE_TOPK) && tid() < a.K) {
       if (a.topk_ids) a.topk_ids[(size_t)l * a.K + tid()] = s.route_ids[tid()];
-      if (a.topk_w) a.topk_w[(size_t)l * a.K + tid()] = s.route_w[tid()];
+      if (a.topk_w) a.topk_w[(size_t)l * a.K + tid()] = s.route_w[tid()] / route_div(a, s);
     }
   } else {
     if (tid() == 0) {
@@ -818,27 +860,18 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
   const uint16_t* Wd = a.down + (size_t)l * EE * H * F;
   const int capg = (NT / TCH) * RPW_G / 2;   // FFN rows per register tile
   const int capd = (NT / TCF) * RPW_D / KK;  // hidden rows per staged tile
-  // In the usual plan each part is one tile: the gate/up rows go to registers
-  // and the down rows to LDS back to back, so the down rows stream while the
-  // gate/up rows are used; the dots wait only for the loads they read.
+  // The gate/up rows stream into registers; the down rows are requested into
+  // LDS only once the gate/up rows are consumed (a wave's loads complete in
+  // issue order, so down rows issued earlier would hold up the gate/up dots),
+  // and they stream while the activations of the other expert tasks arrive.
   Tile<CH, RPW_G, TCH> gu;
   StageTile<CF, RPW_D, TCF> dn;
-  const bool one_g = nf <= capg, one_d = nr <= capd;
-  if (nf > 0)
-    gu.issue(2 * min(nf, capg), [&](int j) {
-      return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + (j >> 1)) * H);
-    });
-  if (one_g && one_d && nr > 0)
-    dn.issue(nr * KK, [&](int j) {
-      return (const uint4*)(Wd + ((size_t)s.route_ids[j % KK] * H + r0 + j / KK) * F);
-    }, s.stage);
   mark(c, 1);
   for (int fc = 0; fc < nf; fc += capg) {
     const int nfc = min(capg, nf - fc);
-    if (fc > 0)
-      gu.issue(2 * nfc, [&](int j) {
-        return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + fc + (j >> 1)) * H);
-      });
+    gu.issue(2 * nfc, [&](int j) {
+      return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + fc + (j >> 1)) * H);
+    });
     gu.dots(s.vec, s.out);
     lds_barrier();
     mark(c, 3);
@@ -855,8 +888,7 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
   // is fixed because the number of lane groups is a multiple of KK
   for (int rc = 0; rc < nr; rc += capd) {
     const int nrc = min(capd, nr - rc);
-    if (!(one_g && one_d))
-      dn.issue(nrc * KK, [&](int j) {
+    dn.issue(nrc * KK, [&](int j) {
         return (const uint4*)(Wd + ((size_t)s.route_ids[j % KK] * H + r0 + rc + j / KK) * F);
       }, s.stage);
     if (rc == 0) {
@@ -869,9 +901,15 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
     dn.dots(s.stage, s.vec + (size_t)(dn.lg % KK) * F, s.out);
     lds_barrier();
     mark(c, 7);
+    const float div = route_div(a, s);
+    float wj[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) wj[j] = j < KK ? s.route_w[j] / div : 0.f;
     for (int q = tid(); q < nrc; q += NT) {
       float y = 0.f;
-      for (int j = 0; j < KK; ++j) y += s.route_w[j] * s.out[q * KK + j];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < KK) y += wj[j] * s.out[q * KK + j];
       st_tagged(a.x + (size_t)l * a.s_x + (size_t)b * H + r0 + rc + q, s.res[rc + q] + y, a.epoch);
     }
     lds_barrier();
@@ -886,7 +924,7 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
 template <int CPL, int TC>
 __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
   constexpr int G = NT / TC;
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   Smem& s = c.s;
   const int r0 = t.a1, n = t.a2, H = a.H;
   const int lg = tid() / TC, tc = tid() % TC;
@@ -937,13 +975,13 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
   for (int j = tid(); j < n; j += NT) {
     const float y = s.out[j];
     if (a.logits) a.logits[r0 + j] = y;
-    if (y > bv) { bv = y; bi = r0 + j; }
+    argmax_merge(y, r0 + j, bv, bi);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o, 64);
     const int oi = __shfl_xor(bi, o, 64);
-    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    argmax_merge(ov, oi, bv, bi);
   }
   float* rv = s.red;
   int* ri = (int*)(s.red + NWAVE);
@@ -951,7 +989,7 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
   lds_barrier();
   if (tid() == 0) {
     for (int q = 1; q < NWAVE; ++q)
-      if (rv[q] > bv || (rv[q] == bv && ri[q] < bi)) { bv = rv[q]; bi = ri[q]; }
+      argmax_merge(rv[q], ri[q], bv, bi);
     st_tagged(a.lmpart + (size_t)t.a3 * 2, bv, a.epoch);
     st_tagged(a.lmpart + (size_t)t.a3 * 2 + 1, __int_as_float(bi), a.epoch);
   }
@@ -959,7 +997,7 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
 }
 
 __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
-  const KArgs& a = c.a;
+  KAC& a = c.a;
   Smem& s = c.s;
   const int n = t.a0;
   if (!gather<2>(c, a.lmpart, 2 * n, s.vec, 1)) return false;
@@ -968,13 +1006,13 @@ __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
   for (int q = tid(); q < n; q += NT) {
     const float v = s.vec[2 * q];
     const int i = __float_as_int(s.vec[2 * q + 1]);
-    if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+    argmax_merge(v, i, bv, bi);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o, 64);
     const int oi = __shfl_xor(bi, o, 64);
-    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    argmax_merge(ov, oi, bv, bi);
   }
   float* rv = s.red;
   int* ri = (int*)(s.red + NWAVE);
@@ -982,7 +1020,7 @@ __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
   lds_barrier();
   if (tid() == 0) {
     for (int q = 1; q < NWAVE; ++q)
-      if (rv[q] > bv || (rv[q] == bv && ri[q] < bi)) { bv = rv[q]; bi = ri[q]; }
+      argmax_merge(rv[q], ri[q], bv, bi);
     a.tok_out[0] = bi;
     a.seq_lens[0] = a.seq_lens[0] + 1;
   }
@@ -995,15 +1033,22 @@ __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
 // head dim. Each variant contains only the
 // task bodies its shapes use, so registers are allocated for them alone.
 template <int CH, int TCH, int CO, int TCO, int CF, int TCF, int HD>
-__global__ void __launch_bounds__(NT) megakernel(KArgs a) {
+__global__ void __launch_bounds__(NT) megakernel(KArgs) {
   __shared__ Smem s;
-  const uint32_t* hdr = a.plan;
+  // explicit kernel arguments start at offset 0 of the kernel-argument segment
+  const KAC* const args = (const KAC*)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint32_t* hdr = args->plan;
   const uint32_t* off = hdr + PLAN_HDR_WORDS;
-  const Task* tasks = (const Task*)((const char*)a.plan + hdr[H_TASK_OFF_BYTES]);
+  const Task* tasks = (const Task*)((const char*)hdr + hdr[H_TASK_OFF_BYTES]);
   const uint32_t beg = off[blockIdx.x], end = off[blockIdx.x + 1];
   if (tid() == 0) s.fail = 0;
   lds_barrier();
   for (uint32_t ti = beg; ti < end; ++ti) {
+    // an opaque copy of the argument pointer per task: fields are loaded where
+    // a body uses them instead of being kept live across the loop
+    const KAC* pa = args;
+    asm volatile("" : "+s"(pa));
+    KAC& a = *pa;
     const Task t = tasks[ti];
     Ctx c{a, s, now(), ti};
     if (a.trace && tid() == 0) {
@@ -1012,7 +1057,7 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs a) {
     }
     bool ok = true;
     switch (t.op) {
-      case OP_QKV: ok = task_qkv<CH, TCH>(c, t); break;
+      case OP_QKV: ok = task_qkv<CH, TCH, HD>(c, t); break;
       case OP_ATTN: ok = task_attn<HD>(c, t); break;
       case OP_COMB: ok = task_comb(c, t); break;
       case OP_O: ok = task_o<CO, TCO>(c, t); break;

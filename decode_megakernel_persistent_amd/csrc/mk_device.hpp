@@ -16,6 +16,12 @@ typedef unsigned u2v __attribute__((ext_vector_type(2)));
 
 constexpr float NEG_INF = -__builtin_inff();
 
+// The kernel argument block as seen by the task bodies: read in place from
+// the kernel-argument segment (constant address space) with scalar loads.
+// Holding all of its fields in scalar registers for the whole persistent
+// loop would exceed the scalar register file and spill.
+typedef const __attribute__((address_space(4))) KArgs KAC;
+
 // The thread index read through an opaque move. Values derived from it
 // cannot be hoisted out of the persistent task loop, which would keep them
 // live across every task body and exhaust the register file.
@@ -44,6 +50,19 @@ __device__ __forceinline__ uint4 ld_nt(const uint4* p) {
 __device__ __forceinline__ uint2 ld_nt2(const uint2* p) {
   const u2v v = __builtin_nontemporal_load((const u2v*)p);
   return make_uint2(v.x, v.y);
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane i's 16 bytes from g land at
+// LDS byte address lds_base + 16 * i (lds_base wave-uniform). Written as
+// inline assembly so that the compiler does not treat every later LDS read
+// as possibly aliasing the transfer (it would wait for all outstanding
+// vector memory operations before each one); the consumer waits for the
+// transfer itself (s_waitcnt vmcnt) before reading its destination.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -122,6 +141,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   const float s = group_sum_last<64>(v);
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
 }
+// Maximum over the wave, returned to every lane (DPP, no LDS).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  // rows not written by a broadcast keep their own value: fmax(v, 0) must not
+  // see the zero that update_dpp supplies for masked rows, so those rows
+  // take the max with themselves instead
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -141,7 +173,7 @@ __device__ __forceinline__ bool tag_is(uint64_t w, uint32_t epoch) { return (uin
 __device__ __forceinline__ float tag_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // Record a device failure: the first one wins the code word.
-__device__ __forceinline__ void raise_status(const KArgs& a, uint32_t code, uint32_t w1, uint32_t w2,
+__device__ __forceinline__ void raise_status(KAC& a, uint32_t code, uint32_t w1, uint32_t w2,
                                              uint32_t w3) {
   if (atomicCAS(a.status, 0u, code) == 0u) {
     __hip_atomic_store(a.status + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -149,13 +181,13 @@ __device__ __forceinline__ void raise_status(const KArgs& a, uint32_t code, uint
     __hip_atomic_store(a.status + 3, w3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
-__device__ __forceinline__ bool aborted(const KArgs& a) {
+__device__ __forceinline__ bool aborted(KAC& a) {
   return __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
 
 // Spin until the word at p carries the current epoch; returns its value.
 // A deadline (from t0) or another workgroup's failure sets *fail.
-__device__ __forceinline__ float get_tagged(const KArgs& a, const uint64_t* p, uint64_t t0,
+__device__ __forceinline__ float get_tagged(KAC& a, const uint64_t* p, uint64_t t0,
                                             uint32_t task, bool* fail) {
   uint64_t w = ld_tagged(p);
   if (tag_is(w, a.epoch)) return tag_value(w);
@@ -181,7 +213,7 @@ __device__ __forceinline__ float get_tagged(const KArgs& a, const uint64_t* p, u
 // sleep, so a word is seen within one round trip of its store landing.
 // Returns false on deadline or another workgroup's failure.
 template <int MAXW, class Addr>
-__device__ __forceinline__ bool read_words(const KArgs& a, const Addr& addr, float* out, uint64_t t0,
+__device__ __forceinline__ bool read_words(KAC& a, const Addr& addr, float* out, uint64_t t0,
                                            uint32_t task) {
   const uint32_t ep = a.epoch;
   uint64_t w[MAXW];
