@@ -49,19 +49,16 @@ constexpr int STAGE_CHUNKS = 12;  // 1 KB wave chunks per wave in the staging ar
 
 struct Smem {
   float vec[LDS_VEC];  // gathered input vector(s), normalised in place
-  // direct-to-LDS staging: the KV pages of an attention task (loaded during
-  // the task before it), the rows of an O task (loaded during the attention
-  // or combine task before it), an expert task's down-projection rows
-  uint4 stage[NWAVE * STAGE_CHUNKS * 64];
+  union {
+    uint4 stage[NWAVE * STAGE_CHUNKS * 64];  // expert: down-projection rows (direct-to-LDS loads)
+    float att[NWAVE * STAGE_CHUNKS * 256];   // attention: per-wave partials; combine: split words
+  };
   float out[2048];     // per-row dot products
   float res[2048];     // residual rows
   float red[64];       // block reductions
   float route_w[16];
   int route_ids[16];
   int fail;
-  int kv_task;          // task whose KV pages are in stage (-1: none)
-  int o_task;           // task whose weight rows are in stage (-1: none)
-  uint32_t kv_ok[NWAVE];  // per wave: bit k = page slot k holds a valid page
   uint64_t tw[4];      // trace: (begin, end) of the routing wait and of the data wait
   uint64_t mk[TRACE_MARKS];  // trace: body-specific marks
 };
@@ -228,16 +225,13 @@ struct StageTile {
   static constexpr int G = NT / TC;
   int nr, lg, tc, w;
 
-  __device__ __forceinline__ void init(int R) {
+  template <class RowPtr>
+  __device__ __forceinline__ void issue(int R, const RowPtr& rowptr, uint4* stage) {
     lg = tid() / TC;
     tc = tid() % TC;
     w = __builtin_amdgcn_readfirstlane(tid() >> 6);
     nr = lg < R ? (R - lg + G - 1) / G : 0;
     if (TC == 64) nr = __builtin_amdgcn_readfirstlane(nr);
-  }
-  template <class RowPtr>
-  __device__ __forceinline__ void issue(int R, const RowPtr& rowptr, uint4* stage) {
-    init(R);
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       if (r < nr) {
@@ -398,95 +392,16 @@ __device__ __forceinline__ float route_div(KAC& a, const Smem& s) {
   return w;
 }
 
-// ------------------------------------------------------------------ loads ahead of a task
-
-// KV page slots of the staging area: one page block (K then V of one kv head,
-// 2 x 16 x D bf16) per slot. K rows keep their 16-byte chunks permuted (chunk
-// c of row r at position c ^ (r mod chunks-per-row)), so that the sixteen
-// lanes that read one chunk of sixteen rows hit distinct LDS banks.
-template <int D>
-struct KvSlots {
-  static constexpr int CPR = D / 8;       // 16-byte chunks per K row
-  static constexpr int KC = 16 * CPR;     // chunks of the K half
-  static constexpr int CHUNKS = 2 * KC;   // chunks per page block
-  static constexpr int N = NWAVE * STAGE_CHUNKS * 64 / CHUNKS;
-};
-
-// Direct-to-LDS loads of the KV pages of attention task nt: this wave's pages
-// k = w, w + 8, ... below the live context go to slot k. ids: lane j holds the
-// physical id of the task's page j; pos: the sequence's position. Slots of
-// pages with an invalid id are left out of kv_ok.
-template <int D>
-__device__ __forceinline__ void kv_prefetch(Ctx& c, const Task& nt, int32_t ids, int pos) {
-  using S = KvSlots<D>;
-  KAC& a = c.a;
-  const int lane = tid() & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid() >> 6);
-  const int n_tok = min(pos + 1, a.bound);
-  const int lim = min(nt.a3, ((n_tok + 15) >> 4) - nt.a2);
-  const uint16_t* lbase = a.pool + (size_t)nt.layer * a.layer_stride + (size_t)nt.a1 * 2 * 16 * D;
-  uint32_t ok = 0;
-  for (int k = w; k < lim; k += NWAVE) {
-    const int32_t phys = __builtin_amdgcn_readlane(ids, k);
-    if (phys < 0 || phys >= a.n_pages) continue;
-    ok |= 1u << k;
-    const uint4* src = (const uint4*)(lbase + (size_t)phys * a.page_stride);
-#pragma unroll
-    for (int j = 0; j < S::CHUNKS / 64; ++j) {
-      const int q = j * 64 + lane;
-      const int r = q / S::CPR, x = q % S::CPR;
-      const int gi = q < S::KC ? r * S::CPR + (x ^ (r & (S::CPR - 1))) : q;
-      dma16(src + gi, lds_addr(c.s.stage + k * S::CHUNKS + j * 64));
-    }
-  }
-  if (lane == 0) c.s.kv_ok[w] = ok;
-}
-
-// Direct-to-LDS loads of the weight rows of the O task that follows (next,
-// or after one combine task), when its rows fit the staging area.
-template <int CO, int TCO>
-__device__ __forceinline__ void o_prefetch(Ctx& c, const Task* nx, const Task* nx2, int layer) {
-  constexpr int RPW = STAGE_CHUNKS / CO < GEMV_RPW_MAX ? STAGE_CHUNKS / CO : GEMV_RPW_MAX;
-  const Task* o = nullptr;
-  int ahead = 0;
-  if (nx && nx->op == OP_O && nx->layer == layer) {
-    o = nx;
-    ahead = 1;
-  } else if (nx && nx->op == OP_COMB && nx2 && nx2->op == OP_O && nx2->layer == layer) {
-    o = nx2;
-    ahead = 2;
-  }
-  if (!o || o->a2 > (NT / TCO) * RPW) return;
-  KAC& a = c.a;
-  const int K = a.Hq * a.D;
-  const uint16_t* W = a.wo + (size_t)layer * a.H * K;
-  const int r0 = o->a1;
-  StageTile<CO, RPW, TCO> tile;
-  tile.issue(o->a2, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * K); }, c.s.stage);
-  if (tid() == 0) c.s.o_task = (int)c.ti + ahead;
-}
-
 // ------------------------------------------------------------------ tasks
 
 template <int CPL, int TC, int D>
-__device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t, const Task* nx) {
+__device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
   constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
   KAC& a = c.a;
   const int l = t.layer, g = t.a0, p0 = t.a1, np = t.a2, nj = 2 * np;
   const int H = a.H;
   const int QR = (a.Hq + 2 * a.Hkv) * D;
   const uint16_t* W = a.wqkv + (size_t)l * QR * H;
-  // When this unit's next task is an attention split of this layer whose
-  // pages fit the staging area, its KV pages are requested here once this
-  // task's rows are consumed; their ids and the position are read first.
-  const bool pf = nx && nx->op == OP_ATTN && nx->layer == l && nx->a3 <= KvSlots<D>::N;
-  int32_t pf_ids = -1;
-  int pf_pos = 0;
-  if (pf) {
-    const int lane = tid() & 63;
-    if (lane < nx->a3) pf_ids = a.page_table[(size_t)nx->a0 * a.max_pages + nx->a2 + lane];
-    pf_pos = a.seq_lens[nx->a0];
-  }
   Tile<CPL, RPW, TC> tile;
   tile.issue(nj, [&](int j) {
     int head, i, row;
@@ -549,16 +464,11 @@ __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t, const Task* nx) 
       }
     }
   }
-  // the queries and new K, V are out: now the next task's KV pages
-  if (pf) {
-    kv_prefetch<D>(c, *nx, pf_ids, pf_pos);
-    if (tid() == 0) c.s.kv_task = (int)c.ti + 1;
-  }
   return true;
 }
 
-template <int D, int CO, int TCO>
-__device__ __forceinline__ bool task_attn(Ctx& c, const Task& t, const Task* nx, const Task* nx2) {
+template <int D>
+__device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   constexpr int KQ = D / 4;     // dims of one lane group in the QK product
   constexpr int NK4 = D / 32;   // 16-byte K loads per lane per page
   constexpr int NB = D / 16;    // 16-dim blocks of the PV product
@@ -570,13 +480,11 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t, const Task* nx,
   const int lane = tid() & 63, w = tid() >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
   const int32_t* prow = a.page_table + (size_t)b * a.max_pages;
-  // pages in the staging area already (requested by the task before this one)?
-  const bool pre = s.kv_task == (int)c.ti;
-  // else this wave's first two page ids, read together with the position
-  // (the plan maps every page below its bound)
+  // this wave's first two page ids, read together with the position (the
+  // plan maps every page below its bound)
   const int first = pg0 + w;
-  const int32_t ph0 = !pre && first < pg0 + npg ? prow[first] : -1;
-  const int32_t ph1 = !pre && first + NWAVE < pg0 + npg ? prow[first + NWAVE] : -1;
+  const int32_t ph0 = first < pg0 + npg ? prow[first] : -1;
+  const int32_t ph1 = first + NWAVE < pg0 + npg ? prow[first + NWAVE] : -1;
   const int pos = a.seq_lens[b];
   const int n_tok = min(pos + 1, a.bound);
   const int pg_lim = min(pg0 + npg, (n_tok + 15) >> 4);
@@ -603,20 +511,8 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t, const Task* nx,
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) vv[nb] = ld_nt2((const uint2*)(vp + nb * 256));
   };
-  // a staged page: K chunks un-permuted on read (see KvSlots), V as stored
-  auto stage_page = [&](uint4 (&kk)[NK4], uint2 (&vv)[NB], int k) {
-    using S = KvSlots<D>;
-    const uint4* sl = s.stage + k * S::CHUNKS;
-#pragma unroll
-    for (int i = 0; i < NK4; ++i) kk[i] = sl[r16 * S::CPR + ((kq * NK4 + i) ^ (r16 & (S::CPR - 1)))];
-    const uint2* vb = (const uint2*)(sl + S::KC);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) vv[nb] = vb[(nb * 16 + r16) * 4 + kq];
-  };
-  if (!pre) {
-    if (cnt > 0) load(k0, v0, first, ph0);
-    if (cnt > 1) load(k1, v1, first + NWAVE, ph1);
-  }
+  if (cnt > 0) load(k0, v0, first, ph0);
+  if (cnt > 1) load(k1, v1, first + NWAVE, ph1);
 
   // inputs: the group's queries and the new token's K and V (bf16 bits), one batch
   float* qv = s.vec;                 // [HG][D]
@@ -730,40 +626,19 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t, const Task* nx,
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, __builtin_bit_cast(v4s, vm), acc[nb], 0, 0, 0);
     }
   };
-  if (pre) {
-    // this wave's pages k = w, w + 8, ... sit in slot k
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct-to-LDS loads
-    const uint32_t okw = s.kv_ok[w];
-    for (int i = 0; i < cnt; ++i) {
-      const int k = w + i * NWAVE;
-      if ((okw >> k) & 1u) {
-        stage_page(k0, v0, k);
-      } else {
-        bad = true;
+  // page i of this wave is in (k0, v0), page i + 1 in flight in (k1, v1)
+  for (int i = 0; i < cnt; ++i) {
+    compute(k0, v0, first + i * NWAVE);
 #pragma unroll
-        for (int q = 0; q < NK4; ++q) k0[q] = make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < NK4; ++q) k0[q] = k1[q];
 #pragma unroll
-        for (int q = 0; q < NB; ++q) v0[q] = make_uint2(0, 0);
-      }
-      compute(k0, v0, first + i * NWAVE);
-    }
-  } else {
-    // page i of this wave is in (k0, v0), page i + 1 in flight in (k1, v1)
-    for (int i = 0; i < cnt; ++i) {
-      compute(k0, v0, first + i * NWAVE);
-#pragma unroll
-      for (int q = 0; q < NK4; ++q) k0[q] = k1[q];
-#pragma unroll
-      for (int q = 0; q < NB; ++q) v0[q] = v1[q];
-      if (i + 2 < cnt) load(k1, v1, first + (i + 2) * NWAVE, prow[first + (i + 2) * NWAVE]);
-    }
+    for (int q = 0; q < NB; ++q) v0[q] = v1[q];
+    if (i + 2 < cnt) load(k1, v1, first + (i + 2) * NWAVE, prow[first + (i + 2) * NWAVE]);
   }
   mark(c, 2);
   if (bad && lane == 0) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)b, 0xFFFFFFFFu);
-  // every wave is done with the staged pages and with q / new K, V in vec
-  lds_barrier();
   // merge hi/lo rows and publish this wave's partial in LDS
-  float* Ow = s.vec;                      // [NWAVE][HG][D]
+  float* Ow = s.att;                      // [NWAVE][HG][D]
   float* mw = s.red;                      // [NWAVE][8]
   float* lw = s.out;                      // [NWAVE][8]
 #pragma unroll
@@ -780,26 +655,26 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t, const Task* nx,
   }
   lds_barrier();
   mark(c, 3);
-  // merge scale of wave q for head h: exp(m_q - M_h), M_h = max over the waves
+  // per-head merge scales over the waves: ew[q][head] = exp(m_q - M), M = max_q m_q
   float* ew = s.out + 64;  // [NWAVE][8]
   float* mm = s.out + 128; // [8] (M, then L)
-  if (tid() < NWAVE * 8) {
-    const int q = tid() >> 3, head = tid() & 7;
-    float M = NEG_INF;
-#pragma unroll
-    for (int u = 0; u < NWAVE; ++u) M = fmaxf(M, mw[u * 8 + head]);
-    const float m = mw[q * 8 + head];
-    ew[q * 8 + head] = m == NEG_INF ? 0.f : expf(m - M);
-    if (q == 0) mm[head] = M;
-  }
-  lds_barrier();
   if (tid() < 8) {
     const int head = tid();
+    float M = NEG_INF;
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) M = fmaxf(M, mw[q * 8 + head]);
     float LL = 0.f;
 #pragma unroll
-    for (int q = 0; q < NWAVE; ++q) LL += ew[q * 8 + head] * lw[q * 8 + head];
+    for (int q = 0; q < NWAVE; ++q) {
+      const float m = mw[q * 8 + head];
+      const float e = m == NEG_INF ? 0.f : expf(m - M);
+      ew[q * 8 + head] = e;
+      LL += e * lw[q * 8 + head];
+    }
+    mm[head] = M;
     mm[8 + head] = LL;
   }
+  lds_barrier();
   const int PS = D + 2;
   uint64_t* dst0 = a.part + (size_t)l * a.s_part +
                    (((size_t)b * a.Hkv + g) * a.S_max + split) * HG * PS;
@@ -808,34 +683,28 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t, const Task* nx,
     float oo = 0.f;
 #pragma unroll
     for (int q = 0; q < NWAVE; ++q) oo += ew[q * 8 + head] * Ow[(q * HG + head) * D + dim];
-    st_tagged(dst0 + (size_t)head * PS + dim, oo, a.epoch);
+    uint64_t* dst = dst0 + (size_t)head * PS;
+    st_tagged(dst + dim, oo, a.epoch);
+    if (dim == 0) {
+      st_tagged(dst + D, mm[head], a.epoch);
+      st_tagged(dst + D + 1, mm[8 + head], a.epoch);
+    }
   }
-  lds_barrier();
-  if (tid() < HG) {
-    st_tagged(dst0 + (size_t)tid() * PS + D, mm[tid()], a.epoch);
-    st_tagged(dst0 + (size_t)tid() * PS + D + 1, mm[8 + tid()], a.epoch);
-  }
-  // the partials are out: now the rows of the O task ahead
-  o_prefetch<CO, TCO>(c, nx, nx2, l);
   return true;
 }
 
-template <int CO, int TCO>
-__device__ __forceinline__ bool task_comb(Ctx& c, const Task& t, const Task* nx) {
+__device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   KAC& a = c.a;
   Smem& s = c.s;
-  // the rows of the O task that follows, unless an attention task on this
-  // unit requested them already
-  if (s.o_task != (int)c.ti + 1) o_prefetch<CO, TCO>(c, nx, nullptr, t.layer);
   const int l = t.layer, b = t.a0, h = t.a1, d0 = t.a2, nd = t.a3, S = t.aux, D = a.D;
   const int HG = a.HG, g = h / HG, hh = h % HG, PS = D + 2;
   const uint64_t* base = a.part + (size_t)l * a.s_part + ((size_t)b * a.Hkv + g) * a.S_max * HG * PS +
                          (size_t)hh * PS;
   const size_t sstride = (size_t)HG * PS;
   // every split's dims d0 .. d0+nd, max and sum in one batch: word i of split
-  // q = i / (nd + 2), j = i % (nd + 2) -> vec[i] (j < nd: value, nd: max, nd+1: sum)
+  // q = i / (nd + 2), j = i % (nd + 2) -> att[i] (j < nd: value, nd: max, nd+1: sum)
   const int W = nd + 2, n = S * W;
-  float* sw = s.vec;
+  float* sw = s.att;
   if (a.trace && tid() == 0) s.tw[2] = now();
   bool ok = true;
   for (int bs = 0; bs < n && ok; bs += 4 * NT) {
@@ -861,33 +730,36 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t, const Task* nx)
   lds_barrier();
   if (a.trace && tid() == 0) s.tw[3] = now();
   if (s.fail) return false;
-  // Wave w merges dims w, w + 8, ... of the task's range; lane j holds splits
-  // j, j + 64, ...: weight of split q = exp(m_q - M) / L with M = max_q m_q and
-  // L = sum_q exp(m_q - M) l_q; per dim, lanes sum their splits in split order,
-  // then the wave sums its lanes (fixed DPP tree).
-  const int lane = tid() & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid() >> 6);
-  if (w < nd) {
+  float* cs = s.out;  // [S] merge weights
+  if (tid() < 64) {
+    const int lane = tid();
     float M = NEG_INF;
     for (int q = lane; q < S; q += 64) M = fmaxf(M, sw[q * W + nd]);
-    M = wave_max_dpp(M);
+    M = wave_max(M);
     float L = 0.f;
     for (int q = lane; q < S; q += 64) {
       const float mq = sw[q * W + nd];
       L += mq == NEG_INF ? 0.f : expf(mq - M) * sw[q * W + nd + 1];
     }
     L = wave_sum(L);
-    for (int dd = w; dd < nd; dd += NWAVE) {
-      float o = 0.f;
-      for (int q = lane; q < S; q += 64) {
-        const float mq = sw[q * W + nd];
-        const float cq = (mq == NEG_INF || L == 0.f) ? 0.f : expf(mq - M) / L;
-        o += cq * sw[q * W + dd];
-      }
-      o = wave_sum(o);
-      if (lane == 0)
-        st_tagged(a.o + (size_t)l * a.s_o + ((size_t)b * a.Hq + h) * D + d0 + dd, o, a.epoch);
+    for (int q = lane; q < S; q += 64) {
+      const float mq = sw[q * W + nd];
+      cs[q] = (mq == NEG_INF || L == 0.f) ? 0.f : expf(mq - M) / L;
     }
+  }
+  lds_barrier();
+  const int NG = NT / nd, sg = tid() / nd, dim = tid() % nd;
+  float acc = 0.f;
+  if (sg < NG)
+    for (int q = sg; q < S; q += NG) acc += cs[q] * sw[q * W + dim];
+  float* red = s.out + 1024;
+  if (sg < NG) red[sg * nd + dim] = acc;
+  lds_barrier();
+  if (tid() < nd) {
+    float o = 0.f;
+#pragma unroll 16
+    for (int q = 0; q < NG; ++q) o += red[q * nd + tid()];
+    st_tagged(a.o + (size_t)l * a.s_o + ((size_t)b * a.Hq + h) * D + d0 + tid(), o, a.epoch);
   }
   return true;
 }
@@ -895,17 +767,12 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t, const Task* nx)
 template <int CPL, int TC>
 __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
   constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
-  constexpr int RPWS = STAGE_CHUNKS / CPL < GEMV_RPW_MAX ? STAGE_CHUNKS / CPL : GEMV_RPW_MAX;
   KAC& a = c.a;
   const int l = t.layer, r0 = t.a1, n = t.a2;
   const int H = a.H, K = a.Hq * a.D;
   const uint16_t* W = a.wo + (size_t)l * H * K;
-  // rows staged by an earlier task of this unit, or streamed into registers now
-  const bool pre = c.s.o_task == (int)c.ti;
   Tile<CPL, RPW, TC> tile;
-  StageTile<CPL, RPWS, TC> st;
-  if (pre) st.init(n);
-  else tile.issue(n, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * K); });
+  tile.issue(n, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * K); });
   // residual rows (layer input, complete once o is): loaded ahead of the wait
   const int th = tid();
   uint64_t rw = 0;
@@ -915,12 +782,7 @@ __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
   }
   if (!gather<8>(c, a.o + (size_t)l * a.s_o, K, c.s.vec, 1)) return false;
   pack_lds(c, c.s.vec, K);
-  if (pre) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct-to-LDS loads
-    st.dots(c.s.stage, c.s.vec, c.s.out);
-  } else {
-    tile.dots(c.s.vec, c.s.out);
-  }
+  tile.dots(c.s.vec, c.s.out);
   lds_barrier();
   bool fail = false;
   if (th < n) {
@@ -1179,11 +1041,7 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
   const uint32_t* off = hdr + PLAN_HDR_WORDS;
   const Task* tasks = (const Task*)((const char*)hdr + hdr[H_TASK_OFF_BYTES]);
   const uint32_t beg = off[blockIdx.x], end = off[blockIdx.x + 1];
-  if (tid() == 0) {
-    s.fail = 0;
-    s.kv_task = -1;
-    s.o_task = -1;
-  }
+  if (tid() == 0) s.fail = 0;
   lds_barrier();
   for (uint32_t ti = beg; ti < end; ++ti) {
     // an opaque copy of the argument pointer per task: fields are loaded where
@@ -1192,9 +1050,6 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
     asm volatile("" : "+s"(pa));
     KAC& a = *pa;
     const Task t = tasks[ti];
-    // the next two tasks of this list (for loads issued ahead of them)
-    const Task* nx = ti + 1 < end ? tasks + ti + 1 : nullptr;
-    const Task* nx2 = ti + 2 < end ? tasks + ti + 2 : nullptr;
     Ctx c{a, s, now(), ti};
     if (a.trace && tid() == 0) {
       s.tw[0] = s.tw[1] = s.tw[2] = s.tw[3] = 0;
@@ -1202,9 +1057,9 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
     }
     bool ok = true;
     switch (t.op) {
-      case OP_QKV: ok = task_qkv<CH, TCH, HD>(c, t, nx); break;
-      case OP_ATTN: ok = task_attn<HD, CO, TCO>(c, t, nx, nx2); break;
-      case OP_COMB: ok = task_comb<CO, TCO>(c, t, nx); break;
+      case OP_QKV: ok = task_qkv<CH, TCH, HD>(c, t); break;
+      case OP_ATTN: ok = task_attn<HD>(c, t); break;
+      case OP_COMB: ok = task_comb(c, t); break;
       case OP_O: ok = task_o<CO, TCO>(c, t); break;
       case OP_ROUTER: ok = task_router<CH, TCH>(c, t); break;
       case OP_EXPERT: ok = task_expert<CH, TCH, CF, TCF>(c, t); break;
