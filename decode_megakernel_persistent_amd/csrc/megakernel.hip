@@ -455,11 +455,11 @@ __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
                          (size_t)g * 2 * 16 * D;
         const int slot = pos & 15;
         if (sec == 1) {
-          base[slot * D + i] = (uint16_t)b0;
-          base[slot * D + i + D / 2] = (uint16_t)b1;
+          base[kv_k_offset(slot, i)] = (uint16_t)b0;
+          base[kv_k_offset(slot, i + D / 2)] = (uint16_t)b1;
         } else {
-          base[16 * D + i * 16 + slot] = (uint16_t)b0;
-          base[16 * D + (i + D / 2) * 16 + slot] = (uint16_t)b1;
+          base[kv_v_offset(slot, i, D)] = (uint16_t)b0;
+          base[kv_v_offset(slot, i + D / 2, D)] = (uint16_t)b1;
         }
       }
     }
@@ -469,7 +469,6 @@ __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
 
 template <int D>
 __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
-  constexpr int KQ = D / 4;     // dims of one lane group in the QK product
   constexpr int NK4 = D / 32;   // 16-byte K loads per lane per page
   constexpr int NB = D / 16;    // 16-dim blocks of the PV product
   constexpr int NS = D / 16;    // MFMA k-steps of the QK product
@@ -480,19 +479,28 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   const int lane = tid() & 63, w = tid() >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
   const int32_t* prow = a.page_table + (size_t)b * a.max_pages;
-  // this wave's first two page ids, read together with the position (the
-  // plan maps every page below its bound)
+  // Pages stream through a ring of NBUF register buffers per wave (wave w
+  // takes the task's pages w, w + NWAVE, ...). The wave's first NBUF page ids
+  // are read directly, together with the position; the ids of every page of
+  // the task go to an LDS table for the rest, so a refill never waits on a
+  // page-table load (the plan maps every page below its bound).
+  constexpr int NBUF = 4;
   const int first = pg0 + w;
-  const int32_t ph0 = first < pg0 + npg ? prow[first] : -1;
-  const int32_t ph1 = first + NWAVE < pg0 + npg ? prow[first + NWAVE] : -1;
+  int32_t ph[NBUF];
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j) ph[j] = first + j * NWAVE < pg0 + npg ? prow[first + j * NWAVE] : -1;
   const int pos = a.seq_lens[b];
+  int* pid = (int*)s.res;  // [npg]
+  int32_t tbl[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) tbl[j] = tid() + j * NT < npg ? prow[pg0 + tid() + j * NT] : -1;
   const int n_tok = min(pos + 1, a.bound);
   const int pg_lim = min(pg0 + npg, (n_tok + 15) >> 4);
   const int cnt = first < pg_lim ? (pg_lim - first + NWAVE - 1) / NWAVE : 0;
   const int cur = pos >> 4, ns = pos & 15;
   const uint16_t* lbase = a.pool + (size_t)l * a.layer_stride + (size_t)g * 2 * 16 * D;
-  uint4 k0[NK4], k1[NK4];
-  uint2 v0[NB], v1[NB];
+  uint4 kb[NBUF][NK4];
+  uint2 vb[NBUF][NB];
   bool bad = false;
   auto load = [&](uint4 (&kk)[NK4], uint2 (&vv)[NB], int pg, int32_t phys) {
     if (phys < 0 || phys >= a.n_pages) {
@@ -503,16 +511,26 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       for (int i = 0; i < NB; ++i) vv[i] = make_uint2(0, 0);
       return;
     }
-    const uint16_t* base = lbase + (size_t)phys * a.page_stride;
-    const uint4* kp = (const uint4*)(base + r16 * D + kq * KQ);
+    // the page block is stored in operand order (kv_k_offset, kv_v_offset):
+    // K chunk i of this lane (dims 32 i + 8 kq .. + 7 of slot r16) and V chunk
+    // m (slots 4 kq .. + 3 of dims 32 m + r16 and 32 m + 16 + r16) are the
+    // lane's 16 bytes of one contiguous kilobyte
+    const uint4* kp = (const uint4*)(lbase + (size_t)phys * a.page_stride) + lane;
 #pragma unroll
-    for (int i = 0; i < NK4; ++i) kk[i] = ld_nt(kp + i);
-    const uint16_t* vp = base + 16 * D + r16 * 16 + kq * 4;
+    for (int i = 0; i < NK4; ++i) kk[i] = ld_nt(kp + 64 * i);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) vv[nb] = ld_nt2((const uint2*)(vp + nb * 256));
+    for (int m = 0; m < NB / 2; ++m) {
+      const uint4 v = ld_nt(kp + 2 * D + 64 * m);
+      vv[2 * m] = make_uint2(v.x, v.y);
+      vv[2 * m + 1] = make_uint2(v.z, v.w);
+    }
   };
-  if (cnt > 0) load(k0, v0, first, ph0);
-  if (cnt > 1) load(k1, v1, first + NWAVE, ph1);
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j)
+    if (j < cnt) load(kb[j], vb[j], first + j * NWAVE, ph[j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (tid() + j * NT < npg) pid[tid() + j * NT] = tbl[j];
 
   // inputs: the group's queries and the new token's K and V (bf16 bits), one batch
   float* qv = s.vec;                 // [HG][D]
@@ -530,10 +548,11 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   v4s qop[NS];
   {
     const bool valid = hh < HG;
-    const float* qp = qv + (valid ? hh : 0) * D + kq * KQ;
+    // k-step st covers dims 8 kq + 32 (st / 2) + 4 (st % 2) .. + 3, as the K chunks
+    const float* qp = qv + (valid ? hh : 0) * D + 8 * kq;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      const float4 x = valid ? *(const float4*)(qp + 4 * st) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 x = valid ? *(const float4*)(qp + 32 * (st >> 1) + 4 * (st & 1)) : make_float4(0.f, 0.f, 0.f, 0.f);
       const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -548,92 +567,124 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
   const float scale = a.attn_scale;
-  auto compute = [&](uint4 (&kk)[NK4], uint2 (&vv)[NB], int pg) {
-    if (pg == cur) {
-      // the new token's slot: its K and V come from this step's QKV tasks
-      if (r16 == ns) {
+  // the new token's slot of page pg: its K and V come from this step's QKV tasks
+  auto patch = [&](uint4 (&kk)[NK4], uint2 (&vv)[NB], int pg) {
+    if (pg != cur) return;
+    if (r16 == ns) {
 #pragma unroll
-        for (int i = 0; i < NK4; ++i) {
-          const float* kn = kvnew + kq * KQ + 8 * i;
-          kk[i] = make_uint4(__float_as_uint(kn[0]) | (__float_as_uint(kn[1]) << 16),
-                             __float_as_uint(kn[2]) | (__float_as_uint(kn[3]) << 16),
-                             __float_as_uint(kn[4]) | (__float_as_uint(kn[5]) << 16),
-                             __float_as_uint(kn[6]) | (__float_as_uint(kn[7]) << 16));
-        }
-      }
-      if (kq == (ns >> 2)) {
-        const int e = ns & 3;
-        const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        const int sh = (e & 1) ? 16 : 0;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const uint32_t vb = __float_as_uint(kvnew[D + nb * 16 + r16]) << sh;
-          const uint32_t x = vv[nb].x, y = vv[nb].y;
-          vv[nb] = e < 2 ? make_uint2((x & keep) | vb, y) : make_uint2(x, (y & keep) | vb);
-        }
+      for (int i = 0; i < NK4; ++i) {
+        const float* kn = kvnew + 8 * kq + 32 * i;
+        kk[i] = make_uint4(__float_as_uint(kn[0]) | (__float_as_uint(kn[1]) << 16),
+                           __float_as_uint(kn[2]) | (__float_as_uint(kn[3]) << 16),
+                           __float_as_uint(kn[4]) | (__float_as_uint(kn[5]) << 16),
+                           __float_as_uint(kn[6]) | (__float_as_uint(kn[7]) << 16));
       }
     }
-    v4f S = {0.f, 0.f, 0.f, 0.f};
+    if (kq == (ns >> 2)) {
+      const int e = ns & 3;
+      const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      const int sh = (e & 1) ? 16 : 0;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      const uint4 kv = kk[st >> 1];
-      const u2v pr = (st & 1) ? u2v{kv.z, kv.w} : u2v{kv.x, kv.y};
-      S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, pr), qop[st], S, 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t vbits = __float_as_uint(kvnew[D + nb * 16 + r16]) << sh;
+        const uint32_t x = vv[nb].x, y = vv[nb].y;
+        vv[nb] = e < 2 ? make_uint2((x & keep) | vbits, y) : make_uint2(x, (y & keep) | vbits);
+      }
     }
-    float sv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x = (S[j] + __shfl_xor(S[j], 8, 64)) * scale;
-      sv[j] = (pg * 16 + 4 * kq + j) < n_tok ? x : NEG_INF;
-    }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m_run, mx);
-    const float alpha = mn == NEG_INF ? 1.f : expf(m_run - mn);
-    float pj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pj[j] = sv[j] == NEG_INF ? 0.f : expf(sv[j] - mn);
-    float ps = (pj[0] + pj[1]) + (pj[2] + pj[3]);
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * alpha + ps;
-    m_run = mn;
-    v4s P;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t hi = f2bf(pj[j]);
-      P[j] = (short)(lo_part ? f2bf(pj[j] - bf2f(hi)) : hi);
-    }
-    float aj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, (4 * kq + j) & 7, 64);
-    // Slots at or past the live context may hold stale bits (even NaN) from an
-    // earlier owner of the page: their probability is 0, but 0 * NaN is not,
-    // so this lane's four V slots 4kq .. 4kq+3 are zeroed where invalid.
+  };
+  // Slots at or past the live context may hold stale bits (even NaN) from an
+  // earlier owner of the page: their probability is 0, but 0 * NaN is not, so
+  // this lane's four V slots 4kq .. 4kq+3 of page pg are zeroed where invalid.
+  auto vmask = [&](int pg, uint32_t& mlo, uint32_t& mhi) {
     const int valid = n_tok - pg * 16;
-    uint32_t mlo = 0xFFFFFFFFu, mhi = 0xFFFFFFFFu;
+    mlo = 0xFFFFFFFFu;
+    mhi = 0xFFFFFFFFu;
     if (valid < 16) {
       const int s0 = 4 * kq;
       mlo = (s0 < valid ? 0x0000FFFFu : 0u) | (s0 + 1 < valid ? 0xFFFF0000u : 0u);
       mhi = (s0 + 2 < valid ? 0x0000FFFFu : 0u) | (s0 + 3 < valid ? 0xFFFF0000u : 0u);
     }
+  };
+  // Two pages per online-softmax update: their MFMA chains, shuffles and
+  // exponentials are independent and overlap. A page index at or past the
+  // live context (the odd page out) contributes nothing.
+  auto compute2 = [&](uint4 (&kA)[NK4], uint2 (&vA)[NB], int pgA, uint4 (&kB)[NK4], uint2 (&vB)[NB],
+                      int pgB) {
+    patch(kA, vA, pgA);
+    patch(kB, vB, pgB);
+    v4f SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const uint4 ka = kA[st >> 1], kb2 = kB[st >> 1];
+      const u2v pa = (st & 1) ? u2v{ka.z, ka.w} : u2v{ka.x, ka.y};
+      const u2v pb = (st & 1) ? u2v{kb2.z, kb2.w} : u2v{kb2.x, kb2.y};
+      SA = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, pa), qop[st], SA, 0, 0, 0);
+      SB = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, pb), qop[st], SB, 0, 0, 0);
+    }
+    float sa[4], sb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float xa = (SA[j] + __shfl_xor(SA[j], 8, 64)) * scale;
+      const float xb = (SB[j] + __shfl_xor(SB[j], 8, 64)) * scale;
+      sa[j] = (pgA * 16 + 4 * kq + j) < n_tok ? xa : NEG_INF;
+      sb[j] = (pgB * 16 + 4 * kq + j) < n_tok ? xb : NEG_INF;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
+                     fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = mn == NEG_INF ? 1.f : expf(m_run - mn);
+    float qa[4], qb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qa[j] = sa[j] == NEG_INF ? 0.f : expf(sa[j] - mn);
+      qb[j] = sb[j] == NEG_INF ? 0.f : expf(sb[j] - mn);
+    }
+    float ps = ((qa[0] + qa[1]) + (qa[2] + qa[3])) + ((qb[0] + qb[1]) + (qb[2] + qb[3]));
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * alpha + ps;
+    m_run = mn;
+    v4s PA, PB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t ha = f2bf(qa[j]), hb = f2bf(qb[j]);
+      PA[j] = (short)(lo_part ? f2bf(qa[j] - bf2f(ha)) : ha);
+      PB[j] = (short)(lo_part ? f2bf(qb[j] - bf2f(hb)) : hb);
+    }
+    float aj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, (4 * kq + j) & 7, 64);
+    uint32_t mla, mha, mlb, mhb;
+    vmask(pgA, mla, mha);
+    vmask(pgB, mlb, mhb);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[nb][j] *= aj[j];
-      const uint2 vm = make_uint2(vv[nb].x & mlo, vv[nb].y & mhi);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, __builtin_bit_cast(v4s, vm), acc[nb], 0, 0, 0);
+      const uint2 va = make_uint2(vA[nb].x & mla, vA[nb].y & mha);
+      const uint2 vb2 = make_uint2(vB[nb].x & mlb, vB[nb].y & mhb);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(PA, __builtin_bit_cast(v4s, va), acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(PB, __builtin_bit_cast(v4s, vb2), acc[nb], 0, 0, 0);
     }
   };
-  // page i of this wave is in (k0, v0), page i + 1 in flight in (k1, v1)
-  for (int i = 0; i < cnt; ++i) {
-    compute(k0, v0, first + i * NWAVE);
+  // page i of this wave is in buffer i % NBUF; pages go two at a time, and a
+  // used buffer takes page i + NBUF
+  static_assert(NBUF % 2 == 0, "pages are taken in pairs");
+  constexpr int NO_PAGE = 1 << 24;  // a page index past any context: contributes nothing
+  for (int i0 = 0; i0 < cnt; i0 += NBUF) {
 #pragma unroll
-    for (int q = 0; q < NK4; ++q) k0[q] = k1[q];
-#pragma unroll
-    for (int q = 0; q < NB; ++q) v0[q] = v1[q];
-    if (i + 2 < cnt) load(k1, v1, first + (i + 2) * NWAVE, prow[first + (i + 2) * NWAVE]);
+    for (int j = 0; j < NBUF; j += 2) {
+      const int i = i0 + j;
+      if (i < cnt) {
+        compute2(kb[j], vb[j], first + i * NWAVE, kb[j + 1], vb[j + 1],
+                 i + 1 < cnt ? first + (i + 1) * NWAVE : NO_PAGE);
+        if (i + NBUF < cnt) load(kb[j], vb[j], first + (i + NBUF) * NWAVE, pid[w + (i + NBUF) * NWAVE]);
+        if (i + 1 + NBUF < cnt)
+          load(kb[j + 1], vb[j + 1], first + (i + 1 + NBUF) * NWAVE, pid[w + (i + 1 + NBUF) * NWAVE]);
+      }
+    }
   }
   mark(c, 2);
   if (bad && lane == 0) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)b, 0xFFFFFFFFu);

@@ -125,6 +125,19 @@ MK_HD inline int qkv_pair(int p, int g, int HG, int D, int Hq, int Hkv, int* hea
   *head = g; *i = p; *row = (Hq + Hkv) * D + g * D + p; return 2;
 }
 
+// Element offsets of K[s][dim] and V[s][dim] of one token slot s within a
+// page block of one (page, layer, kv head) (2 x 16 x D bf16): the order in
+// which the attention MFMA operands are loaded, so that every 64-lane load
+// is one contiguous kilobyte. K chunk i of lane (s, kq) holds dims
+// 32 i + 8 kq .. + 7 of slot s; V chunk m of lane (r, kq) holds slots
+// 4 kq .. + 3 of dims 32 m + r and 32 m + 16 + r.
+MK_HD inline int kv_k_offset(int s, int dim) {
+  return (((dim >> 5) * 4 + ((dim & 31) >> 3)) * 16 + s) * 8 + (dim & 7);
+}
+MK_HD inline int kv_v_offset(int s, int dim, int D) {
+  return 16 * D + (((dim >> 5) * 4 + (s >> 2)) * 16 + (dim & 15)) * 8 + ((dim & 31) >> 4) * 4 + (s & 3);
+}
+
 // Kernel variants: the megakernel is compiled once per shape class, given by
 // the GEMV mappings (lane-group width, 16-byte chunks per lane) of the
 // hidden size, the attention output (query heads x head dim) and the FFN

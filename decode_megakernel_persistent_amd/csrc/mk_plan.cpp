@@ -184,6 +184,10 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   const int pg_total = pg_bound * B * Hkv;
   int pps = o && o->attn_split_pages > 0 ? o->attn_split_pages : (pg_total + n_cu - 1) / n_cu;
   pps = std::max(std::max(1, pps), (pg_bound + 1023) / 1024);  // at most 1024 splits per (b, g)
+  if (pps > 2 * mk::NT) {
+    delete p;
+    return fail(MK_EUNSUPPORTED, "mk_plan: more than " + std::to_string(2 * mk::NT) + " pages per attention split");
+  }
   p->n_split.assign(B, 0);
   for (int b = 0; b < B; ++b) p->n_split[b] = (pg_bound + pps - 1) / pps;
   p->S_max = *std::max_element(p->n_split.begin(), p->n_split.end());

@@ -76,9 +76,22 @@ __global__ void k_fill_kv(uint16_t* pool, const int32_t* page_row, uint64_t seed
     uint32_t g = (uint32_t)(r % Hkv); r /= Hkv;
     uint32_t l = (uint32_t)(r % L); r /= L;
     uint32_t pg = (uint32_t)r;  // logical page index within the sequence
+    // block layout (the library's KV pool format, operand order): K element
+    // ((dim/32*4 + dim%32/8)*16 + s)*8 + dim%8, then V element
+    // ((dim/32*4 + s/4)*16 + dim%16)*8 + (dim%32/16)*4 + s%4
     uint32_t kv, s, i;
-    if (e < (uint64_t)PT * d) { kv = 0; s = (uint32_t)(e / d); i = (uint32_t)(e % d); }
-    else { uint64_t e2 = e - (uint64_t)PT * d; kv = 1; i = (uint32_t)(e2 / PT); s = (uint32_t)(e2 % PT); }
+    if (e < (uint64_t)PT * d) {
+      kv = 0;
+      const uint32_t c = (uint32_t)(e / 8), e8 = (uint32_t)(e % 8), q = c / 16;
+      s = c % 16;
+      i = (q / 4) * 32 + (q % 4) * 8 + e8;
+    } else {
+      kv = 1;
+      const uint64_t e2 = e - (uint64_t)PT * d;
+      const uint32_t c = (uint32_t)(e2 / 8), e8 = (uint32_t)(e2 % 8), q = c / 16, r = c % 16;
+      s = (q % 4) * 4 + (e8 % 4);
+      i = (q / 4) * 32 + (e8 / 4) * 16 + r;
+    }
     uint32_t t = pg * PT + s;
     if (t >= ctx || pg >= n_pg) continue;
     uint64_t kind = kv ? (uint64_t)FX_VCACHE : (uint64_t)FX_KCACHE;

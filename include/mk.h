@@ -36,10 +36,14 @@
  *  - KV pool: bf16 pages of page_tokens (= 16) tokens holding every layer.
  *    For physical page p, layer l, kv head g, the block of 2*16*d elements
  *    starting at element p*page_stride + l*layer_stride + g*(2*16*d) holds
- *    K as [slot][dim] (16*d elements) followed by V as [dim][slot] (16*d
- *    elements), where layer_stride = Hkv*2*16*d and page_stride =
- *    L*layer_stride. Token t of sequence b is in page page_table[b][t/16],
- *    slot t%16.
+ *    K (16*d elements) then V (16*d elements), where layer_stride =
+ *    Hkv*2*16*d and page_stride = L*layer_stride. Token t of sequence b is
+ *    in page page_table[b][t/16], slot s = t%16. Within the block, in the
+ *    order the attention MFMA operands are read (each 64 consecutive
+ *    16-byte chunks are one 64-lane load):
+ *      K[s][dim]: element ((dim/32*4 + dim%32/8)*16 + s)*8 + dim%8
+ *      V[s][dim]: element 16*d + ((dim/32*4 + s/4)*16 + dim%16)*8
+ *                 + (dim%32/16)*4 + s%4
  */
 #ifndef MK_H
 #define MK_H

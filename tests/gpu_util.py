@@ -32,3 +32,13 @@ def argmax_near_tie(logits, a, b):
 
 def flush(msg):
     print(msg, flush=True)
+
+
+def kv_offsets(s, d):
+    """Element offsets, within one (page, layer, kv head) block of the KV pool,
+    of K[s][0..d) and V[s][0..d) for token slot s, in the pool's documented
+    operand order."""
+    dim = torch.arange(d)
+    k = (((dim // 32) * 4 + (dim % 32) // 8) * 16 + s) * 8 + dim % 8
+    v = 16 * d + (((dim // 32) * 4 + s // 4) * 16 + dim % 16) * 8 + ((dim % 32) // 16) * 4 + s % 4
+    return k, v

@@ -14,21 +14,23 @@ import torch
 
 import oracle as O
 from fixtures.session import gpu_session, oracle_inputs, spec
-from gpu_util import HIDDEN_TOL, argmax_near_tie, flush, rel_err, topk_near_tie
+from gpu_util import HIDDEN_TOL, argmax_near_tie, flush, kv_offsets, rel_err, topk_near_tie
 
 pytestmark = pytest.mark.gpu
 
 
+def _block_base(dec, m, b, l, g, pos):
+    d, pt, Hkv, L = m["head_dim"], m["page_tokens"], m["n_kv_heads"], m["n_layers"]
+    page = int(dec.page_table[b, pos // pt])
+    return ((page * L + l) * Hkv + g) * 2 * pt * d
+
+
 def _pool_slot(dec, m, b, l, g, pos):
     """(k [d], v [d]) bf16 at position pos of sequence b in the device pool."""
-    d, pt, Hkv, L = m["head_dim"], m["page_tokens"], m["n_kv_heads"], m["n_layers"]
-    blk = 2 * pt * d
-    page = int(dec.page_table[b, pos // pt])
-    base = ((page * L + l) * Hkv + g) * blk
-    slot = pos % pt
-    k = dec.pool[base + slot * d: base + (slot + 1) * d]
-    v = dec.pool[base + pt * d: base + 2 * pt * d].view(d, pt)[:, slot]
-    return k.cpu(), v.cpu()
+    base = _block_base(dec, m, b, l, g, pos)
+    ko, vo = kv_offsets(pos % m["page_tokens"], m["head_dim"])
+    blk = dec.pool[base: base + 2 * m["page_tokens"] * m["head_dim"]].cpu()
+    return blk[ko], blk[vo]
 
 
 def run_step_parity(name, seed=0, **over):
@@ -96,13 +98,12 @@ def run_step_parity(name, seed=0, **over):
     d, pt, Hkv = m["head_dim"], m["page_tokens"], m["n_kv_heads"]
     for b in range(B):
         pos = w["ctx"][b]
-        page = int(dec.page_table[b, pos // pt])
+        ko, vo = kv_offsets(pos % pt, d)
         for l in range(L):
             for g in range(Hkv):
-                base = ((page * L + l) * Hkv + g) * 2 * pt * d
-                slot = pos % pt
-                mask[base + slot * d: base + (slot + 1) * d] = True
-                mask[base + pt * d + slot: base + 2 * pt * d: pt] = True
+                base = _block_base(dec, m, b, l, g, pos)
+                mask[(base + ko).to(mask.device)] = True
+                mask[(base + vo).to(mask.device)] = True
     assert not bool((changed & ~mask).any()), "pool bytes outside the new slots changed"
 
     # counters: every counter at epoch x producers; sequence lengths advanced

@@ -263,3 +263,23 @@ def test_rope_table_matches_oracle():
         oc, os_ = O.rope_cos_sin(1e4, 128, p)
         assert np.array_equal(c.reshape(n, 64)[p], oc.numpy())
         assert np.array_equal(s.reshape(n, 64)[p], os_.numpy())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kv_page_layout_is_a_bijection(d):
+    # every element of a page block is the K or V of exactly one (slot, dim)
+    import torch
+    from gpu_util import kv_offsets
+    seen = torch.zeros(2 * 16 * d, dtype=torch.int64)
+    for s in range(16):
+        k, v = kv_offsets(s, d)
+        seen[k] += 1
+        seen[v] += 1
+    assert bool((seen == 1).all())
+    # a 64-lane operand load is one contiguous kilobyte: lane L = 16 kq + s of
+    # K chunk i holds dims 32 i + 8 kq .. + 7 at chunk index 64 i + L
+    for i in range(d // 32):
+        for kq in range(4):
+            for s in range(16):
+                k, _ = kv_offsets(s, d)
+                assert int(k[32 * i + 8 * kq]) == (64 * i + 16 * kq + s) * 8
