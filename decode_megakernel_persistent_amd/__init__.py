@@ -159,13 +159,17 @@ def mk_step_bytes(desc, seq_lens, distinct=None):
     return w.value, r.value, wr.value
 
 
-def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0):
+MK_PLAN_ATTN_QUEUE = 1
+MK_PLAN_NO_ATTN_QUEUE = 2
+
+
+def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0, flags=0):
     """Build a plan. page_table: flat host list/array of batch*max_pages int32."""
     B = len(seq_lens)
     sl = (_i32 * B)(*[int(v) for v in seq_lens])
     pt = (_i32 * (B * max_pages))(*[int(v) for v in page_table])
     bd = mk_batch_desc(B, max_pages, sl, pt, bound)
-    op = mk_plan_opts(n_cu, attn_split_pages, 0)
+    op = mk_plan_opts(n_cu, attn_split_pages, flags)
     out = _vp()
     _check(_lib.mk_plan(ctypes.byref(desc), ctypes.byref(bd), ctypes.byref(op), ctypes.byref(out)))
     return out.value

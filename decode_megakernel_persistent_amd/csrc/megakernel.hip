@@ -59,6 +59,7 @@ struct Smem {
   float route_w[16];
   int route_ids[16];
   int fail;
+  uint32_t qnext;      // attention queue: the split this workgroup takes next
   uint64_t tw[4];      // trace: (begin, end) of the routing wait and of the data wait
   uint64_t mk[TRACE_MARKS];  // trace: body-specific marks
 };
@@ -1109,7 +1110,40 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
     bool ok = true;
     switch (t.op) {
       case OP_QKV: ok = task_qkv<CH, TCH, HD>(c, t); break;
-      case OP_ATTN: ok = task_attn<HD>(c, t); break;
+      case OP_ATTN: {
+        // One split, or splits from the shared queue: every pull adds one to
+        // the queue counter; this step's pulls are numbered from base =
+        // (epoch - 1) * (splits + queue tasks), since each queue task's last
+        // pull comes back empty. The next split is pulled while one runs.
+        const bool queue = (t.flags & TF_QUEUE) != 0;
+        uint32_t* qc = a.ctr + (size_t)t.a0 * CTR_LINES * CTR_STRIDE;
+        const uint32_t n_items = queue ? (uint32_t)(a.Hkv * t.a1) : 1u;
+        const uint32_t base = (a.epoch - 1u) * (n_items + (uint32_t)t.a3);
+        if (queue && tid() == 0)
+          s.qnext = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base;
+        if (queue) lds_barrier();
+        Task tt = t;
+        while (true) {
+          uint32_t nxt = 0;
+          if (queue) {
+            const uint32_t idx = s.qnext;
+            if (idx >= n_items) break;
+            lds_barrier();  // every wave has read qnext
+            if (tid() == 0) nxt = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int split = (int)(idx % (uint32_t)t.a1);
+            tt.a0 = 0;
+            tt.a1 = (int)(idx / (uint32_t)t.a1);
+            tt.a2 = split * t.a2;
+            tt.a3 = min(t.a2, ((a.bound + 15) >> 4) - tt.a2);
+            tt.aux = (uint16_t)split;
+          }
+          ok = task_attn<HD>(c, tt);
+          if (!ok || !queue) break;
+          if (tid() == 0) s.qnext = nxt - base;
+          lds_barrier();
+        }
+        break;
+      }
       case OP_COMB: ok = task_comb(c, t); break;
       case OP_O: ok = task_o<CO, TCO>(c, t); break;
       case OP_ROUTER: ok = task_router<CH, TCH>(c, t); break;

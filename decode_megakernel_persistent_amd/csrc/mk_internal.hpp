@@ -20,7 +20,10 @@ namespace mk {
 enum Op : uint8_t {
   OP_NONE = 0,
   OP_QKV = 1,     // a0 = kv group g, a1 = first rotary pair, a2 = pairs
-  OP_ATTN = 2,    // a0 = b, a1 = g, a2 = first page, a3 = pages; aux = split index
+  OP_ATTN = 2,    // a0 = b, a1 = g, a2 = first page, a3 = pages; aux = split index;
+                  // with TF_QUEUE: splits pulled from a shared queue: a0 = queue
+                  // counter, a1 = splits per kv head, a2 = pages per split, a3 =
+                  // queue tasks of the layer
   OP_COMB = 3,    // a0 = b, a1 = query head, a2 = first dim, a3 = dims; aux = splits of (b, g)
   OP_O = 4,       // a1 = first row, a2 = rows
   OP_ROUTER = 5,  // a1 = first expert row, a2 = rows
@@ -33,7 +36,10 @@ enum Op : uint8_t {
   OP_COUNT = 10
 };
 
-enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1 };
+enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2 };
+
+// Pages per attention split when long contexts use the shared split queue.
+constexpr int QUEUE_PAGES = 64;
 
 constexpr uint16_t NO_CTR = 0xFFFF;
 

@@ -165,10 +165,27 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     p->ctr_name.push_back(name);
     return (int32_t)p->targets.size() - 1;
   };
+  // attention: static splits of about pg_total / n_cu pages each, or (when
+  // asked for) a shared queue of QUEUE_PAGES-page splits that every compute
+  // unit pulls from, so that units streaming faster take more of them. On
+  // MI355X the static splits are faster even at 262144 tokens: a pulled split
+  // restarts its page pipeline, its query gather and its merge.
+  const int pg_total = pg_bound * B * Hkv;
+  const int flags = o ? o->flags : 0;
+  int pps = o && o->attn_split_pages > 0 ? o->attn_split_pages : (pg_total + n_cu - 1) / n_cu;
+  const bool queue = !(flags & MK_PLAN_NO_ATTN_QUEUE) && B == 1 && (flags & MK_PLAN_ATTN_QUEUE);
+  if (queue) pps = mk::QUEUE_PAGES;
+  p->attn_queue = queue;
   for (int l = 0; l < L; ++l) {
     const std::string ls = std::to_string(l);
-    for (int g = 0; g < Hkv; ++g) p->c_qkv.push_back(new_ctr("qkv[" + ls + "][" + std::to_string(g) + "]"));
-    for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + ls + "][" + std::to_string(g) + "]"));
+    if (queue) {  // one QKV and one attention counter per layer: a queue task takes any group
+      const int cq = new_ctr("qkv[" + ls + "]"), ca = new_ctr("attn[" + ls + "]");
+      for (int g = 0; g < Hkv; ++g) p->c_qkv.push_back(cq), p->c_attn.push_back(ca);
+      p->c_queue.push_back(new_ctr("queue[" + ls + "]"));
+    } else {
+      for (int g = 0; g < Hkv; ++g) p->c_qkv.push_back(new_ctr("qkv[" + ls + "][" + std::to_string(g) + "]"));
+      for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + ls + "][" + std::to_string(g) + "]"));
+    }
     p->c_comb.push_back(new_ctr("comb[" + ls + "]"));
     p->c_o.push_back(new_ctr("o[" + ls + "]"));
     p->c_router.push_back(moe ? new_ctr("router[" + ls + "]") : -1);
@@ -180,9 +197,6 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     return fail(MK_EUNSUPPORTED, "mk_plan: too many counters");
   }
 
-  // attention splits: pages per split chosen so the step has about n_cu split tasks
-  const int pg_total = pg_bound * B * Hkv;
-  int pps = o && o->attn_split_pages > 0 ? o->attn_split_pages : (pg_total + n_cu - 1) / n_cu;
   pps = std::max(std::max(1, pps), (pg_bound + 1023) / 1024);  // at most 1024 splits per (b, g)
   if (pps > 2 * mk::NT) {
     delete p;
@@ -192,6 +206,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   for (int b = 0; b < B; ++b) p->n_split[b] = (pg_bound + pps - 1) / pps;
   p->S_max = *std::max_element(p->n_split.begin(), p->n_split.end());
   p->comb_dim_tasks = std::max(1, std::min(D / 8, n_cu / std::max(1, B * Hq)));
+  while (p->comb_dim_tasks < D / 8 && (size_t)p->S_max * (ceil_div(D, p->comb_dim_tasks) + 2) > 8192)
+    p->comb_dim_tasks *= 2;  // fewer dims per combine task when there are many splits
 
   std::vector<std::vector<Task>> stages;
   auto ctr16 = [](int c) { return c < 0 ? mk::NO_CTR : (uint16_t)c; };
@@ -212,8 +228,19 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         }
       stages.push_back(st);
     }
-    // ATTN: split-KV tasks per (b, g)
-    {
+    // ATTN: split-KV tasks per (b, g), or one queue task per compute unit
+    if (queue) {
+      std::vector<Task> st;
+      for (int i = 0; i < n_cu; ++i) {
+        Task t = mk_task(mk::OP_ATTN, l);
+        t.flags = mk::TF_QUEUE;
+        t.wait_b = ctr16(p->c_qkv[l * Hkv]);
+        t.signal = ctr16(p->c_attn[l * Hkv]);
+        t.a0 = p->c_queue[l]; t.a1 = p->n_split[0]; t.a2 = mk::QUEUE_PAGES; t.a3 = n_cu;
+        st.push_back(t);
+      }
+      stages.push_back(st);
+    } else {
       std::vector<Task> st;
       for (int b = 0; b < B; ++b)
         for (int g = 0; g < Hkv; ++g) {
@@ -340,10 +367,13 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   }
   p->n_stages = (int)stages.size();
 
-  // producer counts -> targets, then the per-epoch counts carried by the waits
+  // producer counts -> targets, then the per-epoch counts carried by the waits;
+  // a queue counter gains one per split taken and one per queue task's final,
+  // empty pull
   for (auto& st : stages)
     for (auto& t : st)
       if (t.signal != mk::NO_CTR) p->targets[t.signal]++;
+  for (int32_t q : p->c_queue) p->targets[q] = (uint32_t)(Hkv * p->n_split[0] + n_cu);
   for (auto& st : stages)
     for (auto& t : st) {
       if (t.wait_a != mk::NO_CTR) t.cnt_a = (uint16_t)p->targets[t.wait_a];
@@ -445,6 +475,7 @@ void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::
       }
       break;
     case mk::OP_ATTN:
+      if (t.flags & mk::TF_QUEUE) break;  // the queue's splits are counted once per layer
       for (int pg = t.a2; pg < t.a2 + t.a3; ++pg)
         out.push_back({"attn" + ls, ((int64_t)t.a0 * Hkv + t.a1) * 1000000 + pg});
       break;
@@ -533,6 +564,13 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
       }
     }
   }
+  if (p->attn_queue) {  // every split of the queue, once per layer
+    const int pg_bound = (p->bound + 15) / 16;
+    for (int l = 0; l < L; ++l)
+      for (int g = 0; g < m.n_kv_heads; ++g)
+        for (int pg = 0; pg < pg_bound; ++pg)
+          got["attn:" + std::to_string(l)].insert((int64_t)g * 1000000 + pg);
+  }
   for (auto& [key, s0] : want) {
     auto it = got.find(key);
     if (it == got.end()) return fail(MK_EINVAL, "validate: no task covers " + key);
@@ -540,8 +578,9 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
       return fail(MK_EINVAL, "validate: outputs of " + key + " not covered exactly once");
   }
   if (got.size() != want.size()) return fail(MK_EINVAL, "validate: tasks of an unexpected kind");
+  std::set<int32_t> queues(p->c_queue.begin(), p->c_queue.end());
   for (size_t c = 0; c < p->targets.size(); ++c)
-    if (producers[c] != p->targets[c])
+    if (!queues.count((int32_t)c) && producers[c] != p->targets[c])
       return fail(MK_EINVAL, "validate: counter " + p->ctr_name[c] + " target != producer count");
   k = 0;
   for (int cu = 0; cu < p->n_cu; ++cu)
@@ -577,7 +616,11 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
   for (int cu = 0; cu < p->n_cu; ++cu)
     for (auto& t : p->lists[cu]) {
       total[slot(t.op, t.layer, Hkv)]++;
-      if (t.op == mk::OP_QKV || t.op == mk::OP_ATTN) total[slot(t.op, t.layer, t.op == mk::OP_QKV ? t.a0 : t.a1)]++;
+      if (t.op == mk::OP_ATTN && (t.flags & mk::TF_QUEUE)) {
+        for (int g = 0; g < Hkv; ++g) total[slot(t.op, t.layer, g)]++;
+      } else if (t.op == mk::OP_QKV || t.op == mk::OP_ATTN) {
+        total[slot(t.op, t.layer, t.op == mk::OP_QKV ? t.a0 : t.a1)]++;
+      }
     }
   for (int run = 0; run < n_runs; ++run) {
     const uint64_t epoch = (uint64_t)run + 1;
@@ -596,7 +639,8 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
       int l = t.layer;
       switch (t.op) {
         case mk::OP_QKV: return l == 0 || all_done(mk::OP_EXPERT, l - 1, Hkv);
-        case mk::OP_ATTN: return all_done(mk::OP_QKV, l, t.a1);
+        case mk::OP_ATTN:
+          return (t.flags & mk::TF_QUEUE) ? all_done(mk::OP_QKV, l, Hkv) : all_done(mk::OP_QKV, l, t.a1);
         case mk::OP_COMB: return all_done(mk::OP_ATTN, l, t.a1 / HG);
         case mk::OP_O: return all_done(mk::OP_COMB, l, Hkv);
         case mk::OP_ROUTER: return all_done(mk::OP_O, l, Hkv);
@@ -654,10 +698,15 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
         remaining--;
         done[slot(t.op, t.layer, Hkv)]++;
         if (t.op == mk::OP_QKV) done[slot(t.op, t.layer, t.a0)]++;
-        if (t.op == mk::OP_ATTN) done[slot(t.op, t.layer, t.a1)]++;
+        if (t.op == mk::OP_ATTN && (t.flags & mk::TF_QUEUE)) {
+          for (int g = 0; g < Hkv; ++g) done[slot(t.op, t.layer, g)]++;
+        } else if (t.op == mk::OP_ATTN) {
+          done[slot(t.op, t.layer, t.a1)]++;
+        }
         if (t.signal != mk::NO_CTR) ctr[t.signal]++;
       }
     }
+    for (int32_t q : p->c_queue) ctr[q] += p->targets[q];  // the pulls of the queue tasks
     for (size_t c = 0; c < ctr.size(); ++c)
       if (ctr[c] != epoch * p->targets[c])
         return fail(MK_ESTATE, "simulate: counter " + p->ctr_name[c] + " ends epoch off target");

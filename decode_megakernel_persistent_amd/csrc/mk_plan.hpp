@@ -22,7 +22,9 @@ struct mk_plan {
   // counter ids
   std::vector<int32_t> c_qkv, c_attn;  // [L][Hkv]
   std::vector<int32_t> c_comb, c_o, c_router, c_expert;  // [L]
+  std::vector<int32_t> c_queue;  // [L] attention split queue (queue mode)
   int32_t c_lm = -1;
+  bool attn_queue = false;
 
   int32_t S_max = 0;                // attention splits per (b, g), max over b
   int32_t comb_dim_tasks = 1;       // combine tasks per (b, query head)

@@ -53,13 +53,13 @@ class Decoder:
     """
 
     def __init__(self, model, weights, pool, n_pages, seq_lens, page_table, max_pages, bound,
-                 n_cu=0, attn_split_pages=0, device="cuda", trace=False):
+                 n_cu=0, attn_split_pages=0, device="cuda", trace=False, plan_flags=0):
         self.m = dict(model)
         self.device = torch.device(device)
         self.B = len(seq_lens)
         self.desc = model_desc(self.m)
         flat = [int(v) for row in page_table for v in row]
-        self.plan = mk_plan(self.desc, seq_lens, flat, max_pages, bound, n_cu, attn_split_pages)
+        self.plan = mk_plan(self.desc, seq_lens, flat, max_pages, bound, n_cu, attn_split_pages, plan_flags)
         self.bound = bound
         dev = self.device
         self.plan_buf = torch.empty(mk_plan_device_bytes(self.plan), dtype=torch.uint8, device=dev)

@@ -38,7 +38,8 @@ def lease_pages(w, seed=0):
     return pool, rows, max_pages
 
 
-def gpu_session(w, seed=0, device="cuda", weights=None, n_cu=0, attn_split_pages=0, trace=False):
+def gpu_session(w, seed=0, device="cuda", weights=None, n_cu=0, attn_split_pages=0, trace=False,
+                plan_flags=0):
     """A Decoder for workload w with its KV filled; returns (decoder, pool handle, weights)."""
     import decode_megakernel_persistent_amd as mk
     from decode_megakernel_persistent_amd.runtime import Decoder, alloc_kv_pool
@@ -49,7 +50,8 @@ def gpu_session(w, seed=0, device="cuda", weights=None, n_cu=0, attn_split_pages
     W = weights if weights is not None else fxd.weights(m, seed, device)
     bound = max(w["ctx"]) + w["steps"]
     dec = Decoder(m, W, kvpool, w["pool_pages"], w["ctx"], rows, max_pages, bound,
-                  n_cu=n_cu, attn_split_pages=attn_split_pages, device=device, trace=trace)
+                  n_cu=n_cu, attn_split_pages=attn_split_pages, device=device, trace=trace,
+                  plan_flags=plan_flags)
     for b in range(B):
         fxd.fill_kv(kvpool, dec.page_table[b], m, seed, b, w["ctx"][b])
     torch.cuda.synchronize(device)

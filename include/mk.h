@@ -91,8 +91,14 @@ typedef struct mk_batch_desc {
 typedef struct mk_plan_opts {
   int32_t n_cu;                /* workgroups = task lists (0: the current device's CU count) */
   int32_t attn_split_pages;    /* pages per attention task (0: automatic) */
-  int32_t flags;               /* reserved, 0 */
+  int32_t flags;               /* MK_PLAN_* bits, 0 = defaults */
 } mk_plan_opts;
+/* Attention splits from a shared queue that every compute unit pulls from
+ * (megakernel page, caption of Image 2: attention work whose amount depends
+ * on live sequence lengths sits in queues any processor can take from),
+ * instead of one static split per task. Off unless asked for. */
+#define MK_PLAN_ATTN_QUEUE 1     /* use the queue (batch 1) */
+#define MK_PLAN_NO_ATTN_QUEUE 2  /* never use it */
 
 typedef struct mk_plan mk_plan_t;   /* opaque host object */
 typedef struct mk_pool mk_pool_t;   /* opaque host object */

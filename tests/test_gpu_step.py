@@ -33,14 +33,14 @@ def _pool_slot(dec, m, b, l, g, pos):
     return blk[ko], blk[vo]
 
 
-def run_step_parity(name, seed=0, **over):
+def run_step_parity(name, seed=0, plan_flags=0, **over):
     w = spec(name, seed, **over)
     m, B = w["model"], w["batch"]
     L, V = m["n_layers"], m["vocab"]
     moe = m["n_experts"] > 0
     K = m["top_k"] if moe else 1
-    flush(f"[step parity] {name} seed={seed} over={over} B={B} ctx={w['ctx']}")
-    dec, pool, W = gpu_session(w, seed)
+    flush(f"[step parity] {name} seed={seed} over={over} flags={plan_flags} B={B} ctx={w['ctx']}")
+    dec, pool, W = gpu_session(w, seed, plan_flags=plan_flags)
     dev = dec.device
     tok_in = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
     tok_out = torch.full((B,), -1, dtype=torch.int32, device=dev)
@@ -135,6 +135,13 @@ def test_small_moe_step():
 
 def test_small_moe_other_seed():
     run_step_parity("small_moe", seed=7, ctx=[777])
+
+
+def test_attention_split_queue():
+    # attention splits pulled from the shared queue (forced at a short context)
+    import decode_megakernel_persistent_amd as mk
+    run_step_parity("tiny_dense", ctx=[100], plan_flags=mk.MK_PLAN_ATTN_QUEUE)
+    run_step_parity("small_moe", seed=3, ctx=[1500], plan_flags=mk.MK_PLAN_ATTN_QUEUE)
 
 
 def greedy_agreement(name, n_steps, seed=0, **over):

@@ -32,6 +32,7 @@ TASK = np.dtype([("op", "u1"), ("flags", "u1"), ("layer", "<u2"), ("wait_a", "<u
 OP_QKV, OP_ATTN, OP_COMB, OP_O, OP_ROUTER, OP_EXPERT = range(1, 7)
 OP_LM, OP_FINAL = 8, 9
 NO_CTR = 0xFFFF
+TF_QUEUE = 2
 
 
 def declared_functions():
@@ -137,8 +138,10 @@ def qkv_rows(p, g, m):
     return row, row + h2
 
 
-def plan_coverage(tasks, m):
+def plan_coverage(tasks, m, bound):
     S = {}
+    queued = set()
+    pg_bound = -(-bound // m["page_tokens"])
 
     def add(key, items):
         S.setdefault(key, []).extend(items)
@@ -148,6 +151,13 @@ def plan_coverage(tasks, m):
         a0, a1, a2, a3, aux = int(t["a0"]), int(t["a1"]), int(t["a2"]), int(t["a3"]), int(t["aux"])
         if op == OP_QKV:
             add(("qkv", l), [r for p in range(a1, a1 + a2) for r in qkv_rows(p, a0, m)])
+        elif op == OP_ATTN and int(t["flags"]) & TF_QUEUE:
+            # a shared queue of the layer's splits: (kv head, split) -> pages of
+            # split * a2 .. + a2 (a1 splits per head), counted once per layer
+            if l not in queued:
+                queued.add(l)
+                add(("attn", l), [(0, g, p) for g in range(m["n_kv_heads"])
+                                  for p in range(a1 * a2) if p < pg_bound])
         elif op == OP_ATTN:
             add(("attn", l), [(a0, a1, p) for p in range(a2, a2 + a3)])
         elif op == OP_COMB:
@@ -166,33 +176,44 @@ def plan_coverage(tasks, m):
     return S
 
 
-def build_plan(name, n_cu=256, **over):
+def build_plan(name, n_cu=256, flags=0, **over):
     w = spec(name, 0, **over)
     pool, rows, max_pages = lease_pages(w, 0)
     bound = max(w["ctx"]) + w["steps"]
     p = mk.mk_plan(mk.model_desc(w["model"]), w["ctx"], [v for r in rows for v in r], max_pages,
-                   bound, n_cu=n_cu)
+                   bound, n_cu=n_cu, flags=flags)
     return w, pool, p, bound
 
 
-@pytest.mark.parametrize("name,n_cu", [("tiny_dense", 256), ("tiny_dense", 7), ("small_moe", 256),
-                                       ("small_moe", 64), ("moe48_b1_8k", 256)])
-def test_plan_covers_the_oracle_work_exactly_once(name, n_cu):
-    w, pool, p, bound = build_plan(name, n_cu)
+@pytest.mark.parametrize("name,n_cu,flags", [("tiny_dense", 256, 0), ("tiny_dense", 7, 0),
+                                             ("small_moe", 256, 0), ("small_moe", 64, 0),
+                                             ("moe48_b1_8k", 256, 0), ("moe48_b1_256k", 256, 0),
+                                             ("moe48_b1_256k", 256, mk.MK_PLAN_ATTN_QUEUE),
+                                             ("tiny_dense", 16, mk.MK_PLAN_ATTN_QUEUE),
+                                             ("small_moe", 256, mk.MK_PLAN_ATTN_QUEUE)])
+def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
+    w, pool, p, bound = build_plan(name, n_cu, flags)
     try:
         img = mk.mk_plan_export(p)
         n_cu2, n_ctr, cu_off, tasks = decode_plan(img)
         assert n_cu2 == n_cu and mk.mk_plan_n_tasks(p) == len(tasks)
-        got = plan_coverage(tasks, w["model"])
+        got = plan_coverage(tasks, w["model"], bound)
         want = O.work_sets(w["model"], [bound] * w["batch"])
         assert set(got) == set(want)
         for k, items in got.items():
             assert len(items) == len(set(items)), f"{k}: covered more than once"
             assert set(items) == want[k], f"{k}: coverage differs from the oracle's work"
-        # counter targets = number of tasks signalling each counter; waits carry the target
+        # counter targets = number of tasks signalling each counter (a queue
+        # counter: one pull per split plus each queue task's empty last pull);
+        # waits carry the target
         tg = np.array(mk.mk_plan_counter_targets(p), dtype=np.int64)
         sig = tasks["signal"][tasks["signal"] != NO_CTR].astype(np.int64)
-        assert np.array_equal(np.bincount(sig, minlength=n_ctr), tg)
+        want_tg = np.bincount(sig, minlength=n_ctr)
+        qt = tasks[(tasks["op"] == OP_ATTN) & ((tasks["flags"] & TF_QUEUE) != 0)]
+        for q in set(qt["a0"].tolist()):
+            t0 = qt[qt["a0"] == q][0]
+            want_tg[q] = w["model"]["n_kv_heads"] * int(t0["a1"]) + int(t0["a3"])
+        assert np.array_equal(want_tg, tg)
         for wf, cf in (("wait_a", "cnt_a"), ("wait_b", "cnt_b")):
             m_ = tasks[wf] != NO_CTR
             assert np.array_equal(tasks[cf][m_].astype(np.int64), tg[tasks[wf][m_].astype(np.int64)])
@@ -201,6 +222,10 @@ def test_plan_covers_the_oracle_work_exactly_once(name, n_cu):
             lt = tasks[int(cu_off[cu]):int(cu_off[cu + 1])]
             ex = lt["layer"][lt["op"] == OP_EXPERT]
             assert len(ex) == len(set(ex.tolist()))
+        # with the queue asked for, attention splits come from a shared queue:
+        # one queue task per compute unit and layer
+        n_q = int(((tasks["op"] == OP_ATTN) & ((tasks["flags"] & TF_QUEUE) != 0)).sum())
+        assert n_q == (n_cu * w["model"]["n_layers"] if flags else 0)
         mk.mk_plan_validate(p)
         mk.mk_plan_simulate(p, 11, 3)
     finally:
