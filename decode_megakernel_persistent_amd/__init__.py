@@ -19,7 +19,7 @@ MK_OK, MK_EINVAL, MK_ENOMEM, MK_EBOUNDS, MK_EDEVICE, MK_ETIMEOUT, MK_ESTATE, MK_
 STATUS_NAMES = {0: "MK_OK", -1: "MK_EINVAL", -2: "MK_ENOMEM", -3: "MK_EBOUNDS", -4: "MK_EDEVICE",
                 -5: "MK_ETIMEOUT", -6: "MK_ESTATE", -7: "MK_EUNSUPPORTED"}
 (MK_BUF_XATTN, MK_BUF_XFFN, MK_BUF_Q, MK_BUF_PART, MK_BUF_O, MK_BUF_RLOG, MK_BUF_ACT,
- MK_BUF_LMPART, MK_BUF_KVN) = range(9)
+ MK_BUF_LMPART, MK_BUF_KVN, MK_BUF_ROUTE, MK_BUF_Y) = range(11)
 
 _i32, _i64, _u32, _u64, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                          ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t,
@@ -40,7 +40,8 @@ class mk_model_desc(ctypes.Structure):
 
 class mk_batch_desc(ctypes.Structure):
     _fields_ = [("batch", _i32), ("max_pages", _i32), ("seq_lens", ctypes.POINTER(_i32)),
-                ("page_table", ctypes.POINTER(_i32)), ("max_ctx_bound", _i32)]
+                ("page_table", ctypes.POINTER(_i32)), ("max_ctx_bound", _i32),
+                ("ctx_bounds", ctypes.POINTER(_i32))]
 
 
 class mk_plan_opts(ctypes.Structure):
@@ -163,12 +164,15 @@ MK_PLAN_ATTN_QUEUE = 1
 MK_PLAN_NO_ATTN_QUEUE = 2
 
 
-def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0, flags=0):
-    """Build a plan. page_table: flat host list/array of batch*max_pages int32."""
+def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0, flags=0,
+            ctx_bounds=None):
+    """Build a plan. page_table: flat host list/array of batch*max_pages int32;
+    ctx_bounds: per-sequence context bounds, or None (every sequence: bound)."""
     B = len(seq_lens)
     sl = (_i32 * B)(*[int(v) for v in seq_lens])
     pt = (_i32 * (B * max_pages))(*[int(v) for v in page_table])
-    bd = mk_batch_desc(B, max_pages, sl, pt, bound)
+    cb = (_i32 * B)(*[int(v) for v in ctx_bounds]) if ctx_bounds is not None else None
+    bd = mk_batch_desc(B, max_pages, sl, pt, bound, cb)
     op = mk_plan_opts(n_cu, attn_split_pages, flags)
     out = _vp()
     _check(_lib.mk_plan(ctypes.byref(desc), ctypes.byref(bd), ctypes.byref(op), ctypes.byref(out)))

@@ -43,7 +43,7 @@
 namespace mk {
 namespace dev {
 
-constexpr int LDS_VEC = 8192;
+constexpr int LDS_VEC = dev_lds_vec();
 
 constexpr int STAGE_CHUNKS = 12;  // 1 KB wave chunks per wave in the staging area (96 KB)
 
@@ -1079,12 +1079,637 @@ __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
   return true;
 }
 
+// ------------------------------------------------------------------ batch tasks
+//
+// A batch of B = 2 .. 32 sequences (continuous batching over one shared page
+// pool) runs the dense projections (QKV, O, LM head) as MFMA tiles: 16 weight
+// rows x 16 or 32 sequences per v_mfma_f32_16x16x32_bf16, the weights as the
+// A operand straight from HBM and the sequences' inputs as the B operand from
+// LDS. Inputs are fp32; they enter the MFMA as bf16 hi + lo parts (two MFMAs
+// per product, each bf16 x bf16 product exact in fp32), which keeps every
+// projection at fp32-level accuracy. RMSNorm is applied as x * g on the way
+// into LDS and the per-sequence scale 1/sqrt(mean(x^2) + eps) on the way out
+// (W (s x * g) = s W (x * g)). Attention and the split combine are the batch-1
+// bodies, per sequence. The router and top-k run per sequence; expert tasks
+// take the sequences routed to their expert (any number, in groups) so that
+// each selected expert's weights stream once per step.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// LDS of an MFMA batch tile, overlaid on the vector and staging areas.
+// Activation panel chunk (st, cb, lane) holds 8 k values 32 st + 8 (lane / 16)
+// .. + 7 of sequence 16 cb + lane % 16: one ds_read_b128 per lane gives the B
+// operand of k-step st for column block cb.
+struct MtLds {
+  uint4 hi[2][8 * 2 * 64];             // two panels of bf16 hi parts
+  uint4 lo[2][8 * 2 * 64];             // and of lo parts
+  float red[NWAVE][2][4][64];          // k-split partial accumulators
+  float ss[NT];                        // sum-of-squares partials
+  float scale[MAX_BATCH];              // per-sequence norm scale
+  float out[MT_MAX_BLOCKS * 16][MAX_BATCH];  // finished tile: [row][sequence]
+};
+static_assert(sizeof(MtLds) <= sizeof(float) * LDS_VEC + sizeof(uint4) * NWAVE * STAGE_CHUNKS * 64,
+              "MFMA tile LDS exceeds the overlaid areas");
+
+// Input of an MFMA tile: sequence b's K values at words + b * ld (tagged fp32)
+// or, when words is null, the embedding row of sequence b's token (bf16).
+// gain: bf16 norm gains applied on the way in (null: none); norm: scale each
+// sequence's results by 1/sqrt(mean(x^2) + eps).
+struct MtSrc {
+  const uint64_t* words;
+  int64_t ld;
+  const uint16_t* gain;
+  bool norm;
+};
+
+// out[r][b] = sum_k W[row r][k] * x_b[k] (normalised per MtSrc) for r < R <=
+// 16 MT_MAX_BLOCKS, b < B, into MtLds::out. rowptr(r) gives weight row r
+// (bf16, K elements, K a multiple of MT_KP). Waves split the row blocks and,
+// where there are fewer than 8 blocks, the k-steps of every panel (ks waves
+// per block, summed in fixed order). Weights of two panels ahead and the
+// next panel's inputs are in flight while a panel is multiplied. Every load
+// is issued unconditionally (unused slots re-read a valid address) so that
+// the wait counts do not depend on the branch taken.
+template <class RowPtr>
+__device__ __forceinline__ bool mt_tile(Ctx& c, int R, int K, const RowPtr& rowptr, const MtSrc& src) {
+  KAC& a = c.a;
+  MtLds& P = *(MtLds*)&c.s;
+  const int t = tid(), lane = t & 63, w = t >> 6;
+  const int B = a.B, ncb = B > 16 ? 2 : 1, npan = K / MT_KP;
+  const int nrb = (R + 15) >> 4;
+  const int nrbp = nrb <= 1 ? 1 : nrb <= 2 ? 2 : nrb <= 4 ? 4 : 8;
+  const int ks = NWAVE / nrbp, nsl = NWAVE / ks;  // waves per row block, k-steps per panel per wave
+  const int rb = w / ks, kp = w % ks;
+  const bool active = rb < nrb;
+  const uint16_t* wrow = rowptr(min(rb * 16 + (lane & 15), R - 1)) + 8 * (lane >> 4);
+  auto issue_w = [&](int p, uint4 (&wr)[8]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int st = kp + (s < nsl ? s : 0) * ks;
+      wr[s] = ld_nt((const uint4*)(wrow + p * MT_KP + st * 32));
+    }
+  };
+  // panel fill: thread t owns chunks t and t + NT, both of one sequence
+  const int cb_t = (t >> 6) & 1, seq = cb_t * 16 + (lane & 15), kg = lane >> 4, st0 = t >> 7;
+  const bool sv = seq < B;
+  const int sq = sv ? seq : 0;
+  const uint64_t* xw = src.words ? src.words + (size_t)sq * src.ld : nullptr;
+  const uint16_t* xe = src.words ? nullptr : a.embed + (size_t)token_row(a, sq) * K;
+  float ss = 0.f;
+  struct ActRegs { uint64_t v[16]; uint4 e[2]; uint4 g[2]; };
+  auto issue_act = [&](int p, ActRegs& r) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k0 = p * MT_KP + (st0 + 4 * q) * 32 + 8 * kg;
+      if (xw) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.v[8 * q + e] = ld_tagged(xw + k0 + e);
+      } else {
+        r.e[q] = *(const uint4*)(xe + k0);
+      }
+      r.g[q] = src.gain ? *(const uint4*)(src.gain + k0) : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+    }
+  };
+  // check the words' tags (re-reading stale ones), then convert into panel bi
+  auto finish_act = [&](int p, ActRegs& r, int bi) -> bool {
+    if (xw && sv) {
+      const uint32_t ep = a.epoch;
+      uint32_t stale = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) stale |= tag_is(r.v[k], ep) ? 0u : (1u << k);
+      uint32_t it = 0;
+      while (stale) {
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (stale & (1u << k)) r.v[k] = ld_tagged(xw + p * MT_KP + (st0 + 4 * (k >> 3)) * 32 + 8 * kg + (k & 7));
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if ((stale & (1u << k)) && tag_is(r.v[k], ep)) stale &= ~(1u << k);
+        if (stale && (++it & 31u) == 0u) {
+          if (aborted(a)) return false;
+          if (now() - c.t0 > a.timeout_ticks) {
+            raise_status(a, DS_TIMEOUT, c.ti, (uint32_t)seq, 0xFFFFFFFEu);
+            return false;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float x[8];
+      if (xw) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sv ? tag_value(r.v[8 * q + e]) : 0.f;
+      } else {
+        const uint32_t ew[4] = {r.e[q].x, r.e[q].y, r.e[q].z, r.e[q].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sv ? ((e & 1) ? bf_hi(ew[e >> 1]) : bf_lo(ew[e >> 1])) : 0.f;
+      }
+      const uint32_t gw[4] = {r.g[q].x, r.g[q].y, r.g[q].z, r.g[q].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss = fmaf(x[e], x[e], ss);
+        x[e] *= (e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1]);
+      }
+      uint4 hi, lo;
+      split8(x, hi, lo);
+      P.hi[bi][t + q * NT] = hi;
+      P.lo[bi][t + q * NT] = lo;
+    }
+    return true;
+  };
+  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  auto compute = [&](const uint4 (&wr)[8], int bi) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < nsl) {
+        const int st = kp + s * ks;
+        const bf16x8 A = __builtin_bit_cast(bf16x8, wr[s]);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          if (cb < ncb) {
+            const uint4 bh = P.hi[bi][(st * 2 + cb) * 64 + lane], bl = P.lo[bi][(st * 2 + cb) * 64 + lane];
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bh), acc[cb], 0, 0, 0);
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bl), acc[cb], 0, 0, 0);
+          }
+      }
+  };
+  // one panel: next inputs in flight, multiply, refill weights two panels
+  // ahead, land the next inputs in the other buffer; uniform failure
+  auto panel = [&](int p, uint4 (&wr)[8], int bi) -> bool {
+    ActRegs r;
+    const bool more = p + 1 < npan;
+    if (more) issue_act(p + 1, r);
+    if (active) compute(wr, bi);
+    if (p + 2 < npan) issue_w(p + 2, wr);
+    if (more && !finish_act(p + 1, r, bi ^ 1)) c.s.fail = 1;
+    lds_barrier();
+    return c.s.fail == 0;
+  };
+  uint4 wA[8], wB[8];
+  issue_w(0, wA);
+  if (npan > 1) issue_w(1, wB);
+  {
+    ActRegs r;
+    issue_act(0, r);
+    if (!finish_act(0, r, 0)) c.s.fail = 1;
+    lds_barrier();
+    if (c.s.fail) return false;
+  }
+  for (int p = 0; p < npan; p += 2) {
+    if (!panel(p, wA, 0)) return false;
+    if (p + 1 < npan && !panel(p + 1, wB, 1)) return false;
+  }
+  // per-sequence scale: the 16 threads of a sequence, in a fixed order
+  P.ss[t] = ss;
+  if (active && kp > 0) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P.red[w][cb][j][lane] = acc[cb][j];
+  }
+  lds_barrier();
+  if (t < MAX_BATCH) {
+    float tot = 0.f;
+    const int cb = t >> 4, s16 = t & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) tot += P.ss[q * 128 + cb * 64 + g * 16 + s16];
+    P.scale[t] = src.norm ? 1.0f / sqrtf(tot / (float)K + a.eps) : 1.f;
+  }
+  lds_barrier();
+  if (active && kp == 0) {
+    for (int q = 1; q < ks; ++q)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[cb][j] += P.red[w + q][cb][j][lane];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = rb * 16 + 4 * (lane >> 4) + j, sb = cb * 16 + (lane & 15);
+        P.out[row][sb] = acc[cb][j] * P.scale[sb];
+      }
+  }
+  lds_barrier();
+  return true;
+}
+
+// Context bound of sequence b (from the plan image).
+__device__ __forceinline__ int seq_bound(KAC& a, int b) { return a.seq_bound ? a.seq_bound[b] : a.bound; }
+
+// QKV rows of one kv group for every sequence, then the rotary epilogue, the
+// new K/V in the step's words and the KV append at each sequence's position.
+__device__ __forceinline__ bool task_bqkv(Ctx& c, const Task& t) {
+  KAC& a = c.a;
+  const int l = t.layer, g = t.a0, p0 = t.a1, np = t.a2, H = a.H, D = a.D;
+  const int QR = (a.Hq + 2 * a.Hkv) * D;
+  const uint16_t* W = a.wqkv + (size_t)l * QR * H;
+  MtSrc src{l == 0 ? nullptr : a.x + (size_t)(l - 1) * a.s_x, H, a.attn_norm + (size_t)l * H, true};
+  if (a.trace && tid() == 0) c.s.tw[2] = now();
+  if (!mt_tile(c, 2 * np, H, [&](int j) {
+        int head, i, row;
+        qkv_pair(p0 + (j >> 1), g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
+        return W + (size_t)(row + (j & 1) * (D / 2)) * H;
+      }, src))
+    return false;
+  if (a.trace && tid() == 0) c.s.tw[3] = now();
+  const MtLds& P = *(const MtLds*)&c.s;
+  for (int idx = tid(); idx < np * a.B; idx += NT) {
+    const int q = idx / a.B, b = idx - q * a.B;
+    const int pos = a.seq_lens[b];
+    const bool in_bounds = pos >= 0 && pos + 1 <= seq_bound(a, b) && pos < a.n_rope;
+    const int pc = in_bounds ? pos : 0;
+    const int32_t phys = a.page_table[(size_t)b * a.max_pages + (pc >> 4)];
+    int head, i, row;
+    const int sec = qkv_pair(p0 + q, g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
+    const float y0 = P.out[2 * q][b], y1 = P.out[2 * q + 1][b];
+    float r0 = y0, r1 = y1;
+    if (sec < 2) {
+      const float cs = a.rope_cos[(size_t)pc * (D / 2) + i], sn = a.rope_sin[(size_t)pc * (D / 2) + i];
+      r0 = y0 * cs - y1 * sn;
+      r1 = y1 * cs + y0 * sn;
+    }
+    if (sec == 0) {
+      uint64_t* qd = a.q + (size_t)l * a.s_q + ((size_t)b * a.Hq + head) * D;
+      st_tagged(qd + i, r0, a.epoch);
+      st_tagged(qd + i + D / 2, r1, a.epoch);
+    } else {
+      const uint32_t b0 = f2bf(r0), b1 = f2bf(r1);
+      uint64_t* kn = a.kvn + (size_t)l * a.s_kvn + (((size_t)b * a.Hkv + g) * 2 + (sec - 1)) * D;
+      st_tagged(kn + i, __uint_as_float(b0), a.epoch);
+      st_tagged(kn + i + D / 2, __uint_as_float(b1), a.epoch);
+      const bool page_ok = in_bounds && phys >= 0 && phys < a.n_pages;
+      if (!page_ok) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)pos, (uint32_t)phys);
+      else {
+        uint16_t* base = a.pool + (size_t)phys * a.page_stride + (size_t)l * a.layer_stride +
+                         (size_t)g * 2 * 16 * D;
+        const int slot = pos & 15;
+        if (sec == 1) {
+          base[kv_k_offset(slot, i)] = (uint16_t)b0;
+          base[kv_k_offset(slot, i + D / 2)] = (uint16_t)b1;
+        } else {
+          base[kv_v_offset(slot, i, D)] = (uint16_t)b0;
+          base[kv_v_offset(slot, i + D / 2, D)] = (uint16_t)b1;
+        }
+      }
+    }
+  }
+  return true;
+}
+
+// W_o rows for every sequence, plus the residual (the layer's input).
+__device__ __forceinline__ bool task_bo(Ctx& c, const Task& t) {
+  KAC& a = c.a;
+  const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H, K = a.Hq * a.D, B = a.B;
+  const uint16_t* W = a.wo + (size_t)l * H * K;
+  MtSrc src{a.o + (size_t)l * a.s_o, K, nullptr, false};
+  if (a.trace && tid() == 0) c.s.tw[2] = now();
+  if (!mt_tile(c, n, K, [&](int j) { return W + (size_t)(r0 + j) * K; }, src)) return false;
+  if (a.trace && tid() == 0) c.s.tw[3] = now();
+  const MtLds& P = *(const MtLds*)&c.s;
+  bool fail = false;
+  for (int idx = tid(); idx < n * B && !fail; idx += NT) {
+    const int r = idx / B, b = idx - r * B;
+    const float x = resid(c, l, b, r0 + r, &fail);
+    st_tagged(a.xa + (size_t)l * a.s_x + (size_t)b * H + r0 + r, x + P.out[r][b], a.epoch);
+  }
+  if (fail) c.s.fail = 1;
+  lds_barrier();
+  return c.s.fail == 0;
+}
+
+// Gather n tagged words, word i at addr(i), into dst[i] (LDS); uniform result.
+template <int MAXW, class Addr>
+__device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float* dst, int which) {
+  KAC& a = c.a;
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
+  bool ok = true;
+  for (int base = 0; base < n && ok; base += MAXW * NT) {
+    const int t = tid();
+    float v[MAXW];
+    ok = read_words<MAXW>(a, [&](int k) -> const uint64_t* {
+      const int i = base + t + k * NT;
+      return i < n ? addr(i) : nullptr;
+    }, v, c.t0, c.ti);
+    if (ok) {
+#pragma unroll
+      for (int k = 0; k < MAXW; ++k) {
+        const int i = base + t + k * NT;
+        if (i < n) dst[i] = v[k];
+      }
+    }
+  }
+  if (!ok) c.s.fail = 1;
+  lds_barrier();
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
+  return c.s.fail == 0;
+}
+
+// Router rows, softmax and top-k of sequence b: router logits, and per slot
+// the selected expert and its (renormalised) weight as route words.
+template <int CPL, int TC>
+__device__ __forceinline__ bool task_topk(Ctx& c, const Task& t) {
+  constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
+  constexpr int CAP = (NT / TC) * RPW;
+  KAC& a = c.a;
+  Smem& s = c.s;
+  const int l = t.layer, b = t.a0, H = a.H, E = a.E;
+  const uint16_t* W = a.router + (size_t)l * E * H;
+  Tile<CPL, RPW, TC> tile;
+  tile.issue(min(CAP, E), [&](int j) { return (const uint4*)(W + (size_t)j * H); });
+  Gains gn;
+  gn.load(a.ffn_norm + (size_t)l * H, H);
+  if (!gather<4>(c, a.xa + (size_t)l * a.s_x + (size_t)b * H, H, s.vec, 1)) return false;
+  rmsnorm_pack(c, s.vec, H, gn);
+  tile.dots(s.vec, s.out);
+  for (int r0 = CAP; r0 < E; r0 += CAP) {
+    tile.issue(min(CAP, E - r0), [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
+    tile.dots(s.vec, s.out + r0);
+  }
+  lds_barrier();
+  route(c, s.out);
+  const float div = route_div(a, s);
+  for (int e = tid(); e < E; e += NT)
+    st_tagged(a.rlog + (size_t)l * a.s_rlog + (size_t)b * E + e, s.out[e], a.epoch);
+  if (tid() < a.K) {
+    const int j = tid(), id = s.route_ids[j];
+    const float wj = s.route_w[j] / div;
+    uint64_t* rw = a.route + (size_t)l * a.s_route + ((size_t)b * a.K + j) * 2;
+    st_tagged(rw, __int_as_float(id), a.epoch);
+    st_tagged(rw + 1, wj, a.epoch);
+    if (a.topk_ids) a.topk_ids[((size_t)l * a.B + b) * a.K + j] = id;
+    if (a.topk_w) a.topk_w[((size_t)l * a.B + b) * a.K + j] = wj;
+  }
+  return true;
+}
+
+// Rows of a GEMV over several input vectors: lane group lg (TC lanes) holds
+// rows lg + G r (r < RPW) of the current round as CPL 16-byte chunks. Loads
+// are unconditional (rows past the end re-read row R - 1), so that a round's
+// wait does not depend on how many rows the lane group has.
+template <int CPL, int RPW, int TC>
+struct MTile {
+  static constexpr int G = NT / TC;
+  static constexpr int CAP = G * RPW;  // rows per round
+  uint4 w[RPW][CPL];
+  template <class RowPtr>
+  __device__ __forceinline__ void issue(int r0, int R, const RowPtr& rowptr) {
+    const int lg = tid() / TC, tc = tid() % TC;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const uint4* p = rowptr(min(r0 + lg + r * G, R - 1));
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) w[r][cc] = ld_nt(p + tc + cc * TC);
+    }
+  }
+  // out[row * EXP_GROUP + s] for the round's rows < R and inputs s < ns;
+  // input s in split form at u + s * K (floats)
+  __device__ __forceinline__ void dots(int r0, int R, const float* u, int K, int ns, float* out) {
+    const int lg = tid() / TC, tc = tid() % TC;
+    float acc[RPW][EXP_GROUP];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int q = 0; q < EXP_GROUP; ++q) acc[r][q] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+      for (int q = 0; q < EXP_GROUP; ++q)
+        if (q < ns) {
+          const uint4* up = (const uint4*)(u + (size_t)q * K + (tc + cc * TC) * 8);
+          const uint4 uh = up[0], ul = up[1];
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) acc[r][q] = dot8h(w[r][cc], uh, ul, acc[r][q]);
+        }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = r0 + lg + r * G;
+#pragma unroll
+      for (int q = 0; q < EXP_GROUP; ++q)
+        if (q < ns) {
+          const float sum = group_sum_last<TC>(acc[r][q]);
+          if (tc == TC - 1 && row < R) out[row * EXP_GROUP + q] = sum;
+        }
+    }
+  }
+};
+
+// All R rows of a multi-input GEMV, two rounds in flight.
+template <int CPL, int RPW, int TC, class RowPtr>
+__device__ __forceinline__ void mgemv(int R, const RowPtr& rowptr, const float* u, int K, int ns,
+                                      float* out) {
+  using T = MTile<CPL, RPW, TC>;
+  T A, Bt;
+  A.issue(0, R, rowptr);
+  for (int r0 = 0; r0 < R; r0 += 2 * T::CAP) {
+    if (r0 + T::CAP < R) Bt.issue(r0 + T::CAP, R, rowptr);
+    A.dots(r0, R, u, K, ns, out);
+    if (r0 + 2 * T::CAP < R) A.issue(r0 + 2 * T::CAP, R, rowptr);
+    if (r0 + T::CAP < R) Bt.dots(r0 + T::CAP, R, u, K, ns, out);
+  }
+}
+
+// LDS of a batch expert task (overlaid on the vector and staging areas):
+// the inputs of one group of routed sequences in split form, the group's
+// results, and the routed (sequence, slot) list.
+struct ExpLds {
+  float in[EXP_GROUP * 2048];
+  float out[1024 * EXP_GROUP];
+  int list[MAX_BATCH * 16];
+  int wave_cnt[NWAVE];
+};
+static_assert(sizeof(ExpLds) <= sizeof(float) * LDS_VEC + sizeof(uint4) * NWAVE * STAGE_CHUNKS * 64,
+              "expert LDS exceeds the overlaid areas");
+
+// One expert (a0), part q: for every sequence routed to it (in sequence,
+// slot order, EXP_GROUP at a time), the gate/up rows a1 .. a1 + a2 with
+// SwiGLU into the activation words of that (sequence, slot); then the down
+// rows of the same expert over the full activations (from every part of the
+// expert) into the expert-output words y of that (sequence, slot). Dense
+// FFN: expert 0, every sequence in slot 0.
+template <int CH, int TCH, int CF, int TCF>
+__device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
+  KAC& a = c.a;
+  Smem& s = c.s;
+  ExpLds& X = *(ExpLds*)&s;
+  const int l = t.layer, e = t.a0, f0 = t.a1, nf = t.a2;
+  const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
+  const int H = a.H, F = a.F, KK = a.dense ? 1 : a.K, EE = a.dense ? 1 : a.E, B = a.B;
+  const int th = tid(), lane = th & 63, w = th >> 6;
+  // the routed list
+  int ns = 0;
+  if (a.dense) {
+    for (int b = th; b < B; b += NT) X.list[b] = b;
+    ns = B;
+    lds_barrier();
+  } else {
+    const int n = B * KK;  // <= NT (checked by the planner)
+    float* ids = X.out;
+    if (!gather_fn<1>(c, n, [&](int i) { return a.route + (size_t)l * a.s_route + (size_t)i * 2; }, ids, 0))
+      return false;
+    const bool mine = th < n && __float_as_int(ids[th]) == e;
+    const uint64_t m = __ballot(mine);
+    if (lane == 0) X.wave_cnt[w] = __popcll(m);
+    lds_barrier();
+    int off = 0;
+    for (int q = 0; q < w; ++q) off += X.wave_cnt[q];
+    for (int q = 0; q < NWAVE; ++q) ns += X.wave_cnt[q];
+    if (mine) X.list[off + __popcll(m & ((1ull << lane) - 1ull))] = th;
+    lds_barrier();
+  }
+  if (ns == 0) return true;
+  mark(c, 0);
+  Gains gn;
+  gn.load(a.ffn_norm + (size_t)l * H, H);
+  const uint16_t* Wg = a.gate + ((size_t)l * EE + e) * F * H;
+  const uint16_t* Wu = a.up + ((size_t)l * EE + e) * F * H;
+  const uint16_t* Wd = a.down + ((size_t)l * EE + e) * H * F;
+  // gate/up: rows 2f (gate) and 2f + 1 (up) of FFN row f0 + f
+  if (nf > 0)
+    for (int g0 = 0; g0 < ns; g0 += EXP_GROUP) {
+      const int ng = min(EXP_GROUP, ns - g0);
+      if (!gather_fn<4>(c, ng * H, [&](int i) {
+            const int q = i / H, bs = X.list[g0 + q] / KK;
+            return a.xa + (size_t)l * a.s_x + (size_t)bs * H + (i - q * H);
+          }, X.in, 1))
+        return false;
+      for (int q = 0; q < ng; ++q) rmsnorm_pack(c, X.in + (size_t)q * H, H, gn);
+      mgemv<CH, 2, TCH>(2 * nf, [&](int j) {
+          return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + (j >> 1)) * H);
+        }, X.in, H, ng, X.out);
+      lds_barrier();
+      for (int idx = th; idx < nf * ng; idx += NT) {
+        const int f = idx / ng, q = idx - f * ng;
+        const float yg = X.out[(2 * f) * EXP_GROUP + q], yu = X.out[(2 * f + 1) * EXP_GROUP + q];
+        const int ent = X.list[g0 + q];  // b * KK + slot
+        st_tagged(a.act + (size_t)l * a.s_act + (size_t)ent * F + f0 + f, yg / (1.0f + expf(-yg)) * yu, a.epoch);
+      }
+      lds_barrier();
+    }
+  mark(c, 1);
+  // down: rows r0 .. r0 + nr over the full activations of each routed slot
+  if (nr > 0)
+    for (int g0 = 0; g0 < ns; g0 += EXP_GROUP) {
+      const int ng = min(EXP_GROUP, ns - g0);
+      if (!gather_fn<4>(c, ng * F, [&](int i) {
+            const int q = i / F;
+            return a.act + (size_t)l * a.s_act + (size_t)X.list[g0 + q] * F + (i - q * F);
+          }, X.in, 1))
+        return false;
+      for (int q = 0; q < ng; ++q) pack_lds(c, X.in + (size_t)q * F, F);
+      mgemv<CF, 2, TCF>(nr, [&](int j) { return (const uint4*)(Wd + (size_t)(r0 + j) * F); },
+                        X.in, F, ng, X.out);
+      lds_barrier();
+      for (int idx = th; idx < nr * ng; idx += NT) {
+        const int r = idx / ng, q = idx - r * ng;
+        const int ent = X.list[g0 + q];
+        st_tagged(a.y + (size_t)l * a.s_y + (size_t)ent * H + r0 + r, X.out[r * EXP_GROUP + q], a.epoch);
+      }
+      lds_barrier();
+    }
+  mark(c, 2);
+  return true;
+}
+
+// Hidden rows a1 .. a1 + a2 of sequence a0 after the FFN: the residual plus
+// the routing-weighted sum of its experts' outputs, in slot order.
+__device__ __forceinline__ bool task_bcomb(Ctx& c, const Task& t) {
+  KAC& a = c.a;
+  Smem& s = c.s;
+  const int l = t.layer, b = t.a0, r0 = t.a1, nr = t.a2, H = a.H;
+  const int KK = a.dense ? 1 : a.K;
+  // words: [weights (KK, MoE only)] [y slot 0 rows] .. [y slot KK-1 rows] [residual rows]
+  const int nw = a.dense ? 0 : KK;
+  const int n = nw + (KK + 1) * nr;
+  float* v = s.vec;
+  if (!gather_fn<4>(c, n, [&](int i) -> const uint64_t* {
+        if (i < nw) return a.route + (size_t)l * a.s_route + ((size_t)b * KK + i) * 2 + 1;
+        i -= nw;
+        const int j = i / nr, r = i - j * nr;
+        if (j < KK) return a.y + (size_t)l * a.s_y + ((size_t)b * KK + j) * H + r0 + r;
+        return a.xa + (size_t)l * a.s_x + (size_t)b * H + r0 + r;
+      }, v, 1))
+    return false;
+  for (int r = tid(); r < nr; r += NT) {
+    float y = 0.f;
+    for (int j = 0; j < KK; ++j) y += (a.dense ? 1.f : v[j]) * v[nw + j * nr + r];
+    st_tagged(a.x + (size_t)l * a.s_x + (size_t)b * H + r0 + r, v[nw + KK * nr + r] + y, a.epoch);
+  }
+  return true;
+}
+
+// LM-head rows for every sequence, then each sequence's argmax over them.
+__device__ __forceinline__ bool task_blm(Ctx& c, const Task& t) {
+  KAC& a = c.a;
+  const int r0 = t.a1, n = t.a2, H = a.H, B = a.B;
+  MtSrc src{a.x + (size_t)(a.L - 1) * a.s_x, H, a.final_norm, true};
+  if (a.trace && tid() == 0) c.s.tw[2] = now();
+  if (!mt_tile(c, n, H, [&](int j) { return a.lm + (size_t)(r0 + j) * H; }, src)) return false;
+  if (a.trace && tid() == 0) c.s.tw[3] = now();
+  const MtLds& P = *(const MtLds*)&c.s;
+  // 16 threads per sequence
+  const int b = tid() >> 4, sub = tid() & 15;
+  float bv = NEG_INF;
+  int bi = 0x7fffffff;
+  if (b < B)
+    for (int r = sub; r < n; r += 16) {
+      const float y = P.out[r][b];
+      if (a.logits) a.logits[(size_t)b * a.V + r0 + r] = y;
+      argmax_merge(y, r0 + r, bv, bi);
+    }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    argmax_merge(ov, oi, bv, bi);
+  }
+  if (b < B && sub == 0) {
+    uint64_t* dst = a.lmpart + ((size_t)t.a3 * B + b) * 2;
+    st_tagged(dst, bv, a.epoch);
+    st_tagged(dst + 1, __int_as_float(bi), a.epoch);
+  }
+  return true;
+}
+
+// Sequence a1's greedy token: the argmax over every LM-head tile's partial.
+__device__ __forceinline__ bool task_bfinal(Ctx& c, const Task& t) {
+  KAC& a = c.a;
+  Smem& s = c.s;
+  const int n = t.a0, b = t.a1, B = a.B;
+  if (!gather_fn<2>(c, 2 * n, [&](int i) { return a.lmpart + ((size_t)(i >> 1) * B + b) * 2 + (i & 1); },
+                    s.vec, 1))
+    return false;
+  float bv = NEG_INF;
+  int bi = 0x7fffffff;
+  for (int q = tid(); q < n; q += NT) argmax_merge(s.vec[2 * q], __float_as_int(s.vec[2 * q + 1]), bv, bi);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    argmax_merge(ov, oi, bv, bi);
+  }
+  float* rv = s.red;
+  int* ri = (int*)(s.red + NWAVE);
+  if ((tid() & 63) == 0) { rv[tid() >> 6] = bv; ri[tid() >> 6] = bi; }
+  lds_barrier();
+  if (tid() == 0) {
+    for (int q = 1; q < NWAVE; ++q) argmax_merge(rv[q], ri[q], bv, bi);
+    a.tok_out[b] = bi;
+    a.seq_lens[b] = a.seq_lens[b] + 1;
+  }
+  return true;
+}
+
 // One kernel per shape class: CH, CO, CF are the 16-byte chunks per lane of
 // the GEMVs over the hidden size, the attention output (query heads x head
 // dim) and the FFN width, TCH, TCO, TCF their lane-group widths; HD is the
 // head dim. Each variant contains only the
 // task bodies its shapes use, so registers are allocated for them alone.
-template <int CH, int TCH, int CO, int TCO, int CF, int TCF, int HD>
+template <int CH, int TCH, int CO, int TCO, int CF, int TCF, int HD, bool BATCH>
 __global__ void __launch_bounds__(NT) megakernel(KArgs) {
   __shared__ Smem s;
   // explicit kernel arguments start at offset 0 of the kernel-argument segment
@@ -1109,7 +1734,6 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
     }
     bool ok = true;
     switch (t.op) {
-      case OP_QKV: ok = task_qkv<CH, TCH, HD>(c, t); break;
       case OP_ATTN: {
         // One split, or splits from the shared queue: every pull adds one to
         // the queue counter; this step's pulls are numbered from base =
@@ -1145,12 +1769,30 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
         break;
       }
       case OP_COMB: ok = task_comb(c, t); break;
-      case OP_O: ok = task_o<CO, TCO>(c, t); break;
-      case OP_ROUTER: ok = task_router<CH, TCH>(c, t); break;
-      case OP_EXPERT: ok = task_expert<CH, TCH, CF, TCF>(c, t); break;
-      case OP_LM: ok = task_lm<CH, TCH>(c, t); break;
-      case OP_FINAL: ok = task_final(c, t); break;
-      default: break;
+      default:
+        if constexpr (BATCH) {
+          switch (t.op) {
+            case OP_BQKV: ok = task_bqkv(c, t); break;
+            case OP_BO: ok = task_bo(c, t); break;
+            case OP_TOPK: ok = task_topk<CH, TCH>(c, t); break;
+            case OP_BEXP: ok = task_bexp<CH, TCH, CF, TCF>(c, t); break;
+            case OP_BCOMB: ok = task_bcomb(c, t); break;
+            case OP_BLM: ok = task_blm(c, t); break;
+            case OP_BFINAL: ok = task_bfinal(c, t); break;
+            default: break;
+          }
+        } else {
+          switch (t.op) {
+            case OP_QKV: ok = task_qkv<CH, TCH, HD>(c, t); break;
+            case OP_O: ok = task_o<CO, TCO>(c, t); break;
+            case OP_ROUTER: ok = task_router<CH, TCH>(c, t); break;
+            case OP_EXPERT: ok = task_expert<CH, TCH, CF, TCF>(c, t); break;
+            case OP_LM: ok = task_lm<CH, TCH>(c, t); break;
+            case OP_FINAL: ok = task_final(c, t); break;
+            default: break;
+          }
+        }
+        break;
     }
     if (!ok) return;  // uniform: the failure was recorded in the status words
     const uint64_t t_body = (a.trace && tid() == 0) ? now() : 0;
@@ -1185,12 +1827,16 @@ __global__ __launch_bounds__(256) void mk_stream_copy_kernel(uint4* __restrict__
   }
 }
 
-// Kernel variants, indexed by mk::kernel_class (see mk_internal.hpp).
-const void* kernel_for(int cls) {
-  switch (cls) {
-    case 0: return (const void*)megakernel<1, 32, 1, 32, 1, 64, 64>;   // hidden 256, 4x64 heads, FFN 512
-    case 1: return (const void*)megakernel<2, 64, 2, 64, 1, 64, 64>;   // hidden 1024, 16x64 heads, FFN 512
-    case 2: return (const void*)megakernel<4, 64, 8, 64, 3, 32, 128>;  // hidden 2048, 32x128 heads, FFN 768
+// Kernel variants, indexed by mk::kernel_class (see mk_internal.hpp) and by
+// batch (batch 1: GEMV tiles; a batch: MFMA tiles and shared expert tasks).
+const void* kernel_for(int cls, bool batch) {
+  switch (cls * 2 + (batch ? 1 : 0)) {
+    case 0: return (const void*)megakernel<1, 32, 1, 32, 1, 64, 64, false>;   // hidden 256, 4x64 heads, FFN 512
+    case 1: return (const void*)megakernel<1, 32, 1, 32, 1, 64, 64, true>;
+    case 2: return (const void*)megakernel<2, 64, 2, 64, 1, 64, 64, false>;   // hidden 1024, 16x64 heads, FFN 512
+    case 3: return (const void*)megakernel<2, 64, 2, 64, 1, 64, 64, true>;
+    case 4: return (const void*)megakernel<4, 64, 8, 64, 3, 32, 128, false>;  // hidden 2048, 32x128 heads, FFN 768
+    case 5: return (const void*)megakernel<4, 64, 8, 64, 3, 32, 128, true>;
     default: return nullptr;
   }
 }
@@ -1306,10 +1952,12 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
   auto words = [&](int which) { return (int64_t)(p->ws_stride[which] / 8); };
   a.x = buf(MK_BUF_XFFN); a.xa = buf(MK_BUF_XATTN); a.q = buf(MK_BUF_Q); a.kvn = buf(MK_BUF_KVN);
   a.part = buf(MK_BUF_PART); a.o = buf(MK_BUF_O); a.rlog = buf(MK_BUF_RLOG); a.act = buf(MK_BUF_ACT);
-  a.lmpart = buf(MK_BUF_LMPART);
+  a.lmpart = buf(MK_BUF_LMPART); a.route = buf(MK_BUF_ROUTE); a.y = buf(MK_BUF_Y);
   a.s_x = words(MK_BUF_XFFN); a.s_q = words(MK_BUF_Q); a.s_kvn = words(MK_BUF_KVN);
   a.s_part = words(MK_BUF_PART); a.s_o = words(MK_BUF_O); a.s_rlog = words(MK_BUF_RLOG);
-  a.s_act = words(MK_BUF_ACT);
+  a.s_act = words(MK_BUF_ACT); a.s_route = words(MK_BUF_ROUTE); a.s_y = words(MK_BUF_Y);
+  a.seq_bound = (const int32_t*)((const char*)bu->plan +
+                                 reinterpret_cast<const uint32_t*>(p->image.data())[mk::H_BOUND_OFF_BYTES]);
   a.S_max = p->S_max; a.n_lm = p->n_lm;
   a.plan = (const uint32_t*)bu->plan; a.ctr = bu->counters; a.status = bu->status; a.epoch = epoch;
   a.timeout_ticks = (uint64_t)(timeout_ms ? timeout_ms : 2000) * 100000ull;
@@ -1319,7 +1967,7 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
     a.trace = bu->trace;
   }
 
-  const void* kern = mk::dev::kernel_for(p->kernel_class);
+  const void* kern = mk::dev::kernel_for(p->kernel_class, p->batch);
   if (!kern) return fail(MK_EUNSUPPORTED, "mk_decode_step: no kernel variant for this model shape");
   void* args[] = {&a};
   hipError_t e = hipLaunchCooperativeKernel(kern, dim3(p->n_cu), dim3(mk::NT), args, 0,

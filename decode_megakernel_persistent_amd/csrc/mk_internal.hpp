@@ -33,7 +33,18 @@ enum Op : uint8_t {
                   // (7 is unused)
   OP_LM = 8,      // a1 = first row, a2 = rows, a3 = index of this LM tile
   OP_FINAL = 9,   // a0 = LM tiles
-  OP_COUNT = 10
+  // batch (B > 1) tasks: the dense projections cover all sequences at once
+  // as MFMA tiles of 16-row blocks
+  OP_BQKV = 10,   // a0 = kv group g, a1 = first rotary pair, a2 = pairs
+  OP_BO = 11,     // a1 = first row, a2 = rows
+                  // (12 is unused)
+  OP_TOPK = 13,   // a0 = b: router rows, softmax and top-k of one sequence
+  OP_BEXP = 14,   // a0 = expert, a1 = first FFN row, a2 = FFN rows,
+                  // a3 = first hidden row << 16 | hidden rows (down part)
+  OP_BCOMB = 15,  // a0 = b, a1 = first row, a2 = rows: weighted expert sum + residual
+  OP_BLM = 16,    // a1 = first row, a2 = rows, a3 = index of this LM tile
+  OP_BFINAL = 17, // a0 = LM tiles, a1 = b
+  OP_COUNT = 18
 };
 
 enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2 };
@@ -60,10 +71,24 @@ static_assert(sizeof(Task) == 32, "task record is 32 bytes");
 
 // Plan image: u32 header[PLAN_HDR_WORDS], u32 cu_off[n_cu + 1] (task index
 // ranges per list), padding to 32 B, Task tasks[n_tasks] (lists back to back).
-constexpr uint32_t PLAN_MAGIC = 0x32504B4Du;  // "MKP2"
+// After the tasks: int32 seq_bound[B], each sequence's context bound.
+constexpr uint32_t PLAN_MAGIC = 0x33504B4Du;  // "MKP3"
 constexpr int PLAN_HDR_WORDS = 16;
 enum PlanHdr { H_MAGIC = 0, H_NCU = 1, H_NTASKS = 2, H_NCTR = 3, H_TASK_OFF_BYTES = 4,
-               H_STAGES = 5 };
+               H_STAGES = 5, H_BOUND_OFF_BYTES = 6, H_BATCH = 7 };
+
+// Batch projections: MFMA 16x16x32 bf16 tiles of 16 weight rows x 16 or 32
+// sequences. The sequences' inputs stream through LDS in panels of MT_KP
+// elements (bf16 hi and lo parts of every element), and a task holds at most
+// MT_MAX_BLOCKS row blocks. The reduction width must be a multiple of MT_KP.
+constexpr int MAX_BATCH = 32;
+constexpr int MT_KP = 256;
+constexpr int MT_MAX_BLOCKS = 8;
+// Expert tasks of a batch take the sequences routed to them in groups of
+// EXP_GROUP (their inputs are held in LDS together).
+constexpr int EXP_GROUP = 8;
+// Floats of the LDS gather vector of the megakernel.
+MK_HD constexpr int dev_lds_vec() { return 8192; }
 
 // Completion counters: counter c is CTR_LINES sub-counters, one 64-byte line
 // each; a task on compute unit cu increments sub-counter cu % CTR_LINES.
@@ -188,8 +213,11 @@ struct KArgs {
   //  kvn [L][B][Hkv][2][D] new K and V (bf16 bits), part [L][B][Hkv][S_max][HG][D+2]
   //  split partials (o, m, l), o [L][B][Hq][D], rlog [L][B][E], act [L][B][K][F],
   //  lmpart [n_lm][B][2] (value, index)
-  uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart;
-  int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act;
+  //  batch only: route [L][B][K][2] (expert id bits, weight) per selected slot,
+  //  y [L][B][K][H] expert outputs
+  uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart, *route, *y;
+  int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act, s_route, s_y;
+  const int32_t* seq_bound;  // [B] context bound per sequence (in the plan image)
   int32_t S_max, n_lm;
   // plan and sync
   const uint32_t* plan;

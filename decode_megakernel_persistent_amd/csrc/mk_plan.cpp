@@ -75,6 +75,177 @@ int rows_max(int K) {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Ranges of n items in units of u over t tasks: every range but the last is
+// a whole number of units.
+std::vector<std::pair<int, int>> split_units(int n, int u, int t) {
+  auto r = split_even(ceil_div(n, u), t);
+  for (auto& [s0, c] : r) {
+    const int e = std::min(n, (s0 + c) * u);
+    s0 *= u;
+    c = e - s0;
+  }
+  return r;
+}
+
+// Row blocks (16 rows) per task of the MFMA batch projections: a task
+// gathers every sequence's input once, so tasks are a few row blocks each.
+constexpr int QKV_BLOCKS = 4, O_BLOCKS = 4, LM_BLOCKS = mk::MT_MAX_BLOCKS;
+
+// Stages of a batch plan (B > 1), per layer:
+//   BQKV  (16-row blocks of one kv group's rotary pairs, all sequences: MFMA
+//          tile, rotary epilogue, KV append per sequence)
+//   ATTN  (per sequence, kv group and page range of that sequence's bound)
+//   COMB  (per sequence, query head and dim range)
+//   BO    (16-row blocks of W_o, all sequences: MFMA tile, residual)
+//   TOPK  (MoE, one per sequence: router rows, softmax, top-k)
+//   BEXP  (one expert, part q: gate/up rows with SwiGLU, then down rows, for
+//          the sequences routed to it; the down part reads the activations of
+//          every part of the same expert)
+//   BCOMB (per sequence and hidden-row range: weighted sum of its experts'
+//          outputs in slot order, plus the residual)
+// then BLM (16-row blocks of the LM head, all sequences: MFMA tile,
+// per-sequence argmax) and BFINAL (one per sequence).
+mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
+                       std::vector<std::vector<Task>>& stages) {
+  const auto& m = p->m;
+  const int L = m.n_layers, H = m.hidden, Hq = m.n_q_heads, Hkv = m.n_kv_heads, D = m.head_dim;
+  const int B = p->B, HG = p->HG, n_cu = p->n_cu, F = p->F;
+  const bool moe = m.n_experts > 0;
+  const int NE = moe ? m.n_experts : 1;
+  auto ctr16 = [](int c) { return c < 0 ? mk::NO_CTR : (uint16_t)c; };
+  int P = std::max(1, n_cu / NE);
+  P = std::min(P, std::min(F / 8, H / 16));
+  p->n_exp_parts = P;
+  if (NE * P > n_cu) return fail(MK_EUNSUPPORTED, "mk_plan: more expert tasks than compute units");
+  // an expert task holds EXP_GROUP inputs of width H or F and up to 1024 result rows in LDS
+  if (H > 2048 || F > 2048 || 2 * ceil_div(F, P) > 1024 || ceil_div(H, P) > 1024)
+    return fail(MK_EUNSUPPORTED, "mk_plan: batch expert tiles exceed LDS (hidden and FFN <= 2048, "
+                                 "rows per expert task <= 1024): use more compute units");
+  for (int l = 0; l < L; ++l) {
+    {  // BQKV: 8 rotary pairs per row block
+      std::vector<Task> st;
+      for (int g = 0; g < Hkv; ++g)
+        for (int s0 = 0; s0 < p->n_pairs_g; s0 += 8 * QKV_BLOCKS) {
+          Task t = mk_task(mk::OP_BQKV, l);
+          t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_bcomb[l - 1]);
+          t.signal = ctr16(p->c_qkv[l * Hkv + g]);
+          t.a0 = g; t.a1 = s0; t.a2 = std::min(8 * QKV_BLOCKS, p->n_pairs_g - s0);
+          st.push_back(t);
+        }
+      stages.push_back(st);
+    }
+    {  // ATTN
+      std::vector<Task> st;
+      for (int b = 0; b < B; ++b)
+        for (int g = 0; g < Hkv; ++g) {
+          int si = 0;
+          for (auto [s0, c] : split_even(pages_b[b], p->n_split[b])) {
+            Task t = mk_task(mk::OP_ATTN, l);
+            t.wait_b = ctr16(p->c_qkv[l * Hkv + g]);
+            t.signal = ctr16(p->c_attn[l * Hkv + g]);
+            t.a0 = b; t.a1 = g; t.a2 = s0; t.a3 = c; t.aux = (uint16_t)si++;
+            st.push_back(t);
+          }
+        }
+      // longest splits first: dealt round-robin, the units' page counts even out
+      std::stable_sort(st.begin(), st.end(), [](const Task& x, const Task& y) { return x.a3 > y.a3; });
+      stages.push_back(st);
+    }
+    {  // COMB
+      std::vector<Task> st;
+      for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hq; ++h)
+          for (auto [d0, nd] : split_even(D, p->comb_dim_tasks)) {
+            Task t = mk_task(mk::OP_COMB, l);
+            t.wait_b = ctr16(p->c_attn[l * Hkv + h / HG]);
+            t.signal = ctr16(p->c_comb[l]);
+            t.a0 = b; t.a1 = h; t.a2 = d0; t.a3 = nd; t.aux = (uint16_t)p->n_split[b];
+            st.push_back(t);
+          }
+      stages.push_back(st);
+    }
+    {  // BO
+      std::vector<Task> st;
+      for (int s0 = 0; s0 < H; s0 += 16 * O_BLOCKS) {
+        Task t = mk_task(mk::OP_BO, l);
+        t.wait_b = ctr16(p->c_comb[l]);
+        t.signal = ctr16(p->c_o[l]);
+        t.a1 = s0; t.a2 = std::min(16 * O_BLOCKS, H - s0);
+        st.push_back(t);
+      }
+      stages.push_back(st);
+    }
+    if (moe) {  // TOPK
+      std::vector<Task> tk;
+      for (int b = 0; b < B; ++b) {
+        Task t = mk_task(mk::OP_TOPK, l);
+        t.wait_b = ctr16(p->c_o[l]);
+        t.signal = ctr16(p->c_topk[l]);
+        t.a0 = b;
+        tk.push_back(t);
+      }
+      stages.push_back(tk);
+    }
+    {  // BEXP
+      std::vector<Task> st;
+      const auto fr = split_units(F, 8, P), hr = split_units(H, 16, P);
+      for (int e = 0; e < NE; ++e)
+        for (int q = 0; q < P; ++q) {
+          Task t = mk_task(mk::OP_BEXP, l);
+          t.wait_a = moe ? ctr16(p->c_topk[l]) : mk::NO_CTR;
+          t.wait_b = ctr16(p->c_o[l]);
+          t.signal = ctr16(p->c_expert[l]);
+          t.a0 = e;
+          t.a1 = q < (int)fr.size() ? fr[q].first : 0;
+          t.a2 = q < (int)fr.size() ? fr[q].second : 0;
+          t.a3 = q < (int)hr.size() ? (hr[q].first << 16) | hr[q].second : 0;
+          st.push_back(t);
+        }
+      stages.push_back(st);
+    }
+    {  // BCOMB: its words (slots x rows + residual rows + weights) fit the gather vector
+      std::vector<Task> st;
+      const int KK = moe ? m.top_k : 1;
+      const int max_rows = std::max(16, (mk::dev_lds_vec() - KK) / (KK + 1) / 16 * 16);
+      const int per_b = std::max(std::max(1, n_cu / B), ceil_div(H, max_rows));
+      for (int b = 0; b < B; ++b)
+        for (auto [s0, c] : split_units(H, 16, per_b)) {
+          Task t = mk_task(mk::OP_BCOMB, l);
+          t.wait_a = moe ? ctr16(p->c_topk[l]) : mk::NO_CTR;
+          t.wait_b = ctr16(p->c_expert[l]);
+          t.signal = ctr16(p->c_bcomb[l]);
+          t.a0 = b; t.a1 = s0; t.a2 = c;
+          st.push_back(t);
+        }
+      stages.push_back(st);
+    }
+  }
+  {  // BLM, BFINAL
+    std::vector<Task> st;
+    const int rows = 16 * LM_BLOCKS;
+    int i = 0;
+    for (int s0 = 0; s0 < m.vocab; s0 += rows) {
+      Task t = mk_task(mk::OP_BLM, 0);
+      t.wait_b = ctr16(p->c_bcomb[L - 1]);
+      t.signal = ctr16(p->c_lm);
+      t.a1 = s0; t.a2 = std::min(rows, m.vocab - s0); t.a3 = i++;
+      st.push_back(t);
+    }
+    p->n_lm = i;
+    if (p->n_lm > 4096) return fail(MK_EUNSUPPORTED, "mk_plan: more than 4096 LM-head tiles");
+    stages.push_back(st);
+    std::vector<Task> fin;
+    for (int b = 0; b < B; ++b) {
+      Task f = mk_task(mk::OP_BFINAL, 0);
+      f.wait_b = ctr16(p->c_lm);
+      f.a0 = p->n_lm; f.a1 = b;
+      fin.push_back(f);
+    }
+    stages.push_back(fin);
+  }
+  return MK_OK;
+}
+
 }  // namespace
 
 extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
@@ -121,23 +292,40 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
                                        std::to_string(F) + ", head dim " + std::to_string(D));
   }
   const int B = bd->batch;
-  if (B != 1) return fail(MK_EUNSUPPORTED, "mk_plan: only batch 1 is implemented by the kernels");
+  if (B < 1 || B > mk::MAX_BATCH)
+    return fail(MK_EUNSUPPORTED, "mk_plan: batch must be 1 .. " + std::to_string(mk::MAX_BATCH));
+  const bool batch = B > 1;
+  if (batch) {
+    for (int K : {H, Hq * D, F})
+      if (K % mk::MT_KP)
+        return fail(MK_EUNSUPPORTED, "mk_plan: batch plans need hidden, heads x dim and FFN widths "
+                                     "that are multiples of " + std::to_string(mk::MT_KP));
+    if (moe && B * m->top_k > mk::NT)
+      return fail(MK_EUNSUPPORTED, "mk_plan: batch x top_k must be at most " + std::to_string(mk::NT));
+  }
   if (m->page_tokens != 16) return fail(MK_EUNSUPPORTED, "mk_plan: page_tokens must be 16");
   if (!bd->seq_lens || !bd->page_table || bd->max_pages <= 0)
     return fail(MK_EINVAL, "mk_plan: seq_lens / page_table / max_pages missing");
-  const int bound = bd->max_ctx_bound;
-  const int pg_bound = (bound + 15) / 16;
-  if (bound <= 0 || pg_bound > bd->max_pages)
-    return fail(MK_EBOUNDS, "mk_plan: max_ctx_bound needs " + std::to_string(pg_bound) +
+  const int max_bound = bd->max_ctx_bound;
+  if (max_bound <= 0 || (max_bound + 15) / 16 > bd->max_pages)
+    return fail(MK_EBOUNDS, "mk_plan: max_ctx_bound needs " + std::to_string((max_bound + 15) / 16) +
                                 " pages per sequence, page table has " + std::to_string(bd->max_pages));
+  std::vector<int32_t> seq_bound(B);
   for (int b = 0; b < B; ++b) {
-    if (bd->seq_lens[b] < 0 || bd->seq_lens[b] + 1 > bound)
-      return fail(MK_EBOUNDS, "mk_plan: seq_lens[" + std::to_string(b) + "] + 1 exceeds max_ctx_bound");
-    for (int j = 0; j < pg_bound; ++j)
+    const int bb = bd->ctx_bounds ? bd->ctx_bounds[b] : max_bound;
+    if (bb <= 0 || bb > max_bound)
+      return fail(MK_EBOUNDS, "mk_plan: ctx_bounds[" + std::to_string(b) + "] outside (0, max_ctx_bound]");
+    seq_bound[b] = bb;
+    if (bd->seq_lens[b] < 0 || bd->seq_lens[b] + 1 > bb)
+      return fail(MK_EBOUNDS, "mk_plan: seq_lens[" + std::to_string(b) + "] + 1 exceeds its context bound");
+    for (int j = 0; j < (bb + 15) / 16; ++j)
       if (bd->page_table[(int64_t)b * bd->max_pages + j] < 0)
         return fail(MK_EBOUNDS, "mk_plan: sequence " + std::to_string(b) +
                                     " has no page mapped at logical page " + std::to_string(j));
   }
+  // batch 1 runs with its own bound; a batch keeps max_ctx_bound as the plan bound
+  const int bound = batch ? max_bound : seq_bound[0];
+  const int pg_bound = (bound + 15) / 16;
   int n_cu = o && o->n_cu > 0 ? o->n_cu : 0;
   if (n_cu == 0) {
     if (mk_device_cu_count(&n_cu) != MK_OK || n_cu <= 0)
@@ -151,6 +339,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   p->max_pages = bd->max_pages;
   p->bound = bound;
   p->n_cu = n_cu;
+  p->batch = batch;
+  p->seq_bound = seq_bound;
   p->seq_lens.assign(bd->seq_lens, bd->seq_lens + B);
   p->page_table.assign(bd->page_table, bd->page_table + (int64_t)B * bd->max_pages);
   p->kernel_class = kclass;
@@ -170,14 +360,32 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   // unit pulls from, so that units streaming faster take more of them. On
   // MI355X the static splits are faster even at 262144 tokens: a pulled split
   // restarts its page pipeline, its query gather and its merge.
-  const int pg_total = pg_bound * B * Hkv;
+  std::vector<int> pages_b(B);
+  int pg_total = 0;
+  for (int b = 0; b < B; ++b) {
+    pages_b[b] = batch ? (seq_bound[b] + 15) / 16 : pg_bound;
+    pg_total += pages_b[b] * Hkv;
+  }
   const int flags = o ? o->flags : 0;
   int pps = o && o->attn_split_pages > 0 ? o->attn_split_pages : (pg_total + n_cu - 1) / n_cu;
   const bool queue = !(flags & MK_PLAN_NO_ATTN_QUEUE) && B == 1 && (flags & MK_PLAN_ATTN_QUEUE);
   if (queue) pps = mk::QUEUE_PAGES;
+  // a batch: about four splits per unit, so that ragged lengths even out
+  if (batch && !(o && o->attn_split_pages > 0)) pps = std::max(8, ceil_div(pg_total, 4 * n_cu));
   p->attn_queue = queue;
   for (int l = 0; l < L; ++l) {
     const std::string ls = std::to_string(l);
+    if (batch) {
+      for (int g = 0; g < Hkv; ++g) p->c_qkv.push_back(new_ctr("qkv[" + ls + "][" + std::to_string(g) + "]"));
+      for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + ls + "][" + std::to_string(g) + "]"));
+      p->c_comb.push_back(new_ctr("comb[" + ls + "]"));
+      p->c_o.push_back(new_ctr("o[" + ls + "]"));
+      p->c_router.push_back(-1);
+      p->c_topk.push_back(moe ? new_ctr("topk[" + ls + "]") : -1);
+      p->c_expert.push_back(new_ctr("expert[" + ls + "]"));
+      p->c_bcomb.push_back(new_ctr("ffn[" + ls + "]"));
+      continue;
+    }
     if (queue) {  // one QKV and one attention counter per layer: a queue task takes any group
       const int cq = new_ctr("qkv[" + ls + "]"), ca = new_ctr("attn[" + ls + "]");
       for (int g = 0; g < Hkv; ++g) p->c_qkv.push_back(cq), p->c_attn.push_back(ca);
@@ -198,12 +406,13 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   }
 
   pps = std::max(std::max(1, pps), (pg_bound + 1023) / 1024);  // at most 1024 splits per (b, g)
+  if (batch && pps > mk::NT) pps = mk::NT;
   if (pps > 2 * mk::NT) {
     delete p;
     return fail(MK_EUNSUPPORTED, "mk_plan: more than " + std::to_string(2 * mk::NT) + " pages per attention split");
   }
   p->n_split.assign(B, 0);
-  for (int b = 0; b < B; ++b) p->n_split[b] = (pg_bound + pps - 1) / pps;
+  for (int b = 0; b < B; ++b) p->n_split[b] = (pages_b[b] + pps - 1) / pps;
   p->S_max = *std::max_element(p->n_split.begin(), p->n_split.end());
   p->comb_dim_tasks = std::max(1, std::min(D / 8, n_cu / std::max(1, B * Hq)));
   while (p->comb_dim_tasks < D / 8 && (size_t)p->S_max * (ceil_div(D, p->comb_dim_tasks) + 2) > 8192)
@@ -211,7 +420,14 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
 
   std::vector<std::vector<Task>> stages;
   auto ctr16 = [](int c) { return c < 0 ? mk::NO_CTR : (uint16_t)c; };
-  for (int l = 0; l < L; ++l) {
+  if (batch) {
+    mk_status st = batch_stages(p, pages_b, stages);
+    if (st != MK_OK) {
+      delete p;
+      return st;
+    }
+  }
+  for (int l = 0; l < L && !batch; ++l) {
     // QKV: tiles of rotary pairs within one kv group
     {
       std::vector<Task> st;
@@ -253,6 +469,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
             st.push_back(t);
           }
         }
+      // longest splits first: dealt round-robin, the units' page counts even out
+      std::stable_sort(st.begin(), st.end(), [](const Task& x, const Task& y) { return x.a3 > y.a3; });
       stages.push_back(st);
     }
     // COMB: one query head of one sequence, a range of its dims, per task
@@ -339,7 +557,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     }
   }
   // LM head (rows per tile a multiple of the streaming batch) and the final argmax merge
-  {
+  if (!batch) {
     std::vector<Task> st;
     int tch = 64, cplh = 1;
     mk::gemv_map(H, &tch, &cplh);
@@ -405,7 +623,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   // workspace layout: tagged words (8 bytes), per layer
   {
     const int PS = D + 2;
-    size_t per_layer[9] = {
+    size_t per_layer[mk_plan::N_BUF] = {
         (size_t)B * H,                                    // XATTN
         (size_t)B * H,                                    // XFFN
         (size_t)B * Hq * D,                               // Q
@@ -414,9 +632,11 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         moe ? (size_t)B * m->n_experts : 0,               // RLOG
         (size_t)B * K * F,                                // ACT
         0,                                                // LMPART (not per layer)
-        (size_t)B * Hkv * 2 * D};                         // KVN
+        (size_t)B * Hkv * 2 * D,                          // KVN
+        batch && moe ? (size_t)B * K * 2 : 0,             // ROUTE
+        batch ? (size_t)B * K * H : 0};                   // Y
     size_t off = 0;
-    for (int i = 0; i < 9; ++i) {
+    for (int i = 0; i < mk_plan::N_BUF; ++i) {
       p->ws_off[i] = off;
       if (i == MK_BUF_LMPART) {
         p->ws_stride[i] = 0;
@@ -435,7 +655,9 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   {
     size_t hdr = (mk::PLAN_HDR_WORDS + n_cu + 1) * 4;
     size_t task_off = (hdr + 31) & ~size_t(31);
-    p->image.assign(task_off + p->n_tasks * sizeof(Task), 0);
+    const size_t bound_off = task_off + p->n_tasks * sizeof(Task);
+    p->image.assign(bound_off + (size_t)B * 4, 0);
+    std::memcpy(p->image.data() + bound_off, p->seq_bound.data(), (size_t)B * 4);
     uint32_t* w = reinterpret_cast<uint32_t*>(p->image.data());
     w[mk::H_MAGIC] = mk::PLAN_MAGIC;
     w[mk::H_NCU] = (uint32_t)n_cu;
@@ -443,6 +665,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     w[mk::H_NCTR] = (uint32_t)p->targets.size();
     w[mk::H_TASK_OFF_BYTES] = (uint32_t)task_off;
     w[mk::H_STAGES] = (uint32_t)p->n_stages;
+    w[mk::H_BOUND_OFF_BYTES] = (uint32_t)bound_off;
+    w[mk::H_BATCH] = (uint32_t)B;
     uint32_t* off = w + mk::PLAN_HDR_WORDS;
     Task* tasks = reinterpret_cast<Task*>(p->image.data() + task_off);
     uint32_t k = 0;
@@ -467,6 +691,7 @@ void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::
   const std::string ls = ":" + std::to_string(t.layer);
   switch (t.op) {
     case mk::OP_QKV:
+    case mk::OP_BQKV:
       for (int q = t.a1; q < t.a1 + t.a2; ++q) {
         int head, i, row;
         mk::qkv_pair(q, t.a0, p->HG, D, Hq, Hkv, &head, &i, &row);
@@ -492,16 +717,34 @@ void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::
       break;
     }
     case mk::OP_O:
+    case mk::OP_BO:
       for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"o" + ls, r});
       break;
     case mk::OP_ROUTER:
       for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"router" + ls, r});
       break;
+    case mk::OP_TOPK:  // every router row of one sequence, and its top-k
+      for (int r = 0; r < m.n_experts; ++r) out.push_back({"router" + ls, (int64_t)t.a0 * 1000000 + r});
+      out.push_back({"topk" + ls, t.a0});
+      break;
+    case mk::OP_BEXP: {
+      for (int f = t.a1; f < t.a1 + t.a2; ++f) out.push_back({"gateup" + ls, (int64_t)t.a0 * 1000000 + f});
+      const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
+      for (int r = r0; r < r0 + nr; ++r) out.push_back({"down" + ls, (int64_t)t.a0 * 1000000 + r});
+      break;
+    }
+    case mk::OP_BCOMB:
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"ffn" + ls, (int64_t)t.a0 * 1000000 + r});
+      break;
     case mk::OP_LM:
+    case mk::OP_BLM:
       for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"lm", r});
       break;
     case mk::OP_FINAL:
       out.push_back({"final", 0});
+      break;
+    case mk::OP_BFINAL:
+      out.push_back({"final", t.a1});
       break;
   }
 }
@@ -520,12 +763,28 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
     for (int r = 0; r < p->QKV_ROWS; ++r) want["qkv" + ls].insert(r);
     for (int b = 0; b < B; ++b)
       for (int g = 0; g < m.n_kv_heads; ++g)
-        for (int pg = 0; pg < (p->bound + 15) / 16; ++pg)
+        for (int pg = 0; pg < ((p->batch ? p->seq_bound[b] : p->bound) + 15) / 16; ++pg)
           want["attn" + ls].insert(((int64_t)b * m.n_kv_heads + g) * 1000000 + pg);
     for (int b = 0; b < B; ++b)
       for (int h = 0; h < m.n_q_heads; ++h)
         for (int d = 0; d < m.head_dim; ++d) want["comb" + ls].insert(((int64_t)b * m.n_q_heads + h) * 1024 + d);
-    for (int r = 0; r < m.hidden; ++r) want["o" + ls].insert(r), want["down" + ls].insert(r);
+    for (int r = 0; r < m.hidden; ++r) want["o" + ls].insert(r);
+    if (p->batch) {
+      const int NE = moe ? m.n_experts : 1;
+      if (moe)
+        for (int b = 0; b < B; ++b) {
+          for (int r = 0; r < m.n_experts; ++r) want["router" + ls].insert((int64_t)b * 1000000 + r);
+          want["topk" + ls].insert(b);
+        }
+      for (int e = 0; e < NE; ++e) {
+        for (int f = 0; f < p->F; ++f) want["gateup" + ls].insert((int64_t)e * 1000000 + f);
+        for (int r = 0; r < m.hidden; ++r) want["down" + ls].insert((int64_t)e * 1000000 + r);
+      }
+      for (int b = 0; b < B; ++b)
+        for (int r = 0; r < m.hidden; ++r) want["ffn" + ls].insert((int64_t)b * 1000000 + r);
+      continue;
+    }
+    for (int r = 0; r < m.hidden; ++r) want["down" + ls].insert(r);
     if (moe) {
       for (int r = 0; r < m.n_experts; ++r) want["router" + ls].insert(r);
       for (int b = 0; b < B; ++b)
@@ -536,7 +795,7 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
     }
   }
   for (int r = 0; r < m.vocab; ++r) want["lm"].insert(r);
-  want["final"].insert(0);
+  for (int b = 0; b < (p->batch ? B : 1); ++b) want["final"].insert(b);
 
   std::map<std::string, std::multiset<int64_t>> got;
   std::vector<uint32_t> producers(p->targets.size(), 0);
@@ -549,7 +808,7 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
       int st = p->stage_of_task[k++];
       if (st < last) return fail(MK_EINVAL, "validate: list of unit " + std::to_string(cu) + " is not in stage order");
       last = st;
-      if (t.op == mk::OP_EXPERT && !expert_layers.insert(t.layer).second)
+      if ((t.op == mk::OP_EXPERT || t.op == mk::OP_BEXP) && !expert_layers.insert(t.layer).second)
         return fail(MK_EINVAL, "validate: unit " + std::to_string(cu) + " holds two expert tasks of layer " +
                                    std::to_string(t.layer) + " (their down parts would wait on each other)");
       std::vector<std::pair<std::string, int64_t>> outs;
@@ -618,10 +877,14 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
       total[slot(t.op, t.layer, Hkv)]++;
       if (t.op == mk::OP_ATTN && (t.flags & mk::TF_QUEUE)) {
         for (int g = 0; g < Hkv; ++g) total[slot(t.op, t.layer, g)]++;
-      } else if (t.op == mk::OP_QKV || t.op == mk::OP_ATTN) {
-        total[slot(t.op, t.layer, t.op == mk::OP_QKV ? t.a0 : t.a1)]++;
+      } else if (t.op == mk::OP_QKV || t.op == mk::OP_BQKV || t.op == mk::OP_ATTN) {
+        total[slot(t.op, t.layer, t.op == mk::OP_ATTN ? t.a1 : t.a0)]++;
       }
     }
+  const int qkv_op = p->batch ? mk::OP_BQKV : mk::OP_QKV;
+  // two-phase tasks: gate/up published first, the down part waits for every
+  // expert task of its layer
+  auto two_phase = [](int op) { return op == mk::OP_EXPERT || op == mk::OP_BEXP; };
   for (int run = 0; run < n_runs; ++run) {
     const uint64_t epoch = (uint64_t)run + 1;
     std::vector<uint32_t> done(n_slots, 0);
@@ -640,13 +903,20 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
       switch (t.op) {
         case mk::OP_QKV: return l == 0 || all_done(mk::OP_EXPERT, l - 1, Hkv);
         case mk::OP_ATTN:
-          return (t.flags & mk::TF_QUEUE) ? all_done(mk::OP_QKV, l, Hkv) : all_done(mk::OP_QKV, l, t.a1);
+          return (t.flags & mk::TF_QUEUE) ? all_done(qkv_op, l, Hkv) : all_done(qkv_op, l, t.a1);
         case mk::OP_COMB: return all_done(mk::OP_ATTN, l, t.a1 / HG);
         case mk::OP_O: return all_done(mk::OP_COMB, l, Hkv);
         case mk::OP_ROUTER: return all_done(mk::OP_O, l, Hkv);
         case mk::OP_EXPERT: return all_done(mk::OP_O, l, Hkv) && (!moe || all_done(mk::OP_ROUTER, l, Hkv));
         case mk::OP_LM: return all_done(mk::OP_EXPERT, L - 1, Hkv);
         case mk::OP_FINAL: return all_done(mk::OP_LM, 0, Hkv);
+        case mk::OP_BQKV: return l == 0 || all_done(mk::OP_BCOMB, l - 1, Hkv);
+        case mk::OP_BO: return all_done(mk::OP_COMB, l, Hkv);
+        case mk::OP_TOPK: return all_done(mk::OP_BO, l, Hkv);
+        case mk::OP_BEXP: return all_done(mk::OP_BO, l, Hkv) && (!moe || all_done(mk::OP_TOPK, l, Hkv));
+        case mk::OP_BCOMB: return all_done(mk::OP_BEXP, l, Hkv) && (!moe || all_done(mk::OP_TOPK, l, Hkv));
+        case mk::OP_BLM: return all_done(mk::OP_BCOMB, L - 1, Hkv);
+        case mk::OP_BFINAL: return all_done(mk::OP_BLM, 0, Hkv);
       }
       return false;
     };
@@ -657,8 +927,8 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
       for (int cu = 0; cu < p->n_cu; ++cu) {
         if (head[cu] >= p->lists[cu].size()) continue;
         const Task& t = p->lists[cu][head[cu]];
-        if (t.op == mk::OP_EXPERT && phase[cu] == 1) {
-          if (published[t.layer] == total[slot(mk::OP_EXPERT, t.layer, Hkv)]) runnable.push_back(cu);
+        if (two_phase(t.op) && phase[cu] == 1) {
+          if (published[t.layer] == total[slot(t.op, t.layer, Hkv)]) runnable.push_back(cu);
         } else if (waits_ok(t)) {
           runnable.push_back(cu);
         }
@@ -682,7 +952,7 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
       for (size_t i = 0; i < n; ++i) {
         int cu = runnable[i];
         const Task& t = p->lists[cu][head[cu]];
-        if (t.op == mk::OP_EXPERT && phase[cu] == 0) {
+        if (two_phase(t.op) && phase[cu] == 0) {
           if (!inputs_ok(t))
             return fail(MK_ESTATE, "simulate: expert layer " + std::to_string(t.layer) +
                                        " ran before its producers finished");
@@ -690,14 +960,14 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
           published[t.layer]++;
           continue;
         }
-        if (t.op != mk::OP_EXPERT && !inputs_ok(t))
+        if (!two_phase(t.op) && !inputs_ok(t))
           return fail(MK_ESTATE, "simulate: op " + std::to_string(t.op) + " layer " +
                                      std::to_string(t.layer) + " ran before its producers finished");
         phase[cu] = 0;
         head[cu]++;
         remaining--;
         done[slot(t.op, t.layer, Hkv)]++;
-        if (t.op == mk::OP_QKV) done[slot(t.op, t.layer, t.a0)]++;
+        if (t.op == mk::OP_QKV || t.op == mk::OP_BQKV) done[slot(t.op, t.layer, t.a0)]++;
         if (t.op == mk::OP_ATTN && (t.flags & mk::TF_QUEUE)) {
           for (int g = 0; g < Hkv; ++g) done[slot(t.op, t.layer, g)]++;
         } else if (t.op == mk::OP_ATTN) {
@@ -734,7 +1004,8 @@ extern "C" mk_status mk_plan_export(const mk_plan_t* p, void* buf, size_t bytes)
 
 extern "C" mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t layer, size_t* off,
                                     size_t* bytes) {
-  if (!p || !off || !bytes || which < 0 || which > 8) return fail(MK_EINVAL, "mk_plan_buffer: bad args");
+  if (!p || !off || !bytes || which < 0 || which >= mk_plan::N_BUF)
+    return fail(MK_EINVAL, "mk_plan_buffer: bad args");
   const bool per_layer = which != MK_BUF_LMPART;
   if (per_layer && (layer < 0 || layer >= p->m.n_layers)) return fail(MK_EINVAL, "mk_plan_buffer: bad layer");
   *off = p->ws_off[which] + (per_layer ? (size_t)layer * p->ws_stride[which] : 0);

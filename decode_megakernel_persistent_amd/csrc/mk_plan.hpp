@@ -9,7 +9,9 @@
 struct mk_plan {
   mk_model_desc m;
   int32_t B = 0, max_pages = 0, bound = 0, n_cu = 0;
+  bool batch = false;                 // B > 1: MFMA batch tasks
   std::vector<int32_t> seq_lens, page_table;
+  std::vector<int32_t> seq_bound;     // per sequence context bound
 
   // derived shape
   int32_t HG = 0, QKV_ROWS = 0, F = 0, n_pairs_g = 0;
@@ -23,6 +25,7 @@ struct mk_plan {
   std::vector<int32_t> c_qkv, c_attn;  // [L][Hkv]
   std::vector<int32_t> c_comb, c_o, c_router, c_expert;  // [L]
   std::vector<int32_t> c_queue;  // [L] attention split queue (queue mode)
+  std::vector<int32_t> c_topk, c_bcomb;  // [L] batch: top-k per sequence, expert combine
   int32_t c_lm = -1;
   bool attn_queue = false;
 
@@ -33,7 +36,9 @@ struct mk_plan {
   int32_t n_lm = 0, n_stages = 0;
 
   // workspace layout: base offset (bytes) and per-layer stride (bytes) per MK_BUF_*
-  size_t ws_off[9] = {}, ws_stride[9] = {}, ws_layer_bytes[9] = {};
+  static constexpr int N_BUF = 11;
+  size_t ws_off[N_BUF] = {}, ws_stride[N_BUF] = {}, ws_layer_bytes[N_BUF] = {};
+  int32_t n_exp_parts = 1;          // batch: expert tasks per expert
   size_t ws_total = 0;
 
   std::vector<uint8_t> image;  // device image

@@ -49,17 +49,20 @@ class Decoder:
     bf16 tensors (fixtures.device.weights layout). pool: bf16 KV pool tensor.
     seq_lens: host ints (tokens cached per sequence). page_table: host
     [batch][max_pages] ints. bound: the plan stays valid while every
-    sequence's length + 1 <= bound.
+    sequence's length + 1 <= bound; ctx_bounds: per-sequence bounds (each
+    <= bound), or None.
     """
 
     def __init__(self, model, weights, pool, n_pages, seq_lens, page_table, max_pages, bound,
-                 n_cu=0, attn_split_pages=0, device="cuda", trace=False, plan_flags=0):
+                 n_cu=0, attn_split_pages=0, device="cuda", trace=False, plan_flags=0,
+                 ctx_bounds=None):
         self.m = dict(model)
         self.device = torch.device(device)
         self.B = len(seq_lens)
         self.desc = model_desc(self.m)
         flat = [int(v) for row in page_table for v in row]
-        self.plan = mk_plan(self.desc, seq_lens, flat, max_pages, bound, n_cu, attn_split_pages, plan_flags)
+        self.plan = mk_plan(self.desc, seq_lens, flat, max_pages, bound, n_cu, attn_split_pages, plan_flags,
+                            ctx_bounds)
         self.bound = bound
         dev = self.device
         self.plan_buf = torch.empty(mk_plan_device_bytes(self.plan), dtype=torch.uint8, device=dev)

@@ -10,7 +10,8 @@ it into per-operation time splits and a per-stage timeline.
 import numpy as np
 
 OPS = {1: "qkv", 2: "attn", 3: "comb", 4: "o", 5: "router", 6: "expert", 8: "lm",
-       9: "final"}
+       9: "final", 10: "bqkv", 11: "bo", 13: "topk", 14: "bexp", 15: "bcomb", 16: "blm",
+       17: "bfinal"}
 TICK_US = 0.01  # 100 MHz
 
 

@@ -49,9 +49,10 @@ def gpu_session(w, seed=0, device="cuda", weights=None, n_cu=0, attn_split_pages
     kvpool = alloc_kv_pool(m, w["pool_pages"], device)
     W = weights if weights is not None else fxd.weights(m, seed, device)
     bound = max(w["ctx"]) + w["steps"]
+    ctx_bounds = [c + w["steps"] for c in w["ctx"]] if B > 1 else None
     dec = Decoder(m, W, kvpool, w["pool_pages"], w["ctx"], rows, max_pages, bound,
                   n_cu=n_cu, attn_split_pages=attn_split_pages, device=device, trace=trace,
-                  plan_flags=plan_flags)
+                  plan_flags=plan_flags, ctx_bounds=ctx_bounds)
     for b in range(B):
         fxd.fill_kv(kvpool, dec.page_table[b], m, seed, b, w["ctx"][b])
     torch.cuda.synchronize(device)

@@ -32,6 +32,19 @@ WORKLOADS = {
                           pool_pages=16500),
 }
 
+# Batch parity cases on the small shapes: ragged contexts, one of them empty
+# and one a single token, so that batch plans are checked against the oracle
+# at sizes it finishes in seconds.
+_TINY = WORKLOADS["tiny_dense"]["model"]
+_SMALL = WORKLOADS["small_moe"]["model"]
+WORKLOADS.update({
+    "tiny_dense_b3": dict(model=dict(_TINY), batch=3, ctx=[128, 0, 47], steps=16, pool_pages=64),
+    "small_moe_b5": dict(model=dict(_SMALL), batch=5, ctx=[2048, 1, 517, 1300, 16], steps=16,
+                         pool_pages="sum*1.1"),
+    "small_moe_b32": dict(model=dict(_SMALL), batch=32, ctx="uniform[1,1024]", steps=16,
+                          pool_pages="sum*1.1"),
+})
+
 SIGMA_W = 0.02
 SIGMA_KV = 1.0
 NORM_GAIN_BITS = 0x3F80  # bf16 1.0
@@ -53,7 +66,7 @@ def resolve(w, seed=0):
     w = copy.deepcopy(w)
     m, B = w["model"], w["batch"]
     if isinstance(w["ctx"], str):
-        lo, hi = 512, 32768
+        lo, hi = (int(v) for v in w["ctx"][len("uniform["):-1].split(","))
         w["ctx"] = [int(v) for v in host.uniform(seed, host.FX_CTX, B, lo, hi)]
     pt = m["page_tokens"]
     if isinstance(w["pool_pages"], str):

@@ -86,6 +86,10 @@ typedef struct mk_batch_desc {
   const int32_t* page_table;   /* [batch][max_pages] physical page ids, -1 = none */
   int32_t max_ctx_bound;       /* the plan stays valid while every seq_len + 1 <= bound;
                                   every sequence must have ceil(bound/16) pages mapped */
+  const int32_t* ctx_bounds;   /* [batch] per-sequence bounds (<= max_ctx_bound; sequence b
+                                  needs ceil(ctx_bounds[b]/16) pages mapped), or NULL: every
+                                  sequence uses max_ctx_bound. Attention work is split by
+                                  these bounds, so ragged batches plan only live pages. */
 } mk_batch_desc;
 
 typedef struct mk_plan_opts {
@@ -187,7 +191,11 @@ mk_status mk_step_bytes(const mk_model_desc* m, int32_t batch, const int32_t* se
 /* Build the task lists, counters and workspace layout for one batch shape
  * (megakernel page, caption of Image 2: the host decomposes the step into
  * tasks of one tile of one operation each and deals them round-robin over
- * the compute units). */
+ * the compute units). Batch 1 runs GEMV tiles; a batch of 2 .. 64 sequences
+ * (continuous batching with ragged contexts, megakernel page, "Inside the
+ * megakernel serving engine": continuous batching over a paged cache) runs
+ * every projection as MFMA tiles over all sequences, a top-k task per
+ * sequence and expert tasks that pick up the sequences routed to them. */
 mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* b, const mk_plan_opts* o,
                   mk_plan_t** out);
 /* Coverage (every output row / KV page exactly once), counter targets equal
@@ -215,9 +223,13 @@ mk_status mk_plan_upload(const mk_plan_t* p, void* d_plan, size_t bytes, void* h
  *   Q [B][Hq][d] rotated queries, KVN [B][Hkv][2][d] the new token's K and V,
  *   PART [B][Hkv][splits][Hq/Hkv][d+2] attention split partials (o, max, sum),
  *   O [B][Hq][d] combined attention, RLOG [B][E] router logits,
- *   ACT [B][top_k][F] SwiGLU activations. */
+ *   ACT [B][top_k][F] SwiGLU activations;
+ * batch plans only (0 bytes at batch 1):
+ *   ROUTE [B][top_k][2] selected expert id (int bits) and weight per slot,
+ *   Y [B][top_k][H] each selected expert's down-projection output. */
 enum { MK_BUF_XATTN = 0, MK_BUF_XFFN = 1, MK_BUF_Q = 2, MK_BUF_PART = 3, MK_BUF_O = 4,
-       MK_BUF_RLOG = 5, MK_BUF_ACT = 6, MK_BUF_LMPART = 7, MK_BUF_KVN = 8 };
+       MK_BUF_RLOG = 5, MK_BUF_ACT = 6, MK_BUF_LMPART = 7, MK_BUF_KVN = 8,
+       MK_BUF_ROUTE = 9, MK_BUF_Y = 10 };
 mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t layer, size_t* offset,
                          size_t* bytes);
 /* The plan's per-epoch counter targets, [n_counters] (host). */

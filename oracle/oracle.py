@@ -372,6 +372,13 @@ def work_sets(m, ctx_bound):
     elements (b, q head, dim) of the merged attention output; ("o", l) rows;
     ("router", l) rows; ("gateup", l)
     (b, slot, row) for MoE or rows for dense; ("down", l) rows; ("lm",) rows.
+
+    A batch of several sequences reads each expert's weights once for every
+    sequence routed to it, so its expert work is enumerated per expert, for
+    any routing: ("router", l) (b, expert row) router logits; ("topk", l)
+    sequences; ("gateup", l) (expert, FFN row) and ("down", l) (expert,
+    hidden row) over all experts (expert 0 for a dense FFN); ("ffn", l)
+    (b, hidden row) of the weighted expert sum.
     """
     L, H, Hq, Hkv, d = m["n_layers"], m["hidden"], m["n_q_heads"], m["n_kv_heads"], m["head_dim"]
     pt = m["page_tokens"]
@@ -383,6 +390,16 @@ def work_sets(m, ctx_bound):
                         for p in range(-(-ctx_bound[b] // pt))}
         S["comb", l] = {(b, h, i) for b in range(B) for h in range(Hq) for i in range(d)}
         S["o", l] = set(range(H))
+        if B > 1:
+            ne = max(1, m["n_experts"])
+            F = m["expert_ffn"] if m["n_experts"] else m["ffn_dim"]
+            if m["n_experts"]:
+                S["router", l] = {(b, e) for b in range(B) for e in range(m["n_experts"])}
+                S["topk", l] = set(range(B))
+            S["gateup", l] = {(e, f) for e in range(ne) for f in range(F)}
+            S["down", l] = {(e, r) for e in range(ne) for r in range(H)}
+            S["ffn", l] = {(b, r) for b in range(B) for r in range(H)}
+            continue
         if m["n_experts"]:
             S["router", l] = set(range(m["n_experts"]))
             S["gateup", l] = {(b, j, f) for b in range(B) for j in range(m["top_k"])

@@ -31,6 +31,8 @@ TASK = np.dtype([("op", "u1"), ("flags", "u1"), ("layer", "<u2"), ("wait_a", "<u
                  ("aux", "<u2"), ("a0", "<i4"), ("a1", "<i4"), ("a2", "<i4"), ("a3", "<i4")])
 OP_QKV, OP_ATTN, OP_COMB, OP_O, OP_ROUTER, OP_EXPERT = range(1, 7)
 OP_LM, OP_FINAL = 8, 9
+OP_BQKV, OP_BO = 10, 11
+OP_TOPK, OP_BEXP, OP_BCOMB, OP_BLM, OP_BFINAL = range(13, 18)
 NO_CTR = 0xFFFF
 TF_QUEUE = 2
 
@@ -111,7 +113,7 @@ def test_pool_lease_is_all_or_nothing():
 
 def decode_plan(img):
     hdr = np.frombuffer(img, dtype="<u4", count=16)
-    assert hdr[0] == 0x32504B4D
+    assert hdr[0] == 0x33504B4D
     n_cu, n_tasks, n_ctr, off = int(hdr[1]), int(hdr[2]), int(hdr[3]), int(hdr[4])
     cu_off = np.frombuffer(img, dtype="<u4", count=n_cu + 1, offset=64)
     tasks = np.frombuffer(img, dtype=TASK, count=n_tasks, offset=off)
@@ -149,8 +151,22 @@ def plan_coverage(tasks, m, bound):
     for t in tasks:
         op, l = int(t["op"]), int(t["layer"])
         a0, a1, a2, a3, aux = int(t["a0"]), int(t["a1"]), int(t["a2"]), int(t["a3"]), int(t["aux"])
-        if op == OP_QKV:
+        if op in (OP_QKV, OP_BQKV):
             add(("qkv", l), [r for p in range(a1, a1 + a2) for r in qkv_rows(p, a0, m)])
+        elif op == OP_BO:
+            add(("o", l), list(range(a1, a1 + a2)))
+        elif op == OP_TOPK:
+            # one sequence: every router row, then its top-k
+            add(("router", l), [(a0, e) for e in range(m["n_experts"])])
+            add(("topk", l), [a0])
+        elif op == OP_BEXP:
+            # one expert's gate/up rows (expert, FFN row) and down rows (expert, hidden row)
+            add(("gateup", l), [(a0, f) for f in range(a1, a1 + a2)])
+            add(("down", l), [(a0, r) for r in range(a3 >> 16, (a3 >> 16) + (a3 & 0xFFFF))])
+        elif op == OP_BCOMB:
+            add(("ffn", l), [(a0, r) for r in range(a1, a1 + a2)])
+        elif op == OP_BLM:
+            add(("lm",), list(range(a1, a1 + a2)))
         elif op == OP_ATTN and int(t["flags"]) & TF_QUEUE:
             # a shared queue of the layer's splits: (kv head, split) -> pages of
             # split * a2 .. + a2 (a1 splits per head), counted once per layer
@@ -176,12 +192,18 @@ def plan_coverage(tasks, m, bound):
     return S
 
 
+def ctx_bounds(w):
+    """Per-sequence context bounds of a workload's plan."""
+    return [c + w["steps"] for c in w["ctx"]]
+
+
 def build_plan(name, n_cu=256, flags=0, **over):
     w = spec(name, 0, **over)
     pool, rows, max_pages = lease_pages(w, 0)
     bound = max(w["ctx"]) + w["steps"]
+    cb = ctx_bounds(w) if w["batch"] > 1 else None
     p = mk.mk_plan(mk.model_desc(w["model"]), w["ctx"], [v for r in rows for v in r], max_pages,
-                   bound, n_cu=n_cu, flags=flags)
+                   bound, n_cu=n_cu, flags=flags, ctx_bounds=cb)
     return w, pool, p, bound
 
 
@@ -190,7 +212,11 @@ def build_plan(name, n_cu=256, flags=0, **over):
                                              ("moe48_b1_8k", 256, 0), ("moe48_b1_256k", 256, 0),
                                              ("moe48_b1_256k", 256, mk.MK_PLAN_ATTN_QUEUE),
                                              ("tiny_dense", 16, mk.MK_PLAN_ATTN_QUEUE),
-                                             ("small_moe", 256, mk.MK_PLAN_ATTN_QUEUE)])
+                                             ("small_moe", 256, mk.MK_PLAN_ATTN_QUEUE),
+                                             ("tiny_dense_b3", 256, 0), ("tiny_dense_b3", 16, 0),
+                                             ("small_moe_b5", 256, 0), ("small_moe_b5", 40, 0),
+                                             ("small_moe_b32", 256, 0),
+                                             ("moe48_b32_ragged", 256, 0)])
 def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
     w, pool, p, bound = build_plan(name, n_cu, flags)
     try:
@@ -198,7 +224,7 @@ def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
         n_cu2, n_ctr, cu_off, tasks = decode_plan(img)
         assert n_cu2 == n_cu and mk.mk_plan_n_tasks(p) == len(tasks)
         got = plan_coverage(tasks, w["model"], bound)
-        want = O.work_sets(w["model"], [bound] * w["batch"])
+        want = O.work_sets(w["model"], ctx_bounds(w) if w["batch"] > 1 else [bound])
         assert set(got) == set(want)
         for k, items in got.items():
             assert len(items) == len(set(items)), f"{k}: covered more than once"
@@ -220,7 +246,7 @@ def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
         # at most one expert task per compute unit and layer (their down parts wait on each other)
         for cu in range(n_cu):
             lt = tasks[int(cu_off[cu]):int(cu_off[cu + 1])]
-            ex = lt["layer"][lt["op"] == OP_EXPERT]
+            ex = lt["layer"][(lt["op"] == OP_EXPERT) | (lt["op"] == OP_BEXP)]
             assert len(ex) == len(set(ex.tolist()))
         # with the queue asked for, attention splits come from a shared queue:
         # one queue task per compute unit and layer
