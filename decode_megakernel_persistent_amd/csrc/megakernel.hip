@@ -45,18 +45,20 @@ namespace dev {
 
 constexpr int LDS_VEC = dev_lds_vec();
 
-constexpr int STAGE_CHUNKS = 12;  // 1 KB wave chunks per wave in the staging area (96 KB)
+constexpr int STAGE_CHUNKS = 12;  // 1 KB wave chunks per wave in the shared area (96 KB)
+constexpr int DOWN_CHUNKS = 12;   // 16-byte chunks per lane of an expert task's down-projection tile
 
 struct Smem {
   float vec[LDS_VEC];  // gathered input vector(s), normalised in place
   union {
-    uint4 stage[NWAVE * STAGE_CHUNKS * 64];  // expert: down-projection rows (direct-to-LDS loads)
+    uint4 stage[NWAVE * STAGE_CHUNKS * 64];  // batch tasks: staged operands
     float att[NWAVE * STAGE_CHUNKS * 256];   // attention: per-wave partials; combine: split words
   };
   float out[2048];     // per-row dot products
   float res[2048];     // residual rows
   float red[64];       // block reductions
   float route_w[16];
+  float route_wn[16];  // routing weights as applied (renormalised when the model says so)
   int route_ids[16];
   int fail;
   uint32_t qnext;      // attention queue: the split this workgroup takes next
@@ -76,16 +78,28 @@ __device__ __forceinline__ void mark(Ctx& c, int i) {
   if (c.a.trace && tid() == 0) c.s.mk[i] = now();
 }
 
+// Order-preserving 64-bit rank key of router logit v of expert e: a larger
+// logit ranks first, and on equal logits the lower index. (The softmax is
+// monotone, so ranking logits ranks the probabilities.)
+__device__ __forceinline__ uint64_t logit_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFF - e);
+}
+
 // Gather tagged words into LDS: dst[i] = value of word i for i < n, where
 // word i sits at src1 + i for i < n1 and at src2 + (i - n1) after that; MAXW
 // words per thread per batch. which: 0 = routing wait, 1 = data wait (trace
-// slots), -1 = untraced. Uniform result.
+// slots), -1 = untraced. With nsq > 0 the sum of squares of words 0 .. nsq-1
+// is formed on the way (each thread over its words in order, then over the
+// wave) and wave w's part is left in s.red[w] for norm_pack. Uniform result.
 template <int MAXW>
 __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, const uint64_t* src2, int n,
-                                        float* dst, int which) {
+                                        float* dst, int which, int nsq = 0, uint64_t* keys = nullptr) {
   KAC& a = c.a;
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
   bool ok = true;
+  float ss = 0.f, mx = NEG_INF;
   for (int base = 0; base < n && ok; base += MAXW * NT) {
     const int t = tid();
     float v[MAXW];
@@ -98,8 +112,23 @@ __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, co
       for (int k = 0; k < MAXW; ++k) {
         const int i = base + t + k * NT;
         if (i < n) dst[i] = v[k];
+        if (i < nsq) ss = fmaf(v[k], v[k], ss);
+        if (keys && i >= n1 && i < n) {
+          keys[i - n1] = logit_key(v[k], i - n1);
+          mx = fmaxf(mx, v[k]);
+        }
       }
     }
+  }
+  if (nsq > 0) {
+    ss = wave_sum(ss);
+    if ((tid() & 63) == 0) c.s.red[tid() >> 6] = ss;
+  }
+  if (keys) {  // the second source holds router logits: rank keys and per-wave maxima
+    const int pad = ((n - n1 + 31) & ~31) - (n - n1);
+    if (tid() < pad) keys[n - n1 + tid()] = 0ull;
+    mx = wave_max_dpp(mx);
+    if ((tid() & 63) == 0) c.s.red[NWAVE + (tid() >> 6)] = mx;
   }
   if (!ok) c.s.fail = 1;
   lds_barrier();
@@ -107,8 +136,8 @@ __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, co
   return c.s.fail == 0;
 }
 template <int MAXW>
-__device__ __forceinline__ bool gather(Ctx& c, const uint64_t* src, int n, float* dst, int which) {
-  return gather2<MAXW>(c, src, n, src, n, dst, which);
+__device__ __forceinline__ bool gather(Ctx& c, const uint64_t* src, int n, float* dst, int which, int nsq = 0) {
+  return gather2<MAXW>(c, src, n, src, n, dst, which, nsq);
 }
 
 // Norm gains of chunk tid (elements 8*tid .. 8*tid+7) of a vector of K <=
@@ -134,6 +163,31 @@ __device__ __forceinline__ void pack_lds(Ctx& c, float* v, int K) {
     split8(x, hi, lo);
     *(uint4*)(v + 8 * ch) = hi;
     *(uint4*)(v + 8 * ch + 4) = lo;
+  }
+  lds_barrier();
+}
+
+// The second half of rmsnorm_pack, for a vector whose sum of squares the
+// gather already left in s.red (per wave): scale by the gains and pack.
+__device__ __forceinline__ void norm_pack(Ctx& c, float* v, int K, const Gains& gn) {
+  const int t = tid();
+  float x[8];
+  if (t < K / 8) {
+    *(float4*)x = *(const float4*)(v + 8 * t);
+    *(float4*)(x + 4) = *(const float4*)(v + 8 * t + 4);
+  }
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) tot += c.s.red[w];
+  const float rs = 1.0f / sqrtf(tot / (float)K + c.a.eps);
+  if (t < K / 8) {
+    const uint32_t gw[4] = {gn.g.x, gn.g.y, gn.g.z, gn.g.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * rs * ((e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1]));
+    uint4 hi, lo;
+    split8(x, hi, lo);
+    *(uint4*)(v + 8 * t) = hi;
+    *(uint4*)(v + 8 * t + 4) = lo;
   }
   lds_barrier();
 }
@@ -216,54 +270,6 @@ struct Tile {
   }
 };
 
-// A tile like Tile, but its 16-byte chunks go straight from global memory to
-// LDS (direct-to-LDS loads, no registers): wave w's chunk c of row slot r is
-// one 1 KB block at stage[((w * RPW + r) * CPL + c) * 64 + lane], written and
-// later read by the same lane. The caller waits for the loads (vmcnt) before
-// dots().
-template <int CPL, int RPW, int TC>
-struct StageTile {
-  static constexpr int G = NT / TC;
-  int nr, lg, tc, w;
-
-  template <class RowPtr>
-  __device__ __forceinline__ void issue(int R, const RowPtr& rowptr, uint4* stage) {
-    lg = tid() / TC;
-    tc = tid() % TC;
-    w = __builtin_amdgcn_readfirstlane(tid() >> 6);
-    nr = lg < R ? (R - lg + G - 1) / G : 0;
-    if (TC == 64) nr = __builtin_amdgcn_readfirstlane(nr);
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      if (r < nr) {
-        const uint4* p = rowptr(lg + r * G);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-          dma16(p + tc + c * TC, lds_addr(stage + ((w * RPW + r) * CPL + c) * 64));
-      }
-  }
-  __device__ __forceinline__ void dots(const uint4* stage, const float* u, float* out) {
-    const int lane = tid() & 63;
-    float acc[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const uint4* up = (const uint4*)(u + (tc + c * TC) * 8);
-      const uint4 uh = up[0], ul = up[1];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
-        if (r < nr) acc[r] = dot8h(stage[((w * RPW + r) * CPL + c) * 64 + lane], uh, ul, acc[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      if (r < nr) {
-        const float s = group_sum_last<TC>(acc[r]);
-        if (tc == TC - 1) out[lg + r * G] = s;
-      }
-  }
-};
-
 // Token id of sequence b, checked against the vocabulary.
 __device__ __forceinline__ int token_row(KAC& a, int b) {
   int tok = a.tok_in[b];
@@ -288,11 +294,18 @@ __device__ __forceinline__ bool layer_input(Ctx& c, int l, int b, float* dst) {
   KAC& a = c.a;
   if (l == 0) {
     const uint16_t* e = a.embed + (size_t)token_row(a, b) * a.H;
-    for (int i = tid(); i < a.H; i += NT) dst[i] = bf2f(e[i]);
+    float ss = 0.f;
+    for (int i = tid(); i < a.H; i += NT) {
+      const float v = bf2f(e[i]);
+      dst[i] = v;
+      ss = fmaf(v, v, ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid() & 63) == 0) c.s.red[tid() >> 6] = ss;
     lds_barrier();
     return true;
   }
-  return gather<4>(c, a.x + (size_t)(l - 1) * a.s_x + (size_t)b * a.H, a.H, dst, 1);
+  return gather<4>(c, a.x + (size_t)(l - 1) * a.s_x + (size_t)b * a.H, a.H, dst, 1, a.H);
 }
 
 // Residual value of row r entering layer l (read once the layer's inputs are known complete).
@@ -428,7 +441,7 @@ __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
   }
   if (!layer_input(c, l, 0, c.s.vec)) return false;
   mark(c, 0);
-  rmsnorm_pack(c, c.s.vec, H, gn);
+  norm_pack(c, c.s.vec, H, gn);
   mark(c, 1);
   tile.dots(c.s.vec, c.s.out);
   lds_barrier();
@@ -858,8 +871,8 @@ __device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
   tile.issue(n, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
   Gains gn;
   gn.load(a.ffn_norm + (size_t)l * H, H);
-  if (!gather<4>(c, a.xa + (size_t)l * a.s_x, H, c.s.vec, 1)) return false;
-  rmsnorm_pack(c, c.s.vec, H, gn);
+  if (!gather<4>(c, a.xa + (size_t)l * a.s_x, H, c.s.vec, 1, H)) return false;
+  norm_pack(c, c.s.vec, H, gn);
   tile.dots(c.s.vec, c.s.out);
   lds_barrier();
   for (int j = tid(); j < n; j += NT)
@@ -869,14 +882,15 @@ __device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
 
 // Expert task: route (every expert task computes the same top-k), stream the
 // gate/up rows of its slot's expert into registers, SwiGLU them against the
-// normalised hidden state and publish the activations; meanwhile the rows of
-// the down projection stream into LDS; then read every slot's activations and
-// finish its hidden rows: x = x_attn + sum_j w_j * W_down[e_j] a_j (fixed j
-// order). Dense FFN: one slot, expert 0, weight 1.
+// normalised hidden state and publish the activations; then request the rows
+// of the down projection (into the registers the gate/up rows held), read
+// every slot's activations behind them and finish its hidden rows:
+// x = x_attn + sum_j w_j * W_down[e_j] a_j (fixed j order). Dense FFN: one
+// slot, expert 0, weight 1.
 template <int CH, int TCH, int CF, int TCF>
 __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
   constexpr int RPW_G = GEMV_REG_CHUNKS / CH < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CH : GEMV_RPW_MAX;
-  constexpr int RPW_D = STAGE_CHUNKS / CF < GEMV_RPW_MAX ? STAGE_CHUNKS / CF : GEMV_RPW_MAX;
+  constexpr int RPW_D = DOWN_CHUNKS / CF < GEMV_RPW_MAX ? DOWN_CHUNKS / CF : GEMV_RPW_MAX;
   KAC& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, slot = t.aux, f0 = t.a1, nf = t.a2;
@@ -885,39 +899,96 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
   Gains gn;
   gn.load(a.ffn_norm + (size_t)l * H, H);
   const uint64_t* xa = a.xa + (size_t)l * a.s_x + (size_t)b * H;
-  // the router logits and the normalised hidden state in one batch: s.vec =
-  // [x_attn (H) | logits (E)]
+  // The router logits and the hidden state after attention in one batch:
+  // s.vec = [x_attn (H) | logits (E)]; the gather also leaves the rank keys of
+  // the logits, their per-wave maxima and the per-wave sums of squares of
+  // x_attn. Then every thread counts the keys ahead of part of the experts
+  // (rank = number of keys ahead), and the selection, the residual copy and the
+  // norm share the remaining barriers.
   float* lg_ = s.vec + H;
   if (!a.dense) {
-    if (!gather2<5>(c, xa, H, a.rlog + (size_t)l * a.s_rlog + (size_t)b * a.E, H + a.E, s.vec, 0))
+    const int E = a.E, E32 = (E + 31) & ~31;
+    uint64_t* keys = (uint64_t*)(s.out + 1024);  // [E32] (padding keys 0 rank below all)
+    int* partial = (int*)(s.out + 512);          // [parts][E32] (parts * E32 <= 512)
+    if (!gather2<5>(c, xa, H, a.rlog + (size_t)l * a.s_rlog + (size_t)b * E, H + E, s.vec, 0, H, keys))
       return false;
-    route(c, lg_);
-    if ((t.flags & TF_WRITE_TOPK) && tid() < a.K) {
-      if (a.topk_ids) a.topk_ids[(size_t)l * a.K + tid()] = s.route_ids[tid()];
-      if (a.topk_w) a.topk_w[(size_t)l * a.K + tid()] = s.route_w[tid()] / route_div(a, s);
+    const int parts = E32 <= 128 ? 4 : 2;
+    const int chunk = E32 / parts;  // a multiple of 8
+    {
+      const int te = tid() % E32, part = tid() / E32;
+      if (part < parts) {
+        const uint64_t mine = keys[te];
+        int cnt = 0;
+#pragma unroll 2
+        for (int e = part * chunk; e < (part + 1) * chunk; e += 8) {
+          uint4 q[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = *(const uint4*)(keys + e + 2 * i);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            cnt += ((((uint64_t)q[i].y << 32) | q[i].x) > mine) ? 1 : 0;
+            cnt += ((((uint64_t)q[i].w << 32) | q[i].z) > mine) ? 1 : 0;
+          }
+        }
+        partial[part * E32 + te] = cnt;
+      }
+    }
+    for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
+    lds_barrier();
+    if (tid() < E) {
+      int rank = 0;
+      for (int q = 0; q < parts; ++q) rank += partial[q * E32 + tid()];
+      if (rank < a.K) {
+        float M = NEG_INF;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.red[NWAVE + w]);
+        s.route_ids[rank] = tid();
+        s.route_w[rank] = expf(lg_[tid()] - M);  // softmax numerator (see below)
+      }
+    }
+    norm_pack(c, s.vec, H, gn);  // its barrier also publishes the selection
+    if (tid() < a.K) {
+      // weights: softmax over the selection (renormalised), or the probability
+      // of each selected expert (a sum over every expert, off the critical path)
+      float div = 0.f;
+      if (a.norm_topk) {
+        for (int i = 0; i < a.K; ++i) div += s.route_w[i];
+      } else {
+        float M = NEG_INF;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.red[NWAVE + w]);
+        for (int e = 0; e < E; ++e) div += expf(lg_[e] - M);
+      }
+      const float wn = s.route_w[tid()] / div;
+      s.route_wn[tid()] = wn;  // read after later barriers
+      if (t.flags & TF_WRITE_TOPK) {
+        if (a.topk_ids) a.topk_ids[(size_t)l * a.K + tid()] = s.route_ids[tid()];
+        if (a.topk_w) a.topk_w[(size_t)l * a.K + tid()] = wn;
+      }
     }
   } else {
     if (tid() == 0) {
       s.route_ids[0] = 0;
       s.route_w[0] = 1.f;
+      s.route_wn[0] = 1.f;
     }
-    if (!gather<4>(c, xa, H, s.vec, 0)) return false;
+    if (!gather<4>(c, xa, H, s.vec, 0, H)) return false;
+    for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
+    norm_pack(c, s.vec, H, gn);
   }
   mark(c, 0);
-  for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
-  rmsnorm_pack(c, s.vec, H, gn);  // before the weight loads: the gains are not waited behind them
   const int e = s.route_ids[slot];
   const uint16_t* Wg = a.gate + ((size_t)l * EE + e) * F * H;
   const uint16_t* Wu = a.up + ((size_t)l * EE + e) * F * H;
   const uint16_t* Wd = a.down + (size_t)l * EE * H * F;
   const int capg = (NT / TCH) * RPW_G / 2;   // FFN rows per register tile
   const int capd = (NT / TCF) * RPW_D / KK;  // hidden rows per staged tile
-  // The gate/up rows stream into registers; the down rows are requested into
-  // LDS only once the gate/up rows are consumed (a wave's loads complete in
-  // issue order, so down rows issued earlier would hold up the gate/up dots),
-  // and they stream while the activations of the other expert tasks arrive.
+  // The gate/up rows stream into registers; the down rows are requested once
+  // the gate/up rows are consumed (a wave's loads complete in issue order, so
+  // down rows issued earlier would hold up the gate/up dots), and they stream
+  // while the activations of the other expert tasks arrive.
   Tile<CH, RPW_G, TCH> gu;
-  StageTile<CF, RPW_D, TCF> dn;
+  Tile<CF, RPW_D, TCF> dn;
   mark(c, 1);
   for (int fc = 0; fc < nf; fc += capg) {
     const int nfc = min(capg, nf - fc);
@@ -942,26 +1013,18 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
     const int nrc = min(capd, nr - rc);
     dn.issue(nrc * KK, [&](int j) {
         return (const uint4*)(Wd + ((size_t)s.route_ids[j % KK] * H + r0 + rc + j / KK) * F);
-      }, s.stage);
+      });
     if (rc == 0) {
       if (!gather<12>(c, a.act + (size_t)l * a.s_act + (size_t)b * KK * F, KK * F, s.vec, 1)) return false;
       pack_lds(c, s.vec, KK * F);
     }
     mark(c, 5);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct-to-LDS loads
-    mark(c, 6);
-    dn.dots(s.stage, s.vec + (size_t)(dn.lg % KK) * F, s.out);
+    dn.dots(s.vec + (size_t)(dn.lg % KK) * F, s.out);
     lds_barrier();
     mark(c, 7);
-    const float div = route_div(a, s);
-    float wj[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) wj[j] = j < KK ? s.route_w[j] / div : 0.f;
     for (int q = tid(); q < nrc; q += NT) {
       float y = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < KK) y += wj[j] * s.out[q * KK + j];
+      for (int j = 0; j < KK; ++j) y += s.route_wn[j] * s.out[q * KK + j];
       st_tagged(a.x + (size_t)l * a.s_x + (size_t)b * H + r0 + rc + q, s.res[rc + q] + y, a.epoch);
     }
     lds_barrier();
@@ -997,8 +1060,8 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
   issue(Bf, 1);
   Gains gn;
   gn.load(a.final_norm, H);
-  if (!gather<4>(c, a.x + (size_t)(a.L - 1) * a.s_x, H, s.vec, 1)) return false;
-  rmsnorm_pack(c, s.vec, H, gn);
+  if (!gather<4>(c, a.x + (size_t)(a.L - 1) * a.s_x, H, s.vec, 1, H)) return false;
+  norm_pack(c, s.vec, H, gn);
   uint4 uh[CPL], ul[CPL];
 #pragma unroll
   for (int cc = 0; cc < CPL; ++cc) {
