@@ -38,6 +38,7 @@ def parse():
                     help="oracle steps in the CPU baseline sample (0: skip)")
     ap.add_argument("--n-cu", type=int, default=0)
     ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--plan-flags", type=int, default=0, help="MK_PLAN_* bits")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM counter bytes per launch measured by rocprofv3 --pmc")
     return ap.parse_args()
@@ -67,7 +68,8 @@ def main():
     K = m["top_k"] if moe else 1
     print(f"[bench] setting up {a.workload}: B={B} ctx={w['ctx'] if B <= 4 else '...'} "
           f"steps={a.steps} warmup={a.warmup}", file=sys.stderr, flush=True)
-    dec, pool, W = gpu_session(w, a.seed, device=dev, n_cu=a.n_cu, attn_split_pages=a.split_pages)
+    dec, pool, W = gpu_session(w, a.seed, device=dev, n_cu=a.n_cu, attn_split_pages=a.split_pages,
+                               plan_flags=a.plan_flags)
     ctx0 = torch.tensor(w["ctx"], dtype=torch.int32, device=dev)
     tok0 = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
     toks = [tok0.clone(), torch.empty(B, dtype=torch.int32, device=dev)]

@@ -162,6 +162,7 @@ def mk_step_bytes(desc, seq_lens, distinct=None):
 
 MK_PLAN_ATTN_QUEUE = 1
 MK_PLAN_NO_ATTN_QUEUE = 2
+MK_PLAN_SPLIT_UNITS = 4
 
 
 def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0, flags=0,

@@ -638,15 +638,14 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     float sa[4], sb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float xa = (SA[j] + __shfl_xor(SA[j], 8, 64)) * scale;
-      const float xb = (SB[j] + __shfl_xor(SB[j], 8, 64)) * scale;
+      const float xa = xor8_sum(SA[j]) * scale;
+      const float xb = xor8_sum(SB[j]) * scale;
       sa[j] = (pgA * 16 + 4 * kq + j) < n_tok ? xa : NEG_INF;
       sb[j] = (pgB * 16 + 4 * kq + j) < n_tok ? xb : NEG_INF;
     }
     float mx = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
                      fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor32_max(xor16_max(mx));
     const float mn = fmaxf(m_run, mx);
     const float alpha = mn == NEG_INF ? 1.f : expf(m_run - mn);
     float qa[4], qb[4];
@@ -656,8 +655,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       qb[j] = sb[j] == NEG_INF ? 0.f : expf(sb[j] - mn);
     }
     float ps = ((qa[0] + qa[1]) + (qa[2] + qa[3])) + ((qb[0] + qb[1]) + (qb[2] + qb[3]));
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = xor32_sum(xor16_sum(ps));
     l_run = l_run * alpha + ps;
     m_run = mn;
     v4s PA, PB;
@@ -667,9 +665,15 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       PA[j] = (short)(lo_part ? f2bf(qa[j] - bf2f(ha)) : ha);
       PB[j] = (short)(lo_part ? f2bf(qb[j] - bf2f(hb)) : hb);
     }
+    // the scale of output row 4 kq + j, i.e. of head (4 kq + j) & 7, whose
+    // alpha every lane with r16 & 7 == head holds (lane head, for one)
     float aj[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, (4 * kq + j) & 7, 64);
+    for (int j = 0; j < 4; ++j) {
+      const float lo4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j));
+      const float hi4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 + j));
+      aj[j] = (kq & 1) ? hi4 : lo4;
+    }
     uint32_t mla, mha, mlb, mhb;
     vmask(pgA, mla, mha);
     vmask(pgB, mlb, mhb);
@@ -710,7 +714,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float o = acc[nb][j] + __shfl_xor(acc[nb][j], 32, 64);
+      const float o = xor32_sum(acc[nb][j]);
       const int head = 4 * kq + j;
       if (kq < 2 && head < HG) Ow[(w * HG + head) * D + nb * 16 + r16] = o;
     }
@@ -795,28 +799,27 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   lds_barrier();
   if (a.trace && tid() == 0) s.tw[3] = now();
   if (s.fail) return false;
-  float* cs = s.out;  // [S] merge weights
-  if (tid() < 64) {
-    const int lane = tid();
-    float M = NEG_INF;
-    for (int q = lane; q < S; q += 64) M = fmaxf(M, sw[q * W + nd]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int q = lane; q < S; q += 64) {
-      const float mq = sw[q * W + nd];
-      L += mq == NEG_INF ? 0.f : expf(mq - M) * sw[q * W + nd + 1];
-    }
-    L = wave_sum(L);
-    for (int q = lane; q < S; q += 64) {
-      const float mq = sw[q * W + nd];
-      cs[q] = (mq == NEG_INF || L == 0.f) ? 0.f : expf(mq - M) / L;
-    }
+  // every wave forms the global max M = max_q m_q and the denominator
+  // L = sum_q exp(m_q - M) l_q on its own (split q in lane q, q + 64, ...), so
+  // the merge needs no barrier before the weighted sums; thread (sg, dim) then
+  // sums exp(m_q - M) o_q[dim] over its splits q = sg, sg + NG, ...
+  const int lane = tid() & 63;
+  float M = NEG_INF;
+  for (int q = lane; q < S; q += 64) M = fmaxf(M, sw[q * W + nd]);
+  M = wave_max_dpp(M);
+  float L = 0.f;
+  for (int q = lane; q < S; q += 64) {
+    const float mq = sw[q * W + nd];
+    L += mq == NEG_INF ? 0.f : expf(mq - M) * sw[q * W + nd + 1];
   }
-  lds_barrier();
+  L = wave_sum(L);
   const int NG = NT / nd, sg = tid() / nd, dim = tid() % nd;
   float acc = 0.f;
   if (sg < NG)
-    for (int q = sg; q < S; q += NG) acc += cs[q] * sw[q * W + dim];
+    for (int q = sg; q < S; q += NG) {
+      const float mq = sw[q * W + nd];
+      acc += mq == NEG_INF ? 0.f : expf(mq - M) * sw[q * W + dim];
+    }
   float* red = s.out + 1024;
   if (sg < NG) red[sg * nd + dim] = acc;
   lds_barrier();
@@ -824,6 +827,7 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
     float o = 0.f;
 #pragma unroll 16
     for (int q = 0; q < NG; ++q) o += red[q * nd + tid()];
+    o = L > 0.f ? o / L : 0.f;
     st_tagged(a.o + (size_t)l * a.s_o + ((size_t)b * a.Hq + h) * D + d0 + tid(), o, a.epoch);
   }
   return true;

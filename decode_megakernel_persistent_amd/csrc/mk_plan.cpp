@@ -370,6 +370,9 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   int pps = o && o->attn_split_pages > 0 ? o->attn_split_pages : (pg_total + n_cu - 1) / n_cu;
   const bool queue = !(flags & MK_PLAN_NO_ATTN_QUEUE) && B == 1 && (flags & MK_PLAN_ATTN_QUEUE);
   if (queue) pps = mk::QUEUE_PAGES;
+  // QKV tiles on one half of the units, attention splits on the other half
+  const bool split_units = !batch && !queue && (flags & MK_PLAN_SPLIT_UNITS) && n_cu >= 2 * Hkv;
+  if (split_units && !(o && o->attn_split_pages > 0)) pps = (pg_total + n_cu / 2 - 1) / (n_cu / 2);
   // a batch: about four splits per unit, so that ragged lengths even out
   if (batch && !(o && o->attn_split_pages > 0)) pps = std::max(8, ceil_div(pg_total, 4 * n_cu));
   p->attn_queue = queue;
@@ -431,7 +434,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     // QKV: tiles of rotary pairs within one kv group
     {
       std::vector<Task> st;
-      int per_g = std::max(1, n_cu / Hkv);
+      int per_g = std::max(1, (split_units ? n_cu / 2 : n_cu) / Hkv);
       const int cap_pairs = std::max(1, rows_max(H) / 2);
       per_g = std::max(per_g, ceil_div(p->n_pairs_g, cap_pairs));
       for (int g = 0; g < Hkv; ++g)

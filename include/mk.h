@@ -103,6 +103,11 @@ typedef struct mk_plan_opts {
  * instead of one static split per task. Off unless asked for. */
 #define MK_PLAN_ATTN_QUEUE 1     /* use the queue (batch 1) */
 #define MK_PLAN_NO_ATTN_QUEUE 2  /* never use it */
+/* Batch 1, static splits: the QKV tiles of a layer go to one half of the
+ * compute units and its attention splits to the other half, so that the
+ * attention units request their KV pages while the QKV units stream weights
+ * and compute, instead of after them. */
+#define MK_PLAN_SPLIT_UNITS 4
 
 typedef struct mk_plan mk_plan_t;   /* opaque host object */
 typedef struct mk_pool mk_pool_t;   /* opaque host object */
