@@ -61,6 +61,8 @@ struct Smem {
   float route_wn[16];  // routing weights as applied (renormalised when the model says so)
   int route_ids[16];
   int fail;
+  int kv_ti;                 // task index of the attention split whose pages are staged (-1: none)
+  int kv_ok[NWAVE];          // wave w's staged page is valid
   uint32_t qnext;      // attention queue: the split this workgroup takes next
   uint64_t tw[4];      // trace: (begin, end) of the routing wait and of the data wait
   uint64_t mk[TRACE_MARKS];  // trace: body-specific marks
@@ -481,6 +483,44 @@ __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
   return true;
 }
 
+// Staged attention pages: wave w's page block (one (page, layer, kv head)
+// block of 2 x 16 x D bf16, in pool order) at the end of the shared area,
+// after the attention's per-wave partials.
+template <int D>
+__device__ __forceinline__ uint4* staged_page(Smem& s, int w) {
+  return s.stage + (NWAVE * 8 * D * 4) / 16 + w * (4 * D);
+}
+static_assert(NWAVE * 8 * 128 * 4 + STAGE_PAGES * 4 * 128 * 16 <= NWAVE * STAGE_CHUNKS * 64 * 16,
+              "staged pages and attention partials share the staging area");
+
+// Request the first pages of this unit's next attention split ta (task index
+// ti_a of this unit's list) into LDS, wave w taking page w, with direct-to-LDS
+// loads: at the start of the unit's expert task, while it waits for the
+// routing decision and HBM is otherwise idle, so that the split computes from
+// LDS as soon as its queries arrive. The split's own wave w waits for the
+// transfer (vmcnt).
+template <int D>
+__device__ __forceinline__ void stage_kv(Ctx& c, const Task& ta, uint32_t ti_a) {
+  KAC& a = c.a;
+  Smem& s = c.s;
+  const int w = tid() >> 6, lane = tid() & 63;
+  const int b = ta.a0, g = ta.a1, pg0 = ta.a2, npg = ta.a3, l = ta.layer;
+  bool ok = false;
+  if (w < min(npg, STAGE_PAGES)) {
+    const int32_t phys = a.page_table[(size_t)b * a.max_pages + pg0 + w];
+    ok = phys >= 0 && phys < a.n_pages;
+    if (ok) {
+      const uint4* src = (const uint4*)(a.pool + (size_t)phys * a.page_stride + (size_t)l * a.layer_stride +
+                                        (size_t)g * 2 * 16 * D) + lane;
+      uint4* dst = staged_page<D>(s, w);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) dma16(src + 64 * i, lds_addr(dst + 64 * i));
+    }
+  }
+  if (lane == 0) s.kv_ok[w] = ok ? 1 : 0;
+  if (tid() == 0) s.kv_ti = (int)ti_a;
+}
+
 template <int D>
 __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   constexpr int NK4 = D / 32;   // 16-byte K loads per lane per page
@@ -539,9 +579,24 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       vv[2 * m + 1] = make_uint2(v.z, v.w);
     }
   };
+  // this wave's first page may have been staged in LDS by an earlier task of
+  // this unit (stage_kv); the wait covers the transfer, issued two tasks ago
+  const bool staged = cnt > 0 && s.kv_ti == (int)c.ti && s.kv_ok[w];
+  if (staged) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint4* sp = staged_page<D>(s, w) + lane;
+#pragma unroll
+    for (int i = 0; i < NK4; ++i) kb[0][i] = sp[64 * i];
+#pragma unroll
+    for (int m = 0; m < NB / 2; ++m) {
+      const uint4 v = sp[2 * D + 64 * m];
+      vb[0][2 * m] = make_uint2(v.x, v.y);
+      vb[0][2 * m + 1] = make_uint2(v.z, v.w);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NBUF; ++j)
-    if (j < cnt) load(kb[j], vb[j], first + j * NWAVE, ph[j]);
+    if (j < cnt && !(j == 0 && staged)) load(kb[j], vb[j], first + j * NWAVE, ph[j]);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     if (tid() + j * NT < npg) pid[tid() + j * NT] = tbl[j];
@@ -1785,7 +1840,10 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
   const uint32_t* off = hdr + PLAN_HDR_WORDS;
   const Task* tasks = (const Task*)((const char*)hdr + hdr[H_TASK_OFF_BYTES]);
   const uint32_t beg = off[blockIdx.x], end = off[blockIdx.x + 1];
-  if (tid() == 0) s.fail = 0;
+  if (tid() == 0) {
+    s.fail = 0;
+    s.kv_ti = -1;
+  }
   lds_barrier();
   for (uint32_t ti = beg; ti < end; ++ti) {
     // an opaque copy of the argument pointer per task: fields are loaded where
@@ -1800,6 +1858,13 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
       for (int i = 0; i < TRACE_MARKS; ++i) s.mk[i] = 0;
     }
     bool ok = true;
+    if (t.flags & TF_STAGE_KV) {
+      // the first attention task further on in this unit's list (the planner
+      // checked that there is one within STAGE_SCAN tasks)
+      uint32_t ta = ti + 1;
+      while (ta < end && ta <= ti + STAGE_SCAN && tasks[ta].op != OP_ATTN) ++ta;
+      if (ta < end && ta <= ti + STAGE_SCAN) stage_kv<HD>(c, tasks[ta], ta);
+    }
     switch (t.op) {
       case OP_ATTN: {
         // One split, or splits from the shared queue: every pull adds one to

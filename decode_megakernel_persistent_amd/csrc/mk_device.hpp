@@ -52,6 +52,19 @@ __device__ __forceinline__ uint2 ld_nt2(const uint2* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Direct-to-LDS load of 16 bytes per lane: lane i's 16 bytes from g land at
+// LDS byte address lds_base + 16 * i (lds_base wave-uniform). Written as
+// inline assembly so that the compiler does not treat every later LDS read
+// as possibly aliasing the transfer (it would wait for all outstanding
+// vector memory operations before each one); the consumer waits for the
+// transfer itself (s_waitcnt vmcnt) before reading its destination.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }

@@ -47,7 +47,14 @@ enum Op : uint8_t {
   OP_COUNT = 18
 };
 
-enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2 };
+// TF_STAGE_KV: before its body the task requests the first pages of this
+// unit's next attention split (the first attention task at most STAGE_SCAN
+// tasks further on in the same list) into LDS.
+enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4 };
+
+// Attention pages staged ahead of their split: one per wave.
+constexpr int STAGE_PAGES = 8;
+constexpr int STAGE_SCAN = 8;
 
 // Pages per attention split when long contexts use the shared split queue.
 constexpr int QUEUE_PAGES = 64;

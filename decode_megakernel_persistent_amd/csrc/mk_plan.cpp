@@ -618,6 +618,20 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     }
     cursor = (cursor + (int)stages[s0].size()) % n_cu;
   }
+  // batch 1, static splits: a unit's expert task of layer l first stages the
+  // first pages of the unit's next attention split (of layer l + 1, at most
+  // STAGE_SCAN tasks further on) into LDS (TF_STAGE_KV)
+  if (!batch && !queue) {
+    for (auto& lst : p->lists)
+      for (size_t i = 0; i < lst.size(); ++i) {
+        if (lst[i].op != mk::OP_EXPERT) continue;
+        for (size_t j = i + 1; j < lst.size() && j <= i + mk::STAGE_SCAN; ++j)
+          if (lst[j].op == mk::OP_ATTN) {
+            if (lst[j].layer == lst[i].layer + 1) lst[i].flags |= mk::TF_STAGE_KV;
+            break;
+          }
+      }
+  }
   p->stage_of_task.clear();
   for (int cu = 0; cu < n_cu; ++cu)
     for (int s0 : stage_lists[cu]) p->stage_of_task.push_back(s0);
