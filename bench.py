@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--n-cu", type=int, default=0)
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--plan-flags", type=int, default=0, help="MK_PLAN_* bits")
+    ap.add_argument("--batch32-steps", type=int, default=64,
+                    help="timed steps of the batch-32 leg (48-layer MoE at 8K only; 0: skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM counter bytes per launch measured by rocprofv3 --pmc")
     return ap.parse_args()
@@ -52,7 +54,6 @@ def main():
         sys.exit(2)
     import torch
     import decode_megakernel_persistent_amd as mk
-    from fixtures.session import gpu_session, spec
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -60,62 +61,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     copy_gbs = stream_copy_probe(torch, mk, dev)
-    total_steps = a.warmup + a.steps
-    w = spec(a.workload, a.seed, steps=total_steps)
-    m, B = w["model"], w["batch"]
-    L = m["n_layers"]
-    moe = m["n_experts"] > 0
-    K = m["top_k"] if moe else 1
-    print(f"[bench] setting up {a.workload}: B={B} ctx={w['ctx'] if B <= 4 else '...'} "
-          f"steps={a.steps} warmup={a.warmup}", file=sys.stderr, flush=True)
-    dec, pool, W = gpu_session(w, a.seed, device=dev, n_cu=a.n_cu, attn_split_pages=a.split_pages,
-                               plan_flags=a.plan_flags)
-    ctx0 = torch.tensor(w["ctx"], dtype=torch.int32, device=dev)
-    tok0 = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
-    toks = [tok0.clone(), torch.empty(B, dtype=torch.int32, device=dev)]
-    ids = torch.full((a.steps, L, B, K), -1, dtype=torch.int32, device=dev)
-
-    # warm-up, then restore the pre-warm-up state (lengths and first tokens)
-    for s in range(a.warmup):
-        dec.step(toks[s % 2], toks[(s + 1) % 2])
-    torch.cuda.synchronize()
-    dec.check_status()
-    dec.seq_lens.copy_(ctx0)
-    toks[0].copy_(tok0)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for s in range(a.steps):
-        ti, to = toks[s % 2], toks[(s + 1) % 2]
-        dec.step(ti, to, topk_ids=ids[s] if moe else None)
-        ev[s + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dec.check_status()
-    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(a.steps)]
-    ms_total = ev[0].elapsed_time(ev[a.steps])
-    ms_step = ms_total / a.steps
-
-    # algorithmic bytes: weights read (distinct experts per layer from the step's
-    # own top-k ids) + KV read (every cached token incl. the new one) + KV written
-    ids_h = ids.cpu() if moe else None
-    desc = mk.model_desc(m)
-    tot_bytes = 0.0
-    wsum = ksum = 0.0
-    for s in range(a.steps):
-        lens = [c + s for c in w["ctx"]]
-        distinct = [len(set(ids_h[s, l].reshape(-1).tolist())) for l in range(L)] if moe else None
-        wb, kr, kw = mk.mk_step_bytes(desc, lens, distinct)
-        tot_bytes += wb + kr + kw
-        wsum += wb
-        ksum += kr + kw
-    bytes_step = tot_bytes / a.steps
-    achieved_gbs = tot_bytes / (ms_total * 1e-3) / 1e9
-    tok_s = B * a.steps / (ms_total * 1e-3)
-    sol_tok_s = B * HBM_PEAK_GBS * 1e9 / bytes_step
+    r = run_workload(torch, mk, dev, a.workload, a.steps, a.warmup, a)
+    w, dec, pool, W, tok0 = r.pop("w"), r.pop("dec"), r.pop("pool"), r.pop("weights"), r.pop("tok0")
+    m, B, L = w["model"], w["batch"], w["model"]["n_layers"]
+    tok_s, ms_step, per, wall = r["tok_s"], r["ms_step"], r["per"], r["wall"]
+    bytes_step, wsum, ksum = r["bytes_step"], r["wsum"], r["ksum"]
+    achieved_gbs, sol_tok_s = r["achieved_gbs"], r["sol_tok_s"]
+    plan_n_cu, plan_tasks = mk.mk_plan_n_cu(dec.plan), mk.mk_plan_n_tasks(dec.plan)
 
     traffic = None
     if os.path.exists(a.traffic_json):
@@ -130,6 +82,26 @@ def main():
     cpu = None
     if a.cpu_steps > 0:
         cpu = cpu_baseline(w, a, dec, tok0)
+
+    # the metric's second number: the same model at batch 32 (ragged contexts,
+    # one shared pool), with the weights already resident
+    b32 = None
+    if a.batch32_steps > 0 and a.workload == "moe48_b1_8k":
+        mk.mk_pool_free(pool)
+        dec.close()
+        del dec
+        torch.cuda.empty_cache()
+        r32 = run_workload(torch, mk, dev, "moe48_b32_ragged", a.batch32_steps, 2, a, weights=W)
+        mk.mk_pool_free(r32["pool"])
+        r32["dec"].close()
+        pool = dec = None
+        b32 = {"workload": "moe48_b32_ragged", "steps": a.batch32_steps, "warmup": 2,
+               "value": round(r32["tok_s"], 2), "unit": "tok/s",
+               "ms_per_step": round(r32["ms_step"], 4),
+               "context": [min(r32["w"]["ctx"]), max(r32["w"]["ctx"])],
+               "bytes_per_step": r32["bytes_step"],
+               "achieved_gbs": round(r32["achieved_gbs"], 1),
+               "frac": round(r32["achieved_gbs"] / HBM_PEAK_GBS, 4)}
 
     out = {
         "metric": METRIC,
@@ -148,11 +120,11 @@ def main():
                    "context": w["ctx"] if B == 1 else [min(w["ctx"]), max(w["ctx"])],
                    "layers": L, "hidden": m["hidden"], "experts": m["n_experts"],
                    "top_k": m["top_k"], "vocab": m["vocab"], "page_tokens": m["page_tokens"],
-                   "n_cu": mk.mk_plan_n_cu(dec.plan), "tasks": mk.mk_plan_n_tasks(dec.plan)},
+                   "n_cu": plan_n_cu, "tasks": plan_tasks},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
-        "bytes_per_step": {"weights": wsum / a.steps, "kv": ksum / a.steps, "total": bytes_step},
+        "bytes_per_step": {"weights": wsum, "kv": ksum, "total": bytes_step},
         "stream_copy": {"gbs": round(copy_gbs, 1), "bytes_per_launch": 2 * COPY_BYTES,
                         "frac_of_copy": round(achieved_gbs / copy_gbs, 4)},
         "sol_tok_s": round(sol_tok_s, 1),
@@ -162,10 +134,73 @@ def main():
                     "p90": round(sorted(per)[(9 * len(per)) // 10], 4)},
         "host_wall_s": round(wall, 3),
         "cpu_baseline": cpu,
+        "batch32": b32,
     }
     print(json.dumps(out), flush=True)
-    mk.mk_pool_free(pool)
-    dec.close()
+    if dec is not None:
+        mk.mk_pool_free(pool)
+        dec.close()
+
+
+def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
+    """Set up workload `name`, run `warmup` steps, restore the starting state,
+    time `steps` greedy steps with HIP events on the launch stream, and count
+    the algorithmic bytes of every timed step (weights actually read, from
+    the step's own top-k ids, plus KV read and written)."""
+    from fixtures.session import gpu_session, spec
+    w = spec(name, a.seed, steps=warmup + steps)
+    m, B = w["model"], w["batch"]
+    L = m["n_layers"]
+    moe = m["n_experts"] > 0
+    K = m["top_k"] if moe else 1
+    print(f"[bench] setting up {name}: B={B} ctx={w['ctx'] if B <= 4 else '...'} "
+          f"steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+    dec, pool, W = gpu_session(w, a.seed, device=dev, n_cu=a.n_cu, attn_split_pages=a.split_pages,
+                               plan_flags=a.plan_flags, weights=weights)
+    ctx0 = torch.tensor(w["ctx"], dtype=torch.int32, device=dev)
+    tok0 = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
+    toks = [tok0.clone(), torch.empty(B, dtype=torch.int32, device=dev)]
+    ids = torch.full((steps, L, B, K), -1, dtype=torch.int32, device=dev)
+
+    # warm-up, then restore the pre-warm-up state (lengths and first tokens)
+    for s in range(warmup):
+        dec.step(toks[s % 2], toks[(s + 1) % 2])
+    torch.cuda.synchronize()
+    dec.check_status()
+    dec.seq_lens.copy_(ctx0)
+    toks[0].copy_(tok0)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(steps):
+        ti, to = toks[s % 2], toks[(s + 1) % 2]
+        dec.step(ti, to, topk_ids=ids[s] if moe else None)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec.check_status()
+    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(steps)]
+    ms_total = ev[0].elapsed_time(ev[steps])
+
+    ids_h = ids.cpu() if moe else None
+    desc = mk.model_desc(m)
+    tot_bytes = wsum = ksum = 0.0
+    for s in range(steps):
+        lens = [c + s for c in w["ctx"]]
+        distinct = [len(set(ids_h[s, l].reshape(-1).tolist())) for l in range(L)] if moe else None
+        wb, kr, kw = mk.mk_step_bytes(desc, lens, distinct)
+        tot_bytes += wb + kr + kw
+        wsum += wb
+        ksum += kr + kw
+    bytes_step = tot_bytes / steps
+    return {"w": w, "dec": dec, "pool": pool, "weights": W, "tok0": tok0,
+            "tok_s": B * steps / (ms_total * 1e-3), "ms_step": ms_total / steps, "per": per,
+            "wall": wall, "bytes_step": bytes_step, "wsum": wsum / steps, "ksum": ksum / steps,
+            "achieved_gbs": tot_bytes / (ms_total * 1e-3) / 1e9,
+            "sol_tok_s": B * HBM_PEAK_GBS * 1e9 / bytes_step}
 
 
 def stream_copy_probe(torch, mk, dev, reps=5):
