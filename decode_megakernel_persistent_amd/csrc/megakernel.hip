@@ -1483,27 +1483,6 @@ __device__ __forceinline__ bool task_bqkv(Ctx& c, const Task& t) {
   return true;
 }
 
-// W_o rows for every sequence, plus the residual (the layer's input).
-__device__ __forceinline__ bool task_bo(Ctx& c, const Task& t) {
-  KAC& a = c.a;
-  const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H, K = a.Hq * a.D, B = a.B;
-  const uint16_t* W = a.wo + (size_t)l * H * K;
-  MtSrc src{a.o + (size_t)l * a.s_o, K, nullptr, false};
-  if (a.trace && tid() == 0) c.s.tw[2] = now();
-  if (!mt_tile(c, n, K, [&](int j) { return W + (size_t)(r0 + j) * K; }, src)) return false;
-  if (a.trace && tid() == 0) c.s.tw[3] = now();
-  const MtLds& P = *(const MtLds*)&c.s;
-  bool fail = false;
-  for (int idx = tid(); idx < n * B && !fail; idx += NT) {
-    const int r = idx / B, b = idx - r * B;
-    const float x = resid(c, l, b, r0 + r, &fail);
-    st_tagged(a.xa + (size_t)l * a.s_x + (size_t)b * H + r0 + r, x + P.out[r][b], a.epoch);
-  }
-  if (fail) c.s.fail = 1;
-  lds_barrier();
-  return c.s.fail == 0;
-}
-
 // Gather n tagged words, word i at addr(i), into dst[i] (LDS); uniform result.
 template <int MAXW, class Addr>
 __device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float* dst, int which) {
@@ -1529,6 +1508,50 @@ __device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float
   lds_barrier();
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
   return c.s.fail == 0;
+}
+
+// W_o rows of every sequence over reduction block kb (a0) of the a3 blocks
+// of the attention output: blocks 1 .. a3-1 publish partial sums (OPART);
+// block 0 adds them in block order to its own and adds the residual (the
+// layer's input), which it gathers together with them in one batch.
+__device__ __forceinline__ bool task_bo(Ctx& c, const Task& t) {
+  KAC& a = c.a;
+  const int l = t.layer, kb = t.a0, r0 = t.a1, n = t.a2, KB = t.a3 > 0 ? t.a3 : 1;
+  const int H = a.H, K = a.Hq * a.D, B = a.B, Kb = K / KB, k0 = kb * Kb;
+  const uint16_t* W = a.wo + (size_t)l * H * K + k0;
+  MtSrc src{a.o + (size_t)l * a.s_o + k0, K, nullptr, false};
+  if (a.trace && tid() == 0) c.s.tw[2] = now();
+  if (!mt_tile(c, n, Kb, [&](int j) { return W + (size_t)(r0 + j) * K; }, src)) return false;
+  if (a.trace && tid() == 0) c.s.tw[3] = now();
+  MtLds& P = *(MtLds*)&c.s;
+  if (kb > 0) {
+    uint64_t* dst = a.opart + (size_t)l * a.s_opart + (size_t)(kb - 1) * B * H;
+    for (int idx = tid(); idx < n * B; idx += NT) {
+      const int r = idx / B, b = idx - r * B;
+      st_tagged(dst + (size_t)b * H + r0 + r, P.out[r][b], a.epoch);
+    }
+    return true;
+  }
+  // word (q, b, r) at red[(q * B + b) * n + r]: q = 0 the residual (layer > 0),
+  // q >= 1 the partial of block q; the tile's panel area is free by now
+  float* red = (float*)P.hi;
+  const int bn = B * n;
+  const uint64_t* xin = l > 0 ? a.x + (size_t)(l - 1) * a.s_x : nullptr;
+  const uint64_t* op = a.opart + (size_t)l * a.s_opart;
+  if (!gather_fn<8>(c, KB * bn, [&](int i) -> const uint64_t* {
+        const int q = i / bn, rem = i - q * bn, b = rem / n, r = rem - b * n;
+        if (q == 0) return xin ? xin + (size_t)b * H + r0 + r : nullptr;
+        return op + ((size_t)(q - 1) * B + b) * H + r0 + r;
+      }, red, 0))
+    return false;
+  for (int idx = tid(); idx < bn; idx += NT) {
+    const int r = idx / B, b = idx - r * B;
+    float y = P.out[r][b];
+    for (int q = 1; q < KB; ++q) y += red[(q * B + b) * n + r];
+    const float x = l > 0 ? red[b * n + r] : bf2f(a.embed[(size_t)token_row(a, b) * H + r0 + r]);
+    st_tagged(a.xa + (size_t)l * a.s_x + (size_t)b * H + r0 + r, x + y, a.epoch);
+  }
+  return true;
 }
 
 // Router rows, softmax and top-k of sequence b: router logits, and per slot
@@ -2085,6 +2108,7 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
   a.x = buf(MK_BUF_XFFN); a.xa = buf(MK_BUF_XATTN); a.q = buf(MK_BUF_Q); a.kvn = buf(MK_BUF_KVN);
   a.part = buf(MK_BUF_PART); a.o = buf(MK_BUF_O); a.rlog = buf(MK_BUF_RLOG); a.act = buf(MK_BUF_ACT);
   a.lmpart = buf(MK_BUF_LMPART); a.route = buf(MK_BUF_ROUTE); a.y = buf(MK_BUF_Y);
+  a.opart = buf(MK_BUF_OPART); a.s_opart = words(MK_BUF_OPART);
   a.s_x = words(MK_BUF_XFFN); a.s_q = words(MK_BUF_Q); a.s_kvn = words(MK_BUF_KVN);
   a.s_part = words(MK_BUF_PART); a.s_o = words(MK_BUF_O); a.s_rlog = words(MK_BUF_RLOG);
   a.s_act = words(MK_BUF_ACT); a.s_route = words(MK_BUF_ROUTE); a.s_y = words(MK_BUF_Y);

@@ -222,8 +222,8 @@ struct KArgs {
   //  lmpart [n_lm][B][2] (value, index)
   //  batch only: route [L][B][K][2] (expert id bits, weight) per selected slot,
   //  y [L][B][K][H] expert outputs
-  uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart, *route, *y;
-  int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act, s_route, s_y;
+  uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart, *route, *y, *opart;
+  int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act, s_route, s_y, s_opart;
   const int32_t* seq_bound;  // [B] context bound per sequence (in the plan image)
   int32_t S_max, n_lm;
   // plan and sync

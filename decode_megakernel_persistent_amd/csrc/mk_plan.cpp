@@ -90,6 +90,8 @@ std::vector<std::pair<int, int>> split_units(int n, int u, int t) {
 // Row blocks (16 rows) per task of the MFMA batch projections: a task
 // gathers every sequence's input once, so tasks are a few row blocks each.
 constexpr int QKV_BLOCKS = 4, O_BLOCKS = 4, LM_BLOCKS = mk::MT_MAX_BLOCKS;
+// words the reducing O task gathers into LDS (partials and residual)
+constexpr int O_RED_WORDS = 16384;
 
 // Stages of a batch plan (B > 1), per layer:
 //   BQKV  (16-row blocks of one kv group's rotary pairs, all sequences: MFMA
@@ -164,16 +166,23 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
           }
       stages.push_back(st);
     }
-    {  // BO
-      std::vector<Task> st;
-      for (int s0 = 0; s0 < H; s0 += 16 * O_BLOCKS) {
-        Task t = mk_task(mk::OP_BO, l);
-        t.wait_b = ctr16(p->c_comb[l]);
-        t.signal = ctr16(p->c_o[l]);
-        t.a1 = s0; t.a2 = std::min(16 * O_BLOCKS, H - s0);
-        st.push_back(t);
+    {  // BO, split over o_kb blocks of the reduction: blocks 1 .. o_kb-1
+       // publish partial sums, then block 0 adds them and the residual
+      const int KB = p->o_kb;
+      for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 0 && KB == 1) continue;
+        std::vector<Task> st;
+        for (int s0 = 0; s0 < H; s0 += 16 * O_BLOCKS)
+          for (int kb = pass == 0 ? 1 : 0; kb < (pass == 0 ? KB : 1); ++kb) {
+            Task t = mk_task(mk::OP_BO, l);
+            t.wait_b = ctr16(p->c_comb[l]);
+            if (pass == 1 && KB > 1) t.wait_a = ctr16(p->c_opart[l]);
+            t.signal = ctr16(pass == 0 ? p->c_opart[l] : p->c_o[l]);
+            t.a0 = kb; t.a1 = s0; t.a2 = std::min(16 * O_BLOCKS, H - s0); t.a3 = KB;
+            st.push_back(t);
+          }
+        stages.push_back(st);
       }
-      stages.push_back(st);
     }
     if (moe) {  // TOPK
       std::vector<Task> tk;
@@ -348,6 +357,16 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   p->QKV_ROWS = (Hq + 2 * Hkv) * D;
   p->F = F;
   p->n_pairs_g = (p->HG * D + 2 * D) / 2;
+  if (batch) {
+    // O projection: row blocks of 16 O_BLOCKS rows, split over o_kb blocks of
+    // the reduction (whole MT_KP panels) while about one task per unit
+    // remains and the reducing task's words fit its LDS gather area
+    const int Kq = Hq * D, n_rb = ceil_div(H, 16 * O_BLOCKS), npan = Kq / mk::MT_KP;
+    int kb = 1;
+    while (npan % (2 * kb) == 0 && n_rb * 2 * kb <= n_cu && 2 * kb * B * 16 * O_BLOCKS <= O_RED_WORDS)
+      kb *= 2;
+    p->o_kb = kb;
+  }
   const int HG = p->HG, K = moe ? m->top_k : 1;
 
   auto new_ctr = [&](const std::string& name) {
@@ -383,6 +402,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + ls + "][" + std::to_string(g) + "]"));
       p->c_comb.push_back(new_ctr("comb[" + ls + "]"));
       p->c_o.push_back(new_ctr("o[" + ls + "]"));
+      p->c_opart.push_back(p->o_kb > 1 ? new_ctr("opart[" + ls + "]") : -1);
       p->c_router.push_back(-1);
       p->c_topk.push_back(moe ? new_ctr("topk[" + ls + "]") : -1);
       p->c_expert.push_back(new_ctr("expert[" + ls + "]"));
@@ -651,7 +671,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         0,                                                // LMPART (not per layer)
         (size_t)B * Hkv * 2 * D,                          // KVN
         batch && moe ? (size_t)B * K * 2 : 0,             // ROUTE
-        batch ? (size_t)B * K * H : 0};                   // Y
+        batch ? (size_t)B * K * H : 0,                    // Y
+        batch ? (size_t)(p->o_kb - 1) * B * H : 0};       // OPART
     size_t off = 0;
     for (int i = 0; i < mk_plan::N_BUF; ++i) {
       p->ws_off[i] = off;
@@ -734,8 +755,11 @@ void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::
       break;
     }
     case mk::OP_O:
-    case mk::OP_BO:
       for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"o" + ls, r});
+      break;
+    case mk::OP_BO:  // the partial sums of blocks 1 .. kb-1 end in block 0's rows
+      if (t.a0 == 0)
+        for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"o" + ls, r});
       break;
     case mk::OP_ROUTER:
       for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"router" + ls, r});

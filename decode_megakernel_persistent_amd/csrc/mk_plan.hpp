@@ -26,6 +26,8 @@ struct mk_plan {
   std::vector<int32_t> c_comb, c_o, c_router, c_expert;  // [L]
   std::vector<int32_t> c_queue;  // [L] attention split queue (queue mode)
   std::vector<int32_t> c_topk, c_bcomb;  // [L] batch: top-k per sequence, expert combine
+  std::vector<int32_t> c_opart;          // [L] batch: partial O projections (-1: not split)
+  int o_kb = 1;                          // batch: reduction blocks of the O projection
   int32_t c_lm = -1;
   bool attn_queue = false;
 
@@ -36,7 +38,7 @@ struct mk_plan {
   int32_t n_lm = 0, n_stages = 0;
 
   // workspace layout: base offset (bytes) and per-layer stride (bytes) per MK_BUF_*
-  static constexpr int N_BUF = 11;
+  static constexpr int N_BUF = 12;
   size_t ws_off[N_BUF] = {}, ws_stride[N_BUF] = {}, ws_layer_bytes[N_BUF] = {};
   int32_t n_exp_parts = 1;          // batch: expert tasks per expert
   size_t ws_total = 0;

@@ -145,6 +145,8 @@ def plan_coverage(tasks, m, bound):
     queued = set()
     pg_bound = -(-bound // m["page_tokens"])
 
+    o_blocks = {}
+
     def add(key, items):
         S.setdefault(key, []).extend(items)
 
@@ -154,7 +156,11 @@ def plan_coverage(tasks, m, bound):
         if op in (OP_QKV, OP_BQKV):
             add(("qkv", l), [r for p in range(a1, a1 + a2) for r in qkv_rows(p, a0, m)])
         elif op == OP_BO:
-            add(("o", l), list(range(a1, a1 + a2)))
+            # reduction block a0 of a3: block 0 finishes rows a1 .. a1 + a2
+            # (its own partial sum plus those of blocks 1 .. a3-1)
+            if a0 == 0:
+                add(("o", l), list(range(a1, a1 + a2)))
+            o_blocks.setdefault((l, a1, a2, max(a3, 1)), []).append(a0)
         elif op == OP_TOPK:
             # one sequence: every router row, then its top-k
             add(("router", l), [(a0, e) for e in range(m["n_experts"])])
@@ -189,6 +195,8 @@ def plan_coverage(tasks, m, bound):
             add(("down", l), list(range(a3 >> 16, (a3 >> 16) + (a3 & 0xFFFF))))
         elif op == OP_LM:
             add(("lm",), list(range(a1, a1 + a2)))
+    for (l, a1, a2, kb), blocks in o_blocks.items():
+        assert sorted(blocks) == list(range(kb)), f"o rows {a1}+{a2} of layer {l}: blocks {blocks}"
     return S
 
 
