@@ -779,39 +779,29 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   }
   lds_barrier();
   mark(c, 3);
-  // per-head merge scales over the waves: ew[q][head] = exp(m_q - M), M = max_q m_q
-  float* ew = s.out + 64;  // [NWAVE][8]
-  float* mm = s.out + 128; // [8] (M, then L)
-  if (tid() < 8) {
-    const int head = tid();
-    float M = NEG_INF;
-#pragma unroll
-    for (int q = 0; q < NWAVE; ++q) M = fmaxf(M, mw[q * 8 + head]);
-    float LL = 0.f;
-#pragma unroll
-    for (int q = 0; q < NWAVE; ++q) {
-      const float m = mw[q * 8 + head];
-      const float e = m == NEG_INF ? 0.f : expf(m - M);
-      ew[q * 8 + head] = e;
-      LL += e * lw[q * 8 + head];
-    }
-    mm[head] = M;
-    mm[8 + head] = LL;
-  }
-  lds_barrier();
+  // merge over the waves: every thread forms the scales of its own heads,
+  // exp(m_q - M) with M = max_q m_q, so no further barrier is needed
   const int PS = D + 2;
   uint64_t* dst0 = a.part + (size_t)l * a.s_part +
                    (((size_t)b * a.Hkv + g) * a.S_max + split) * HG * PS;
   for (int idx = tid(); idx < HG * D; idx += NT) {
     const int head = idx / D, dim = idx % D;
-    float oo = 0.f;
+    float M = NEG_INF;
 #pragma unroll
-    for (int q = 0; q < NWAVE; ++q) oo += ew[q * 8 + head] * Ow[(q * HG + head) * D + dim];
+    for (int q = 0; q < NWAVE; ++q) M = fmaxf(M, mw[q * 8 + head]);
+    float oo = 0.f, LL = 0.f;
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) {
+      const float m = mw[q * 8 + head];
+      const float e = m == NEG_INF ? 0.f : expf(m - M);
+      oo += e * Ow[(q * HG + head) * D + dim];
+      LL += e * lw[q * 8 + head];
+    }
     uint64_t* dst = dst0 + (size_t)head * PS;
     st_tagged(dst + dim, oo, a.epoch);
     if (dim == 0) {
-      st_tagged(dst + D, mm[head], a.epoch);
-      st_tagged(dst + D + 1, mm[8 + head], a.epoch);
+      st_tagged(dst + D, M, a.epoch);
+      st_tagged(dst + D + 1, LL, a.epoch);
     }
   }
   return true;
@@ -876,12 +866,20 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
       acc += mq == NEG_INF ? 0.f : expf(mq - M) * sw[q * W + dim];
     }
   float* red = s.out + 1024;
-  if (sg < NG) red[sg * nd + dim] = acc;
+  int nred = NG;
+  if (nd == 16) {
+    // the four rows of a wave hold split groups 4w .. 4w+3 of the same 16 dims:
+    // sum them across rows, leaving one partial per wave
+    acc = xor32_sum(xor16_sum(acc));
+    if ((tid() & 63) < 16) red[(tid() >> 6) * 16 + dim] = acc;
+    nred = NWAVE;
+  } else if (sg < NG) {
+    red[sg * nd + dim] = acc;
+  }
   lds_barrier();
   if (tid() < nd) {
     float o = 0.f;
-#pragma unroll 16
-    for (int q = 0; q < NG; ++q) o += red[q * nd + tid()];
+    for (int q = 0; q < nred; ++q) o += red[q * nd + tid()];
     o = L > 0.f ? o / L : 0.f;
     st_tagged(a.o + (size_t)l * a.s_o + ((size_t)b * a.Hq + h) * D + d0 + tid(), o, a.epoch);
   }
