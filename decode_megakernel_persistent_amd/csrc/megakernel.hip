@@ -525,7 +525,7 @@ template <int D>
 __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   constexpr int NK4 = D / 32;   // 16-byte K loads per lane per page
   constexpr int NB = D / 16;    // 16-dim blocks of the PV product
-  constexpr int NS = D / 16;    // MFMA k-steps of the QK product
+  constexpr int NS = D / 32;    // MFMA k-steps of the QK product (16x16x32)
   KAC& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, g = t.a1, pg0 = t.a2, npg = t.a3, split = t.aux;
@@ -614,21 +614,25 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   // r16 >= 8 the bf16 residual q - bf16(q) of head r16 - 8
   const int hh = r16 & 7;
   const bool lo_part = r16 >= 8;
-  v4s qop[NS];
+  // k-step st (MFMA 16x16x32) covers dims 32 st + 8 kq .. + 7, as K chunk st
+  uint4 qop[NS];
   {
     const bool valid = hh < HG;
-    // k-step st covers dims 8 kq + 32 (st / 2) + 4 (st % 2) .. + 3, as the K chunks
     const float* qp = qv + (valid ? hh : 0) * D + 8 * kq;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      const float4 x = valid ? *(const float4*)(qp + 32 * (st >> 1) + 4 * (st & 1)) : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
+      uint32_t h[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t hi = f2bf(xs[j]);
-        const uint32_t v = lo_part ? f2bf(xs[j] - bf2f(hi)) : hi;
-        qop[st][j] = (short)v;
+      for (int half = 0; half < 2; ++half) {
+        const float4 x = valid ? *(const float4*)(qp + 32 * st + 4 * half) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t hi = f2bf(xs[j]);
+          h[4 * half + j] = lo_part ? f2bf(xs[j] - bf2f(hi)) : hi;
+        }
       }
+      qop[st] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     }
   }
   float m_run = NEG_INF, l_run = 0.f;
@@ -684,11 +688,9 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     v4f SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      const uint4 ka = kA[st >> 1], kb2 = kB[st >> 1];
-      const u2v pa = (st & 1) ? u2v{ka.z, ka.w} : u2v{ka.x, ka.y};
-      const u2v pb = (st & 1) ? u2v{kb2.z, kb2.w} : u2v{kb2.x, kb2.y};
-      SA = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, pa), qop[st], SA, 0, 0, 0);
-      SB = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, pb), qop[st], SB, 0, 0, 0);
+      const bf16x8 qs = __builtin_bit_cast(bf16x8, qop[st]);
+      SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kA[st]), qs, SA, 0, 0, 0);
+      SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kB[st]), qs, SB, 0, 0, 0);
     }
     float sa[4], sb[4];
 #pragma unroll
@@ -732,14 +734,17 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     uint32_t mla, mha, mlb, mhb;
     vmask(pgA, mla, mha);
     vmask(pgB, mlb, mhb);
+    // one MFMA 16x16x32 per 16 dims over both pages: reduction index
+    // 8 kq + e is token 4 kq + e of page A for e < 4 and of page B for e >= 4,
+    // so each lane's own probabilities and V slots form its operands
+    const u2v pa2 = __builtin_bit_cast(u2v, PA), pb2 = __builtin_bit_cast(u2v, PB);
+    const bf16x8 P2 = __builtin_bit_cast(bf16x8, u4v{pa2.x, pa2.y, pb2.x, pb2.y});
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[nb][j] *= aj[j];
-      const uint2 va = make_uint2(vA[nb].x & mla, vA[nb].y & mha);
-      const uint2 vb2 = make_uint2(vB[nb].x & mlb, vB[nb].y & mhb);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(PA, __builtin_bit_cast(v4s, va), acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(PB, __builtin_bit_cast(v4s, vb2), acc[nb], 0, 0, 0);
+      const u4v v2 = {vA[nb].x & mla, vA[nb].y & mha, vB[nb].x & mlb, vB[nb].y & mhb};
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P2, __builtin_bit_cast(bf16x8, v2), acc[nb], 0, 0, 0);
     }
   };
   // page i of this wave is in buffer i % NBUF; pages go two at a time, and a
@@ -1214,7 +1219,6 @@ __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
 // take the sequences routed to their expert (any number, in groups) so that
 // each selected expert's weights stream once per step.
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // LDS of an MFMA batch tile, overlaid on the vector and staging areas.
 // Activation panel chunk (st, cb, lane) holds 8 k values 32 st + 8 (lane / 16)

@@ -88,6 +88,7 @@ __device__ __forceinline__ float dot8(const uint4 w, const float* u, float s) {
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Dot of 8 bf16 weights (one 16-byte chunk) with 8 activations given as a
 // hi/lo bf16 split (uh = bf16(u), ul = bf16(u - uh), two per 32-bit word in
