@@ -142,6 +142,43 @@ __device__ __forceinline__ bool gather(Ctx& c, const uint64_t* src, int n, float
   return gather2<MAXW>(c, src, n, src, n, dst, which, nsq);
 }
 
+// Gather n tagged words (n even) into LDS already in split form (see
+// pack_lds): word i's bf16 hi and lo parts land in chunk i / 8, paired with
+// word i ^ 1, which the neighbouring lane holds (DPP quad permutation), so no
+// separate conversion pass or barrier follows. Uniform result.
+template <int MAXW>
+__device__ __forceinline__ bool gather_split(Ctx& c, const uint64_t* src, int n, float* dst, int which) {
+  KAC& a = c.a;
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
+  uint32_t* dw = (uint32_t*)dst;
+  bool ok = true;
+  for (int base = 0; base < n && ok; base += MAXW * NT) {
+    const int t = tid();
+    float v[MAXW];
+    ok = read_words<MAXW>(a, [&](int k) -> const uint64_t* {
+      const int i = base + t + k * NT;
+      return i < n ? src + i : nullptr;
+    }, v, c.t0, c.ti);
+#pragma unroll
+    for (int k = 0; k < MAXW; ++k) {
+      const int i = base + t + k * NT;
+      const uint32_t h = f2bf(v[k]);
+      const uint32_t lo = f2bf(v[k] - bf2f(h));
+      const uint32_t hn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0xB1, 0xF, 0xF, false);
+      const uint32_t ln = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0xB1, 0xF, 0xF, false);
+      if (ok && i < n && !(i & 1)) {
+        const int ch = i >> 3, e = i & 7;
+        dw[8 * ch + (e >> 1)] = h | (hn << 16);
+        dw[8 * ch + 4 + (e >> 1)] = lo | (ln << 16);
+      }
+    }
+  }
+  if (!ok) c.s.fail = 1;
+  lds_barrier();
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
+  return c.s.fail == 0;
+}
+
 // Norm gains of chunk tid (elements 8*tid .. 8*tid+7) of a vector of K <=
 // 8*NT elements, loaded ahead of a task's wait.
 struct Gains {
@@ -907,8 +944,7 @@ __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
     if (l == 0) rw = tag_word(bf2f(a.embed[(size_t)token_row(a, 0) * a.H + r0 + th]), a.epoch);
     else rw = ld_tagged(a.x + (size_t)(l - 1) * a.s_x + r0 + th);
   }
-  if (!gather<8>(c, a.o + (size_t)l * a.s_o, K, c.s.vec, 1)) return false;
-  pack_lds(c, c.s.vec, K);
+  if (!gather_split<8>(c, a.o + (size_t)l * a.s_o, K, c.s.vec, 1)) return false;
   tile.dots(c.s.vec, c.s.out);
   lds_barrier();
   bool fail = false;
@@ -1077,8 +1113,8 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
         return (const uint4*)(Wd + ((size_t)s.route_ids[j % KK] * H + r0 + rc + j / KK) * F);
       });
     if (rc == 0) {
-      if (!gather<12>(c, a.act + (size_t)l * a.s_act + (size_t)b * KK * F, KK * F, s.vec, 1)) return false;
-      pack_lds(c, s.vec, KK * F);
+      if (!gather_split<12>(c, a.act + (size_t)l * a.s_act + (size_t)b * KK * F, KK * F, s.vec, 1))
+        return false;
     }
     mark(c, 5);
     dn.dots(s.vec + (size_t)(dn.lg % KK) * F, s.out);
