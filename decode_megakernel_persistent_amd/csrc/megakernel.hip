@@ -1521,9 +1521,14 @@ __device__ __forceinline__ bool task_bqkv(Ctx& c, const Task& t) {
   return true;
 }
 
-// Gather n tagged words, word i at addr(i), into dst[i] (LDS); uniform result.
-template <int MAXW, class Addr>
-__device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float* dst, int which) {
+struct IdentIdx {
+  __device__ __forceinline__ int operator()(int i) const { return i; }
+};
+
+// Gather n tagged words, word i at addr(i), into dst[di(i)] (LDS); uniform result.
+template <int MAXW, class Addr, class DstIdx = IdentIdx>
+__device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float* dst, int which,
+                                          const DstIdx& di = DstIdx()) {
   KAC& a = c.a;
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
   bool ok = true;
@@ -1538,7 +1543,7 @@ __device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float
 #pragma unroll
       for (int k = 0; k < MAXW; ++k) {
         const int i = base + t + k * NT;
-        if (i < n) dst[i] = v[k];
+        if (i < n) dst[di(i)] = v[k];
       }
     }
   }
@@ -1630,78 +1635,71 @@ __device__ __forceinline__ bool task_topk(Ctx& c, const Task& t) {
   return true;
 }
 
-// Rows of a GEMV over several input vectors: lane group lg (TC lanes) holds
-// rows lg + G r (r < RPW) of the current round as CPL 16-byte chunks. Loads
-// are unconditional (rows past the end re-read row R - 1), so that a round's
-// wait does not depend on how many rows the lane group has.
-template <int CPL, int RPW, int TC>
-struct MTile {
-  static constexpr int G = NT / TC;
-  static constexpr int CAP = G * RPW;  // rows per round
-  uint4 w[RPW][CPL];
-  template <class RowPtr>
-  __device__ __forceinline__ void issue(int r0, int R, const RowPtr& rowptr) {
-    const int lg = tid() / TC, tc = tid() % TC;
+// Expert GEMM on MFMA: R weight rows (bf16, K elements each, rowptr(r))
+// against up to 16 input columns held in LDS in split form (column n at
+// in + n * ld floats, chunk c = elements 8c .. 8c+7 as 4 words of bf16 hi
+// pairs then 4 words of lo pairs): out(r, n) = sum_k W[r][k] x_n[k]. Waves
+// take pairs of 16-row blocks round-robin; per k-step of 32 each lane loads
+// 16 bytes of one weight row (row r16 of the block, k 32 st + 8 kq .. + 7, the
+// A operand) and reads that chunk of column r16 (hi and lo: two B operands),
+// two MFMA 16x16x32 per block. Weights of the next KC k-steps are in flight
+// while a group is multiplied. epi(rb, acc) receives block rb's accumulators:
+// lane (n = r16, kq) holds rows 16 rb + 4 kq + j, j < 4, of column n (n >=
+// ncols repeats column ncols - 1 and is to be ignored). K % (32 KC) == 0.
+template <class RowPtr, class Epi>
+__device__ __forceinline__ void mfma_rows(int R, int K, const RowPtr& rowptr, const float* in, int ld,
+                                          int ncols, const Epi& epi) {
+  constexpr int KC = 4;
+  const int lane = tid() & 63, w = tid() >> 6, r16 = lane & 15, kq = lane >> 4;
+  const int nrb = (R + 15) >> 4, nks = K >> 5;
+  const float* inn = in + (size_t)min(r16, ncols - 1) * ld + 8 * kq;
+  for (int rbA = 2 * w; rbA < nrb; rbA += 2 * NWAVE) {
+    const int rbB = min(rbA + 1, nrb - 1);
+    const uint16_t* wa = rowptr(min(rbA * 16 + r16, R - 1)) + 8 * kq;
+    const uint16_t* wb = rowptr(min(rbB * 16 + r16, R - 1)) + 8 * kq;
+    v4f accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+    uint4 xa[KC], xb[KC], ya[KC], yb[KC];
+    auto load = [&](uint4 (&pa)[KC], uint4 (&pb)[KC], int s0) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const uint4* p = rowptr(min(r0 + lg + r * G, R - 1));
+      for (int i = 0; i < KC; ++i) {
+        pa[i] = ld_nt((const uint4*)(wa + 32 * (s0 + i)));
+        pb[i] = ld_nt((const uint4*)(wb + 32 * (s0 + i)));
+      }
+    };
+    auto mul = [&](const uint4 (&pa)[KC], const uint4 (&pb)[KC], int s0) {
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) w[r][cc] = ld_nt(p + tc + cc * TC);
+      for (int i = 0; i < KC; ++i) {
+        const uint4* ip = (const uint4*)(inn + 32 * (s0 + i));
+        const bf16x8 hi = __builtin_bit_cast(bf16x8, ip[0]), lo = __builtin_bit_cast(bf16x8, ip[1]);
+        const bf16x8 A = __builtin_bit_cast(bf16x8, pa[i]), Bw = __builtin_bit_cast(bf16x8, pb[i]);
+        accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, hi, accA, 0, 0, 0);
+        accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, lo, accA, 0, 0, 0);
+        accB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Bw, hi, accB, 0, 0, 0);
+        accB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Bw, lo, accB, 0, 0, 0);
+      }
+    };
+    load(xa, xb, 0);
+    for (int s0 = 0; s0 < nks; s0 += 2 * KC) {
+      if (s0 + KC < nks) load(ya, yb, s0 + KC);
+      mul(xa, xb, s0);
+      if (s0 + 2 * KC < nks) load(xa, xb, s0 + 2 * KC);
+      if (s0 + KC < nks) mul(ya, yb, s0 + KC);
     }
-  }
-  // out[row * EXP_GROUP + s] for the round's rows < R and inputs s < ns;
-  // input s in split form at u + s * K (floats)
-  __device__ __forceinline__ void dots(int r0, int R, const float* u, int K, int ns, float* out) {
-    const int lg = tid() / TC, tc = tid() % TC;
-    float acc[RPW][EXP_GROUP];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int q = 0; q < EXP_GROUP; ++q) acc[r][q] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < CPL; ++cc)
-#pragma unroll
-      for (int q = 0; q < EXP_GROUP; ++q)
-        if (q < ns) {
-          const uint4* up = (const uint4*)(u + (size_t)q * K + (tc + cc * TC) * 8);
-          const uint4 uh = up[0], ul = up[1];
-#pragma unroll
-          for (int r = 0; r < RPW; ++r) acc[r][q] = dot8h(w[r][cc], uh, ul, acc[r][q]);
-        }
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int row = r0 + lg + r * G;
-#pragma unroll
-      for (int q = 0; q < EXP_GROUP; ++q)
-        if (q < ns) {
-          const float sum = group_sum_last<TC>(acc[r][q]);
-          if (tc == TC - 1 && row < R) out[row * EXP_GROUP + q] = sum;
-        }
-    }
-  }
-};
-
-// All R rows of a multi-input GEMV, two rounds in flight.
-template <int CPL, int RPW, int TC, class RowPtr>
-__device__ __forceinline__ void mgemv(int R, const RowPtr& rowptr, const float* u, int K, int ns,
-                                      float* out) {
-  using T = MTile<CPL, RPW, TC>;
-  T A, Bt;
-  A.issue(0, R, rowptr);
-  for (int r0 = 0; r0 < R; r0 += 2 * T::CAP) {
-    if (r0 + T::CAP < R) Bt.issue(r0 + T::CAP, R, rowptr);
-    A.dots(r0, R, u, K, ns, out);
-    if (r0 + 2 * T::CAP < R) A.issue(r0 + 2 * T::CAP, R, rowptr);
-    if (r0 + T::CAP < R) Bt.dots(r0 + T::CAP, R, u, K, ns, out);
+    epi(rbA, accA);
+    if (rbB != rbA) epi(rbB, accB);
   }
 }
 
+// Column stride (floats) of an expert task's inputs in LDS: a padding of 8
+// floats shifts consecutive columns by 8 banks.
+__device__ __forceinline__ int exp_ld(int K) { return K + 8; }
+
 // LDS of a batch expert task (overlaid on the vector and staging areas):
-// the inputs of one group of routed sequences in split form, the group's
-// results, and the routed (sequence, slot) list.
+// the inputs of one group of routed sequences in split form, and the routed
+// (sequence, slot) list.
 struct ExpLds {
-  float in[EXP_GROUP * 2048];
-  float out[1024 * EXP_GROUP];
+  float in[EXP_GROUP * (2048 + 8)];
+  float ids[MAX_BATCH * 16];
   int list[MAX_BATCH * 16];
   int wave_cnt[NWAVE];
 };
@@ -1712,7 +1710,9 @@ static_assert(sizeof(ExpLds) <= sizeof(float) * LDS_VEC + sizeof(uint4) * NWAVE 
 // slot order, EXP_GROUP at a time), the gate/up rows a1 .. a1 + a2 with
 // SwiGLU into the activation words of that (sequence, slot); then the down
 // rows of the same expert over the full activations (from every part of the
-// expert) into the expert-output words y of that (sequence, slot). Dense
+// expert) into the expert-output words y of that (sequence, slot). Both are
+// MFMA GEMMs with the group's inputs as the columns, so the time is the
+// weights' streaming time whatever the number of routed sequences. Dense
 // FFN: expert 0, every sequence in slot 0.
 template <int CH, int TCH, int CF, int TCF>
 __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
@@ -1731,7 +1731,7 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
     lds_barrier();
   } else {
     const int n = B * KK;  // <= NT (checked by the planner)
-    float* ids = X.out;
+    float* ids = X.ids;
     if (!gather_fn<1>(c, n, [&](int i) { return a.route + (size_t)l * a.s_route + (size_t)i * 2; }, ids, 0))
       return false;
     const bool mine = th < n && __float_as_int(ids[th]) == e;
@@ -1751,26 +1751,34 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
   const uint16_t* Wg = a.gate + ((size_t)l * EE + e) * F * H;
   const uint16_t* Wu = a.up + ((size_t)l * EE + e) * F * H;
   const uint16_t* Wd = a.down + ((size_t)l * EE + e) * H * F;
+  const int ldh = exp_ld(H), ldf = exp_ld(F);
+  const int kq = lane >> 4, r16 = lane & 15;
   // gate/up: rows 2f (gate) and 2f + 1 (up) of FFN row f0 + f
   if (nf > 0)
     for (int g0 = 0; g0 < ns; g0 += EXP_GROUP) {
       const int ng = min(EXP_GROUP, ns - g0);
+      // column q at the padded stride
       if (!gather_fn<4>(c, ng * H, [&](int i) {
             const int q = i / H, bs = X.list[g0 + q] / KK;
             return a.xa + (size_t)l * a.s_x + (size_t)bs * H + (i - q * H);
-          }, X.in, 1))
+          }, X.in, 1, [&](int i) { const int q = i / H; return q * ldh + (i - q * H); }))
         return false;
-      for (int q = 0; q < ng; ++q) rmsnorm_pack(c, X.in + (size_t)q * H, H, gn);
-      mgemv<CH, 2, TCH>(2 * nf, [&](int j) {
-          return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + (j >> 1)) * H);
-        }, X.in, H, ng, X.out);
-      lds_barrier();
-      for (int idx = th; idx < nf * ng; idx += NT) {
-        const int f = idx / ng, q = idx - f * ng;
-        const float yg = X.out[(2 * f) * EXP_GROUP + q], yu = X.out[(2 * f + 1) * EXP_GROUP + q];
-        const int ent = X.list[g0 + q];  // b * KK + slot
-        st_tagged(a.act + (size_t)l * a.s_act + (size_t)ent * F + f0 + f, yg / (1.0f + expf(-yg)) * yu, a.epoch);
-      }
+      for (int q = 0; q < ng; ++q) rmsnorm_pack(c, X.in + (size_t)q * ldh, H, gn);
+      mfma_rows(2 * nf, H, [&](int j) {
+          return ((j & 1) ? Wu : Wg) + (size_t)(f0 + (j >> 1)) * H;
+        }, X.in, ldh, ng, [&](int rb, const v4f& acc) {
+          // rows 16 rb + 4 kq + j: j = 0, 1 gate and up of one FFN row, j = 2, 3 of the next
+          if (r16 < ng) {
+            const int ent = X.list[g0 + r16];  // b * KK + slot
+            uint64_t* dst = a.act + (size_t)l * a.s_act + (size_t)ent * F + f0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int f = (rb * 16 + 4 * kq + 2 * h) >> 1;
+              const float yg = acc[2 * h], yu = acc[2 * h + 1];
+              if (f < nf) st_tagged(dst + f, yg / (1.0f + expf(-yg)) * yu, a.epoch);
+            }
+          }
+        });
       lds_barrier();
     }
   mark(c, 1);
@@ -1778,20 +1786,22 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
   if (nr > 0)
     for (int g0 = 0; g0 < ns; g0 += EXP_GROUP) {
       const int ng = min(EXP_GROUP, ns - g0);
-      if (!gather_fn<4>(c, ng * F, [&](int i) {
-            const int q = i / F;
-            return a.act + (size_t)l * a.s_act + (size_t)X.list[g0 + q] * F + (i - q * F);
-          }, X.in, 1))
-        return false;
-      for (int q = 0; q < ng; ++q) pack_lds(c, X.in + (size_t)q * F, F);
-      mgemv<CF, 2, TCF>(nr, [&](int j) { return (const uint4*)(Wd + (size_t)(r0 + j) * F); },
-                        X.in, F, ng, X.out);
-      lds_barrier();
-      for (int idx = th; idx < nr * ng; idx += NT) {
-        const int r = idx / ng, q = idx - r * ng;
-        const int ent = X.list[g0 + q];
-        st_tagged(a.y + (size_t)l * a.s_y + (size_t)ent * H + r0 + r, X.out[r * EXP_GROUP + q], a.epoch);
-      }
+      for (int q = 0; q < ng; ++q)
+        if (!gather_split<4>(c, a.act + (size_t)l * a.s_act + (size_t)X.list[g0 + q] * F, F,
+                             X.in + (size_t)q * ldf, 1))
+          return false;
+      mfma_rows(nr, F, [&](int j) { return Wd + (size_t)(r0 + j) * F; }, X.in, ldf, ng,
+                [&](int rb, const v4f& acc) {
+          if (r16 < ng) {
+            const int ent = X.list[g0 + r16];
+            uint64_t* dst = a.y + (size_t)l * a.s_y + (size_t)ent * H + r0;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int r = rb * 16 + 4 * kq + jj;
+              if (r < nr) st_tagged(dst + r, acc[jj], a.epoch);
+            }
+          }
+        });
       lds_barrier();
     }
   mark(c, 2);
