@@ -1649,7 +1649,7 @@ __device__ __forceinline__ bool task_topk(Ctx& c, const Task& t) {
 template <class RowPtr, class Epi>
 __device__ __forceinline__ void mfma_rows(int R, int K, const RowPtr& rowptr, const float* in, int ld,
                                           int ncols, const Epi& epi) {
-  constexpr int KC = 4;
+  constexpr int KC = 8;
   const int lane = tid() & 63, w = tid() >> 6, r16 = lane & 15, kq = lane >> 4;
   const int nrb = (R + 15) >> 4, nks = K >> 5;
   const float* inn = in + (size_t)min(r16, ncols - 1) * ld + 8 * kq;

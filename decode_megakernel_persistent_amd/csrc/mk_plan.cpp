@@ -120,8 +120,9 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
   p->n_exp_parts = P;
   if (NE * P > n_cu) return fail(MK_EUNSUPPORTED, "mk_plan: more expert tasks than compute units");
   // an expert task holds EXP_GROUP inputs of width H or F and up to 1024 result rows in LDS
-  if (H % 128 || F % 128)
-    return fail(MK_EUNSUPPORTED, "mk_plan: batch plans need hidden and FFN widths that are multiples of 128");
+  // expert GEMMs stream the reduction in groups of 8 k-steps of 32
+  if (H % 256 || F % 256)
+    return fail(MK_EUNSUPPORTED, "mk_plan: batch plans need hidden and FFN widths that are multiples of 256");
   if (H > 2048 || F > 2048 || 2 * ceil_div(F, P) > 1024 || ceil_div(H, P) > 1024)
     return fail(MK_EUNSUPPORTED, "mk_plan: batch expert tiles exceed LDS (hidden and FFN <= 2048, "
                                  "rows per expert task <= 1024): use more compute units");
