@@ -1309,43 +1309,47 @@ __device__ __forceinline__ bool mt_tile(Ctx& c, int R, int K, const RowPtr& rowp
       wr[s] = ld_nt((const uint4*)(wrow + p * MT_KP + st * 32));
     }
   };
-  // panel fill: thread t owns chunks t and t + NT, both of one sequence
-  const int cb_t = (t >> 6) & 1, seq = cb_t * 16 + (lane & 15), kg = lane >> 4, st0 = t >> 7;
+  // panel fill: wave w fills column block cb_t = w & 1, k-group kg = w >> 1
+  // of every k-step; lanes 4 m .. 4 m + 3 hold words 2 jw, 2 jw + 1 of the
+  // chunk (8 k values) of sequence 16 cb_t + m, so each load instruction reads
+  // whole 64-byte runs of 16 sequences, two tagged words per lane
+  const int cb_t = w & 1, kg = w >> 1, m4 = lane >> 2, jw = lane & 3;
+  const int seq = cb_t * 16 + m4;
   const bool sv = seq < B;
   const int sq = sv ? seq : 0;
-  const uint64_t* xw = src.words ? src.words + (size_t)sq * src.ld : nullptr;
-  const uint16_t* xe = src.words ? nullptr : a.embed + (size_t)token_row(a, sq) * K;
+  const int kl = 8 * kg + 2 * jw;  // this lane's first k within a k-step
+  const bool xw = src.words != nullptr;
+  const tag_rsrc rx = tagged_rsrc(xw ? src.words : (const uint64_t*)a.embed,
+                                  xw ? (uint32_t)(((size_t)(B - 1) * src.ld + K) * 8) : 0u);
+  const uint32_t xoff = (uint32_t)(((size_t)sq * src.ld + kl) * 8);
+  const uint16_t* xe = xw ? nullptr : a.embed + (size_t)token_row(a, sq) * K + kl;
   float ss = 0.f;
-  struct ActRegs { uint64_t v[16]; uint4 e[2]; uint4 g[2]; };
+  struct ActRegs { uint4 v[8]; uint32_t e[8]; uint32_t g[8]; };
   auto issue_act = [&](int p, ActRegs& r) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int k0 = p * MT_KP + (st0 + 4 * q) * 32 + 8 * kg;
-      if (xw) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r.v[8 * q + e] = ld_tagged(xw + k0 + e);
-      } else {
-        r.e[q] = *(const uint4*)(xe + k0);
-      }
-      r.g[q] = src.gain ? *(const uint4*)(src.gain + k0) : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+    for (int i = 0; i < 8; ++i) {
+      const int k0 = p * MT_KP + i * 32;
+      if (xw) r.v[i] = ld_tagged2(rx, xoff + (uint32_t)k0 * 8u);
+      else r.e[i] = *(const uint32_t*)(xe + k0);
+      r.g[i] = src.gain ? *(const uint32_t*)(src.gain + k0 + kl) : 0x3F803F80u;
     }
   };
-  // check the words' tags (re-reading stale ones), then convert into panel bi
+  // check the words' tags (re-reading stale pairs), then convert into panel bi
   auto finish_act = [&](int p, ActRegs& r, int bi) -> bool {
     if (xw && sv) {
       const uint32_t ep = a.epoch;
       uint32_t stale = 0;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) stale |= tag_is(r.v[k], ep) ? 0u : (1u << k);
+      for (int i = 0; i < 8; ++i) stale |= tag2_is(r.v[i], ep) ? 0u : (1u << i);
       uint32_t it = 0;
       while (stale) {
         __builtin_amdgcn_s_sleep(2);
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if (stale & (1u << k)) r.v[k] = ld_tagged(xw + p * MT_KP + (st0 + 4 * (k >> 3)) * 32 + 8 * kg + (k & 7));
+        for (int i = 0; i < 8; ++i)
+          if (stale & (1u << i)) r.v[i] = ld_tagged2(rx, xoff + (uint32_t)(p * MT_KP + i * 32) * 8u);
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if ((stale & (1u << k)) && tag_is(r.v[k], ep)) stale &= ~(1u << k);
+        for (int i = 0; i < 8; ++i)
+          if ((stale & (1u << i)) && tag2_is(r.v[i], ep)) stale &= ~(1u << i);
         if (stale && (++it & 31u) == 0u) {
           if (aborted(a)) return false;
           if (now() - c.t0 > a.timeout_ticks) {
@@ -1355,27 +1359,27 @@ __device__ __forceinline__ bool mt_tile(Ctx& c, int R, int K, const RowPtr& rowp
         }
       }
     }
+    uint32_t* ph = (uint32_t*)P.hi[bi];
+    uint32_t* pl = (uint32_t*)P.lo[bi];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float x[8];
+    for (int i = 0; i < 8; ++i) {
+      float x0, x1;
       if (xw) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = sv ? tag_value(r.v[8 * q + e]) : 0.f;
+        x0 = sv ? __uint_as_float(r.v[i].x) : 0.f;
+        x1 = sv ? __uint_as_float(r.v[i].z) : 0.f;
       } else {
-        const uint32_t ew[4] = {r.e[q].x, r.e[q].y, r.e[q].z, r.e[q].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = sv ? ((e & 1) ? bf_hi(ew[e >> 1]) : bf_lo(ew[e >> 1])) : 0.f;
+        x0 = sv ? bf_lo(r.e[i]) : 0.f;
+        x1 = sv ? bf_hi(r.e[i]) : 0.f;
       }
-      const uint32_t gw[4] = {r.g[q].x, r.g[q].y, r.g[q].z, r.g[q].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ss = fmaf(x[e], x[e], ss);
-        x[e] *= (e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1]);
-      }
-      uint4 hi, lo;
-      split8(x, hi, lo);
-      P.hi[bi][t + q * NT] = hi;
-      P.lo[bi][t + q * NT] = lo;
+      ss = fmaf(x0, x0, ss);
+      ss = fmaf(x1, x1, ss);
+      x0 *= bf_lo(r.g[i]);
+      x1 *= bf_hi(r.g[i]);
+      const uint32_t h0 = f2bf(x0), h1 = f2bf(x1);
+      const uint32_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
+      const int word = ((i * 2 + cb_t) * 64 + kg * 16 + m4) * 4 + jw;
+      ph[word] = h0 | (h1 << 16);
+      pl[word] = l0 | (l1 << 16);
     }
     return true;
   };
@@ -1436,7 +1440,7 @@ __device__ __forceinline__ bool mt_tile(Ctx& c, int R, int K, const RowPtr& rowp
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) tot += P.ss[q * 128 + cb * 64 + g * 16 + s16];
+      for (int j = 0; j < 4; ++j) tot += P.ss[(2 * q + cb) * 64 + 4 * s16 + j];
     P.scale[t] = src.norm ? 1.0f / sqrtf(tot / (float)K + a.eps) : 1.f;
   }
   lds_barrier();

@@ -193,6 +193,24 @@ __device__ __forceinline__ void st_tagged(uint64_t* p, float v, uint32_t epoch) 
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool tag_is(uint64_t w, uint32_t epoch) { return (uint32_t)(w >> 32) == epoch; }
+
+// Two neighbouring tagged words in one 16-byte load with the same coherence
+// as ld_tagged (the L2 of this XCD is bypassed): a buffer resource over
+// nbytes at base (wave-uniform), byte offset off (a multiple of 16). Each
+// aligned 8-byte half is one word as its single store wrote it, so each half's
+// tag vouches for its own value. Offsets at or past nbytes read zeros (a
+// stale tag), never another allocation. .x/.y = word 0 (value, tag), .z/.w =
+// word 1.
+typedef __amdgpu_buffer_rsrc_t tag_rsrc;
+__device__ __forceinline__ tag_rsrc tagged_rsrc(const uint64_t* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld_tagged2(tag_rsrc r, uint32_t off) {
+  // cache policy: sc1 (device coherence, as ld_tagged), bit 31: volatile
+  const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, (int)0x80000010u);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ bool tag2_is(const uint4& v, uint32_t epoch) { return v.y == epoch && v.w == epoch; }
 __device__ __forceinline__ float tag_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // Record a device failure: the first one wins the code word.
