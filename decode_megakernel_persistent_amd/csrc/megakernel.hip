@@ -1344,6 +1344,7 @@ __device__ __forceinline__ bool mt_tile(Ctx& c, int R, int K, const RowPtr& rowp
       uint32_t it = 0;
       while (stale) {
         __builtin_amdgcn_s_sleep(2);
+        tagged_reload_fence();
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (stale & (1u << i)) r.v[i] = ld_tagged2(rx, xoff + (uint32_t)(p * MT_KP + i * 32) * 8u);

@@ -205,11 +205,14 @@ typedef __amdgpu_buffer_rsrc_t tag_rsrc;
 __device__ __forceinline__ tag_rsrc tagged_rsrc(const uint64_t* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)nbytes, 0x00020000);
 }
+// A caller that re-reads a word in a loop puts a compiler memory barrier
+// (tagged_reload_fence) between the reads, so that they are not merged.
 __device__ __forceinline__ uint4 ld_tagged2(tag_rsrc r, uint32_t off) {
-  // cache policy: sc1 (device coherence, as ld_tagged), bit 31: volatile
-  const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, (int)0x80000010u);
+  // cache policy: sc1 (device coherence, as ld_tagged)
+  const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ void tagged_reload_fence() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ bool tag2_is(const uint4& v, uint32_t epoch) { return v.y == epoch && v.w == epoch; }
 __device__ __forceinline__ float tag_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
