@@ -95,6 +95,61 @@ __device__ __forceinline__ uint64_t logit_key(float v, int e) {
 // slots), -1 = untraced. With nsq > 0 the sum of squares of words 0 .. nsq-1
 // is formed on the way (each thread over its words in order, then over the
 // wave) and wave w's part is left in s.red[w] for norm_pack. Uniform result.
+// Byte offset of a tagged word in the workspace.
+__device__ __forceinline__ uint32_t ws_off(const KAC& a, const uint64_t* p) {
+  return (uint32_t)((const char*)p - (const char*)a.ws);
+}
+
+// Read MAXP pairs of neighbouring tagged words of this thread (pair k at
+// workspace byte offset off(k), a multiple of 16, or NO_PAIR) into out[2k],
+// out[2k + 1], one 16-byte load per pair, re-reading stale pairs like
+// read_words. Returns false on deadline or another workgroup's failure.
+constexpr uint32_t NO_PAIR = 0xFFFFFFFFu;
+template <int MAXP, class Off>
+__device__ __forceinline__ bool read_pairs(KAC& a, const Off& off, float* out, uint64_t t0, uint32_t task) {
+  const tag_rsrc r = tagged_rsrc(a.ws, a.ws_bytes);
+  const uint32_t ep = a.epoch;
+  uint4 w[MAXP];
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) {
+    const uint32_t o = off(k);
+    w[k] = o != NO_PAIR ? ld_tagged2(r, o) : make_uint4(0u, ep, 0u, ep);
+  }
+  uint32_t stale = 0;
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) stale |= tag2_is(w[k], ep) ? 0u : (1u << k);
+  uint32_t it = 0;
+  while (stale) {
+    __builtin_amdgcn_s_sleep(2);
+    tagged_reload_fence();
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k)
+      if (stale & (1u << k)) w[k] = ld_tagged2(r, off(k));
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k)
+      if ((stale & (1u << k)) && tag2_is(w[k], ep)) stale &= ~(1u << k);
+    if (stale && (++it & 31u) == 0u) {
+      if (aborted(a)) return false;
+      if (now() - t0 > a.timeout_ticks) {
+        raise_status(a, DS_TIMEOUT, task, (uint32_t)__builtin_ctz(stale), 0xFFFFFFFDu);
+        return false;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) {
+    out[2 * k] = __uint_as_float(w[k].x);
+    out[2 * k + 1] = __uint_as_float(w[k].z);
+  }
+  return true;
+}
+
+// Whether words of src1 (n1 of them) then src2 (up to n) can be read in
+// 16-byte pairs: even counts and even word offsets in the workspace.
+__device__ __forceinline__ bool pairable(const KAC& a, const uint64_t* src1, int n1, const uint64_t* src2, int n) {
+  return !((n1 | n | (int)(ws_off(a, src1) >> 3) | (int)(ws_off(a, src2) >> 3)) & 1);
+}
+
 template <int MAXW>
 __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, const uint64_t* src2, int n,
                                         float* dst, int which, int nsq = 0, uint64_t* keys = nullptr) {
@@ -102,6 +157,35 @@ __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, co
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
   bool ok = true;
   float ss = 0.f, mx = NEG_INF;
+  if (pairable(a, src1, n1, src2, n)) {
+    // pairs (2j, 2j + 1), j = base / 2 + t + k NT: one 16-byte load each
+    constexpr int MAXP = (MAXW + 1) / 2;
+    const uint32_t o1 = ws_off(a, src1), o2 = ws_off(a, src2);
+    for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
+      const int t = tid();
+      float v[2 * MAXP];
+      ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
+        const int i = base + 2 * (t + k * NT);
+        return i < n1 ? o1 + 8u * i : (i < n ? o2 + 8u * (i - n1) : NO_PAIR);
+      }, v, c.t0, c.ti);
+      if (ok) {
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+          const int i = base + 2 * (t + k * NT);
+          if (i < n) *(float2*)(dst + i) = make_float2(v[2 * k], v[2 * k + 1]);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            if (i + e < nsq) ss = fmaf(v[2 * k + e], v[2 * k + e], ss);
+            if (keys && i + e >= n1 && i + e < n) {
+              keys[i + e - n1] = logit_key(v[2 * k + e], i + e - n1);
+              mx = fmaxf(mx, v[2 * k + e]);
+            }
+          }
+        }
+      }
+    }
+  }
+  else
   for (int base = 0; base < n && ok; base += MAXW * NT) {
     const int t = tid();
     float v[MAXW];
@@ -152,6 +236,31 @@ __device__ __forceinline__ bool gather_split(Ctx& c, const uint64_t* src, int n,
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
   uint32_t* dw = (uint32_t*)dst;
   bool ok = true;
+  if (pairable(a, src, n, src, n)) {
+    // pairs (2j, 2j + 1) in one 16-byte load: the thread holds both bf16 halves
+    constexpr int MAXP = (MAXW + 1) / 2;
+    const uint32_t o = ws_off(a, src);
+    for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
+      const int t = tid();
+      float v[2 * MAXP];
+      ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
+        const int i = base + 2 * (t + k * NT);
+        return i < n ? o + 8u * i : NO_PAIR;
+      }, v, c.t0, c.ti);
+#pragma unroll
+      for (int k = 0; k < MAXP; ++k) {
+        const int i = base + 2 * (t + k * NT);
+        const uint32_t h0 = f2bf(v[2 * k]), h1 = f2bf(v[2 * k + 1]);
+        const uint32_t l0 = f2bf(v[2 * k] - bf2f(h0)), l1 = f2bf(v[2 * k + 1] - bf2f(h1));
+        if (ok && i < n) {
+          const int ch = i >> 3, e = i & 7;
+          dw[8 * ch + (e >> 1)] = h0 | (h1 << 16);
+          dw[8 * ch + 4 + (e >> 1)] = l0 | (l1 << 16);
+        }
+      }
+    }
+  }
+  else
   for (int base = 0; base < n && ok; base += MAXW * NT) {
     const int t = tid();
     float v[MAXW];
@@ -2156,6 +2265,11 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
   a.tok_in = io->tokens_in; a.tok_out = io->tokens_out; a.topk_ids = io->topk_ids;
   a.topk_w = io->topk_w; a.logits = io->logits;
   char* ws = (char*)bu->workspace;
+  if (p->ws_total >= (1ull << 32))
+    return fail(MK_EUNSUPPORTED, "mk_decode_step: workspace of 4 GiB or more");
+  if ((uintptr_t)ws & 255) return fail(MK_EINVAL, "mk_decode_step: workspace not 256-byte aligned");
+  a.ws = (const uint64_t*)ws;
+  a.ws_bytes = (uint32_t)p->ws_total;
   auto buf = [&](int which) { return (uint64_t*)(ws + p->ws_off[which]); };
   auto words = [&](int which) { return (int64_t)(p->ws_stride[which] / 8); };
   a.x = buf(MK_BUF_XFFN); a.xa = buf(MK_BUF_XATTN); a.q = buf(MK_BUF_Q); a.kvn = buf(MK_BUF_KVN);

@@ -223,6 +223,8 @@ struct KArgs {
   //  batch only: route [L][B][K][2] (expert id bits, weight) per selected slot,
   //  y [L][B][K][H] expert outputs
   uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart, *route, *y, *opart;
+  const uint64_t* ws;  // the workspace holding all of them (256-byte aligned)
+  uint32_t ws_bytes;   // its size (under 4 GiB)
   int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act, s_route, s_y, s_opart;
   const int32_t* seq_bound;  // [B] context bound per sequence (in the plan image)
   int32_t S_max, n_lm;
