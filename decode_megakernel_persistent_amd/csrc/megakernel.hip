@@ -972,6 +972,29 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   float* sw = s.att;
   if (a.trace && tid() == 0) s.tw[2] = now();
   bool ok = true;
+  if (!(nd & 1) && !((ws_off(a, base) >> 3) & 1)) {
+    // in pairs: split q's words are nd / 2 pairs of dims, then the pair (max, sum)
+    const int WP = W / 2, np = S * WP;
+    const uint32_t ob = ws_off(a, base);
+    for (int bs = 0; bs < np && ok; bs += 2 * NT) {
+      const int t = tid();
+      float v[4];
+      ok = read_pairs<2>(a, [&](int k) -> uint32_t {
+        const int pi = bs + t + k * NT;
+        if (pi >= np) return NO_PAIR;
+        const int q = pi / WP, j = 2 * (pi - q * WP);
+        return ob + 8u * (uint32_t)(q * sstride + (j < nd ? d0 + j : D + (j - nd)));
+      }, v, c.t0, c.ti);
+      if (ok) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int pi = bs + t + k * NT;
+          if (pi < np) *(float2*)(sw + 2 * pi) = make_float2(v[2 * k], v[2 * k + 1]);
+        }
+      }
+    }
+  }
+  else
   for (int bs = 0; bs < n && ok; bs += 4 * NT) {
     const int t = tid();
     float v[4];
@@ -1667,6 +1690,39 @@ __device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float
   return c.s.fail == 0;
 }
 
+// gather_fn reading word pairs (i, i + 1), i even, with one 16-byte load:
+// for the caller, n is even and, for every even i, addr(i) (nullptr: none) is
+// a word at an even workspace word offset followed by word i + 1, and
+// di(i + 1) = di(i) + 1 with di(i) even. Uniform result.
+template <int MAXW, class Addr, class DstIdx = IdentIdx>
+__device__ __forceinline__ bool gather_fn_pairs(Ctx& c, int n, const Addr& addr, float* dst, int which,
+                                                const DstIdx& di = DstIdx()) {
+  KAC& a = c.a;
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
+  constexpr int MAXP = (MAXW + 1) / 2;
+  bool ok = true;
+  for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
+    const int t = tid();
+    float v[2 * MAXP];
+    ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
+      const int i = base + 2 * (t + k * NT);
+      const uint64_t* p = i < n ? addr(i) : nullptr;
+      return p ? ws_off(a, p) : NO_PAIR;
+    }, v, c.t0, c.ti);
+    if (ok) {
+#pragma unroll
+      for (int k = 0; k < MAXP; ++k) {
+        const int i = base + 2 * (t + k * NT);
+        if (i < n) *(float2*)(dst + di(i)) = make_float2(v[2 * k], v[2 * k + 1]);
+      }
+    }
+  }
+  if (!ok) c.s.fail = 1;
+  lds_barrier();
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
+  return c.s.fail == 0;
+}
+
 // W_o rows of every sequence over reduction block kb (a0) of the a3 blocks
 // of the attention output: blocks 1 .. a3-1 publish partial sums (OPART);
 // block 0 adds them in block order to its own and adds the residual (the
@@ -1695,11 +1751,14 @@ __device__ __forceinline__ bool task_bo(Ctx& c, const Task& t) {
   const int bn = B * n;
   const uint64_t* xin = l > 0 ? a.x + (size_t)(l - 1) * a.s_x : nullptr;
   const uint64_t* op = a.opart + (size_t)l * a.s_opart;
-  if (!gather_fn<8>(c, KB * bn, [&](int i) -> const uint64_t* {
-        const int q = i / bn, rem = i - q * bn, b = rem / n, r = rem - b * n;
-        if (q == 0) return xin ? xin + (size_t)b * H + r0 + r : nullptr;
-        return op + ((size_t)(q - 1) * B + b) * H + r0 + r;
-      }, red, 0))
+  auto waddr = [&](int i) -> const uint64_t* {
+    const int q = i / bn, rem = i - q * bn, b = rem / n, r = rem - b * n;
+    if (q == 0) return xin ? xin + (size_t)b * H + r0 + r : nullptr;
+    return op + ((size_t)(q - 1) * B + b) * H + r0 + r;
+  };
+  // pairs of rows (r, r + 1): even n, r0 and H keep every pair in one row range
+  const bool pairs = !((n | r0 | H) & 1) && !((ws_off(a, op) >> 3) & 1) && !(xin && ((ws_off(a, xin) >> 3) & 1));
+  if (!(pairs ? gather_fn_pairs<8>(c, KB * bn, waddr, red, 0) : gather_fn<8>(c, KB * bn, waddr, red, 0)))
     return false;
   for (int idx = tid(); idx < bn; idx += NT) {
     const int r = idx / B, b = idx - r * B;
@@ -1872,7 +1931,8 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
     for (int g0 = 0; g0 < ns; g0 += EXP_GROUP) {
       const int ng = min(EXP_GROUP, ns - g0);
       // column q at the padded stride
-      if (!gather_fn<4>(c, ng * H, [&](int i) {
+      // H is even (a multiple of 256 for batch plans): pairs stay in one column
+      if (!gather_fn_pairs<4>(c, ng * H, [&](int i) {
             const int q = i / H, bs = X.list[g0 + q] / KK;
             return a.xa + (size_t)l * a.s_x + (size_t)bs * H + (i - q * H);
           }, X.in, 1, [&](int i) { const int q = i / H; return q * ldh + (i - q * H); }))
