@@ -48,6 +48,11 @@ constexpr int LDS_VEC = dev_lds_vec();
 constexpr int STAGE_CHUNKS = 12;  // 1 KB wave chunks per wave in the shared area (96 KB)
 constexpr int DOWN_CHUNKS = 12;   // 16-byte chunks per lane of an expert task's down-projection tile
 
+// Attention: register page buffers per wave, and the page ids of a split
+// that are read ahead with its staged pages.
+constexpr int ATT_NBUF = 4;
+constexpr int ATT_IDS = NWAVE * ATT_NBUF;
+
 struct Smem {
   float vec[LDS_VEC];  // gathered input vector(s), normalised in place
   union {
@@ -63,6 +68,7 @@ struct Smem {
   int fail;
   int kv_ti;                 // task index of the attention split whose pages are staged (-1: none)
   int kv_ok[NWAVE];          // wave w's staged page is valid
+  int kv_ids[ATT_IDS + 1];   // its first ATT_IDS page ids, then the sequence's position
   uint32_t qnext;      // attention queue: the split this workgroup takes next
   uint64_t tw[4];      // trace: (begin, end) of the routing wait and of the data wait
   uint64_t mk[TRACE_MARKS];  // trace: body-specific marks
@@ -663,6 +669,13 @@ __device__ __forceinline__ void stage_kv(Ctx& c, const Task& ta, uint32_t ti_a) 
       for (int i = 0; i < D / 16; ++i) dma16(src + 64 * i, lds_addr(dst + 64 * i));
     }
   }
+  // the ids of the split's first ATT_IDS pages and the position, so that the
+  // split issues its page loads without a page-table round trip
+  if (w == 0) {
+    const int32_t* prow = a.page_table + (size_t)b * a.max_pages + pg0;
+    if (lane < min(npg, ATT_IDS)) dma4(prow + lane, lds_addr(s.kv_ids));
+    else if (lane == ATT_IDS) dma4(a.seq_lens + b, lds_addr(s.kv_ids));
+  }
   if (lane == 0) s.kv_ok[w] = ok ? 1 : 0;
   if (tid() == 0) s.kv_ti = (int)ti_a;
 }
@@ -684,16 +697,22 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   // are read directly, together with the position; the ids of every page of
   // the task go to an LDS table for the rest, so a refill never waits on a
   // page-table load (the plan maps every page below its bound).
-  constexpr int NBUF = 4;
+  constexpr int NBUF = ATT_NBUF;
   const int first = pg0 + w;
+  // ids and position read ahead by stage_kv (in LDS since the staging task's
+  // first wait for its loads), else from memory
+  const bool pre = s.kv_ti == (int)c.ti;
   int32_t ph[NBUF];
 #pragma unroll
-  for (int j = 0; j < NBUF; ++j) ph[j] = first + j * NWAVE < pg0 + npg ? prow[first + j * NWAVE] : -1;
-  const int pos = a.seq_lens[b];
+  for (int j = 0; j < NBUF; ++j)
+    ph[j] = first + j * NWAVE < pg0 + npg ? (pre ? s.kv_ids[w + j * NWAVE] : prow[first + j * NWAVE]) : -1;
+  const int pos = pre ? s.kv_ids[ATT_IDS] : a.seq_lens[b];
+  // the id table for refills (pages past each wave's first NBUF)
+  const bool refill = npg > NWAVE * NBUF;
   int* pid = (int*)s.res;  // [npg]
   int32_t tbl[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) tbl[j] = tid() + j * NT < npg ? prow[pg0 + tid() + j * NT] : -1;
+  for (int j = 0; j < 2; ++j) tbl[j] = refill && tid() + j * NT < npg ? prow[pg0 + tid() + j * NT] : -1;
   const int n_tok = min(pos + 1, a.bound);
   const int pg_lim = min(pg0 + npg, (n_tok + 15) >> 4);
   const int cnt = first < pg_lim ? (pg_lim - first + NWAVE - 1) / NWAVE : 0;
@@ -726,10 +745,10 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     }
   };
   // this wave's first page may have been staged in LDS by an earlier task of
-  // this unit (stage_kv); the wait covers the transfer, issued two tasks ago
-  const bool staged = cnt > 0 && s.kv_ti == (int)c.ti && s.kv_ok[w];
+  // this unit (stage_kv): that task waited for loads it issued after the
+  // transfer, so the page has landed
+  const bool staged = cnt > 0 && pre && s.kv_ok[w];
   if (staged) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const uint4* sp = staged_page<D>(s, w) + lane;
 #pragma unroll
     for (int i = 0; i < NK4; ++i) kb[0][i] = sp[64 * i];
@@ -743,9 +762,10 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
 #pragma unroll
   for (int j = 0; j < NBUF; ++j)
     if (j < cnt && !(j == 0 && staged)) load(kb[j], vb[j], first + j * NWAVE, ph[j]);
+  if (refill)
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    if (tid() + j * NT < npg) pid[tid() + j * NT] = tbl[j];
+    for (int j = 0; j < 2; ++j)
+      if (tid() + j * NT < npg) pid[tid() + j * NT] = tbl[j];
 
   // inputs: the group's queries and the new token's K and V (bf16 bits), one batch
   float* qv = s.vec;                 // [HG][D]

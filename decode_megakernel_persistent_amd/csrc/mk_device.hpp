@@ -61,6 +61,11 @@ __device__ __forceinline__ uint2 ld_nt2(const uint2* p) {
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
   asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
+// Direct-to-LDS load of 4 bytes per lane: lane i's word lands at LDS byte
+// address lds_base + 4 * i (lds_base wave-uniform); same waiting rule.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)p;
 }
