@@ -22,6 +22,7 @@
 // then LM (rows of the LM head, local argmax) and FINAL (argmax merge).
 #include <algorithm>
 #include <array>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <numeric>
@@ -29,6 +30,7 @@
 #include <set>
 #include <string>
 #include <tuple>
+#include <queue>
 #include <vector>
 
 #include "mk.h"
@@ -439,6 +441,29 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   }
   p->n_split.assign(B, 0);
   for (int b = 0; b < B; ++b) p->n_split[b] = (pages_b[b] + pps - 1) / pps;
+  if (batch && !(o && o->attn_split_pages > 0) && pg_total > 0) {
+    // a batch: 4 n_cu splits in all, each sequence's share in proportion to
+    // its pages (largest remainders), so that the splits are about equal and
+    // come out at four per unit; at least one split per sequence, at least 8
+    // and at most NT pages per split
+    const int64_t T = std::max<int64_t>(B, 4LL * n_cu / std::max(1, Hkv));
+    int64_t tot = 0;
+    for (int b = 0; b < B; ++b) tot += pages_b[b];
+    std::vector<std::pair<double, int>> rem;
+    int64_t given = 0;
+    for (int b = 0; b < B; ++b) {
+      const double q = (double)pages_b[b] * (double)T / (double)std::max<int64_t>(1, tot);
+      p->n_split[b] = std::max(1, (int)q);
+      given += p->n_split[b];
+      rem.push_back({q - std::floor(q), b});
+    }
+    std::stable_sort(rem.begin(), rem.end(), [](auto& x, auto& y) { return x.first > y.first; });
+    for (size_t i = 0; i < rem.size() && given < T; ++i, ++given) p->n_split[rem[i].second]++;
+    for (int b = 0; b < B; ++b) {
+      const int lo = std::max(1, ceil_div(pages_b[b], mk::NT)), hi = std::max(1, ceil_div(pages_b[b], 8));
+      p->n_split[b] = std::min(std::max(p->n_split[b], lo), std::max(lo, hi));
+    }
+  }
   p->S_max = *std::max_element(p->n_split.begin(), p->n_split.end());
   p->comb_dim_tasks = std::max(1, std::min(D / 8, n_cu / std::max(1, B * Hq)));
   while (p->comb_dim_tasks < D / 8 && (size_t)p->S_max * (ceil_div(D, p->comb_dim_tasks) + 2) > 8192)
@@ -629,17 +654,37 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       return fail(MK_EUNSUPPORTED, "mk_plan: counter with 0 or > 65535 producers");
     }
 
-  // deal every stage round-robin over the units, continuing where the last stage ended
+  // deal every stage round-robin over the units, continuing where the last
+  // stage ended. A batch's attention stage (splits of ragged sequences, more
+  // than one per unit, longest first) goes by pages instead: each split to
+  // the unit with the fewest pages of this stage so far (ties in round-robin
+  // order), so that no unit streams a fifth split while the others are done.
   p->lists.assign(n_cu, {});
   std::vector<std::vector<int>> stage_lists(n_cu);
   int cursor = 0;
   for (int s0 = 0; s0 < (int)stages.size(); ++s0) {
-    for (size_t i = 0; i < stages[s0].size(); ++i) {
-      int cu = (cursor + (int)i) % n_cu;
-      p->lists[cu].push_back(stages[s0][i]);
-      stage_lists[cu].push_back(s0);
+    const auto& st = stages[s0];
+    const bool by_pages = batch && !st.empty() && st[0].op == mk::OP_ATTN && (int)st.size() > n_cu;
+    if (by_pages) {
+      using Load = std::pair<int64_t, int>;  // (pages so far, round-robin rank)
+      std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+      for (int r = 0; r < n_cu; ++r) heap.push({0, r});
+      for (const Task& t : st) {
+        auto [pages, r] = heap.top();
+        heap.pop();
+        const int cu = (cursor + r) % n_cu;
+        p->lists[cu].push_back(t);
+        stage_lists[cu].push_back(s0);
+        heap.push({pages + t.a3, r});
+      }
+    } else {
+      for (size_t i = 0; i < st.size(); ++i) {
+        int cu = (cursor + (int)i) % n_cu;
+        p->lists[cu].push_back(st[i]);
+        stage_lists[cu].push_back(s0);
+      }
     }
-    cursor = (cursor + (int)stages[s0].size()) % n_cu;
+    cursor = (cursor + (int)st.size()) % n_cu;
   }
   // batch 1, static splits: a unit's expert task of layer l first stages the
   // first pages of the unit's next attention split (of layer l + 1, at most
