@@ -294,6 +294,71 @@ __device__ __forceinline__ bool gather_split(Ctx& c, const uint64_t* src, int n,
   return c.s.fail == 0;
 }
 
+struct IdentIdx {
+  __device__ __forceinline__ int operator()(int i) const { return i; }
+};
+
+// Gather n tagged words, word i at addr(i), into dst[di(i)] (LDS); uniform result.
+template <int MAXW, class Addr, class DstIdx = IdentIdx>
+__device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float* dst, int which,
+                                          const DstIdx& di = DstIdx()) {
+  KAC& a = c.a;
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
+  bool ok = true;
+  for (int base = 0; base < n && ok; base += MAXW * NT) {
+    const int t = tid();
+    float v[MAXW];
+    ok = read_words<MAXW>(a, [&](int k) -> const uint64_t* {
+      const int i = base + t + k * NT;
+      return i < n ? addr(i) : nullptr;
+    }, v, c.t0, c.ti);
+    if (ok) {
+#pragma unroll
+      for (int k = 0; k < MAXW; ++k) {
+        const int i = base + t + k * NT;
+        if (i < n) dst[di(i)] = v[k];
+      }
+    }
+  }
+  if (!ok) c.s.fail = 1;
+  lds_barrier();
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
+  return c.s.fail == 0;
+}
+
+// gather_fn reading word pairs (i, i + 1), i even, with one 16-byte load:
+// for the caller, n is even and, for every even i, addr(i) (nullptr: none) is
+// a word at an even workspace word offset followed by word i + 1, and
+// di(i + 1) = di(i) + 1 with di(i) even. Uniform result.
+template <int MAXW, class Addr, class DstIdx = IdentIdx>
+__device__ __forceinline__ bool gather_fn_pairs(Ctx& c, int n, const Addr& addr, float* dst, int which,
+                                                const DstIdx& di = DstIdx()) {
+  KAC& a = c.a;
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
+  constexpr int MAXP = (MAXW + 1) / 2;
+  bool ok = true;
+  for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
+    const int t = tid();
+    float v[2 * MAXP];
+    ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
+      const int i = base + 2 * (t + k * NT);
+      const uint64_t* p = i < n ? addr(i) : nullptr;
+      return p ? ws_off(a, p) : NO_PAIR;
+    }, v, c.t0, c.ti);
+    if (ok) {
+#pragma unroll
+      for (int k = 0; k < MAXP; ++k) {
+        const int i = base + 2 * (t + k * NT);
+        if (i < n) *(float2*)(dst + di(i)) = make_float2(v[2 * k], v[2 * k + 1]);
+      }
+    }
+  }
+  if (!ok) c.s.fail = 1;
+  lds_barrier();
+  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
+  return c.s.fail == 0;
+}
+
 // Norm gains of chunk tid (elements 8*tid .. 8*tid+7) of a vector of K <=
 // 8*NT elements, loaded ahead of a task's wait.
 struct Gains {
@@ -1418,6 +1483,7 @@ struct MtLds {
   float red[NWAVE][2][4][64];          // k-split partial accumulators
   float ss[NT];                        // sum-of-squares partials
   float scale[MAX_BATCH];              // per-sequence norm scale
+  float ssum[MAX_BATCH];               // per-sequence sum of squares of the tile's inputs
   float out[MT_MAX_BLOCKS * 16][MAX_BATCH];  // finished tile: [row][sequence]
 };
 static_assert(sizeof(MtLds) <= sizeof(float) * LDS_VEC + sizeof(uint4) * NWAVE * STAGE_CHUNKS * 64,
@@ -1432,6 +1498,7 @@ struct MtSrc {
   int64_t ld;
   const uint16_t* gain;
   bool norm;
+  int k0 = 0;  // embedding rows: first column read (rows of ld elements)
 };
 
 // out[r][b] = sum_k W[row r][k] * x_b[k] (normalised per MtSrc) for r < R <=
@@ -1474,7 +1541,7 @@ __device__ __forceinline__ bool mt_tile(Ctx& c, int R, int K, const RowPtr& rowp
   const tag_rsrc rx = tagged_rsrc(xw ? src.words : (const uint64_t*)a.embed,
                                   xw ? (uint32_t)(((size_t)(B - 1) * src.ld + K) * 8) : 0u);
   const uint32_t xoff = (uint32_t)(((size_t)sq * src.ld + kl) * 8);
-  const uint16_t* xe = xw ? nullptr : a.embed + (size_t)token_row(a, sq) * K + kl;
+  const uint16_t* xe = xw ? nullptr : a.embed + (size_t)token_row(a, sq) * src.ld + src.k0 + kl;
   float ss = 0.f;
   struct ActRegs { uint4 v[8]; uint32_t e[8]; uint32_t g[8]; };
   auto issue_act = [&](int p, ActRegs& r) {
@@ -1595,6 +1662,7 @@ __device__ __forceinline__ bool mt_tile(Ctx& c, int R, int K, const RowPtr& rowp
 #pragma unroll
       for (int j = 0; j < 4; ++j) tot += P.ss[(2 * q + cb) * 64 + 4 * s16 + j];
     P.scale[t] = src.norm ? 1.0f / sqrtf(tot / (float)K + a.eps) : 1.f;
+    P.ssum[t] = tot;
   }
   lds_barrier();
   if (active && kp == 0) {
@@ -1625,16 +1693,58 @@ __device__ __forceinline__ bool task_bqkv(Ctx& c, const Task& t) {
   const int l = t.layer, g = t.a0, p0 = t.a1, np = t.a2, H = a.H, D = a.D;
   const int QR = (a.Hq + 2 * a.Hkv) * D;
   const uint16_t* W = a.wqkv + (size_t)l * QR * H;
-  MtSrc src{l == 0 ? nullptr : a.x + (size_t)(l - 1) * a.s_x, H, a.attn_norm + (size_t)l * H, true};
+  // reduction block kb of KB over the hidden state (KB = 1: the whole row)
+  const int kb = t.a3 & 0xFF, KB = max(1, t.a3 >> 8), Kb = H / KB, k0 = kb * Kb;
+  MtSrc src{l == 0 ? nullptr : a.x + (size_t)(l - 1) * a.s_x + k0, H, a.attn_norm + (size_t)l * H + k0,
+            KB == 1, k0};
   if (a.trace && tid() == 0) c.s.tw[2] = now();
-  if (!mt_tile(c, 2 * np, H, [&](int j) {
+  if (!mt_tile(c, 2 * np, Kb, [&](int j) {
         int head, i, row;
         qkv_pair(p0 + (j >> 1), g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
-        return W + (size_t)(row + (j & 1) * (D / 2)) * H;
+        return W + (size_t)(row + (j & 1) * (D / 2)) * H + k0;
       }, src))
     return false;
   if (a.trace && tid() == 0) c.s.tw[3] = now();
-  const MtLds& P = *(const MtLds*)&c.s;
+  MtLds& P = *(MtLds*)&c.s;
+  if (KB > 1) {
+    // partial record of (block kb, row block rb, sequence b): the rows, the
+    // sum of squares of this block's inputs, a pad word
+    const int nrb_g = ((a.HG * D + 2 * D) / 2 + BQKV_PAIRS - 1) / BQKV_PAIRS;
+    const int nrb = a.Hkv * nrb_g, rb = g * nrb_g + p0 / BQKV_PAIRS;
+    const int W2 = 2 * np + 2;
+    uint64_t* qp = a.qpart + (size_t)l * a.s_qpart;
+    auto rec = [&](int q, int b) { return qp + (((size_t)q * nrb + rb) * a.B + b) * QPART_STRIDE; };
+    if (kb > 0) {
+      for (int idx = tid(); idx < a.B * W2; idx += NT) {
+        const int b = idx / W2, r = idx - b * W2;
+        const float v = r < 2 * np ? P.out[r][b] : (r == 2 * np ? P.ssum[b] : 0.f);
+        st_tagged(rec(kb - 1, b) + r, v, a.epoch);
+      }
+      return true;
+    }
+    // block 0: add the other blocks' partial rows and sums of squares (in
+    // block order), then normalise; the tile's panel area is free by now
+    float* red = (float*)P.hi;  // word (q, b, r) at red[(q * B + b) * W2 + r]
+    const int bw = a.B * W2;
+    if (!gather_fn_pairs<8>(c, (KB - 1) * bw, [&](int i) {
+          const int q = i / bw, rem = i - q * bw, b = rem / W2;
+          return rec(q, b) + (rem - b * W2);
+        }, red, 0))
+      return false;
+    if (tid() < a.B) {
+      float ss = P.ssum[tid()];
+      for (int q = 0; q < KB - 1; ++q) ss += red[(q * a.B + tid()) * W2 + 2 * np];
+      P.scale[tid()] = 1.0f / sqrtf(ss / (float)H + a.eps);
+    }
+    lds_barrier();
+    for (int idx = tid(); idx < 2 * np * a.B; idx += NT) {
+      const int r = idx / a.B, b = idx - r * a.B;
+      float y = P.out[r][b];
+      for (int q = 0; q < KB - 1; ++q) y += red[(q * a.B + b) * W2 + r];
+      P.out[r][b] = y * P.scale[b];
+    }
+    lds_barrier();
+  }
   for (int idx = tid(); idx < np * a.B; idx += NT) {
     const int q = idx / a.B, b = idx - q * a.B;
     const int pos = a.seq_lens[b];
@@ -1676,71 +1786,6 @@ __device__ __forceinline__ bool task_bqkv(Ctx& c, const Task& t) {
     }
   }
   return true;
-}
-
-struct IdentIdx {
-  __device__ __forceinline__ int operator()(int i) const { return i; }
-};
-
-// Gather n tagged words, word i at addr(i), into dst[di(i)] (LDS); uniform result.
-template <int MAXW, class Addr, class DstIdx = IdentIdx>
-__device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float* dst, int which,
-                                          const DstIdx& di = DstIdx()) {
-  KAC& a = c.a;
-  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
-  bool ok = true;
-  for (int base = 0; base < n && ok; base += MAXW * NT) {
-    const int t = tid();
-    float v[MAXW];
-    ok = read_words<MAXW>(a, [&](int k) -> const uint64_t* {
-      const int i = base + t + k * NT;
-      return i < n ? addr(i) : nullptr;
-    }, v, c.t0, c.ti);
-    if (ok) {
-#pragma unroll
-      for (int k = 0; k < MAXW; ++k) {
-        const int i = base + t + k * NT;
-        if (i < n) dst[di(i)] = v[k];
-      }
-    }
-  }
-  if (!ok) c.s.fail = 1;
-  lds_barrier();
-  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
-  return c.s.fail == 0;
-}
-
-// gather_fn reading word pairs (i, i + 1), i even, with one 16-byte load:
-// for the caller, n is even and, for every even i, addr(i) (nullptr: none) is
-// a word at an even workspace word offset followed by word i + 1, and
-// di(i + 1) = di(i) + 1 with di(i) even. Uniform result.
-template <int MAXW, class Addr, class DstIdx = IdentIdx>
-__device__ __forceinline__ bool gather_fn_pairs(Ctx& c, int n, const Addr& addr, float* dst, int which,
-                                                const DstIdx& di = DstIdx()) {
-  KAC& a = c.a;
-  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
-  constexpr int MAXP = (MAXW + 1) / 2;
-  bool ok = true;
-  for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
-    const int t = tid();
-    float v[2 * MAXP];
-    ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
-      const int i = base + 2 * (t + k * NT);
-      const uint64_t* p = i < n ? addr(i) : nullptr;
-      return p ? ws_off(a, p) : NO_PAIR;
-    }, v, c.t0, c.ti);
-    if (ok) {
-#pragma unroll
-      for (int k = 0; k < MAXP; ++k) {
-        const int i = base + 2 * (t + k * NT);
-        if (i < n) *(float2*)(dst + di(i)) = make_float2(v[2 * k], v[2 * k + 1]);
-      }
-    }
-  }
-  if (!ok) c.s.fail = 1;
-  lds_barrier();
-  if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which + 1] = now();
-  return c.s.fail == 0;
 }
 
 // W_o rows of every sequence over reduction block kb (a0) of the a3 blocks
@@ -2356,6 +2401,7 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
   a.part = buf(MK_BUF_PART); a.o = buf(MK_BUF_O); a.rlog = buf(MK_BUF_RLOG); a.act = buf(MK_BUF_ACT);
   a.lmpart = buf(MK_BUF_LMPART); a.route = buf(MK_BUF_ROUTE); a.y = buf(MK_BUF_Y);
   a.opart = buf(MK_BUF_OPART); a.s_opart = words(MK_BUF_OPART);
+  a.qpart = buf(MK_BUF_QPART); a.s_qpart = words(MK_BUF_QPART);
   a.s_x = words(MK_BUF_XFFN); a.s_q = words(MK_BUF_Q); a.s_kvn = words(MK_BUF_KVN);
   a.s_part = words(MK_BUF_PART); a.s_o = words(MK_BUF_O); a.s_rlog = words(MK_BUF_RLOG);
   a.s_act = words(MK_BUF_ACT); a.s_route = words(MK_BUF_ROUTE); a.s_y = words(MK_BUF_Y);

@@ -52,6 +52,12 @@ enum Op : uint8_t {
 // tasks further on in the same list) into LDS.
 enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4 };
 
+// Batch QKV tasks: rotary pairs per row block (the rows of a block are 2
+// BQKV_PAIRS), and the words per (reduction block, row block, sequence) of
+// a partial QKV projection: the rows, the sum of squares, a pad word.
+constexpr int BQKV_PAIRS = 32;
+constexpr int QPART_STRIDE = 2 * BQKV_PAIRS + 2;
+
 // Attention pages staged ahead of their split: one per wave.
 constexpr int STAGE_PAGES = 8;
 constexpr int STAGE_SCAN = 8;
@@ -222,10 +228,10 @@ struct KArgs {
   //  lmpart [n_lm][B][2] (value, index)
   //  batch only: route [L][B][K][2] (expert id bits, weight) per selected slot,
   //  y [L][B][K][H] expert outputs
-  uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart, *route, *y, *opart;
+  uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart, *route, *y, *opart, *qpart;
   const uint64_t* ws;  // the workspace holding all of them (256-byte aligned)
   uint32_t ws_bytes;   // its size (under 4 GiB)
-  int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act, s_route, s_y, s_opart;
+  int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act, s_route, s_y, s_opart, s_qpart;
   const int32_t* seq_bound;  // [B] context bound per sequence (in the plan image)
   int32_t S_max, n_lm;
   // plan and sync

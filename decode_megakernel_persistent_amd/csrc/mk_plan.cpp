@@ -92,6 +92,8 @@ std::vector<std::pair<int, int>> split_units(int n, int u, int t) {
 // Row blocks (16 rows) per task of the MFMA batch projections: a task
 // gathers every sequence's input once, so tasks are a few row blocks each.
 constexpr int QKV_BLOCKS = 4, O_BLOCKS = 4, LM_BLOCKS = mk::MT_MAX_BLOCKS;
+static_assert(8 * QKV_BLOCKS == mk::BQKV_PAIRS && mk::QPART_STRIDE == 2 * 8 * QKV_BLOCKS + 2,
+              "batch QKV row blocks as the kernel reads their partial sums");
 // words the reducing O task gathers into LDS (partials and residual)
 constexpr int O_RED_WORDS = 16384;
 
@@ -129,17 +131,27 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
     return fail(MK_EUNSUPPORTED, "mk_plan: batch expert tiles exceed LDS (hidden and FFN <= 2048, "
                                  "rows per expert task <= 1024): use more compute units");
   for (int l = 0; l < L; ++l) {
-    {  // BQKV: 8 rotary pairs per row block
-      std::vector<Task> st;
-      for (int g = 0; g < Hkv; ++g)
-        for (int s0 = 0; s0 < p->n_pairs_g; s0 += 8 * QKV_BLOCKS) {
-          Task t = mk_task(mk::OP_BQKV, l);
-          t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_bcomb[l - 1]);
-          t.signal = ctr16(p->c_qkv[l * Hkv + g]);
-          t.a0 = g; t.a1 = s0; t.a2 = std::min(8 * QKV_BLOCKS, p->n_pairs_g - s0);
-          st.push_back(t);
-        }
-      stages.push_back(st);
+    {  // BQKV: 8 QKV_BLOCKS rotary pairs per row block, split over q_kb blocks
+       // of the reduction: blocks 1 .. q_kb-1 publish partial sums (and
+       // their sums of squares), then block 0 adds them, normalises, rotates
+       // and appends
+      const int KB = p->q_kb;
+      for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 0 && KB == 1) continue;
+        std::vector<Task> st;
+        for (int g = 0; g < Hkv; ++g)
+          for (int s0 = 0; s0 < p->n_pairs_g; s0 += 8 * QKV_BLOCKS)
+            for (int kb = pass == 0 ? 1 : 0; kb < (pass == 0 ? KB : 1); ++kb) {
+              Task t = mk_task(mk::OP_BQKV, l);
+              t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_bcomb[l - 1]);
+              if (pass == 1 && KB > 1) t.wait_a = ctr16(p->c_qpart[l]);
+              t.signal = ctr16(pass == 0 ? p->c_qpart[l] : p->c_qkv[l * Hkv + g]);
+              t.a0 = g; t.a1 = s0; t.a2 = std::min(8 * QKV_BLOCKS, p->n_pairs_g - s0);
+              t.a3 = kb | (KB << 8);
+              st.push_back(t);
+            }
+        stages.push_back(st);
+      }
     }
     {  // ATTN
       std::vector<Task> st;
@@ -371,6 +383,13 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     while (npan % (2 * kb) == 0 && n_rb * 2 * kb <= n_cu && 2 * kb * B * 16 * O_BLOCKS <= O_RED_WORDS)
       kb *= 2;
     p->o_kb = kb;
+    // QKV projection: the same over the hidden state, while the reducing
+    // task's words (partial rows and sums of squares) fit its gather area
+    const int RS = 2 * 8 * QKV_BLOCKS + 2, npq = H / mk::MT_KP;
+    p->q_rb = Hkv * ceil_div(p->n_pairs_g, 8 * QKV_BLOCKS);
+    int qk = 1;
+    while (npq % (2 * qk) == 0 && p->q_rb * 2 * qk <= n_cu && (2 * qk - 1) * B * RS <= O_RED_WORDS) qk *= 2;
+    p->q_kb = qk;
   }
   const int HG = p->HG, K = moe ? m->top_k : 1;
 
@@ -408,6 +427,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       p->c_comb.push_back(new_ctr("comb[" + ls + "]"));
       p->c_o.push_back(new_ctr("o[" + ls + "]"));
       p->c_opart.push_back(p->o_kb > 1 ? new_ctr("opart[" + ls + "]") : -1);
+      p->c_qpart.push_back(p->q_kb > 1 ? new_ctr("qpart[" + ls + "]") : -1);
       p->c_router.push_back(-1);
       p->c_topk.push_back(moe ? new_ctr("topk[" + ls + "]") : -1);
       p->c_expert.push_back(new_ctr("expert[" + ls + "]"));
@@ -720,7 +740,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         (size_t)B * Hkv * 2 * D,                          // KVN
         batch && moe ? (size_t)B * K * 2 : 0,             // ROUTE
         batch ? (size_t)B * K * H : 0,                    // Y
-        batch ? (size_t)(p->o_kb - 1) * B * H : 0};       // OPART
+        batch ? (size_t)(p->o_kb - 1) * B * H : 0,        // OPART
+        batch ? (size_t)(p->q_kb - 1) * p->q_rb * B * (2 * 8 * QKV_BLOCKS + 2) : 0};  // QPART
     size_t off = 0;
     for (int i = 0; i < mk_plan::N_BUF; ++i) {
       p->ws_off[i] = off;
@@ -777,7 +798,8 @@ void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::
   const std::string ls = ":" + std::to_string(t.layer);
   switch (t.op) {
     case mk::OP_QKV:
-    case mk::OP_BQKV:
+    case mk::OP_BQKV:  // the partial sums of blocks 1 .. kb-1 end in block 0's rows
+      if ((t.a3 & 0xFF) != 0) break;
       for (int q = t.a1; q < t.a1 + t.a2; ++q) {
         int head, i, row;
         mk::qkv_pair(q, t.a0, p->HG, D, Hq, Hkv, &head, &i, &row);

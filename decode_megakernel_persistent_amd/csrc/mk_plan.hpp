@@ -28,6 +28,9 @@ struct mk_plan {
   std::vector<int32_t> c_topk, c_bcomb;  // [L] batch: top-k per sequence, expert combine
   std::vector<int32_t> c_opart;          // [L] batch: partial O projections (-1: not split)
   int o_kb = 1;                          // batch: reduction blocks of the O projection
+  std::vector<int32_t> c_qpart;          // [L] batch: partial QKV projections (-1: not split)
+  int q_kb = 1;                          // batch: reduction blocks of the QKV projection
+  int q_rb = 0;                          // batch: QKV row blocks (tasks per reduction block)
   int32_t c_lm = -1;
   bool attn_queue = false;
 
@@ -38,7 +41,7 @@ struct mk_plan {
   int32_t n_lm = 0, n_stages = 0;
 
   // workspace layout: base offset (bytes) and per-layer stride (bytes) per MK_BUF_*
-  static constexpr int N_BUF = 12;
+  static constexpr int N_BUF = 13;
   size_t ws_off[N_BUF] = {}, ws_stride[N_BUF] = {}, ws_layer_bytes[N_BUF] = {};
   int32_t n_exp_parts = 1;          // batch: expert tasks per expert
   size_t ws_total = 0;

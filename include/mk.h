@@ -233,10 +233,14 @@ mk_status mk_plan_upload(const mk_plan_t* p, void* d_plan, size_t bytes, void* h
  *   ROUTE [B][top_k][2] selected expert id (int bits) and weight per slot,
  *   Y [B][top_k][H] each selected expert's down-projection output,
  *   OPART [kb - 1][B][H] partial O projections over reduction blocks 1 .. kb-1
- *   (the O projection is split over kb blocks of the attention output). */
+ *   (the O projection is split over kb blocks of the attention output),
+ *   QPART [qkb - 1][row blocks][B][rows + 2] partial QKV projections over
+ *   reduction blocks 1 .. qkb-1 of the hidden state, per row block of the
+ *   QKV tasks: the block's rows, then the block's sum of squares of the
+ *   hidden state (for the RMSNorm), then a zero pad word. */
 enum { MK_BUF_XATTN = 0, MK_BUF_XFFN = 1, MK_BUF_Q = 2, MK_BUF_PART = 3, MK_BUF_O = 4,
        MK_BUF_RLOG = 5, MK_BUF_ACT = 6, MK_BUF_LMPART = 7, MK_BUF_KVN = 8,
-       MK_BUF_ROUTE = 9, MK_BUF_Y = 10, MK_BUF_OPART = 11 };
+       MK_BUF_ROUTE = 9, MK_BUF_Y = 10, MK_BUF_OPART = 11, MK_BUF_QPART = 12 };
 mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t layer, size_t* offset,
                          size_t* bytes);
 /* The plan's per-epoch counter targets, [n_counters] (host). */

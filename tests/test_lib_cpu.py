@@ -146,6 +146,7 @@ def plan_coverage(tasks, m, bound):
     pg_bound = -(-bound // m["page_tokens"])
 
     o_blocks = {}
+    q_blocks = {}
 
     def add(key, items):
         S.setdefault(key, []).extend(items)
@@ -153,8 +154,14 @@ def plan_coverage(tasks, m, bound):
     for t in tasks:
         op, l = int(t["op"]), int(t["layer"])
         a0, a1, a2, a3, aux = int(t["a0"]), int(t["a1"]), int(t["a2"]), int(t["a3"]), int(t["aux"])
-        if op in (OP_QKV, OP_BQKV):
+        if op == OP_QKV:
             add(("qkv", l), [r for p in range(a1, a1 + a2) for r in qkv_rows(p, a0, m)])
+        elif op == OP_BQKV:
+            # reduction block a3 & 0xFF of a3 >> 8: block 0 finishes the rows
+            # (its own partial sum plus those of blocks 1 ..)
+            if a3 & 0xFF == 0:
+                add(("qkv", l), [r for p in range(a1, a1 + a2) for r in qkv_rows(p, a0, m)])
+            q_blocks.setdefault((l, a0, a1, a2, max(a3 >> 8, 1)), []).append(a3 & 0xFF)
         elif op == OP_BO:
             # reduction block a0 of a3: block 0 finishes rows a1 .. a1 + a2
             # (its own partial sum plus those of blocks 1 .. a3-1)
@@ -197,6 +204,8 @@ def plan_coverage(tasks, m, bound):
             add(("lm",), list(range(a1, a1 + a2)))
     for (l, a1, a2, kb), blocks in o_blocks.items():
         assert sorted(blocks) == list(range(kb)), f"o rows {a1}+{a2} of layer {l}: blocks {blocks}"
+    for (l, g, a1, a2, kb), blocks in q_blocks.items():
+        assert sorted(blocks) == list(range(kb)), f"qkv pairs {a1}+{a2} of group {g}, layer {l}: blocks {blocks}"
     return S
 
 
