@@ -276,6 +276,39 @@ def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
         mk.mk_pool_free(pool)
 
 
+@pytest.mark.parametrize("name,n_cu,tight", [("moe48_b32_ragged", 256, True), ("small_moe_b32", 256, False),
+                                             ("small_moe_b5", 40, False)])
+def test_batch_attention_splits_are_balanced(name, n_cu, tight):
+    # every sequence gets a share of 4 n_cu / Hkv splits in proportion to its
+    # pages (at least one), each split goes to the unit with the fewest pages
+    # so far: no unit is more than one split's pages above another
+    w, pool, p, bound = build_plan(name, n_cu)
+    try:
+        n_cu2, n_ctr, cu_off, tasks = decode_plan(mk.mk_plan_export(p))
+        cu_of = np.searchsorted(np.asarray(cu_off), np.arange(len(tasks)), side="right") - 1
+        m = w["model"]
+        hkv, B = m["n_kv_heads"], w["batch"]
+        for l in (0, m["n_layers"] - 1):
+            sel = np.where((tasks["op"] == OP_ATTN) & (tasks["layer"] == l))[0]
+            per_b = np.bincount(tasks["a0"][sel].astype(np.int64), minlength=B) // hkv
+            pages_b = np.array([-(-c // m["page_tokens"]) for c in ctx_bounds(w)])
+            cap = np.maximum(1, -(-pages_b // 8))  # splits of at least 8 pages
+            T = max(B, 4 * n_cu // hkv)
+            floor_share = np.minimum(cap, np.maximum(1, pages_b * T // pages_b.sum()))
+            assert (per_b >= 1).all() and (per_b <= cap).all()
+            assert per_b.sum() >= min(T, floor_share.sum())
+            pages = np.bincount(cu_of[sel], weights=tasks["a3"][sel].astype(np.float64), minlength=n_cu)
+            biggest = int(tasks["a3"][sel].max())
+            busy = pages[pages > 0]
+            assert busy.max() - busy.min() <= biggest
+            if tight:  # long ragged contexts: four splits on every unit, pages within 5 %
+                assert (np.bincount(cu_of[sel], minlength=n_cu) == 4).all()
+                assert busy.max() <= 1.05 * pages.sum() / n_cu
+    finally:
+        mk.mk_plan_free(p)
+        mk.mk_pool_free(pool)
+
+
 def test_plan_is_deterministic():
     w, pool, p1, bound = build_plan("small_moe")
     _, pool2, p2, _ = build_plan("small_moe")
