@@ -1180,18 +1180,18 @@ template <int CPL, int TC>
 __device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
   constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
   KAC& a = c.a;
-  const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H;
+  const int l = t.layer, b = t.a0, r0 = t.a1, n = t.a2, H = a.H;
   const uint16_t* W = a.router + (size_t)l * a.E * H;
   Tile<CPL, RPW, TC> tile;
   tile.issue(n, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
   Gains gn;
   gn.load(a.ffn_norm + (size_t)l * H, H);
-  if (!gather<4>(c, a.xa + (size_t)l * a.s_x, H, c.s.vec, 1, H)) return false;
+  if (!gather<4>(c, a.xa + (size_t)l * a.s_x + (size_t)b * H, H, c.s.vec, 1, H)) return false;
   norm_pack(c, c.s.vec, H, gn);
   tile.dots(c.s.vec, c.s.out);
   lds_barrier();
   for (int j = tid(); j < n; j += NT)
-    st_tagged(a.rlog + (size_t)l * a.s_rlog + r0 + j, c.s.out[j], a.epoch);
+    st_tagged(a.rlog + (size_t)l * a.s_rlog + (size_t)b * a.E + r0 + j, c.s.out[j], a.epoch);
   return true;
 }
 
@@ -1844,23 +1844,29 @@ __device__ __forceinline__ bool task_topk(Ctx& c, const Task& t) {
   KAC& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, H = a.H, E = a.E;
-  const uint16_t* W = a.router + (size_t)l * E * H;
-  Tile<CPL, RPW, TC> tile;
-  tile.issue(min(CAP, E), [&](int j) { return (const uint4*)(W + (size_t)j * H); });
-  Gains gn;
-  gn.load(a.ffn_norm + (size_t)l * H, H);
-  if (!gather<4>(c, a.xa + (size_t)l * a.s_x + (size_t)b * H, H, s.vec, 1)) return false;
-  rmsnorm_pack(c, s.vec, H, gn);
-  tile.dots(s.vec, s.out);
-  for (int r0 = CAP; r0 < E; r0 += CAP) {
-    tile.issue(min(CAP, E - r0), [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
-    tile.dots(s.vec, s.out + r0);
+  const bool read = (t.flags & TF_LOGITS) != 0;  // the router tasks computed the logits
+  if (read) {
+    if (!gather<4>(c, a.rlog + (size_t)l * a.s_rlog + (size_t)b * E, E, s.out, 1)) return false;
+  } else {
+    const uint16_t* W = a.router + (size_t)l * E * H;
+    Tile<CPL, RPW, TC> tile;
+    tile.issue(min(CAP, E), [&](int j) { return (const uint4*)(W + (size_t)j * H); });
+    Gains gn;
+    gn.load(a.ffn_norm + (size_t)l * H, H);
+    if (!gather<4>(c, a.xa + (size_t)l * a.s_x + (size_t)b * H, H, s.vec, 1)) return false;
+    rmsnorm_pack(c, s.vec, H, gn);
+    tile.dots(s.vec, s.out);
+    for (int r0 = CAP; r0 < E; r0 += CAP) {
+      tile.issue(min(CAP, E - r0), [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
+      tile.dots(s.vec, s.out + r0);
+    }
+    lds_barrier();
   }
-  lds_barrier();
   route(c, s.out);
   const float div = route_div(a, s);
-  for (int e = tid(); e < E; e += NT)
-    st_tagged(a.rlog + (size_t)l * a.s_rlog + (size_t)b * E + e, s.out[e], a.epoch);
+  if (!read)
+    for (int e = tid(); e < E; e += NT)
+      st_tagged(a.rlog + (size_t)l * a.s_rlog + (size_t)b * E + e, s.out[e], a.epoch);
   if (tid() < a.K) {
     const int j = tid(), id = s.route_ids[j];
     const float wj = s.route_w[j] / div;
@@ -2216,6 +2222,7 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
           switch (t.op) {
             case OP_BQKV: ok = task_bqkv(c, t); break;
             case OP_BO: ok = task_bo(c, t); break;
+            case OP_ROUTER: ok = task_router<CH, TCH>(c, t); break;
             case OP_TOPK: ok = task_topk<CH, TCH>(c, t); break;
             case OP_BEXP: ok = task_bexp<CH, TCH, CF, TCF>(c, t); break;
             case OP_BCOMB: ok = task_bcomb(c, t); break;

@@ -47,10 +47,12 @@ enum Op : uint8_t {
   OP_COUNT = 18
 };
 
+// TF_LOGITS (batch top-k): the router rows of the sequence were computed by
+// router tasks; the task reads the logits instead of computing them.
 // TF_STAGE_KV: before its body the task requests the first pages of this
 // unit's next attention split (the first attention task at most STAGE_SCAN
 // tasks further on in the same list) into LDS.
-enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4 };
+enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4, TF_LOGITS = 8 };
 
 // Batch QKV tasks: rotary pairs per row block (the rows of a block are 2
 // BQKV_PAIRS), and the words per (reduction block, row block, sequence) of

@@ -201,11 +201,23 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
         stages.push_back(st);
       }
     }
-    if (moe) {  // TOPK
+    if (moe) {  // ROUTER rows (a few tasks per sequence), then TOPK per sequence
+      const int nr = std::max(1, std::min(std::min(8, m.n_experts), n_cu / B));
+      std::vector<Task> rt;
+      for (int b = 0; b < B; ++b)
+        for (auto [r0, n] : split_even(m.n_experts, nr)) {
+          Task t = mk_task(mk::OP_ROUTER, l);
+          t.wait_b = ctr16(p->c_o[l]);
+          t.signal = ctr16(p->c_router[l]);
+          t.a0 = b; t.a1 = r0; t.a2 = n;
+          rt.push_back(t);
+        }
+      stages.push_back(rt);
       std::vector<Task> tk;
       for (int b = 0; b < B; ++b) {
         Task t = mk_task(mk::OP_TOPK, l);
-        t.wait_b = ctr16(p->c_o[l]);
+        t.flags = mk::TF_LOGITS;
+        t.wait_b = ctr16(p->c_router[l]);
         t.signal = ctr16(p->c_topk[l]);
         t.a0 = b;
         tk.push_back(t);
@@ -428,7 +440,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       p->c_o.push_back(new_ctr("o[" + ls + "]"));
       p->c_opart.push_back(p->o_kb > 1 ? new_ctr("opart[" + ls + "]") : -1);
       p->c_qpart.push_back(p->q_kb > 1 ? new_ctr("qpart[" + ls + "]") : -1);
-      p->c_router.push_back(-1);
+      p->c_router.push_back(moe ? new_ctr("router[" + ls + "]") : -1);
       p->c_topk.push_back(moe ? new_ctr("topk[" + ls + "]") : -1);
       p->c_expert.push_back(new_ctr("expert[" + ls + "]"));
       p->c_bcomb.push_back(new_ctr("ffn[" + ls + "]"));
@@ -831,11 +843,12 @@ void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::
       if (t.a0 == 0)
         for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"o" + ls, r});
       break;
-    case mk::OP_ROUTER:
-      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"router" + ls, r});
+    case mk::OP_ROUTER:  // rows a1 .. a1 + a2 of sequence a0
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"router" + ls, (int64_t)t.a0 * 1000000 + r});
       break;
-    case mk::OP_TOPK:  // every router row of one sequence, and its top-k
-      for (int r = 0; r < m.n_experts; ++r) out.push_back({"router" + ls, (int64_t)t.a0 * 1000000 + r});
+    case mk::OP_TOPK:  // every router row of one sequence (unless read), and its top-k
+      if (!(t.flags & mk::TF_LOGITS))
+        for (int r = 0; r < m.n_experts; ++r) out.push_back({"router" + ls, (int64_t)t.a0 * 1000000 + r});
       out.push_back({"topk" + ls, t.a0});
       break;
     case mk::OP_BEXP: {
@@ -1017,13 +1030,14 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
           return (t.flags & mk::TF_QUEUE) ? all_done(qkv_op, l, Hkv) : all_done(qkv_op, l, t.a1);
         case mk::OP_COMB: return all_done(mk::OP_ATTN, l, t.a1 / HG);
         case mk::OP_O: return all_done(mk::OP_COMB, l, Hkv);
-        case mk::OP_ROUTER: return all_done(mk::OP_O, l, Hkv);
+        case mk::OP_ROUTER: return all_done(p->batch ? mk::OP_BO : mk::OP_O, l, Hkv);
         case mk::OP_EXPERT: return all_done(mk::OP_O, l, Hkv) && (!moe || all_done(mk::OP_ROUTER, l, Hkv));
         case mk::OP_LM: return all_done(mk::OP_EXPERT, L - 1, Hkv);
         case mk::OP_FINAL: return all_done(mk::OP_LM, 0, Hkv);
         case mk::OP_BQKV: return l == 0 || all_done(mk::OP_BCOMB, l - 1, Hkv);
         case mk::OP_BO: return all_done(mk::OP_COMB, l, Hkv);
-        case mk::OP_TOPK: return all_done(mk::OP_BO, l, Hkv);
+        case mk::OP_TOPK:
+          return all_done(mk::OP_BO, l, Hkv) && (!(t.flags & mk::TF_LOGITS) || all_done(mk::OP_ROUTER, l, Hkv));
         case mk::OP_BEXP: return all_done(mk::OP_BO, l, Hkv) && (!moe || all_done(mk::OP_TOPK, l, Hkv));
         case mk::OP_BCOMB: return all_done(mk::OP_BEXP, l, Hkv) && (!moe || all_done(mk::OP_TOPK, l, Hkv));
         case mk::OP_BLM: return all_done(mk::OP_BCOMB, L - 1, Hkv);

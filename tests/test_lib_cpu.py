@@ -35,6 +35,7 @@ OP_BQKV, OP_BO = 10, 11
 OP_TOPK, OP_BEXP, OP_BCOMB, OP_BLM, OP_BFINAL = range(13, 18)
 NO_CTR = 0xFFFF
 TF_QUEUE = 2
+TF_LOGITS = 8
 
 
 def declared_functions():
@@ -147,6 +148,7 @@ def plan_coverage(tasks, m, bound):
 
     o_blocks = {}
     q_blocks = {}
+    batch = bool((tasks["op"] == OP_BQKV).any())
 
     def add(key, items):
         S.setdefault(key, []).extend(items)
@@ -169,8 +171,10 @@ def plan_coverage(tasks, m, bound):
                 add(("o", l), list(range(a1, a1 + a2)))
             o_blocks.setdefault((l, a1, a2, max(a3, 1)), []).append(a0)
         elif op == OP_TOPK:
-            # one sequence: every router row, then its top-k
-            add(("router", l), [(a0, e) for e in range(m["n_experts"])])
+            # one sequence: every router row (unless router tasks computed
+            # them: TF_LOGITS), then its top-k
+            if not int(t["flags"]) & TF_LOGITS:
+                add(("router", l), [(a0, e) for e in range(m["n_experts"])])
             add(("topk", l), [a0])
         elif op == OP_BEXP:
             # one expert's gate/up rows (expert, FFN row) and down rows (expert, hidden row)
@@ -194,7 +198,8 @@ def plan_coverage(tasks, m, bound):
         elif op == OP_O:
             add(("o", l), list(range(a1, a1 + a2)))
         elif op == OP_ROUTER:
-            add(("router", l), list(range(a1, a1 + a2)))
+            # rows a1 .. a1 + a2 (of sequence a0 in a batch plan)
+            add(("router", l), [(a0, r) if batch else r for r in range(a1, a1 + a2)])
         elif op == OP_EXPERT:
             # gate/up part: (b, slot, FFN row) for MoE, FFN row for a dense FFN;
             # down part: hidden rows a3 >> 16 .. + (a3 & 0xFFFF)
