@@ -99,11 +99,16 @@ constexpr int O_RED_WORDS = 16384;
 
 // Stages of a batch plan (B > 1), per layer:
 //   BQKV  (16-row blocks of one kv group's rotary pairs, all sequences: MFMA
-//          tile, rotary epilogue, KV append per sequence)
+//          tile over one reduction block of the hidden state; blocks 1 ..
+//          publish partial sums, block 0 adds them, then the rotary epilogue
+//          and the KV append per sequence)
 //   ATTN  (per sequence, kv group and page range of that sequence's bound)
 //   COMB  (per sequence, query head and dim range)
-//   BO    (16-row blocks of W_o, all sequences: MFMA tile, residual)
-//   TOPK  (MoE, one per sequence: router rows, softmax, top-k)
+//   BO    (16-row blocks of W_o, all sequences: MFMA tile over one reduction
+//          block of the attention output; block 0 adds the others' partial
+//          sums and the residual)
+//   ROUTER (MoE, per sequence and range of router rows)
+//   TOPK  (MoE, one per sequence: reads the router logits, softmax, top-k)
 //   BEXP  (one expert, part q: gate/up rows with SwiGLU, then down rows, for
 //          the sequences routed to it; the down part reads the activations of
 //          every part of the same expert)
