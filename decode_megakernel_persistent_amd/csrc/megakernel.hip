@@ -1823,7 +1823,7 @@ __device__ __forceinline__ bool task_bo(Ctx& c, const Task& t) {
   };
   // pairs of rows (r, r + 1): even n, r0 and H keep every pair in one row range
   const bool pairs = !((n | r0 | H) & 1) && !((ws_off(a, op) >> 3) & 1) && !(xin && ((ws_off(a, xin) >> 3) & 1));
-  if (!(pairs ? gather_fn_pairs<8>(c, KB * bn, waddr, red, 0) : gather_fn<8>(c, KB * bn, waddr, red, 0)))
+  if (!(pairs ? gather_fn_pairs<16>(c, KB * bn, waddr, red, 0) : gather_fn<8>(c, KB * bn, waddr, red, 0)))
     return false;
   for (int idx = tid(); idx < bn; idx += NT) {
     const int r = idx / B, b = idx - r * B;
