@@ -1043,7 +1043,48 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   return true;
 }
 
+// Batch combine of nh = nd / D whole query heads h .. h + nh - 1 of one kv
+// group (d0 = 0, nd = nh D <= NT): per split, the heads' words are one
+// contiguous run of nh (D + 2), gathered in pairs into the shared area (no
+// pages are staged in a batch plan); thread (head, dim) then merges its
+// output over the splits in split order.
+static_assert(COMB_BATCH_WORDS == NWAVE * STAGE_CHUNKS * 64 * 4, "batch combine words fill the shared area");
+__device__ __forceinline__ bool task_comb_heads(Ctx& c, const Task& t) {
+  KAC& a = c.a;
+  Smem& s = c.s;
+  const int l = t.layer, b = t.a0, h = t.a1, nd = t.a3, S = t.aux, D = a.D;
+  const int HG = a.HG, g = h / HG, PS = D + 2, W = nd / D * PS;
+  const uint64_t* base = a.part + (size_t)l * a.s_part + ((size_t)b * a.Hkv + g) * a.S_max * HG * PS +
+                         (size_t)(h % HG) * PS;
+  const size_t sstride = (size_t)HG * PS;
+  float* sw = s.att;  // [S][W]
+  // W is even and so is every run's workspace word offset
+  if (!gather_fn_pairs<8>(c, S * W, [&](int i) {
+        const int q = i / W;
+        return base + q * sstride + (i - q * W);
+      }, sw, 1))
+    return false;
+  const int tt = tid();
+  if (tt < nd) {
+    const int hh = tt / D, dim = tt - hh * D;
+    const float* col = sw + hh * PS;
+    float M = NEG_INF;
+    for (int q = 0; q < S; ++q) M = fmaxf(M, col[q * W + D]);
+    float L = 0.f, acc = 0.f;
+    for (int q = 0; q < S; ++q) {
+      const float mq = col[q * W + D];
+      const float e = mq == NEG_INF ? 0.f : expf(mq - M);
+      L += e * col[q * W + D + 1];
+      acc += e * col[q * W + dim];
+    }
+    const float o = L > 0.f ? acc / L : 0.f;
+    st_tagged(a.o + (size_t)l * a.s_o + ((size_t)b * a.Hq + h + hh) * D + dim, o, a.epoch);
+  }
+  return true;
+}
+
 __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
+  if (t.a3 > c.a.D) return task_comb_heads(c, t);
   KAC& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, h = t.a1, d0 = t.a2, nd = t.a3, S = t.aux, D = a.D;

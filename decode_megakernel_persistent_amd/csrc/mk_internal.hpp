@@ -60,6 +60,9 @@ enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4, TF_
 constexpr int BQKV_PAIRS = 32;
 constexpr int QPART_STRIDE = 2 * BQKV_PAIRS + 2;
 
+// Words (floats) a batch combine task may gather: the whole shared area.
+constexpr int COMB_BATCH_WORDS = 24576;
+
 // Attention pages staged ahead of their split: one per wave.
 constexpr int STAGE_PAGES = 8;
 constexpr int STAGE_SCAN = 8;

@@ -175,11 +175,16 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
       std::stable_sort(st.begin(), st.end(), [](const Task& x, const Task& y) { return x.a3 > y.a3; });
       stages.push_back(st);
     }
-    {  // COMB
+    {  // COMB: whole heads (nh of one kv group per task) while there are more
+       // (sequence, head) pairs than units, else as many dim ranges as fit
       std::vector<Task> st;
+      int nh = 1;
+      while (p->comb_dim_tasks == 1 && B * Hq / nh > n_cu && HG % (2 * nh) == 0 && 2 * nh * D <= mk::NT &&
+             (int64_t)p->S_max * 2 * nh * (D + 2) <= mk::COMB_BATCH_WORDS)
+        nh *= 2;
       for (int b = 0; b < B; ++b)
-        for (int h = 0; h < Hq; ++h)
-          for (auto [d0, nd] : split_even(D, p->comb_dim_tasks)) {
+        for (int h = 0; h < Hq; h += nh)
+          for (auto [d0, nd] : split_even(nh * D, nh > 1 ? 1 : p->comb_dim_tasks)) {
             Task t = mk_task(mk::OP_COMB, l);
             t.wait_b = ctr16(p->c_attn[l * Hkv + h / HG]);
             t.signal = ctr16(p->c_comb[l]);
@@ -829,9 +834,9 @@ void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::
       for (int pg = t.a2; pg < t.a2 + t.a3; ++pg)
         out.push_back({"attn" + ls, ((int64_t)t.a0 * Hkv + t.a1) * 1000000 + pg});
       break;
-    case mk::OP_COMB:
+    case mk::OP_COMB:  // dims a2 .. a2 + a3 of heads a1, a1 + 1, .. taken as one run
       for (int d = t.a2; d < t.a2 + t.a3; ++d)
-        out.push_back({"comb" + ls, ((int64_t)t.a0 * Hq + t.a1) * 1024 + d});
+        out.push_back({"comb" + ls, ((int64_t)t.a0 * Hq + t.a1 + d / D) * 1024 + d % D});
       break;
     case mk::OP_EXPERT: {
       const bool moe = m.n_experts > 0;

@@ -193,8 +193,9 @@ def plan_coverage(tasks, m, bound):
                                   for p in range(a1 * a2) if p < pg_bound])
         elif op == OP_ATTN:
             add(("attn", l), [(a0, a1, p) for p in range(a2, a2 + a3)])
-        elif op == OP_COMB:
-            add(("comb", l), [(a0, a1, i) for i in range(a2, a2 + a3)])
+        elif op == OP_COMB:  # dims a2 .. a2 + a3 of heads a1, a1 + 1, .. as one run
+            D = m["head_dim"]
+            add(("comb", l), [(a0, a1 + i // D, i % D) for i in range(a2, a2 + a3)])
         elif op == OP_O:
             add(("o", l), list(range(a1, a1 + a2)))
         elif op == OP_ROUTER:
