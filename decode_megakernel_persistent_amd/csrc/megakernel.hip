@@ -18,16 +18,19 @@
 // so that a finished step leaves every counter at steps x producers.
 //
 // Task bodies:
-//  - projections (QKV, O, router, expert gate/up, expert down, LM head) are
-//    GEMVs: each lane group of 64 (or 32) lanes holds whole rows as 16-byte
-//    bf16 chunks, accumulates in fp32 and reduces with DPP row operations;
-//    RMSNorm is recomputed by every consumer tile from the gathered vector;
-//    RoPE + KV append, residual adds, SwiGLU, the weighted expert combine and
-//    the local argmax are epilogues;
-//  - paged attention splits use MFMA 16x16x16 bf16 tiles on 16-token pages
+//  - batch 1: projections (QKV, O, router, expert gate/up, expert down, LM
+//    head) are GEMVs: each lane group of 64 (or 32) lanes holds whole rows as
+//    16-byte bf16 chunks, accumulates in fp32 and reduces with DPP row
+//    operations; RMSNorm is recomputed by every consumer tile from the
+//    gathered vector; RoPE + KV append, residual adds, SwiGLU, the weighted
+//    expert combine and the local argmax are epilogues;
+//  - batches of 2 .. 32 sequences: the same projections as MFMA 16x16x32
+//    bf16 tiles (see the batch tasks below);
+//  - paged attention splits use MFMA 16x16x32 bf16 tiles on 16-token pages
 //    (queries and probabilities carried as bf16 hi + lo pairs), an online
 //    softmax across pages and a log-sum-exp merge across waves;
 //  - the split combine is a log-sum-exp merge in fixed split order.
+// Consumers read neighbouring tagged words in pairs, one 16-byte load each.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
