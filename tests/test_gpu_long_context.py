@@ -26,8 +26,8 @@ def test_small_moe_long_context():
     run_step_parity("small_moe", ctx=[262143], pool_pages=16500)
 
 
-def layer0_reference(m, seed, tok, pos):
-    """Oracle pieces of layer 0 for one sequence at position pos: q [Hq][d]
+def layer0_reference(m, seed, tok, pos, b=0):
+    """Oracle pieces of layer 0 for sequence b at position pos: q [Hq][d]
     after rotation, bf16 k and v of the new token [Hkv][d], attention output
     [Hq][d] over the pos prior tokens and the new one."""
     W = HostWeights(m, seed, cache=False)
@@ -46,8 +46,8 @@ def layer0_reference(m, seed, tok, pos):
     hg = Hq // Hkv
     out = torch.empty(Hq, d, dtype=torch.float32)
     for g in range(Hkv):
-        K = torch.cat([kv.k(0, 0, g, pos), k_new[g:g + 1]])
-        V = torch.cat([kv.v(0, 0, g, pos), v_new[g:g + 1]])
+        K = torch.cat([kv.k(0, b, g, pos), k_new[g:g + 1]])
+        V = torch.cat([kv.v(0, b, g, pos), v_new[g:g + 1]])
         out[g * hg:(g + 1) * hg] = O.attention(q[g * hg:(g + 1) * hg], K, V)
     return q, k_new, v_new, out
 
