@@ -150,6 +150,16 @@ def route(r, k, norm_topk=True):
     return ids, w
 
 
+def route_given(r, ids, norm_topk=True):
+    """Routing weights of a given selection: w = pi[ids] (/ sum pi[ids])."""
+    pi = softmax(r)
+    ids = torch.as_tensor(list(ids), dtype=torch.int64)
+    w = pi[ids]
+    if norm_topk:
+        w = w / w.sum()
+    return ids, w
+
+
 def silu(z):
     return z / (1.0 + torch.exp(-z))
 
@@ -200,13 +210,20 @@ class OracleKV:
 
 # ---------------------------------------------------------------- the step
 
-def decode_step(m, W, kv, tokens, dt=torch.float32):
+def decode_step(m, W, kv, tokens, dt=torch.float32, force_ids=None):
     """One decode step for every sequence b: token tokens[b] at position kv.len[b].
 
     Returns a dict with per-sequence lists: next (int), logits [V],
     x_attn[l] / x_ffn[l] (hidden after each residual), topk_ids[l],
     topk_w[l], router_logits[l], k_new[l] / v_new[l] (bf16 [Hkv][d]).
     The KV state gains one token per sequence.
+
+    force_ids: optional {(b, l): k expert ids}. Where the router's k-th and
+    (k+1)-th probabilities tie to within fp32 rounding, two correct
+    implementations may select different experts; a comparison then
+    continues from the other side's selection: the listed ids replace the
+    top-k of sequence b at layer l, and their weights are the same
+    probabilities of the same softmax, renormalised over those ids.
     """
     L, H, Hq, Hkv, d = m["n_layers"], m["hidden"], m["n_q_heads"], m["n_kv_heads"], m["head_dim"]
     hg = Hq // Hkv
@@ -240,7 +257,10 @@ def decode_step(m, W, kv, tokens, dt=torch.float32):
             u = rmsnorm(x, W.ffn_norm(l), eps)
             if moe:
                 r = matvec(W.router(l), u)
-                ids, wts = route(r, m["top_k"], bool(m["norm_topk"]))
+                if force_ids is not None and (b, l) in force_ids:
+                    ids, wts = route_given(r, force_ids[b, l], bool(m["norm_topk"]))
+                else:
+                    ids, wts = route(r, m["top_k"], bool(m["norm_topk"]))
                 y = torch.zeros(H, dtype=dt)
                 for j in range(m["top_k"]):
                     e = int(ids[j])
@@ -266,6 +286,55 @@ def decode_step(m, W, kv, tokens, dt=torch.float32):
     for b in range(len(tokens)):
         kv.len[b] += 1
     return out
+
+
+def near_tie(r, k, rel):
+    """True when the k-th and (k+1)-th largest softmax probabilities of the
+    router logits r differ by less than rel of the k-th: fp32 logits summed
+    in another order can then rank them either way."""
+    p = softmax(r.double())
+    s = torch.sort(p, descending=True).values
+    return k < s.numel() and (s[k - 1] - s[k]).item() < rel * s[k - 1].item()
+
+
+def decode_step_following(m, W, kv, tokens, other_ids, rel, dt=torch.float32):
+    """decode_step, continuing from another implementation's routing where
+    the two may both be right.
+
+    other_ids[b][l]: the other side's k expert ids of sequence b at layer l.
+    Where the oracle's own top-k differs from them and the oracle's choice is
+    a near-tie (near_tie(router logits, k, rel)), the other side's ids are
+    taken at that layer (force_ids of decode_step) and the step is run again
+    from the start, so that later layers are compared on the same routing.
+    Returns (out, forced, differ): forced lists the (b, l) taken from
+    other_ids; differ lists the (b, l) where the ids differ without a
+    near-tie. The KV state gains one token per sequence, as in decode_step.
+    """
+    start = list(kv.len)
+    force = {}
+    k = m["top_k"]
+    while True:
+        kv.len = list(start)
+        out = decode_step(m, W, kv, tokens, dt, force_ids=force)
+        if not m["n_experts"]:
+            return out, [], []
+        new, differ = None, []
+        for b in range(len(tokens)):
+            for l in range(m["n_layers"]):
+                mine = [int(v) for v in out["topk_ids"][b][l]]
+                theirs = [int(v) for v in other_ids[b][l]]
+                if mine == theirs or (b, l) in force:
+                    continue
+                if near_tie(out["router_logits"][b][l], k, rel):
+                    new = (b, l, theirs)
+                    break
+                differ.append((b, l))
+                break  # later layers of this sequence follow another routing
+            if new:
+                break
+        if new is None:
+            return out, sorted(force), differ
+        force[new[0], new[1]] = new[2]
 
 
 # ---------------------------------------------------------------- speed-of-light
@@ -409,3 +478,50 @@ def work_sets(m, ctx_bound):
         S["down", l] = set(range(H))
     S["lm", ] = set(range(m["vocab"]))
     return S
+
+
+# ---------------------------------------------------------------- completion counters
+
+def qkv_row_group(m, r):
+    """kv group of row r of W_qkv: q rows by their query head's group (query
+    head h uses kv head h // (Hq/Hkv)), then the k rows, then the v rows of
+    each kv head."""
+    Hq, Hkv, d = m["n_q_heads"], m["n_kv_heads"], m["head_dim"]
+    if r < Hq * d:
+        return (r // d) // (Hq // Hkv)
+    if r < (Hq + Hkv) * d:
+        return (r - Hq * d) // d
+    return (r - (Hq + Hkv) * d) // d
+
+
+def expected_counters(m, ctx_bound, S=None):
+    """Completion count per dependency class and step, from the work alone.
+
+    A finished task adds to its class's counter the number of outputs it
+    produced, so after a step each counter has grown by the size of its
+    class's share of work_sets, whatever the tiling. Classes (names as
+    "op[layer]" or "op[layer][kv head]"): qkv per kv group (rows of W_qkv
+    whose head belongs to the group), attn per kv group ((sequence, page)
+    pairs of that kv head), comb, o, router, expert (gate/up outputs plus
+    down rows), and for a batch topk and ffn; lm for the LM head. Returns
+    {name: count}. S: work_sets(m, ctx_bound) if already at hand.
+    """
+    if S is None:
+        S = work_sets(m, ctx_bound)
+    L, Hkv = m["n_layers"], m["n_kv_heads"]
+    out = {}
+    for l in range(L):
+        for g in range(Hkv):
+            out[f"qkv[{l}][{g}]"] = sum(1 for r in S["qkv", l] if qkv_row_group(m, r) == g)
+            out[f"attn[{l}][{g}]"] = sum(1 for (_, gg, _) in S["attn", l] if gg == g)
+        out[f"comb[{l}]"] = len(S["comb", l])
+        out[f"o[{l}]"] = len(S["o", l])
+        if ("router", l) in S:
+            out[f"router[{l}]"] = len(S["router", l])
+        if ("topk", l) in S:
+            out[f"topk[{l}]"] = len(S["topk", l])
+        out[f"expert[{l}]"] = len(S["gateup", l]) + len(S["down", l])
+        if ("ffn", l) in S:
+            out[f"ffn[{l}]"] = len(S["ffn", l])
+    out["lm"] = len(S["lm", ])
+    return out
