@@ -92,6 +92,7 @@ _SIGS = {
     "mk_plan_upload": (_i32, [_vp, _vp, _sz, _vp]),
     "mk_plan_buffer": (_i32, [_vp, _i32, _i32, _P(_sz), _P(_sz)]),
     "mk_plan_counter_targets": (_i32, [_vp, _vp, _i32]),
+    "mk_plan_counter_name": (ctypes.c_char_p, [_vp, _i32]),
     "mk_plan_free": (None, [_vp]),
     "mk_decode_step": (_i32, [_vp, _P(mk_weights), _P(mk_kv), _P(mk_io), _P(mk_step_buffers),
                               _u32, _u32, _vp]),
@@ -162,7 +163,6 @@ def mk_step_bytes(desc, seq_lens, distinct=None):
 
 MK_PLAN_ATTN_QUEUE = 1
 MK_PLAN_NO_ATTN_QUEUE = 2
-MK_PLAN_SPLIT_UNITS = 4
 
 
 def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0, flags=0,
@@ -234,6 +234,17 @@ def mk_plan_counter_targets(p):
     buf = (_u32 * n)()
     _check(_lib.mk_plan_counter_targets(p, buf, n))
     return list(buf)
+
+
+def mk_plan_counter_name(p, i):
+    r = _lib.mk_plan_counter_name(p, i)
+    if r is None:
+        raise MkError(MK_EINVAL, mk_last_error())
+    return r.decode()
+
+
+def mk_plan_counter_names(p):
+    return [mk_plan_counter_name(p, i) for i in range(_lib.mk_plan_n_counters(p))]
 
 
 def mk_plan_free(p):

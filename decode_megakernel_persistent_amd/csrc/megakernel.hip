@@ -14,8 +14,9 @@
 // that releases with an L2 writeback and acquires with an L2 invalidate costs
 // several microseconds per dependency stage; a tagged word needs neither,
 // because the value and its completion mark travel in one coherent access.
-// Each task also adds one to its completion counter (spread over 8 lines),
-// so that a finished step leaves every counter at steps x producers.
+// Each task also adds the number of outputs it produced to its completion
+// counter (spread over 8 lines), so that a finished step leaves every counter
+// at steps x the outputs of its class.
 //
 // Task bodies:
 //  - batch 1: projections (QKV, O, router, expert gate/up, expert down, LM
@@ -98,12 +99,6 @@ __device__ __forceinline__ uint64_t logit_key(float v, int e) {
   return ((uint64_t)o << 32) | (uint32_t)(0xFFFF - e);
 }
 
-// Gather tagged words into LDS: dst[i] = value of word i for i < n, where
-// word i sits at src1 + i for i < n1 and at src2 + (i - n1) after that; MAXW
-// words per thread per batch. which: 0 = routing wait, 1 = data wait (trace
-// slots), -1 = untraced. With nsq > 0 the sum of squares of words 0 .. nsq-1
-// is formed on the way (each thread over its words in order, then over the
-// wave) and wave w's part is left in s.red[w] for norm_pack. Uniform result.
 // Byte offset of a tagged word in the workspace.
 __device__ __forceinline__ uint32_t ws_off(const KAC& a, const uint64_t* p) {
   return (uint32_t)((const char*)p - (const char*)a.ws);
@@ -153,12 +148,17 @@ __device__ __forceinline__ bool read_pairs(KAC& a, const Off& off, float* out, u
   return true;
 }
 
-// Whether words of src1 (n1 of them) then src2 (up to n) can be read in
-// 16-byte pairs: even counts and even word offsets in the workspace.
-__device__ __forceinline__ bool pairable(const KAC& a, const uint64_t* src1, int n1, const uint64_t* src2, int n) {
-  return !((n1 | n | (int)(ws_off(a, src1) >> 3) | (int)(ws_off(a, src2) >> 3)) & 1);
-}
-
+// Gather tagged words into LDS: dst[i] = value of word i for i < n, where
+// word i sits at src1 + i for i < n1 and at src2 + (i - n1) after that,
+// read as pairs (2j, 2j + 1) with one 16-byte load each: n1 and n are even
+// and both sources start at an even workspace word (the planner lays out
+// every buffer so). MAXW words per thread per batch. which: 0 = routing
+// wait, 1 = data wait (trace slots), -1 = untraced. With nsq > 0 the sum of
+// squares of words 0 .. nsq-1 is formed on the way (each thread over its
+// words in order, then over the wave) and wave w's part is left in s.red[w]
+// for norm_pack. With keys, the words of src2 are router logits: their rank
+// keys go to keys[] and the per-wave maxima to s.red[NWAVE + w]. Uniform
+// result.
 template <int MAXW>
 __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, const uint64_t* src2, int n,
                                         float* dst, int which, int nsq = 0, uint64_t* keys = nullptr) {
@@ -166,51 +166,27 @@ __device__ __forceinline__ bool gather2(Ctx& c, const uint64_t* src1, int n1, co
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
   bool ok = true;
   float ss = 0.f, mx = NEG_INF;
-  if (pairable(a, src1, n1, src2, n)) {
-    // pairs (2j, 2j + 1), j = base / 2 + t + k NT: one 16-byte load each
-    constexpr int MAXP = (MAXW + 1) / 2;
-    const uint32_t o1 = ws_off(a, src1), o2 = ws_off(a, src2);
-    for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
-      const int t = tid();
-      float v[2 * MAXP];
-      ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
-        const int i = base + 2 * (t + k * NT);
-        return i < n1 ? o1 + 8u * i : (i < n ? o2 + 8u * (i - n1) : NO_PAIR);
-      }, v, c.t0, c.ti);
-      if (ok) {
-#pragma unroll
-        for (int k = 0; k < MAXP; ++k) {
-          const int i = base + 2 * (t + k * NT);
-          if (i < n) *(float2*)(dst + i) = make_float2(v[2 * k], v[2 * k + 1]);
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            if (i + e < nsq) ss = fmaf(v[2 * k + e], v[2 * k + e], ss);
-            if (keys && i + e >= n1 && i + e < n) {
-              keys[i + e - n1] = logit_key(v[2 * k + e], i + e - n1);
-              mx = fmaxf(mx, v[2 * k + e]);
-            }
-          }
-        }
-      }
-    }
-  }
-  else
-  for (int base = 0; base < n && ok; base += MAXW * NT) {
+  constexpr int MAXP = (MAXW + 1) / 2;
+  const uint32_t o1 = ws_off(a, src1), o2 = ws_off(a, src2);
+  for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
     const int t = tid();
-    float v[MAXW];
-    ok = read_words<MAXW>(a, [&](int k) -> const uint64_t* {
-      const int i = base + t + k * NT;
-      return i < n1 ? src1 + i : (i < n ? src2 + (i - n1) : nullptr);
+    float v[2 * MAXP];
+    ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
+      const int i = base + 2 * (t + k * NT);
+      return i < n1 ? o1 + 8u * i : (i < n ? o2 + 8u * (i - n1) : NO_PAIR);
     }, v, c.t0, c.ti);
     if (ok) {
 #pragma unroll
-      for (int k = 0; k < MAXW; ++k) {
-        const int i = base + t + k * NT;
-        if (i < n) dst[i] = v[k];
-        if (i < nsq) ss = fmaf(v[k], v[k], ss);
-        if (keys && i >= n1 && i < n) {
-          keys[i - n1] = logit_key(v[k], i - n1);
-          mx = fmaxf(mx, v[k]);
+      for (int k = 0; k < MAXP; ++k) {
+        const int i = base + 2 * (t + k * NT);
+        if (i < n) *(float2*)(dst + i) = make_float2(v[2 * k], v[2 * k + 1]);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          if (i + e < nsq) ss = fmaf(v[2 * k + e], v[2 * k + e], ss);
+          if (keys && i + e >= n1 && i + e < n) {
+            keys[i + e - n1] = logit_key(v[2 * k + e], i + e - n1);
+            mx = fmaxf(mx, v[2 * k + e]);
+          }
         }
       }
     }
@@ -235,9 +211,9 @@ __device__ __forceinline__ bool gather(Ctx& c, const uint64_t* src, int n, float
   return gather2<MAXW>(c, src, n, src, n, dst, which, nsq);
 }
 
-// Gather n tagged words (n even) into LDS already in split form (see
-// pack_lds): word i's bf16 hi and lo parts land in chunk i / 8, paired with
-// word i ^ 1, which the neighbouring lane holds (DPP quad permutation), so no
+// Gather n tagged words (n even, src at an even workspace word) into LDS
+// already in split form (see pack_lds): the pair (2j, 2j + 1) arrives in one
+// 16-byte load, and its bf16 hi and lo parts land in chunk 2j / 8, so no
 // separate conversion pass or barrier follows. Uniform result.
 template <int MAXW>
 __device__ __forceinline__ bool gather_split(Ctx& c, const uint64_t* src, int n, float* dst, int which) {
@@ -245,49 +221,24 @@ __device__ __forceinline__ bool gather_split(Ctx& c, const uint64_t* src, int n,
   if (which >= 0 && a.trace && tid() == 0) c.s.tw[2 * which] = now();
   uint32_t* dw = (uint32_t*)dst;
   bool ok = true;
-  if (pairable(a, src, n, src, n)) {
-    // pairs (2j, 2j + 1) in one 16-byte load: the thread holds both bf16 halves
-    constexpr int MAXP = (MAXW + 1) / 2;
-    const uint32_t o = ws_off(a, src);
-    for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
-      const int t = tid();
-      float v[2 * MAXP];
-      ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
-        const int i = base + 2 * (t + k * NT);
-        return i < n ? o + 8u * i : NO_PAIR;
-      }, v, c.t0, c.ti);
-#pragma unroll
-      for (int k = 0; k < MAXP; ++k) {
-        const int i = base + 2 * (t + k * NT);
-        const uint32_t h0 = f2bf(v[2 * k]), h1 = f2bf(v[2 * k + 1]);
-        const uint32_t l0 = f2bf(v[2 * k] - bf2f(h0)), l1 = f2bf(v[2 * k + 1] - bf2f(h1));
-        if (ok && i < n) {
-          const int ch = i >> 3, e = i & 7;
-          dw[8 * ch + (e >> 1)] = h0 | (h1 << 16);
-          dw[8 * ch + 4 + (e >> 1)] = l0 | (l1 << 16);
-        }
-      }
-    }
-  }
-  else
-  for (int base = 0; base < n && ok; base += MAXW * NT) {
+  constexpr int MAXP = (MAXW + 1) / 2;
+  const uint32_t o = ws_off(a, src);
+  for (int base = 0; base < n && ok; base += 2 * MAXP * NT) {
     const int t = tid();
-    float v[MAXW];
-    ok = read_words<MAXW>(a, [&](int k) -> const uint64_t* {
-      const int i = base + t + k * NT;
-      return i < n ? src + i : nullptr;
+    float v[2 * MAXP];
+    ok = read_pairs<MAXP>(a, [&](int k) -> uint32_t {
+      const int i = base + 2 * (t + k * NT);
+      return i < n ? o + 8u * i : NO_PAIR;
     }, v, c.t0, c.ti);
 #pragma unroll
-    for (int k = 0; k < MAXW; ++k) {
-      const int i = base + t + k * NT;
-      const uint32_t h = f2bf(v[k]);
-      const uint32_t lo = f2bf(v[k] - bf2f(h));
-      const uint32_t hn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0xB1, 0xF, 0xF, false);
-      const uint32_t ln = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0xB1, 0xF, 0xF, false);
-      if (ok && i < n && !(i & 1)) {
+    for (int k = 0; k < MAXP; ++k) {
+      const int i = base + 2 * (t + k * NT);
+      const uint32_t h0 = f2bf(v[2 * k]), h1 = f2bf(v[2 * k + 1]);
+      const uint32_t l0 = f2bf(v[2 * k] - bf2f(h0)), l1 = f2bf(v[2 * k + 1] - bf2f(h1));
+      if (ok && i < n) {
         const int ch = i >> 3, e = i & 7;
-        dw[8 * ch + (e >> 1)] = h | (hn << 16);
-        dw[8 * ch + 4 + (e >> 1)] = lo | (ln << 16);
+        dw[8 * ch + (e >> 1)] = h0 | (h1 << 16);
+        dw[8 * ch + 4 + (e >> 1)] = l0 | (l1 << 16);
       }
     }
   }
@@ -981,9 +932,10 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P2, __builtin_bit_cast(bf16x8, v2), acc[nb], 0, 0, 0);
     }
   };
-  // page i of this wave is in buffer i % NBUF; pages go two at a time, and a
-  // used buffer takes page i + NBUF
-  static_assert(NBUF % 2 == 0, "pages are taken in pairs");
+  // pages go two at a time: the pair being computed sits in buffers 0 and 1
+  // while the pair after it is in flight in buffers 2 and 3; the two halves
+  // of the ring alternate roles, and the pair body is instantiated once per
+  // half.
   constexpr int NO_PAGE = 1 << 24;  // a page index past any context: contributes nothing
   for (int i0 = 0; i0 < cnt; i0 += NBUF) {
 #pragma unroll
@@ -1086,8 +1038,11 @@ __device__ __forceinline__ bool task_comb_heads(Ctx& c, const Task& t) {
   return true;
 }
 
+template <bool BATCH>
 __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
-  if (t.a3 > c.a.D) return task_comb_heads(c, t);
+  if constexpr (BATCH) {
+    if (t.a3 > c.a.D) return task_comb_heads(c, t);
+  }
   KAC& a = c.a;
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, h = t.a1, d0 = t.a2, nd = t.a3, S = t.aux, D = a.D;
@@ -1095,51 +1050,29 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   const uint64_t* base = a.part + (size_t)l * a.s_part + ((size_t)b * a.Hkv + g) * a.S_max * HG * PS +
                          (size_t)hh * PS;
   const size_t sstride = (size_t)HG * PS;
-  // every split's dims d0 .. d0+nd, max and sum in one batch: word i of split
-  // q = i / (nd + 2), j = i % (nd + 2) -> att[i] (j < nd: value, nd: max, nd+1: sum)
-  const int W = nd + 2, n = S * W;
+  // every split's dims d0 .. d0+nd, max and sum in one batch, in pairs (nd
+  // even, every word offset even): split q's words are nd / 2 pairs of dims,
+  // then the pair (max, sum), at att[q * (nd + 2) ..]
+  const int W = nd + 2;
   float* sw = s.att;
   if (a.trace && tid() == 0) s.tw[2] = now();
   bool ok = true;
-  if (!(nd & 1) && !((ws_off(a, base) >> 3) & 1)) {
-    // in pairs: split q's words are nd / 2 pairs of dims, then the pair (max, sum)
-    const int WP = W / 2, np = S * WP;
-    const uint32_t ob = ws_off(a, base);
-    for (int bs = 0; bs < np && ok; bs += 2 * NT) {
-      const int t = tid();
-      float v[4];
-      ok = read_pairs<2>(a, [&](int k) -> uint32_t {
-        const int pi = bs + t + k * NT;
-        if (pi >= np) return NO_PAIR;
-        const int q = pi / WP, j = 2 * (pi - q * WP);
-        return ob + 8u * (uint32_t)(q * sstride + (j < nd ? d0 + j : D + (j - nd)));
-      }, v, c.t0, c.ti);
-      if (ok) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int pi = bs + t + k * NT;
-          if (pi < np) *(float2*)(sw + 2 * pi) = make_float2(v[2 * k], v[2 * k + 1]);
-        }
-      }
-    }
-  }
-  else
-  for (int bs = 0; bs < n && ok; bs += 4 * NT) {
+  const int WP = W / 2, np = S * WP;
+  const uint32_t ob = ws_off(a, base);
+  for (int bs = 0; bs < np && ok; bs += 2 * NT) {
     const int t = tid();
     float v[4];
-    const uint64_t* ptr[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = bs + t + k * NT;
-      const int q = i / W, j = i - q * W;
-      ptr[k] = i < n ? base + q * sstride + (j < nd ? d0 + j : D + (j - nd)) : nullptr;
-    }
-    ok = read_words<4>(a, [&](int k) -> const uint64_t* { return ptr[k]; }, v, c.t0, c.ti);
+    ok = read_pairs<2>(a, [&](int k) -> uint32_t {
+      const int pi = bs + t + k * NT;
+      if (pi >= np) return NO_PAIR;
+      const int q = pi / WP, j = 2 * (pi - q * WP);
+      return ob + 8u * (uint32_t)(q * sstride + (j < nd ? d0 + j : D + (j - nd)));
+    }, v, c.t0, c.ti);
     if (ok) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = bs + t + k * NT;
-        if (i < n) sw[i] = v[k];
+      for (int k = 0; k < 2; ++k) {
+        const int pi = bs + t + k * NT;
+        if (pi < np) *(float2*)(sw + 2 * pi) = make_float2(v[2 * k], v[2 * k + 1]);
       }
     }
   }
@@ -2218,6 +2151,7 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
       for (int i = 0; i < TRACE_MARKS; ++i) s.mk[i] = 0;
     }
     bool ok = true;
+    uint32_t units = t.units;  // outputs this task adds to its completion counter
     if (t.flags & TF_STAGE_KV) {
       // the first attention task further on in this unit's list (the planner
       // checked that there is one within STAGE_SCAN tasks)
@@ -2254,13 +2188,14 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
             tt.aux = (uint16_t)split;
           }
           ok = task_attn<HD>(c, tt);
+          if (queue) units += (uint32_t)tt.a3;  // a pulled split adds its pages
           if (!ok || !queue) break;
           if (tid() == 0) s.qnext = nxt - base;
           lds_barrier();
         }
         break;
       }
-      case OP_COMB: ok = task_comb(c, t); break;
+      case OP_COMB: ok = task_comb<BATCH>(c, t); break;
       default:
         if constexpr (BATCH) {
           switch (t.op) {
@@ -2293,7 +2228,7 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
     if (tid() == 0) {
       if (t.signal != NO_CTR)
         __hip_atomic_fetch_add(a.ctr + ((size_t)t.signal * CTR_LINES + blockIdx.x % CTR_LINES) * CTR_STRIDE,
-                               1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                               units, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (a.trace) {
         uint64_t* tr = a.trace + (size_t)ti * TRACE_WORDS;
         tr[0] = c.t0;

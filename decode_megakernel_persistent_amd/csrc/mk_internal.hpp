@@ -72,15 +72,20 @@ constexpr int QUEUE_PAGES = 64;
 
 constexpr uint16_t NO_CTR = 0xFFFF;
 
-// wait_a / wait_b name the producer classes a task depends on (wait_a: the
-// routing decision, wait_b: the data) with their per-step producer counts;
-// signal is the completion counter the task increments. The device waits on
-// the tagged data itself (see TaggedWord); the counters record completions.
+// wait_a / wait_b name the producer classes (completion counters) a task
+// depends on (wait_a: the routing decision, wait_b: the data); the device
+// waits on the tagged data itself (see tag_word), so these name the
+// dependency for the validator and the simulator. signal is the completion
+// counter the task adds `units` to when it finishes: the number of outputs it
+// produced (rows, pages, elements or sequences of its operation), so that a
+// counter grows by its class's whole work per step whatever the tiling.
+// Tasks that produce only partial sums of another task's outputs signal no
+// counter. rsv is zero.
 struct Task {
   uint8_t op, flags;
   uint16_t layer;
   uint16_t wait_a, wait_b;
-  uint16_t cnt_a, cnt_b;
+  uint16_t units, rsv;
   uint16_t signal;
   uint16_t aux;
   int32_t a0, a1, a2, a3;
@@ -90,7 +95,7 @@ static_assert(sizeof(Task) == 32, "task record is 32 bytes");
 // Plan image: u32 header[PLAN_HDR_WORDS], u32 cu_off[n_cu + 1] (task index
 // ranges per list), padding to 32 B, Task tasks[n_tasks] (lists back to back).
 // After the tasks: int32 seq_bound[B], each sequence's context bound.
-constexpr uint32_t PLAN_MAGIC = 0x33504B4Du;  // "MKP3"
+constexpr uint32_t PLAN_MAGIC = 0x34504B4Du;  // "MKP4"
 constexpr int PLAN_HDR_WORDS = 16;
 enum PlanHdr { H_MAGIC = 0, H_NCU = 1, H_NTASKS = 2, H_NCTR = 3, H_TASK_OFF_BYTES = 4,
                H_STAGES = 5, H_BOUND_OFF_BYTES = 6, H_BATCH = 7 };

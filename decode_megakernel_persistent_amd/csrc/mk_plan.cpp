@@ -149,9 +149,10 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
             for (int kb = pass == 0 ? 1 : 0; kb < (pass == 0 ? KB : 1); ++kb) {
               Task t = mk_task(mk::OP_BQKV, l);
               t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_bcomb[l - 1]);
-              if (pass == 1 && KB > 1) t.wait_a = ctr16(p->c_qpart[l]);
-              t.signal = ctr16(pass == 0 ? p->c_qpart[l] : p->c_qkv[l * Hkv + g]);
+              // blocks 1 .. publish partial sums only: no completion counter
+              t.signal = pass == 0 ? mk::NO_CTR : ctr16(p->c_qkv[l * Hkv + g]);
               t.a0 = g; t.a1 = s0; t.a2 = std::min(8 * QKV_BLOCKS, p->n_pairs_g - s0);
+              t.units = (uint16_t)(pass == 0 ? 0 : 2 * t.a2);
               t.a3 = kb | (KB << 8);
               st.push_back(t);
             }
@@ -168,6 +169,7 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
             t.wait_b = ctr16(p->c_qkv[l * Hkv + g]);
             t.signal = ctr16(p->c_attn[l * Hkv + g]);
             t.a0 = b; t.a1 = g; t.a2 = s0; t.a3 = c; t.aux = (uint16_t)si++;
+            t.units = (uint16_t)c;
             st.push_back(t);
           }
         }
@@ -189,6 +191,7 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
             t.wait_b = ctr16(p->c_attn[l * Hkv + h / HG]);
             t.signal = ctr16(p->c_comb[l]);
             t.a0 = b; t.a1 = h; t.a2 = d0; t.a3 = nd; t.aux = (uint16_t)p->n_split[b];
+            t.units = (uint16_t)nd;
             st.push_back(t);
           }
       stages.push_back(st);
@@ -203,9 +206,9 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
           for (int kb = pass == 0 ? 1 : 0; kb < (pass == 0 ? KB : 1); ++kb) {
             Task t = mk_task(mk::OP_BO, l);
             t.wait_b = ctr16(p->c_comb[l]);
-            if (pass == 1 && KB > 1) t.wait_a = ctr16(p->c_opart[l]);
-            t.signal = ctr16(pass == 0 ? p->c_opart[l] : p->c_o[l]);
+            t.signal = pass == 0 ? mk::NO_CTR : ctr16(p->c_o[l]);
             t.a0 = kb; t.a1 = s0; t.a2 = std::min(16 * O_BLOCKS, H - s0); t.a3 = KB;
+            t.units = (uint16_t)(pass == 0 ? 0 : t.a2);
             st.push_back(t);
           }
         stages.push_back(st);
@@ -220,6 +223,7 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
           t.wait_b = ctr16(p->c_o[l]);
           t.signal = ctr16(p->c_router[l]);
           t.a0 = b; t.a1 = r0; t.a2 = n;
+          t.units = (uint16_t)n;
           rt.push_back(t);
         }
       stages.push_back(rt);
@@ -230,6 +234,7 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
         t.wait_b = ctr16(p->c_router[l]);
         t.signal = ctr16(p->c_topk[l]);
         t.a0 = b;
+        t.units = 1;
         tk.push_back(t);
       }
       stages.push_back(tk);
@@ -247,6 +252,7 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
           t.a1 = q < (int)fr.size() ? fr[q].first : 0;
           t.a2 = q < (int)fr.size() ? fr[q].second : 0;
           t.a3 = q < (int)hr.size() ? (hr[q].first << 16) | hr[q].second : 0;
+          t.units = (uint16_t)(t.a2 + (t.a3 & 0xFFFF));
           st.push_back(t);
         }
       stages.push_back(st);
@@ -263,6 +269,7 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
           t.wait_b = ctr16(p->c_expert[l]);
           t.signal = ctr16(p->c_bcomb[l]);
           t.a0 = b; t.a1 = s0; t.a2 = c;
+          t.units = (uint16_t)c;
           st.push_back(t);
         }
       stages.push_back(st);
@@ -277,6 +284,7 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
       t.wait_b = ctr16(p->c_bcomb[L - 1]);
       t.signal = ctr16(p->c_lm);
       t.a1 = s0; t.a2 = std::min(rows, m.vocab - s0); t.a3 = i++;
+      t.units = (uint16_t)t.a2;
       st.push_back(t);
     }
     p->n_lm = i;
@@ -313,6 +321,11 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   if (F <= 0) return fail(MK_EINVAL, "mk_plan: ffn width must be positive");
   if (moe && (m->top_k <= 0 || m->top_k > m->n_experts || m->top_k > 16 || m->n_experts > 256))
     return fail(MK_EUNSUPPORTED, "mk_plan: MoE needs 0 < top_k <= min(16, n_experts), n_experts <= 256");
+  // activations pass between tasks as pairs of tagged words read with one
+  // 16-byte load: every gathered run (hidden, heads x dim, top_k x FFN,
+  // router logits) has an even length and starts at an even word
+  if (moe && m->n_experts % 2)
+    return fail(MK_EUNSUPPORTED, "mk_plan: the number of experts must be even");
   int tc, cpl;
   for (int K : {H, Hq * D, F})
     if (!mk::gemv_map(K, &tc, &cpl))
@@ -435,9 +448,6 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   int pps = o && o->attn_split_pages > 0 ? o->attn_split_pages : (pg_total + n_cu - 1) / n_cu;
   const bool queue = !(flags & MK_PLAN_NO_ATTN_QUEUE) && B == 1 && (flags & MK_PLAN_ATTN_QUEUE);
   if (queue) pps = mk::QUEUE_PAGES;
-  // QKV tiles on one half of the units, attention splits on the other half
-  const bool split_units = !batch && !queue && (flags & MK_PLAN_SPLIT_UNITS) && n_cu >= 2 * Hkv;
-  if (split_units && !(o && o->attn_split_pages > 0)) pps = (pg_total + n_cu / 2 - 1) / (n_cu / 2);
   // a batch: about four splits per unit, so that ragged lengths even out
   if (batch && !(o && o->attn_split_pages > 0)) pps = std::max(8, ceil_div(pg_total, 4 * n_cu));
   p->attn_queue = queue;
@@ -448,8 +458,6 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + ls + "][" + std::to_string(g) + "]"));
       p->c_comb.push_back(new_ctr("comb[" + ls + "]"));
       p->c_o.push_back(new_ctr("o[" + ls + "]"));
-      p->c_opart.push_back(p->o_kb > 1 ? new_ctr("opart[" + ls + "]") : -1);
-      p->c_qpart.push_back(p->q_kb > 1 ? new_ctr("qpart[" + ls + "]") : -1);
       p->c_router.push_back(moe ? new_ctr("router[" + ls + "]") : -1);
       p->c_topk.push_back(moe ? new_ctr("topk[" + ls + "]") : -1);
       p->c_expert.push_back(new_ctr("expert[" + ls + "]"));
@@ -507,7 +515,10 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     }
   }
   p->S_max = *std::max_element(p->n_split.begin(), p->n_split.end());
-  p->comb_dim_tasks = std::max(1, std::min(D / 8, n_cu / std::max(1, B * Hq)));
+  // combine tasks per (sequence, query head): a power of two (D is 64 or
+  // 128, so every task takes an even run of dims), at most D / 8
+  p->comb_dim_tasks = 1;
+  while (2 * p->comb_dim_tasks <= D / 8 && 2 * p->comb_dim_tasks * B * Hq <= n_cu) p->comb_dim_tasks *= 2;
   while (p->comb_dim_tasks < D / 8 && (size_t)p->S_max * (ceil_div(D, p->comb_dim_tasks) + 2) > 8192)
     p->comb_dim_tasks *= 2;  // fewer dims per combine task when there are many splits
 
@@ -524,7 +535,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     // QKV: tiles of rotary pairs within one kv group
     {
       std::vector<Task> st;
-      int per_g = std::max(1, (split_units ? n_cu / 2 : n_cu) / Hkv);
+      int per_g = std::max(1, n_cu / Hkv);
       const int cap_pairs = std::max(1, rows_max(H) / 2);
       per_g = std::max(per_g, ceil_div(p->n_pairs_g, cap_pairs));
       for (int g = 0; g < Hkv; ++g)
@@ -533,6 +544,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
           t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_expert[l - 1]);
           t.signal = ctr16(p->c_qkv[l * Hkv + g]);
           t.a0 = g; t.a1 = s0; t.a2 = c;
+          t.units = (uint16_t)(2 * c);
           st.push_back(t);
         }
       stages.push_back(st);
@@ -546,6 +558,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         t.wait_b = ctr16(p->c_qkv[l * Hkv]);
         t.signal = ctr16(p->c_attn[l * Hkv]);
         t.a0 = p->c_queue[l]; t.a1 = p->n_split[0]; t.a2 = mk::QUEUE_PAGES; t.a3 = n_cu;
+        t.units = 0;  // each split pulled adds its pages
         st.push_back(t);
       }
       stages.push_back(st);
@@ -559,6 +572,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
             t.wait_b = ctr16(p->c_qkv[l * Hkv + g]);
             t.signal = ctr16(p->c_attn[l * Hkv + g]);
             t.a0 = b; t.a1 = g; t.a2 = s0; t.a3 = c; t.aux = (uint16_t)si++;
+            t.units = (uint16_t)c;
             st.push_back(t);
           }
         }
@@ -576,6 +590,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
             t.wait_b = ctr16(p->c_attn[l * Hkv + h / HG]);
             t.signal = ctr16(p->c_comb[l]);
             t.a0 = b; t.a1 = h; t.a2 = d0; t.a3 = nd; t.aux = (uint16_t)p->n_split[b];
+            t.units = (uint16_t)nd;
             st.push_back(t);
           }
       stages.push_back(st);
@@ -589,6 +604,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         t.wait_b = ctr16(p->c_comb[l]);
         t.signal = ctr16(p->c_o[l]);
         t.a1 = s0; t.a2 = c;
+        t.units = (uint16_t)c;
         st.push_back(t);
       }
       stages.push_back(st);
@@ -603,6 +619,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         t.wait_b = ctr16(p->c_o[l]);
         t.signal = ctr16(p->c_router[l]);
         t.a1 = s0; t.a2 = c;
+        t.units = (uint16_t)c;
         st.push_back(t);
       }
       stages.push_back(st);
@@ -644,6 +661,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
           if (moe && gu[i][1] == 0 && gu[i][2] == 0) t.flags |= mk::TF_WRITE_TOPK;
         }
         if (i < dn.size()) t.a3 = (dn[i].first << 16) | dn[i].second;
+        t.units = (uint16_t)(t.a2 + (t.a3 & 0xFFFF));
         st.push_back(t);
       }
       stages.push_back(st);
@@ -663,6 +681,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       t.wait_b = ctr16(p->c_expert[L - 1]);
       t.signal = ctr16(p->c_lm);
       t.a1 = s0; t.a2 = std::min(rows, m->vocab - s0); t.a3 = i++;
+      t.units = (uint16_t)t.a2;
       st.push_back(t);
     }
     p->n_lm = i;
@@ -678,22 +697,20 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   }
   p->n_stages = (int)stages.size();
 
-  // producer counts -> targets, then the per-epoch counts carried by the waits;
-  // a queue counter gains one per split taken and one per queue task's final,
-  // empty pull
+  // targets: the outputs per step of each counter's class (the sum of its
+  // tasks' units); the attention splits pulled from a queue add their pages
+  // (every page below the bound, per kv head); a queue counter gains one per
+  // split taken and one per queue task's final, empty pull
   for (auto& st : stages)
     for (auto& t : st)
-      if (t.signal != mk::NO_CTR) p->targets[t.signal]++;
+      if (t.signal != mk::NO_CTR) p->targets[t.signal] += t.units;
+  if (queue)
+    for (int l = 0; l < L; ++l) p->targets[p->c_attn[l * Hkv]] = (uint32_t)(Hkv * pg_bound);
   for (int32_t q : p->c_queue) p->targets[q] = (uint32_t)(Hkv * p->n_split[0] + n_cu);
-  for (auto& st : stages)
-    for (auto& t : st) {
-      if (t.wait_a != mk::NO_CTR) t.cnt_a = (uint16_t)p->targets[t.wait_a];
-      if (t.wait_b != mk::NO_CTR) t.cnt_b = (uint16_t)p->targets[t.wait_b];
-    }
   for (auto v : p->targets)
-    if (v == 0 || v > 65535) {
+    if (v == 0) {
       delete p;
-      return fail(MK_EUNSUPPORTED, "mk_plan: counter with 0 or > 65535 producers");
+      return fail(MK_EUNSUPPORTED, "mk_plan: counter with no producer");
     }
 
   // deal every stage round-robin over the units, continuing where the last
@@ -950,7 +967,7 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
       for (auto& [key, v] : outs) got[key].insert(v);
       if (t.signal != mk::NO_CTR) {
         if (t.signal >= p->targets.size()) return fail(MK_EINVAL, "validate: signal counter out of range");
-        producers[t.signal]++;
+        producers[t.signal] += t.units;
         if (ctr_stage[t.signal] >= 0 && ctr_stage[t.signal] != st)
           return fail(MK_EINVAL, "validate: counter signalled from two stages");
         ctr_stage[t.signal] = st;
@@ -971,20 +988,25 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
       return fail(MK_EINVAL, "validate: outputs of " + key + " not covered exactly once");
   }
   if (got.size() != want.size()) return fail(MK_EINVAL, "validate: tasks of an unexpected kind");
+  // a counter's target is the outputs its tasks produce per step (the
+  // attention splits of a queue add their pages on the device: every page
+  // below the bound, per kv head)
   std::set<int32_t> queues(p->c_queue.begin(), p->c_queue.end());
+  if (p->attn_queue)
+    for (int l = 0; l < L; ++l) producers[p->c_attn[l * m.n_kv_heads]] += m.n_kv_heads * ((p->bound + 15) / 16);
   for (size_t c = 0; c < p->targets.size(); ++c)
     if (!queues.count((int32_t)c) && producers[c] != p->targets[c])
-      return fail(MK_EINVAL, "validate: counter " + p->ctr_name[c] + " target != producer count");
+      return fail(MK_EINVAL, "validate: counter " + p->ctr_name[c] + " target != the outputs of its tasks");
   k = 0;
   for (int cu = 0; cu < p->n_cu; ++cu)
     for (auto& t : p->lists[cu]) {
       int st = p->stage_of_task[k++];
-      for (auto [w, cnt] : {std::pair<uint16_t, uint16_t>{t.wait_a, t.cnt_a}, {t.wait_b, t.cnt_b}}) {
+      for (uint16_t w : {t.wait_a, t.wait_b}) {
         if (w == mk::NO_CTR) continue;
         if (w >= p->targets.size()) return fail(MK_EINVAL, "validate: wait counter out of range");
-        if (cnt != p->targets[w]) return fail(MK_EINVAL, "validate: wait count != target of " + p->ctr_name[w]);
         if (ctr_stage[w] >= st) return fail(MK_EINVAL, "validate: task waits on a counter of its own or a later stage");
       }
+      if (t.signal == mk::NO_CTR && t.units != 0) return fail(MK_EINVAL, "validate: units without a counter");
     }
   return MK_OK;
 }
@@ -992,10 +1014,14 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
 // ------------------------------------------------------------------ simulation
 
 // Runs the per-unit lists on n_cu virtual units under seeded random
-// interleavings. A task may start when its waits are satisfied; an expert
-// task first publishes its activations (gate/up part) and then waits until
-// every expert task of its layer has published before it completes (down
-// part). Every task's reads are checked against the completed producers.
+// interleavings, modelling the waits the device performs: a task starts only
+// once every task producing data it reads has finished (the device polls the
+// tagged words themselves; here the producers of a word are taken by class,
+// a superset of the words a task reads, so a deadlock on the device is a
+// deadlock here). Two-phase tasks: an expert task first publishes its gate/up
+// activations, then its down part waits until every expert task of its layer
+// has published. A unit runs its list in order, one task at a time. Every
+// run must finish (no deadlock) with every counter at epoch x target.
 extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t n_runs) {
   if (!p || n_runs <= 0) return fail(MK_EINVAL, "mk_plan_simulate: bad args");
   const auto& m = p->m;
@@ -1003,21 +1029,33 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
   const bool moe = m.n_experts > 0;
   std::mt19937_64 rng(seed);
   std::vector<uint64_t> ctr(p->targets.size(), 0);
-  auto slot = [&](int op, int l, int g) { return ((size_t)op * (L + 1) + l) * (Hkv + 1) + g; };
-  const size_t n_slots = (mk::OP_COUNT + 1) * (L + 1) * (Hkv + 1);
+  // task kinds: the op, or a kind of its own for the partial sums of a split
+  // reduction (batch QKV / O blocks 1 ..), which block 0 reads
+  constexpr int K_QPART = mk::OP_COUNT, K_OPART = mk::OP_COUNT + 1, N_KIND = mk::OP_COUNT + 2;
+  auto kind = [](const Task& t) -> int {
+    if (t.op == mk::OP_BQKV && (t.a3 & 0xFF) != 0) return K_QPART;
+    if (t.op == mk::OP_BO && t.a0 != 0) return K_OPART;
+    return t.op;
+  };
+  auto slot = [&](int k, int l, int g) { return ((size_t)k * (L + 1) + l) * (Hkv + 1) + g; };
+  const size_t n_slots = (size_t)N_KIND * (L + 1) * (Hkv + 1);
   std::vector<uint32_t> total(n_slots, 0);
+  auto group_of = [&](const Task& t) -> int {  // kv group of a QKV or attention task, Hkv: any
+    if (t.op == mk::OP_ATTN) return (t.flags & mk::TF_QUEUE) ? Hkv : t.a1;
+    if (t.op == mk::OP_QKV || t.op == mk::OP_BQKV) return t.a0;
+    return Hkv;
+  };
   for (int cu = 0; cu < p->n_cu; ++cu)
     for (auto& t : p->lists[cu]) {
-      total[slot(t.op, t.layer, Hkv)]++;
-      if (t.op == mk::OP_ATTN && (t.flags & mk::TF_QUEUE)) {
-        for (int g = 0; g < Hkv; ++g) total[slot(t.op, t.layer, g)]++;
-      } else if (t.op == mk::OP_QKV || t.op == mk::OP_BQKV || t.op == mk::OP_ATTN) {
-        total[slot(t.op, t.layer, t.op == mk::OP_ATTN ? t.a1 : t.a0)]++;
+      total[slot(kind(t), t.layer, Hkv)]++;
+      const int g = group_of(t);
+      if (t.op == mk::OP_ATTN && g == Hkv) {
+        for (int gg = 0; gg < Hkv; ++gg) total[slot(kind(t), t.layer, gg)]++;
+      } else if (g < Hkv) {
+        total[slot(kind(t), t.layer, g)]++;
       }
     }
   const int qkv_op = p->batch ? mk::OP_BQKV : mk::OP_QKV;
-  // two-phase tasks: gate/up published first, the down part waits for every
-  // expert task of its layer
   auto two_phase = [](int op) { return op == mk::OP_EXPERT || op == mk::OP_BEXP; };
   for (int run = 0; run < n_runs; ++run) {
     const uint64_t epoch = (uint64_t)run + 1;
@@ -1025,27 +1063,25 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
     std::vector<uint32_t> published(L, 0);      // expert gate/up parts finished per layer
     std::vector<size_t> head(p->n_cu, 0);
     std::vector<char> phase(p->n_cu, 0);        // expert task at the head: 1 = published
-    auto all_done = [&](int op, int l, int g) { return done[slot(op, l, g)] == total[slot(op, l, g)]; };
-    auto waits_ok = [&](const Task& t) {
-      if (t.wait_a != mk::NO_CTR && ctr[t.wait_a] < epoch * t.cnt_a) return false;
-      if (t.wait_b != mk::NO_CTR && ctr[t.wait_b] < epoch * t.cnt_b) return false;
-      return true;
-    };
-    // what each task reads must be complete when it runs (independent of the counters)
+    auto all_done = [&](int k, int l, int g) { return done[slot(k, l, g)] == total[slot(k, l, g)]; };
+    // the data a task reads: complete when every producer (by class) finished
     auto inputs_ok = [&](const Task& t) -> bool {
-      int l = t.layer;
-      switch (t.op) {
-        case mk::OP_QKV: return l == 0 || all_done(mk::OP_EXPERT, l - 1, Hkv);
-        case mk::OP_ATTN:
-          return (t.flags & mk::TF_QUEUE) ? all_done(qkv_op, l, Hkv) : all_done(qkv_op, l, t.a1);
+      const int l = t.layer;
+      const int ffn_op = p->batch ? mk::OP_BCOMB : mk::OP_EXPERT;
+      switch (kind(t)) {
+        case mk::OP_QKV: return l == 0 || all_done(ffn_op, l - 1, Hkv);
+        case mk::OP_ATTN: return all_done(qkv_op, l, group_of(t));
         case mk::OP_COMB: return all_done(mk::OP_ATTN, l, t.a1 / HG);
         case mk::OP_O: return all_done(mk::OP_COMB, l, Hkv);
         case mk::OP_ROUTER: return all_done(p->batch ? mk::OP_BO : mk::OP_O, l, Hkv);
         case mk::OP_EXPERT: return all_done(mk::OP_O, l, Hkv) && (!moe || all_done(mk::OP_ROUTER, l, Hkv));
         case mk::OP_LM: return all_done(mk::OP_EXPERT, L - 1, Hkv);
         case mk::OP_FINAL: return all_done(mk::OP_LM, 0, Hkv);
-        case mk::OP_BQKV: return l == 0 || all_done(mk::OP_BCOMB, l - 1, Hkv);
-        case mk::OP_BO: return all_done(mk::OP_COMB, l, Hkv);
+        case K_QPART: return l == 0 || all_done(ffn_op, l - 1, Hkv);
+        case mk::OP_BQKV:
+          return (l == 0 || all_done(ffn_op, l - 1, Hkv)) && all_done(K_QPART, l, Hkv);
+        case K_OPART: return all_done(mk::OP_COMB, l, Hkv);
+        case mk::OP_BO: return all_done(mk::OP_COMB, l, Hkv) && all_done(K_OPART, l, Hkv);
         case mk::OP_TOPK:
           return all_done(mk::OP_BO, l, Hkv) && (!(t.flags & mk::TF_LOGITS) || all_done(mk::OP_ROUTER, l, Hkv));
         case mk::OP_BEXP: return all_done(mk::OP_BO, l, Hkv) && (!moe || all_done(mk::OP_TOPK, l, Hkv));
@@ -1064,7 +1100,7 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
         const Task& t = p->lists[cu][head[cu]];
         if (two_phase(t.op) && phase[cu] == 1) {
           if (published[t.layer] == total[slot(t.op, t.layer, Hkv)]) runnable.push_back(cu);
-        } else if (waits_ok(t)) {
+        } else if (inputs_ok(t)) {
           runnable.push_back(cu);
         }
       }
@@ -1075,7 +1111,7 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
           if (head[cu] < p->lists[cu].size()) {
             const Task& t = p->lists[cu][head[cu]];
             msg += " unit " + std::to_string(cu) + " op " + std::to_string(t.op) + " layer " +
-                   std::to_string(t.layer) + " waits " +
+                   std::to_string(t.layer) + " reads " +
                    (t.wait_b != mk::NO_CTR ? p->ctr_name[t.wait_b] : std::string("-"));
             ++shown;
           }
@@ -1088,30 +1124,27 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
         int cu = runnable[i];
         const Task& t = p->lists[cu][head[cu]];
         if (two_phase(t.op) && phase[cu] == 0) {
-          if (!inputs_ok(t))
-            return fail(MK_ESTATE, "simulate: expert layer " + std::to_string(t.layer) +
-                                       " ran before its producers finished");
           phase[cu] = 1;
           published[t.layer]++;
           continue;
         }
-        if (!two_phase(t.op) && !inputs_ok(t))
-          return fail(MK_ESTATE, "simulate: op " + std::to_string(t.op) + " layer " +
-                                     std::to_string(t.layer) + " ran before its producers finished");
         phase[cu] = 0;
         head[cu]++;
         remaining--;
-        done[slot(t.op, t.layer, Hkv)]++;
-        if (t.op == mk::OP_QKV || t.op == mk::OP_BQKV) done[slot(t.op, t.layer, t.a0)]++;
-        if (t.op == mk::OP_ATTN && (t.flags & mk::TF_QUEUE)) {
-          for (int g = 0; g < Hkv; ++g) done[slot(t.op, t.layer, g)]++;
-        } else if (t.op == mk::OP_ATTN) {
-          done[slot(t.op, t.layer, t.a1)]++;
+        done[slot(kind(t), t.layer, Hkv)]++;
+        const int g = group_of(t);
+        if (t.op == mk::OP_ATTN && g == Hkv) {
+          for (int gg = 0; gg < Hkv; ++gg) done[slot(kind(t), t.layer, gg)]++;
+        } else if (g < Hkv) {
+          done[slot(kind(t), t.layer, g)]++;
         }
-        if (t.signal != mk::NO_CTR) ctr[t.signal]++;
+        if (t.signal != mk::NO_CTR) ctr[t.signal] += t.units;
       }
     }
-    for (int32_t q : p->c_queue) ctr[q] += p->targets[q];  // the pulls of the queue tasks
+    // the queue tasks' pulls, and the pages of the splits they took
+    for (int32_t q : p->c_queue) ctr[q] += p->targets[q];
+    if (p->attn_queue)
+      for (int l = 0; l < L; ++l) ctr[p->c_attn[l * Hkv]] += (uint64_t)Hkv * ((p->bound + 15) / 16);
     for (size_t c = 0; c < ctr.size(); ++c)
       if (ctr[c] != epoch * p->targets[c])
         return fail(MK_ESTATE, "simulate: counter " + p->ctr_name[c] + " ends epoch off target");
@@ -1146,6 +1179,14 @@ extern "C" mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t l
   *off = p->ws_off[which] + (per_layer ? (size_t)layer * p->ws_stride[which] : 0);
   *bytes = p->ws_layer_bytes[which];
   return MK_OK;
+}
+
+extern "C" const char* mk_plan_counter_name(const mk_plan_t* p, int32_t i) {
+  if (!p || i < 0 || i >= (int32_t)p->ctr_name.size()) {
+    fail(MK_EINVAL, "mk_plan_counter_name: no such counter");
+    return nullptr;
+  }
+  return p->ctr_name[i].c_str();
 }
 
 extern "C" mk_status mk_plan_counter_targets(const mk_plan_t* p, uint32_t* out, int32_t n) {

@@ -26,9 +26,7 @@ struct mk_plan {
   std::vector<int32_t> c_comb, c_o, c_router, c_expert;  // [L]
   std::vector<int32_t> c_queue;  // [L] attention split queue (queue mode)
   std::vector<int32_t> c_topk, c_bcomb;  // [L] batch: top-k per sequence, expert combine
-  std::vector<int32_t> c_opart;          // [L] batch: partial O projections (-1: not split)
   int o_kb = 1;                          // batch: reduction blocks of the O projection
-  std::vector<int32_t> c_qpart;          // [L] batch: partial QKV projections (-1: not split)
   int q_kb = 1;                          // batch: reduction blocks of the QKV projection
   int q_rb = 0;                          // batch: QKV row blocks (tasks per reduction block)
   int32_t c_lm = -1;

@@ -118,9 +118,9 @@ class Decoder:
             raise MkError(st, msg)
 
     def counters(self):
-        """Completion counts per counter (sum of its lines), as a host int64 tensor."""
-        c = self.ctr.view(-1, CTR_LINES, 16)[:, :, 0].to(torch.int64)
-        return c.sum(dim=1).cpu()
+        """Completion counts per counter (sum of its lines modulo 2^32), as a host int64 tensor."""
+        c = self.ctr.view(-1, CTR_LINES, 16)[:, :, 0].to(torch.int64) & 0xFFFFFFFF
+        return c.sum(dim=1).cpu() % (1 << 32)
 
     def buffer(self, which, layer=0):
         """Workspace sub-buffer (MK_BUF_*) of one layer: its tagged u64 words (device view)."""

@@ -103,11 +103,6 @@ typedef struct mk_plan_opts {
  * instead of one static split per task. Off unless asked for. */
 #define MK_PLAN_ATTN_QUEUE 1     /* use the queue (batch 1) */
 #define MK_PLAN_NO_ATTN_QUEUE 2  /* never use it */
-/* Batch 1, static splits: the QKV tiles of a layer go to one half of the
- * compute units and its attention splits to the other half, so that the
- * attention units request their KV pages while the QKV units stream weights
- * and compute, instead of after them. */
-#define MK_PLAN_SPLIT_UNITS 4
 
 typedef struct mk_plan mk_plan_t;   /* opaque host object */
 typedef struct mk_pool mk_pool_t;   /* opaque host object */
@@ -154,8 +149,11 @@ typedef struct mk_step_buffers {
                                                first step; thereafter every step on this
                                                workspace uses a larger epoch */
   uint32_t* counters; size_t counter_bytes; /* completion counters, 8 sub-counters of one
-                                               64-byte line each per counter; each step adds
-                                               the counter's target to the sum of its lines */
+                                               64-byte line each per counter, zero-filled
+                                               before the first step; every finished task adds
+                                               the number of outputs it produced, so each step
+                                               adds the counter's target to the sum of its
+                                               lines (modulo 2^32) */
   uint32_t* status;                         /* 4 words, zeroed once */
   uint64_t* trace; size_t trace_bytes;      /* NULL (no tracing), or 16 u64 per task
                                                (128 * mk_plan_n_tasks bytes), indexed by
@@ -196,7 +194,7 @@ mk_status mk_step_bytes(const mk_model_desc* m, int32_t batch, const int32_t* se
 /* Build the task lists, counters and workspace layout for one batch shape
  * (megakernel page, caption of Image 2: the host decomposes the step into
  * tasks of one tile of one operation each and deals them round-robin over
- * the compute units). Batch 1 runs GEMV tiles; a batch of 2 .. 64 sequences
+ * the compute units). Batch 1 runs GEMV tiles; a batch of 2 .. 32 sequences
  * (continuous batching with ragged contexts, megakernel page, "Inside the
  * megakernel serving engine": continuous batching over a paged cache) runs
  * every projection as MFMA tiles over all sequences, a top-k task per
@@ -204,11 +202,15 @@ mk_status mk_step_bytes(const mk_model_desc* m, int32_t batch, const int32_t* se
 mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* b, const mk_plan_opts* o,
                   mk_plan_t** out);
 /* Coverage (every output row / KV page exactly once), counter targets equal
- * producer counts, per-list stage order. MK_OK or MK_EINVAL with a message. */
+ * the outputs of the tasks that signal them, per-list stage order, waits on
+ * earlier stages only. MK_OK or MK_EINVAL with a message. */
 mk_status mk_plan_validate(const mk_plan_t* p);
 /* Execute the lists on n_cu virtual compute units under seeded random
- * interleavings, n_runs times; fails (MK_ESTATE) on a read before its
- * producers finished or on a deadlock (message names the blocked tasks). */
+ * interleavings, n_runs times, each unit in list order and each task
+ * starting only once every producer of the data it reads has finished (the
+ * waits the device performs, taken per producer class); fails (MK_ESTATE) on
+ * a deadlock (message names the blocked tasks) or a counter that does not
+ * end at epoch x target. */
 mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t n_runs);
 size_t mk_plan_device_bytes(const mk_plan_t* p);
 size_t mk_plan_workspace_bytes(const mk_plan_t* p);
@@ -243,8 +245,19 @@ enum { MK_BUF_XATTN = 0, MK_BUF_XFFN = 1, MK_BUF_Q = 2, MK_BUF_PART = 3, MK_BUF_
        MK_BUF_ROUTE = 9, MK_BUF_Y = 10, MK_BUF_OPART = 11, MK_BUF_QPART = 12 };
 mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t layer, size_t* offset,
                          size_t* bytes);
-/* The plan's per-epoch counter targets, [n_counters] (host). */
+/* The plan's per-step counter targets, [n_counters] (host): for each
+ * completion counter, the outputs its class produces in one step -- QKV rows
+ * of a kv group, (sequence, page) pairs of a kv head's attention, combined
+ * attention elements, O rows, router rows, selected sequences (batch top-k),
+ * expert gate/up outputs plus down rows, expert-combine rows (batch), LM-head
+ * rows. An attention queue's head counter (batch 1 with MK_PLAN_ATTN_QUEUE)
+ * instead gains one per split taken plus one per queue task. */
 mk_status mk_plan_counter_targets(const mk_plan_t* p, uint32_t* out, int32_t n);
+/* Name of counter i: "<class>[<layer>]" or "<class>[<layer>][<kv head>]"
+ * (classes qkv, attn, comb, o, router, topk, expert, ffn, queue) or "lm";
+ * the string lives as long as the plan. NULL (and mk_last_error) if i is out
+ * of range. */
+const char* mk_plan_counter_name(const mk_plan_t* p, int32_t i);
 void mk_plan_free(mk_plan_t* p);
 
 /* ---- one decode step (asynchronous on hip_stream) ----

@@ -5,8 +5,9 @@
   model under a seeded random sequence of leases, extensions and releases;
 - the exported plan image, decoded here from its documented record format,
   covers exactly the oracle's work enumeration (every output row, every
-  (sequence, kv head, page), every (sequence, query head)) once, and every
-  counter's target equals the number of tasks that signal it;
+  (sequence, kv head, page), every (sequence, query head)) once; every
+  counter's target equals the outputs of the tasks that signal it, and the
+  oracle's completion count of that counter's class, looked up by name;
 - plans validate, simulate without deadlock under random interleavings,
   and are byte-identical when built twice;
 - calls outside the declared bounds fail before anything launches.
@@ -21,13 +22,14 @@ import pytest
 import decode_megakernel_persistent_amd as mk
 import oracle as O
 from fixtures.session import lease_pages, spec
+from gpu_util import check_counters_against_oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # Task record (32 bytes): u8 op, u8 flags, u16 layer, u16 wait_a, u16 wait_b,
-# u16 cnt_a, u16 cnt_b, u16 signal, u16 aux, i32 a0, a1, a2, a3.
+# u16 units, u16 rsv, u16 signal, u16 aux, i32 a0, a1, a2, a3.
 TASK = np.dtype([("op", "u1"), ("flags", "u1"), ("layer", "<u2"), ("wait_a", "<u2"),
-                 ("wait_b", "<u2"), ("cnt_a", "<u2"), ("cnt_b", "<u2"), ("signal", "<u2"),
+                 ("wait_b", "<u2"), ("units", "<u2"), ("rsv", "<u2"), ("signal", "<u2"),
                  ("aux", "<u2"), ("a0", "<i4"), ("a1", "<i4"), ("a2", "<i4"), ("a3", "<i4")])
 OP_QKV, OP_ATTN, OP_COMB, OP_O, OP_ROUTER, OP_EXPERT = range(1, 7)
 OP_LM, OP_FINAL = 8, 9
@@ -114,7 +116,7 @@ def test_pool_lease_is_all_or_nothing():
 
 def decode_plan(img):
     hdr = np.frombuffer(img, dtype="<u4", count=16)
-    assert hdr[0] == 0x33504B4D
+    assert hdr[0] == 0x34504B4D
     n_cu, n_tasks, n_ctr, off = int(hdr[1]), int(hdr[2]), int(hdr[3]), int(hdr[4])
     cu_off = np.frombuffer(img, dtype="<u4", count=n_cu + 1, offset=64)
     tasks = np.frombuffer(img, dtype=TASK, count=n_tasks, offset=off)
@@ -252,20 +254,25 @@ def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
         for k, items in got.items():
             assert len(items) == len(set(items)), f"{k}: covered more than once"
             assert set(items) == want[k], f"{k}: coverage differs from the oracle's work"
-        # counter targets = number of tasks signalling each counter (a queue
-        # counter: one pull per split plus each queue task's empty last pull);
-        # waits carry the target
+        # counter targets = outputs of the tasks signalling each counter (a
+        # queue counter: one pull per split plus each queue task's empty last
+        # pull; queued splits add their pages on the device)
         tg = np.array(mk.mk_plan_counter_targets(p), dtype=np.int64)
-        sig = tasks["signal"][tasks["signal"] != NO_CTR].astype(np.int64)
-        want_tg = np.bincount(sig, minlength=n_ctr)
+        has = tasks["signal"] != NO_CTR
+        want_tg = np.bincount(tasks["signal"][has].astype(np.int64),
+                              weights=tasks["units"][has].astype(np.float64), minlength=n_ctr).astype(np.int64)
+        assert not tasks["units"][~has].any() and not tasks["rsv"].any()
+        names = mk.mk_plan_counter_names(p)
         qt = tasks[(tasks["op"] == OP_ATTN) & ((tasks["flags"] & TF_QUEUE) != 0)]
         for q in set(qt["a0"].tolist()):
             t0 = qt[qt["a0"] == q][0]
             want_tg[q] = w["model"]["n_kv_heads"] * int(t0["a1"]) + int(t0["a3"])
+            want_tg[names.index("attn[%d]" % int(t0["layer"]))] += (
+                w["model"]["n_kv_heads"] * -(-bound // w["model"]["page_tokens"]))
         assert np.array_equal(want_tg, tg)
-        for wf, cf in (("wait_a", "cnt_a"), ("wait_b", "cnt_b")):
-            m_ = tasks[wf] != NO_CTR
-            assert np.array_equal(tasks[cf][m_].astype(np.int64), tg[tasks[wf][m_].astype(np.int64)])
+        # ... and the oracle's completion count of each counter's class
+        exp = O.expected_counters(w["model"], ctx_bounds(w) if w["batch"] > 1 else [bound], want)
+        check_counters_against_oracle(names, tg, exp)
         # at most one expert task per compute unit and layer (their down parts wait on each other)
         for cu in range(n_cu):
             lt = tasks[int(cu_off[cu]):int(cu_off[cu + 1])]
