@@ -62,7 +62,7 @@ def main():
     torch.cuda.set_device(dev)
     copy_gbs = stream_copy_probe(torch, mk, dev)
     r = run_workload(torch, mk, dev, a.workload, a.steps, a.warmup, a)
-    w, dec, pool, W, tok0 = r.pop("w"), r.pop("dec"), r.pop("pool"), r.pop("weights"), r.pop("tok0")
+    w, dec, pool, W = r.pop("w"), r.pop("dec"), r.pop("pool"), r.pop("weights")
     m, B, L = w["model"], w["batch"], w["model"]["n_layers"]
     tok_s, ms_step, per, wall = r["tok_s"], r["ms_step"], r["per"], r["wall"]
     bytes_step, wsum, ksum = r["bytes_step"], r["wsum"], r["ksum"]
@@ -81,7 +81,7 @@ def main():
 
     cpu = None
     if a.cpu_steps > 0:
-        cpu = cpu_baseline(w, a, dec, tok0)
+        cpu = cpu_baseline(w, a, r["hist"], r["ids"], W)
 
     # the metric's second number: the same model at batch 32 (ragged contexts,
     # one shared pool), with the weights already resident
@@ -94,6 +94,7 @@ def main():
         r32 = run_workload(torch, mk, dev, "moe48_b32_ragged", a.batch32_steps, 2, a, weights=W)
         mk.mk_pool_free(r32["pool"])
         r32["dec"].close()
+        r32.clear()
         pool = dec = None
         b32 = {"workload": "moe48_b32_ragged", "steps": a.batch32_steps, "warmup": 2,
                "value": round(r32["tok_s"], 2), "unit": "tok/s",
@@ -137,9 +138,18 @@ def main():
         "batch32": b32,
     }
     print(json.dumps(out), flush=True)
+    # ordered teardown: plans and pools freed, every device buffer released
+    # and the device idle before the interpreter (and the HIP runtime with
+    # it) shuts down
     if dec is not None:
         mk.mk_pool_free(pool)
         dec.close()
+    del dec, W, r
+    torch.cuda.synchronize()
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
@@ -159,16 +169,18 @@ def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
                                plan_flags=a.plan_flags, weights=weights)
     ctx0 = torch.tensor(w["ctx"], dtype=torch.int32, device=dev)
     tok0 = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
-    toks = [tok0.clone(), torch.empty(B, dtype=torch.int32, device=dev)]
+    # hist[s]: the tokens step s reads; step s writes hist[s + 1]
+    hist = torch.empty((max(steps, warmup) + 1, B), dtype=torch.int32, device=dev)
     ids = torch.full((steps, L, B, K), -1, dtype=torch.int32, device=dev)
 
     # warm-up, then restore the pre-warm-up state (lengths and first tokens)
+    hist[0].copy_(tok0)
     for s in range(warmup):
-        dec.step(toks[s % 2], toks[(s + 1) % 2])
+        dec.step(hist[s], hist[s + 1])
     torch.cuda.synchronize()
     dec.check_status()
     dec.seq_lens.copy_(ctx0)
-    toks[0].copy_(tok0)
+    hist[0].copy_(tok0)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -176,8 +188,7 @@ def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
     t0 = time.perf_counter()
     ev[0].record(stream)
     for s in range(steps):
-        ti, to = toks[s % 2], toks[(s + 1) % 2]
-        dec.step(ti, to, topk_ids=ids[s] if moe else None)
+        dec.step(hist[s], hist[s + 1], topk_ids=ids[s] if moe else None)
         ev[s + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -196,7 +207,8 @@ def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
         wsum += wb
         ksum += kr + kw
     bytes_step = tot_bytes / steps
-    return {"w": w, "dec": dec, "pool": pool, "weights": W, "tok0": tok0,
+    return {"w": w, "dec": dec, "pool": pool, "weights": W, "hist": hist[:steps + 1].cpu().tolist(),
+            "ids": ids_h,
             "tok_s": B * steps / (ms_total * 1e-3), "ms_step": ms_total / steps, "per": per,
             "wall": wall, "bytes_step": bytes_step, "wsum": wsum / steps, "ksum": ksum / steps,
             "achieved_gbs": tot_bytes / (ms_total * 1e-3) / 1e9,
@@ -224,37 +236,74 @@ def stream_copy_probe(torch, mk, dev, reps=5):
     return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(w, a, dec, tok0):
-    """The oracle on the host cores, on a bounded sample of the same workload.
+def host_description():
+    """nproc, the cores this process may run on, the CPU model and host RAM."""
+    info = {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu"] = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                info["ram_gib"] = round(int(line.split()[1]) / 2 ** 20, 1)
+                break
+    except OSError:
+        pass
+    return info
 
-    Sample: the first a.cpu_steps decode steps from the workload's starting
-    state (same context, same first token), each run once untimed to
-    materialise the weights it touches in host memory and once timed.
+
+def cpu_baseline(w, a, hist, ids, Wd):
+    """The oracle on the host cores, on a bounded sample of the same workload,
+    teacher-forced on the GPU's run.
+
+    Sample: the first a.cpu_steps timed steps. Step s takes the GPU's input
+    tokens of that step (and its routing where the oracle's own top-k is a
+    near-tie) and its argmax is compared with the GPU's output token. The
+    weights a step touches are copied to host memory before it is timed (from
+    the device tensors the fixture generator filled); the KV is the oracle's
+    own contiguous copy, drawn by the host generator.
     """
     import torch
     import oracle as O
+    from fixtures.hostmodel import DeviceCopyWeights
     from fixtures.session import oracle_inputs
     m = w["model"]
-    B = w["batch"]
-    n = a.cpu_steps
-    W, kv_warm = oracle_inputs(dict(w, steps=n), a.seed, cache=True)
-    _, kv = oracle_inputs(dict(w, steps=n), a.seed, cache=True)
-    times = []
-    t_in = [int(t) for t in tok0.cpu().tolist()]
+    B, L = w["batch"], m["n_layers"]
+    moe = m["n_experts"] > 0
+    n = min(a.cpu_steps, len(hist) - 1)
+    Wh = DeviceCopyWeights(m, Wd, a.seed)
+    _, kv = oracle_inputs(dict(w, steps=n), a.seed, cache=False)
+    times, agree, forced_n, differ_n = [], 0, 0, 0
     for s in range(n):
-        O.decode_step(m, W, kv_warm, t_in)          # untimed: materialises this step's weights
+        routing = [[[int(v) for v in ids[s, l, b]] for l in range(L)] for b in range(B)] if moe else None
+        for l in range(L):  # the weights this step reads, resident before the timed region
+            Wh.wqkv(l), Wh.wo(l)
+            if moe:
+                Wh.router(l)
+                for e in {int(v) for v in ids[s, l].reshape(-1).tolist()}:
+                    Wh.gate(l, e), Wh.up(l, e), Wh.down(l, e)
+            else:
+                Wh.gate(l), Wh.up(l), Wh.down(l)
+        Wh.lm_head()
         t0 = time.perf_counter()
-        r = O.decode_step(m, W, kv, t_in)
+        r, forced, differ = O.decode_step_following(m, Wh, kv, hist[s], routing, 1e-5)
         times.append(time.perf_counter() - t0)
-        t_in = r["next"]
+        forced_n += len(forced)
+        differ_n += len(differ)
+        agree += sum(1 for b in range(B) if r["next"][b] == hist[s + 1][b])
         if sum(times) > 60:
             break
     dt = sum(times) / len(times)
+    host = host_description()
     return {"value": round(B / dt, 4), "unit": "tok/s", "cores": torch.get_num_threads(),
             "kind": "oracle",
-            "sample": f"{len(times)} decode step(s) of {a.workload} from its starting context, "
-                      f"weights resident in host memory (materialised in an untimed pass), "
-                      f"mean {dt:.3f} s per step"}
+            "sample": f"{len(times)} decode step(s) of {a.workload}: the first timed steps, teacher-forced "
+                      f"on the GPU's input tokens; weights resident in host memory before timing; "
+                      f"mean {dt:.3f} s per step",
+            "agreement": f"{agree}/{len(times) * B} next tokens equal the GPU's",
+            "routing_near_ties_followed": forced_n, "routing_differences": differ_n,
+            "host": host}
 
 
 if __name__ == "__main__":

@@ -91,3 +91,47 @@ class HostKV:
     def v(self, l, b, g, ctx):
         d = self.m["head_dim"]
         return host.normal_bf16(self.seed, host.FX_VCACHE, l, b, g, 0, ctx * d, SIGMA_KV).view(ctx, d)
+
+
+class DeviceCopyWeights(HostWeights):
+    """The same weights, copied to the host from the device tensors that
+    fixtures.device.weights filled (the device implementation of the same
+    generator, pinned bit for bit to the host one by a GPU test). Reading
+    back is much faster than drawing tens of GB again on the host; the
+    values are the generator's, not any result of the decode step."""
+
+    def __init__(self, model, dev_weights, seed=0, cache=True):
+        super().__init__(model, seed, cache)
+        self.D = dev_weights
+
+    def _get(self, key, fn):
+        if key in self._c:
+            return self._c[key]
+        t = fn().cpu()
+        if self.cache:
+            self._c[key] = t
+        return t
+
+    def embed_row(self, tok):
+        return self.D["embed"][tok].cpu()
+
+    def wqkv(self, l):
+        return self._get(("wqkv", l), lambda: self.D["w_qkv"][l])
+
+    def wo(self, l):
+        return self._get(("wo", l), lambda: self.D["w_o"][l])
+
+    def router(self, l):
+        return self._get(("router", l), lambda: self.D["router"][l])
+
+    def gate(self, l, e=0):
+        return self._get(("gate", l, e), lambda: self.D["gate"][l, e])
+
+    def up(self, l, e=0):
+        return self._get(("up", l, e), lambda: self.D["up"][l, e])
+
+    def down(self, l, e=0):
+        return self._get(("down", l, e), lambda: self.D["down"][l, e])
+
+    def lm_head(self):
+        return self._get(("lm",), lambda: self.D["lm_head"])

@@ -7,8 +7,8 @@
   benchmark times, checked on outputs the oracle computes one by one -- the
   queries, the new K and V in the pool and the attention output of layer 0
   (all 32 query heads over all 262145 positions) -- plus the properties
-  that hold at any size: status, counters, sequence length, a token in the
-  vocabulary.
+  that hold at any size: status, completion counters against the oracle's
+  counts, sequence length, a token in the vocabulary.
 """
 import pytest
 import torch
@@ -16,7 +16,7 @@ import torch
 import oracle as O
 from fixtures.hostmodel import HostKV, HostWeights
 from fixtures.session import gpu_session, spec
-from gpu_util import HIDDEN_TOL, flush, rel_err
+from gpu_util import HIDDEN_TOL, check_device_counters, flush, rel_err
 from test_gpu_step import _pool_slot, run_step_parity
 
 pytestmark = pytest.mark.gpu
@@ -68,8 +68,7 @@ def test_moe48_262144_layer0_sampled():
     assert 0 <= int(tok_out[0]) < m["vocab"]
     assert dec.seq_lens.cpu().tolist() == [pos + 1]
     import decode_megakernel_persistent_amd as mk
-    tg = torch.tensor(mk.mk_plan_counter_targets(dec.plan), dtype=torch.int64)
-    assert torch.equal(dec.counters(), tg * dec.epoch)
+    check_device_counters(dec, w)
 
     flush("  oracle: layer 0 at full context")
     q_ref, k_ref, v_ref, o_ref = layer0_reference(m, 0, w["tokens"][0], pos)

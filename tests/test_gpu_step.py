@@ -5,16 +5,19 @@ GPU and the same step in the oracle (fp32 math on the same bf16 weights,
 contiguous KV), then compares: the greedy token (exact, or a reported
 near-tie), logits and the hidden state after every attention and FFN
 residual (max-abs relative error <= 2e-2), the new K and V written into the
-paged pool, the router's top-k ids (bit-exact, or a reported near-tie), the
-untouched rest of the pool (bit-exact) and the dependency counters
-(bit-exact: epoch x producer count).
+paged pool, the router's top-k ids (bit-exact; where the oracle's own choice
+is a near-tie, the oracle continues from the GPU's ids, so the later layers
+are still compared), the untouched rest of the pool (bit-exact) and the
+completion counters (bit-exact: steps x the oracle's count of each class's
+outputs).
 """
 import pytest
 import torch
 
 import oracle as O
 from fixtures.session import gpu_session, oracle_inputs, spec
-from gpu_util import HIDDEN_TOL, argmax_near_tie, flush, kv_offsets, rel_err, topk_near_tie
+from gpu_util import (NEAR_TIE, argmax_near_tie, check_device_counters, compare_sequence, flush,
+                      gpu_routing, kv_offsets)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,42 +55,17 @@ def run_step_parity(name, seed=0, plan_flags=0, **over):
     torch.cuda.synchronize()
     dec.check_status()
 
+    # the oracle follows the GPU's routing only where its own is a near-tie
     Wh, kv = oracle_inputs(w, seed)
-    ref = O.decode_step(m, Wh, kv, w["tokens"])
-
-    report = {}
+    ref, forced, differ = O.decode_step_following(m, Wh, kv, w["tokens"],
+                                                  [gpu_routing(ids, b) for b in range(B)], NEAR_TIE)
+    assert not differ, f"top-k differs from the oracle without a near-tie at (sequence, layer) {differ}"
+    if forced:
+        flush(f"  near-ties in top-k followed at (sequence, layer) {forced}")
+    worst = 0.0
     for b in range(B):
-        diverged = False
-        for l in range(L):
-            if moe:
-                g_ids = ids[l, b].cpu().tolist()
-                o_ids = ref["topk_ids"][b][l].tolist()
-                if g_ids != o_ids:
-                    assert topk_near_tie(ref["router_logits"][b][l], K), \
-                        f"layer {l}: top-k {g_ids} != oracle {o_ids} without a near-tie"
-                    flush(f"  near-tie in top-k at layer {l}: {g_ids} vs {o_ids}")
-                    diverged = True
-                    break
-                assert rel_err(tw[l, b], ref["topk_w"][b][l]) < 1e-3
-                assert rel_err(dec.router_logits(l)[b], ref["router_logits"][b][l]) < HIDDEN_TOL
-            e_a = rel_err(dec.hidden_after_attn(l)[b], ref["x_attn"][b][l])
-            e_f = rel_err(dec.hidden_after_ffn(l)[b], ref["x_ffn"][b][l])
-            report[(b, l)] = (e_a, e_f)
-            assert e_a < HIDDEN_TOL, f"layer {l} attention residual rel err {e_a}"
-            assert e_f < HIDDEN_TOL, f"layer {l} FFN residual rel err {e_f}"
-            pos = w["ctx"][b]
-            for g in range(m["n_kv_heads"]):
-                k, v = _pool_slot(dec, m, b, l, g, pos)
-                assert rel_err(k.float(), ref["k_new"][b][l][g].float()) < HIDDEN_TOL
-                assert rel_err(v.float(), ref["v_new"][b][l][g].float()) < HIDDEN_TOL
-        if not diverged:
-            e_l = rel_err(logits[b], ref["logits"][b])
-            assert e_l < HIDDEN_TOL, f"logits rel err {e_l}"
-            got, want = int(tok_out[b]), ref["next"][b]
-            if got != want:
-                assert argmax_near_tie(ref["logits"][b], got, want), f"next {got} != {want}"
-                flush(f"  near-tie in argmax: {got} vs {want}")
-    worst = max(max(v) for v in report.values()) if report else 0.0
+        worst = max(worst, compare_sequence(dec, m, b, ref, b, ids if moe else None, tw, logits, tok_out,
+                                            w["ctx"][b], _pool_slot))
     flush(f"  worst hidden rel err {worst:.3e}")
 
     # KV pool: only the new slots changed
@@ -106,11 +84,11 @@ def run_step_parity(name, seed=0, plan_flags=0, **over):
                 mask[(base + vo).to(mask.device)] = True
     assert not bool((changed & ~mask).any()), "pool bytes outside the new slots changed"
 
-    # counters: every counter at epoch x producers; sequence lengths advanced
-    import decode_megakernel_persistent_amd as mk
-    tg = torch.tensor(mk.mk_plan_counter_targets(dec.plan), dtype=torch.int64)
-    assert torch.equal(dec.counters(), tg * dec.epoch)
+    # counters: every class at steps x the oracle's count of its outputs;
+    # sequence lengths advanced
+    check_device_counters(dec, w)
     assert dec.seq_lens.cpu().tolist() == [c + 1 for c in w["ctx"]]
+    import decode_megakernel_persistent_amd as mk
     mk.mk_pool_free(pool)
     dec.close()
     return worst
@@ -144,39 +122,50 @@ def test_attention_split_queue():
     run_step_parity("small_moe", seed=3, ctx=[1500], plan_flags=mk.MK_PLAN_ATTN_QUEUE)
 
 
-def greedy_agreement(name, n_steps, seed=0, **over):
+def greedy_agreement(name, n_steps, seed=0, weights_from_device=False, **over):
     """Run n_steps on the GPU feeding back its own tokens; the oracle is
-    teacher-forced on the GPU's input tokens and its argmax compared."""
+    teacher-forced on the GPU's input tokens (and on its routing where the
+    oracle's own is a near-tie) and its argmax compared."""
     w = spec(name, seed, steps=n_steps, **over)
     m, B = w["model"], w["batch"]
+    L = m["n_layers"]
+    K = m["top_k"] if m["n_experts"] else 1
     flush(f"[greedy] {name} steps={n_steps} seed={seed}")
-    dec, pool, W = gpu_session(w, seed)
+    dec, pool, Wd = gpu_session(w, seed)
     dev = dec.device
-    toks = [torch.tensor(w["tokens"], dtype=torch.int32, device=dev),
-            torch.empty(B, dtype=torch.int32, device=dev)]
-    seq_in = []
-    seq_out = []
+    hist = torch.empty((n_steps + 1, B), dtype=torch.int32, device=dev)
+    hist[0] = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
+    ids = torch.full((n_steps, L, B, K), -1, dtype=torch.int32, device=dev)
     for s in range(n_steps):
-        dec.step(toks[s % 2], toks[(s + 1) % 2])
-        seq_in.append(toks[s % 2].clone())
-        seq_out.append(toks[(s + 1) % 2].clone())
+        dec.step(hist[s], hist[s + 1], topk_ids=ids[s] if m["n_experts"] else None)
     torch.cuda.synchronize()
     dec.check_status()
-    gin = [t.cpu().tolist() for t in seq_in]
-    gout = [t.cpu().tolist() for t in seq_out]
-    Wh, kv = oracle_inputs(w, seed)
-    agree = near = 0
+    gh = hist.cpu().tolist()
+    if weights_from_device:
+        from fixtures.hostmodel import DeviceCopyWeights
+        Wh = DeviceCopyWeights(m, Wd, seed)
+        _, kv = oracle_inputs(w, seed, cache=False)
+    else:
+        Wh, kv = oracle_inputs(w, seed)
+    agree = near = n_forced = n_differ = 0
     for s in range(n_steps):
-        ref = O.decode_step(m, Wh, kv, gin[s])
+        routing = [gpu_routing(ids[s], b) for b in range(B)] if m["n_experts"] else None
+        ref, forced, differ = O.decode_step_following(m, Wh, kv, gh[s], routing, NEAR_TIE)
+        n_forced += len(forced)
+        n_differ += len(differ)
         for b in range(B):
-            if ref["next"][b] == gout[s][b]:
+            if ref["next"][b] == gh[s + 1][b]:
                 agree += 1
-            elif argmax_near_tie(ref["logits"][b], ref["next"][b], gout[s][b]):
+            elif argmax_near_tie(ref["logits"][b], ref["next"][b], gh[s + 1][b]):
                 near += 1
+        if (s + 1) % 8 == 0 or s + 1 == n_steps:
+            flush(f"  oracle step {s + 1}/{n_steps}: agreement {agree}, near-ties {near}")
     total = n_steps * B
-    flush(f"  agreement {agree}/{total}, near-ties {near}")
+    flush(f"  agreement {agree}/{total}, near-ties {near}, routing near-ties followed {n_forced}, "
+          f"routing differences {n_differ}")
     assert (agree + near) / total >= 0.99
     assert dec.seq_lens.cpu().tolist() == [c + n_steps for c in w["ctx"]]
+    check_device_counters(dec, w)
     mk_free = __import__("decode_megakernel_persistent_amd").mk_pool_free
     mk_free(pool)
     dec.close()
