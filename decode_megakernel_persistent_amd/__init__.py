@@ -96,6 +96,7 @@ _SIGS = {
     "mk_plan_free": (None, [_vp]),
     "mk_decode_step": (_i32, [_vp, _P(mk_weights), _P(mk_kv), _P(mk_io), _P(mk_step_buffers),
                               _u32, _u32, _vp]),
+    "mk_decode_step_static": (_i32, [_vp, _P(mk_weights), _P(mk_kv), _P(mk_io), _vp, _sz, _vp, _u32, _vp]),
     "mk_step_status": (_i32, [_vp]),
     "mk_pool_create": (_i32, [_i32, _i32, _i32, _vp, _P(_vp)]),
     "mk_pool_lease": (_i32, [_vp, _i64, _i32, _P(_i32)]),
@@ -254,6 +255,14 @@ def mk_plan_free(p):
 def mk_decode_step(p, weights, kv, io, bufs, epoch, timeout_ms, stream):
     _check(_lib.mk_decode_step(p, ctypes.byref(weights), ctypes.byref(kv), ctypes.byref(io),
                                ctypes.byref(bufs), epoch, timeout_ms, stream))
+
+
+MK_STATIC_SCRATCH_BYTES = 128 << 20
+
+
+def mk_decode_step_static(p, weights, kv, io, d_plan, plan_bytes, d_status, timeout_ms, stream):
+    _check(_lib.mk_decode_step_static(p, ctypes.byref(weights), ctypes.byref(kv), ctypes.byref(io), d_plan,
+                                      plan_bytes, d_status, timeout_ms, stream))
 
 
 def mk_step_status(h_status4):

@@ -37,6 +37,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "mk.h"
@@ -2255,6 +2257,13 @@ __global__ __launch_bounds__(256) void mk_stream_copy_kernel(uint4* __restrict__
   }
 }
 
+// Zero-fill of n 16-byte words (a kernel, not a memset node, so that a
+// caller may capture it in a graph).
+__global__ __launch_bounds__(256) void mk_zero_kernel(uint4* __restrict__ p, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+}
+
 // Kernel variants, indexed by mk::kernel_class (see mk_internal.hpp) and by
 // batch (batch 1: GEMV tiles; a batch: MFMA tiles and shared expert tasks).
 const void* kernel_for(int cls, bool batch) {
@@ -2336,10 +2345,105 @@ extern "C" mk_status mk_step_status(const uint32_t* h) {
   }
 }
 
+// One step of plan p with the step buffers bu (checked by the caller).
+static mk_status launch_step(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv, const mk_io* io,
+                             const mk_step_buffers* bu, uint32_t epoch, uint32_t timeout_ms, void* stream);
+
 extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv,
                                     const mk_io* io, const mk_step_buffers* bu, uint32_t epoch,
                                     uint32_t timeout_ms, void* stream) {
   if (!p || !w || !kv || !io || !bu) return fail(MK_EINVAL, "mk_decode_step: NULL argument");
+  if (!bu->plan || bu->plan_bytes < p->image.size() || !bu->workspace ||
+      bu->workspace_bytes < p->ws_total || !bu->counters ||
+      bu->counter_bytes < p->targets.size() * mk::CTR_LINES * mk::CTR_STRIDE * 4 || !bu->status)
+    return fail(MK_EINVAL, "mk_decode_step: step buffers missing or too small");
+  return launch_step(p, w, kv, io, bu, epoch, timeout_ms, stream);
+}
+
+// ------------------------------------------------------------------ static scratch
+//
+// The allocation-free step keeps the workspace (tagged activations) and the
+// completion counters of its plan in this file-scope array instead of caller
+// buffers. Each device holds its own copy; its address on the current device
+// is looked up once per device with hipGetSymbolAddress and used wherever the
+// host needs the array's memory (the array's name in host code is not a
+// device address).
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)MK_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+
+namespace {
+struct StaticState {
+  uint8_t* ptr = nullptr;  // the device address of scratch on this device
+  uint64_t plan_uid = 0;   // plan whose workspace the scratch holds (0: none)
+  uint32_t epoch = 0;      // last epoch used on it
+};
+std::mutex g_static_mu;
+std::map<int, StaticState> g_static;  // per device
+}  // namespace
+
+extern "C" mk_status mk_decode_step_static(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv,
+                                           const mk_io* io, const void* d_plan, size_t plan_bytes,
+                                           uint32_t* d_status, uint32_t timeout_ms, void* stream) {
+  if (!p || !w || !kv || !io || !d_plan || !d_status)
+    return fail(MK_EINVAL, "mk_decode_step_static: NULL argument");
+  if (plan_bytes < p->image.size()) return fail(MK_EINVAL, "mk_decode_step_static: plan buffer too small");
+  const size_t ws = (p->ws_total + 255) & ~(size_t)255;
+  const size_t ctr = p->targets.size() * mk::CTR_LINES * mk::CTR_STRIDE * 4;
+  if (ws + ctr > STATIC_SCRATCH_BYTES)
+    return fail(MK_EBOUNDS, "mk_decode_step_static: the plan needs " + std::to_string(ws + ctr) +
+                                " bytes of workspace and counters; the static scratch holds " +
+                                std::to_string(STATIC_SCRATCH_BYTES) + " (use mk_decode_step)");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  uint8_t* base = nullptr;
+  uint32_t epoch = 0;
+  bool clear = false;
+  {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    StaticState& st = g_static[dev];
+    if (!st.ptr) {
+      e = hipGetSymbolAddress((void**)&st.ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        st.ptr = nullptr;
+        return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      }
+    }
+    // a plan other than the last one on this device: its workspace and
+    // counters start from zero and its epochs from 1
+    if (st.plan_uid != p->uid) {
+      st.plan_uid = p->uid;
+      st.epoch = 0;
+      clear = true;
+    }
+    if (st.epoch == 0xFFFFFFFFu) return fail(MK_ESTATE, "mk_decode_step_static: epochs of this plan exhausted");
+    epoch = ++st.epoch;
+    base = st.ptr;
+  }
+  if (clear) {
+    const size_t n = (ws + ctr) / 16;
+    int32_t cus = 0;
+    mk_status sc = mk_device_cu_count(&cus);
+    if (sc != MK_OK) return sc;
+    const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, (size_t)cus * 8);
+    hipLaunchKernelGGL(mk::dev::mk_zero_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (uint4*)base, n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "mk_decode_step_static: zero-fill launch");
+  }
+  mk_step_buffers bu;
+  std::memset(&bu, 0, sizeof bu);
+  bu.plan = d_plan;
+  bu.plan_bytes = plan_bytes;
+  bu.workspace = base;
+  bu.workspace_bytes = ws;
+  bu.counters = (uint32_t*)(base + ws);
+  bu.counter_bytes = ctr;
+  bu.status = d_status;
+  return launch_step(p, w, kv, io, &bu, epoch, timeout_ms, stream);
+}
+
+static mk_status launch_step(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv, const mk_io* io,
+                             const mk_step_buffers* bu, uint32_t epoch, uint32_t timeout_ms, void* stream) {
   const auto& m = p->m;
   const bool moe = m.n_experts > 0;
   if (!w->embed || !w->attn_norm || !w->w_qkv || !w->w_o || !w->ffn_norm || !w->gate || !w->up ||
@@ -2351,10 +2455,6 @@ extern "C" mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, con
     return fail(MK_EBOUNDS, "mk_decode_step: rotary tables cover fewer positions than the plan bound");
   if (kv->n_pages <= 0) return fail(MK_EINVAL, "mk_decode_step: empty KV pool");
   if (!io->tokens_in || !io->tokens_out) return fail(MK_EINVAL, "mk_decode_step: missing token buffers");
-  if (!bu->plan || bu->plan_bytes < p->image.size() || !bu->workspace ||
-      bu->workspace_bytes < p->ws_total || !bu->counters ||
-      bu->counter_bytes < p->targets.size() * mk::CTR_LINES * mk::CTR_STRIDE * 4 || !bu->status)
-    return fail(MK_EINVAL, "mk_decode_step: step buffers missing or too small");
   if (epoch == 0) return fail(MK_EINVAL, "mk_decode_step: epoch must be >= 1");
 
   mk::KArgs a;

@@ -22,6 +22,7 @@
 // then LM (rows of the LM head, local argmax) and FINAL (argmax merge).
 #include <algorithm>
 #include <array>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -395,6 +396,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   if (n_cu > 4096) return fail(MK_EINVAL, "mk_plan: n_cu too large");
 
   auto* p = new mk_plan_t();
+  static std::atomic<uint64_t> next_uid{1};
+  p->uid = next_uid.fetch_add(1);
   p->m = *m;
   p->B = B;
   p->max_pages = bd->max_pages;

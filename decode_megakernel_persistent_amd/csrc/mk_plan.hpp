@@ -7,6 +7,7 @@
 #include "mk_internal.hpp"
 
 struct mk_plan {
+  uint64_t uid = 0;  // unique per plan built in this process (never reused)
   mk_model_desc m;
   int32_t B = 0, max_pages = 0, bound = 0, n_cu = 0;
   bool batch = false;                 // B > 1: MFMA batch tasks

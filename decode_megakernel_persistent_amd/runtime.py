@@ -12,7 +12,7 @@ import torch
 
 from . import (
     MK_BUF_O, MK_BUF_Q, MK_BUF_RLOG, MK_BUF_XATTN, MK_BUF_XFFN,
-    MkError, MK_OK, mk_decode_step, mk_io, mk_kv, mk_kv_pool_elems, mk_plan, mk_plan_buffer,
+    MkError, MK_OK, mk_decode_step, mk_decode_step_static, mk_io, mk_kv, mk_kv_pool_elems, mk_plan, mk_plan_buffer,
     mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks, mk_plan_upload,
     mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_step_status, mk_weights,
     model_desc,
@@ -109,6 +109,15 @@ class Decoder:
         io = mk_io(_ptr(tokens_in), _ptr(tokens_out), _ptr(topk_ids), _ptr(topk_w), _ptr(logits))
         mk_decode_step(self.plan, self._w, self._kv, io, self._bufs, self.epoch, timeout_ms,
                        torch.cuda.current_stream(self.device).cuda_stream)
+
+    def step_static(self, tokens_in, tokens_out, topk_ids=None, topk_w=None, logits=None, timeout_ms=0):
+        """Enqueue one decode step through the allocation-free entry point:
+        the workspace and counters live in the library's static scratch
+        (this decoder's own workspace, counters and epochs are not used)."""
+        io = mk_io(_ptr(tokens_in), _ptr(tokens_out), _ptr(topk_ids), _ptr(topk_w), _ptr(logits))
+        mk_decode_step_static(self.plan, self._w, self._kv, io, self.plan_buf.data_ptr(), self.plan_buf.numel(),
+                              self.status.data_ptr(), timeout_ms,
+                              torch.cuda.current_stream(self.device).cuda_stream)
 
     def check_status(self):
         """Synchronise and raise MkError if the device recorded a failure."""

@@ -272,6 +272,29 @@ void mk_plan_free(mk_plan_t* p);
 mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv,
                          const mk_io* io, const mk_step_buffers* bufs, uint32_t epoch,
                          uint32_t timeout_ms, void* hip_stream);
+/* ---- one decode step that allocates nothing (asynchronous on hip_stream) ----
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as mk_decode_step, with the plan's workspace and completion counters
+ * held in a static scratch array of the library (MK_STATIC_SCRATCH_BYTES per
+ * device, taken when the library's kernels are first loaded on the device and
+ * held until the process ends) instead of caller buffers. No allocation and
+ * no allocating library call is made. The caller passes the inputs and
+ * outputs: the plan image uploaded with mk_plan_upload (d_plan, plan_bytes),
+ * the weights, the KV cache and io as for mk_decode_step, and 4 status words
+ * (device, zeroed once; read and decoded as for mk_decode_step). The library
+ * keeps the epochs: a plan other than the last one used on this device starts
+ * from a zero-filled scratch (a fill kernel on hip_stream) and epoch 1, and
+ * every further step of it uses the next epoch. Every call on one device
+ * shares that device's scratch: calls that overlap on one device (other
+ * streams, other threads) race and must be serialised by the caller; the
+ * counters and tagged activations are not readable through this entry point.
+ * MK_EBOUNDS if the plan's workspace and counters exceed the scratch (large
+ * batch plans: use mk_decode_step). */
+#define MK_STATIC_SCRATCH_BYTES (128u << 20)
+mk_status mk_decode_step_static(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv,
+                                const mk_io* io, const void* d_plan, size_t plan_bytes,
+                                uint32_t* d_status, uint32_t timeout_ms, void* hip_stream);
 /* Decode a host copy of the 4 status words: MK_OK, MK_ETIMEOUT (word 1: task
  * index, word 2: counter, word 3: value seen) or MK_EBOUNDS (context past the
  * plan bound). Sets mk_last_error. */

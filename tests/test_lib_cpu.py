@@ -397,3 +397,22 @@ def test_kv_page_layout_is_a_bijection(d):
             for s in range(16):
                 k, _ = kv_offsets(s, d)
                 assert int(k[32 * i + 8 * kq]) == (64 * i + 16 * kq + s) * 8
+
+
+def test_static_step_rejects_plans_beyond_its_scratch():
+    # the batch-32 ragged plan of the 48-layer MoE needs more than the static
+    # scratch holds: rejected before any device call (pointers are never read)
+    w, pool, p, bound = build_plan("moe48_b32_ragged", 256)
+    try:
+        need = mk.mk_plan_workspace_bytes(p) + mk.mk_plan_counter_bytes(p)
+        assert need > mk.MK_STATIC_SCRATCH_BYTES
+        W, kv, io = mk.mk_weights(), mk.mk_kv(), mk.mk_io()
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode_step_static(p, W, kv, io, 1, mk.mk_plan_device_bytes(p), 1, 0, None)
+        assert e.value.status == mk.MK_EBOUNDS and "static scratch" in str(e.value)
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode_step_static(p, W, kv, io, None, 0, 1, 0, None)
+        assert e.value.status == mk.MK_EINVAL
+    finally:
+        mk.mk_plan_free(p)
+        mk.mk_pool_free(pool)
