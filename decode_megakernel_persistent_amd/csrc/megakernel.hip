@@ -954,48 +954,60 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   }
   mark(c, 2);
   if (bad && lane == 0) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)b, 0xFFFFFFFFu);
-  // merge hi/lo rows and publish this wave's partial in LDS
-  float* Ow = s.att;                      // [NWAVE][HG][D]
+  // merge the hi/lo rows (row r and r + 8 of the product, lanes L and L ^ 32)
+  // and publish this wave's partial in LDS, head fastest: lane (r16, kq < 2)
+  // holds heads 4 kq .. + 3 of dim 16 nb + r16, one 16-byte store per nb
+  float* Ow = s.att;                      // [NWAVE][D][8]
   float* mw = s.red;                      // [NWAVE][8]
   float* lw = s.out;                      // [NWAVE][8]
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float o = xor32_sum(acc[nb][j]);
-      const int head = 4 * kq + j;
-      if (kq < 2 && head < HG) Ow[(w * HG + head) * D + nb * 16 + r16] = o;
-    }
+  for (int nb = 0; nb < NB; ++nb) {
+    float4 o4;
+    o4.x = xor32_sum(acc[nb][0]);
+    o4.y = xor32_sum(acc[nb][1]);
+    o4.z = xor32_sum(acc[nb][2]);
+    o4.w = xor32_sum(acc[nb][3]);
+    if (kq < 2) *(float4*)(Ow + ((w * D) + nb * 16 + r16) * 8 + 4 * kq) = o4;
+  }
   if (lane < 8) {
     mw[w * 8 + lane] = m_run;
     lw[w * 8 + lane] = l_run;
   }
   lds_barrier();
   mark(c, 3);
-  // merge over the waves: every thread forms the scales of its own heads,
-  // exp(m_q - M) with M = max_q m_q, so no further barrier is needed
+  // merge over the waves. Every wave forms the 64 scales exp(m_q,h - M_h) of
+  // (wave q, head h) in its lanes (lane 8 q + h; M_h = max_q m_q,h, over lanes
+  // of equal h: xor 8, 16, 32) and the heads' sums L_h; thread (dim, head
+  // pair) then sums its two heads' outputs with the scales as scalars.
+  const int wq = lane >> 3, hw = lane & 7;
+  const float mq = hw < HG ? mw[wq * 8 + hw] : NEG_INF;
+  float Mh = fmaxf(mq, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mq), 0x128, 0xF, 0xF, false)));
+  Mh = xor32_max(xor16_max(Mh));
+  const float e = mq == NEG_INF ? 0.f : expf(mq - Mh);
+  const float Lh = xor32_sum(xor16_sum(xor8_sum(e * (hw < HG ? lw[wq * 8 + hw] : 0.f))));
   const int PS = D + 2;
   uint64_t* dst0 = a.part + (size_t)l * a.s_part +
                    (((size_t)b * a.Hkv + g) * a.S_max + split) * HG * PS;
-  for (int idx = tid(); idx < HG * D; idx += NT) {
-    const int head = idx / D, dim = idx % D;
-    float M = NEG_INF;
-#pragma unroll
-    for (int q = 0; q < NWAVE; ++q) M = fmaxf(M, mw[q * 8 + head]);
-    float oo = 0.f, LL = 0.f;
+  for (int idx = tid(); idx < (HG + 1) / 2 * D; idx += NT) {
+    const int hp = __builtin_amdgcn_readfirstlane(idx / D);  // head pair, uniform in a wave (D % 64 == 0)
+    const int dim = idx - hp * D;
+    float o0 = 0.f, o1 = 0.f;
 #pragma unroll
     for (int q = 0; q < NWAVE; ++q) {
-      const float m = mw[q * 8 + head];
-      const float e = m == NEG_INF ? 0.f : expf(m - M);
-      oo += e * Ow[(q * HG + head) * D + dim];
-      LL += e * lw[q * 8 + head];
+      const float e0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), q * 8 + 2 * hp));
+      const float e1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), q * 8 + 2 * hp + 1));
+      const float2 v = *(const float2*)(Ow + ((q * D) + dim) * 8 + 2 * hp);
+      o0 = fmaf(e0, v.x, o0);
+      o1 = fmaf(e1, v.y, o1);
     }
-    uint64_t* dst = dst0 + (size_t)head * PS;
-    st_tagged(dst + dim, oo, a.epoch);
-    if (dim == 0) {
-      st_tagged(dst + D, M, a.epoch);
-      st_tagged(dst + D + 1, LL, a.epoch);
-    }
+    uint64_t* dst = dst0 + (size_t)(2 * hp) * PS;
+    st_tagged(dst + dim, o0, a.epoch);
+    if (2 * hp + 1 < HG) st_tagged(dst + PS + dim, o1, a.epoch);
+  }
+  if (tid() < HG) {  // lanes 0 .. HG-1 of wave 0: head h's M and L
+    uint64_t* dst = dst0 + (size_t)tid() * PS;
+    st_tagged(dst + D, Mh, a.epoch);
+    st_tagged(dst + D + 1, Lh, a.epoch);
   }
   return true;
 }
