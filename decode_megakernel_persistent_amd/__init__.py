@@ -80,6 +80,7 @@ _SIGS = {
     "mk_step_bytes": (_i32, [_P(mk_model_desc), _i32, _P(_i32), _P(_i32), _P(ctypes.c_double),
                              _P(ctypes.c_double), _P(ctypes.c_double)]),
     "mk_plan": (_i32, [_P(mk_model_desc), _P(mk_batch_desc), _P(mk_plan_opts), _P(_vp)]),
+    "mk_plan_update": (_i32, [_vp, _P(_i32), _P(_i32), _i32, _P(_i32), _P(_i32)]),
     "mk_plan_validate": (_i32, [_vp]),
     "mk_plan_simulate": (_i32, [_vp, _u64, _i32]),
     "mk_plan_device_bytes": (_sz, [_vp]),
@@ -162,6 +163,8 @@ def mk_step_bytes(desc, seq_lens, distinct=None):
     return w.value, r.value, wr.value
 
 
+_plan_shape = {}   # plan handle -> (batch, page-table width), for mk_plan_update's argument check
+
 MK_PLAN_ATTN_QUEUE = 1
 MK_PLAN_NO_ATTN_QUEUE = 2
 
@@ -178,7 +181,26 @@ def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pag
     op = mk_plan_opts(n_cu, attn_split_pages, flags)
     out = _vp()
     _check(_lib.mk_plan(ctypes.byref(desc), ctypes.byref(bd), ctypes.byref(op), ctypes.byref(out)))
+    _plan_shape[out.value] = (B, max_pages)
     return out.value
+
+
+MK_PLAN_CHANGED_IMAGE, MK_PLAN_CHANGED_WORKSPACE, MK_PLAN_CHANGED_COUNTERS = 1, 2, 4
+
+
+def mk_plan_update(p, seq_lens, page_table, bound, ctx_bounds=None):
+    """Refresh plan p in place; returns the MK_PLAN_CHANGED_* bits."""
+    B = len(seq_lens)
+    if (B, len(page_table) // max(B, 1)) != _plan_shape.get(p) or len(page_table) % max(B, 1) \
+            or (ctx_bounds is not None and len(ctx_bounds) != B):
+        raise ValueError(f"mk_plan_update: batch {B} / page table of {len(page_table)} entries do not match "
+                         f"the plan's (batch, pages per row) {_plan_shape.get(p)}")
+    sl = (_i32 * B)(*[int(v) for v in seq_lens])
+    pt = (_i32 * len(page_table))(*[int(v) for v in page_table])
+    cb = (_i32 * B)(*[int(v) for v in ctx_bounds]) if ctx_bounds is not None else None
+    ch = _i32()
+    _check(_lib.mk_plan_update(p, sl, pt, bound, cb, ctypes.byref(ch)))
+    return ch.value
 
 
 def mk_plan_validate(p):
@@ -249,6 +271,7 @@ def mk_plan_counter_names(p):
 
 
 def mk_plan_free(p):
+    _plan_shape.pop(p, None)
     _lib.mk_plan_free(p)
 
 

@@ -399,6 +399,9 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   static std::atomic<uint64_t> next_uid{1};
   p->uid = next_uid.fetch_add(1);
   p->m = *m;
+  p->opts.n_cu = n_cu;
+  p->opts.attn_split_pages = o ? o->attn_split_pages : 0;
+  p->opts.flags = o ? o->flags : 0;
   p->B = B;
   p->max_pages = bd->max_pages;
   p->bound = bound;
@@ -829,15 +832,53 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   return MK_OK;
 }
 
+extern "C" mk_status mk_plan_update(mk_plan_t* p, const int32_t* seq_lens, const int32_t* page_table,
+                                    int32_t max_ctx_bound, const int32_t* ctx_bounds, int32_t* changed) {
+  if (!p || !seq_lens || !page_table) return fail(MK_EINVAL, "mk_plan_update: NULL argument");
+  mk_batch_desc bd;
+  bd.batch = p->B;
+  bd.max_pages = p->max_pages;
+  bd.seq_lens = seq_lens;
+  bd.page_table = page_table;
+  bd.max_ctx_bound = max_ctx_bound;
+  bd.ctx_bounds = ctx_bounds;
+  mk_plan_t* q = nullptr;
+  const mk_status st = mk_plan(&p->m, &bd, &p->opts, &q);
+  if (st != MK_OK) return st;  // the plan is unchanged
+  int32_t fl = 0;
+  if (q->image != p->image) fl |= MK_PLAN_CHANGED_IMAGE;
+  bool same_ws = q->ws_total == p->ws_total;
+  for (int i = 0; i < mk_plan::N_BUF && same_ws; ++i)
+    same_ws = q->ws_off[i] == p->ws_off[i] && q->ws_stride[i] == p->ws_stride[i];
+  if (!same_ws) fl |= MK_PLAN_CHANGED_WORKSPACE;
+  if (q->targets != p->targets || q->ctr_name != p->ctr_name) fl |= MK_PLAN_CHANGED_COUNTERS;
+  // the handle keeps its identity (and a static scratch its contents and
+  // epochs) unless the step must start again: the attention queue numbers
+  // its pulls from the epoch and this step's item count, so a count change
+  // needs fresh counters and epochs as much as a new layout does
+  const uint64_t uid = (fl & (MK_PLAN_CHANGED_WORKSPACE | MK_PLAN_CHANGED_COUNTERS)) ? q->uid : p->uid;
+  std::swap(*p, *q);
+  p->uid = uid;
+  delete q;
+  if (changed) *changed = fl;
+  return MK_OK;
+}
+
 // ------------------------------------------------------------------ validation
 
 namespace {
 
-// Expand the outputs a task produces into integer keys per (op, layer).
-void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::string, int64_t>>& out) {
+// Output classes of the coverage check; the LM head and the final argmax sit
+// in the slot of layer n_layers.
+enum OutKind { K_QKV, K_ATTN, K_COMB, K_GATEUP, K_DOWN, K_O, K_ROUTER, K_TOPK, K_FFN, K_LM, K_FINAL, N_KIND };
+const char* const kind_name[N_KIND] = {"qkv", "attn", "comb", "gateup", "down", "o",
+                                       "router", "topk", "ffn", "lm", "final"};
+
+// Expand the outputs a task produces into integer keys: emit(kind, key).
+template <class Emit>
+void task_outputs(const mk_plan_t* p, const Task& t, Emit&& emit) {
   const auto& m = p->m;
   const int D = m.head_dim, Hkv = m.n_kv_heads, Hq = m.n_q_heads;
-  const std::string ls = ":" + std::to_string(t.layer);
   switch (t.op) {
     case mk::OP_QKV:
     case mk::OP_BQKV:  // the partial sums of blocks 1 .. kb-1 end in block 0's rows
@@ -845,60 +886,57 @@ void task_outputs(const mk_plan_t* p, const Task& t, std::vector<std::pair<std::
       for (int q = t.a1; q < t.a1 + t.a2; ++q) {
         int head, i, row;
         mk::qkv_pair(q, t.a0, p->HG, D, Hq, Hkv, &head, &i, &row);
-        out.push_back({"qkv" + ls, row});
-        out.push_back({"qkv" + ls, row + D / 2});
+        emit(K_QKV, row);
+        emit(K_QKV, row + D / 2);
       }
       break;
     case mk::OP_ATTN:
       if (t.flags & mk::TF_QUEUE) break;  // the queue's splits are counted once per layer
-      for (int pg = t.a2; pg < t.a2 + t.a3; ++pg)
-        out.push_back({"attn" + ls, ((int64_t)t.a0 * Hkv + t.a1) * 1000000 + pg});
+      for (int pg = t.a2; pg < t.a2 + t.a3; ++pg) emit(K_ATTN, ((int64_t)t.a0 * Hkv + t.a1) * 1000000 + pg);
       break;
     case mk::OP_COMB:  // dims a2 .. a2 + a3 of heads a1, a1 + 1, .. taken as one run
-      for (int d = t.a2; d < t.a2 + t.a3; ++d)
-        out.push_back({"comb" + ls, ((int64_t)t.a0 * Hq + t.a1 + d / D) * 1024 + d % D});
+      for (int d = t.a2; d < t.a2 + t.a3; ++d) emit(K_COMB, ((int64_t)t.a0 * Hq + t.a1 + d / D) * 1024 + d % D);
       break;
     case mk::OP_EXPERT: {
       const bool moe = m.n_experts > 0;
-      for (int f = t.a1; f < t.a1 + t.a2; ++f)
-        out.push_back({"gateup" + ls, moe ? ((int64_t)t.a0 * 64 + t.aux) * 1000000 + f : f});
+      for (int f = t.a1; f < t.a1 + t.a2; ++f) emit(K_GATEUP, moe ? ((int64_t)t.a0 * 64 + t.aux) * 1000000 + f : f);
       const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
-      for (int r = r0; r < r0 + nr; ++r) out.push_back({"down" + ls, r});
+      for (int r = r0; r < r0 + nr; ++r) emit(K_DOWN, r);
       break;
     }
     case mk::OP_O:
-      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"o" + ls, r});
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) emit(K_O, r);
       break;
     case mk::OP_BO:  // the partial sums of blocks 1 .. kb-1 end in block 0's rows
       if (t.a0 == 0)
-        for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"o" + ls, r});
+        for (int r = t.a1; r < t.a1 + t.a2; ++r) emit(K_O, r);
       break;
     case mk::OP_ROUTER:  // rows a1 .. a1 + a2 of sequence a0
-      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"router" + ls, (int64_t)t.a0 * 1000000 + r});
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) emit(K_ROUTER, (int64_t)t.a0 * 1000000 + r);
       break;
     case mk::OP_TOPK:  // every router row of one sequence (unless read), and its top-k
       if (!(t.flags & mk::TF_LOGITS))
-        for (int r = 0; r < m.n_experts; ++r) out.push_back({"router" + ls, (int64_t)t.a0 * 1000000 + r});
-      out.push_back({"topk" + ls, t.a0});
+        for (int r = 0; r < m.n_experts; ++r) emit(K_ROUTER, (int64_t)t.a0 * 1000000 + r);
+      emit(K_TOPK, t.a0);
       break;
     case mk::OP_BEXP: {
-      for (int f = t.a1; f < t.a1 + t.a2; ++f) out.push_back({"gateup" + ls, (int64_t)t.a0 * 1000000 + f});
+      for (int f = t.a1; f < t.a1 + t.a2; ++f) emit(K_GATEUP, (int64_t)t.a0 * 1000000 + f);
       const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
-      for (int r = r0; r < r0 + nr; ++r) out.push_back({"down" + ls, (int64_t)t.a0 * 1000000 + r});
+      for (int r = r0; r < r0 + nr; ++r) emit(K_DOWN, (int64_t)t.a0 * 1000000 + r);
       break;
     }
     case mk::OP_BCOMB:
-      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"ffn" + ls, (int64_t)t.a0 * 1000000 + r});
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) emit(K_FFN, (int64_t)t.a0 * 1000000 + r);
       break;
     case mk::OP_LM:
     case mk::OP_BLM:
-      for (int r = t.a1; r < t.a1 + t.a2; ++r) out.push_back({"lm", r});
+      for (int r = t.a1; r < t.a1 + t.a2; ++r) emit(K_LM, r);
       break;
     case mk::OP_FINAL:
-      out.push_back({"final", 0});
+      emit(K_FINAL, 0);
       break;
     case mk::OP_BFINAL:
-      out.push_back({"final", t.a1});
+      emit(K_FINAL, t.a1);
       break;
   }
 }
@@ -910,48 +948,48 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
   const auto& m = p->m;
   const int L = m.n_layers, B = p->B;
   const bool moe = m.n_experts > 0;
-  // expected output sets
-  std::map<std::string, std::set<int64_t>> want;
+  // expected outputs per (class, layer); the LM head and argmax at layer L
+  auto slot = [L](int kind, int layer) { return (size_t)kind * (L + 1) + layer; };
+  std::vector<std::vector<int64_t>> want((size_t)N_KIND * (L + 1)), got(want.size());
   for (int l = 0; l < L; ++l) {
-    const std::string ls = ":" + std::to_string(l);
-    for (int r = 0; r < p->QKV_ROWS; ++r) want["qkv" + ls].insert(r);
+    auto w = [&](int kind) -> std::vector<int64_t>& { return want[slot(kind, l)]; };
+    for (int r = 0; r < p->QKV_ROWS; ++r) w(K_QKV).push_back(r);
     for (int b = 0; b < B; ++b)
       for (int g = 0; g < m.n_kv_heads; ++g)
         for (int pg = 0; pg < ((p->batch ? p->seq_bound[b] : p->bound) + 15) / 16; ++pg)
-          want["attn" + ls].insert(((int64_t)b * m.n_kv_heads + g) * 1000000 + pg);
+          w(K_ATTN).push_back(((int64_t)b * m.n_kv_heads + g) * 1000000 + pg);
     for (int b = 0; b < B; ++b)
       for (int h = 0; h < m.n_q_heads; ++h)
-        for (int d = 0; d < m.head_dim; ++d) want["comb" + ls].insert(((int64_t)b * m.n_q_heads + h) * 1024 + d);
-    for (int r = 0; r < m.hidden; ++r) want["o" + ls].insert(r);
+        for (int d = 0; d < m.head_dim; ++d) w(K_COMB).push_back(((int64_t)b * m.n_q_heads + h) * 1024 + d);
+    for (int r = 0; r < m.hidden; ++r) w(K_O).push_back(r);
     if (p->batch) {
       const int NE = moe ? m.n_experts : 1;
       if (moe)
         for (int b = 0; b < B; ++b) {
-          for (int r = 0; r < m.n_experts; ++r) want["router" + ls].insert((int64_t)b * 1000000 + r);
-          want["topk" + ls].insert(b);
+          for (int r = 0; r < m.n_experts; ++r) w(K_ROUTER).push_back((int64_t)b * 1000000 + r);
+          w(K_TOPK).push_back(b);
         }
       for (int e = 0; e < NE; ++e) {
-        for (int f = 0; f < p->F; ++f) want["gateup" + ls].insert((int64_t)e * 1000000 + f);
-        for (int r = 0; r < m.hidden; ++r) want["down" + ls].insert((int64_t)e * 1000000 + r);
+        for (int f = 0; f < p->F; ++f) w(K_GATEUP).push_back((int64_t)e * 1000000 + f);
+        for (int r = 0; r < m.hidden; ++r) w(K_DOWN).push_back((int64_t)e * 1000000 + r);
       }
       for (int b = 0; b < B; ++b)
-        for (int r = 0; r < m.hidden; ++r) want["ffn" + ls].insert((int64_t)b * 1000000 + r);
+        for (int r = 0; r < m.hidden; ++r) w(K_FFN).push_back((int64_t)b * 1000000 + r);
       continue;
     }
-    for (int r = 0; r < m.hidden; ++r) want["down" + ls].insert(r);
+    for (int r = 0; r < m.hidden; ++r) w(K_DOWN).push_back(r);
     if (moe) {
-      for (int r = 0; r < m.n_experts; ++r) want["router" + ls].insert(r);
+      for (int r = 0; r < m.n_experts; ++r) w(K_ROUTER).push_back(r);
       for (int b = 0; b < B; ++b)
         for (int j = 0; j < m.top_k; ++j)
-          for (int f = 0; f < p->F; ++f) want["gateup" + ls].insert(((int64_t)b * 64 + j) * 1000000 + f);
+          for (int f = 0; f < p->F; ++f) w(K_GATEUP).push_back(((int64_t)b * 64 + j) * 1000000 + f);
     } else {
-      for (int f = 0; f < p->F; ++f) want["gateup" + ls].insert(f);
+      for (int f = 0; f < p->F; ++f) w(K_GATEUP).push_back(f);
     }
   }
-  for (int r = 0; r < m.vocab; ++r) want["lm"].insert(r);
-  for (int b = 0; b < (p->batch ? B : 1); ++b) want["final"].insert(b);
+  for (int r = 0; r < m.vocab; ++r) want[slot(K_LM, L)].push_back(r);
+  for (int b = 0; b < (p->batch ? B : 1); ++b) want[slot(K_FINAL, L)].push_back(b);
 
-  std::map<std::string, std::multiset<int64_t>> got;
   std::vector<uint32_t> producers(p->targets.size(), 0);
   std::vector<int> ctr_stage(p->targets.size(), -1);
   size_t k = 0;
@@ -965,9 +1003,11 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
       if ((t.op == mk::OP_EXPERT || t.op == mk::OP_BEXP) && !expert_layers.insert(t.layer).second)
         return fail(MK_EINVAL, "validate: unit " + std::to_string(cu) + " holds two expert tasks of layer " +
                                    std::to_string(t.layer) + " (their down parts would wait on each other)");
-      std::vector<std::pair<std::string, int64_t>> outs;
-      task_outputs(p, t, outs);
-      for (auto& [key, v] : outs) got[key].insert(v);
+      if (t.layer >= L && t.op != mk::OP_LM && t.op != mk::OP_BLM && t.op != mk::OP_FINAL && t.op != mk::OP_BFINAL)
+        return fail(MK_EINVAL, "validate: task of layer " + std::to_string(t.layer) + " beyond the model");
+      const int tl = (t.op == mk::OP_LM || t.op == mk::OP_BLM || t.op == mk::OP_FINAL || t.op == mk::OP_BFINAL)
+                         ? L : t.layer;
+      task_outputs(p, t, [&](int kind, int64_t v) { got[slot(kind, tl)].push_back(v); });
       if (t.signal != mk::NO_CTR) {
         if (t.signal >= p->targets.size()) return fail(MK_EINVAL, "validate: signal counter out of range");
         producers[t.signal] += t.units;
@@ -981,16 +1021,22 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
     const int pg_bound = (p->bound + 15) / 16;
     for (int l = 0; l < L; ++l)
       for (int g = 0; g < m.n_kv_heads; ++g)
-        for (int pg = 0; pg < pg_bound; ++pg)
-          got["attn:" + std::to_string(l)].insert((int64_t)g * 1000000 + pg);
+        for (int pg = 0; pg < pg_bound; ++pg) got[slot(K_ATTN, l)].push_back((int64_t)g * 1000000 + pg);
   }
-  for (auto& [key, s0] : want) {
-    auto it = got.find(key);
-    if (it == got.end()) return fail(MK_EINVAL, "validate: no task covers " + key);
-    if (it->second.size() != s0.size() || std::set<int64_t>(it->second.begin(), it->second.end()) != s0)
+  // every expected output exactly once, nothing else
+  for (size_t i = 0; i < want.size(); ++i) {
+    auto& a = want[i];
+    auto& b = got[i];
+    std::sort(a.begin(), a.end());
+    std::sort(b.begin(), b.end());
+    if (a != b) {
+      const int kind = (int)(i / (L + 1)), layer = (int)(i % (L + 1));
+      const std::string key = std::string(kind_name[kind]) + (layer < L ? ":" + std::to_string(layer) : "");
+      if (b.empty()) return fail(MK_EINVAL, "validate: no task covers " + key);
+      if (a.empty()) return fail(MK_EINVAL, "validate: tasks of an unexpected kind (" + key + ")");
       return fail(MK_EINVAL, "validate: outputs of " + key + " not covered exactly once");
+    }
   }
-  if (got.size() != want.size()) return fail(MK_EINVAL, "validate: tasks of an unexpected kind");
   // a counter's target is the outputs its tasks produce per step (the
   // attention splits of a queue add their pages on the device: every page
   // below the bound, per kv head)

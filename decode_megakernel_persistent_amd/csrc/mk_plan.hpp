@@ -9,6 +9,7 @@
 struct mk_plan {
   uint64_t uid = 0;  // unique per plan built in this process (never reused)
   mk_model_desc m;
+  mk_plan_opts opts = {};  // as built (n_cu resolved), for mk_plan_update
   int32_t B = 0, max_pages = 0, bound = 0, n_cu = 0;
   bool batch = false;                 // B > 1: MFMA batch tasks
   std::vector<int32_t> seq_lens, page_table;

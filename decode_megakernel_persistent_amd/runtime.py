@@ -12,10 +12,11 @@ import torch
 
 from . import (
     MK_BUF_O, MK_BUF_Q, MK_BUF_RLOG, MK_BUF_XATTN, MK_BUF_XFFN,
-    MkError, MK_OK, mk_decode_step, mk_decode_step_static, mk_io, mk_kv, mk_kv_pool_elems, mk_plan, mk_plan_buffer,
-    mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks, mk_plan_upload,
-    mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_step_status, mk_weights,
-    model_desc,
+    MK_PLAN_CHANGED_COUNTERS, MK_PLAN_CHANGED_IMAGE, MK_PLAN_CHANGED_WORKSPACE,
+    MkError, MK_OK, mk_decode_step, mk_decode_step_static, mk_io, mk_kv, mk_kv_pool_elems, mk_plan,
+    mk_plan_buffer, mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks,
+    mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers,
+    mk_step_status, mk_weights, model_desc,
 )
 
 TRACE_WORDS = 16    # u64 per task in the optional trace buffer
@@ -74,23 +75,68 @@ class Decoder:
         mk_plan_upload(self.plan, self.plan_buf.data_ptr(), self.plan_buf.numel(), stream)
         self.page_table = torch.tensor(flat, dtype=torch.int32, device=dev).view(self.B, max_pages)
         self.seq_lens = torch.tensor([int(v) for v in seq_lens], dtype=torch.int32, device=dev)
-        self.rope_cos, self.rope_sin = rope_tables(self.m, bound, dev)
         self.pool = pool
+        self.n_pages = n_pages
         self.W = weights
         self.epoch = 0
         self._w = mk_weights(*[_ptr(weights.get(k)) for k, _ in mk_weights._fields_])
-        self._kv = mk_kv(pool.data_ptr(), n_pages, self.page_table.data_ptr(),
-                         self.seq_lens.data_ptr(), self.rope_cos.data_ptr(),
-                         self.rope_sin.data_ptr(), bound)
+        self._set_rope(bound)
         self.trace = None
         if trace:
             n = mk_plan_n_tasks(self.plan) * TRACE_WORDS
             self.trace = torch.zeros(n, dtype=torch.int64, device=dev)
+        self._set_bufs()
+
+    def _set_rope(self, n_pos):
+        self.rope_cos, self.rope_sin = rope_tables(self.m, n_pos, self.device)
+        self._kv = mk_kv(self.pool.data_ptr(), self.n_pages, self.page_table.data_ptr(),
+                         self.seq_lens.data_ptr(), self.rope_cos.data_ptr(),
+                         self.rope_sin.data_ptr(), n_pos)
+
+    def _set_bufs(self):
         self._bufs = mk_step_buffers(self.plan_buf.data_ptr(), self.plan_buf.numel(),
                                      self.ws.data_ptr(), self.ws.numel(), self.ctr.data_ptr(),
                                      self.ctr.numel() * 4, self.status.data_ptr(),
                                      _ptr(self.trace),
                                      0 if self.trace is None else self.trace.numel() * 8)
+
+    def update(self, seq_lens, page_table, bound, ctx_bounds=None):
+        """Refresh the plan for new lengths / page table / bounds of the same
+        batch (mk_plan_update) and apply what changed, in stream order after
+        the steps already enqueued: the device image, a fresh workspace,
+        counters and epochs where the planner asks for them, the device page
+        table and lengths, and larger rope tables if the bound outgrew them.
+        Returns the MK_PLAN_CHANGED_* bits."""
+        flat = [int(v) for row in page_table for v in row]
+        ch = mk_plan_update(self.plan, seq_lens, flat, bound, ctx_bounds)
+        dev = self.device
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        if ch & MK_PLAN_CHANGED_IMAGE:
+            n = mk_plan_device_bytes(self.plan)
+            if n > self.plan_buf.numel():
+                self.plan_buf = torch.empty(n, dtype=torch.uint8, device=dev)
+            mk_plan_upload(self.plan, self.plan_buf.data_ptr(), self.plan_buf.numel(), stream)
+        if ch & (MK_PLAN_CHANGED_WORKSPACE | MK_PLAN_CHANGED_COUNTERS):
+            nw, nc = mk_plan_workspace_bytes(self.plan), mk_plan_counter_bytes(self.plan) // 4
+            if nw != self.ws.numel():
+                self.ws = torch.zeros(nw, dtype=torch.uint8, device=dev)
+            else:
+                self.ws.zero_()
+            if nc != self.ctr.numel():
+                self.ctr = torch.zeros(nc, dtype=torch.int32, device=dev)
+            else:
+                self.ctr.zero_()
+            self.epoch = 0
+            if self.trace is not None:
+                n = mk_plan_n_tasks(self.plan) * TRACE_WORDS
+                self.trace = torch.zeros(n, dtype=torch.int64, device=dev)
+        self.page_table.copy_(torch.tensor(flat, dtype=torch.int32).view_as(self.page_table))
+        self.seq_lens.copy_(torch.tensor([int(v) for v in seq_lens], dtype=torch.int32))
+        if bound > self._kv.n_rope_pos:
+            self._set_rope(bound)
+        self.bound = bound
+        self._set_bufs()
+        return ch
 
     def close(self):
         if self.plan:

@@ -23,8 +23,8 @@
  *    deadline, a context past the plan's bound) are written to the status
  *    words, which the caller reads after its next synchronisation and
  *    decodes with mk_step_status.
- *  - Threads: a plan is immutable once built and may be used from several
- *    threads; a pool is single-threaded.
+ *  - Threads: a plan is immutable except through mk_plan_update and may be
+ *    used from several threads; a pool is single-threaded.
  *  - Determinism: the same inputs give the same plan bytes and the same
  *    output bits (kern page, "The harness": running twice and diffing is a
  *    test).
@@ -201,6 +201,26 @@ mk_status mk_step_bytes(const mk_model_desc* m, int32_t batch, const int32_t* se
  * sequence and expert tasks that pick up the sequences routed to them. */
 mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* b, const mk_plan_opts* o,
                   mk_plan_t** out);
+/* Refresh a plan for the next steps of the same batch (same size, page-table
+ * width, model and options): new sequence lengths and page table (host; e.g.
+ * after the pool mapped a sequence's next page at a 16-token boundary, or a
+ * sequence was replaced in its batch slot) and new context bounds, with the
+ * same meaning as in mk_batch_desc. The plan is rebuilt in place and is then
+ * byte-identical to mk_plan of the same arguments. *changed (may be NULL)
+ * receives MK_PLAN_CHANGED_* bits: IMAGE -- the device image changed:
+ * upload it again before the next step; WORKSPACE -- the workspace layout
+ * changed; COUNTERS -- the counters or their targets changed. After either
+ * of the last two, start again as after mk_plan: a zero-filled workspace of
+ * mk_plan_workspace_bytes, zeroed counters, epochs from 1
+ * (mk_decode_step_static does this by itself). The device page table and
+ * sequence lengths are the caller's buffers: copy the new values there.
+ * On failure (e.g. MK_EBOUNDS for a length past its bound) the plan is left
+ * as it was. A plan may not be updated while a step that uses it runs. */
+#define MK_PLAN_CHANGED_IMAGE 1
+#define MK_PLAN_CHANGED_WORKSPACE 2
+#define MK_PLAN_CHANGED_COUNTERS 4
+mk_status mk_plan_update(mk_plan_t* p, const int32_t* seq_lens, const int32_t* page_table,
+                         int32_t max_ctx_bound, const int32_t* ctx_bounds, int32_t* changed);
 /* Coverage (every output row / KV page exactly once), counter targets equal
  * the outputs of the tasks that signal them, per-list stage order, waits on
  * earlier stages only. MK_OK or MK_EINVAL with a message. */

@@ -416,3 +416,67 @@ def test_static_step_rejects_plans_beyond_its_scratch():
     finally:
         mk.mk_plan_free(p)
         mk.mk_pool_free(pool)
+
+
+def fresh_export(w, lens, flat, max_pages, bound, cb, n_cu, flags):
+    q = mk.mk_plan(mk.model_desc(w["model"]), lens, flat, max_pages, bound, n_cu=n_cu, flags=flags,
+                   ctx_bounds=cb)
+    try:
+        return mk.mk_plan_export(q), mk.mk_plan_counter_targets(q), mk.mk_plan_workspace_bytes(q)
+    finally:
+        mk.mk_plan_free(q)
+
+
+@pytest.mark.parametrize("name,n_cu,flags", [("tiny_dense", 16, 0), ("small_moe", 256, 0),
+                                             ("tiny_dense", 16, mk.MK_PLAN_ATTN_QUEUE),
+                                             ("small_moe_b5", 256, 0), ("tiny_dense_b3", 40, 0),
+                                             ("moe48_b1_8k", 256, 0), ("moe48_b32_ragged", 256, 0)])
+def test_plan_update_equals_rebuild(name, n_cu, flags):
+    """mk_plan_update leaves the plan byte-identical to mk_plan of the same
+    arguments, reports exactly what differs from before, and a failed update
+    leaves the plan as it was."""
+    w, pool, p, bound = build_plan(name, n_cu, flags)
+    B, pt = w["batch"], w["model"]["page_tokens"]
+    rows = mk.mk_pool_page_table(pool, list(range(B)), -(-bound // pt))
+    max_pages = len(rows[0])
+    flat = [v for r in rows for v in r]
+    rng = random.Random(5)
+    lens = list(w["ctx"])
+    try:
+        before = (mk.mk_plan_export(p), mk.mk_plan_counter_targets(p), mk.mk_plan_workspace_bytes(p))
+        cases = [("same", lens, flat, ctx_bounds(w) if B > 1 else None),
+                 ("one step on", [c + 1 for c in lens], flat, ctx_bounds(w) if B > 1 else None),
+                 ("tight bounds", lens, flat, [c + 1 for c in lens] if B > 1 else None)]
+        if B > 1:
+            # sequences swap batch slots: rows, lengths and bounds move together
+            perm = list(range(B))
+            rng.shuffle(perm)
+            cb = ctx_bounds(w)
+            cases.append(("slots permuted", [lens[i] for i in perm],
+                          [v for i in perm for v in rows[i]], [cb[i] for i in perm]))
+        for label, sl, pt_flat, cb in cases:
+            bd = max(cb) if cb is not None else (bound if label != "tight bounds" else max(sl) + 1)
+            ch = mk.mk_plan_update(p, sl, pt_flat, bd, cb)
+            after = (mk.mk_plan_export(p), mk.mk_plan_counter_targets(p), mk.mk_plan_workspace_bytes(p))
+            assert after == fresh_export(w, sl, pt_flat, max_pages, bd, cb, n_cu, flags), label
+            want = ((mk.MK_PLAN_CHANGED_IMAGE if after[0] != before[0] else 0)
+                    | (mk.MK_PLAN_CHANGED_COUNTERS if after[1] != before[1] else 0))
+            assert ch & ~mk.MK_PLAN_CHANGED_WORKSPACE == want, label
+            if after[2] != before[2]:
+                assert ch & mk.MK_PLAN_CHANGED_WORKSPACE, label
+            if label == "same":
+                assert ch == 0
+            mk.mk_plan_validate(p)
+            before = after
+        # a length past its bound fails and changes nothing
+        bad = [c + 1 for c in lens]
+        bad[0] = (max(cases[-1][3]) if B > 1 else bd) + 5
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_plan_update(p, bad, cases[-1][2], max(cases[-1][3]) if B > 1 else bd, cases[-1][3])
+        assert e.value.status == mk.MK_EBOUNDS
+        assert (mk.mk_plan_export(p), mk.mk_plan_counter_targets(p), mk.mk_plan_workspace_bytes(p)) == before
+        with pytest.raises(ValueError):
+            mk.mk_plan_update(p, lens, flat[:-1], bound, None if B == 1 else ctx_bounds(w))
+    finally:
+        mk.mk_plan_free(p)
+        mk.mk_pool_free(pool)
