@@ -2236,9 +2236,13 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
         }
         break;
     }
-    if (!ok) return;  // uniform: the failure was recorded in the status words
+    // A failure (recorded in the status words) may reach only some threads
+    // (a residual wait in one lane): it is shared through LDS, so that the
+    // whole workgroup leaves together.
+    if (!ok) s.fail = 1;
     const uint64_t t_body = (a.trace && tid() == 0) ? now() : 0;
     lds_barrier();  // LDS is reused by the next task
+    if (s.fail) return;
     if (tid() == 0) {
       if (t.signal != NO_CTR)
         __hip_atomic_fetch_add(a.ctr + ((size_t)t.signal * CTR_LINES + blockIdx.x % CTR_LINES) * CTR_STRIDE,
@@ -2346,9 +2350,15 @@ extern "C" mk_status mk_step_status(const uint32_t* h) {
   if (!h) return fail(MK_EINVAL, "mk_step_status: NULL");
   switch (h[0]) {
     case mk::DS_OK: return MK_OK;
-    case mk::DS_TIMEOUT:
-      return fail(MK_ETIMEOUT, "device wait timed out: task " + std::to_string(h[1]) + " buffer word " +
-                                   std::to_string(h[2]) + " tag seen " + std::to_string(h[3]));
+    case mk::DS_TIMEOUT: {
+      // word 3 tells the kind of wait: a gather of word pairs, a batch
+      // activation panel, or a single word (then word 3 is the tag it held)
+      const std::string what = h[3] == 0xFFFFFFFDu   ? "gather of word pairs (stale pair " + std::to_string(h[2]) + ")"
+                               : h[3] == 0xFFFFFFFEu ? "activation panel of sequence " + std::to_string(h[2])
+                                                     : "buffer word " + std::to_string(h[2]) + " tag seen " +
+                                                           std::to_string(h[3]);
+      return fail(MK_ETIMEOUT, "device wait timed out: task " + std::to_string(h[1]) + ", " + what);
+    }
     case mk::DS_BOUNDS:
       return fail(MK_EBOUNDS, "device bounds check failed: task " + std::to_string(h[1]) +
                                   " (token, position or page outside the plan/pool)");

@@ -12,7 +12,7 @@ import torch
 
 from . import (
     MK_BUF_O, MK_BUF_Q, MK_BUF_RLOG, MK_BUF_XATTN, MK_BUF_XFFN,
-    MK_PLAN_CHANGED_COUNTERS, MK_PLAN_CHANGED_IMAGE, MK_PLAN_CHANGED_WORKSPACE,
+    MK_PLAN_ATTN_QUEUE, MK_PLAN_CHANGED_COUNTERS, MK_PLAN_CHANGED_IMAGE, MK_PLAN_CHANGED_WORKSPACE,
     MkError, MK_OK, mk_decode_step, mk_decode_step_static, mk_io, mk_kv, mk_kv_pool_elems, mk_plan,
     mk_plan_buffer, mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks,
     mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers,
@@ -61,6 +61,7 @@ class Decoder:
         self.device = torch.device(device)
         self.B = len(seq_lens)
         self.desc = model_desc(self.m)
+        self.plan_flags = plan_flags
         flat = [int(v) for row in page_table for v in row]
         self.plan = mk_plan(self.desc, seq_lens, flat, max_pages, bound, n_cu, attn_split_pages, plan_flags,
                             ctx_bounds)
@@ -164,6 +165,18 @@ class Decoder:
         mk_decode_step_static(self.plan, self._w, self._kv, io, self.plan_buf.data_ptr(), self.plan_buf.numel(),
                               self.status.data_ptr(), timeout_ms,
                               torch.cuda.current_stream(self.device).cuda_stream)
+
+    def recover(self, seq_lens):
+        """Make the decoder usable after a failed step (status words set):
+        zero the status and counters, put back the sequence lengths of
+        before the step and, with the attention queue, start again from a
+        zero-filled workspace and epoch 1. The next step uses a new epoch."""
+        self.status.zero_()
+        self.ctr.zero_()
+        self.seq_lens.copy_(torch.tensor([int(v) for v in seq_lens], dtype=torch.int32))
+        if self.plan_flags & MK_PLAN_ATTN_QUEUE:
+            self.ws.zero_()
+            self.epoch = 0
 
     def check_status(self):
         """Synchronise and raise MkError if the device recorded a failure."""

@@ -288,7 +288,12 @@ void mk_plan_free(mk_plan_t* p);
  * On completion every seq_lens[b] has grown by one: the new token's K and V
  * sit at position seq_lens[b] (old value) of its sequence. timeout_ms bounds
  * every dependency wait (0: 2000 ms); on expiry the kernel records
- * MK_ETIMEOUT in the status words and every workgroup exits. */
+ * MK_ETIMEOUT in the status words and every workgroup exits. After a failed
+ * step the outputs, the new token's K/V slots and the counters are
+ * undefined and a sequence's length may or may not have advanced: zero the
+ * status words and the counters, restore seq_lens and run the step again
+ * with a larger epoch (a plan with the attention queue: start again as after
+ * mk_plan, from a zero-filled workspace and epoch 1). */
 mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv,
                          const mk_io* io, const mk_step_buffers* bufs, uint32_t epoch,
                          uint32_t timeout_ms, void* hip_stream);
@@ -309,15 +314,22 @@ mk_status mk_decode_step(const mk_plan_t* p, const mk_weights* w, const mk_kv* k
  * shares that device's scratch: calls that overlap on one device (other
  * streams, other threads) race and must be serialised by the caller; the
  * counters and tagged activations are not readable through this entry point.
+ * After a failed step, zero the status words, restore seq_lens and call again
+ * (the next epoch); a plan with the attention queue must be built again.
  * MK_EBOUNDS if the plan's workspace and counters exceed the scratch (large
  * batch plans: use mk_decode_step). */
 #define MK_STATIC_SCRATCH_BYTES (128u << 20)
 mk_status mk_decode_step_static(const mk_plan_t* p, const mk_weights* w, const mk_kv* kv,
                                 const mk_io* io, const void* d_plan, size_t plan_bytes,
                                 uint32_t* d_status, uint32_t timeout_ms, void* hip_stream);
-/* Decode a host copy of the 4 status words: MK_OK, MK_ETIMEOUT (word 1: task
- * index, word 2: counter, word 3: value seen) or MK_EBOUNDS (context past the
- * plan bound). Sets mk_last_error. */
+/* Decode a host copy of the 4 status words: MK_OK, MK_ETIMEOUT (word 1: the
+ * index of the task that waited, in the plan's task order; words 2 and 3:
+ * what it waited for -- word 3 = 0xFFFFFFFD: a gather of tagged word pairs,
+ * word 2 the first stale pair of the thread that gave up; 0xFFFFFFFE: a
+ * batch activation panel, word 2 the sequence; otherwise word 2 is the
+ * offset of the awaited word in its buffer and word 3 the tag it held) or
+ * MK_EBOUNDS (word 1: the task; a token, position or page outside the plan
+ * or pool). Sets mk_last_error. */
 mk_status mk_step_status(const uint32_t* h_status);
 
 /* ---- page/slot pool (pure host; kern page, "The runtime") ----

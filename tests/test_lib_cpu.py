@@ -355,6 +355,10 @@ def test_step_status_decoding():
     assert mk.mk_step_status([0, 0, 0, 0])[0] == mk.MK_OK
     st, msg = mk.mk_step_status([1, 17, 3, 42])
     assert st == mk.MK_ETIMEOUT and "task 17" in msg and "word 3" in msg and "tag seen 42" in msg
+    st, msg = mk.mk_step_status([1, 9, 4, 0xFFFFFFFD])
+    assert st == mk.MK_ETIMEOUT and "task 9" in msg and "pair 4" in msg
+    st, msg = mk.mk_step_status([1, 9, 2, 0xFFFFFFFE])
+    assert st == mk.MK_ETIMEOUT and "sequence 2" in msg
     assert mk.mk_step_status([2, 5, 0, 0])[0] == mk.MK_EBOUNDS
 
 
