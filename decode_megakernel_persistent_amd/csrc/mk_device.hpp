@@ -199,23 +199,32 @@ __device__ __forceinline__ void st_tagged(uint64_t* p, float v, uint32_t epoch) 
 }
 __device__ __forceinline__ bool tag_is(uint64_t w, uint32_t epoch) { return (uint32_t)(w >> 32) == epoch; }
 
-// Two neighbouring tagged words in one 16-byte load with the same coherence
-// as ld_tagged (the L2 of this XCD is bypassed): a buffer resource over
-// nbytes at base (wave-uniform), byte offset off (a multiple of 16). Each
-// aligned 8-byte half is one word as its single store wrote it, so each half's
-// tag vouches for its own value. Offsets at or past nbytes read zeros (a
-// stale tag), never another allocation. .x/.y = word 0 (value, tag), .z/.w =
-// word 1.
+// Two neighbouring tagged words (byte offset off, a multiple of 16, in a
+// buffer of nbytes at base) read as two 8-byte loads, both in flight
+// together, each with the same coherence as ld_tagged (sc1: this XCD's L2 is
+// bypassed). Each load is the very instruction that the AMDGPU backend emits
+// for a relaxed agent-scope 64-bit atomic load (LLVM "User Guide for AMDGPU
+// Backend", memory model code sequences for GFX942, which gfx950 follows:
+// load atomic monotonic, agent scope = buffer/global load with sc1), so each
+// word arrives whole, as its single 8-byte store wrote it, and its tag
+// vouches for its own value. A 16-byte load of the pair would not be an
+// atomic access in that model: the scheduling barrier keeps the compiler
+// from merging the two loads into one (a CPU test checks the built code
+// object for it). The buffer resource makes offsets at or past nbytes read
+// zeros (a stale tag), never another allocation. .x/.y = word 0 (value,
+// tag), .z/.w = word 1.
 typedef __amdgpu_buffer_rsrc_t tag_rsrc;
 __device__ __forceinline__ tag_rsrc tagged_rsrc(const uint64_t* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)nbytes, 0x00020000);
 }
+typedef unsigned int tag_u2 __attribute__((ext_vector_type(2)));
 // A caller that re-reads a word in a loop puts a compiler memory barrier
 // (tagged_reload_fence) between the reads, so that they are not merged.
 __device__ __forceinline__ uint4 ld_tagged2(tag_rsrc r, uint32_t off) {
-  // cache policy: sc1 (device coherence, as ld_tagged)
-  const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
-  return make_uint4(v.x, v.y, v.z, v.w);
+  const tag_u2 w0 = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16);  // cache policy 16: sc1
+  __builtin_amdgcn_sched_barrier(0);
+  const tag_u2 w1 = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8u, 0, 16);
+  return make_uint4(w0.x, w0.y, w1.x, w1.y);
 }
 __device__ __forceinline__ void tagged_reload_fence() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ bool tag2_is(const uint4& v, uint32_t epoch) { return v.y == epoch && v.w == epoch; }

@@ -484,3 +484,27 @@ def test_plan_update_equals_rebuild(name, n_cu, flags):
     finally:
         mk.mk_plan_free(p)
         mk.mk_pool_free(pool)
+
+
+def test_tagged_pair_reads_stay_8_byte_loads(tmp_path):
+    """The device code reads tagged words only with 8-byte loads: every
+    buffer load with device coherence (sc1) in the built gfx950 code object
+    is a dwordx2 (the form of a 64-bit atomic load), and no 16-byte buffer
+    load exists, i.e. the compiler did not merge a pair of word loads."""
+    import shutil
+    import subprocess
+    llvm = "/opt/rocm/llvm/bin"
+    tools = [shutil.which("objcopy"), os.path.join(llvm, "clang-offload-bundler"), os.path.join(llvm, "llvm-objdump")]
+    if not all(t and os.path.exists(t) for t in tools):
+        pytest.skip("objcopy / clang-offload-bundler / llvm-objdump not available")
+    lib = os.path.join(ROOT, "decode_megakernel_persistent_amd", "libmk.so")
+    fb, co = tmp_path / "fatbin", tmp_path / "gfx950.co"
+    subprocess.run([tools[0], "--dump-section", f".hip_fatbin={fb}", lib], check=True)
+    subprocess.run([tools[1], "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fb}",
+                    f"--output={co}", "--unbundle"], check=True)
+    dis = subprocess.run([tools[2], "-d", str(co)], check=True, capture_output=True, text=True).stdout
+    loads = [l for l in dis.splitlines() if "buffer_load_dword" in l]
+    coherent = [l for l in loads if re.search(r"\bsc1\b", l)]
+    assert coherent, "no device-coherent buffer loads found"
+    assert all("buffer_load_dwordx2" in l for l in coherent), [l for l in coherent if "dwordx2" not in l][:3]
+    assert not any("buffer_load_dwordx4" in l for l in loads)
