@@ -101,6 +101,9 @@ _SIGS = {
     "mk_step_status": (_i32, [_vp]),
     "mk_pool_create": (_i32, [_i32, _i32, _i32, _vp, _P(_vp)]),
     "mk_pool_lease": (_i32, [_vp, _i64, _i32, _P(_i32)]),
+    "mk_pool_lease_prefix": (_i32, [_vp, _i64, _vp, _i32, _i32, _P(_i32), _P(_i32), _P(_i32), _P(_i32)]),
+    "mk_pool_finish": (_i32, [_vp, _i64, _vp, _i32]),
+    "mk_pool_cached_pages": (_i32, [_vp]),
     "mk_pool_extend": (_i32, [_vp, _i64, _i32]),
     "mk_pool_release": (_i32, [_vp, _i64]),
     "mk_pool_page_table": (_i32, [_vp, _vp, _i32, _i32, _vp]),
@@ -306,6 +309,26 @@ def mk_pool_lease(pool, seq_id, tokens):
     slot = _i32()
     _check(_lib.mk_pool_lease(pool, seq_id, tokens, ctypes.byref(slot)))
     return slot.value
+
+
+def mk_pool_lease_prefix(pool, seq_id, prompt, tokens):
+    """Lease with prefix sharing: returns (slot, matched tokens, copy_src, copy_dst)."""
+    n = len(prompt)
+    pr = (_i32 * max(n, 1))(*[int(v) for v in prompt])
+    slot, m, cs, cd = _i32(), _i32(), _i32(), _i32()
+    _check(_lib.mk_pool_lease_prefix(pool, seq_id, pr, n, tokens, ctypes.byref(slot), ctypes.byref(m),
+                                     ctypes.byref(cs), ctypes.byref(cd)))
+    return slot.value, m.value, cs.value, cd.value
+
+
+def mk_pool_finish(pool, seq_id, tokens):
+    n = len(tokens)
+    tk = (_i32 * max(n, 1))(*[int(v) for v in tokens])
+    _check(_lib.mk_pool_finish(pool, seq_id, tk, n))
+
+
+def mk_pool_cached_pages(pool):
+    return _lib.mk_pool_cached_pages(pool)
 
 
 def mk_pool_extend(pool, seq_id, tokens):

@@ -71,12 +71,37 @@ extern "C" mk_status mk_step_bytes(const mk_model_desc* m, int32_t batch, const 
 
 // ------------------------------------------------------------------ pool
 
+// Pages, sequence slots and prefix checkpoints (kern page, "The runtime": a
+// request leases its worst case and a slot, all or nothing; when it ends its
+// pages freeze in place as a checkpoint; a later request with the same
+// prefix shares the whole pages and gets a copy of the page the prefix ends
+// inside; a token radix tree finds the longest checkpoint).
+//
+// ref[page] counts the page's holders: every live sequence whose list holds
+// it, plus one while a checkpoint node holds it; a page is on the free list
+// exactly when its count is zero. Checkpoint nodes form a tree with one page
+// per node: a node's tokens are the tokens whose K/V its page holds (page_tokens
+// of them, or fewer for the tail page of a sequence, which is always a leaf).
+// Siblings never hold equal token runs.
 struct mk_pool {
+  struct Node {
+    int32_t page = -1;  // -1: the root
+    std::vector<int32_t> tokens;
+    int32_t parent = -1;
+    std::vector<int32_t> children;
+    uint64_t tick = 0, order = 0;  // last use; insertion number
+    bool alive = true;
+  };
   int32_t n_pages, pt, n_slots;
   std::deque<int32_t> free_list;
   std::vector<char> slot_used;
+  std::vector<int32_t> ref;
+  std::vector<int32_t> node_of;  // checkpoint node holding a page, or -1
   std::map<int64_t, std::vector<int32_t>> pages;
   std::map<int64_t, int32_t> slot;
+  std::vector<Node> nodes;  // nodes[0] is the root; a child's index exceeds its parent's
+  uint64_t clock = 0, inserted = 0;
+  int32_t cached = 0;  // live checkpoint nodes (= pages they hold)
 };
 
 extern "C" mk_status mk_pool_create(int32_t n_pages, int32_t pt, int32_t n_slots,
@@ -87,6 +112,9 @@ extern "C" mk_status mk_pool_create(int32_t n_pages, int32_t pt, int32_t n_slots
   p->pt = pt;
   p->n_slots = n_slots;
   p->slot_used.assign(n_slots, 0);
+  p->ref.assign(n_pages, 0);
+  p->node_of.assign(n_pages, -1);
+  p->nodes.emplace_back();
   std::vector<char> seen(n_pages, 0);
   for (int32_t i = 0; i < n_pages; ++i) {
     int32_t v = order ? order[i] : i;
@@ -101,28 +129,161 @@ extern "C" mk_status mk_pool_create(int32_t n_pages, int32_t pt, int32_t n_slots
   return MK_OK;
 }
 
-static int32_t pages_for(const mk_pool* p, int64_t tokens) {
-  return (int32_t)((tokens + p->pt - 1) / p->pt);
+namespace {
+
+int32_t pages_for(const mk_pool* p, int64_t tokens) { return (int32_t)((tokens + p->pt - 1) / p->pt); }
+
+int32_t lowest_free_slot(const mk_pool* p) {
+  for (int32_t i = 0; i < p->n_slots; ++i)
+    if (!p->slot_used[i]) return i;
+  return -1;
 }
 
-extern "C" mk_status mk_pool_lease(mk_pool_t* p, int64_t seq, int32_t tokens, int32_t* slot_out) {
-  if (!p || tokens < 0) return fail(MK_EINVAL, "mk_pool_lease: bad args");
-  if (p->pages.count(seq)) return fail(MK_ESTATE, "mk_pool_lease: sequence already holds a lease");
-  int32_t need = pages_for(p, tokens);
-  int32_t slot = -1;
-  for (int32_t i = 0; i < p->n_slots; ++i)
-    if (!p->slot_used[i]) { slot = i; break; }
-  if (slot < 0) return fail(MK_ENOMEM, "mk_pool_lease: no free sequence slot");
-  if (need > (int32_t)p->free_list.size())
-    return fail(MK_ENOMEM, "mk_pool_lease: " + std::to_string(need) + " pages needed, " +
-                               std::to_string(p->free_list.size()) + " free");
-  std::vector<int32_t> got(p->free_list.begin(), p->free_list.begin() + need);
-  p->free_list.erase(p->free_list.begin(), p->free_list.begin() + need);
-  p->pages[seq] = std::move(got);
+// Checkpoint pages that evictions could free: the nodes of every subtree in
+// which no page has a holder besides its node (children before parents).
+int64_t evictable(const mk_pool* p) {
+  std::vector<char> ev(p->nodes.size(), 0);
+  int64_t n = 0;
+  for (size_t i = p->nodes.size(); i-- > 1;) {
+    const auto& nd = p->nodes[i];
+    if (!nd.alive || p->ref[nd.page] != 1) continue;
+    bool all = true;
+    for (int32_t c : nd.children) all = all && ev[c];
+    if (all) {
+      ev[i] = 1;
+      ++n;
+    }
+  }
+  return n;
+}
+
+// Evict the least recently used leaf whose page only its node holds (ties:
+// the earlier inserted); its page goes to the back of the free list.
+bool evict_one(mk_pool* p) {
+  int32_t best = -1;
+  for (size_t i = 1; i < p->nodes.size(); ++i) {
+    const auto& nd = p->nodes[i];
+    if (!nd.alive || !nd.children.empty() || p->ref[nd.page] != 1) continue;
+    if (best < 0 || nd.tick < p->nodes[best].tick ||
+        (nd.tick == p->nodes[best].tick && nd.order < p->nodes[best].order))
+      best = (int32_t)i;
+  }
+  if (best < 0) return false;
+  auto& nd = p->nodes[best];
+  nd.alive = false;
+  auto& sib = p->nodes[nd.parent].children;
+  sib.erase(std::find(sib.begin(), sib.end(), best));
+  p->ref[nd.page] = 0;
+  p->node_of[nd.page] = -1;
+  p->free_list.push_back(nd.page);
+  --p->cached;
+  return true;
+}
+
+// Make n pages free, evicting checkpoints under pressure; all or nothing.
+bool ensure_free(mk_pool* p, int64_t n) {
+  if ((int64_t)p->free_list.size() >= n) return true;
+  if ((int64_t)p->free_list.size() + evictable(p) < n) return false;
+  while ((int64_t)p->free_list.size() < n) evict_one(p);
+  return true;
+}
+
+std::vector<int32_t> take_free(mk_pool* p, int32_t n) {
+  std::vector<int32_t> got(p->free_list.begin(), p->free_list.begin() + n);
+  p->free_list.erase(p->free_list.begin(), p->free_list.begin() + n);
+  for (int32_t pg : got) p->ref[pg] = 1;
+  return got;
+}
+
+// Longest checkpointed prefix of tokens[0, limit): the full nodes matched
+// whole (path) and the node the match ends inside (-1: none). At each page
+// the child with the longest common run wins (ties: the earlier inserted).
+int32_t match_prefix(const mk_pool* p, const int32_t* tokens, int32_t limit, std::vector<int32_t>& path,
+                     int32_t* inside) {
+  int32_t node = 0, pos = 0;
+  *inside = -1;
+  while (pos < limit) {
+    const int32_t span = std::min(p->pt, limit - pos);
+    int32_t best = -1, best_n = 0;
+    for (int32_t c : p->nodes[node].children) {
+      const auto& t = p->nodes[c].tokens;
+      int32_t n = 0;
+      while (n < span && n < (int32_t)t.size() && t[n] == tokens[pos + n]) ++n;
+      if (n > best_n || (n == best_n && n > 0 && p->nodes[c].order < p->nodes[best].order)) {
+        best = c;
+        best_n = n;
+      }
+    }
+    if (best < 0) break;
+    if (best_n == p->pt) {
+      path.push_back(best);
+      node = best;
+      pos += p->pt;
+      continue;
+    }
+    *inside = best;
+    pos += best_n;
+    break;
+  }
+  return pos;
+}
+
+mk_status lease_impl(mk_pool* p, int64_t seq, const int32_t* prompt, int32_t n_prompt, int32_t tokens,
+                     int32_t* slot_out, int32_t* matched, int32_t* copy_src, int32_t* copy_dst,
+                     const char* who) {
+  if (p->pages.count(seq)) return fail(MK_ESTATE, std::string(who) + ": sequence already holds a lease");
+  const int32_t slot = lowest_free_slot(p);
+  if (slot < 0) return fail(MK_ENOMEM, std::string(who) + ": no free sequence slot");
+  std::vector<int32_t> path;
+  int32_t inside = -1, m = 0;
+  // the prompt's last token always runs: it gives the next token's logits
+  if (prompt && n_prompt > 1) m = match_prefix(p, prompt, n_prompt - 1, path, &inside);
+  const int32_t need = pages_for(p, tokens) - (int32_t)path.size();
+  // pin what the lease reuses, so that no eviction takes it
+  for (int32_t n : path) ++p->ref[p->nodes[n].page];
+  if (inside >= 0) ++p->ref[p->nodes[inside].page];
+  if (!ensure_free(p, need)) {
+    for (int32_t n : path) --p->ref[p->nodes[n].page];
+    if (inside >= 0) --p->ref[p->nodes[inside].page];
+    return fail(MK_ENOMEM, std::string(who) + ": " + std::to_string(need) + " pages needed, " +
+                               std::to_string(p->free_list.size()) + " free and " +
+                               std::to_string(evictable(p)) + " held by checkpoints no one reads");
+  }
+  std::vector<int32_t> list;
+  for (int32_t n : path) {
+    list.push_back(p->nodes[n].page);
+    p->nodes[n].tick = ++p->clock;
+  }
+  const std::vector<int32_t> fresh = take_free(p, need);
+  list.insert(list.end(), fresh.begin(), fresh.end());
+  if (inside >= 0) {
+    --p->ref[p->nodes[inside].page];
+    p->nodes[inside].tick = ++p->clock;
+  }
+  p->pages[seq] = std::move(list);
   p->slot_used[slot] = 1;
   p->slot[seq] = slot;
   if (slot_out) *slot_out = slot;
+  if (matched) *matched = m;
+  if (copy_src) *copy_src = inside >= 0 ? p->nodes[inside].page : -1;
+  if (copy_dst) *copy_dst = inside >= 0 ? fresh[0] : -1;
   return MK_OK;
+}
+
+}  // namespace
+
+extern "C" mk_status mk_pool_lease(mk_pool_t* p, int64_t seq, int32_t tokens, int32_t* slot_out) {
+  if (!p || tokens < 0) return fail(MK_EINVAL, "mk_pool_lease: bad args");
+  return lease_impl(p, seq, nullptr, 0, tokens, slot_out, nullptr, nullptr, nullptr, "mk_pool_lease");
+}
+
+extern "C" mk_status mk_pool_lease_prefix(mk_pool_t* p, int64_t seq, const int32_t* prompt, int32_t n_prompt,
+                                          int32_t tokens, int32_t* slot_out, int32_t* matched,
+                                          int32_t* copy_src, int32_t* copy_dst) {
+  if (!p || (!prompt && n_prompt) || n_prompt < 0 || tokens < n_prompt)
+    return fail(MK_EINVAL, "mk_pool_lease_prefix: bad args (worst case below the prompt length?)");
+  return lease_impl(p, seq, prompt, n_prompt, tokens, slot_out, matched, copy_src, copy_dst,
+                    "mk_pool_lease_prefix");
 }
 
 extern "C" mk_status mk_pool_extend(mk_pool_t* p, int64_t seq, int32_t tokens) {
@@ -131,11 +292,9 @@ extern "C" mk_status mk_pool_extend(mk_pool_t* p, int64_t seq, int32_t tokens) {
   if (it == p->pages.end()) return fail(MK_ESTATE, "mk_pool_extend: sequence not leased");
   int32_t need = pages_for(p, tokens) - (int32_t)it->second.size();
   if (need <= 0) return MK_OK;
-  if (need > (int32_t)p->free_list.size()) return fail(MK_ENOMEM, "mk_pool_extend: pool exhausted");
-  for (int32_t i = 0; i < need; ++i) {
-    it->second.push_back(p->free_list.front());
-    p->free_list.pop_front();
-  }
+  if (!ensure_free(p, need)) return fail(MK_ENOMEM, "mk_pool_extend: pool exhausted");
+  const std::vector<int32_t> fresh = take_free(p, need);
+  it->second.insert(it->second.end(), fresh.begin(), fresh.end());
   return MK_OK;
 }
 
@@ -143,11 +302,66 @@ extern "C" mk_status mk_pool_release(mk_pool_t* p, int64_t seq) {
   if (!p) return fail(MK_EINVAL, "mk_pool_release: bad args");
   auto it = p->pages.find(seq);
   if (it == p->pages.end()) return fail(MK_ESTATE, "mk_pool_release: sequence not leased");
-  for (int32_t pg : it->second) p->free_list.push_back(pg);
+  for (int32_t pg : it->second)
+    if (--p->ref[pg] == 0) p->free_list.push_back(pg);
   p->pages.erase(it);
   p->slot_used[p->slot[seq]] = 0;
   p->slot.erase(seq);
   return MK_OK;
+}
+
+extern "C" mk_status mk_pool_finish(mk_pool_t* p, int64_t seq, const int32_t* tokens, int32_t n_tokens) {
+  if (!p || (!tokens && n_tokens) || n_tokens < 0) return fail(MK_EINVAL, "mk_pool_finish: bad args");
+  auto it = p->pages.find(seq);
+  if (it == p->pages.end()) return fail(MK_ESTATE, "mk_pool_finish: sequence not leased");
+  const std::vector<int32_t>& list = it->second;
+  if (pages_for(p, n_tokens) > (int32_t)list.size())
+    return fail(MK_EBOUNDS, "mk_pool_finish: more tokens than the sequence's pages hold");
+  // freeze the pages holding tokens 0 .. n_tokens-1 along the token path; a
+  // run that the tree already holds keeps its node (this page is then freed).
+  // Below the first run the tree lacks, every page becomes a new node, and
+  // none of those may already be a checkpoint's (tokens that disagree with
+  // a shared page's).
+  auto run_at = [&](int32_t j) {
+    const int32_t n = std::min(p->pt, n_tokens - j * p->pt);
+    return std::vector<int32_t>(tokens + (size_t)j * p->pt, tokens + (size_t)j * p->pt + n);
+  };
+  auto child_with = [&](int32_t node, const std::vector<int32_t>& run) {
+    for (int32_t c : p->nodes[node].children)
+      if (p->nodes[c].tokens == run) return c;
+    return -1;
+  };
+  {
+    int32_t node = 0;
+    for (int32_t j = 0; j * p->pt < n_tokens; ++j) {
+      const int32_t hit = node >= 0 ? child_with(node, run_at(j)) : -1;
+      if (hit < 0 && p->node_of[list[j]] >= 0)
+        return fail(MK_EINVAL, "mk_pool_finish: the tokens of page " + std::to_string(j) +
+                                   " disagree with the checkpoint the sequence shares there");
+      node = hit;
+    }
+  }
+  int32_t node = 0;
+  for (int32_t j = 0; j * p->pt < n_tokens; ++j) {
+    const std::vector<int32_t> run = run_at(j);
+    int32_t hit = child_with(node, run);
+    if (hit < 0) {
+      mk_pool::Node nd;
+      nd.page = list[j];
+      nd.tokens = run;
+      nd.parent = node;
+      nd.order = ++p->inserted;
+      p->nodes.push_back(std::move(nd));
+      hit = (int32_t)p->nodes.size() - 1;
+      p->nodes[node].children.push_back(hit);
+      p->node_of[list[j]] = hit;
+      ++p->ref[list[j]];
+      ++p->cached;
+    }
+    p->nodes[hit].tick = ++p->clock;
+    node = hit;
+  }
+  return mk_pool_release(p, seq);
 }
 
 extern "C" mk_status mk_pool_page_table(const mk_pool_t* p, const int64_t* ids, int32_t n,
@@ -165,6 +379,7 @@ extern "C" mk_status mk_pool_page_table(const mk_pool_t* p, const int64_t* ids, 
 }
 
 extern "C" int32_t mk_pool_free_pages(const mk_pool_t* p) { return p ? (int32_t)p->free_list.size() : -1; }
+extern "C" int32_t mk_pool_cached_pages(const mk_pool_t* p) { return p ? p->cached : -1; }
 extern "C" int32_t mk_pool_seq_pages(const mk_pool_t* p, int64_t seq) {
   if (!p) return -1;
   auto it = p->pages.find(seq);

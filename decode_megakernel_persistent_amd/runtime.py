@@ -15,7 +15,7 @@ from . import (
     MK_PLAN_ATTN_QUEUE, MK_PLAN_CHANGED_COUNTERS, MK_PLAN_CHANGED_IMAGE, MK_PLAN_CHANGED_WORKSPACE,
     MkError, MK_OK, mk_decode_step, mk_decode_step_static, mk_io, mk_kv, mk_kv_pool_elems, mk_plan,
     mk_plan_buffer, mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks,
-    mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers,
+    mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_stream_copy,
     mk_step_status, mk_weights, model_desc,
 )
 
@@ -41,6 +41,15 @@ def alloc_kv_pool(model, n_pages, device, zero=True):
     n = mk_kv_pool_elems(desc, n_pages)
     mk = torch.zeros if zero else torch.empty
     return mk(n, dtype=torch.bfloat16, device=device)
+
+
+def copy_kv_page(model, pool, src, dst):
+    """Copy KV page src to page dst of a device pool (every layer of the page;
+    a page is contiguous in the pool layout), in stream order: the private
+    copy of the page a shared prefix ends inside."""
+    n = mk_kv_pool_elems(model_desc(model), 1) * pool.element_size()
+    base = pool.data_ptr()
+    mk_stream_copy(base + dst * n, base + src * n, n, torch.cuda.current_stream(pool.device).cuda_stream)
 
 
 class Decoder:

@@ -33,7 +33,7 @@ def lib():
         L.fx_gpu_fill_const_bf16.restype = ctypes.c_int
         L.fx_gpu_fill_const_bf16.argtypes = [vp, u64, ctypes.c_uint16, vp]
         L.fx_gpu_fill_kv.restype = ctypes.c_int
-        L.fx_gpu_fill_kv.argtypes = [vp, vp, u64, u32, u32, u32, u32, u32, u32, u32, vp]
+        L.fx_gpu_fill_kv.argtypes = [vp, vp, u64, u32, u32, u32, u32, u32, u32, u32, u32, vp]
         _LIB = L
     return _LIB
 
@@ -97,11 +97,12 @@ def weights(m, seed=0, device="cuda"):
     return W
 
 
-def fill_kv(pool, page_row_dev, m, seed, b, ctx):
-    """Prior KV of sequence b (tokens 0 .. ctx-1) into its pages of the device pool.
+def fill_kv(pool, page_row_dev, m, seed, b, ctx, start=0):
+    """Prior KV of sequence b (tokens start .. ctx-1) into its pages of the device pool.
 
     page_row_dev: int32 device tensor, the sequence's row of the page table.
-    Values equal fixtures.HostKV(m, seed).k / .v element for element.
+    Values equal fixtures.HostKV(m, seed).k / .v element for element; slots
+    of tokens below start (e.g. pages shared with a checkpoint) are not written.
     """
     assert pool.dtype == torch.bfloat16 and page_row_dev.dtype == torch.int32
     n_pg = page_row_dev.numel()
@@ -109,10 +110,10 @@ def fill_kv(pool, page_row_dev, m, seed, b, ctx):
     need = (ctx + pt - 1) // pt
     if need > n_pg:
         raise ValueError("fill_kv: page row shorter than the context")
-    rows = page_row_dev[:need].cpu()
+    rows = page_row_dev[start // pt:need].cpu()
     n_pages = pool.numel() // (m["n_layers"] * m["n_kv_heads"] * 2 * pt * m["head_dim"])
-    if need and (int(rows.min()) < 0 or int(rows.max()) >= n_pages):
+    if rows.numel() and (int(rows.min()) < 0 or int(rows.max()) >= n_pages):
         raise ValueError("fill_kv: page id outside the pool")
-    _ok(lib().fx_gpu_fill_kv(pool.data_ptr(), page_row_dev.data_ptr(), seed, b, ctx, n_pg,
+    _ok(lib().fx_gpu_fill_kv(pool.data_ptr(), page_row_dev.data_ptr(), seed, b, start, ctx, n_pg,
                              m["n_layers"], m["n_kv_heads"], m["head_dim"], pt, _stream()),
         "fx_gpu_fill_kv")

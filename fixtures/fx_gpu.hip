@@ -63,9 +63,9 @@ __global__ void k_fill_const(uint16_t* dst, uint64_t n, uint16_t bits) {
 // p*page_stride + l*layer_stride + g*2*PT*d holds K as [slot][dim] followed
 // by V as [dim][slot]. Token t sits in page page_table[t / PT], slot t % PT.
 // Element (t, i) of K (V) of (l, g) is normal(key(seed, tag(KCACHE (VCACHE),
-// l, b, g)), t*d + i, 1). Slots at t >= ctx are left untouched.
+// l, b, g)), t*d + i, 1). Slots at t < t0 or t >= ctx are left untouched.
 __global__ void k_fill_kv(uint16_t* pool, const int32_t* page_row, uint64_t seed, uint32_t b,
-                          uint32_t ctx, uint32_t n_pg, uint32_t L, uint32_t Hkv, uint32_t d,
+                          uint32_t t0, uint32_t ctx, uint32_t n_pg, uint32_t L, uint32_t Hkv, uint32_t d,
                           uint32_t PT, uint64_t total, float c) {
   const uint64_t blk = 2ull * PT * d;
   const uint64_t layer_stride = (uint64_t)Hkv * blk;
@@ -93,7 +93,7 @@ __global__ void k_fill_kv(uint16_t* pool, const int32_t* page_row, uint64_t seed
       i = (q / 4) * 32 + (e8 / 4) * 16 + r;
     }
     uint32_t t = pg * PT + s;
-    if (t >= ctx || pg >= n_pg) continue;
+    if (t < t0 || t >= ctx || pg >= n_pg) continue;
     uint64_t kind = kv ? (uint64_t)FX_VCACHE : (uint64_t)FX_KCACHE;
     uint64_t tag = (kind << 56) | ((uint64_t)l << 40) | ((uint64_t)b << 20) | g;
     uint64_t phys = (uint64_t)page_row[pg];
@@ -139,14 +139,14 @@ int fx_gpu_fill_const_bf16(void* dst, uint64_t n, uint16_t bits, void* stream) {
 
 // page_row: device pointer to this sequence's row of the page table (n_pg entries).
 int fx_gpu_fill_kv(void* pool, const int32_t* page_row, uint64_t seed, uint32_t b,
-                   uint32_t ctx, uint32_t n_pg, uint32_t L, uint32_t Hkv, uint32_t d,
+                   uint32_t t0, uint32_t ctx, uint32_t n_pg, uint32_t L, uint32_t Hkv, uint32_t d,
                    uint32_t PT, void* stream) {
   uint64_t need = ((uint64_t)ctx + PT - 1) / PT;
   if (need > n_pg) return -1;
   uint64_t total = need * L * Hkv * 2ull * PT * d;
   if (total == 0) return 0;
   hipLaunchKernelGGL(k_fill_kv, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)stream,
-                     (uint16_t*)pool, page_row, seed, b, ctx, (uint32_t)need, L, Hkv, d, PT,
+                     (uint16_t*)pool, page_row, seed, b, t0, ctx, (uint32_t)need, L, Hkv, d, PT,
                      total, 1.0f * 7.62939453125e-06f);
   return (int)hipGetLastError();
 }

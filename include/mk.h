@@ -332,22 +332,54 @@ mk_status mk_decode_step_static(const mk_plan_t* p, const mk_weights* w, const m
  * or pool). Sets mk_last_error. */
 mk_status mk_step_status(const uint32_t* h_status);
 
-/* ---- page/slot pool (pure host; kern page, "The runtime") ----
+/* ---- page/slot pool with prefix sharing (pure host; kern page, "The runtime") ----
  * n_pages pages of page_tokens tokens, n_slots sequence slots. The free list
  * starts in initial_order (a permutation of [0, n_pages); NULL = ascending).
  * A lease takes ceil(tokens/page_tokens) pages from the front of the free list
- * and the lowest free slot, all or nothing; a release appends the sequence's
- * pages, in its page order, to the back. */
+ * and the lowest free slot, all or nothing (MK_ENOMEM: nothing changed); a
+ * release returns every page no one else holds to the back of the free list,
+ * in the sequence's page order.
+ * Prefix sharing: mk_pool_finish freezes a finished sequence's pages in place
+ * as a checkpoint, keyed by the tokens whose K/V they hold, in a token radix
+ * tree with one page per node (a run the tree already holds keeps its node;
+ * the duplicate page is freed). mk_pool_lease_prefix finds the longest
+ * checkpointed prefix of a prompt, at most n_prompt - 1 tokens (the last
+ * prompt token always runs, giving the next token's logits): the sequence's
+ * list starts with the checkpoint's whole pages inside the match, shared and
+ * never written by anyone; if the match ends inside a page, the first fresh
+ * page is that page's private copy -- the caller copies page *copy_src to
+ * page *copy_dst in the device pool (whole pages are contiguous, see the KV
+ * layout) before the sequence's next step writes it -- so every page has at
+ * most one writer. Positions >= *matched must then be filled (prefilled or
+ * decoded) by the caller. At each page the longest common run wins, ties to
+ * the earlier checkpoint. Under pressure (a lease or extension that the free
+ * list cannot serve) checkpoint pages that no sequence holds are evicted,
+ * least recently used leaf first (ties: earlier inserted), all or nothing; an
+ * evicted checkpoint is dropped (it is not parked in host memory). */
 mk_status mk_pool_create(int32_t n_pages, int32_t page_tokens, int32_t n_slots,
                          const int32_t* initial_order, mk_pool_t** out);
 mk_status mk_pool_lease(mk_pool_t* p, int64_t seq_id, int32_t worst_case_tokens,
                         int32_t* slot_out);
+/* prompt: host [n_prompt] token ids; worst_case_tokens >= n_prompt (else
+ * MK_EINVAL). Outputs (each may be NULL): slot, tokens reused (*matched),
+ * and the page copy to make (-1, -1: none). */
+mk_status mk_pool_lease_prefix(mk_pool_t* p, int64_t seq_id, const int32_t* prompt, int32_t n_prompt,
+                               int32_t worst_case_tokens, int32_t* slot_out, int32_t* matched,
+                               int32_t* copy_src, int32_t* copy_dst);
 mk_status mk_pool_extend(mk_pool_t* p, int64_t seq_id, int32_t worst_case_tokens);
 mk_status mk_pool_release(mk_pool_t* p, int64_t seq_id);
+/* Freeze the pages holding the first n_tokens tokens of seq_id (tokens: host
+ * [n_tokens], the ids whose K/V those pages hold, from position 0) as a
+ * checkpoint, then release the sequence. MK_EBOUNDS if its pages hold fewer
+ * tokens; MK_EINVAL if the tokens disagree with a checkpoint page the
+ * sequence shares (nothing changed then). */
+mk_status mk_pool_finish(mk_pool_t* p, int64_t seq_id, const int32_t* tokens, int32_t n_tokens);
 /* out[i][j] = page j of seq_ids[i], -1 past its pages (host [n][max_pages]). */
 mk_status mk_pool_page_table(const mk_pool_t* p, const int64_t* seq_ids, int32_t n,
                              int32_t max_pages, int32_t* out);
 int32_t mk_pool_free_pages(const mk_pool_t* p);
+/* Pages held by checkpoints. */
+int32_t mk_pool_cached_pages(const mk_pool_t* p);
 int32_t mk_pool_seq_pages(const mk_pool_t* p, int64_t seq_id);
 void mk_pool_free(mk_pool_t* p);
 

@@ -41,6 +41,7 @@ are taken in the working precision.
 Library primitives used as steps: matrix-vector products (torch.mv), the
 stable sort (torch.sort(stable=True)) and torch.argmax (first maximum).
 """
+import copy
 import math
 from collections import deque
 
@@ -386,14 +387,30 @@ def speed_of_light(bytes_per_step, bandwidth):
 # ---------------------------------------------------------------- pool model
 
 class PoolModel:
-    """Plain model of the page/slot pool.
+    """Plain model of the page/slot pool with prefix sharing.
 
-    The free list is a deque holding the initial page order; a lease of a
-    sequence's worst case takes ceil(tokens / page_tokens) pages from the
-    front, all or nothing (kern page, "The runtime": a request leases the
-    pages its worst case needs and a state slot, all or nothing); a release
-    appends the sequence's pages, in its page order, to the back. Slots are
-    the lowest free index.
+    Pages, slots and leases (kern page, "The runtime": a request leases the
+    pages its worst case needs and a state slot, all or nothing): the free
+    list is a deque holding the initial page order; a lease takes
+    ceil(tokens / page_tokens) pages from the front; slots are the lowest
+    free index. Every page records who holds it (sequences, checkpoint
+    nodes); it returns to the back of the free list when no one does, a
+    finished or released sequence's pages in its page order.
+
+    Prefix sharing (same passage: when a request ends its pages freeze in
+    place as a checkpoint; a later request with the same prefix shares the
+    whole pages and gets a copy of only the page the prefix ends inside, so
+    that every page has at most one writer; a token radix tree finds the
+    longest checkpoint for a prompt). Readings: one checkpoint node per page,
+    holding the tokens whose K/V the page holds (a tail page holds fewer);
+    a run the tree already holds at that place is not frozen twice; the
+    reusable prefix of a prompt of n tokens is at most n - 1 tokens (the
+    last one runs to give the next token's logits); of equally long matches
+    ending inside a page, the earlier checkpoint's page is copied. Under
+    pressure (the passage parks checkpoints in host memory; here they are
+    dropped) the least recently used checkpoint leaf that no sequence holds
+    goes first, ties to the earlier checkpoint; "use" is a lease sharing or
+    copying it, or a finish freezing or meeting it, each in path order.
     """
 
     def __init__(self, order, page_tokens, n_slots):
@@ -402,26 +419,160 @@ class PoolModel:
         self.slots_free = list(range(n_slots))
         self.pages = {}
         self.slot = {}
+        self.holders = {int(p): set() for p in order}
+        self.nodes = {}          # id -> dict(page, run, parent, made, used)
+        self.clock = 0
+        self.made = 0
 
-    def lease(self, seq, tokens):
-        need = -(-tokens // self.pt)
-        if seq in self.pages or need > len(self.free) or not self.slots_free:
+    # -- checkpoints
+    def _children(self, parent):
+        return sorted((i for i, n in self.nodes.items() if n["parent"] == parent),
+                      key=lambda i: self.nodes[i]["made"])
+
+    def _chain(self, i):
+        """Node ids from the root's child down to node i."""
+        out = []
+        while i is not None:
+            out.append(i)
+            i = self.nodes[i]["parent"]
+        return out[::-1]
+
+    def _tokens(self, i):
+        return [t for j in self._chain(i) for t in self.nodes[j]["run"]]
+
+    def _use(self, i):
+        self.clock += 1
+        self.nodes[i]["used"] = self.clock
+
+    def lookup(self, prompt):
+        """(tokens reused, node ids shared whole, node copied or None), by
+        brute force over every checkpoint's token path."""
+        limit = len(prompt) - 1
+        if limit <= 0:
+            return 0, [], None
+        best_m, best = 0, None
+        for i in sorted(self.nodes, key=lambda i: self.nodes[i]["made"]):
+            path = self._tokens(i)
+            c = 0
+            while c < min(limit, len(path)) and path[c] == prompt[c]:
+                c += 1
+            start = len(path) - len(self.nodes[i]["run"])
+            if c <= start:
+                continue                      # the match ends in an ancestor
+            if c > best_m:
+                best_m, best = c, i
+        if best is None:
+            return 0, [], None
+        chain = self._chain(best)
+        if best_m % self.pt == 0:
+            return best_m, chain, None        # the match fills node best's page
+        return best_m, chain[:-1], best
+
+    def _evict_one(self):
+        leaves = [i for i in self.nodes if not self._children(i)
+                  and self.holders[self.nodes[i]["page"]] == {("node", i)}]
+        if not leaves:
             return False
-        self.pages[seq] = [self.free.popleft() for _ in range(need)]
+        i = min(leaves, key=lambda i: (self.nodes[i]["used"], self.nodes[i]["made"]))
+        pg = self.nodes.pop(i)["page"]
+        self.holders[pg].clear()
+        self.free.append(pg)
+        return True
+
+    def _make_free(self, n):
+        """Evict until n pages are free; all or nothing."""
+        trial = copy.deepcopy(self)
+        while len(trial.free) < n:
+            if not trial._evict_one():
+                return False
+        self.__dict__.update(trial.__dict__)
+        return True
+
+    # -- leases
+    def lease(self, seq, tokens, prompt=None):
+        """(slot, tokens reused, copy source page, copy destination page), or
+        None when refused (nothing changes then)."""
+        if seq in self.pages or not self.slots_free:
+            return None
+        m, shared, inside = self.lookup(list(prompt)) if prompt is not None else (0, [], None)
+        need = -(-tokens // self.pt) - len(shared)
+        pinned = [self.nodes[i]["page"] for i in shared + ([inside] if inside is not None else [])]
+        for pg in pinned:
+            self.holders[pg].add(("pin", seq))
+        ok = self._make_free(need)
+        for pg in pinned:
+            self.holders[pg].discard(("pin", seq))
+        if not ok:
+            return None
+        fresh = [self.free.popleft() for _ in range(need)]
+        pages = [self.nodes[i]["page"] for i in shared] + fresh
+        for pg in pages:
+            self.holders[pg].add(("seq", seq))
+        for i in shared:
+            self._use(i)
+        if inside is not None:
+            self._use(inside)
+        self.pages[seq] = pages
         self.slots_free.sort()
         self.slot[seq] = self.slots_free.pop(0)
-        return True
+        if inside is None:
+            return self.slot[seq], m, -1, -1
+        return self.slot[seq], m, self.nodes[inside]["page"], fresh[0]
 
     def extend(self, seq, tokens):
         need = -(-tokens // self.pt) - len(self.pages[seq])
-        if need > len(self.free):
+        if need <= 0:
+            return True
+        if not self._make_free(need):
             return False
-        self.pages[seq] += [self.free.popleft() for _ in range(max(0, need))]
+        fresh = [self.free.popleft() for _ in range(need)]
+        for pg in fresh:
+            self.holders[pg].add(("seq", seq))
+        self.pages[seq] += fresh
         return True
 
     def release(self, seq):
-        self.free.extend(self.pages.pop(seq))
+        for pg in self.pages.pop(seq):
+            self.holders[pg].discard(("seq", seq))
+            if not self.holders[pg]:
+                self.free.append(pg)
         self.slots_free.append(self.slot.pop(seq))
+
+    def finish(self, seq, tokens):
+        """Freeze seq's pages under its tokens, then release it. Returns
+        "ok", "bounds" (more tokens than its pages hold) or "disagree" (a
+        page it shares holds other tokens); nothing changes unless "ok"."""
+        pages = self.pages[seq]
+        runs = [list(tokens[j:j + self.pt]) for j in range(0, len(tokens), self.pt)]
+        if len(runs) > len(pages):
+            return "bounds"
+        frozen = {n["page"] for n in self.nodes.values()}
+        parent, on_tree, plan = None, True, []
+        for j, run in enumerate(runs):
+            hit = None
+            if on_tree:
+                hit = next((i for i in self._children(parent) if self.nodes[i]["run"] == run), None)
+            if hit is None:
+                on_tree = False               # below a new node there is nothing to meet
+                if pages[j] in frozen:
+                    return "disagree"
+            plan.append(hit)
+            parent = hit
+        parent = None
+        for j, run in enumerate(runs):
+            hit = plan[j]
+            if hit is None:
+                self.made += 1
+                hit = ("n", self.made)
+                self.nodes[hit] = dict(page=pages[j], run=run, parent=parent, made=self.made, used=0)
+                self.holders[pages[j]].add(("node", hit))
+            self._use(hit)
+            parent = hit
+        self.release(seq)
+        return "ok"
+
+    def cached(self):
+        return len(self.nodes)
 
     def page_table(self, seqs, max_pages):
         t = [[-1] * max_pages for _ in seqs]

@@ -497,9 +497,11 @@ def test_tagged_pair_reads_stay_8_byte_loads(tmp_path):
     tools = [shutil.which("objcopy"), os.path.join(llvm, "clang-offload-bundler"), os.path.join(llvm, "llvm-objdump")]
     if not all(t and os.path.exists(t) for t in tools):
         pytest.skip("objcopy / clang-offload-bundler / llvm-objdump not available")
-    lib = os.path.join(ROOT, "decode_megakernel_persistent_amd", "libmk.so")
+    # objcopy rewrites the file it reads: work on a copy, never the loaded library
+    lib = tmp_path / "libmk.so"
+    shutil.copy(os.path.join(ROOT, "decode_megakernel_persistent_amd", "libmk.so"), lib)
     fb, co = tmp_path / "fatbin", tmp_path / "gfx950.co"
-    subprocess.run([tools[0], "--dump-section", f".hip_fatbin={fb}", lib], check=True)
+    subprocess.run([tools[0], "--dump-section", f".hip_fatbin={fb}", str(lib)], check=True)
     subprocess.run([tools[1], "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fb}",
                     f"--output={co}", "--unbundle"], check=True)
     dis = subprocess.run([tools[2], "-d", str(co)], check=True, capture_output=True, text=True).stdout
