@@ -19,7 +19,7 @@ MK_OK, MK_EINVAL, MK_ENOMEM, MK_EBOUNDS, MK_EDEVICE, MK_ETIMEOUT, MK_ESTATE, MK_
 STATUS_NAMES = {0: "MK_OK", -1: "MK_EINVAL", -2: "MK_ENOMEM", -3: "MK_EBOUNDS", -4: "MK_EDEVICE",
                 -5: "MK_ETIMEOUT", -6: "MK_ESTATE", -7: "MK_EUNSUPPORTED"}
 (MK_BUF_XATTN, MK_BUF_XFFN, MK_BUF_Q, MK_BUF_PART, MK_BUF_O, MK_BUF_RLOG, MK_BUF_ACT,
- MK_BUF_LMPART, MK_BUF_KVN, MK_BUF_ROUTE, MK_BUF_Y, MK_BUF_OPART, MK_BUF_QPART) = range(13)
+ MK_BUF_LMPART, MK_BUF_KVN, MK_BUF_ROUTE, MK_BUF_Y, MK_BUF_OPART, MK_BUF_QPART, MK_BUF_LOGIT) = range(14)
 
 _i32, _i64, _u32, _u64, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                          ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t,
@@ -58,9 +58,16 @@ class mk_kv(ctypes.Structure):
                 ("rope_cos", _vp), ("rope_sin", _vp), ("n_rope_pos", _i32)]
 
 
+class mk_sampling(ctypes.Structure):
+    _fields_ = [("temperature", _vp), ("top_k", _vp), ("top_p", _vp), ("min_p", _vp), ("uniform", _vp)]
+
+
 class mk_io(ctypes.Structure):
     _fields_ = [("tokens_in", _vp), ("tokens_out", _vp), ("topk_ids", _vp), ("topk_w", _vp),
-                ("logits", _vp)]
+                ("logits", _vp), ("sampling", ctypes.POINTER(mk_sampling))]
+
+
+MK_SAMPLE_TOP_K_MAX = 64
 
 
 class mk_step_buffers(ctypes.Structure):

@@ -76,6 +76,7 @@ struct Smem {
   int kv_ok[NWAVE];          // wave w's staged page is valid
   int kv_ids[ATT_IDS + 1];   // its first ATT_IDS page ids, then the sequence's position
   uint32_t qnext;      // attention queue: the split this workgroup takes next
+  int tok;             // sampling: the drawn token
   uint64_t tw[4];      // trace: (begin, end) of the routing wait and of the data wait
   uint64_t mk[TRACE_MARKS];  // trace: body-specific marks
 };
@@ -1396,6 +1397,7 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
   for (int j = tid(); j < n; j += NT) {
     const float y = s.out[j];
     if (a.logits) a.logits[r0 + j] = y;
+    if (a.smp_u) st_tagged(a.lw + r0 + j, y, a.epoch);
     argmax_merge(y, r0 + j, bv, bi);
   }
 #pragma unroll
@@ -1414,6 +1416,161 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
     st_tagged(a.lmpart + (size_t)t.a3 * 2, bv, a.epoch);
     st_tagged(a.lmpart + (size_t)t.a3 * 2 + 1, __int_as_float(bi), a.epoch);
   }
+  return true;
+}
+
+// ------------------------------------------------------------------ sampling
+//
+// Sampling beyond greedy (the Kinetic book's sampler flags, in llama.cpp's
+// default order restricted to top-k, top-p, min-p and temperature, with the
+// caller's uniform draw u): the top_k largest logits are found exactly, then
+// filtered and drawn from in one wave.
+
+// Order-preserving 64-bit key of logit v of token id: a larger logit ranks
+// first, equal logits the lower id; key 0 ranks below every logit.
+__device__ __forceinline__ uint64_t tok_key(float v, uint32_t id) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
+
+// Sort the n keys at k (LDS; n a power of two >= 2, written before a
+// barrier) into descending order: a bitonic network, every thread taking
+// part, a barrier after each stage.
+__device__ void lds_sort_desc(uint64_t* k, int n) {
+  for (int size = 2; size <= n; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid(); i < n / 2; i += NT) {
+        const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x = k[lo], y = k[hi];
+        if ((x < y) == desc) {
+          k[lo] = y;
+          k[hi] = x;
+        }
+      }
+      lds_barrier();
+    }
+}
+
+__device__ __forceinline__ float wave_scan_incl(float x) {
+  const int lane = tid() & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Candidates per sequence: top_k outside 1 .. MK_SAMPLE_TOP_K_MAX is served
+// as that maximum; 1 is greedy.
+__device__ __forceinline__ int sample_k(KAC& a, int b) {
+  int k = a.smp_k[b];
+  if (k <= 0 || k > MK_SAMPLE_TOP_K_MAX) k = MK_SAMPLE_TOP_K_MAX;
+  return k < a.V ? k : a.V;
+}
+__device__ __forceinline__ bool sampling(KAC& a, int b) {
+  return a.smp_u && a.smp_t[b] > 0.f && sample_k(a, b) > 1;
+}
+
+// Sequence b's sampled token into *tok (LDS). The n LM-head tiles hold
+// `rows` rows each (the last maybe fewer); tile i's largest logit is value
+// tv(i) at row ti(i); the logits themselves are the tagged words a.lw + b*V.
+// The K largest tile maxima bound the K largest logits from below, so only
+// those K tiles are scanned; logits at or above the running threshold are
+// collected, and when the buffer fills its K largest are kept and the
+// threshold raised to the K-th. Returns false (uniformly) on deadline or
+// another workgroup's failure.
+template <class TV, class TI>
+__device__ bool sample_seq(Ctx& c, int b, int n, int rows, const TV& tv, const TI& ti, int* tok) {
+  KAC& a = c.a;
+  Smem& s = c.s;
+  constexpr int CAP = 4096, ROUND = NT * 4;
+  uint64_t* keys = (uint64_t*)s.stage;  // tile maxima, then candidates (CAP keys each)
+  uint64_t* cand = keys + CAP;
+  int* tiles = (int*)s.res;
+  int* cnt = (int*)s.out;
+  const int K = sample_k(a, b);
+  int n2 = 2;
+  while (n2 < n) n2 <<= 1;
+  for (int i = tid(); i < n2; i += NT) keys[i] = i < n ? tok_key(tv(i), (uint32_t)ti(i)) : 0ull;
+  lds_barrier();
+  lds_sort_desc(keys, n2);
+  const int nt = n < K ? n : K;
+  uint64_t thr = n <= K ? 0ull : keys[K - 1];
+  if (tid() < nt) tiles[tid()] = (int)(key_id(keys[tid()]) / (uint32_t)rows);
+  if (tid() == 0) *cnt = 0;
+  lds_barrier();
+  const uint64_t* lw = a.lw + (size_t)b * a.V;
+  for (int j = 0; j < nt; ++j) {
+    const int r0 = tiles[j] * rows, nr = min(rows, a.V - r0);
+    for (int base = 0; base < nr; base += ROUND) {
+      float v[4];
+      const bool ok = read_words<4>(a, [&](int k) -> const uint64_t* {
+        const int r = base + tid() + k * NT;
+        return r < nr ? lw + r0 + r : nullptr;
+      }, v, c.t0, c.ti);
+      if (!ok) s.fail = 1;
+      if (ok)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int r = base + tid() + k * NT;
+          const uint64_t key = tok_key(v[k], (uint32_t)(r0 + r));
+          if (r < nr && key >= thr) cand[atomicAdd(cnt, 1)] = key;
+        }
+      lds_barrier();
+      if (s.fail) return false;
+      const int m = *cnt;
+      if (m > CAP - ROUND) {  // keep the K largest, raise the threshold
+        int m2 = 2;
+        while (m2 < m) m2 <<= 1;
+        for (int i = m + tid(); i < m2; i += NT) cand[i] = 0ull;
+        lds_barrier();
+        lds_sort_desc(cand, m2);
+        thr = cand[K - 1];
+        if (tid() == 0) *cnt = K;
+        lds_barrier();
+      }
+    }
+  }
+  {
+    const int m = *cnt;  // >= K: the K tile maxima themselves were collected
+    int m2 = 2;
+    while (m2 < m) m2 <<= 1;
+    for (int i = m + tid(); i < m2; i += NT) cand[i] = 0ull;
+    lds_barrier();
+    lds_sort_desc(cand, m2);
+  }
+  if (tid() < 64) {
+    const int lane = tid();
+    const bool in = lane < K;
+    const uint64_t key = in ? cand[lane] : 0ull;
+    const float z = in ? key_value(key) : 0.f;
+    const float z0 = key_value(cand[0]);
+    const float T = a.smp_t[b], P = a.smp_p[b], MP = a.smp_minp[b], u = a.smp_u[b];
+    // top-p: softmax over the candidates at temperature 1, most likely first
+    const float e = in ? expf(z - z0) : 0.f;
+    const float p = e / wave_sum(e);
+    const float before = wave_scan_incl(p) - p;
+    bool keep = in && (lane == 0 || P >= 1.f || before < P);
+    // min-p: at least min_p times as likely as the best (the best always stays)
+    if (MP > 0.f) keep = keep && (lane == 0 || z >= z0 + logf(MP));
+    // temperature, then the draw
+    const float w = keep ? expf((z - z0) / T) : 0.f;
+    const float cw = wave_scan_incl(w);
+    const float W = __shfl(cw, 63, 64);
+    const uint64_t hit = __ballot(keep && cw > u * W);
+    const uint64_t kept = __ballot(keep);
+    const int pick = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(kept);
+    if (lane == pick) *tok = (int)key_id(key);
+  }
+  lds_barrier();
   return true;
 }
 
@@ -1439,6 +1596,17 @@ __device__ __forceinline__ bool task_final(Ctx& c, const Task& t) {
   int* ri = (int*)(s.red + NWAVE);
   if ((tid() & 63) == 0) { rv[tid() >> 6] = bv; ri[tid() >> 6] = bi; }
   lds_barrier();
+  if (sampling(a, 0)) {
+    int* tok = &s.tok;
+    if (!sample_seq(c, 0, n, t.a2, [&](int i) { return s.vec[2 * i]; },
+                    [&](int i) { return __float_as_int(s.vec[2 * i + 1]); }, tok))
+      return false;
+    if (tid() == 0) {
+      a.tok_out[0] = *tok;
+      a.seq_lens[0] = a.seq_lens[0] + 1;
+    }
+    return true;
+  }
   if (tid() == 0) {
     for (int q = 1; q < NWAVE; ++q)
       argmax_merge(rv[q], ri[q], bv, bi);
@@ -2088,6 +2256,7 @@ __device__ __forceinline__ bool task_blm(Ctx& c, const Task& t) {
     for (int r = sub; r < n; r += 16) {
       const float y = P.out[r][b];
       if (a.logits) a.logits[(size_t)b * a.V + r0 + r] = y;
+      if (a.smp_u) st_tagged(a.lw + (size_t)b * a.V + r0 + r, y, a.epoch);
       argmax_merge(y, r0 + r, bv, bi);
     }
 #pragma unroll
@@ -2125,6 +2294,17 @@ __device__ __forceinline__ bool task_bfinal(Ctx& c, const Task& t) {
   int* ri = (int*)(s.red + NWAVE);
   if ((tid() & 63) == 0) { rv[tid() >> 6] = bv; ri[tid() >> 6] = bi; }
   lds_barrier();
+  if (sampling(a, b)) {
+    int* tok = &s.tok;
+    if (!sample_seq(c, b, n, t.a2, [&](int i) { return s.vec[2 * i]; },
+                    [&](int i) { return __float_as_int(s.vec[2 * i + 1]); }, tok))
+      return false;
+    if (tid() == 0) {
+      a.tok_out[b] = *tok;
+      a.seq_lens[b] = a.seq_lens[b] + 1;
+    }
+    return true;
+  }
   if (tid() == 0) {
     for (int q = 1; q < NWAVE; ++q) argmax_merge(rv[q], ri[q], bv, bi);
     a.tok_out[b] = bi;
@@ -2510,6 +2690,14 @@ static mk_status launch_step(const mk_plan_t* p, const mk_weights* w, const mk_k
   a.lmpart = buf(MK_BUF_LMPART); a.route = buf(MK_BUF_ROUTE); a.y = buf(MK_BUF_Y);
   a.opart = buf(MK_BUF_OPART); a.s_opart = words(MK_BUF_OPART);
   a.qpart = buf(MK_BUF_QPART); a.s_qpart = words(MK_BUF_QPART);
+  a.lw = buf(MK_BUF_LOGIT);
+  if (io->sampling) {
+    const mk_sampling* sm = io->sampling;
+    if (!sm->temperature || !sm->top_k || !sm->top_p || !sm->min_p || !sm->uniform)
+      return fail(MK_EINVAL, "mk_decode_step: a sampling array is NULL");
+    a.smp_t = sm->temperature; a.smp_k = sm->top_k; a.smp_p = sm->top_p; a.smp_minp = sm->min_p;
+    a.smp_u = sm->uniform;
+  }
   a.s_x = words(MK_BUF_XFFN); a.s_q = words(MK_BUF_Q); a.s_kvn = words(MK_BUF_KVN);
   a.s_part = words(MK_BUF_PART); a.s_o = words(MK_BUF_O); a.s_rlog = words(MK_BUF_RLOG);
   a.s_act = words(MK_BUF_ACT); a.s_route = words(MK_BUF_ROUTE); a.s_y = words(MK_BUF_Y);

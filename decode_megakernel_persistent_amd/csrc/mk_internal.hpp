@@ -32,7 +32,7 @@ enum Op : uint8_t {
                   // (may be 0), over every slot of sequence 0
                   // (7 is unused)
   OP_LM = 8,      // a1 = first row, a2 = rows, a3 = index of this LM tile
-  OP_FINAL = 9,   // a0 = LM tiles
+  OP_FINAL = 9,   // a0 = LM tiles, a2 = rows per tile
   // batch (B > 1) tasks: the dense projections cover all sequences at once
   // as MFMA tiles of 16-row blocks
   OP_BQKV = 10,   // a0 = kv group g, a1 = first rotary pair, a2 = pairs
@@ -43,7 +43,7 @@ enum Op : uint8_t {
                   // a3 = first hidden row << 16 | hidden rows (down part)
   OP_BCOMB = 15,  // a0 = b, a1 = first row, a2 = rows: weighted expert sum + residual
   OP_BLM = 16,    // a1 = first row, a2 = rows, a3 = index of this LM tile
-  OP_BFINAL = 17, // a0 = LM tiles, a1 = b
+  OP_BFINAL = 17, // a0 = LM tiles, a1 = b, a2 = rows per tile
   OP_COUNT = 18
 };
 
@@ -239,6 +239,10 @@ struct KArgs {
   //  batch only: route [L][B][K][2] (expert id bits, weight) per selected slot,
   //  y [L][B][K][H] expert outputs
   uint64_t *x, *xa, *q, *kvn, *part, *o, *rlog, *act, *lmpart, *route, *y, *opart, *qpart;
+  uint64_t* lw;  // logit words [B][V] (written by sampling steps only)
+  // sampling (device [B] arrays; smp_u == NULL: greedy for every sequence)
+  const float *smp_t, *smp_p, *smp_minp, *smp_u;
+  const int32_t* smp_k;
   const uint64_t* ws;  // the workspace holding all of them (256-byte aligned)
   uint32_t ws_bytes;   // its size (under 4 GiB)
   int64_t s_x, s_q, s_kvn, s_part, s_o, s_rlog, s_act, s_route, s_y, s_opart, s_qpart;

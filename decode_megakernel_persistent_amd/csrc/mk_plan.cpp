@@ -296,6 +296,7 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
       Task f = mk_task(mk::OP_BFINAL, 0);
       f.wait_b = ctr16(p->c_lm);
       f.a0 = p->n_lm; f.a1 = b;
+      f.a2 = rows;  // rows per LM-head tile (the last may hold fewer)
       fin.push_back(f);
     }
     stages.push_back(fin);
@@ -699,6 +700,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     Task f = mk_task(mk::OP_FINAL, 0);
     f.wait_b = ctr16(p->c_lm);
     f.a0 = p->n_lm;
+    f.a2 = rows;  // rows per LM-head tile (the last may hold fewer)
     stages.push_back({f});
   }
   p->n_stages = (int)stages.size();
@@ -786,13 +788,14 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         batch && moe ? (size_t)B * K * 2 : 0,             // ROUTE
         batch ? (size_t)B * K * H : 0,                    // Y
         batch ? (size_t)(p->o_kb - 1) * B * H : 0,        // OPART
-        batch ? (size_t)(p->q_kb - 1) * p->q_rb * B * (2 * 8 * QKV_BLOCKS + 2) : 0};  // QPART
+        batch ? (size_t)(p->q_kb - 1) * p->q_rb * B * (2 * 8 * QKV_BLOCKS + 2) : 0,   // QPART
+        0};                                               // LOGIT (not per layer)
     size_t off = 0;
     for (int i = 0; i < mk_plan::N_BUF; ++i) {
       p->ws_off[i] = off;
-      if (i == MK_BUF_LMPART) {
+      if (i == MK_BUF_LMPART || i == MK_BUF_LOGIT) {
         p->ws_stride[i] = 0;
-        p->ws_layer_bytes[i] = (size_t)p->n_lm * B * 2 * 8;
+        p->ws_layer_bytes[i] = i == MK_BUF_LMPART ? (size_t)p->n_lm * B * 2 * 8 : (size_t)B * m->vocab * 8;
         off = align256(off + p->ws_layer_bytes[i]);
       } else {
         p->ws_stride[i] = per_layer[i] * 8;
@@ -1223,7 +1226,7 @@ extern "C" mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t l
                                     size_t* bytes) {
   if (!p || !off || !bytes || which < 0 || which >= mk_plan::N_BUF)
     return fail(MK_EINVAL, "mk_plan_buffer: bad args");
-  const bool per_layer = which != MK_BUF_LMPART;
+  const bool per_layer = which != MK_BUF_LMPART && which != MK_BUF_LOGIT;
   if (per_layer && (layer < 0 || layer >= p->m.n_layers)) return fail(MK_EINVAL, "mk_plan_buffer: bad layer");
   *off = p->ws_off[which] + (per_layer ? (size_t)layer * p->ws_stride[which] : 0);
   *bytes = p->ws_layer_bytes[which];

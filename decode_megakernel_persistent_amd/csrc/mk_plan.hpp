@@ -41,7 +41,7 @@ struct mk_plan {
   int32_t n_lm = 0, n_stages = 0;
 
   // workspace layout: base offset (bytes) and per-layer stride (bytes) per MK_BUF_*
-  static constexpr int N_BUF = 13;
+  static constexpr int N_BUF = 14;
   size_t ws_off[N_BUF] = {}, ws_stride[N_BUF] = {}, ws_layer_bytes[N_BUF] = {};
   int32_t n_exp_parts = 1;          // batch: expert tasks per expert
   size_t ws_total = 0;

@@ -16,7 +16,7 @@ from . import (
     MkError, MK_OK, mk_decode_step, mk_decode_step_static, mk_io, mk_kv, mk_kv_pool_elems, mk_plan,
     mk_plan_buffer, mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks,
     mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_stream_copy,
-    mk_step_status, mk_weights, model_desc,
+    mk_sampling, mk_step_status, mk_weights, model_desc,
 )
 
 TRACE_WORDS = 16    # u64 per task in the optional trace buffer
@@ -159,10 +159,16 @@ class Decoder:
         except Exception:
             pass
 
-    def step(self, tokens_in, tokens_out, topk_ids=None, topk_w=None, logits=None, timeout_ms=0):
-        """Enqueue one decode step on the current stream (asynchronous)."""
+    def step(self, tokens_in, tokens_out, topk_ids=None, topk_w=None, logits=None, timeout_ms=0,
+             sampling=None):
+        """Enqueue one decode step on the current stream (asynchronous).
+        sampling: None (greedy), or a dict of device [batch] tensors
+        temperature (f32), top_k (i32), top_p (f32), min_p (f32), uniform (f32)."""
         self.epoch += 1
         io = mk_io(_ptr(tokens_in), _ptr(tokens_out), _ptr(topk_ids), _ptr(topk_w), _ptr(logits))
+        if sampling is not None:
+            self._smp = mk_sampling(*[_ptr(sampling[k]) for k, _ in mk_sampling._fields_])
+            io.sampling = ctypes.pointer(self._smp)
         mk_decode_step(self.plan, self._w, self._kv, io, self._bufs, self.epoch, timeout_ms,
                        torch.cuda.current_stream(self.device).cuda_stream)
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1
+#define MK_ABI_VERSION 2
 
 typedef enum mk_status {
   MK_OK = 0,
@@ -133,13 +133,44 @@ typedef struct mk_kv {
   int32_t n_rope_pos;        /* positions covered by the tables (>= max_ctx_bound) */
 } mk_kv;
 
+/* Sampling of the next token beyond greedy, per sequence, in the step's last
+ * stage (the Kinetic book, "Pick the sampling" and the sampler flags: the
+ * llama.cpp samplers and their default order -- top-k, top-p, min-p, then
+ * temperature -- and temperature 0 always takes the likeliest token). Every
+ * array is device [batch], read when the step's last stage runs:
+ *   temperature  <= 0: greedy (as with no sampling); else the logits of the
+ *                kept candidates are divided by it before the draw;
+ *   top_k        candidates: the top_k largest logits (ties to the lower
+ *                id); values <= 0 ("all") or above MK_SAMPLE_TOP_K_MAX are
+ *                served as MK_SAMPLE_TOP_K_MAX (the device keeps at most that
+ *                many candidates);
+ *   top_p        keep the shortest run of candidates, most likely first,
+ *                whose probabilities (softmax over the candidates at
+ *                temperature 1) add up to at least top_p; >= 1: off;
+ *   min_p        keep candidates at least min_p times as likely as the best;
+ *                <= 0: off;
+ *   uniform      one draw u in [0, 1) per sequence and step, supplied by the
+ *                caller (so that a seeded run repeats): the token is the
+ *                first kept candidate, most likely first, at which the
+ *                running sum of exp((z - z_max) / temperature) exceeds u
+ *                times its total. */
+#define MK_SAMPLE_TOP_K_MAX 64
+typedef struct mk_sampling {
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  const float* min_p;
+  const float* uniform;
+} mk_sampling;
+
 /* Per-step inputs and outputs. */
 typedef struct mk_io {
   const int32_t* tokens_in;  /* device [batch] */
-  int32_t* tokens_out;       /* device [batch] greedy next tokens; may alias nothing else */
+  int32_t* tokens_out;       /* device [batch] next tokens (greedy, or sampled); may alias nothing else */
   int32_t* topk_ids;         /* device [L][batch][top_k] or NULL */
   float* topk_w;             /* device [L][batch][top_k] or NULL */
   float* logits;             /* device [batch][vocab] or NULL */
+  const mk_sampling* sampling; /* host struct of device arrays, or NULL: greedy for every sequence */
 } mk_io;
 
 /* Caller-owned device buffers of a plan. */
@@ -242,10 +273,11 @@ int32_t mk_plan_n_cu(const mk_plan_t* p);
 mk_status mk_plan_export(const mk_plan_t* p, void* host_buf, size_t bytes);
 mk_status mk_plan_upload(const mk_plan_t* p, void* d_plan, size_t bytes, void* hip_stream);
 /* Workspace sub-buffer `which` (MK_BUF_*) of layer `layer` (ignored for
- * MK_BUF_LMPART): byte offset and size. Every workspace buffer holds tagged
- * words: u64 = (epoch << 32) | fp32 bits of the value, written by the step
- * of that epoch (KVN holds bf16 bits in the low 16 bits of the value; LMPART
- * holds (value, index) pairs per LM-head tile). Per layer:
+ * MK_BUF_LMPART and MK_BUF_LOGIT): byte offset and size. Every workspace
+ * buffer holds tagged words: u64 = (epoch << 32) | fp32 bits of the value,
+ * written by the step of that epoch (KVN holds bf16 bits in the low 16 bits
+ * of the value; LMPART holds (value, index) pairs per LM-head tile; LOGIT
+ * [B][vocab] the logits, written only by steps that sample). Per layer:
  *   XATTN [B][H] hidden after the attention residual, XFFN [B][H] layer output,
  *   Q [B][Hq][d] rotated queries, KVN [B][Hkv][2][d] the new token's K and V,
  *   PART [B][Hkv][splits][Hq/Hkv][d+2] attention split partials (o, max, sum),
@@ -262,7 +294,8 @@ mk_status mk_plan_upload(const mk_plan_t* p, void* d_plan, size_t bytes, void* h
  *   hidden state (for the RMSNorm), then a zero pad word. */
 enum { MK_BUF_XATTN = 0, MK_BUF_XFFN = 1, MK_BUF_Q = 2, MK_BUF_PART = 3, MK_BUF_O = 4,
        MK_BUF_RLOG = 5, MK_BUF_ACT = 6, MK_BUF_LMPART = 7, MK_BUF_KVN = 8,
-       MK_BUF_ROUTE = 9, MK_BUF_Y = 10, MK_BUF_OPART = 11, MK_BUF_QPART = 12 };
+       MK_BUF_ROUTE = 9, MK_BUF_Y = 10, MK_BUF_OPART = 11, MK_BUF_QPART = 12,
+       MK_BUF_LOGIT = 13 };
 mk_status mk_plan_buffer(const mk_plan_t* p, int32_t which, int32_t layer, size_t* offset,
                          size_t* bytes);
 /* The plan's per-step counter targets, [n_counters] (host): for each

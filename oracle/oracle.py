@@ -177,6 +177,48 @@ def argmax(v):
 
 # ---------------------------------------------------------------- KV state
 
+def sample_next(logits, temperature, top_k, top_p, min_p, u, k_max=64):
+    """The next token drawn from one sequence's logits, in fp64.
+
+    The Kinetic book ("Pick the sampling", the sampler flags) runs the
+    llama.cpp samplers in their default order; of them this takes top-k,
+    top-p, min-p and temperature, in that order, then one draw, and
+    temperature 0 always takes the likeliest token. Readings: ties in the
+    logits rank the lower id first; top_k outside 1 .. k_max means k_max (the
+    device keeps at most k_max candidates); top-p keeps the shortest run of
+    candidates, most likely first, whose probabilities (softmax over the
+    candidates at temperature 1) sum to at least top_p; min-p keeps the
+    candidates at least min_p times as likely as the best; the best
+    candidate is always kept; the draw takes the first kept candidate, most
+    likely first, at which the running sum of exp((z - z_max) / T) exceeds
+    u times its total (u in [0, 1) is given, not drawn here).
+    """
+    z = logits.double()
+    if temperature <= 0:
+        return argmax(z)
+    k = top_k if 1 <= top_k <= k_max else k_max
+    k = min(k, z.numel())
+    if k == 1:
+        return argmax(z)
+    _, order = torch.sort(-z, stable=True)       # descending, equal values by lower id
+    cand = order[:k]
+    zc = z[cand]
+    p = torch.softmax(zc, dim=0)
+    keep = torch.ones(k, dtype=torch.bool)
+    if top_p < 1:
+        cum = torch.cumsum(p, dim=0)
+        reach = int(torch.nonzero(cum >= top_p)[0]) if bool((cum >= top_p).any()) else k - 1
+        keep[reach + 1:] = False
+    if min_p > 0:
+        keep &= p >= min_p * p[0]
+    keep[0] = True
+    w = torch.where(keep, torch.exp((zc - zc[0]) / temperature), torch.zeros_like(zc))
+    run = torch.cumsum(w, dim=0)
+    hit = torch.nonzero(keep & (run > u * run[-1]))
+    pick = int(hit[0]) if hit.numel() else int(torch.nonzero(keep)[-1])
+    return int(cand[pick])
+
+
 class OracleKV:
     """Contiguous bf16 KV per (layer, sequence, kv head), with a length per sequence."""
 

@@ -52,7 +52,7 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(mk._lib, n), f"libmk.so does not export {n}"
         assert n in mk.EXPORTED, f"binding does not wrap {n}"
-    assert mk.mk_abi_version() == 1
+    assert mk.mk_abi_version() == 2
 
 
 def test_pool_matches_oracle_model():
