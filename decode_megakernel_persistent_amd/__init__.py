@@ -177,6 +177,7 @@ _plan_shape = {}   # plan handle -> (batch, page-table width), for mk_plan_updat
 
 MK_PLAN_ATTN_QUEUE = 1
 MK_PLAN_NO_ATTN_QUEUE = 2
+MK_PLAN_PREFILL = 4
 
 
 def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0, flags=0,

@@ -711,6 +711,26 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   Smem& s = c.s;
   const int l = t.layer, b = t.a0, g = t.a1, pg0 = t.a2, npg = t.a3, split = t.aux;
   const int HG = a.HG;
+  if ((t.flags & TF_PREFILL) && b > 0) {
+    // chunk row b reads pool slots that rows 0 .. b-1 write in this step:
+    // wait for those rows' K and V words of this head (each stored after its
+    // writer released its pool slots), then acquire
+    const int n = b * 2 * D;
+    bool ok = true;
+    for (int base = 0; base < n && ok; base += NT * 4) {
+      float v[4];
+      ok = read_words<4>(a, [&](int k) -> const uint64_t* {
+        const int i = base + tid() + k * NT;
+        if (i >= n) return nullptr;
+        const int j = i / (2 * D), e = i - j * 2 * D;
+        return a.kvn + (size_t)l * a.s_kvn + ((size_t)j * a.Hkv + g) * 2 * D + e;
+      }, v, c.t0, c.ti);
+    }
+    if (!ok) s.fail = 1;
+    lds_barrier();
+    if (s.fail) return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
   const int lane = tid() & 63, w = tid() >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
   const int32_t* prow = a.page_table + (size_t)b * a.max_pages;
@@ -1904,45 +1924,58 @@ __device__ __forceinline__ bool task_bqkv(Ctx& c, const Task& t) {
     }
     lds_barrier();
   }
-  for (int idx = tid(); idx < np * a.B; idx += NT) {
-    const int q = idx / a.B, b = idx - q * a.B;
-    const int pos = a.seq_lens[b];
-    const bool in_bounds = pos >= 0 && pos + 1 <= seq_bound(a, b) && pos < a.n_rope;
-    const int pc = in_bounds ? pos : 0;
-    const int32_t phys = a.page_table[(size_t)b * a.max_pages + (pc >> 4)];
-    int head, i, row;
-    const int sec = qkv_pair(p0 + q, g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
-    const float y0 = P.out[2 * q][b], y1 = P.out[2 * q + 1][b];
-    float r0 = y0, r1 = y1;
-    if (sec < 2) {
-      const float cs = a.rope_cos[(size_t)pc * (D / 2) + i], sn = a.rope_sin[(size_t)pc * (D / 2) + i];
-      r0 = y0 * cs - y1 * sn;
-      r1 = y1 * cs + y0 * sn;
-    }
-    if (sec == 0) {
-      uint64_t* qd = a.q + (size_t)l * a.s_q + ((size_t)b * a.Hq + head) * D;
-      st_tagged(qd + i, r0, a.epoch);
-      st_tagged(qd + i + D / 2, r1, a.epoch);
-    } else {
-      const uint32_t b0 = f2bf(r0), b1 = f2bf(r1);
-      uint64_t* kn = a.kvn + (size_t)l * a.s_kvn + (((size_t)b * a.Hkv + g) * 2 + (sec - 1)) * D;
-      st_tagged(kn + i, __uint_as_float(b0), a.epoch);
-      st_tagged(kn + i + D / 2, __uint_as_float(b1), a.epoch);
-      const bool page_ok = in_bounds && phys >= 0 && phys < a.n_pages;
-      if (!page_ok) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)pos, (uint32_t)phys);
-      else {
-        uint16_t* base = a.pool + (size_t)phys * a.page_stride + (size_t)l * a.layer_stride +
-                         (size_t)g * 2 * 16 * D;
-        const int slot = pos & 15;
-        if (sec == 1) {
-          base[kv_k_offset(slot, i)] = (uint16_t)b0;
-          base[kv_k_offset(slot, i + D / 2)] = (uint16_t)b1;
-        } else {
-          base[kv_v_offset(slot, i, D)] = (uint16_t)b0;
-          base[kv_v_offset(slot, i + D / 2, D)] = (uint16_t)b1;
+  // With TF_PREFILL the chunk's later rows read these pool slots in this
+  // step: every thread writes its slots, releases them, then stores the
+  // tagged words those rows wait on (one pass per kind of write).
+  const bool pf = (t.flags & TF_PREFILL) != 0;
+  for (int pass = pf ? 0 : 1; pass < 2; ++pass) {
+    for (int idx = tid(); idx < np * a.B; idx += NT) {
+      const int q = idx / a.B, b = idx - q * a.B;
+      const int pos = a.seq_lens[b];
+      const bool in_bounds = pos >= 0 && pos + 1 <= seq_bound(a, b) && pos < a.n_rope;
+      const int pc = in_bounds ? pos : 0;
+      const int32_t phys = a.page_table[(size_t)b * a.max_pages + (pc >> 4)];
+      int head, i, row;
+      const int sec = qkv_pair(p0 + q, g, a.HG, D, a.Hq, a.Hkv, &head, &i, &row);
+      const float y0 = P.out[2 * q][b], y1 = P.out[2 * q + 1][b];
+      float r0 = y0, r1 = y1;
+      if (sec < 2) {
+        const float cs = a.rope_cos[(size_t)pc * (D / 2) + i], sn = a.rope_sin[(size_t)pc * (D / 2) + i];
+        r0 = y0 * cs - y1 * sn;
+        r1 = y1 * cs + y0 * sn;
+      }
+      if (sec == 0) {
+        if (pass == 1) {
+          uint64_t* qd = a.q + (size_t)l * a.s_q + ((size_t)b * a.Hq + head) * D;
+          st_tagged(qd + i, r0, a.epoch);
+          st_tagged(qd + i + D / 2, r1, a.epoch);
+        }
+      } else {
+        const uint32_t b0 = f2bf(r0), b1 = f2bf(r1);
+        if (pass == 1) {
+          uint64_t* kn = a.kvn + (size_t)l * a.s_kvn + (((size_t)b * a.Hkv + g) * 2 + (sec - 1)) * D;
+          st_tagged(kn + i, __uint_as_float(b0), a.epoch);
+          st_tagged(kn + i + D / 2, __uint_as_float(b1), a.epoch);
+        }
+        if (pass == 0 || !pf) {
+          const bool page_ok = in_bounds && phys >= 0 && phys < a.n_pages;
+          if (!page_ok) raise_status(a, DS_BOUNDS, c.ti, (uint32_t)pos, (uint32_t)phys);
+          else {
+            uint16_t* base = a.pool + (size_t)phys * a.page_stride + (size_t)l * a.layer_stride +
+                             (size_t)g * 2 * 16 * D;
+            const int slot = pos & 15;
+            if (sec == 1) {
+              base[kv_k_offset(slot, i)] = (uint16_t)b0;
+              base[kv_k_offset(slot, i + D / 2)] = (uint16_t)b1;
+            } else {
+              base[kv_v_offset(slot, i, D)] = (uint16_t)b0;
+              base[kv_v_offset(slot, i + D / 2, D)] = (uint16_t)b1;
+            }
+          }
         }
       }
     }
+    if (pass == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   }
   return true;
 }

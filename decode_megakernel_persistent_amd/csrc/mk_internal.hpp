@@ -52,7 +52,10 @@ enum Op : uint8_t {
 // TF_STAGE_KV: before its body the task requests the first pages of this
 // unit's next attention split (the first attention task at most STAGE_SCAN
 // tasks further on in the same list) into LDS.
-enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4, TF_LOGITS = 8 };
+// TF_PREFILL (chunked-prefill plans): a QKV task makes its pool writes visible
+// before its tagged words; an attention task of chunk row b first waits for
+// rows 0 .. b-1's K and V words and then reads the pool.
+enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4, TF_LOGITS = 8, TF_PREFILL = 16 };
 
 // Batch QKV tasks: rotary pairs per row block (the rows of a block are 2
 // BQKV_PAIRS), and the words per (reduction block, row block, sequence) of

@@ -386,6 +386,17 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         return fail(MK_EBOUNDS, "mk_plan: sequence " + std::to_string(b) +
                                     " has no page mapped at logical page " + std::to_string(j));
   }
+  const bool prefill = o && (o->flags & MK_PLAN_PREFILL);
+  if (prefill) {
+    if (!batch) return fail(MK_EINVAL, "mk_plan: a prefill chunk has 2 .. 32 rows");
+    for (int b = 1; b < B; ++b) {
+      if (bd->seq_lens[b] != bd->seq_lens[0] + b)
+        return fail(MK_EINVAL, "mk_plan: prefill rows must be consecutive positions of one sequence");
+      for (int j = 0; j < bd->max_pages; ++j)
+        if (bd->page_table[(int64_t)b * bd->max_pages + j] != bd->page_table[j])
+          return fail(MK_EINVAL, "mk_plan: prefill rows must share one page-table row");
+    }
+  }
   // batch 1 runs with its own bound; a batch keeps max_ctx_bound as the plan bound
   const int bound = batch ? max_bound : seq_bound[0];
   const int pg_bound = (bound + 15) / 16;
@@ -767,6 +778,10 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
           }
       }
   }
+  if (prefill)
+    for (auto& lst : p->lists)
+      for (auto& t : lst)
+        if (t.op == mk::OP_BQKV || t.op == mk::OP_ATTN) t.flags |= mk::TF_PREFILL;
   p->stage_of_task.clear();
   for (int cu = 0; cu < n_cu; ++cu)
     for (int s0 : stage_lists[cu]) p->stage_of_task.push_back(s0);

@@ -103,6 +103,16 @@ typedef struct mk_plan_opts {
  * instead of one static split per task. Off unless asked for. */
 #define MK_PLAN_ATTN_QUEUE 1     /* use the queue (batch 1) */
 #define MK_PLAN_NO_ATTN_QUEUE 2  /* never use it */
+/* Chunked prefill: the batch rows are 2 .. 32 consecutive prompt tokens of
+ * ONE sequence (every page-table row the same, seq_lens[i] = seq_lens[0] + i,
+ * tokens_in the chunk's tokens in order), run as one step of the batch path:
+ * MFMA tiles over the chunk's rows write their K and V into the shared pages
+ * (row i at position seq_lens[0] + i) and row i attends to the tokens before
+ * it, the chunk's earlier rows included -- each row's result is the decode
+ * step of its token, so the chunk equals its tokens decoded one by one. The
+ * last row's next token continues the sequence; afterwards its length is
+ * seq_lens[0] + chunk (each row's own seq_lens entry grows by one). */
+#define MK_PLAN_PREFILL 4
 
 typedef struct mk_plan mk_plan_t;   /* opaque host object */
 typedef struct mk_pool mk_pool_t;   /* opaque host object */

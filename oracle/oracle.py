@@ -177,6 +177,16 @@ def argmax(v):
 
 # ---------------------------------------------------------------- KV state
 
+def prefill(m, W, kv, tokens, dt=torch.float32):
+    """A prompt chunk of one sequence (batch row 0 of kv): the decode step of
+    each token in order, each attending to every token before it. A prefill
+    computes the same K, V and hidden states as decoding the prompt one token
+    at a time; this is that definition (the megakernel page's continuous
+    batching fills pages from prompts; the pages give no separate prefill
+    arithmetic). Returns the list of per-token step results."""
+    return [decode_step(m, W, kv, [t], dt) for t in tokens]
+
+
 def sample_next(logits, temperature, top_k, top_p, min_p, u, k_max=64):
     """The next token drawn from one sequence's logits, in fp64.
 
