@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--plan-flags", type=int, default=0, help="MK_PLAN_* bits")
     ap.add_argument("--batch32-steps", type=int, default=64,
                     help="timed steps of the batch-32 leg (48-layer MoE at 8K only; 0: skip)")
+    ap.add_argument("--sample-steps", type=int, default=64,
+                    help="timed steps of the sampling leg (same workload, top-k/top-p/temperature; 0: skip)")
+    ap.add_argument("--prefill-steps", type=int, default=16,
+                    help="timed 32-token prefill chunks after 8192 prior tokens (48-layer MoE; 0: skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM counter bytes per launch measured by rocprofv3 --pmc")
     return ap.parse_args()
@@ -83,19 +87,36 @@ def main():
     if a.cpu_steps > 0:
         cpu = cpu_baseline(w, a, r["hist"], r["ids"], W)
 
+    # every further leg sets up its own session on the resident weights
+    mk.mk_pool_free(pool)
+    dec.close()
+    dec = pool = None
+    torch.cuda.empty_cache()
+
+    # sampling beyond greedy in the last stage: the same workload
+    smp = None
+    if a.sample_steps > 0:
+        rs = run_workload(torch, mk, dev, a.workload, a.sample_steps, 2, a, weights=W, sampling=True)
+        smp = {"steps": a.sample_steps, "settings": "temperature 0.8, top_k 40, top_p 0.95, min_p 0.05, "
+                                                   "one seeded uniform per sequence and step",
+               "value": round(rs["tok_s"], 2), "unit": "tok/s", "ms_per_step": round(rs["ms_step"], 4),
+               "ms_over_greedy": round(rs["ms_step"] - ms_step, 4)}
+        mk.mk_pool_free(rs["pool"])
+        rs["dec"].close()
+        rs.clear()
+        torch.cuda.empty_cache()
+
+    # chunked prefill: 32 prompt tokens of one sequence per step
+    pre = None
+    if a.prefill_steps > 0 and a.workload == "moe48_b1_8k":
+        pre = prefill_leg(torch, mk, dev, W, a)
+        torch.cuda.empty_cache()
+
     # the metric's second number: the same model at batch 32 (ragged contexts,
     # one shared pool), with the weights already resident
     b32 = None
     if a.batch32_steps > 0 and a.workload == "moe48_b1_8k":
-        mk.mk_pool_free(pool)
-        dec.close()
-        del dec
-        torch.cuda.empty_cache()
         r32 = run_workload(torch, mk, dev, "moe48_b32_ragged", a.batch32_steps, 2, a, weights=W)
-        mk.mk_pool_free(r32["pool"])
-        r32["dec"].close()
-        r32.clear()
-        pool = dec = None
         b32 = {"workload": "moe48_b32_ragged", "steps": a.batch32_steps, "warmup": 2,
                "value": round(r32["tok_s"], 2), "unit": "tok/s",
                "ms_per_step": round(r32["ms_step"], 4),
@@ -103,6 +124,9 @@ def main():
                "bytes_per_step": r32["bytes_step"],
                "achieved_gbs": round(r32["achieved_gbs"], 1),
                "frac": round(r32["achieved_gbs"] / HBM_PEAK_GBS, 4)}
+        mk.mk_pool_free(r32["pool"])
+        r32["dec"].close()
+        r32.clear()
 
     out = {
         "metric": METRIC,
@@ -136,15 +160,14 @@ def main():
         "host_wall_s": round(wall, 3),
         "cpu_baseline": cpu,
         "batch32": b32,
+        "sampling": smp,
+        "prefill": pre,
     }
     print(json.dumps(out), flush=True)
-    # ordered teardown: plans and pools freed, every device buffer released
-    # and the device idle before the interpreter (and the HIP runtime with
-    # it) shuts down
-    if dec is not None:
-        mk.mk_pool_free(pool)
-        dec.close()
-    del dec, W, r
+    # ordered teardown: plans and pools freed (above), every device buffer
+    # released and the device idle before the interpreter (and the HIP
+    # runtime with it) shuts down
+    del W, r
     torch.cuda.synchronize()
     import gc
     gc.collect()
@@ -152,11 +175,12 @@ def main():
     torch.cuda.synchronize()
 
 
-def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
+def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None, sampling=False):
     """Set up workload `name`, run `warmup` steps, restore the starting state,
-    time `steps` greedy steps with HIP events on the launch stream, and count
-    the algorithmic bytes of every timed step (weights actually read, from
-    the step's own top-k ids, plus KV read and written)."""
+    time `steps` steps (greedy, or sampled with fixed settings and seeded
+    uniform draws) with HIP events on the launch stream, and count the
+    algorithmic bytes of every timed step (weights actually read, from the
+    step's own top-k ids, plus KV read and written)."""
     from fixtures.session import gpu_session, spec
     w = spec(name, a.seed, steps=warmup + steps)
     m, B = w["model"], w["batch"]
@@ -172,11 +196,18 @@ def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
     # hist[s]: the tokens step s reads; step s writes hist[s + 1]
     hist = torch.empty((max(steps, warmup) + 1, B), dtype=torch.int32, device=dev)
     ids = torch.full((steps, L, B, K), -1, dtype=torch.int32, device=dev)
+    smp = [None] * max(steps, warmup)
+    if sampling:
+        g = torch.Generator().manual_seed(a.seed + 99)
+        U = torch.rand((max(steps, warmup), B), generator=g).to(dev)
+        base = dict(temperature=torch.full((B,), 0.8, device=dev), top_k=torch.full((B,), 40, dtype=torch.int32, device=dev),
+                    top_p=torch.full((B,), 0.95, device=dev), min_p=torch.full((B,), 0.05, device=dev))
+        smp = [dict(base, uniform=U[s]) for s in range(max(steps, warmup))]
 
     # warm-up, then restore the pre-warm-up state (lengths and first tokens)
     hist[0].copy_(tok0)
     for s in range(warmup):
-        dec.step(hist[s], hist[s + 1])
+        dec.step(hist[s], hist[s + 1], sampling=smp[s])
     torch.cuda.synchronize()
     dec.check_status()
     dec.seq_lens.copy_(ctx0)
@@ -188,7 +219,7 @@ def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
     t0 = time.perf_counter()
     ev[0].record(stream)
     for s in range(steps):
-        dec.step(hist[s], hist[s + 1], topk_ids=ids[s] if moe else None)
+        dec.step(hist[s], hist[s + 1], topk_ids=ids[s] if moe else None, sampling=smp[s])
         ev[s + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -213,6 +244,66 @@ def run_workload(torch, mk, dev, name, steps, warmup, a, weights=None):
             "wall": wall, "bytes_step": bytes_step, "wsum": wsum / steps, "ksum": ksum / steps,
             "achieved_gbs": tot_bytes / (ms_total * 1e-3) / 1e9,
             "sol_tok_s": B * HBM_PEAK_GBS * 1e9 / bytes_step}
+
+
+def prefill_leg(torch, mk, dev, W, a, C=32, p0=8192):
+    """Chunked prefill of the 48-layer MoE: one sequence with p0 prior tokens
+    runs C-token chunks (MK_PLAN_PREFILL: C batch rows at consecutive
+    positions sharing one page row); each timed step is one chunk, the next
+    step the next C positions. Bytes per step are those this design reads:
+    the weights the chunk's routing touches and, per row, the K/V of every
+    token before it (each row streams the prior context)."""
+    from decode_megakernel_persistent_amd.runtime import Decoder, alloc_kv_pool
+    from fixtures import device as fxd
+    from fixtures.session import spec
+    m = spec("moe48_b1_8k", a.seed)["model"]
+    L, V, K, pt = m["n_layers"], m["vocab"], m["top_k"], m["page_tokens"]
+    warm, steps = 2, a.prefill_steps
+    total = p0 + C * (warm + steps + 1)  # the last chunk's last row reads up to its own bound
+    n_pages = -(-total // pt)
+    pool = mk.mk_pool_create(n_pages, pt, 1, None)
+    mk.mk_pool_lease(pool, 0, total)
+    row = mk.mk_pool_page_table(pool, [0], n_pages)[0]
+    kv = alloc_kv_pool(m, n_pages, dev)
+    fxd.fill_kv(kv, torch.tensor(row, dtype=torch.int32, device=dev), m, a.seed, 0, p0)
+    lens = [p0 + i for i in range(C)]
+    bounds = [x + C * (warm + steps) for x in lens]
+    print(f"[bench] prefill: {C}-token chunks after {p0} tokens, {steps} timed", file=sys.stderr, flush=True)
+    dec = Decoder(m, W, kv, n_pages, lens, [row] * C, n_pages, max(bounds), device=dev,
+                  plan_flags=mk.MK_PLAN_PREFILL, ctx_bounds=bounds)
+    g = torch.Generator().manual_seed(a.seed + 5)
+    toks = torch.randint(0, V, (warm + steps, C), generator=g, dtype=torch.int32).to(dev)
+    out = torch.empty((warm + steps, C), dtype=torch.int32, device=dev)
+    ids = torch.full((steps, L, C, K), -1, dtype=torch.int32, device=dev)
+    for s in range(warm):
+        dec.step(toks[s], out[s])
+    torch.cuda.synchronize()
+    dec.check_status()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        dec.step(toks[warm + s], out[warm + s], topk_ids=ids[s])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec.check_status()
+    ms = e0.elapsed_time(e1) / steps
+    ids_h = ids.cpu()
+    desc = mk.model_desc(m)
+    tot = 0.0
+    for s in range(steps):
+        ln = [x + C * (warm + s) for x in lens]
+        distinct = [len(set(ids_h[s, l].reshape(-1).tolist())) for l in range(L)]
+        wb, kr, kw = mk.mk_step_bytes(desc, ln, distinct)
+        tot += wb + kr + kw
+    bytes_step = tot / steps
+    dec.close()
+    mk.mk_pool_free(pool)
+    del kv
+    gbs = bytes_step / (ms * 1e-3) / 1e9
+    return {"chunk": C, "prior_tokens": p0, "steps": steps, "value": round(C / (ms * 1e-3), 1),
+            "unit": "prompt tok/s", "ms_per_chunk": round(ms, 4), "bytes_per_chunk": bytes_step,
+            "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def stream_copy_probe(torch, mk, dev, reps=5):
@@ -287,7 +378,7 @@ def cpu_baseline(w, a, hist, ids, Wd):
                 Wh.gate(l), Wh.up(l), Wh.down(l)
         Wh.lm_head()
         t0 = time.perf_counter()
-        r, forced, differ = O.decode_step_following(m, Wh, kv, hist[s], routing, 1e-5)
+        r, forced, differ = O.decode_step_following(m, Wh, kv, hist[s], routing, 1e-3)
         times.append(time.perf_counter() - t0)
         forced_n += len(forced)
         differ_n += len(differ)

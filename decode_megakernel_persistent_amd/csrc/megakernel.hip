@@ -1511,9 +1511,11 @@ template <class TV, class TI>
 __device__ bool sample_seq(Ctx& c, int b, int n, int rows, const TV& tv, const TI& ti, int* tok) {
   KAC& a = c.a;
   Smem& s = c.s;
-  constexpr int CAP = 4096, ROUND = NT * 4;
-  uint64_t* keys = (uint64_t*)s.stage;  // tile maxima, then candidates (CAP keys each)
-  uint64_t* cand = keys + CAP;
+  constexpr int NKEY = 4096, CAP = 8192, PER = 8, ROUND = NT * PER;
+  static_assert(sizeof(Smem::stage) >= (NKEY + CAP) * sizeof(uint64_t), "sampling keys exceed the shared area");
+  static_assert(CAP - ROUND >= MK_SAMPLE_TOP_K_MAX, "a round must fit after keeping the top k");
+  uint64_t* keys = (uint64_t*)s.stage;  // tile maxima (NKEY), then candidates (CAP): 96 KB
+  uint64_t* cand = keys + NKEY;
   int* tiles = (int*)s.res;
   int* cnt = (int*)s.out;
   const int K = sample_k(a, b);
@@ -1527,36 +1529,42 @@ __device__ bool sample_seq(Ctx& c, int b, int n, int rows, const TV& tv, const T
   if (tid() < nt) tiles[tid()] = (int)(key_id(keys[tid()]) / (uint32_t)rows);
   if (tid() == 0) *cnt = 0;
   lds_barrier();
+  // the nt tiles' rows as one index space (element e: tile e / rows, row
+  // e % rows, past the vocabulary in the last tile: none), PER words per
+  // thread per round
   const uint64_t* lw = a.lw + (size_t)b * a.V;
-  for (int j = 0; j < nt; ++j) {
-    const int r0 = tiles[j] * rows, nr = min(rows, a.V - r0);
-    for (int base = 0; base < nr; base += ROUND) {
-      float v[4];
-      const bool ok = read_words<4>(a, [&](int k) -> const uint64_t* {
-        const int r = base + tid() + k * NT;
-        return r < nr ? lw + r0 + r : nullptr;
-      }, v, c.t0, c.ti);
-      if (!ok) s.fail = 1;
-      if (ok)
+  const int total = nt * rows;
+  for (int base = 0; base < total; base += ROUND) {
+    float v[PER];
+    const bool ok = read_words<PER>(a, [&](int k) -> const uint64_t* {
+      const int e = base + tid() + k * NT;
+      if (e >= total) return nullptr;
+      const int r = tiles[e / rows] * rows + e % rows;
+      return r < a.V ? lw + r : nullptr;
+    }, v, c.t0, c.ti);
+    if (!ok) s.fail = 1;
+    if (ok)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int r = base + tid() + k * NT;
-          const uint64_t key = tok_key(v[k], (uint32_t)(r0 + r));
-          if (r < nr && key >= thr) cand[atomicAdd(cnt, 1)] = key;
+      for (int k = 0; k < PER; ++k) {
+        const int e = base + tid() + k * NT;
+        const int r = e < total ? tiles[e / rows] * rows + e % rows : a.V;
+        if (r < a.V) {
+          const uint64_t key = tok_key(v[k], (uint32_t)r);
+          if (key >= thr) cand[atomicAdd(cnt, 1)] = key;
         }
-      lds_barrier();
-      if (s.fail) return false;
-      const int m = *cnt;
-      if (m > CAP - ROUND) {  // keep the K largest, raise the threshold
-        int m2 = 2;
-        while (m2 < m) m2 <<= 1;
-        for (int i = m + tid(); i < m2; i += NT) cand[i] = 0ull;
-        lds_barrier();
-        lds_sort_desc(cand, m2);
-        thr = cand[K - 1];
-        if (tid() == 0) *cnt = K;
-        lds_barrier();
       }
+    lds_barrier();
+    if (s.fail) return false;
+    const int m = *cnt;
+    if (m > CAP - ROUND) {  // keep the K largest, raise the threshold
+      int m2 = 2;
+      while (m2 < m) m2 <<= 1;
+      for (int i = m + tid(); i < m2; i += NT) cand[i] = 0ull;
+      lds_barrier();
+      lds_sort_desc(cand, m2);
+      thr = cand[K - 1];
+      if (tid() == 0) *cnt = K;
+      lds_barrier();
     }
   }
   {
