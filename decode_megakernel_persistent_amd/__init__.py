@@ -50,7 +50,7 @@ class mk_plan_opts(ctypes.Structure):
 
 class mk_weights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("embed", "attn_norm", "w_qkv", "w_o", "ffn_norm", "router",
-                                   "gate", "up", "down", "final_norm", "lm_head")]
+                                   "gate", "up", "down", "final_norm", "lm_head", "router_fold")]
 
 
 class mk_kv(ctypes.Structure):
@@ -82,6 +82,7 @@ _SIGS = {
     "mk_last_error": (ctypes.c_char_p, []),
     "mk_device_cu_count": (_i32, [_P(_i32)]),
     "mk_stream_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "mk_router_fold": (_i32, [_vp, _vp, _vp, _vp]),
     "mk_rope_table": (_i32, [_f32, _i32, _i32, _vp, _vp]),
     "mk_kv_pool_elems": (_i64, [_P(mk_model_desc), _i64]),
     "mk_step_bytes": (_i32, [_P(mk_model_desc), _i32, _P(_i32), _P(_i32), _P(ctypes.c_double),
@@ -146,6 +147,11 @@ def mk_device_cu_count():
     return n.value
 
 
+def mk_router_fold(desc, weights, out_ptr, stream_ptr):
+    """out = W_r diag(ffn_norm) W_o per layer (fp32 [L][E][Hq d], device)."""
+    _check(_lib.mk_router_fold(ctypes.byref(desc), ctypes.byref(weights), out_ptr, stream_ptr))
+
+
 def mk_stream_copy(dst_ptr, src_ptr, nbytes, stream_ptr):
     _check(_lib.mk_stream_copy(dst_ptr, src_ptr, nbytes, stream_ptr))
 
@@ -178,6 +184,7 @@ _plan_shape = {}   # plan handle -> (batch, page-table width), for mk_plan_updat
 MK_PLAN_ATTN_QUEUE = 1
 MK_PLAN_NO_ATTN_QUEUE = 2
 MK_PLAN_PREFILL = 4
+MK_PLAN_NO_ROUTER_FOLD = 8
 
 
 def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0, flags=0,

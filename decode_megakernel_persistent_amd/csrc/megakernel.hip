@@ -1207,6 +1207,88 @@ __device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
   return true;
 }
 
+// Router logits before the RMSNorm's 1/rms scale (TF_FOLD, batch 1): rows
+// r0 .. r0 + n of W_r (g * x) + F o, where x is the layer input, o the
+// attention output and F = W_r diag(g) W_o (fp32, mk_router_fold). The router
+// reads RMSNorm(x + W_o o), so this equals its logits times rms(x + W_o o);
+// it needs only what the O tasks need and runs beside them, and the expert
+// tasks apply the scale, which they compute for their own input anyway.
+template <int CPL, int TC>
+__device__ __forceinline__ bool task_router_fold(Ctx& c, const Task& t) {
+  constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
+  constexpr int FR = 4;  // folded rows per task (the planner gives at most four)
+  constexpr int FQ = 4;  // 16-byte chunks of a folded row per thread (Hq d <= 8192)
+  KAC& a = c.a;
+  Smem& s = c.s;
+  const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H, K = a.Hq * a.D, K4 = K / 4;
+  const uint16_t* W = a.router + (size_t)l * a.E * H;
+  Tile<CPL, RPW, TC> tile;
+  tile.issue(n, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
+  const float4* F = (const float4*)(a.rfold + ((size_t)l * a.E + r0) * K);
+  float4 fr[FR][FQ];
+#pragma unroll
+  for (int r = 0; r < FR; ++r)
+#pragma unroll
+    for (int q = 0; q < FQ; ++q) {
+      const int i = tid() + q * NT;
+      fr[r][q] = r < n && i < K4 ? F[(size_t)r * K4 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  Gains gn;
+  gn.load(a.ffn_norm + (size_t)l * H, H);
+  // s.vec = [x (H) | o (K)]
+  float* ov = s.vec + H;
+  if (l == 0) {
+    const uint16_t* e = a.embed + (size_t)token_row(a, 0) * H;
+    for (int i = tid(); i < H; i += NT) s.vec[i] = bf2f(e[i]);
+    if (!gather<8>(c, a.o + (size_t)l * a.s_o, K, ov, 1)) return false;
+  } else {
+    if (!gather2<6>(c, a.x + (size_t)(l - 1) * a.s_x, H, a.o + (size_t)l * a.s_o, H + K, s.vec, 1)) return false;
+  }
+  // x * g into split form (no norm)
+  if (tid() < H / 8) {
+    float x[8];
+    *(float4*)x = *(const float4*)(s.vec + 8 * tid());
+    *(float4*)(x + 4) = *(const float4*)(s.vec + 8 * tid() + 4);
+    const uint32_t gw[4] = {gn.g.x, gn.g.y, gn.g.z, gn.g.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= (e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1]);
+    uint4 hi, lo;
+    split8(x, hi, lo);
+    *(uint4*)(s.vec + 8 * tid()) = hi;
+    *(uint4*)(s.vec + 8 * tid() + 4) = lo;
+  }
+  lds_barrier();
+  tile.dots(s.vec, s.out);
+  float acc[FR];
+#pragma unroll
+  for (int r = 0; r < FR; ++r) {
+    acc[r] = 0.f;
+#pragma unroll
+    for (int q = 0; q < FQ; ++q) {
+      const int i = tid() + q * NT;
+      if (i < K4) {
+        const float4 o4 = *(const float4*)(ov + 4 * i);
+        acc[r] = fmaf(fr[r][q].x, o4.x, acc[r]);
+        acc[r] = fmaf(fr[r][q].y, o4.y, acc[r]);
+        acc[r] = fmaf(fr[r][q].z, o4.z, acc[r]);
+        acc[r] = fmaf(fr[r][q].w, o4.w, acc[r]);
+      }
+    }
+    acc[r] = wave_sum(acc[r]);
+  }
+  if ((tid() & 63) == 0)
+#pragma unroll
+    for (int r = 0; r < FR; ++r) s.red[r * NWAVE + (tid() >> 6)] = acc[r];
+  lds_barrier();
+  if (tid() < n) {
+    float v = s.out[tid()];
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) v += s.red[tid() * NWAVE + w];
+    st_tagged(a.rlog + (size_t)l * a.s_rlog + r0 + tid(), v, a.epoch);
+  }
+  return true;
+}
+
 // Expert task: route (every expert task computes the same top-k), stream the
 // gate/up rows of its slot's expert into registers, SwiGLU them against the
 // normalised hidden state and publish the activations; then request the rows
@@ -1262,6 +1344,15 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
     }
     for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
     lds_barrier();
+    // folded router logits still lack the RMSNorm's 1/rms of x_attn, whose
+    // per-wave sums of squares the gather left in s.red[0 .. NWAVE)
+    float sc = 1.f;
+    if (t.flags & TF_FOLD) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) tot += s.red[w];
+      sc = 1.0f / sqrtf(tot / (float)H + a.eps);
+    }
     if (tid() < E) {
       int rank = 0;
       for (int q = 0; q < parts; ++q) rank += partial[q * E32 + tid()];
@@ -1270,7 +1361,7 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.red[NWAVE + w]);
         s.route_ids[rank] = tid();
-        s.route_w[rank] = expf(lg_[tid()] - M);  // softmax numerator (see below)
+        s.route_w[rank] = expf((lg_[tid()] - M) * sc);  // softmax numerator (see below)
       }
     }
     norm_pack(c, s.vec, H, gn);  // its barrier also publishes the selection
@@ -1284,7 +1375,7 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
         float M = NEG_INF;
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.red[NWAVE + w]);
-        for (int e = 0; e < E; ++e) div += expf(lg_[e] - M);
+        for (int e = 0; e < E; ++e) div += expf((lg_[e] - M) * sc);
       }
       const float wn = s.route_w[tid()] / div;
       s.route_wn[tid()] = wn;  // read after later barriers
@@ -2448,7 +2539,9 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
           switch (t.op) {
             case OP_QKV: ok = task_qkv<CH, TCH, HD>(c, t); break;
             case OP_O: ok = task_o<CO, TCO>(c, t); break;
-            case OP_ROUTER: ok = task_router<CH, TCH>(c, t); break;
+            case OP_ROUTER:
+              ok = (t.flags & TF_FOLD) ? task_router_fold<CH, TCH>(c, t) : task_router<CH, TCH>(c, t);
+              break;
             case OP_EXPERT: ok = task_expert<CH, TCH, CF, TCF>(c, t); break;
             case OP_LM: ok = task_lm<CH, TCH>(c, t); break;
             case OP_FINAL: ok = task_final(c, t); break;
@@ -2494,6 +2587,53 @@ __global__ __launch_bounds__(256) void mk_stream_copy_kernel(uint4* __restrict__
   }
 }
 
+// out[l][e][j] = sum_h R[l][e][h] g[l][h] O[l][h][j] (mk_router_fold): a
+// 32 (e) x 64 (j) tile per workgroup of 256 threads, 2 x 4 outputs per
+// thread, h in LDS-staged steps of 32. Each term is a product of three bf16
+// values (at most 24 significant bits), exact in fp32; sums in fp32.
+__global__ __launch_bounds__(256) void mk_router_fold_kernel(const uint16_t* __restrict__ R,
+                                                             const uint16_t* __restrict__ g,
+                                                             const uint16_t* __restrict__ O,
+                                                             float* __restrict__ out, int E, int H, int K) {
+  __shared__ float As[32][33];
+  __shared__ float Bs[32][64];
+  const int l = blockIdx.z, e0 = blockIdx.y * 32, j0 = blockIdx.x * 64;
+  const int te = threadIdx.x / 16, tj = threadIdx.x % 16;
+  const uint16_t* Rl = R + (size_t)l * E * H;
+  const uint16_t* gl = g + (size_t)l * H;
+  const uint16_t* Ol = O + (size_t)l * H * K;
+  float acc[2][4] = {};
+  for (int h0 = 0; h0 < H; h0 += 32) {
+    for (int i = threadIdx.x; i < 32 * 32; i += 256) {
+      const int e = i / 32, h = i % 32;
+      As[e][h] = e0 + e < E && h0 + h < H ? bf2f(Rl[(size_t)(e0 + e) * H + h0 + h]) * bf2f(gl[h0 + h]) : 0.f;
+    }
+    for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+      const int h = i / 64, j = i % 64;
+      Bs[h][j] = h0 + h < H && j0 + j < K ? bf2f(Ol[(size_t)(h0 + h) * K + j0 + j]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int h = 0; h < 32; ++h) {
+      const float a0 = As[2 * te][h], a1 = As[2 * te + 1][h];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float bv = Bs[h][4 * tj + q];
+        acc[0][q] = fmaf(a0, bv, acc[0][q]);
+        acc[1][q] = fmaf(a1, bv, acc[1][q]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + 2 * te + r, j = j0 + 4 * tj + q;
+      if (e < E && j < K) out[((size_t)l * E + e) * K + j] = acc[r][q];
+    }
+}
+
 // Zero-fill of n 16-byte words (a kernel, not a memset node, so that a
 // caller may capture it in a graph).
 __global__ __launch_bounds__(256) void mk_zero_kernel(uint4* __restrict__ p, size_t n) {
@@ -2535,6 +2675,20 @@ extern "C" mk_status mk_device_cu_count(int32_t* n_cu) {
   e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   *n_cu = v;
+  return MK_OK;
+}
+
+extern "C" mk_status mk_router_fold(const mk_model_desc* m, const mk_weights* w, float* out, void* stream) {
+  if (!m || !w || !out) return fail(MK_EINVAL, "mk_router_fold: NULL argument");
+  if (m->n_experts <= 0) return fail(MK_EINVAL, "mk_router_fold: a dense model has no router");
+  if (!w->router || !w->ffn_norm || !w->w_o) return fail(MK_EINVAL, "mk_router_fold: missing weight pointer");
+  const int E = m->n_experts, H = m->hidden, K = m->n_q_heads * m->head_dim, L = m->n_layers;
+  if (E <= 0 || H <= 0 || K <= 0 || L <= 0) return fail(MK_EINVAL, "mk_router_fold: bad shape");
+  hipLaunchKernelGGL(mk::dev::mk_router_fold_kernel, dim3((K + 63) / 64, (E + 31) / 32, L), dim3(256), 0,
+                     (hipStream_t)stream, (const uint16_t*)w->router, (const uint16_t*)w->ffn_norm,
+                     (const uint16_t*)w->w_o, out, E, H, K);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "mk_router_fold");
   return MK_OK;
 }
 
@@ -2711,6 +2865,9 @@ static mk_status launch_step(const mk_plan_t* p, const mk_weights* w, const mk_k
   a.ffn_norm = (const uint16_t*)w->ffn_norm; a.router = (const uint16_t*)w->router;
   a.gate = (const uint16_t*)w->gate; a.up = (const uint16_t*)w->up; a.down = (const uint16_t*)w->down;
   a.final_norm = (const uint16_t*)w->final_norm; a.lm = (const uint16_t*)w->lm_head;
+  a.rfold = w->router_fold;
+  if (p->router_fold && !w->router_fold)
+    return fail(MK_EINVAL, "mk_decode_step: this plan reads the folded router (mk_router_fold) and it is NULL");
   a.pool = (uint16_t*)kv->pool;
   a.layer_stride = (int64_t)m.n_kv_heads * 2 * 16 * m.head_dim;
   a.page_stride = (int64_t)m.n_layers * a.layer_stride;

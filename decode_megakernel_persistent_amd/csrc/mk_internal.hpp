@@ -55,7 +55,10 @@ enum Op : uint8_t {
 // TF_PREFILL (chunked-prefill plans): a QKV task makes its pool writes visible
 // before its tagged words; an attention task of chunk row b first waits for
 // rows 0 .. b-1's K and V words and then reads the pool.
-enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4, TF_LOGITS = 8, TF_PREFILL = 16 };
+// TF_FOLD (batch-1 MoE): router tasks form the logits before the RMSNorm
+// scale from x and o (W_r (g x) + (W_r diag(g) W_o) o); expert tasks apply it.
+enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4, TF_LOGITS = 8, TF_PREFILL = 16,
+                           TF_FOLD = 32 };
 
 // Batch QKV tasks: rotary pairs per row block (the rows of a block are 2
 // BQKV_PAIRS), and the words per (reduction block, row block, sequence) of
@@ -220,6 +223,7 @@ struct KArgs {
   // weights (bf16)
   const uint16_t *embed, *attn_norm, *wqkv, *wo, *ffn_norm, *router, *gate, *up, *down,
       *final_norm, *lm;
+  const float* rfold;  // [L][E][Hq D] W_r diag(g) W_o (folded router), or NULL
   // KV cache
   uint16_t* pool;
   int64_t page_stride, layer_stride;  // bf16 elements

@@ -465,6 +465,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   const int flags = o ? o->flags : 0;
   int pps = o && o->attn_split_pages > 0 ? o->attn_split_pages : (pg_total + n_cu - 1) / n_cu;
   const bool queue = !(flags & MK_PLAN_NO_ATTN_QUEUE) && B == 1 && (flags & MK_PLAN_ATTN_QUEUE);
+  p->router_fold = !batch && moe && !(flags & MK_PLAN_NO_ROUTER_FOLD);
   if (queue) pps = mk::QUEUE_PAGES;
   // a batch: about four splits per unit, so that ragged lengths even out
   if (batch && !(o && o->attn_split_pages > 0)) pps = std::max(8, ceil_div(pg_total, 4 * n_cu));
@@ -613,10 +614,14 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
           }
       stages.push_back(st);
     }
-    // O
+    // O; with the router folded, the router tasks (four expert rows each)
+    // join the O stage on units of their own: both read only the attention
+    // output and the layer input
+    const bool fold = p->router_fold;
+    const int n_rf = fold ? ceil_div(m->n_experts, 4) : 0;
     {
       std::vector<Task> st;
-      int nt = std::max(n_cu, ceil_div(H, rows_max(Hq * D)));
+      int nt = std::max(n_cu - n_rf, ceil_div(H, rows_max(Hq * D)));
       for (auto [s0, c] : split_even(H, nt)) {
         Task t = mk_task(mk::OP_O, l);
         t.wait_b = ctr16(p->c_comb[l]);
@@ -625,10 +630,20 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         t.units = (uint16_t)c;
         st.push_back(t);
       }
+      if (fold)
+        for (auto [s0, c] : split_even(m->n_experts, n_rf)) {
+          Task t = mk_task(mk::OP_ROUTER, l);
+          t.flags |= mk::TF_FOLD;
+          t.wait_b = ctr16(p->c_comb[l]);
+          t.signal = ctr16(p->c_router[l]);
+          t.a1 = s0; t.a2 = c;
+          t.units = (uint16_t)c;
+          st.push_back(t);
+        }
       stages.push_back(st);
     }
     int n_router = 0;
-    if (moe) {
+    if (moe && !fold) {
       std::vector<Task> st;
       int nt = std::max(std::min(n_cu, ceil_div(m->n_experts, 8)), ceil_div(m->n_experts, rows_max(H)));
       n_router = nt;
@@ -678,6 +693,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
           t.a0 = gu[i][0]; t.aux = (uint16_t)gu[i][1]; t.a1 = gu[i][2]; t.a2 = gu[i][3];
           if (moe && gu[i][1] == 0 && gu[i][2] == 0) t.flags |= mk::TF_WRITE_TOPK;
         }
+        if (fold) t.flags |= mk::TF_FOLD;
         if (i < dn.size()) t.a3 = (dn[i].first << 16) | dn[i].second;
         t.units = (uint16_t)(t.a2 + (t.a3 & 0xFFFF));
         st.push_back(t);
@@ -1140,7 +1156,9 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
         case mk::OP_ATTN: return all_done(qkv_op, l, group_of(t));
         case mk::OP_COMB: return all_done(mk::OP_ATTN, l, t.a1 / HG);
         case mk::OP_O: return all_done(mk::OP_COMB, l, Hkv);
-        case mk::OP_ROUTER: return all_done(p->batch ? mk::OP_BO : mk::OP_O, l, Hkv);
+        case mk::OP_ROUTER:
+          if (t.flags & mk::TF_FOLD) return all_done(mk::OP_COMB, l, Hkv) && (l == 0 || all_done(ffn_op, l - 1, Hkv));
+          return all_done(p->batch ? mk::OP_BO : mk::OP_O, l, Hkv);
         case mk::OP_EXPERT: return all_done(mk::OP_O, l, Hkv) && (!moe || all_done(mk::OP_ROUTER, l, Hkv));
         case mk::OP_LM: return all_done(mk::OP_EXPERT, L - 1, Hkv);
         case mk::OP_FINAL: return all_done(mk::OP_LM, 0, Hkv);

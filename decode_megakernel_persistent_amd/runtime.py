@@ -12,10 +12,10 @@ import torch
 
 from . import (
     MK_BUF_O, MK_BUF_Q, MK_BUF_RLOG, MK_BUF_XATTN, MK_BUF_XFFN,
-    MK_PLAN_ATTN_QUEUE, MK_PLAN_CHANGED_COUNTERS, MK_PLAN_CHANGED_IMAGE, MK_PLAN_CHANGED_WORKSPACE,
+    MK_PLAN_ATTN_QUEUE, MK_PLAN_NO_ROUTER_FOLD, MK_PLAN_CHANGED_COUNTERS, MK_PLAN_CHANGED_IMAGE, MK_PLAN_CHANGED_WORKSPACE,
     MkError, MK_OK, mk_decode_step, mk_decode_step_static, mk_io, mk_kv, mk_kv_pool_elems, mk_plan,
     mk_plan_buffer, mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks,
-    mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_stream_copy,
+    mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_stream_copy, mk_router_fold,
     mk_sampling, mk_step_status, mk_weights, model_desc,
 )
 
@@ -89,6 +89,17 @@ class Decoder:
         self.n_pages = n_pages
         self.W = weights
         self.epoch = 0
+        # batch-1 MoE plans read the folded router W_r diag(g) W_o: made once
+        # per weight set and kept in the weights dict
+        self.router_folded = (self.B == 1 and self.m["n_experts"] > 0
+                              and not (plan_flags & MK_PLAN_NO_ROUTER_FOLD))
+        if self.router_folded and weights.get("router_fold") is None:
+            m = self.m
+            fold = torch.empty((m["n_layers"], m["n_experts"], m["n_q_heads"] * m["head_dim"]),
+                               dtype=torch.float32, device=dev)
+            w0 = mk_weights(*[_ptr(weights.get(k)) for k, _ in mk_weights._fields_])
+            mk_router_fold(self.desc, w0, fold.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+            weights["router_fold"] = fold
         self._w = mk_weights(*[_ptr(weights.get(k)) for k, _ in mk_weights._fields_])
         self._set_rope(bound)
         self.trace = None
@@ -230,7 +241,13 @@ class Decoder:
         return self._current(MK_BUF_XFFN, layer, (self.B, self.m["hidden"]))
 
     def router_logits(self, layer):
-        return self._current(MK_BUF_RLOG, layer, (self.B, self.m["n_experts"]))
+        """Router logits [B][E]. A folded router stores them before the
+        RMSNorm's 1/rms of the hidden state after attention, applied here."""
+        r = self._current(MK_BUF_RLOG, layer, (self.B, self.m["n_experts"]))
+        if self.router_folded:
+            x = self.hidden_after_attn(layer).double()
+            r = (r.double() / torch.sqrt((x * x).mean(dim=1, keepdim=True) + self.m["rms_eps"])).float()
+        return r
 
     def queries(self, layer):
         return self._current(MK_BUF_Q, layer, (self.B, self.m["n_q_heads"], self.m["head_dim"]))

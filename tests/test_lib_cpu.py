@@ -510,3 +510,37 @@ def test_tagged_pair_reads_stay_8_byte_loads(tmp_path):
     assert coherent, "no device-coherent buffer loads found"
     assert all("buffer_load_dwordx2" in l for l in coherent), [l for l in coherent if "dwordx2" not in l][:3]
     assert not any("buffer_load_dwordx4" in l for l in loads)
+
+
+TF_FOLD = 32
+
+
+@pytest.mark.parametrize("name", ["small_moe", "moe48_b1_8k"])
+def test_folded_router_runs_beside_the_o_projection(name):
+    """Batch-1 MoE plans put the router tasks (flagged TF_FOLD) into the O
+    stage on units of their own, and flag the expert tasks that apply the
+    RMSNorm scale; MK_PLAN_NO_ROUTER_FOLD keeps the separate router stage."""
+    for flags, folded in ((0, True), (mk.MK_PLAN_NO_ROUTER_FOLD, False)):
+        w, pool, p, bound = build_plan(name, 256, flags)
+        try:
+            n_cu, _, cu_off, tasks = decode_plan(mk.mk_plan_export(p))
+            L = w["model"]["n_layers"]
+            rt = tasks[tasks["op"] == OP_ROUTER]
+            ex = tasks[tasks["op"] == OP_EXPERT]
+            assert bool(((rt["flags"] & TF_FOLD) != 0).all()) == folded
+            assert bool(((ex["flags"] & TF_FOLD) != 0).all()) == folded
+            if folded:
+                assert (rt["a2"] <= 4).all()            # four expert rows per task at most
+                for l in (0, L - 1):
+                    # one O or router task per unit: each unit's list has exactly one of them
+                    units = []
+                    for cu in range(n_cu):
+                        lst = tasks[cu_off[cu]:cu_off[cu + 1]]
+                        k = ((lst["layer"] == l) & ((lst["op"] == OP_O) | (lst["op"] == OP_ROUTER))).sum()
+                        units.append(int(k))
+                    assert units == [1] * n_cu
+            mk.mk_plan_validate(p)
+            mk.mk_plan_simulate(p, 3, 2)
+        finally:
+            mk.mk_plan_free(p)
+            mk.mk_pool_free(pool)
