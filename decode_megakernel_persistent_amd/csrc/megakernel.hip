@@ -672,7 +672,8 @@ static_assert(NWAVE * 8 * 128 * 4 + STAGE_PAGES * 4 * 128 * 16 <= NWAVE * STAGE_
 // loads: at the start of the unit's expert task, while it waits for the
 // routing decision and HBM is otherwise idle, so that the split computes from
 // LDS as soon as its queries arrive. The split's own wave w waits for the
-// transfer (vmcnt).
+// transfer (vmcnt). (Issued after the routing gather instead, the step was
+// 2 % slower.)
 template <int D>
 __device__ __forceinline__ void stage_kv(Ctx& c, const Task& ta, uint32_t ti_a) {
   KAC& a = c.a;
@@ -1208,80 +1209,61 @@ __device__ __forceinline__ bool task_router(Ctx& c, const Task& t) {
 }
 
 // Router logits before the RMSNorm's 1/rms scale (TF_FOLD, batch 1): rows
-// r0 .. r0 + n of W_r (g * x) + F o, where x is the layer input, o the
-// attention output and F = W_r diag(g) W_o (fp32, mk_router_fold). The router
-// reads RMSNorm(x + W_o o), so this equals its logits times rms(x + W_o o);
-// it needs only what the O tasks need and runs beside them, and the expert
-// tasks apply the scale, which they compute for their own input anyway.
-template <int CPL, int TC>
+// r0 .. r0 + n of F [x | o], where x is the layer input, o the attention
+// output and F = [W_r diag(g) | W_r diag(g) W_o] (fp32, mk_router_fold). The
+// router reads RMSNorm(x + W_o o), so this equals its logits times
+// rms(x + W_o o); it needs only what the O tasks need and runs beside them,
+// and the expert tasks apply the scale, which they compute for their own
+// input anyway. One fp32 GEMV: the rows' chunks are requested up front, the
+// inputs gathered behind them, then dots, wave sums and one barrier.
 __device__ __forceinline__ bool task_router_fold(Ctx& c, const Task& t) {
-  constexpr int RPW = GEMV_REG_CHUNKS / CPL < GEMV_RPW_MAX ? GEMV_REG_CHUNKS / CPL : GEMV_RPW_MAX;
   constexpr int FR = 4;  // folded rows per task (the planner gives at most four)
-  constexpr int FQ = 4;  // 16-byte chunks of a folded row per thread (Hq d <= 8192)
+  constexpr int FQ = 4;  // 16-byte chunks of a folded row per thread (H + Hq d <= 8192)
   KAC& a = c.a;
   Smem& s = c.s;
-  const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H, K = a.Hq * a.D, K4 = K / 4;
-  const uint16_t* W = a.router + (size_t)l * a.E * H;
-  Tile<CPL, RPW, TC> tile;
-  tile.issue(n, [&](int j) { return (const uint4*)(W + (size_t)(r0 + j) * H); });
-  const float4* F = (const float4*)(a.rfold + ((size_t)l * a.E + r0) * K);
+  const int l = t.layer, r0 = t.a1, n = t.a2, H = a.H, K = a.Hq * a.D, KW = (H + K) / 4;
+  const float4* F = (const float4*)(a.rfold + ((size_t)l * a.E + r0) * (H + K));
   float4 fr[FR][FQ];
 #pragma unroll
   for (int r = 0; r < FR; ++r)
 #pragma unroll
     for (int q = 0; q < FQ; ++q) {
       const int i = tid() + q * NT;
-      fr[r][q] = r < n && i < K4 ? F[(size_t)r * K4 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      fr[r][q] = r < n && i < KW ? F[(size_t)r * KW + i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  Gains gn;
-  gn.load(a.ffn_norm + (size_t)l * H, H);
-  // s.vec = [x (H) | o (K)]
-  float* ov = s.vec + H;
+  // s.vec = [x (H) | o (K)], fp32
   if (l == 0) {
     const uint16_t* e = a.embed + (size_t)token_row(a, 0) * H;
     for (int i = tid(); i < H; i += NT) s.vec[i] = bf2f(e[i]);
-    if (!gather<8>(c, a.o + (size_t)l * a.s_o, K, ov, 1)) return false;
+    if (!gather<8>(c, a.o + (size_t)l * a.s_o, K, s.vec + H, 1)) return false;
   } else {
     if (!gather2<6>(c, a.x + (size_t)(l - 1) * a.s_x, H, a.o + (size_t)l * a.s_o, H + K, s.vec, 1)) return false;
   }
-  // x * g into split form (no norm)
-  if (tid() < H / 8) {
-    float x[8];
-    *(float4*)x = *(const float4*)(s.vec + 8 * tid());
-    *(float4*)(x + 4) = *(const float4*)(s.vec + 8 * tid() + 4);
-    const uint32_t gw[4] = {gn.g.x, gn.g.y, gn.g.z, gn.g.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= (e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1]);
-    uint4 hi, lo;
-    split8(x, hi, lo);
-    *(uint4*)(s.vec + 8 * tid()) = hi;
-    *(uint4*)(s.vec + 8 * tid() + 4) = lo;
-  }
-  lds_barrier();
-  tile.dots(s.vec, s.out);
   float acc[FR];
 #pragma unroll
-  for (int r = 0; r < FR; ++r) {
-    acc[r] = 0.f;
+  for (int r = 0; r < FR; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int q = 0; q < FQ; ++q) {
-      const int i = tid() + q * NT;
-      if (i < K4) {
-        const float4 o4 = *(const float4*)(ov + 4 * i);
-        acc[r] = fmaf(fr[r][q].x, o4.x, acc[r]);
-        acc[r] = fmaf(fr[r][q].y, o4.y, acc[r]);
-        acc[r] = fmaf(fr[r][q].z, o4.z, acc[r]);
-        acc[r] = fmaf(fr[r][q].w, o4.w, acc[r]);
+  for (int q = 0; q < FQ; ++q) {
+    const int i = tid() + q * NT;
+    if (i < KW) {
+      const float4 v = *(const float4*)(s.vec + 4 * i);
+#pragma unroll
+      for (int r = 0; r < FR; ++r) {
+        acc[r] = fmaf(fr[r][q].x, v.x, acc[r]);
+        acc[r] = fmaf(fr[r][q].y, v.y, acc[r]);
+        acc[r] = fmaf(fr[r][q].z, v.z, acc[r]);
+        acc[r] = fmaf(fr[r][q].w, v.w, acc[r]);
       }
     }
-    acc[r] = wave_sum(acc[r]);
   }
+#pragma unroll
+  for (int r = 0; r < FR; ++r) acc[r] = wave_sum(acc[r]);
   if ((tid() & 63) == 0)
 #pragma unroll
     for (int r = 0; r < FR; ++r) s.red[r * NWAVE + (tid() >> 6)] = acc[r];
   lds_barrier();
   if (tid() < n) {
-    float v = s.out[tid()];
+    float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) v += s.red[tid() * NWAVE + w];
     st_tagged(a.rlog + (size_t)l * a.s_rlog + r0 + tid(), v, a.epoch);
@@ -2540,7 +2522,7 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
             case OP_QKV: ok = task_qkv<CH, TCH, HD>(c, t); break;
             case OP_O: ok = task_o<CO, TCO>(c, t); break;
             case OP_ROUTER:
-              ok = (t.flags & TF_FOLD) ? task_router_fold<CH, TCH>(c, t) : task_router<CH, TCH>(c, t);
+              ok = (t.flags & TF_FOLD) ? task_router_fold(c, t) : task_router<CH, TCH>(c, t);
               break;
             case OP_EXPERT: ok = task_expert<CH, TCH, CF, TCF>(c, t); break;
             case OP_LM: ok = task_lm<CH, TCH>(c, t); break;
@@ -2599,6 +2581,7 @@ __global__ __launch_bounds__(256) void mk_router_fold_kernel(const uint16_t* __r
   __shared__ float Bs[32][64];
   const int l = blockIdx.z, e0 = blockIdx.y * 32, j0 = blockIdx.x * 64;
   const int te = threadIdx.x / 16, tj = threadIdx.x % 16;
+  const size_t ld = (size_t)H + K;  // output row: [R diag(g) (H) | R diag(g) O (K)]
   const uint16_t* Rl = R + (size_t)l * E * H;
   const uint16_t* gl = g + (size_t)l * H;
   const uint16_t* Ol = O + (size_t)l * H * K;
@@ -2630,8 +2613,19 @@ __global__ __launch_bounds__(256) void mk_router_fold_kernel(const uint16_t* __r
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = e0 + 2 * te + r, j = j0 + 4 * tj + q;
-      if (e < E && j < K) out[((size_t)l * E + e) * K + j] = acc[r][q];
+      if (e < E && j < K) out[((size_t)l * E + e) * ld + H + j] = acc[r][q];
     }
+}
+
+// The first H columns of mk_router_fold's rows: R[l][e][h] g[l][h] (exact in fp32).
+__global__ __launch_bounds__(256) void mk_router_scale_kernel(const uint16_t* __restrict__ R,
+                                                              const uint16_t* __restrict__ g,
+                                                              float* __restrict__ out, int L, int E, int H, int K) {
+  const size_t n = (size_t)L * E * H, stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const size_t h = i % H, le = i / H, l = le / E;
+    out[le * ((size_t)H + K) + h] = bf2f(R[i]) * bf2f(g[l * H + h]);
+  }
 }
 
 // Zero-fill of n 16-byte words (a kernel, not a memset node, so that a
@@ -2684,6 +2678,10 @@ extern "C" mk_status mk_router_fold(const mk_model_desc* m, const mk_weights* w,
   if (!w->router || !w->ffn_norm || !w->w_o) return fail(MK_EINVAL, "mk_router_fold: missing weight pointer");
   const int E = m->n_experts, H = m->hidden, K = m->n_q_heads * m->head_dim, L = m->n_layers;
   if (E <= 0 || H <= 0 || K <= 0 || L <= 0) return fail(MK_EINVAL, "mk_router_fold: bad shape");
+  if ((H + K) % 4 || H + K > mk::dev::LDS_VEC)
+    return fail(MK_EUNSUPPORTED, "mk_router_fold: hidden + heads x dim must be a multiple of 4, at most 8192");
+  hipLaunchKernelGGL(mk::dev::mk_router_scale_kernel, dim3(1024), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)w->router, (const uint16_t*)w->ffn_norm, out, L, E, H, K);
   hipLaunchKernelGGL(mk::dev::mk_router_fold_kernel, dim3((K + 63) / 64, (E + 31) / 32, L), dim3(256), 0,
                      (hipStream_t)stream, (const uint16_t*)w->router, (const uint16_t*)w->ffn_norm,
                      (const uint16_t*)w->w_o, out, E, H, K);

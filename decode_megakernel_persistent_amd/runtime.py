@@ -95,7 +95,7 @@ class Decoder:
                               and not (plan_flags & MK_PLAN_NO_ROUTER_FOLD))
         if self.router_folded and weights.get("router_fold") is None:
             m = self.m
-            fold = torch.empty((m["n_layers"], m["n_experts"], m["n_q_heads"] * m["head_dim"]),
+            fold = torch.empty((m["n_layers"], m["n_experts"], m["hidden"] + m["n_q_heads"] * m["head_dim"]),
                                dtype=torch.float32, device=dev)
             w0 = mk_weights(*[_ptr(weights.get(k)) for k, _ in mk_weights._fields_])
             mk_router_fold(self.desc, w0, fold.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)

@@ -115,10 +115,10 @@ typedef struct mk_plan_opts {
 #define MK_PLAN_PREFILL 4
 /* Batch-1 MoE plans compute the router logits beside the O projection:
  * since the router reads RMSNorm(x + W_o o), its logits before the norm's
- * 1/rms scale are W_r (g * x) + (W_r diag(g) W_o) o, which needs only the
- * layer input x and the attention output o; the expert tasks apply the
- * scale, which they compute anyway. The product W_r diag(g) W_o is made once
- * by mk_router_fold. This flag keeps the router as its own stage after O. */
+ * 1/rms scale are [W_r diag(g) | W_r diag(g) W_o] [x | o], which needs only
+ * the layer input x and the attention output o; the expert tasks apply the
+ * scale, which they compute anyway. The folded matrix is made once by
+ * mk_router_fold. This flag keeps the router as its own stage after O. */
 #define MK_PLAN_NO_ROUTER_FOLD 8
 
 typedef struct mk_plan mk_plan_t;   /* opaque host object */
@@ -137,7 +137,8 @@ typedef struct mk_weights {
   const void* down;        /* [L][E][hidden][F] (MoE) or [L][hidden][ffn] */
   const void* final_norm;  /* [hidden] */
   const void* lm_head;     /* [vocab][hidden] (untied) */
-  const float* router_fold; /* fp32 [L][E][Hq d]: W_r diag(ffn_norm) W_o per layer, made by
+  const float* router_fold; /* fp32 [L][E][hidden + Hq d]: per layer and expert the row
+                               [W_r diag(ffn_norm) | W_r diag(ffn_norm) W_o], made by
                                mk_router_fold from the weights above; read by batch-1 MoE plans
                                (unless MK_PLAN_NO_ROUTER_FOLD), NULL otherwise */
 } mk_weights;
@@ -232,11 +233,14 @@ mk_status mk_stream_copy(void* dst, const void* src, size_t bytes, void* stream)
  * in fp64 and rounded to fp32. Host outputs of n_pos*d/2 floats each. */
 mk_status mk_rope_table(float theta, int32_t head_dim, int32_t n_pos, float* cos_out,
                         float* sin_out);
-/* out[l][e][j] = sum_h W_r[l][e][h] * ffn_norm[l][h] * W_o[l][h][j] (fp32,
- * [L][E][Hq d], device), from w->router, w->ffn_norm and w->w_o; enqueued on
- * hip_stream. Needed once per set of weights by batch-1 MoE plans (see
- * MK_PLAN_NO_ROUTER_FOLD): each term is a product of three bf16 values, exact
- * in fp32, summed in fp32. MK_EINVAL for a dense model or a missing pointer. */
+/* The folded router (fp32 [L][E][hidden + Hq d], device): row (l, e) is
+ * out[h] = W_r[l][e][h] * ffn_norm[l][h] for h < hidden, then
+ * out[hidden + j] = sum_h W_r[l][e][h] * ffn_norm[l][h] * W_o[l][h][j], from
+ * w->router, w->ffn_norm and w->w_o; enqueued on hip_stream. Needed once per
+ * set of weights by batch-1 MoE plans (see MK_PLAN_NO_ROUTER_FOLD): each term
+ * is a product of bf16 values, exact in fp32, summed in fp32. MK_EINVAL for a
+ * dense model or a missing pointer; MK_EUNSUPPORTED if hidden + Hq d is not a
+ * multiple of 4 or exceeds 8192. */
 mk_status mk_router_fold(const mk_model_desc* m, const mk_weights* w, float* out, void* hip_stream);
 /* Elements (bf16) of a KV pool of n_pages pages. */
 int64_t mk_kv_pool_elems(const mk_model_desc* m, int64_t n_pages);

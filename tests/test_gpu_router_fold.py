@@ -1,6 +1,7 @@
 """The folded router (batch-1 MoE) on the GPU.
 
-- mk_router_fold against the product W_r diag(g) W_o in fp64 from the host
+- mk_router_fold: its first columns W_r diag(g) exactly, and the product
+  W_r diag(g) W_o against fp64 from the host
   weights (each term is a product of three bf16 values, exact in fp32; the
   fp32 sums of H = 1024 terms carry a rounding walk of about sqrt(H) 2^-24,
   2e-6 of the result's scale, so 1e-5 is the bar), with non-unit gains so
@@ -27,15 +28,17 @@ def test_fold_equals_the_fp64_product():
     g = torch.Generator().manual_seed(3)
     gains = (0.5 + torch.rand((L, H), generator=g)).to(torch.bfloat16)
     W["ffn_norm"] = gains.cuda()
-    out = torch.empty((L, E, K), dtype=torch.float32, device="cuda")
+    out = torch.empty((L, E, H + K), dtype=torch.float32, device="cuda")
     w = mk.mk_weights(*[W[k].data_ptr() if W.get(k) is not None else None for k, _ in mk.mk_weights._fields_])
     mk.mk_router_fold(mk.model_desc(m), w, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     Hw = HostWeights(m, 0)
     for l in range(L):
-        want = (Hw.router(l).double() * gains[l].double()[None, :]) @ Hw.wo(l).double()
+        rg = Hw.router(l).double() * gains[l].double()[None, :]
         got = out[l].cpu().double()
-        err = ((got - want).abs().max() / want.abs().max()).item()
+        assert torch.equal(got[:, :H], rg), f"layer {l}: W_r diag(g) is not exact"
+        want = rg @ Hw.wo(l).double()
+        err = ((got[:, H:] - want).abs().max() / want.abs().max()).item()
         assert err < 1e-5, f"layer {l}: fold rel err {err}"
 
 
