@@ -185,6 +185,7 @@ MK_PLAN_ATTN_QUEUE = 1
 MK_PLAN_NO_ATTN_QUEUE = 2
 MK_PLAN_PREFILL = 4
 MK_PLAN_NO_ROUTER_FOLD = 8
+MK_PLAN_NO_EXPERT_SHARE = 16
 
 
 def mk_plan(desc, seq_lens, page_table, max_pages, bound, n_cu=0, attn_split_pages=0, flags=0,

@@ -2219,6 +2219,9 @@ struct ExpLds {
   float ids[MAX_BATCH * 16];
   int list[MAX_BATCH * 16];
   int wave_cnt[NWAVE];
+  int ecnt[MAX_SHARE_EXPERTS];  // sequences routed to each expert (TF_SHARE)
+  int ne[MAX_SHARE_EXPERTS];    // the experts with any, ascending
+  int n_ne;
 };
 static_assert(sizeof(ExpLds) <= sizeof(float) * LDS_VEC + sizeof(uint4) * NWAVE * STAGE_CHUNKS * 64,
               "expert LDS exceeds the overlaid areas");
@@ -2236,42 +2239,43 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
   KAC& a = c.a;
   Smem& s = c.s;
   ExpLds& X = *(ExpLds*)&s;
-  const int l = t.layer, e = t.a0, f0 = t.a1, nf = t.a2;
-  const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
+  const int l = t.layer;
   const int H = a.H, F = a.F, KK = a.dense ? 1 : a.K, EE = a.dense ? 1 : a.E, B = a.B;
   const int th = tid(), lane = th & 63, w = th >> 6;
-  // the routed list
-  int ns = 0;
-  if (a.dense) {
-    for (int b = th; b < B; b += NT) X.list[b] = b;
-    ns = B;
-    lds_barrier();
-  } else {
-    const int n = B * KK;  // <= NT (checked by the planner)
-    float* ids = X.ids;
-    if (!gather_fn<1>(c, n, [&](int i) { return a.route + (size_t)l * a.s_route + (size_t)i * 2; }, ids, 0))
+  const int n = B * KK;  // routed (sequence, slot) entries, <= NT (checked by the planner)
+  if (!a.dense) {
+    if (!gather_fn<1>(c, n, [&](int i) { return a.route + (size_t)l * a.s_route + (size_t)i * 2; }, X.ids, 0))
       return false;
-    const bool mine = th < n && __float_as_int(ids[th]) == e;
+  }
+  // the routed list of expert e (entries b * KK + slot, ascending) into X.list; uniform count
+  auto routed = [&](int e) -> int {
+    if (a.dense) {
+      for (int b = th; b < B; b += NT) X.list[b] = b;
+      lds_barrier();
+      return B;
+    }
+    const bool mine = th < n && __float_as_int(X.ids[th]) == e;
     const uint64_t m = __ballot(mine);
     if (lane == 0) X.wave_cnt[w] = __popcll(m);
     lds_barrier();
-    int off = 0;
+    int off = 0, ns = 0;
     for (int q = 0; q < w; ++q) off += X.wave_cnt[q];
     for (int q = 0; q < NWAVE; ++q) ns += X.wave_cnt[q];
     if (mine) X.list[off + __popcll(m & ((1ull << lane) - 1ull))] = th;
     lds_barrier();
-  }
-  if (ns == 0) return true;
-  mark(c, 0);
+    return ns;
+  };
   Gains gn;
   gn.load(a.ffn_norm + (size_t)l * H, H);
-  const uint16_t* Wg = a.gate + ((size_t)l * EE + e) * F * H;
-  const uint16_t* Wu = a.up + ((size_t)l * EE + e) * F * H;
-  const uint16_t* Wd = a.down + ((size_t)l * EE + e) * H * F;
   const int ldh = exp_ld(H), ldf = exp_ld(F);
   const int kq = lane >> 4, r16 = lane & 15;
-  // gate/up: rows 2f (gate) and 2f + 1 (up) of FFN row f0 + f
-  if (nf > 0)
+  // gate/up rows of FFN rows f0 .. f0 + nf of expert e, for its routed sequences
+  auto gateup = [&](int e, int f0, int nf) -> bool {
+    const int ns = routed(e);
+    if (ns == 0 || nf == 0) return true;
+    const uint16_t* Wg = a.gate + ((size_t)l * EE + e) * F * H;
+    const uint16_t* Wu = a.up + ((size_t)l * EE + e) * F * H;
+    // rows 2f (gate) and 2f + 1 (up) of FFN row f0 + f
     for (int g0 = 0; g0 < ns; g0 += EXP_GROUP) {
       const int ng = min(EXP_GROUP, ns - g0);
       // column q at the padded stride
@@ -2299,9 +2303,13 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
         });
       lds_barrier();
     }
-  mark(c, 1);
-  // down: rows r0 .. r0 + nr over the full activations of each routed slot
-  if (nr > 0)
+    return true;
+  };
+  // down rows r0 .. r0 + nr of expert e over the full activations of each routed slot
+  auto down = [&](int e, int r0, int nr) -> bool {
+    const int ns = routed(e);
+    if (ns == 0 || nr == 0) return true;
+    const uint16_t* Wd = a.down + ((size_t)l * EE + e) * H * F;
     for (int g0 = 0; g0 < ns; g0 += EXP_GROUP) {
       const int ng = min(EXP_GROUP, ns - g0);
       for (int q = 0; q < ng; ++q)
@@ -2322,6 +2330,67 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
         });
       lds_barrier();
     }
+    return true;
+  };
+  mark(c, 0);
+  if (!(t.flags & TF_SHARE)) {
+    // one expert (a0), part q: gate/up rows a1 .. a1 + a2, down rows a3
+    const int e = t.a0, f0 = t.a1, nf = t.a2, r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
+    if (!gateup(e, f0, nf)) return false;
+    mark(c, 1);
+    if (!down(e, r0, nr)) return false;
+    mark(c, 2);
+    return true;
+  }
+  // Share aux of a1: list the experts any sequence chose (ascending), then
+  // take rows [i T_g / a1, (i + 1) T_g / a1) of their concatenated gate/up
+  // rows (8 FFN rows per unit) and likewise of their down rows (16 per unit)
+  const int E = a.E;
+  for (int i = th; i < E; i += NT) X.ecnt[i] = 0;
+  lds_barrier();
+  if (th < n) {
+    const int id = __float_as_int(X.ids[th]);
+    if (id >= 0 && id < E) atomicAdd(&X.ecnt[id], 1);
+  }
+  lds_barrier();
+  if (w == 0) {
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const bool ne = e < E && X.ecnt[e] > 0;
+      const uint64_t m = __ballot(ne);
+      if (ne) X.ne[base + __popcll(m & ((1ull << lane) - 1ull))] = e;
+      base += __popcll(m);
+    }
+    if (lane == 0) X.n_ne = base;
+  }
+  lds_barrier();
+  const int n_ne = X.n_ne, T = t.a1, me = t.aux;
+  {
+    const int U = F / 8;
+    const int64_t tot = (int64_t)n_ne * U;
+    int64_t u = tot * me / T;
+    const int64_t ub = tot * (me + 1) / T;
+    while (u < ub) {
+      const int i = (int)(u / U), fu = (int)(u % U);
+      const int take = (int)min((int64_t)(U - fu), ub - u);
+      if (!gateup(X.ne[i], 8 * fu, 8 * take)) return false;
+      u += take;
+    }
+  }
+  mark(c, 1);
+  {
+    const int U = H / 16;
+    const int64_t tot = (int64_t)n_ne * U;
+    int64_t u = tot * me / T;
+    const int64_t ub = tot * (me + 1) / T;
+    while (u < ub) {
+      const int i = (int)(u / U), fu = (int)(u % U);
+      const int take = (int)min((int64_t)(U - fu), ub - u);
+      if (!down(X.ne[i], 16 * fu, 16 * take)) return false;
+      u += take;
+    }
+  }
   mark(c, 2);
   return true;
 }

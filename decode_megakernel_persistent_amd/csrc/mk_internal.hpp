@@ -57,8 +57,10 @@ enum Op : uint8_t {
 // rows 0 .. b-1's K and V words and then reads the pool.
 // TF_FOLD (batch-1 MoE): router tasks form the logits before the RMSNorm
 // scale from x and o (W_r (g x) + (W_r diag(g) W_o) o); expert tasks apply it.
+// TF_SHARE (batch MoE): the expert task is share aux of a1 of the layer's
+// expert work over the experts the routing chose (rows assigned on device).
 enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4, TF_LOGITS = 8, TF_PREFILL = 16,
-                           TF_FOLD = 32 };
+                           TF_FOLD = 32, TF_SHARE = 64 };
 
 // Batch QKV tasks: rotary pairs per row block (the rows of a block are 2
 // BQKV_PAIRS), and the words per (reduction block, row block, sequence) of
@@ -72,6 +74,7 @@ constexpr int COMB_BATCH_WORDS = 24576;
 // Attention pages staged ahead of their split: one per wave.
 constexpr int STAGE_PAGES = 8;
 constexpr int STAGE_SCAN = 8;
+constexpr int MAX_SHARE_EXPERTS = 256;  // experts a shared expert task can list
 
 // Pages per attention split when long contexts use the shared split queue.
 constexpr int QUEUE_PAGES = 64;

@@ -128,6 +128,8 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
   int P = std::max(1, n_cu / NE);
   P = std::min(P, std::min(F / 8, H / 16));
   p->n_exp_parts = P;
+  const bool share = moe && NE <= mk::MAX_SHARE_EXPERTS && !(p->opts.flags & MK_PLAN_NO_EXPERT_SHARE);
+  p->expert_share = share;
   if (NE * P > n_cu) return fail(MK_EUNSUPPORTED, "mk_plan: more expert tasks than compute units");
   // an expert task holds EXP_GROUP inputs of width H or F and up to 1024 result rows in LDS
   // expert GEMMs stream the reduction in groups of 8 k-steps of 32
@@ -240,20 +242,32 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
       }
       stages.push_back(tk);
     }
-    {  // BEXP
+    {  // BEXP: fixed (expert, part) per task, or shares of the chosen experts' rows
       std::vector<Task> st;
       const auto fr = split_units(F, 8, P), hr = split_units(H, 16, P);
+      const int T = NE * P;
+      const int64_t W = (int64_t)NE * (F + H);  // outputs per layer: every expert's rows
       for (int e = 0; e < NE; ++e)
         for (int q = 0; q < P; ++q) {
           Task t = mk_task(mk::OP_BEXP, l);
           t.wait_a = moe ? ctr16(p->c_topk[l]) : mk::NO_CTR;
           t.wait_b = ctr16(p->c_o[l]);
           t.signal = ctr16(p->c_expert[l]);
-          t.a0 = e;
-          t.a1 = q < (int)fr.size() ? fr[q].first : 0;
-          t.a2 = q < (int)fr.size() ? fr[q].second : 0;
-          t.a3 = q < (int)hr.size() ? (hr[q].first << 16) | hr[q].second : 0;
-          t.units = (uint16_t)(t.a2 + (t.a3 & 0xFFFF));
+          if (share) {
+            // the device assigns the rows; the counter counts every expert's
+            // rows once per layer, an equal part per task
+            const int i = e * P + q;
+            t.flags |= mk::TF_SHARE;
+            t.aux = (uint16_t)i;
+            t.a1 = T;
+            t.units = (uint16_t)(W * (i + 1) / T - W * i / T);
+          } else {
+            t.a0 = e;
+            t.a1 = q < (int)fr.size() ? fr[q].first : 0;
+            t.a2 = q < (int)fr.size() ? fr[q].second : 0;
+            t.a3 = q < (int)hr.size() ? (hr[q].first << 16) | hr[q].second : 0;
+            t.units = (uint16_t)(t.a2 + (t.a3 & 0xFFFF));
+          }
           st.push_back(t);
         }
       stages.push_back(st);
@@ -954,6 +968,7 @@ void task_outputs(const mk_plan_t* p, const Task& t, Emit&& emit) {
       emit(K_TOPK, t.a0);
       break;
     case mk::OP_BEXP: {
+      if (t.flags & mk::TF_SHARE) break;  // the shares cover every expert's rows once per layer
       for (int f = t.a1; f < t.a1 + t.a2; ++f) emit(K_GATEUP, (int64_t)t.a0 * 1000000 + f);
       const int r0 = t.a3 >> 16, nr = t.a3 & 0xFFFF;
       for (int r = r0; r < r0 + nr; ++r) emit(K_DOWN, (int64_t)t.a0 * 1000000 + r);
@@ -1051,6 +1066,12 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
       }
     }
   }
+  if (p->expert_share)  // the expert shares of a layer cover every expert's rows once
+    for (int l = 0; l < L; ++l)
+      for (int e = 0; e < m.n_experts; ++e) {
+        for (int f = 0; f < p->F; ++f) got[slot(K_GATEUP, l)].push_back((int64_t)e * 1000000 + f);
+        for (int r = 0; r < m.hidden; ++r) got[slot(K_DOWN, l)].push_back((int64_t)e * 1000000 + r);
+      }
   if (p->attn_queue) {  // every split of the queue, once per layer
     const int pg_bound = (p->bound + 15) / 16;
     for (int l = 0; l < L; ++l)

@@ -34,6 +34,7 @@ struct mk_plan {
   int32_t c_lm = -1;
   bool attn_queue = false;
   bool router_fold = false;         // batch-1 MoE: router tasks beside O (TF_FOLD)
+  bool expert_share = false;        // batch MoE: expert rows shared by live routing (TF_SHARE)
 
   int32_t S_max = 0;                // attention splits per (b, g), max over b
   int32_t comb_dim_tasks = 1;       // combine tasks per (b, query head)

@@ -30,6 +30,8 @@ WORKLOADS = {
                              steps=256, pool_pages="sum*1.1"),
     "moe48_b1_256k": dict(model=dict(_MOE48), batch=1, ctx=[262144], steps=256,
                           pool_pages=16500),
+    "moe48_b4_8k": dict(model=dict(_MOE48), batch=4, ctx=[8192, 8192, 8192, 8192], steps=256,
+                        pool_pages="sum*1.1"),
 }
 
 # Batch parity cases on the small shapes: ragged contexts, one of them empty

@@ -120,6 +120,14 @@ typedef struct mk_plan_opts {
  * scale, which they compute anyway. The folded matrix is made once by
  * mk_router_fold. This flag keeps the router as its own stage after O. */
 #define MK_PLAN_NO_ROUTER_FOLD 8
+/* Batch MoE plans share the layer's expert work by live routing: every
+ * expert task reads the routing (which it needs anyway), lists the experts
+ * at least one sequence was routed to, and takes an equal share of their
+ * gate/up rows and of their down rows (the megakernel page, caption of Image
+ * 2: MoE work whose amount depends on the routing goes where processors are
+ * free), so no unit idles on an expert nobody chose. This flag keeps one
+ * fixed (expert, part) per task. */
+#define MK_PLAN_NO_EXPERT_SHARE 16
 
 typedef struct mk_plan mk_plan_t;   /* opaque host object */
 typedef struct mk_pool mk_pool_t;   /* opaque host object */

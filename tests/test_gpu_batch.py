@@ -2,7 +2,8 @@
 
 A batch plan runs the dense projections as MFMA tiles over all sequences, a
 router/top-k task per sequence and expert tasks shared by the sequences
-routed to them. Each case compares every sequence of one step with the
+routed to them; each expert task takes an equal share of the rows of the
+experts the routing chose (one case keeps a fixed expert part per task). Each case compares every sequence of one step with the
 oracle exactly as the batch-1 cases do (greedy token, logits, hidden state
 after every residual, new K/V in the pool, top-k ids, counters), on ragged
 contexts that include an empty one and a single token.
@@ -31,3 +32,10 @@ def test_small_moe_batch32_ragged():
 
 def test_small_moe_batch5_greedy_16():
     greedy_agreement("small_moe_b5", 16)
+
+
+def test_small_moe_batch5_fixed_expert_parts():
+    # every expert task on one fixed (expert, part), not shares of the
+    # experts the routing chose
+    import decode_megakernel_persistent_amd as mk
+    run_step_parity("small_moe_b5", plan_flags=mk.MK_PLAN_NO_EXPERT_SHARE)

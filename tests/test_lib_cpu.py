@@ -38,6 +38,7 @@ OP_TOPK, OP_BEXP, OP_BCOMB, OP_BLM, OP_BFINAL = range(13, 18)
 NO_CTR = 0xFFFF
 TF_QUEUE = 2
 TF_LOGITS = 8
+TF_SHARE = 64
 
 
 def declared_functions():
@@ -178,6 +179,14 @@ def plan_coverage(tasks, m, bound):
             if not int(t["flags"]) & TF_LOGITS:
                 add(("router", l), [(a0, e) for e in range(m["n_experts"])])
             add(("topk", l), [a0])
+        elif op == OP_BEXP and int(t["flags"]) & TF_SHARE:
+            # shares of the layer's expert work, rows assigned on the device
+            # from the routing: together every expert's rows, once per layer
+            if ("share", l) not in queued:
+                queued.add(("share", l))
+                F = m["expert_ffn"] if m["n_experts"] else m["ffn_dim"]
+                add(("gateup", l), [(e, f) for e in range(m["n_experts"]) for f in range(F)])
+                add(("down", l), [(e, r) for e in range(m["n_experts"]) for r in range(m["hidden"])])
         elif op == OP_BEXP:
             # one expert's gate/up rows (expert, FFN row) and down rows (expert, hidden row)
             add(("gateup", l), [(a0, f) for f in range(a1, a1 + a2)])
