@@ -73,7 +73,7 @@ struct Smem {
   int route_ids[16];
   int fail;
   int kv_ti;                 // task index of the attention split whose pages are staged (-1: none)
-  int kv_ok[NWAVE];          // wave w's staged page is valid
+  int kv_ok[STAGE_PAGES];    // staged page k of the split is valid
   int kv_ids[ATT_IDS + 1];   // its first ATT_IDS page ids, then the sequence's position
   uint32_t qnext;      // attention queue: the split this workgroup takes next
   int tok;             // sampling: the drawn token
@@ -236,12 +236,12 @@ __device__ __forceinline__ bool gather_split(Ctx& c, const uint64_t* src, int n,
 #pragma unroll
     for (int k = 0; k < MAXP; ++k) {
       const int i = base + 2 * (t + k * NT);
-      const uint32_t h0 = f2bf(v[2 * k]), h1 = f2bf(v[2 * k + 1]);
-      const uint32_t l0 = f2bf(v[2 * k] - bf2f(h0)), l1 = f2bf(v[2 * k + 1] - bf2f(h1));
+      uint32_t hw, lw;
+      split2(v[2 * k], v[2 * k + 1], hw, lw);
       if (ok && i < n) {
         const int ch = i >> 3, e = i & 7;
-        dw[8 * ch + (e >> 1)] = h0 | (h1 << 16);
-        dw[8 * ch + 4 + (e >> 1)] = l0 | (l1 << 16);
+        dw[8 * ch + (e >> 1)] = hw;
+        dw[8 * ch + 4 + (e >> 1)] = lw;
       }
     }
   }
@@ -636,7 +636,7 @@ __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
       st_tagged(qd + i, r0, a.epoch);
       st_tagged(qd + i + D / 2, r1, a.epoch);
     } else {
-      const uint32_t b0 = f2bf(r0), b1 = f2bf(r1);
+      const uint32_t bb = pk_bf16(r0, r1), b0 = bb & 0xFFFFu, b1 = bb >> 16;
       uint64_t* kn = a.kvn + (size_t)l * a.s_kvn + ((size_t)g * 2 + (sec - 1)) * D;
       st_tagged(kn + i, __uint_as_float(b0), a.epoch);
       st_tagged(kn + i + D / 2, __uint_as_float(b1), a.epoch);
@@ -657,18 +657,21 @@ __device__ __forceinline__ bool task_qkv(Ctx& c, const Task& t) {
   return true;
 }
 
-// Staged attention pages: wave w's page block (one (page, layer, kv head)
-// block of 2 x 16 x D bf16, in pool order) at the end of the shared area,
-// after the attention's per-wave partials.
+// Staged attention page k of a split (one (page, layer, kv head) block of
+// 2 x 16 x D bf16, in pool order) in the shared area. The split's per-wave
+// partials overlay the first pages: every wave reads its staged pages into
+// registers before the query gather's barrier and writes its partial after
+// it.
 template <int D>
-__device__ __forceinline__ uint4* staged_page(Smem& s, int w) {
-  return s.stage + (NWAVE * 8 * D * 4) / 16 + w * (4 * D);
+__device__ __forceinline__ uint4* staged_page(Smem& s, int k) {
+  return s.stage + k * (4 * D);
 }
-static_assert(NWAVE * 8 * 128 * 4 + STAGE_PAGES * 4 * 128 * 16 <= NWAVE * STAGE_CHUNKS * 64 * 16,
-              "staged pages and attention partials share the staging area");
+static_assert(STAGE_PAGES * 4 * 128 * 16 <= NWAVE * STAGE_CHUNKS * 64 * 16, "staged pages fit the shared area");
+static_assert(NWAVE * 8 * 128 * 4 <= NWAVE * STAGE_CHUNKS * 64 * 16, "attention partials fit the shared area");
 
 // Request the first pages of this unit's next attention split ta (task index
-// ti_a of this unit's list) into LDS, wave w taking page w, with direct-to-LDS
+// ti_a of this unit's list) into LDS, wave w taking pages w and w + NWAVE
+// (the ones it computes first), with direct-to-LDS
 // loads: at the start of the unit's expert task, while it waits for the
 // routing decision and HBM is otherwise idle, so that the split computes from
 // LDS as soon as its queries arrive. The split's own wave w waits for the
@@ -680,14 +683,22 @@ __device__ __forceinline__ void stage_kv(Ctx& c, const Task& ta, uint32_t ti_a) 
   Smem& s = c.s;
   const int w = tid() >> 6, lane = tid() & 63;
   const int b = ta.a0, g = ta.a1, pg0 = ta.a2, npg = ta.a3, l = ta.layer;
-  bool ok = false;
-  if (w < min(npg, STAGE_PAGES)) {
-    const int32_t phys = a.page_table[(size_t)b * a.max_pages + pg0 + w];
-    ok = phys >= 0 && phys < a.n_pages;
-    if (ok) {
-      const uint4* src = (const uint4*)(a.pool + (size_t)phys * a.page_stride + (size_t)l * a.layer_stride +
+  const int nst = min(npg, STAGE_PAGES);
+  int32_t phys[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int k = w + NWAVE * j;
+    phys[j] = k < nst ? a.page_table[(size_t)b * a.max_pages + pg0 + k] : -1;
+  }
+  bool ok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int k = w + NWAVE * j;
+    ok[j] = k < nst && phys[j] >= 0 && phys[j] < a.n_pages;
+    if (ok[j]) {
+      const uint4* src = (const uint4*)(a.pool + (size_t)phys[j] * a.page_stride + (size_t)l * a.layer_stride +
                                         (size_t)g * 2 * 16 * D) + lane;
-      uint4* dst = staged_page<D>(s, w);
+      uint4* dst = staged_page<D>(s, k);
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) dma16(src + 64 * i, lds_addr(dst + 64 * i));
     }
@@ -699,7 +710,10 @@ __device__ __forceinline__ void stage_kv(Ctx& c, const Task& ta, uint32_t ti_a) 
     if (lane < min(npg, ATT_IDS)) dma4(prow + lane, lds_addr(s.kv_ids));
     else if (lane == ATT_IDS) dma4(a.seq_lens + b, lds_addr(s.kv_ids));
   }
-  if (lane == 0) s.kv_ok[w] = ok ? 1 : 0;
+  if (lane == 0) {
+    s.kv_ok[w] = ok[0] ? 1 : 0;
+    if (w + NWAVE < STAGE_PAGES) s.kv_ok[w + NWAVE] = ok[1] ? 1 : 0;
+  }
   if (tid() == 0) s.kv_ti = (int)ti_a;
 }
 
@@ -787,24 +801,29 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       vv[2 * m + 1] = make_uint2(v.z, v.w);
     }
   };
-  // this wave's first page may have been staged in LDS by an earlier task of
-  // this unit (stage_kv): that task waited for loads it issued after the
-  // transfer, so the page has landed
-  const bool staged = cnt > 0 && pre && s.kv_ok[w];
-  if (staged) {
-    const uint4* sp = staged_page<D>(s, w) + lane;
+  // this wave's first two pages may have been staged in LDS by an earlier
+  // task of this unit (stage_kv): that task waited for loads it issued after
+  // the transfer, so the pages have landed
+  bool staged[2];
 #pragma unroll
-    for (int i = 0; i < NK4; ++i) kb[0][i] = sp[64 * i];
+  for (int j = 0; j < 2; ++j) {
+    const int k = w + NWAVE * j;
+    staged[j] = j < cnt && k < STAGE_PAGES && pre && s.kv_ok[k];
+    if (staged[j]) {
+      const uint4* sp = staged_page<D>(s, k) + lane;
 #pragma unroll
-    for (int m = 0; m < NB / 2; ++m) {
-      const uint4 v = sp[2 * D + 64 * m];
-      vb[0][2 * m] = make_uint2(v.x, v.y);
-      vb[0][2 * m + 1] = make_uint2(v.z, v.w);
+      for (int i = 0; i < NK4; ++i) kb[j][i] = sp[64 * i];
+#pragma unroll
+      for (int m = 0; m < NB / 2; ++m) {
+        const uint4 v = sp[2 * D + 64 * m];
+        vb[j][2 * m] = make_uint2(v.x, v.y);
+        vb[j][2 * m + 1] = make_uint2(v.z, v.w);
+      }
     }
   }
 #pragma unroll
   for (int j = 0; j < NBUF; ++j)
-    if (j < cnt && !(j == 0 && staged)) load(kb[j], vb[j], first + j * NWAVE, ph[j]);
+    if (j < cnt && !(j < 2 && staged[j])) load(kb[j], vb[j], first + j * NWAVE, ph[j]);
   if (refill)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -830,20 +849,20 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     const float* qp = qv + (valid ? hh : 0) * D + 8 * kq;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      uint32_t h[8];
+      uint32_t h[4];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const float4 x = valid ? *(const float4*)(qp + 32 * st + 4 * half) : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t hi = f2bf(xs[j]);
-          h[4 * half + j] = lo_part ? f2bf(xs[j] - bf2f(hi)) : hi;
-        }
+        uint32_t hw, lw;
+        split2(x.x, x.y, hw, lw);
+        h[2 * half] = lo_part ? lw : hw;
+        split2(x.z, x.w, hw, lw);
+        h[2 * half + 1] = lo_part ? lw : hw;
       }
-      qop[st] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      qop[st] = make_uint4(h[0], h[1], h[2], h[3]);
     }
   }
+  mark(c, 4);
   float m_run = NEG_INF, l_run = 0.f;
   v4f acc[NB];
 #pragma unroll
@@ -924,12 +943,14 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     ps = xor32_sum(xor16_sum(ps));
     l_run = l_run * alpha + ps;
     m_run = mn;
-    v4s PA, PB;
+    uint32_t pw[4];  // P operand words: page A's tokens 4 kq .. + 3, then page B's
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t ha = f2bf(qa[j]), hb = f2bf(qb[j]);
-      PA[j] = (short)(lo_part ? f2bf(qa[j] - bf2f(ha)) : ha);
-      PB[j] = (short)(lo_part ? f2bf(qb[j] - bf2f(hb)) : hb);
+    for (int j = 0; j < 2; ++j) {
+      uint32_t hw, lw;
+      split2(qa[2 * j], qa[2 * j + 1], hw, lw);
+      pw[j] = lo_part ? lw : hw;
+      split2(qb[2 * j], qb[2 * j + 1], hw, lw);
+      pw[2 + j] = lo_part ? lw : hw;
     }
     // the scale of output row 4 kq + j, i.e. of head (4 kq + j) & 7, whose
     // alpha every lane with r16 & 7 == head holds (lane head, for one)
@@ -946,8 +967,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     // one MFMA 16x16x32 per 16 dims over both pages: reduction index
     // 8 kq + e is token 4 kq + e of page A for e < 4 and of page B for e >= 4,
     // so each lane's own probabilities and V slots form its operands
-    const u2v pa2 = __builtin_bit_cast(u2v, PA), pb2 = __builtin_bit_cast(u2v, PB);
-    const bf16x8 P2 = __builtin_bit_cast(bf16x8, u4v{pa2.x, pa2.y, pb2.x, pb2.y});
+    const bf16x8 P2 = __builtin_bit_cast(bf16x8, u4v{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -1855,11 +1875,11 @@ __device__ __forceinline__ bool mt_tile(Ctx& c, int R, int K, const RowPtr& rowp
       ss = fmaf(x1, x1, ss);
       x0 *= bf_lo(r.g[i]);
       x1 *= bf_hi(r.g[i]);
-      const uint32_t h0 = f2bf(x0), h1 = f2bf(x1);
-      const uint32_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
+      uint32_t hw, lw;
+      split2(x0, x1, hw, lw);
       const int word = ((i * 2 + cb_t) * 64 + kg * 16 + m4) * 4 + jw;
-      ph[word] = h0 | (h1 << 16);
-      pl[word] = l0 | (l1 << 16);
+      ph[word] = hw;
+      pl[word] = lw;
     }
     return true;
   };
@@ -2032,7 +2052,7 @@ __device__ __forceinline__ bool task_bqkv(Ctx& c, const Task& t) {
           st_tagged(qd + i + D / 2, r1, a.epoch);
         }
       } else {
-        const uint32_t b0 = f2bf(r0), b1 = f2bf(r1);
+        const uint32_t bb = pk_bf16(r0, r1), b0 = bb & 0xFFFFu, b1 = bb >> 16;
         if (pass == 1) {
           uint64_t* kn = a.kvn + (size_t)l * a.s_kvn + (((size_t)b * a.Hkv + g) * 2 + (sec - 1)) * D;
           st_tagged(kn + i, __uint_as_float(b0), a.epoch);

@@ -73,10 +73,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f2v_t __attribute__((ext_vector_type(2)));
+// Two fp32 values to packed bf16 bits (x in bits 0..15, y in 16..31), round
+// to nearest even: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  const f2v_t v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// fp32 -> bf16 bits, round to nearest even
+__device__ __forceinline__ uint32_t f2bf(float f) { return pk_bf16(f, 0.f) & 0xFFFFu; }
+// hi/lo bf16 split of a pair: hi = bf16(x) | bf16(y) << 16, lo likewise of
+// the residuals x - hi, y - hi (each residual is exact in fp32)
+__device__ __forceinline__ void split2(float x, float y, uint32_t& hi, uint32_t& lo) {
+  hi = pk_bf16(x, y);
+  lo = pk_bf16(x - bf_lo(hi), y - bf_hi(hi));
 }
 
 // dot of 8 bf16 weights (one 16-byte chunk) with 8 floats
@@ -111,14 +122,11 @@ __device__ __forceinline__ float dot8h(const uint4 w, const uint4 uh, const uint
 
 // hi/lo bf16 split of 8 floats: words (hi of u[2j] | hi of u[2j+1] << 16), then lo.
 __device__ __forceinline__ void split8(const float* u, uint4& hi, uint4& lo) {
-  uint32_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f2bf(u[e]);
-    l[e] = f2bf(u[e] - bf2f(h[e]));
-  }
-  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+  for (int e = 0; e < 4; ++e) split2(u[2 * e], u[2 * e + 1], h[e], l[e]);
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 template <int CTRL, int ROW_MASK = 0xF>

@@ -71,8 +71,9 @@ constexpr int QPART_STRIDE = 2 * BQKV_PAIRS + 2;
 // Words (floats) a batch combine task may gather: the whole shared area.
 constexpr int COMB_BATCH_WORDS = 24576;
 
-// Attention pages staged ahead of their split: one per wave.
-constexpr int STAGE_PAGES = 8;
+// Attention pages staged ahead of their split: the split's first twelve
+// pages (wave w takes pages w and w + 8), 96 KB at a head dim of 128.
+constexpr int STAGE_PAGES = 12;
 constexpr int STAGE_SCAN = 8;
 constexpr int MAX_SHARE_EXPERTS = 256;  // experts a shared expert task can list
 
