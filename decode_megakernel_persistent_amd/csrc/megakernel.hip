@@ -867,7 +867,9 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   v4f acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
-  const float scale = a.attn_scale;
+  // scores in log2 units (scale log2 e), so that every softmax weight is one
+  // 2^x; the partial maxima published below are in the same units
+  const float scale = a.attn_scale * LOG2E_F;
   // the new token's slot of page pg: its K and V come from this step's QKV tasks
   auto patch = [&](uint4 (&kk)[NK4], uint2 (&vv)[NB], int pg) {
     if (pg != cur) return;
@@ -932,12 +934,15 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
                      fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
     mx = xor32_max(xor16_max(mx));
     const float mn = fmaxf(m_run, mx);
-    const float alpha = mn == NEG_INF ? 1.f : expf(m_run - mn);
+    // with no live score yet (mn = -inf) every weight and alpha are 2^-inf = 0
+    // against a zero reference (nothing has been accumulated)
+    const float mz = mn == NEG_INF ? 0.f : mn;
+    const float alpha = exp2_hw(m_run - mz);
     float qa[4], qb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      qa[j] = sa[j] == NEG_INF ? 0.f : expf(sa[j] - mn);
-      qb[j] = sb[j] == NEG_INF ? 0.f : expf(sb[j] - mn);
+      qa[j] = exp2_hw(sa[j] - mz);
+      qb[j] = exp2_hw(sb[j] - mz);
     }
     float ps = ((qa[0] + qa[1]) + (qa[2] + qa[3])) + ((qb[0] + qb[1]) + (qb[2] + qb[3]));
     ps = xor32_sum(xor16_sum(ps));
@@ -1017,7 +1022,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   }
   lds_barrier();
   mark(c, 3);
-  // merge over the waves. Every wave forms the 64 scales exp(m_q,h - M_h) of
+  // merge over the waves. Every wave forms the 64 scales 2^(m_q,h - M_h) of
   // (wave q, head h) in its lanes (lane 8 q + h; M_h = max_q m_q,h, over lanes
   // of equal h: xor 8, 16, 32) and the heads' sums L_h; thread (dim, head
   // pair) then sums its two heads' outputs with the scales as scalars.
@@ -1025,7 +1030,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   const float mq = hw < HG ? mw[wq * 8 + hw] : NEG_INF;
   float Mh = fmaxf(mq, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mq), 0x128, 0xF, 0xF, false)));
   Mh = xor32_max(xor16_max(Mh));
-  const float e = mq == NEG_INF ? 0.f : expf(mq - Mh);
+  const float e = exp2_hw(mq - (Mh == NEG_INF ? 0.f : Mh));
   const float Lh = xor32_sum(xor16_sum(xor8_sum(e * (hw < HG ? lw[wq * 8 + hw] : 0.f))));
   const int PS = D + 2;
   uint64_t* dst0 = a.part + (size_t)l * a.s_part +
@@ -1081,10 +1086,11 @@ __device__ __forceinline__ bool task_comb_heads(Ctx& c, const Task& t) {
     const float* col = sw + hh * PS;
     float M = NEG_INF;
     for (int q = 0; q < S; ++q) M = fmaxf(M, col[q * W + D]);
+    const float Mz = M == NEG_INF ? 0.f : M;  // split maxima are in log2 units
     float L = 0.f, acc = 0.f;
     for (int q = 0; q < S; ++q) {
       const float mq = col[q * W + D];
-      const float e = mq == NEG_INF ? 0.f : expf(mq - M);
+      const float e = exp2_hw(mq - Mz);
       L += e * col[q * W + D + 1];
       acc += e * col[q * W + dim];
     }
@@ -1137,17 +1143,19 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   if (a.trace && tid() == 0) s.tw[3] = now();
   if (s.fail) return false;
   // every wave forms the global max M = max_q m_q and the denominator
-  // L = sum_q exp(m_q - M) l_q on its own (split q in lane q, q + 64, ...), so
-  // the merge needs no barrier before the weighted sums; thread (sg, dim) then
-  // sums exp(m_q - M) o_q[dim] over its splits q = sg, sg + NG, ...
+  // L = sum_q 2^(m_q - M) l_q on its own (split q in lane q, q + 64, ...;
+  // the split maxima are in log2 units), so the merge needs no barrier
+  // before the weighted sums; thread (sg, dim) then sums 2^(m_q - M) o_q[dim]
+  // over its splits q = sg, sg + NG, ...
   const int lane = tid() & 63;
   float M = NEG_INF;
   for (int q = lane; q < S; q += 64) M = fmaxf(M, sw[q * W + nd]);
   M = wave_max_dpp(M);
+  const float Mz = M == NEG_INF ? 0.f : M;
   float L = 0.f;
   for (int q = lane; q < S; q += 64) {
     const float mq = sw[q * W + nd];
-    L += mq == NEG_INF ? 0.f : expf(mq - M) * sw[q * W + nd + 1];
+    L += exp2_hw(mq - Mz) * sw[q * W + nd + 1];
   }
   L = wave_sum(L);
   const int NG = NT / nd, sg = tid() / nd, dim = tid() % nd;
@@ -1155,7 +1163,7 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
   if (sg < NG)
     for (int q = sg; q < S; q += NG) {
       const float mq = sw[q * W + nd];
-      acc += mq == NEG_INF ? 0.f : expf(mq - M) * sw[q * W + dim];
+      acc += exp2_hw(mq - Mz) * sw[q * W + dim];
     }
   float* red = s.out + 1024;
   int nred = NG;

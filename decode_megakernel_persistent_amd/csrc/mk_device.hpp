@@ -73,6 +73,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
+// 2^x with one v_exp_f32 (about 1 ulp; results below 2^-126 flush to 0,
+// 2^-inf = 0): for softmax weights, whose scores are kept in log2 units
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float LOG2E_F = 1.44269504088896341f;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f2v_t __attribute__((ext_vector_type(2)));
 // Two fp32 values to packed bf16 bits (x in bits 0..15, y in 16..31), round
