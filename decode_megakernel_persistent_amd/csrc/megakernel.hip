@@ -1354,46 +1354,12 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
     }
     for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
     lds_barrier();
-    // folded router logits still lack the RMSNorm's 1/rms of x_attn, whose
-    // per-wave sums of squares the gather left in s.red[0 .. NWAVE)
-    float sc = 1.f;
-    if (t.flags & TF_FOLD) {
-      float tot = 0.f;
-#pragma unroll
-      for (int w = 0; w < NWAVE; ++w) tot += s.red[w];
-      sc = 1.0f / sqrtf(tot / (float)H + a.eps);
-    }
     if (tid() < E) {
       int rank = 0;
       for (int q = 0; q < parts; ++q) rank += partial[q * E32 + tid()];
-      if (rank < a.K) {
-        float M = NEG_INF;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.red[NWAVE + w]);
-        s.route_ids[rank] = tid();
-        s.route_w[rank] = expf((lg_[tid()] - M) * sc);  // softmax numerator (see below)
-      }
+      if (rank < a.K) s.route_ids[rank] = tid();
     }
     norm_pack(c, s.vec, H, gn);  // its barrier also publishes the selection
-    if (tid() < a.K) {
-      // weights: softmax over the selection (renormalised), or the probability
-      // of each selected expert (a sum over every expert, off the critical path)
-      float div = 0.f;
-      if (a.norm_topk) {
-        for (int i = 0; i < a.K; ++i) div += s.route_w[i];
-      } else {
-        float M = NEG_INF;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.red[NWAVE + w]);
-        for (int e = 0; e < E; ++e) div += expf((lg_[e] - M) * sc);
-      }
-      const float wn = s.route_w[tid()] / div;
-      s.route_wn[tid()] = wn;  // read after later barriers
-      if (t.flags & TF_WRITE_TOPK) {
-        if (a.topk_ids) a.topk_ids[(size_t)l * a.K + tid()] = s.route_ids[tid()];
-        if (a.topk_w) a.topk_w[(size_t)l * a.K + tid()] = wn;
-      }
-    }
   } else {
     if (tid() == 0) {
       s.route_ids[0] = 0;
@@ -1404,6 +1370,42 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
     for (int q = tid(); q < nr; q += NT) s.res[q] = s.vec[r0 + q];
     norm_pack(c, s.vec, H, gn);
   }
+  // The routing weights (lanes 0 .. K-1 of wave 0) are formed once the
+  // gate/up rows are requested: only the down combine, after later barriers,
+  // reads them. Softmax over the selection (renormalised), or the probability
+  // of each selected expert (a sum over every expert); folded router logits
+  // still lack the RMSNorm's 1/rms of x_attn, whose per-wave sums of squares
+  // the gather left in s.red[0 .. NWAVE), beside the per-wave logit maxima.
+  auto route_weights = [&]() {
+    if (a.dense || tid() >= a.K) return;
+    const int E = a.E;
+    float sc = 1.f;
+    if (t.flags & TF_FOLD) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) tot += s.red[w];
+      sc = 1.0f / sqrtf(tot / (float)H + a.eps);
+    }
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.red[NWAVE + w]);
+    const int id = s.route_ids[tid()];
+    const float num = expf((lg_[id] - M) * sc);  // softmax numerator
+    s.route_w[tid()] = num;  // read back by this wave below (LDS runs a wave's accesses in order)
+    __builtin_amdgcn_wave_barrier();
+    float div = 0.f;
+    if (a.norm_topk) {
+      for (int i = 0; i < a.K; ++i) div += s.route_w[i];
+    } else {
+      for (int e = 0; e < E; ++e) div += expf((lg_[e] - M) * sc);
+    }
+    const float wn = num / div;
+    s.route_wn[tid()] = wn;  // read after later barriers
+    if (t.flags & TF_WRITE_TOPK) {
+      if (a.topk_ids) a.topk_ids[(size_t)l * a.K + tid()] = id;
+      if (a.topk_w) a.topk_w[(size_t)l * a.K + tid()] = wn;
+    }
+  };
   mark(c, 0);
   const int e = s.route_ids[slot];
   const uint16_t* Wg = a.gate + ((size_t)l * EE + e) * F * H;
@@ -1418,11 +1420,13 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
   Tile<CH, RPW_G, TCH> gu;
   Tile<CF, RPW_D, TCF> dn;
   mark(c, 1);
+  if (nf == 0) route_weights();
   for (int fc = 0; fc < nf; fc += capg) {
     const int nfc = min(capg, nf - fc);
     gu.issue(2 * nfc, [&](int j) {
       return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + fc + (j >> 1)) * H);
     });
+    if (fc == 0) route_weights();
     gu.dots(s.vec, s.out);
     lds_barrier();
     mark(c, 3);
