@@ -910,25 +910,31 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
   };
   // Two pages per online-softmax update: their MFMA chains, shuffles and
   // exponentials are independent and overlap. A page index at or past the
-  // live context (the odd page out) contributes nothing.
+  // live context contributes nothing. With two = false (a wave's odd last
+  // page) page B is left out altogether: a wave issues one instruction at a
+  // time and shares its SIMD's vector unit, so work on an empty page would
+  // hold up the waves with two.
   auto compute2 = [&](uint4 (&kA)[NK4], uint2 (&vA)[NB], int pgA, uint4 (&kB)[NK4], uint2 (&vB)[NB],
-                      int pgB) {
+                      int pgB, bool two) {
     patch(kA, vA, pgA);
-    patch(kB, vB, pgB);
+    if (two) patch(kB, vB, pgB);
     v4f SA = {0.f, 0.f, 0.f, 0.f}, SB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const bf16x8 qs = __builtin_bit_cast(bf16x8, qop[st]);
       SA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kA[st]), qs, SA, 0, 0, 0);
-      SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kB[st]), qs, SB, 0, 0, 0);
+      if (two) SB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kB[st]), qs, SB, 0, 0, 0);
     }
     float sa[4], sb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float xa = xor8_sum(SA[j]) * scale;
-      const float xb = xor8_sum(SB[j]) * scale;
       sa[j] = (pgA * 16 + 4 * kq + j) < n_tok ? xa : NEG_INF;
-      sb[j] = (pgB * 16 + 4 * kq + j) < n_tok ? xb : NEG_INF;
+      sb[j] = NEG_INF;
+      if (two) {
+        const float xb = xor8_sum(SB[j]) * scale;
+        sb[j] = (pgB * 16 + 4 * kq + j) < n_tok ? xb : NEG_INF;
+      }
     }
     float mx = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
                      fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
@@ -942,7 +948,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       qa[j] = exp2_hw(sa[j] - mz);
-      qb[j] = exp2_hw(sb[j] - mz);
+      qb[j] = two ? exp2_hw(sb[j] - mz) : 0.f;
     }
     float ps = ((qa[0] + qa[1]) + (qa[2] + qa[3])) + ((qb[0] + qb[1]) + (qb[2] + qb[3]));
     ps = xor32_sum(xor16_sum(ps));
@@ -954,8 +960,11 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       uint32_t hw, lw;
       split2(qa[2 * j], qa[2 * j + 1], hw, lw);
       pw[j] = lo_part ? lw : hw;
-      split2(qb[2 * j], qb[2 * j + 1], hw, lw);
-      pw[2 + j] = lo_part ? lw : hw;
+      pw[2 + j] = 0u;
+      if (two) {
+        split2(qb[2 * j], qb[2 * j + 1], hw, lw);
+        pw[2 + j] = lo_part ? lw : hw;
+      }
     }
     // the scale of output row 4 kq + j, i.e. of head (4 kq + j) & 7, whose
     // alpha every lane with r16 & 7 == head holds (lane head, for one)
@@ -966,9 +975,9 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
       const float hi4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 + j));
       aj[j] = (kq & 1) ? hi4 : lo4;
     }
-    uint32_t mla, mha, mlb, mhb;
+    uint32_t mla, mha, mlb = 0u, mhb = 0u;
     vmask(pgA, mla, mha);
-    vmask(pgB, mlb, mhb);
+    if (two) vmask(pgB, mlb, mhb);
     // one MFMA 16x16x32 per 16 dims over both pages: reduction index
     // 8 kq + e is token 4 kq + e of page A for e < 4 and of page B for e >= 4,
     // so each lane's own probabilities and V slots form its operands
@@ -977,7 +986,7 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[nb][j] *= aj[j];
-      const u4v v2 = {vA[nb].x & mla, vA[nb].y & mha, vB[nb].x & mlb, vB[nb].y & mhb};
+      const u4v v2 = {vA[nb].x & mla, vA[nb].y & mha, two ? vB[nb].x & mlb : 0u, two ? vB[nb].y & mhb : 0u};
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P2, __builtin_bit_cast(bf16x8, v2), acc[nb], 0, 0, 0);
     }
   };
@@ -991,8 +1000,10 @@ __device__ __forceinline__ bool task_attn(Ctx& c, const Task& t) {
     for (int j = 0; j < NBUF; j += 2) {
       const int i = i0 + j;
       if (i < cnt) {
-        compute2(kb[j], vb[j], first + i * NWAVE, kb[j + 1], vb[j + 1],
-                 i + 1 < cnt ? first + (i + 1) * NWAVE : NO_PAGE);
+        if (i + 1 < cnt)
+          compute2(kb[j], vb[j], first + i * NWAVE, kb[j + 1], vb[j + 1], first + (i + 1) * NWAVE, true);
+        else
+          compute2(kb[j], vb[j], first + i * NWAVE, kb[j + 1], vb[j + 1], NO_PAGE, false);
         if (i + NBUF < cnt) load(kb[j], vb[j], first + (i + NBUF) * NWAVE, pid[w + (i + NBUF) * NWAVE]);
         if (i + 1 + NBUF < cnt)
           load(kb[j + 1], vb[j + 1], first + (i + 1 + NBUF) * NWAVE, pid[w + (i + 1 + NBUF) * NWAVE]);
