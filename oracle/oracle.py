@@ -350,13 +350,30 @@ def near_tie(r, k, rel):
     return k < s.numel() and (s[k - 1] - s[k]).item() < rel * s[k - 1].item()
 
 
+def ids_near_tie(r, mine, theirs, rel):
+    """True when the id lists mine and theirs can both be the descending
+    ranking of the softmax probabilities of router logits r, up to rounding:
+    at every slot where they differ, the two experts' probabilities differ by
+    less than rel of the larger. This covers a different k-th expert (the
+    k-th and (k+1)-th nearly tie, as near_tie) and two selected experts in
+    the other order (slot order is the ranking, and fp32 logits summed in
+    another order can rank nearly equal probabilities either way)."""
+    p = softmax(r.double())
+    for a, b in zip(mine, theirs):
+        if a != b:
+            pa, pb = p[int(a)].item(), p[int(b)].item()
+            if abs(pa - pb) >= rel * max(pa, pb):
+                return False
+    return True
+
+
 def decode_step_following(m, W, kv, tokens, other_ids, rel, dt=torch.float32):
     """decode_step, continuing from another implementation's routing where
     the two may both be right.
 
     other_ids[b][l]: the other side's k expert ids of sequence b at layer l.
-    Where the oracle's own top-k differs from them and the oracle's choice is
-    a near-tie (near_tie(router logits, k, rel)), the other side's ids are
+    Where the oracle's own top-k differs from them and the two lists are a
+    near-tie (ids_near_tie(router logits, mine, theirs, rel)), the other side's ids are
     taken at that layer (force_ids of decode_step) and the step is run again
     from the start, so that later layers are compared on the same routing.
     Returns (out, forced, differ): forced lists the (b, l) taken from
@@ -378,7 +395,7 @@ def decode_step_following(m, W, kv, tokens, other_ids, rel, dt=torch.float32):
                 theirs = [int(v) for v in other_ids[b][l]]
                 if mine == theirs or (b, l) in force:
                     continue
-                if near_tie(out["router_logits"][b][l], k, rel):
+                if ids_near_tie(out["router_logits"][b][l], mine, theirs, rel):
                     new = (b, l, theirs)
                     break
                 differ.append((b, l))

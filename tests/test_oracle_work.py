@@ -7,10 +7,11 @@
   work, written here as closed forms (rows of W_qkv per kv group are its
   query heads' rows plus one k and one v head; pages per kv head are the
   pages below each sequence's bound);
-- near_tie and decode_step_following: an exact tie between two experts
-  (identical router rows) is a near-tie, and following the other side's
-  choice there equals a step with those ids forced; a disagreement away
-  from a tie is reported, not followed.
+- near_tie, ids_near_tie and decode_step_following: an exact tie between
+  two experts (identical router rows) is a near-tie, at the k-th slot and
+  inside the selection (the same two experts in the other order), and
+  following the other side's choice there equals a step with those ids
+  forced; a disagreement away from a tie is reported, not followed.
 """
 import itertools
 
@@ -178,6 +179,38 @@ def test_following_does_not_hide_a_real_difference():
     same = [[own["topk_ids"][0][l].tolist() for l in range(2)]]
     out2, forced2, differ2 = O.decode_step_following(m, W, kv, [3], same, 1e-5)
     assert forced2 == [] and differ2 == [] and torch.equal(out2["logits"][0], own["logits"][0])
+
+
+def test_following_an_order_swap_inside_the_selection():
+    # top-2 of (0, a, a, 0): experts 1 and 2 are both selected and tie, so
+    # the other order of the same two experts is a near-tie and is followed
+    m, W = tied_moe(2)
+    kv = O.OracleKV(m, [7], 2, HostKV(m, seed=11))
+    own = O.decode_step(m, W, kv, [3])
+    ids = own["topk_ids"][0][0].tolist()
+    assert sorted(ids) in ([1, 2], [0, 3])
+    swapped = ids[::-1]
+    assert O.ids_near_tie(own["router_logits"][0][0], ids, swapped, 1e-5)
+    other = [[swapped, own["topk_ids"][0][1].tolist()]]
+    kv.len = [7]
+    out, forced, differ = O.decode_step_following(m, W, kv, [3], other, 1e-5)
+    assert forced == [(0, 0)] and differ == []
+    kv2 = O.OracleKV(m, [7], 2, HostKV(m, seed=11))
+    want = O.decode_step(m, W, kv2, [3], force_ids={(0, 0): swapped})
+    assert torch.equal(out["x_ffn"][0][0], want["x_ffn"][0][0])
+    assert torch.equal(out["logits"][0], want["logits"][0])
+
+
+def test_ids_near_tie_rule():
+    r = torch.tensor([1.0, 3.0, 2.0, 2.0, 0.5])
+    assert O.ids_near_tie(r, [1, 2], [1, 3], 1e-5)      # k-th and (k+1)-th equal
+    assert O.ids_near_tie(r, [1, 2, 3], [1, 3, 2], 1e-5)  # equal pair inside the selection
+    assert not O.ids_near_tie(r, [1, 2], [2, 1], 1e-5)  # 3.0 and 2.0 are far apart
+    assert not O.ids_near_tie(r, [1, 2], [1, 0], 1e-5)
+    assert O.ids_near_tie(r, [1, 2], [1, 2], 0.0)       # equal lists
+    # relative threshold: logits 0 and -1e-6 give probabilities about 1e-6 apart
+    q = torch.tensor([0.0, -1e-6, -5.0])
+    assert O.ids_near_tie(q, [0, 1], [1, 0], 1e-5) and not O.ids_near_tie(q, [0, 1], [1, 0], 1e-7)
 
 
 def test_forced_weights_are_the_renormalised_probabilities():
