@@ -31,7 +31,8 @@
 //    (queries and probabilities carried as bf16 hi + lo pairs), an online
 //    softmax across pages and a log-sum-exp merge across waves;
 //  - the split combine is a log-sum-exp merge in fixed split order.
-// Consumers read neighbouring tagged words in pairs, one 16-byte load each.
+// Consumers read neighbouring tagged words in pairs: two 8-byte loads in
+// flight together, each a whole tagged word.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -109,7 +110,7 @@ __device__ __forceinline__ uint32_t ws_off(const KAC& a, const uint64_t* p) {
 
 // Read MAXP pairs of neighbouring tagged words of this thread (pair k at
 // workspace byte offset off(k), a multiple of 16, or NO_PAIR) into out[2k],
-// out[2k + 1], one 16-byte load per pair, re-reading stale pairs like
+// out[2k + 1], two 8-byte loads per pair (ld_tagged2), re-reading stale pairs like
 // read_words. Returns false on deadline or another workgroup's failure.
 constexpr uint32_t NO_PAIR = 0xFFFFFFFFu;
 template <int MAXP, class Off>
@@ -153,7 +154,7 @@ __device__ __forceinline__ bool read_pairs(KAC& a, const Off& off, float* out, u
 
 // Gather tagged words into LDS: dst[i] = value of word i for i < n, where
 // word i sits at src1 + i for i < n1 and at src2 + (i - n1) after that,
-// read as pairs (2j, 2j + 1) with one 16-byte load each: n1 and n are even
+// read as pairs (2j, 2j + 1) with ld_tagged2: n1 and n are even
 // and both sources start at an even workspace word (the planner lays out
 // every buffer so). MAXW words per thread per batch. which: 0 = routing
 // wait, 1 = data wait (trace slots), -1 = untraced. With nsq > 0 the sum of
@@ -216,7 +217,7 @@ __device__ __forceinline__ bool gather(Ctx& c, const uint64_t* src, int n, float
 
 // Gather n tagged words (n even, src at an even workspace word) into LDS
 // already in split form (see pack_lds): the pair (2j, 2j + 1) arrives in one
-// 16-byte load, and its bf16 hi and lo parts land in chunk 2j / 8, so no
+// read (ld_tagged2), and its bf16 hi and lo parts land in chunk 2j / 8, so no
 // separate conversion pass or barrier follows. Uniform result.
 template <int MAXW>
 __device__ __forceinline__ bool gather_split(Ctx& c, const uint64_t* src, int n, float* dst, int which) {
@@ -283,7 +284,7 @@ __device__ __forceinline__ bool gather_fn(Ctx& c, int n, const Addr& addr, float
   return c.s.fail == 0;
 }
 
-// gather_fn reading word pairs (i, i + 1), i even, with one 16-byte load:
+// gather_fn reading word pairs (i, i + 1), i even, with one ld_tagged2:
 // for the caller, n is even and, for every even i, addr(i) (nullptr: none) is
 // a word at an even workspace word offset followed by word i + 1, and
 // di(i + 1) = di(i) + 1 with di(i) even. Uniform result.
@@ -1475,10 +1476,13 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
   return true;
 }
 
-// LM head tile: rows stream through registers in double-buffered batches of
-// LM_BATCH rows per lane group; every lane group walks the same number of
-// batches (rows past the tile's end re-read its last row and are ignored), so
-// the loop issues its loads unconditionally.
+// LM head tile: rows stream through registers in a ring of LM_RING batches
+// of LM_BATCH rows per lane group, so that LM_RING - 1 batches are in flight
+// while one is reduced (a batch's registers are refilled as soon as it has
+// been reduced: no copy between buffers, which would wait for the batch in
+// flight before the next request); every lane group walks the same number
+// of batches (rows past the tile's end re-read its last row and are
+// ignored), so the loop issues its loads unconditionally.
 template <int CPL, int TC>
 __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
   constexpr int G = NT / TC;
@@ -1488,8 +1492,8 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
   const int lg = tid() / TC, tc = tid() % TC;
   const int per = (n + G - 1) / G;                       // rows per lane group
   int nb = (per + LM_BATCH - 1) / LM_BATCH;
-  nb = nb < 2 ? 2 : nb;                                  // >= 2 (two batches are issued up front)
-  uint4 A[LM_BATCH][CPL], Bf[LM_BATCH][CPL];
+  nb = nb < LM_RING ? LM_RING : nb;                      // >= LM_RING (the ring is filled up front)
+  uint4 W[LM_RING][LM_BATCH][CPL];
   auto row_of = [&](int bi, int r) { return min(lg + (bi * LM_BATCH + r) * G, n - 1); };
   auto issue = [&](uint4 (&w)[LM_BATCH][CPL], int bi) {
 #pragma unroll
@@ -1499,8 +1503,8 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
       for (int cc = 0; cc < CPL; ++cc) w[r][cc] = ld_nt(p + tc + cc * TC);
     }
   };
-  issue(A, 0);
-  issue(Bf, 1);
+#pragma unroll
+  for (int k = 0; k < LM_RING; ++k) issue(W[k], k);
   Gains gn;
   gn.load(a.final_norm, H);
   if (!gather<4>(c, a.x + (size_t)(a.L - 1) * a.s_x, H, s.vec, 1, H)) return false;
@@ -1511,21 +1515,23 @@ __device__ __forceinline__ bool task_lm(Ctx& c, const Task& t) {
     uh[cc] = ((const uint4*)(s.vec + (tc + cc * TC) * 8))[0];
     ul[cc] = ((const uint4*)(s.vec + (tc + cc * TC) * 8))[1];
   }
-  // batch bi is in A; batch bi + 1 is in flight in Bf
-  for (int bi = 0; bi < nb; ++bi) {
+  // batch bi sits in ring slot bi % LM_RING
+  for (int b0 = 0; b0 < nb; b0 += LM_RING) {
 #pragma unroll
-    for (int r = 0; r < LM_BATCH; ++r) {
-      float sum = 0.f;
+    for (int k = 0; k < LM_RING; ++k) {
+      const int bi = b0 + k;
+      if (bi < nb) {
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) sum = dot8h(A[r][cc], uh[cc], ul[cc], sum);
-      sum = group_sum_last<TC>(sum);
-      if (tc == TC - 1) s.out[row_of(bi, r)] = sum;
+        for (int r = 0; r < LM_BATCH; ++r) {
+          float sum = 0.f;
+#pragma unroll
+          for (int cc = 0; cc < CPL; ++cc) sum = dot8h(W[k][r][cc], uh[cc], ul[cc], sum);
+          sum = group_sum_last<TC>(sum);
+          if (tc == TC - 1) s.out[row_of(bi, r)] = sum;
+        }
+        if (bi + LM_RING < nb) issue(W[k], bi + LM_RING);
+      }
     }
-#pragma unroll
-    for (int r = 0; r < LM_BATCH; ++r)
-#pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) A[r][cc] = Bf[r][cc];
-    if (bi + 2 < nb) issue(Bf, bi + 2);
   }
   lds_barrier();
   float bv = NEG_INF;

@@ -219,6 +219,8 @@ MK_HD inline int kernel_class(int hidden, int attn_out, int ffn, int head_dim) {
 
 // LM-head tiles stream their rows in batches of LM_BATCH rows per lane group.
 constexpr int LM_BATCH = 2;
+// Batches of an LM-head tile in flight together (a ring of registers).
+constexpr int LM_RING = 3;
 
 struct KArgs {
   // shape

@@ -337,8 +337,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   if (F <= 0) return fail(MK_EINVAL, "mk_plan: ffn width must be positive");
   if (moe && (m->top_k <= 0 || m->top_k > m->n_experts || m->top_k > 16 || m->n_experts > 256))
     return fail(MK_EUNSUPPORTED, "mk_plan: MoE needs 0 < top_k <= min(16, n_experts), n_experts <= 256");
-  // activations pass between tasks as pairs of tagged words read with one
-  // 16-byte load: every gathered run (hidden, heads x dim, top_k x FFN,
+  // activations pass between tasks as pairs of neighbouring tagged words
+  // read together: every gathered run (hidden, heads x dim, top_k x FFN,
   // router logits) has an even length and starts at an even word
   if (moe && m->n_experts % 2)
     return fail(MK_EUNSUPPORTED, "mk_plan: the number of experts must be even");
@@ -484,6 +484,18 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   // a batch: about four splits per unit, so that ragged lengths even out
   if (batch && !(o && o->attn_split_pages > 0)) pps = std::max(8, ceil_div(pg_total, 4 * n_cu));
   p->attn_queue = queue;
+  // batch 1, static splits: when splits of two pages per wave fit on at most
+  // 3/5 of the units, attention and its combine run on those units (set A)
+  // and the O projection and router on the others (set B), so that the O
+  // rows stream while attention runs
+  int n_attn_units = 0;
+  if (!batch && !queue && !(o && o->attn_split_pages > 0) && moe) {
+    const int S = ceil_div(pg_bound, 2 * mk::NWAVE);
+    if (Hkv * S <= (3 * n_cu) / 5 && Hkv * S >= n_cu / 4) {
+      pps = ceil_div(pg_bound, S);
+      n_attn_units = Hkv * S;
+    }
+  }
   for (int l = 0; l < L; ++l) {
     const std::string ls = std::to_string(l);
     if (batch) {
@@ -551,7 +563,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   // combine tasks per (sequence, query head): a power of two (D is 64 or
   // 128, so every task takes an even run of dims), at most D / 8
   p->comb_dim_tasks = 1;
-  while (2 * p->comb_dim_tasks <= D / 8 && 2 * p->comb_dim_tasks * B * Hq <= n_cu) p->comb_dim_tasks *= 2;
+  const int comb_units = n_attn_units > 0 ? n_attn_units : n_cu;
+  while (2 * p->comb_dim_tasks <= D / 8 && 2 * p->comb_dim_tasks * B * Hq <= comb_units) p->comb_dim_tasks *= 2;
   while (p->comb_dim_tasks < D / 8 && (size_t)p->S_max * (ceil_div(D, p->comb_dim_tasks) + 2) > 8192)
     p->comb_dim_tasks *= 2;  // fewer dims per combine task when there are many splits
 
@@ -635,7 +648,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     const int n_rf = fold ? ceil_div(m->n_experts, 4) : 0;
     {
       std::vector<Task> st;
-      int nt = std::max(n_cu - n_rf, ceil_div(H, rows_max(Hq * D)));
+      const int o_units = n_attn_units > 0 ? n_cu - n_attn_units : n_cu;
+      int nt = std::max(o_units - n_rf, ceil_div(H, rows_max(Hq * D)));
       for (auto [s0, c] : split_even(H, nt)) {
         Task t = mk_task(mk::OP_O, l);
         t.wait_b = ctr16(p->c_comb[l]);
@@ -785,6 +799,17 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         stage_lists[cu].push_back(s0);
         heap.push({pages + t.a3, r});
       }
+    } else if (n_attn_units > 0 && !st.empty() && st[0].op != mk::OP_QKV && st[0].op != mk::OP_EXPERT &&
+               st[0].op != mk::OP_LM && st[0].op != mk::OP_FINAL) {
+      // attention and combine on units 0 .. A-1, O and router on A .. n_cu-1
+      const bool set_a = st[0].op == mk::OP_ATTN || st[0].op == mk::OP_COMB;
+      const int u0 = set_a ? 0 : n_attn_units, nu = set_a ? n_attn_units : n_cu - n_attn_units;
+      for (size_t i = 0; i < st.size(); ++i) {
+        int cu = u0 + (int)(i % (size_t)nu);
+        p->lists[cu].push_back(st[i]);
+        stage_lists[cu].push_back(s0);
+      }
+      continue;
     } else {
       for (size_t i = 0; i < st.size(); ++i) {
         int cu = (cursor + (int)i) % n_cu;

@@ -541,15 +541,63 @@ def test_folded_router_runs_beside_the_o_projection(name):
             if folded:
                 assert (rt["a2"] <= 4).all()            # four expert rows per task at most
                 for l in (0, L - 1):
-                    # one O or router task per unit: each unit's list has exactly one of them
-                    units = []
+                    # one O or router task per unit of the O stage: every unit,
+                    # or (attention on units of its own) every unit without an
+                    # attention split
+                    units, attn = [], []
                     for cu in range(n_cu):
                         lst = tasks[cu_off[cu]:cu_off[cu + 1]]
                         k = ((lst["layer"] == l) & ((lst["op"] == OP_O) | (lst["op"] == OP_ROUTER))).sum()
                         units.append(int(k))
-                    assert units == [1] * n_cu
+                        attn.append(int(((lst["layer"] == l) & (lst["op"] == OP_ATTN)).sum()))
+                    if any(u == 0 for u in units):
+                        assert units == [0 if a else 1 for a in attn]
+                    else:
+                        assert units == [1] * n_cu
             mk.mk_plan_validate(p)
             mk.mk_plan_simulate(p, 3, 2)
         finally:
             mk.mk_plan_free(p)
             mk.mk_pool_free(pool)
+
+
+TF_STAGE_KV = 4
+
+
+@pytest.mark.parametrize("name", ["moe48_b1_8k", "moe48_b1_256k"])
+def test_batch1_attention_and_o_projection_on_disjoint_units(name):
+    """At 8K the batch-1 plan runs attention (splits of at most two pages per
+    wave) and the combine on units 0 .. A-1 and the O projection and router
+    on the others, so that the O rows stream while attention runs; QKV and
+    the expert stage use every unit once per layer, and only the expert tasks
+    of attention units stage the next layer's pages. A long context keeps
+    attention on every unit."""
+    w, pool, p, bound = build_plan(name, 256, 0)
+    try:
+        n_cu, _, cu_off, tasks = decode_plan(mk.mk_plan_export(p))
+        L = w["model"]["n_layers"]
+        cu_of = np.repeat(np.arange(n_cu), np.diff(cu_off))
+        for l in (0, L // 2, L - 1):
+            at = (tasks["layer"] == l) & (tasks["op"] == OP_ATTN)
+            a_units = np.unique(cu_of[at])
+            if name == "moe48_b1_256k":
+                assert len(a_units) == n_cu
+                continue
+            A = len(a_units)
+            assert (a_units == np.arange(A)).all() and n_cu // 4 <= A <= 3 * n_cu // 5
+            assert at.sum() == A and (tasks["a3"][at] <= 16).all()
+            cm = (tasks["layer"] == l) & (tasks["op"] == OP_COMB)
+            assert (cu_of[cm] < A).all()
+            orr = (tasks["layer"] == l) & ((tasks["op"] == OP_O) | (tasks["op"] == OP_ROUTER))
+            assert (cu_of[orr] >= A).all() and np.unique(cu_of[orr]).size == n_cu - A
+            for op in (OP_QKV, OP_EXPERT):
+                m = (tasks["layer"] == l) & (tasks["op"] == op)
+                assert np.bincount(cu_of[m], minlength=n_cu).tolist() == [1] * n_cu
+            ex = (tasks["layer"] == l) & (tasks["op"] == OP_EXPERT)
+            staged = cu_of[ex & ((tasks["flags"] & TF_STAGE_KV) != 0)]
+            want = np.arange(A) if l < L - 1 else np.arange(0)
+            assert (np.sort(staged) == want).all()
+        mk.mk_plan_validate(p)
+    finally:
+        mk.mk_plan_free(p)
+        mk.mk_pool_free(pool)
