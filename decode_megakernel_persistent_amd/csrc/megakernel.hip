@@ -66,11 +66,11 @@ struct Smem {
     uint4 stage[NWAVE * STAGE_CHUNKS * 64];  // batch tasks: staged operands
     float att[NWAVE * STAGE_CHUNKS * 256];   // attention: per-wave partials; combine: split words
   };
-  float out[2048];     // per-row dot products
+  alignas(16) float out[2048];     // per-row dot products
   float res[2048];     // residual rows
   float red[64];       // block reductions
   float route_w[16];
-  float route_wn[16];  // routing weights as applied (renormalised when the model says so)
+  alignas(16) float route_wn[16];  // routing weights as applied (renormalised when the model says so)
   int route_ids[16];
   int fail;
   int kv_ti;                 // task index of the attention split whose pages are staged (-1: none)
@@ -1170,6 +1170,7 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
     L += exp2_hw(mq - Mz) * sw[q * W + nd + 1];
   }
   L = wave_sum(L);
+  mark(c, 0);
   const int NG = NT / nd, sg = tid() / nd, dim = tid() % nd;
   float acc = 0.f;
   if (sg < NG)
@@ -1179,19 +1180,29 @@ __device__ __forceinline__ bool task_comb(Ctx& c, const Task& t) {
     }
   float* red = s.out + 1024;
   int nred = NG;
-  if (nd == 16) {
-    // the four rows of a wave hold split groups 4w .. 4w+3 of the same 16 dims:
-    // sum them across rows, leaving one partial per wave
-    acc = xor32_sum(xor16_sum(acc));
-    if ((tid() & 63) < 16) red[(tid() >> 6) * 16 + dim] = acc;
+  if (nd <= 32) {
+    // a wave holds 64 / nd split groups of the same nd dims (lanes nd apart):
+    // sum them across the wave, leaving one partial per wave
+    if (nd <= 8) acc = xor8_sum(acc);
+    if (nd <= 16) acc = xor16_sum(acc);
+    acc = xor32_sum(acc);
+    if ((tid() & 63) < nd) red[(tid() >> 6) * nd + dim] = acc;
     nred = NWAVE;
   } else if (sg < NG) {
     red[sg * nd + dim] = acc;
   }
+  mark(c, 1);
   lds_barrier();
+  mark(c, 2);
   if (tid() < nd) {
+    // nred <= NWAVE partials, read together and summed in order
+    float pv[NWAVE];
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) pv[q] = q < nred ? red[q * nd + tid()] : 0.f;
     float o = 0.f;
-    for (int q = 0; q < nred; ++q) o += red[q * nd + tid()];
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q)
+      if (q < nred) o += pv[q];
     o = L > 0.f ? o / L : 0.f;
     st_tagged(a.o + (size_t)l * a.s_o + ((size_t)b * a.Hq + h) * D + d0 + tid(), o, a.epoch);
   }
@@ -1216,7 +1227,9 @@ __device__ __forceinline__ bool task_o(Ctx& c, const Task& t) {
   }
   if (!gather_split<8>(c, a.o + (size_t)l * a.s_o, K, c.s.vec, 1)) return false;
   tile.dots(c.s.vec, c.s.out);
+  mark(c, 0);
   lds_barrier();
+  mark(c, 1);
   bool fail = false;
   if (th < n) {
     const float x = tag_is(rw, a.epoch) ? tag_value(rw) : resid(c, l, 0, r0 + th, &fail);
@@ -1468,7 +1481,22 @@ __device__ __forceinline__ bool task_expert(Ctx& c, const Task& t) {
     mark(c, 7);
     for (int q = tid(); q < nrc; q += NT) {
       float y = 0.f;
-      for (int j = 0; j < KK; ++j) y += s.route_wn[j] * s.out[q * KK + j];
+      if ((KK & 3) == 0) {
+        // KK <= 16 slots in float4 reads (independent of one another, so
+        // not each waiting for the last), summed in slot order
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+          if (4 * jb < KK) {
+            const float4 wv = *(const float4*)(s.route_wn + 4 * jb);
+            const float4 ov = *(const float4*)(s.out + q * KK + 4 * jb);
+            y += wv.x * ov.x;
+            y += wv.y * ov.y;
+            y += wv.z * ov.z;
+            y += wv.w * ov.w;
+          }
+      } else {
+        for (int j = 0; j < KK; ++j) y += s.route_wn[j] * s.out[q * KK + j];
+      }
       st_tagged(a.x + (size_t)l * a.s_x + (size_t)b * H + r0 + rc + q, s.res[rc + q] + y, a.epoch);
     }
     lds_barrier();
