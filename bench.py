@@ -45,6 +45,9 @@ def parse():
                     help="timed steps of the sampling leg (same workload, top-k/top-p/temperature; 0: skip)")
     ap.add_argument("--prefill-steps", type=int, default=16,
                     help="timed 32-token prefill chunks after 8192 prior tokens (48-layer MoE; 0: skip)")
+    ap.add_argument("--trace-steps", type=int, default=0,
+                    help="after the timed run, this many steps with the per-task trace on (0: none)")
+    ap.add_argument("--trace-out", default="", help="markdown file for the traced steps' per-layer timeline")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM counter bytes per launch measured by rocprofv3 --pmc")
     return ap.parse_args()
@@ -92,6 +95,10 @@ def main():
     dec.close()
     dec = pool = None
     torch.cuda.empty_cache()
+
+    if a.trace_steps > 0:
+        trace_leg(torch, mk, dev, W, a)
+        torch.cuda.empty_cache()
 
     # sampling beyond greedy in the last stage: the same workload
     smp = None
@@ -325,6 +332,41 @@ def stream_copy_probe(torch, mk, dev, reps=5):
     del src, dst
     torch.cuda.empty_cache()
     return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+
+
+def trace_leg(torch, mk, dev, W, a):
+    """a.trace_steps steps of the same workload with the per-task trace on
+    (outside the timed run: the trace adds stores to every task); the last
+    step's per-layer timeline goes to stderr and, with --trace-out, to a
+    markdown file."""
+    from decode_megakernel_persistent_amd import trace as T
+    from fixtures.session import gpu_session, spec
+    # the plan of the timed run (its context bound), traced over its first steps
+    w = spec(a.workload, a.seed, steps=max(a.warmup + a.steps, 2 + a.trace_steps))
+    B = w["batch"]
+    dec, pool, _ = gpu_session(w, a.seed, device=dev, n_cu=a.n_cu, attn_split_pages=a.split_pages,
+                               plan_flags=a.plan_flags, weights=W, trace=True)
+    hist = torch.empty((3 + a.trace_steps, B), dtype=torch.int32, device=dev)
+    hist[0].copy_(torch.tensor(w["tokens"], dtype=torch.int32, device=dev))
+    for s in range(2 + a.trace_steps):
+        dec.step(hist[s], hist[s + 1])
+    torch.cuda.synchronize()
+    dec.check_status()
+    d = T.decode(dec.trace)
+    rows, (pmed, pmin, pmax) = T.layer_timeline(d)
+    lines = [f"per-task trace of the last of {2 + a.trace_steps} steps of `{a.workload}`",
+             "", "    " + T.format_summary(T.summary(d)).replace("\n", "\n    "), "",
+             f"per layer: median {pmed:.2f} us (min {pmin:.2f}, max {pmax:.2f})", "",
+             "| stage | tasks per layer | median end (us) | last end (us) |", "|---|---|---|---|"]
+    for name, (med, mx, n) in sorted(rows.items(), key=lambda kv: kv[1][0]):
+        lines.append(f"| {name} | {n} | {med:.2f} | {mx:.2f} |")
+    text = "\n".join(lines)
+    print(text, file=sys.stderr, flush=True)
+    if a.trace_out:
+        with open(a.trace_out, "w") as f:
+            f.write(text + "\n")
+    mk.mk_pool_free(pool)
+    dec.close()
 
 
 def host_description():

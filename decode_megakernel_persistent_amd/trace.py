@@ -83,3 +83,31 @@ def format_summary(sm):
         lines.append(f"{name:8s} {v['n']:6d} {v['total']:8.2f} {v['pre']:8.2f} {v['wait']:8.2f} "
                      f"{v['body']:8.2f} {v['signal']:8.2f}")
     return "\n".join(lines)
+
+
+def layer_timeline(d, layers=None):
+    """Per operation of a layer: (median, last) task end in us after the median
+    end of the previous layer's last stage (the expert stage at batch 1, the
+    expert combine in a batch), averaged over `layers` (default: the middle
+    layers); and the per-layer durations (median, min, max)."""
+    ops = [int(o) for o in np.unique(d["op"]) if int(o) in OPS]
+    batch = 15 in ops
+    last_op = 15 if batch else 6
+    L = int(d["layer"][d["op"] == last_op].max()) + 1
+    if layers is None:
+        layers = range(max(1, L // 6), max(2, L - L // 6))
+    ends = {l: float(np.median(d["end"][(d["op"] == last_op) & (d["layer"] == l)])) for l in range(L)}
+    rows = {}
+    for op in ops:
+        if op in (8, 9, 16, 17):  # LM head and final task: once per step
+            continue
+        med, mx = [], []
+        for l in layers:
+            m = (d["op"] == op) & (d["layer"] == l)
+            if l - 1 in ends and m.any():
+                med.append(float(np.median(d["end"][m])) - ends[l - 1])
+                mx.append(float(np.max(d["end"][m])) - ends[l - 1])
+        if med:
+            rows[OPS[op]] = (float(np.mean(med)), float(np.mean(mx)), int(((d["op"] == op) & (d["layer"] == layers[0])).sum()))
+    per = [ends[l] - ends[l - 1] for l in range(1, L)]
+    return rows, (float(np.median(per)), float(min(per)), float(max(per)))
