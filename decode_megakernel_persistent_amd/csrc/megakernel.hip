@@ -2138,49 +2138,71 @@ __device__ __forceinline__ bool task_bqkv(Ctx& c, const Task& t) {
   return true;
 }
 
-// W_o rows of every sequence over reduction block kb (a0) of the a3 blocks
-// of the attention output: blocks 1 .. a3-1 publish partial sums (OPART);
-// block 0 adds them in block order to its own and adds the residual (the
-// layer's input), which it gathers together with them in one batch.
+// Batch O projection. A tile: W_o rows a1 .. a1 + a2 of every sequence over
+// reduction block kb (a0) of the a3 blocks of the attention output; with one
+// block it adds the residual (the layer's input) and finishes the rows, else
+// it publishes its partial sums (OPART, slot kb). A summing task (TF_REDUCE)
+// finishes rows a1 .. a1 + a2: it gathers the a3 blocks' partial sums of
+// those rows and their residual in one batch and adds them in block order,
+// so the reduction is spread over as many tasks as the tiles (a single task
+// per row block gathering every other block's rows took ~20 us at batch 32).
 __device__ __forceinline__ bool task_bo(Ctx& c, const Task& t) {
   KAC& a = c.a;
   const int l = t.layer, kb = t.a0, r0 = t.a1, n = t.a2, KB = t.a3 > 0 ? t.a3 : 1;
-  const int H = a.H, K = a.Hq * a.D, B = a.B, Kb = K / KB, k0 = kb * Kb;
+  const int H = a.H, K = a.Hq * a.D, B = a.B;
+  const uint64_t* xin = l > 0 ? a.x + (size_t)(l - 1) * a.s_x : nullptr;
+  const uint64_t* op = a.opart + (size_t)l * a.s_opart;
+  if (t.flags & TF_REDUCE) {
+    // rows r0 .. r0 + n: the KB blocks' partial sums and the residual; word
+    // (q, b, r) at red[(q * B + b) * n + r], q = 0 the residual (layer > 0),
+    // q >= 1 the partial of block q - 1; summed in block order
+    float* red = c.s.vec;
+    const int bn = B * n;
+    auto waddr = [&](int i) -> const uint64_t* {
+      const int q = i / bn, rem = i - q * bn, b = rem / n, r = rem - b * n;
+      if (q == 0) return xin ? xin + (size_t)b * H + r0 + r : nullptr;
+      return op + ((size_t)(q - 1) * B + b) * H + r0 + r;
+    };
+    // pairs of rows (r, r + 1): even n, r0 and H keep every pair in one row range
+    const bool pairs = !((n | r0 | H) & 1) && !((ws_off(a, op) >> 3) & 1) && !(xin && ((ws_off(a, xin) >> 3) & 1));
+    if (!(pairs ? gather_fn_pairs<16>(c, (KB + 1) * bn, waddr, red, 0)
+                : gather_fn<8>(c, (KB + 1) * bn, waddr, red, 0)))
+      return false;
+    for (int idx = tid(); idx < bn; idx += NT) {
+      const int r = idx / B, b = idx - r * B;
+      float y = red[(B + b) * n + r];
+      for (int q = 2; q <= KB; ++q) y += red[(q * B + b) * n + r];
+      const float x = l > 0 ? red[b * n + r] : bf2f(a.embed[(size_t)token_row(a, b) * H + r0 + r]);
+      st_tagged(a.xa + (size_t)l * a.s_x + (size_t)b * H + r0 + r, x + y, a.epoch);
+    }
+    return true;
+  }
+  const int Kb = K / KB, k0 = kb * Kb;
   const uint16_t* W = a.wo + (size_t)l * H * K + k0;
   MtSrc src{a.o + (size_t)l * a.s_o + k0, K, nullptr, false};
   if (a.trace && tid() == 0) c.s.tw[2] = now();
   if (!mt_tile(c, n, Kb, [&](int j) { return W + (size_t)(r0 + j) * K; }, src)) return false;
   if (a.trace && tid() == 0) c.s.tw[3] = now();
   MtLds& P = *(MtLds*)&c.s;
-  if (kb > 0) {
-    uint64_t* dst = a.opart + (size_t)l * a.s_opart + (size_t)(kb - 1) * B * H;
+  if (KB > 1) {  // publish the tile's partial sums (block kb)
+    uint64_t* dst = a.opart + (size_t)l * a.s_opart + (size_t)kb * B * H;
     for (int idx = tid(); idx < n * B; idx += NT) {
       const int r = idx / B, b = idx - r * B;
       st_tagged(dst + (size_t)b * H + r0 + r, P.out[r][b], a.epoch);
     }
     return true;
   }
-  // word (q, b, r) at red[(q * B + b) * n + r]: q = 0 the residual (layer > 0),
-  // q >= 1 the partial of block q; the tile's panel area is free by now
-  float* red = (float*)P.hi;
-  const int bn = B * n;
-  const uint64_t* xin = l > 0 ? a.x + (size_t)(l - 1) * a.s_x : nullptr;
-  const uint64_t* op = a.opart + (size_t)l * a.s_opart;
-  auto waddr = [&](int i) -> const uint64_t* {
-    const int q = i / bn, rem = i - q * bn, b = rem / n, r = rem - b * n;
-    if (q == 0) return xin ? xin + (size_t)b * H + r0 + r : nullptr;
-    return op + ((size_t)(q - 1) * B + b) * H + r0 + r;
-  };
-  // pairs of rows (r, r + 1): even n, r0 and H keep every pair in one row range
-  const bool pairs = !((n | r0 | H) & 1) && !((ws_off(a, op) >> 3) & 1) && !(xin && ((ws_off(a, xin) >> 3) & 1));
-  if (!(pairs ? gather_fn_pairs<16>(c, KB * bn, waddr, red, 0) : gather_fn<8>(c, KB * bn, waddr, red, 0)))
+  // one block: the tile finishes its rows with the residual
+  float* res = (float*)P.hi;  // the tile's panel area is free by now
+  if (!gather_fn<8>(c, B * n, [&](int i) -> const uint64_t* {
+        const int b = i / n, r = i - b * n;
+        return xin ? xin + (size_t)b * H + r0 + r : nullptr;
+      }, res, 0))
     return false;
-  for (int idx = tid(); idx < bn; idx += NT) {
+  for (int idx = tid(); idx < n * B; idx += NT) {
     const int r = idx / B, b = idx - r * B;
-    float y = P.out[r][b];
-    for (int q = 1; q < KB; ++q) y += red[(q * B + b) * n + r];
-    const float x = l > 0 ? red[b * n + r] : bf2f(a.embed[(size_t)token_row(a, b) * H + r0 + r]);
-    st_tagged(a.xa + (size_t)l * a.s_x + (size_t)b * H + r0 + r, x + y, a.epoch);
+    const float x = l > 0 ? res[b * n + r] : bf2f(a.embed[(size_t)token_row(a, b) * H + r0 + r]);
+    st_tagged(a.xa + (size_t)l * a.s_x + (size_t)b * H + r0 + r, x + P.out[r][b], a.epoch);
   }
   return true;
 }

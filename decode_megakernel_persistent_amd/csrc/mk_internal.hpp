@@ -36,7 +36,8 @@ enum Op : uint8_t {
   // batch (B > 1) tasks: the dense projections cover all sequences at once
   // as MFMA tiles of 16-row blocks
   OP_BQKV = 10,   // a0 = kv group g, a1 = first rotary pair, a2 = pairs
-  OP_BO = 11,     // a1 = first row, a2 = rows
+  OP_BO = 11,     // a0 = reduction block, a1 = first row, a2 = rows, a3 = reduction blocks
+                  // (TF_REDUCE: the rows' sum over the blocks)
                   // (12 is unused)
   OP_TOPK = 13,   // a0 = b: router rows, softmax and top-k of one sequence
   OP_BEXP = 14,   // a0 = expert, a1 = first FFN row, a2 = FFN rows,
@@ -59,8 +60,12 @@ enum Op : uint8_t {
 // scale from x and o (W_r (g x) + (W_r diag(g) W_o) o); expert tasks apply it.
 // TF_SHARE (batch MoE): the expert task is share aux of a1 of the layer's
 // expert work over the experts the routing chose (rows assigned on device).
+// TF_REDUCE (batch O projection split over a3 > 1 reduction blocks): the
+// task adds the a3 blocks' partial sums of rows a1 .. a1 + a2 and the
+// residual; without it, a task of block a0 publishes the partial sums of
+// rows a1 .. a1 + a2 (its tile).
 enum TaskFlags : uint8_t { TF_WRITE_TOPK = 1, TF_QUEUE = 2, TF_STAGE_KV = 4, TF_LOGITS = 8, TF_PREFILL = 16,
-                           TF_FOLD = 32, TF_SHARE = 64 };
+                           TF_FOLD = 32, TF_SHARE = 64, TF_REDUCE = 128 };
 
 // Batch QKV tasks: rotary pairs per row block (the rows of a block are 2
 // BQKV_PAIRS), and the words per (reduction block, row block, sequence) of

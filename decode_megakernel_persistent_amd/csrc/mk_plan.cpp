@@ -199,22 +199,44 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
           }
       stages.push_back(st);
     }
-    {  // BO, split over o_kb blocks of the reduction: blocks 1 .. o_kb-1
-       // publish partial sums, then block 0 adds them and the residual
+    {  // BO, split over o_kb blocks of the reduction: every block publishes
+       // the partial sums of its tile, then each of o_kb slices of a row
+       // block adds the blocks' partial sums of its rows and the residual
+       // (the reduction spread over as many tasks as the tiles)
       const int KB = p->o_kb;
-      for (int pass = 0; pass < 2; ++pass) {
-        if (pass == 0 && KB == 1) continue;
+      if (KB == 1) {
         std::vector<Task> st;
-        for (int s0 = 0; s0 < H; s0 += 16 * O_BLOCKS)
-          for (int kb = pass == 0 ? 1 : 0; kb < (pass == 0 ? KB : 1); ++kb) {
+        for (int s0 = 0; s0 < H; s0 += 16 * O_BLOCKS) {
+          Task t = mk_task(mk::OP_BO, l);
+          t.wait_b = ctr16(p->c_comb[l]);
+          t.signal = ctr16(p->c_o[l]);
+          t.a0 = 0; t.a1 = s0; t.a2 = std::min(16 * O_BLOCKS, H - s0); t.a3 = 1;
+          t.units = (uint16_t)t.a2;
+          st.push_back(t);
+        }
+        stages.push_back(st);
+      } else {
+        std::vector<Task> tiles, sums;
+        for (int s0 = 0; s0 < H; s0 += 16 * O_BLOCKS) {
+          const int n = std::min(16 * O_BLOCKS, H - s0);
+          for (int kb = 0; kb < KB; ++kb) {
             Task t = mk_task(mk::OP_BO, l);
             t.wait_b = ctr16(p->c_comb[l]);
-            t.signal = pass == 0 ? mk::NO_CTR : ctr16(p->c_o[l]);
-            t.a0 = kb; t.a1 = s0; t.a2 = std::min(16 * O_BLOCKS, H - s0); t.a3 = KB;
-            t.units = (uint16_t)(pass == 0 ? 0 : t.a2);
-            st.push_back(t);
+            t.a0 = kb; t.a1 = s0; t.a2 = n; t.a3 = KB;
+            tiles.push_back(t);
           }
-        stages.push_back(st);
+          for (auto [r0, c] : split_even(n, KB)) {
+            Task t = mk_task(mk::OP_BO, l);
+            t.flags = mk::TF_REDUCE;
+            t.wait_b = ctr16(p->c_comb[l]);
+            t.signal = ctr16(p->c_o[l]);
+            t.a1 = s0 + r0; t.a2 = c; t.a3 = KB;
+            t.units = (uint16_t)c;
+            sums.push_back(t);
+          }
+        }
+        stages.push_back(tiles);
+        stages.push_back(sums);
       }
     }
     if (moe) {  // ROUTER rows (a few tasks per sequence), then TOPK per sequence
@@ -857,7 +879,7 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         (size_t)B * Hkv * 2 * D,                          // KVN
         batch && moe ? (size_t)B * K * 2 : 0,             // ROUTE
         batch ? (size_t)B * K * H : 0,                    // Y
-        batch ? (size_t)(p->o_kb - 1) * B * H : 0,        // OPART
+        batch && p->o_kb > 1 ? (size_t)p->o_kb * B * H : 0,  // OPART
         batch ? (size_t)(p->q_kb - 1) * p->q_rb * B * (2 * 8 * QKV_BLOCKS + 2) : 0,   // QPART
         0};                                               // LOGIT (not per layer)
     size_t off = 0;
@@ -980,8 +1002,8 @@ void task_outputs(const mk_plan_t* p, const Task& t, Emit&& emit) {
     case mk::OP_O:
       for (int r = t.a1; r < t.a1 + t.a2; ++r) emit(K_O, r);
       break;
-    case mk::OP_BO:  // the partial sums of blocks 1 .. kb-1 end in block 0's rows
-      if (t.a0 == 0)
+    case mk::OP_BO:  // tiles of several reduction blocks publish partial sums; the sums finish rows
+      if (t.a3 <= 1 || (t.flags & mk::TF_REDUCE))
         for (int r = t.a1; r < t.a1 + t.a2; ++r) emit(K_O, r);
       break;
     case mk::OP_ROUTER:  // rows a1 .. a1 + a2 of sequence a0
@@ -1163,7 +1185,7 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
   constexpr int K_QPART = mk::OP_COUNT, K_OPART = mk::OP_COUNT + 1, N_KIND = mk::OP_COUNT + 2;
   auto kind = [](const Task& t) -> int {
     if (t.op == mk::OP_BQKV && (t.a3 & 0xFF) != 0) return K_QPART;
-    if (t.op == mk::OP_BO && t.a0 != 0) return K_OPART;
+    if (t.op == mk::OP_BO && t.a3 > 1 && !(t.flags & mk::TF_REDUCE)) return K_OPART;
     return t.op;
   };
   auto slot = [&](int k, int l, int g) { return ((size_t)k * (L + 1) + l) * (Hkv + 1) + g; };

@@ -325,8 +325,9 @@ mk_status mk_plan_upload(const mk_plan_t* p, void* d_plan, size_t bytes, void* h
  * batch plans only (0 bytes at batch 1):
  *   ROUTE [B][top_k][2] selected expert id (int bits) and weight per slot,
  *   Y [B][top_k][H] each selected expert's down-projection output,
- *   OPART [kb - 1][B][H] partial O projections over reduction blocks 1 .. kb-1
- *   (the O projection is split over kb blocks of the attention output),
+ *   OPART [kb][B][H] partial O projections over reduction blocks 0 .. kb-1
+ *   (the O projection is split over kb > 1 blocks of the attention output;
+ *   0 bytes when kb = 1),
  *   QPART [qkb - 1][row blocks][B][rows + 2] partial QKV projections over
  *   reduction blocks 1 .. qkb-1 of the hidden state, per row block of the
  *   QKV tasks: the block's rows, then the block's sum of squares of the

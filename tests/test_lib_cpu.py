@@ -39,6 +39,7 @@ NO_CTR = 0xFFFF
 TF_QUEUE = 2
 TF_LOGITS = 8
 TF_SHARE = 64
+TF_REDUCE = 128
 
 
 def declared_functions():
@@ -168,11 +169,13 @@ def plan_coverage(tasks, m, bound):
                 add(("qkv", l), [r for p in range(a1, a1 + a2) for r in qkv_rows(p, a0, m)])
             q_blocks.setdefault((l, a0, a1, a2, max(a3 >> 8, 1)), []).append(a3 & 0xFF)
         elif op == OP_BO:
-            # reduction block a0 of a3: block 0 finishes rows a1 .. a1 + a2
-            # (its own partial sum plus those of blocks 1 .. a3-1)
-            if a0 == 0:
+            # a3 == 1: the tile finishes rows a1 .. a1 + a2; otherwise the tile of
+            # reduction block a0 publishes their partial sums and a summing task
+            # (TF_REDUCE) finishes rows a1 .. a1 + a2 from the a3 blocks' sums
+            if a3 <= 1 or int(t["flags"]) & TF_REDUCE:
                 add(("o", l), list(range(a1, a1 + a2)))
-            o_blocks.setdefault((l, a1, a2, max(a3, 1)), []).append(a0)
+            if not int(t["flags"]) & TF_REDUCE:
+                o_blocks.setdefault((l, a1, a2, max(a3, 1)), []).append(a0)
         elif op == OP_TOPK:
             # one sequence: every router row (unless router tasks computed
             # them: TF_LOGITS), then its top-k
