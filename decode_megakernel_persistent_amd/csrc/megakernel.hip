@@ -2608,6 +2608,7 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
   const uint32_t* hdr = args->plan;
   const uint32_t* off = hdr + PLAN_HDR_WORDS;
   const Task* tasks = (const Task*)((const char*)hdr + hdr[H_TASK_OFF_BYTES]);
+  const Task* splits = (const Task*)((const char*)hdr + hdr[H_SPLIT_OFF_BYTES]);  // queue plans
   const uint32_t beg = off[blockIdx.x], end = off[blockIdx.x + 1];
   if (tid() == 0) {
     s.fail = 0;
@@ -2637,13 +2638,14 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
     }
     switch (t.op) {
       case OP_ATTN: {
-        // One split, or splits from the shared queue: every pull adds one to
+        // One split, or splits from the shared queue (records a1 .. a1 + a2
+        // of the plan's split table, longest first): every pull adds one to
         // the queue counter; this step's pulls are numbered from base =
         // (epoch - 1) * (splits + queue tasks), since each queue task's last
         // pull comes back empty. The next split is pulled while one runs.
         const bool queue = (t.flags & TF_QUEUE) != 0;
         uint32_t* qc = a.ctr + (size_t)t.a0 * CTR_LINES * CTR_STRIDE;
-        const uint32_t n_items = queue ? (uint32_t)(a.Hkv * t.a1) : 1u;
+        const uint32_t n_items = queue ? (uint32_t)t.a2 : 1u;
         const uint32_t base = (a.epoch - 1u) * (n_items + (uint32_t)t.a3);
         if (queue && tid() == 0)
           s.qnext = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base;
@@ -2656,12 +2658,8 @@ __global__ void __launch_bounds__(NT) megakernel(KArgs) {
             if (idx >= n_items) break;
             lds_barrier();  // every wave has read qnext
             if (tid() == 0) nxt = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int split = (int)(idx % (uint32_t)t.a1);
-            tt.a0 = 0;
-            tt.a1 = (int)(idx / (uint32_t)t.a1);
-            tt.a2 = split * t.a2;
-            tt.a3 = min(t.a2, ((a.bound + 15) >> 4) - tt.a2);
-            tt.aux = (uint16_t)split;
+            tt = splits[t.a1 + idx];
+            tt.layer = t.layer;
           }
           ok = task_attn<HD>(c, tt);
           if (queue) units += (uint32_t)tt.a3;  // a pulled split adds its pages

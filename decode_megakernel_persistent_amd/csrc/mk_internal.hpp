@@ -22,8 +22,8 @@ enum Op : uint8_t {
   OP_QKV = 1,     // a0 = kv group g, a1 = first rotary pair, a2 = pairs
   OP_ATTN = 2,    // a0 = b, a1 = g, a2 = first page, a3 = pages; aux = split index;
                   // with TF_QUEUE: splits pulled from a shared queue: a0 = queue
-                  // counter, a1 = splits per kv head, a2 = pages per split, a3 =
-                  // queue tasks of the layer
+                  // counter, a1 = first record of the splits in the plan's split
+                  // table, a2 = splits, a3 = queue tasks of the layer
   OP_COMB = 3,    // a0 = b, a1 = query head, a2 = first dim, a3 = dims; aux = splits of (b, g)
   OP_O = 4,       // a1 = first row, a2 = rows
   OP_ROUTER = 5,  // a1 = first expert row, a2 = rows
@@ -110,10 +110,13 @@ static_assert(sizeof(Task) == 32, "task record is 32 bytes");
 // Plan image: u32 header[PLAN_HDR_WORDS], u32 cu_off[n_cu + 1] (task index
 // ranges per list), padding to 32 B, Task tasks[n_tasks] (lists back to back).
 // After the tasks: int32 seq_bound[B], each sequence's context bound.
-constexpr uint32_t PLAN_MAGIC = 0x34504B4Du;  // "MKP4"
+// Then (queue plans) Task splits[H_NSPLITS]: the attention splits that queue
+// tasks pull (op OP_ATTN, a0 = b, a1 = g, a2 = first page, a3 = pages, aux
+// = split index; the layer is the queue task's), longest first.
+constexpr uint32_t PLAN_MAGIC = 0x35504B4Du;  // "MKP5"
 constexpr int PLAN_HDR_WORDS = 16;
 enum PlanHdr { H_MAGIC = 0, H_NCU = 1, H_NTASKS = 2, H_NCTR = 3, H_TASK_OFF_BYTES = 4,
-               H_STAGES = 5, H_BOUND_OFF_BYTES = 6, H_BATCH = 7 };
+               H_STAGES = 5, H_BOUND_OFF_BYTES = 6, H_BATCH = 7, H_SPLIT_OFF_BYTES = 8, H_NSPLITS = 9 };
 
 // Batch projections: MFMA 16x16x32 bf16 tiles of 16 weight rows x 16 or 32
 // sequences. The sequences' inputs stream through LDS in panels of MT_KP

@@ -176,9 +176,28 @@ mk_status batch_stages(mk_plan_t* p, const std::vector<int>& pages_b,
             st.push_back(t);
           }
         }
-      // longest splits first: dealt round-robin, the units' page counts even out
+      // longest splits first: dealt round-robin (the units' page counts even
+      // out), or pulled from the queue in this order by one queue task per unit
       std::stable_sort(st.begin(), st.end(), [](const Task& x, const Task& y) { return x.a3 > y.a3; });
-      stages.push_back(st);
+      if (p->attn_queue) {
+        if (l == 0) {
+          p->split_table = st;
+          for (auto& t : p->split_table) t.layer = 0, t.wait_b = t.signal = mk::NO_CTR, t.units = 0;
+        }
+        std::vector<Task> qs;
+        for (int i = 0; i < n_cu; ++i) {
+          Task t = mk_task(mk::OP_ATTN, l);
+          t.flags = mk::TF_QUEUE;
+          t.wait_b = ctr16(p->c_qkv[l * Hkv]);
+          t.signal = ctr16(p->c_attn[l * Hkv]);
+          t.a0 = p->c_queue[l]; t.a1 = 0; t.a2 = (int32_t)p->split_table.size(); t.a3 = n_cu;
+          t.units = 0;  // each split pulled adds its pages
+          qs.push_back(t);
+        }
+        stages.push_back(qs);
+      } else {
+        stages.push_back(st);
+      }
     }
     {  // COMB: whole heads (nh of one kv group per task) while there are more
        // (sequence, head) pairs than units, else as many dim ranges as fit
@@ -500,10 +519,11 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   }
   const int flags = o ? o->flags : 0;
   int pps = o && o->attn_split_pages > 0 ? o->attn_split_pages : (pg_total + n_cu - 1) / n_cu;
-  const bool queue = !(flags & MK_PLAN_NO_ATTN_QUEUE) && B == 1 && (flags & MK_PLAN_ATTN_QUEUE);
+  const bool queue = !(flags & MK_PLAN_NO_ATTN_QUEUE) && !prefill && (flags & MK_PLAN_ATTN_QUEUE);
   p->router_fold = !batch && moe && !(flags & MK_PLAN_NO_ROUTER_FOLD);
-  if (queue) pps = mk::QUEUE_PAGES;
+  if (queue && !batch) pps = mk::QUEUE_PAGES;
   // a batch: about four splits per unit, so that ragged lengths even out
+  // (dealt statically, or pulled from the queue longest first)
   if (batch && !(o && o->attn_split_pages > 0)) pps = std::max(8, ceil_div(pg_total, 4 * n_cu));
   p->attn_queue = queue;
   // batch 1, static splits: when splits of two pages per wave fit on at most
@@ -522,7 +542,13 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     const std::string ls = std::to_string(l);
     if (batch) {
       for (int g = 0; g < Hkv; ++g) p->c_qkv.push_back(new_ctr("qkv[" + ls + "][" + std::to_string(g) + "]"));
-      for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + ls + "][" + std::to_string(g) + "]"));
+      if (queue) {  // a queue task takes splits of any kv head: one attention counter per layer
+        const int ca = new_ctr("attn[" + ls + "]");
+        for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(ca);
+        p->c_queue.push_back(new_ctr("queue[" + ls + "]"));
+      } else {
+        for (int g = 0; g < Hkv; ++g) p->c_attn.push_back(new_ctr("attn[" + ls + "][" + std::to_string(g) + "]"));
+      }
       p->c_comb.push_back(new_ctr("comb[" + ls + "]"));
       p->c_o.push_back(new_ctr("o[" + ls + "]"));
       p->c_router.push_back(moe ? new_ctr("router[" + ls + "]") : -1);
@@ -618,14 +644,25 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       stages.push_back(st);
     }
     // ATTN: split-KV tasks per (b, g), or one queue task per compute unit
+    // pulling the splits of QUEUE_PAGES pages of every kv head (kv head major)
     if (queue) {
+      if (l == 0) {
+        p->split_table.clear();
+        for (int g = 0; g < Hkv; ++g)
+          for (int si = 0; si < p->n_split[0]; ++si) {
+            Task t = mk_task(mk::OP_ATTN, 0);
+            t.a0 = 0; t.a1 = g; t.a2 = si * mk::QUEUE_PAGES;
+            t.a3 = std::min(mk::QUEUE_PAGES, pg_bound - t.a2); t.aux = (uint16_t)si;
+            p->split_table.push_back(t);
+          }
+      }
       std::vector<Task> st;
       for (int i = 0; i < n_cu; ++i) {
         Task t = mk_task(mk::OP_ATTN, l);
         t.flags = mk::TF_QUEUE;
         t.wait_b = ctr16(p->c_qkv[l * Hkv]);
         t.signal = ctr16(p->c_attn[l * Hkv]);
-        t.a0 = p->c_queue[l]; t.a1 = p->n_split[0]; t.a2 = mk::QUEUE_PAGES; t.a3 = n_cu;
+        t.a0 = p->c_queue[l]; t.a1 = 0; t.a2 = (int32_t)p->split_table.size(); t.a3 = n_cu;
         t.units = 0;  // each split pulled adds its pages
         st.push_back(t);
       }
@@ -789,9 +826,11 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   for (auto& st : stages)
     for (auto& t : st)
       if (t.signal != mk::NO_CTR) p->targets[t.signal] += t.units;
+  uint32_t table_pages = 0;
+  for (const Task& t : p->split_table) table_pages += (uint32_t)t.a3;
   if (queue)
-    for (int l = 0; l < L; ++l) p->targets[p->c_attn[l * Hkv]] = (uint32_t)(Hkv * pg_bound);
-  for (int32_t q : p->c_queue) p->targets[q] = (uint32_t)(Hkv * p->n_split[0] + n_cu);
+    for (int l = 0; l < L; ++l) p->targets[p->c_attn[l * Hkv]] = table_pages;
+  for (int32_t q : p->c_queue) p->targets[q] = (uint32_t)(p->split_table.size() + n_cu);
   for (auto v : p->targets)
     if (v == 0) {
       delete p;
@@ -902,9 +941,12 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
   {
     size_t hdr = (mk::PLAN_HDR_WORDS + n_cu + 1) * 4;
     size_t task_off = (hdr + 31) & ~size_t(31);
-    const size_t bound_off = task_off + p->n_tasks * sizeof(Task);
+    const size_t split_off = task_off + p->n_tasks * sizeof(Task);
+    const size_t bound_off = split_off + p->split_table.size() * sizeof(Task);
     p->image.assign(bound_off + (size_t)B * 4, 0);
     std::memcpy(p->image.data() + bound_off, p->seq_bound.data(), (size_t)B * 4);
+    if (!p->split_table.empty())
+      std::memcpy(p->image.data() + split_off, p->split_table.data(), p->split_table.size() * sizeof(Task));
     uint32_t* w = reinterpret_cast<uint32_t*>(p->image.data());
     w[mk::H_MAGIC] = mk::PLAN_MAGIC;
     w[mk::H_NCU] = (uint32_t)n_cu;
@@ -913,6 +955,8 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
     w[mk::H_TASK_OFF_BYTES] = (uint32_t)task_off;
     w[mk::H_STAGES] = (uint32_t)p->n_stages;
     w[mk::H_BOUND_OFF_BYTES] = (uint32_t)bound_off;
+    w[mk::H_SPLIT_OFF_BYTES] = (uint32_t)split_off;
+    w[mk::H_NSPLITS] = (uint32_t)p->split_table.size();
     w[mk::H_BATCH] = (uint32_t)B;
     uint32_t* off = w + mk::PLAN_HDR_WORDS;
     Task* tasks = reinterpret_cast<Task*>(p->image.data() + task_off);
@@ -1119,12 +1163,11 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
         for (int f = 0; f < p->F; ++f) got[slot(K_GATEUP, l)].push_back((int64_t)e * 1000000 + f);
         for (int r = 0; r < m.hidden; ++r) got[slot(K_DOWN, l)].push_back((int64_t)e * 1000000 + r);
       }
-  if (p->attn_queue) {  // every split of the queue, once per layer
-    const int pg_bound = (p->bound + 15) / 16;
+  if (p->attn_queue)  // every split of the queue's table, once per layer
     for (int l = 0; l < L; ++l)
-      for (int g = 0; g < m.n_kv_heads; ++g)
-        for (int pg = 0; pg < pg_bound; ++pg) got[slot(K_ATTN, l)].push_back((int64_t)g * 1000000 + pg);
-  }
+      for (const Task& t : p->split_table)
+        for (int pg = t.a2; pg < t.a2 + t.a3; ++pg)
+          got[slot(K_ATTN, l)].push_back(((int64_t)t.a0 * m.n_kv_heads + t.a1) * 1000000 + pg);
   // every expected output exactly once, nothing else
   for (size_t i = 0; i < want.size(); ++i) {
     auto& a = want[i];
@@ -1143,8 +1186,10 @@ extern "C" mk_status mk_plan_validate(const mk_plan_t* p) {
   // attention splits of a queue add their pages on the device: every page
   // below the bound, per kv head)
   std::set<int32_t> queues(p->c_queue.begin(), p->c_queue.end());
+  uint32_t table_pages = 0;
+  for (const Task& t : p->split_table) table_pages += (uint32_t)t.a3;
   if (p->attn_queue)
-    for (int l = 0; l < L; ++l) producers[p->c_attn[l * m.n_kv_heads]] += m.n_kv_heads * ((p->bound + 15) / 16);
+    for (int l = 0; l < L; ++l) producers[p->c_attn[l * m.n_kv_heads]] += table_pages;
   for (size_t c = 0; c < p->targets.size(); ++c)
     if (!queues.count((int32_t)c) && producers[c] != p->targets[c])
       return fail(MK_EINVAL, "validate: counter " + p->ctr_name[c] + " target != the outputs of its tasks");
@@ -1297,7 +1342,7 @@ extern "C" mk_status mk_plan_simulate(const mk_plan_t* p, uint64_t seed, int32_t
     // the queue tasks' pulls, and the pages of the splits they took
     for (int32_t q : p->c_queue) ctr[q] += p->targets[q];
     if (p->attn_queue)
-      for (int l = 0; l < L; ++l) ctr[p->c_attn[l * Hkv]] += (uint64_t)Hkv * ((p->bound + 15) / 16);
+      for (int l = 0; l < L; ++l) ctr[p->c_attn[l * Hkv]] += p->targets[p->c_attn[l * Hkv]];
     for (size_t c = 0; c < ctr.size(); ++c)
       if (ctr[c] != epoch * p->targets[c])
         return fail(MK_ESTATE, "simulate: counter " + p->ctr_name[c] + " ends epoch off target");

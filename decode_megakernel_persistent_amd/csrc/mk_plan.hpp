@@ -40,6 +40,7 @@ struct mk_plan {
   int32_t comb_dim_tasks = 1;       // combine tasks per (b, query head)
   int32_t kernel_class = -1;        // compiled kernel variant for this shape
   std::vector<int32_t> n_split;     // per b
+  std::vector<mk::Task> split_table;  // queue plans: the splits queue tasks pull (every layer)
   int32_t n_lm = 0, n_stages = 0;
 
   // workspace layout: base offset (bytes) and per-layer stride (bytes) per MK_BUF_*

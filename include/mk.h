@@ -100,8 +100,11 @@ typedef struct mk_plan_opts {
 /* Attention splits from a shared queue that every compute unit pulls from
  * (megakernel page, caption of Image 2: attention work whose amount depends
  * on live sequence lengths sits in queues any processor can take from),
- * instead of one static split per task. Off unless asked for. */
-#define MK_PLAN_ATTN_QUEUE 1     /* use the queue (batch 1) */
+ * instead of one static split per task: one queue task per unit and layer
+ * pulls splits, longest first, from a table in the plan image (batch 1:
+ * splits of 64 pages; a batch: the splits the static plan would deal).
+ * Decode plans only (not MK_PLAN_PREFILL). Off unless asked for. */
+#define MK_PLAN_ATTN_QUEUE 1     /* use the queue */
 #define MK_PLAN_NO_ATTN_QUEUE 2  /* never use it */
 /* Chunked prefill: the batch rows are 2 .. 32 consecutive prompt tokens of
  * ONE sequence (every page-table row the same, seq_lens[i] = seq_lens[0] + i,

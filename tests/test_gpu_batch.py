@@ -39,3 +39,11 @@ def test_small_moe_batch5_fixed_expert_parts():
     # experts the routing chose
     import decode_megakernel_persistent_amd as mk
     run_step_parity("small_moe_b5", plan_flags=mk.MK_PLAN_NO_EXPERT_SHARE)
+
+
+def test_batch_attention_split_queue():
+    # the batch's attention splits pulled from one shared queue (longest
+    # first, from the plan's split table) instead of dealt to fixed units
+    import decode_megakernel_persistent_amd as mk
+    run_step_parity("small_moe_b5", plan_flags=mk.MK_PLAN_ATTN_QUEUE)
+    run_step_parity("small_moe_b32", plan_flags=mk.MK_PLAN_ATTN_QUEUE)

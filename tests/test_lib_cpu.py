@@ -118,12 +118,18 @@ def test_pool_lease_is_all_or_nothing():
 
 def decode_plan(img):
     hdr = np.frombuffer(img, dtype="<u4", count=16)
-    assert hdr[0] == 0x34504B4D
+    assert hdr[0] == 0x35504B4D
     n_cu, n_tasks, n_ctr, off = int(hdr[1]), int(hdr[2]), int(hdr[3]), int(hdr[4])
     cu_off = np.frombuffer(img, dtype="<u4", count=n_cu + 1, offset=64)
     tasks = np.frombuffer(img, dtype=TASK, count=n_tasks, offset=off)
     assert cu_off[0] == 0 and cu_off[-1] == n_tasks and np.all(np.diff(cu_off.astype(np.int64)) >= 0)
     return n_cu, n_ctr, cu_off, tasks
+
+
+def decode_splits(img):
+    """The plan's split table (queue plans): the attention splits queue tasks pull."""
+    hdr = np.frombuffer(img, dtype="<u4", count=16)
+    return np.frombuffer(img, dtype=TASK, count=int(hdr[9]), offset=int(hdr[8]))
 
 
 def qkv_rows(p, g, m):
@@ -145,7 +151,7 @@ def qkv_rows(p, g, m):
     return row, row + h2
 
 
-def plan_coverage(tasks, m, bound):
+def plan_coverage(tasks, m, bound, splits=None):
     S = {}
     queued = set()
     pg_bound = -(-bound // m["page_tokens"])
@@ -199,12 +205,12 @@ def plan_coverage(tasks, m, bound):
         elif op == OP_BLM:
             add(("lm",), list(range(a1, a1 + a2)))
         elif op == OP_ATTN and int(t["flags"]) & TF_QUEUE:
-            # a shared queue of the layer's splits: (kv head, split) -> pages of
-            # split * a2 .. + a2 (a1 splits per head), counted once per layer
+            # a shared queue of the layer's splits: records a1 .. a1 + a2 of the
+            # plan's split table (b, kv head, first page, pages), once per layer
             if l not in queued:
                 queued.add(l)
-                add(("attn", l), [(0, g, p) for g in range(m["n_kv_heads"])
-                                  for p in range(a1 * a2) if p < pg_bound])
+                add(("attn", l), [(int(s["a0"]), int(s["a1"]), p) for s in splits[a1:a1 + a2]
+                                  for p in range(int(s["a2"]), int(s["a2"]) + int(s["a3"]))])
         elif op == OP_ATTN:
             add(("attn", l), [(a0, a1, p) for p in range(a2, a2 + a3)])
         elif op == OP_COMB:  # dims a2 .. a2 + a3 of heads a1, a1 + 1, .. as one run
@@ -253,14 +259,16 @@ def build_plan(name, n_cu=256, flags=0, **over):
                                              ("tiny_dense_b3", 256, 0), ("tiny_dense_b3", 16, 0),
                                              ("small_moe_b5", 256, 0), ("small_moe_b5", 40, 0),
                                              ("small_moe_b32", 256, 0),
-                                             ("moe48_b32_ragged", 256, 0)])
+                                             ("small_moe_b5", 40, mk.MK_PLAN_ATTN_QUEUE),
+                                             ("moe48_b32_ragged", 256, 0),
+                                             ("moe48_b32_ragged", 256, mk.MK_PLAN_ATTN_QUEUE)])
 def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
     w, pool, p, bound = build_plan(name, n_cu, flags)
     try:
         img = mk.mk_plan_export(p)
         n_cu2, n_ctr, cu_off, tasks = decode_plan(img)
         assert n_cu2 == n_cu and mk.mk_plan_n_tasks(p) == len(tasks)
-        got = plan_coverage(tasks, w["model"], bound)
+        got = plan_coverage(tasks, w["model"], bound, decode_splits(img))
         want = O.work_sets(w["model"], ctx_bounds(w) if w["batch"] > 1 else [bound])
         assert set(got) == set(want)
         for k, items in got.items():
@@ -276,11 +284,12 @@ def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
         assert not tasks["units"][~has].any() and not tasks["rsv"].any()
         names = mk.mk_plan_counter_names(p)
         qt = tasks[(tasks["op"] == OP_ATTN) & ((tasks["flags"] & TF_QUEUE) != 0)]
+        splits = decode_splits(img)
         for q in set(qt["a0"].tolist()):
             t0 = qt[qt["a0"] == q][0]
-            want_tg[q] = w["model"]["n_kv_heads"] * int(t0["a1"]) + int(t0["a3"])
-            want_tg[names.index("attn[%d]" % int(t0["layer"]))] += (
-                w["model"]["n_kv_heads"] * -(-bound // w["model"]["page_tokens"]))
+            want_tg[q] = int(t0["a2"]) + int(t0["a3"])
+            want_tg[names.index("attn[%d]" % int(t0["layer"]))] += int(
+                splits["a3"][int(t0["a1"]):int(t0["a1"]) + int(t0["a2"])].sum())
         assert np.array_equal(want_tg, tg)
         # ... and the oracle's completion count of each counter's class
         exp = O.expected_counters(w["model"], ctx_bounds(w) if w["batch"] > 1 else [bound], want)
