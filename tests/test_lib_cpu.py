@@ -613,3 +613,34 @@ def test_batch1_attention_and_o_projection_on_disjoint_units(name):
     finally:
         mk.mk_plan_free(p)
         mk.mk_pool_free(pool)
+
+
+def test_trace_layer_timeline_on_a_synthetic_trace():
+    """trace.layer_timeline on a hand-built trace of 4 layers of a batch-1
+    step: stage ends relative to the previous layer's median expert end, and
+    per-layer durations, match the times written in."""
+    from decode_megakernel_persistent_amd import trace as T
+    rows = []
+    t = 1000  # ticks of 10 ns
+
+    def task(op, layer, cu, start_us, end_us):
+        r = np.zeros(16, dtype=np.uint64)
+        r[0] = int(t + start_us * 100)
+        r[5] = r[6] = int(t + end_us * 100)
+        r[7] = (cu << 32) | (op << 16) | layer
+        rows.append(r)
+
+    for l in range(4):
+        base = 40.0 * l
+        for cu in range(2):
+            task(1, l, cu, base, base + 6 + cu)            # qkv
+            task(2, l, cu, base + 7, base + 14 + cu)       # attn
+            task(6, l, cu, base + 20, base + 40 + 2 * cu)  # expert
+    d = T.decode(np.stack(rows).view(np.int64))
+    stage, (pmed, pmin, pmax) = T.layer_timeline(d, layers=[1, 2])
+    # expert median end of layer l is 40 l + 41 (us after the first start)
+    assert abs(pmed - 40.0) < 1e-6 and abs(pmin - 40.0) < 1e-6 and abs(pmax - 40.0) < 1e-6
+    med, last, n = stage["qkv"]
+    assert n == 2 and abs(med - (6.5 - 41 + 40)) < 1e-6 and abs(last - (7 - 41 + 40)) < 1e-6
+    med, last, n = stage["expert"]
+    assert abs(med - 40.0) < 1e-6 and abs(last - 41.0) < 1e-6
