@@ -8,6 +8,8 @@ every compute unit):
   after the attention and FFN residuals, the new K and V in the pool, then
   the logits over all 151936 rows and the greedy token -- and the completion
   counters against the oracle's count of each class's outputs;
+- the same whole step planned over 240 units (attention units and O/router
+  units in other proportions);
 - batch 1 at 8192: 32 consecutive greedy steps, the oracle teacher-forced on
   the GPU's input tokens, agreeing on at least 99 % of the next tokens;
 - batch 32 with ragged contexts of 512 to 32768 tokens: the same whole-step
@@ -44,20 +46,20 @@ class OneSequence:
         return self.kv.v(l, self.b, g, c)
 
 
-def run_full_step(name, sample):
+def run_full_step(name, sample, n_cu=0):
     w = spec(name, 0)
     m, B = w["model"], w["batch"]
     L, K, V = m["n_layers"], m["top_k"], m["vocab"]
     flush(f"[full step] {name}: batch {B}, contexts {min(w['ctx'])}..{max(w['ctx'])}: "
           f"setting up weights and KV on the device")
-    dec, pool, Wd = gpu_session(w, 0)
+    dec, pool, Wd = gpu_session(w, 0, n_cu=n_cu)
     dev = dec.device
     tok_in = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
     tok_out = torch.full((B,), -1, dtype=torch.int32, device=dev)
     ids = torch.full((L, B, K), -1, dtype=torch.int32, device=dev)
     tw = torch.zeros((L, B, K), dtype=torch.float32, device=dev)
     logits = torch.zeros((B, V), dtype=torch.float32, device=dev)
-    flush("  one step")
+    flush(f"  one step on {n_cu or 'every'} units")
     dec.step(tok_in, tok_out, ids, tw, logits)
     torch.cuda.synchronize()
     dec.check_status()
@@ -82,6 +84,12 @@ def run_full_step(name, sample):
 
 def test_moe48_8k_whole_step():
     run_full_step("moe48_b1_8k", lambda ctx: [0])
+
+
+def test_moe48_8k_whole_step_on_240_units():
+    # a plan over 240 units: attention on 132 of them, O and router tasks on
+    # the other 108, some of which run two
+    run_full_step("moe48_b1_8k", lambda ctx: [0], n_cu=240)
 
 
 def test_moe48_8k_greedy_32():

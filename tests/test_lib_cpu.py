@@ -252,7 +252,8 @@ def build_plan(name, n_cu=256, flags=0, **over):
 
 @pytest.mark.parametrize("name,n_cu,flags", [("tiny_dense", 256, 0), ("tiny_dense", 7, 0),
                                              ("small_moe", 256, 0), ("small_moe", 64, 0),
-                                             ("moe48_b1_8k", 256, 0), ("moe48_b1_256k", 256, 0),
+                                             ("moe48_b1_8k", 256, 0), ("moe48_b1_8k", 240, 0),
+                                             ("moe48_b1_256k", 256, 0),
                                              ("moe48_b1_256k", 256, mk.MK_PLAN_ATTN_QUEUE),
                                              ("tiny_dense", 16, mk.MK_PLAN_ATTN_QUEUE),
                                              ("small_moe", 256, mk.MK_PLAN_ATTN_QUEUE),
