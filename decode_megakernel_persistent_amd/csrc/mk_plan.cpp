@@ -97,6 +97,9 @@ static_assert(8 * QKV_BLOCKS == mk::BQKV_PAIRS && mk::QPART_STRIDE == 2 * 8 * QK
               "batch QKV row blocks as the kernel reads their partial sums");
 // words the reducing O task gathers into LDS (partials and residual)
 constexpr int O_RED_WORDS = 16384;
+// Batch 1 with attention on units of its own: an attention unit's QKV task
+// takes this share of the rotary pairs of another unit's.
+constexpr double QKV_ATTN_UNIT_SHARE = 0.5;
 
 // Stages of a batch plan (B > 1), per layer:
 //   BQKV  (16-row blocks of one kv group's rotary pairs, all sequences: MFMA
@@ -632,15 +635,48 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
       int per_g = std::max(1, n_cu / Hkv);
       const int cap_pairs = std::max(1, rows_max(H) / 2);
       per_g = std::max(per_g, ceil_div(p->n_pairs_g, cap_pairs));
-      for (int g = 0; g < Hkv; ++g)
-        for (auto [s0, c] : split_even(p->n_pairs_g, per_g)) {
-          Task t = mk_task(mk::OP_QKV, l);
-          t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_expert[l - 1]);
-          t.signal = ctr16(p->c_qkv[l * Hkv + g]);
-          t.a0 = g; t.a1 = s0; t.a2 = c;
-          t.units = (uint16_t)(2 * c);
-          st.push_back(t);
+      auto qkv_task = [&](int g, int s0, int c) {
+        Task t = mk_task(mk::OP_QKV, l);
+        t.wait_b = l == 0 ? mk::NO_CTR : ctr16(p->c_expert[l - 1]);
+        t.signal = ctr16(p->c_qkv[l * Hkv + g]);
+        t.a0 = g; t.a1 = s0; t.a2 = c;
+        t.units = (uint16_t)(2 * c);
+        return t;
+      };
+      if (n_attn_units > 0 && per_g * Hkv == n_cu) {
+        // unit i runs task i (group i mod Hkv); an attention unit takes
+        // QKV_ATTN_UNIT_SHARE of the pairs of another unit, so that it starts
+        // its split (and requests the pages not staged) earlier
+        for (int i = 0; i < n_cu; ++i) st.push_back(Task{});
+        for (int g = 0; g < Hkv; ++g) {
+          std::vector<int> us;
+          double wsum = 0.0;
+          for (int i = g; i < n_cu; i += Hkv) {
+            us.push_back(i);
+            wsum += i < n_attn_units ? QKV_ATTN_UNIT_SHARE : 1.0;
+          }
+          std::vector<int> cnt(us.size());
+          std::vector<std::pair<double, int>> rem;
+          int given = 0;
+          for (size_t k = 0; k < us.size(); ++k) {
+            const double q = p->n_pairs_g * (us[k] < n_attn_units ? QKV_ATTN_UNIT_SHARE : 1.0) / wsum;
+            cnt[k] = std::min(cap_pairs, (int)q);
+            given += cnt[k];
+            rem.push_back({q - std::floor(q), (int)k});
+          }
+          std::stable_sort(rem.begin(), rem.end(), [](auto& x, auto& y) { return x.first > y.first; });
+          for (size_t k = 0; given < p->n_pairs_g; k = (k + 1) % rem.size())
+            if (cnt[rem[k].second] < cap_pairs) cnt[rem[k].second]++, given++;
+          int s0 = 0;
+          for (size_t k = 0; k < us.size(); ++k) {
+            st[us[k]] = qkv_task(g, s0, cnt[k]);
+            s0 += cnt[k];
+          }
         }
+      } else {
+        for (int g = 0; g < Hkv; ++g)
+          for (auto [s0, c] : split_even(p->n_pairs_g, per_g)) st.push_back(qkv_task(g, s0, c));
+      }
       stages.push_back(st);
     }
     // ATTN: split-KV tasks per (b, g), or one queue task per compute unit
@@ -860,11 +896,13 @@ extern "C" mk_status mk_plan(const mk_model_desc* m, const mk_batch_desc* bd,
         stage_lists[cu].push_back(s0);
         heap.push({pages + t.a3, r});
       }
-    } else if (n_attn_units > 0 && !st.empty() && st[0].op != mk::OP_QKV && st[0].op != mk::OP_EXPERT &&
-               st[0].op != mk::OP_LM && st[0].op != mk::OP_FINAL) {
-      // attention and combine on units 0 .. A-1, O and router on A .. n_cu-1
+    } else if (n_attn_units > 0 && !st.empty() && st[0].op != mk::OP_EXPERT && st[0].op != mk::OP_LM &&
+               st[0].op != mk::OP_FINAL && (st[0].op != mk::OP_QKV || (int)st.size() == n_cu)) {
+      // attention and combine on units 0 .. A-1, O and router on A .. n_cu-1,
+      // QKV task i on unit i
       const bool set_a = st[0].op == mk::OP_ATTN || st[0].op == mk::OP_COMB;
-      const int u0 = set_a ? 0 : n_attn_units, nu = set_a ? n_attn_units : n_cu - n_attn_units;
+      const bool all = st[0].op == mk::OP_QKV;
+      const int u0 = set_a || all ? 0 : n_attn_units, nu = all ? n_cu : set_a ? n_attn_units : n_cu - n_attn_units;
       for (size_t i = 0; i < st.size(); ++i) {
         int cu = u0 + (int)(i % (size_t)nu);
         p->lists[cu].push_back(st[i]);

@@ -606,6 +606,11 @@ def test_batch1_attention_and_o_projection_on_disjoint_units(name):
             for op in (OP_QKV, OP_EXPERT):
                 m = (tasks["layer"] == l) & (tasks["op"] == op)
                 assert np.bincount(cu_of[m], minlength=n_cu).tolist() == [1] * n_cu
+            # an attention unit's QKV task has about half the rotary pairs of an O unit's
+            q = (tasks["layer"] == l) & (tasks["op"] == OP_QKV)
+            pa = tasks["a2"][q & (cu_of < A)].mean()
+            pb = tasks["a2"][q & (cu_of >= A)].mean()
+            assert 0.4 < pa / pb < 0.6
             ex = (tasks["layer"] == l) & (tasks["op"] == OP_EXPERT)
             staged = cu_of[ex & ((tasks["flags"] & TF_STAGE_KV) != 0)]
             want = np.arange(A) if l < L - 1 else np.arange(0)
