@@ -56,8 +56,8 @@ def parse():
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every GPU box here has one GPU); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the decode step runs on a single device "
+              "and there is no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import decode_megakernel_persistent_amd as mk

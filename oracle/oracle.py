@@ -33,7 +33,7 @@ query head h to kv head h // (Hq/Hkv); the router takes a softmax over all
 experts, keeps the top k (ties to the lower index) and renormalises over
 them; argmax ties go to the lower index; the LM head is untied.
 
-Precision. The benchmark spec fixes fp32 math on bf16 weights: `dt` defaults
+Precision. The decode step is specified as fp32 math on bf16 weights: `dt` defaults
 to torch.float32; torch.float64 is a cross-check mode. Weights are the
 same bf16 bits as the GPU's, widened exactly. Decisions (top-k, argmax)
 are taken in the working precision.
