@@ -18,6 +18,7 @@ import re
 
 import numpy as np
 import pytest
+from hypothesis import HealthCheck, given, settings, strategies as st
 
 import decode_megakernel_persistent_amd as mk
 import oracle as O
@@ -266,48 +267,87 @@ def build_plan(name, n_cu=256, flags=0, **over):
 def test_plan_covers_the_oracle_work_exactly_once(name, n_cu, flags):
     w, pool, p, bound = build_plan(name, n_cu, flags)
     try:
-        img = mk.mk_plan_export(p)
-        n_cu2, n_ctr, cu_off, tasks = decode_plan(img)
-        assert n_cu2 == n_cu and mk.mk_plan_n_tasks(p) == len(tasks)
-        got = plan_coverage(tasks, w["model"], bound, decode_splits(img))
-        want = O.work_sets(w["model"], ctx_bounds(w) if w["batch"] > 1 else [bound])
-        assert set(got) == set(want)
-        for k, items in got.items():
-            assert len(items) == len(set(items)), f"{k}: covered more than once"
-            assert set(items) == want[k], f"{k}: coverage differs from the oracle's work"
-        # counter targets = outputs of the tasks signalling each counter (a
-        # queue counter: one pull per split plus each queue task's empty last
-        # pull; queued splits add their pages on the device)
-        tg = np.array(mk.mk_plan_counter_targets(p), dtype=np.int64)
-        has = tasks["signal"] != NO_CTR
-        want_tg = np.bincount(tasks["signal"][has].astype(np.int64),
-                              weights=tasks["units"][has].astype(np.float64), minlength=n_ctr).astype(np.int64)
-        assert not tasks["units"][~has].any() and not tasks["rsv"].any()
-        names = mk.mk_plan_counter_names(p)
-        qt = tasks[(tasks["op"] == OP_ATTN) & ((tasks["flags"] & TF_QUEUE) != 0)]
-        splits = decode_splits(img)
-        for q in set(qt["a0"].tolist()):
-            t0 = qt[qt["a0"] == q][0]
-            want_tg[q] = int(t0["a2"]) + int(t0["a3"])
-            want_tg[names.index("attn[%d]" % int(t0["layer"]))] += int(
-                splits["a3"][int(t0["a1"]):int(t0["a1"]) + int(t0["a2"])].sum())
-        assert np.array_equal(want_tg, tg)
-        # ... and the oracle's completion count of each counter's class
-        exp = O.expected_counters(w["model"], ctx_bounds(w) if w["batch"] > 1 else [bound], want)
-        check_counters_against_oracle(names, tg, exp)
-        # at most one expert task per compute unit and layer (their down parts wait on each other)
-        for cu in range(n_cu):
-            lt = tasks[int(cu_off[cu]):int(cu_off[cu + 1])]
-            ex = lt["layer"][(lt["op"] == OP_EXPERT) | (lt["op"] == OP_BEXP)]
-            assert len(ex) == len(set(ex.tolist()))
-        # with the queue asked for, attention splits come from a shared queue:
-        # one queue task per compute unit and layer
-        n_q = int(((tasks["op"] == OP_ATTN) & ((tasks["flags"] & TF_QUEUE) != 0)).sum())
-        assert n_q == (n_cu * w["model"]["n_layers"] if flags else 0)
-        mk.mk_plan_validate(p)
-        mk.mk_plan_simulate(p, 11, 3)
+        check_plan_against_oracle(w, p, bound, n_cu, flags)
     finally:
         mk.mk_plan_free(p)
+        mk.mk_pool_free(pool)
+
+
+def check_plan_against_oracle(w, p, bound, n_cu, flags):
+    """The exported plan covers the oracle's work enumeration exactly once, its
+    counter targets are the oracle's output counts, and it validates and
+    simulates."""
+    img = mk.mk_plan_export(p)
+    n_cu2, n_ctr, cu_off, tasks = decode_plan(img)
+    assert n_cu2 == n_cu and mk.mk_plan_n_tasks(p) == len(tasks)
+    got = plan_coverage(tasks, w["model"], bound, decode_splits(img))
+    want = O.work_sets(w["model"], ctx_bounds(w) if w["batch"] > 1 else [bound])
+    assert set(got) == set(want)
+    for k, items in got.items():
+        assert len(items) == len(set(items)), f"{k}: covered more than once"
+        assert set(items) == want[k], f"{k}: coverage differs from the oracle's work"
+    # counter targets = outputs of the tasks signalling each counter (a
+    # queue counter: one pull per split plus each queue task's empty last
+    # pull; queued splits add their pages on the device)
+    tg = np.array(mk.mk_plan_counter_targets(p), dtype=np.int64)
+    has = tasks["signal"] != NO_CTR
+    want_tg = np.bincount(tasks["signal"][has].astype(np.int64),
+                          weights=tasks["units"][has].astype(np.float64), minlength=n_ctr).astype(np.int64)
+    assert not tasks["units"][~has].any() and not tasks["rsv"].any()
+    names = mk.mk_plan_counter_names(p)
+    qt = tasks[(tasks["op"] == OP_ATTN) & ((tasks["flags"] & TF_QUEUE) != 0)]
+    splits = decode_splits(img)
+    for q in set(qt["a0"].tolist()):
+        t0 = qt[qt["a0"] == q][0]
+        want_tg[q] = int(t0["a2"]) + int(t0["a3"])
+        want_tg[names.index("attn[%d]" % int(t0["layer"]))] += int(
+            splits["a3"][int(t0["a1"]):int(t0["a1"]) + int(t0["a2"])].sum())
+    assert np.array_equal(want_tg, tg)
+    # ... and the oracle's completion count of each counter's class
+    exp = O.expected_counters(w["model"], ctx_bounds(w) if w["batch"] > 1 else [bound], want)
+    check_counters_against_oracle(names, tg, exp)
+    # at most one expert task per compute unit and layer (their down parts wait on each other)
+    for cu in range(n_cu):
+        lt = tasks[int(cu_off[cu]):int(cu_off[cu + 1])]
+        ex = lt["layer"][(lt["op"] == OP_EXPERT) | (lt["op"] == OP_BEXP)]
+        assert len(ex) == len(set(ex.tolist()))
+    # with the queue asked for, attention splits come from a shared queue:
+    # one queue task per compute unit and layer
+    n_q = int(((tasks["op"] == OP_ATTN) & ((tasks["flags"] & TF_QUEUE) != 0)).sum())
+    assert n_q == (n_cu * w["model"]["n_layers"] if flags else 0)
+    mk.mk_plan_validate(p)
+    mk.mk_plan_simulate(p, 11, 3)
+
+
+# Random shapes around the two small models: batch 1 to 32, ragged contexts
+# (some empty), few or many steps ahead, unit counts from 8 to 256, with and
+# without the attention queue. Every plan the library accepts must pass the
+# checks above; a shape it cannot serve must be refused with
+# MK_EUNSUPPORTED, never built wrong. Seeded draws: the same cases every run.
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(base=st.sampled_from(["tiny_dense", "small_moe"]), B=st.one_of(st.just(1), st.integers(2, 32)),
+       data=st.data(), steps=st.integers(1, 48), n_cu=st.integers(8, 256), queue=st.booleans())
+def test_random_plans_cover_the_oracle_work_exactly_once(base, B, data, steps, n_cu, queue):
+    hi = 600 if base == "tiny_dense" else 1500
+    ctx = data.draw(st.lists(st.integers(0, hi), min_size=B, max_size=B), label="ctx")
+    flags = mk.MK_PLAN_ATTN_QUEUE if queue else 0
+    w = spec(base, 0, batch=B, ctx=ctx, steps=steps, pool_pages="sum*1.1")
+    pool, rows, max_pages = lease_pages(w, 0)
+    try:
+        bound = max(w["ctx"]) + w["steps"]
+        cb = ctx_bounds(w) if B > 1 else None
+        try:
+            p = mk.mk_plan(mk.model_desc(w["model"]), w["ctx"], [v for r in rows for v in r], max_pages,
+                           bound, n_cu=n_cu, flags=flags, ctx_bounds=cb)
+        except mk.MkError as e:
+            assert e.status == mk.MK_EUNSUPPORTED, str(e)
+            return
+        try:
+            check_plan_against_oracle(w, p, bound, n_cu, flags)
+        finally:
+            mk.mk_plan_free(p)
+    finally:
         mk.mk_pool_free(pool)
 
 
