@@ -6,7 +6,9 @@ routed to them; each expert task takes an equal share of the rows of the
 experts the routing chose (one case keeps a fixed expert part per task). Each case compares every sequence of one step with the
 oracle exactly as the batch-1 cases do (greedy token, logits, hidden state
 after every residual, new K/V in the pool, top-k ids, counters), on ragged
-contexts that include an empty one and a single token.
+contexts that include an empty one and a single token. Six more cases draw
+their shape (model, batch, contexts, steps ahead, unit count, attention
+queue) from a seeded generator.
 """
 import pytest
 
@@ -47,3 +49,44 @@ def test_batch_attention_split_queue():
     import decode_megakernel_persistent_amd as mk
     run_step_parity("small_moe_b5", plan_flags=mk.MK_PLAN_ATTN_QUEUE)
     run_step_parity("small_moe_b32", plan_flags=mk.MK_PLAN_ATTN_QUEUE)
+
+
+def random_shapes(n, seed=7):
+    """n seeded step shapes around the two small models that the planner
+    accepts: batch 1 to 12, ragged contexts (some empty), 1 to 40 steps
+    ahead, 64 to 256 units, with and without the attention queue."""
+    import random
+    import decode_megakernel_persistent_amd as mk
+    from fixtures.session import lease_pages, spec
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        base = rng.choice(["tiny_dense", "small_moe"])
+        B = 1 if rng.random() < 0.3 else rng.randint(2, 12)
+        hi = 600 if base == "tiny_dense" else 1200
+        ctx = [rng.choice([0, 1, rng.randint(0, hi)]) if rng.random() < 0.2 else rng.randint(0, hi)
+               for _ in range(B)]
+        steps = rng.randint(1, 40)
+        n_cu = rng.randint(64, 256)
+        flags = mk.MK_PLAN_ATTN_QUEUE if rng.random() < 0.4 else 0
+        w = spec(base, 0, batch=B, ctx=ctx, steps=steps, pool_pages="sum*1.1")
+        pool, rows, max_pages = lease_pages(w, 0)
+        try:
+            cb = [c + steps for c in w["ctx"]] if B > 1 else None
+            p = mk.mk_plan(mk.model_desc(w["model"]), w["ctx"], [v for r in rows for v in r], max_pages,
+                           max(w["ctx"]) + steps, n_cu=n_cu, flags=flags, ctx_bounds=cb)
+            mk.mk_plan_free(p)
+        except mk.MkError:
+            continue  # a shape the library refuses (checked on the CPU)
+        finally:
+            mk.mk_pool_free(pool)
+        out.append((base, dict(batch=B, ctx=ctx, steps=steps, pool_pages="sum*1.1"), n_cu, flags))
+    return out
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_shape_step_parity(case):
+    # one step of a seeded random shape (see random_shapes) against the
+    # oracle, every sequence as in the named cases above
+    base, over, n_cu, flags = random_shapes(6)[case]
+    run_step_parity(base, plan_flags=flags, n_cu=n_cu, **over)
