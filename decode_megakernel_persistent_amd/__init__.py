@@ -50,7 +50,8 @@ class mk_plan_opts(ctypes.Structure):
 
 class mk_weights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("embed", "attn_norm", "w_qkv", "w_o", "ffn_norm", "router",
-                                   "gate", "up", "down", "final_norm", "lm_head", "router_fold")]
+                                   "gate", "up", "down", "final_norm", "lm_head", "router_fold",
+                                   "expert_tiles")]
 
 
 class mk_kv(ctypes.Structure):
@@ -83,6 +84,7 @@ _SIGS = {
     "mk_device_cu_count": (_i32, [_P(_i32)]),
     "mk_stream_copy": (_i32, [_vp, _vp, _sz, _vp]),
     "mk_router_fold": (_i32, [_vp, _vp, _vp, _vp]),
+    "mk_expert_tile": (_i32, [_vp, _vp, _vp, _vp]),
     "mk_rope_table": (_i32, [_f32, _i32, _i32, _vp, _vp]),
     "mk_kv_pool_elems": (_i64, [_P(mk_model_desc), _i64]),
     "mk_step_bytes": (_i32, [_P(mk_model_desc), _i32, _P(_i32), _P(_i32), _P(ctypes.c_double),
@@ -150,6 +152,11 @@ def mk_device_cu_count():
 def mk_router_fold(desc, weights, out_ptr, stream_ptr):
     """out = W_r diag(ffn_norm) W_o per layer (fp32 [L][E][Hq d], device)."""
     _check(_lib.mk_router_fold(ctypes.byref(desc), ctypes.byref(weights), out_ptr, stream_ptr))
+
+
+def mk_expert_tile(desc, weights, out_ptr, stream_ptr):
+    """Fill out_ptr (device) with the expert weights in MFMA tile order (mk.h)."""
+    _check(_lib.mk_expert_tile(ctypes.byref(desc), ctypes.byref(weights), out_ptr, stream_ptr))
 
 
 def mk_stream_copy(dst_ptr, src_ptr, nbytes, stream_ptr):

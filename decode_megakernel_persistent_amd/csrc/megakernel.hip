@@ -2251,19 +2251,22 @@ __device__ __forceinline__ bool task_topk(Ctx& c, const Task& t) {
   return true;
 }
 
-// Expert GEMM on MFMA: R weight rows (bf16, K elements each, rowptr(r))
-// against up to 16 input columns held in LDS in split form (column n at
-// in + n * ld floats, chunk c = elements 8c .. 8c+7 as 4 words of bf16 hi
-// pairs then 4 words of lo pairs): out(r, n) = sum_k W[r][k] x_n[k]. Waves
-// take pairs of 16-row blocks round-robin; per k-step of 32 each lane loads
-// 16 bytes of one weight row (row r16 of the block, k 32 st + 8 kq .. + 7, the
-// A operand) and reads that chunk of column r16 (hi and lo: two B operands),
+// Expert GEMM on MFMA: R weight rows (bf16, K elements each) against up to
+// 16 input columns held in LDS in split form (column n at in + n * ld
+// floats, chunk c = elements 8c .. 8c+7 as 4 words of bf16 hi pairs then 4
+// words of lo pairs): out(r, n) = sum_k W[r][k] x_n[k]. Waves take pairs of
+// 16-row blocks round-robin; per k-step of 32 each lane loads 16 bytes of
+// the A operand (row r16 of the block, k 32 st + 8 kq .. + 7): this lane's
+// 16 bytes of k-step 0 of row block rb are at base(rb), those of k-step st
+// stride uint4 further on (row-major weights: 16 rows x 64 bytes per wave
+// load; the tile order of mk_expert_tile: one contiguous kilobyte). Each
+// lane reads that chunk of column r16 (hi and lo: two B operands),
 // two MFMA 16x16x32 per block. Weights of the next KC k-steps are in flight
 // while a group is multiplied. epi(rb, acc) receives block rb's accumulators:
 // lane (n = r16, kq) holds rows 16 rb + 4 kq + j, j < 4, of column n (n >=
 // ncols repeats column ncols - 1 and is to be ignored). K % (32 KC) == 0.
-template <class RowPtr, class Epi>
-__device__ __forceinline__ void mfma_rows(int R, int K, const RowPtr& rowptr, const float* in, int ld,
+template <class RowBase, class Epi>
+__device__ __forceinline__ void mfma_rows(int R, int K, const RowBase& base, int stride, const float* in, int ld,
                                           int ncols, const Epi& epi) {
   constexpr int KC = 8;
   const int lane = tid() & 63, w = tid() >> 6, r16 = lane & 15, kq = lane >> 4;
@@ -2271,15 +2274,15 @@ __device__ __forceinline__ void mfma_rows(int R, int K, const RowPtr& rowptr, co
   const float* inn = in + (size_t)min(r16, ncols - 1) * ld + 8 * kq;
   for (int rbA = 2 * w; rbA < nrb; rbA += 2 * NWAVE) {
     const int rbB = min(rbA + 1, nrb - 1);
-    const uint16_t* wa = rowptr(min(rbA * 16 + r16, R - 1)) + 8 * kq;
-    const uint16_t* wb = rowptr(min(rbB * 16 + r16, R - 1)) + 8 * kq;
+    const uint4* wa = base(rbA);
+    const uint4* wb = base(rbB);
     v4f accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
     uint4 xa[KC], xb[KC], ya[KC], yb[KC];
     auto load = [&](uint4 (&pa)[KC], uint4 (&pb)[KC], int s0) {
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
-        pa[i] = ld_nt((const uint4*)(wa + 32 * (s0 + i)));
-        pb[i] = ld_nt((const uint4*)(wb + 32 * (s0 + i)));
+        pa[i] = ld_nt(wa + stride * (s0 + i));
+        pb[i] = ld_nt(wb + stride * (s0 + i));
       }
     };
     auto mul = [&](const uint4 (&pa)[KC], const uint4 (&pb)[KC], int s0) {
@@ -2385,9 +2388,17 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
           }, X.in, 1, [&](int i) { const int q = i / H; return q * ldh + (i - q * H); }))
         return false;
       for (int q = 0; q < ng; ++q) rmsnorm_pack(c, X.in + (size_t)q * ldh, H, gn);
-      mfma_rows(2 * nf, H, [&](int j) {
-          return ((j & 1) ? Wu : Wg) + (size_t)(f0 + (j >> 1)) * H;
-        }, X.in, ldh, ng, [&](int rb, const v4f& acc) {
+      // rows 2f (gate) and 2f + 1 (up) of FFN row f0 + f: from the tile copy
+      // when there is one (its 16-row blocks start at FFN rows 8i), else row-major
+      const bool tl = a.etile && (f0 & 7) == 0 && (nf & 7) == 0;
+      const uint4* gt = tl ? (const uint4*)(a.etile + ((size_t)l * EE + e) * 3 * F * H) +
+                                 (size_t)(f0 >> 3) * (H >> 5) * 64 + lane
+                           : nullptr;
+      mfma_rows(2 * nf, H, [&](int rb) -> const uint4* {
+          if (tl) return gt + (size_t)rb * (H >> 5) * 64;
+          const int j = min(rb * 16 + r16, 2 * nf - 1);
+          return (const uint4*)(((j & 1) ? Wu : Wg) + (size_t)(f0 + (j >> 1)) * H + 8 * kq);
+        }, tl ? 64 : 4, X.in, ldh, ng, [&](int rb, const v4f& acc) {
           // rows 16 rb + 4 kq + j: j = 0, 1 gate and up of one FFN row, j = 2, 3 of the next
           if (r16 < ng) {
             const int ent = X.list[g0 + r16];  // b * KK + slot
@@ -2415,7 +2426,15 @@ __device__ __forceinline__ bool task_bexp(Ctx& c, const Task& t) {
         if (!gather_split<4>(c, a.act + (size_t)l * a.s_act + (size_t)X.list[g0 + q] * F, F,
                              X.in + (size_t)q * ldf, 1))
           return false;
-      mfma_rows(nr, F, [&](int j) { return Wd + (size_t)(r0 + j) * F; }, X.in, ldf, ng,
+      // hidden rows r0 + j: the tile copy's down part (16-row blocks from row 0) or row-major
+      const bool tl = a.etile && (r0 & 15) == 0 && (nr & 15) == 0;
+      const uint4* dt = tl ? (const uint4*)(a.etile + ((size_t)l * EE + e) * 3 * F * H + 2 * (size_t)F * H) +
+                                 (size_t)(r0 >> 4) * (F >> 5) * 64 + lane
+                           : nullptr;
+      mfma_rows(nr, F, [&](int rb) -> const uint4* {
+          if (tl) return dt + (size_t)rb * (F >> 5) * 64;
+          return (const uint4*)(Wd + (size_t)(r0 + min(rb * 16 + r16, nr - 1)) * F + 8 * kq);
+        }, tl ? 64 : 4, X.in, ldf, ng,
                 [&](int rb, const v4f& acc) {
           if (r16 < ng) {
             const int ent = X.list[g0 + r16];
@@ -2796,6 +2815,41 @@ __global__ __launch_bounds__(256) void mk_router_scale_kernel(const uint16_t* __
 
 // Zero-fill of n 16-byte words (a kernel, not a memset node, so that a
 // caller may capture it in a graph).
+// Expert weights in MFMA tile order (mk_expert_tile). Per layer l and
+// expert e, 3 F H bf16: the gate/up rows (row 2f = gate row f, 2f + 1 = up
+// row f) as 2F/16 row blocks, then the down rows as H/16 row blocks; a row
+// block of K columns is K/32 tiles of 64 x 16 bytes, lane t holding the 8
+// values of row 16 rb + t % 16 at columns 32 s + 8 (t / 16) .. + 7: the
+// A operand of v_mfma_f32_16x16x32_bf16 for k-step s, one kilobyte per wave
+// load. One uint4 per thread, grid-stride.
+__global__ __launch_bounds__(256) void mk_expert_tile_kernel(const uint16_t* __restrict__ gate,
+                                                             const uint16_t* __restrict__ up,
+                                                             const uint16_t* __restrict__ down,
+                                                             uint4* __restrict__ out, int LE, int H, int F) {
+  const size_t per = (size_t)3 * F * H / 8;  // uint4 per (layer, expert)
+  const size_t gu = (size_t)2 * F * H / 8;
+  const size_t n = per * (size_t)LE;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t le = i / per, q = i - le * per;
+    const int lane = (int)(q & 63);
+    const size_t t = q >> 6;  // tile index within the part
+    const uint16_t* src;
+    if (q < gu) {
+      const int ks = H >> 5;
+      const size_t rb = t / ks, st = t - rb * ks;
+      const size_t j = rb * 16 + (lane & 15);  // interleaved gate/up row
+      src = ((j & 1) ? up : gate) + (le * F + (j >> 1)) * H + st * 32 + 8 * (lane >> 4);
+    } else {
+      const int ks = F >> 5;
+      const size_t t2 = t - gu / 64;
+      const size_t rb = t2 / ks, st = t2 - rb * ks;
+      const size_t r = rb * 16 + (lane & 15);
+      src = down + (le * H + r) * F + st * 32 + 8 * (lane >> 4);
+    }
+    out[i] = *(const uint4*)src;
+  }
+}
+
 __global__ __launch_bounds__(256) void mk_zero_kernel(uint4* __restrict__ p, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = make_uint4(0, 0, 0, 0);
@@ -2835,6 +2889,23 @@ extern "C" mk_status mk_device_cu_count(int32_t* n_cu) {
   e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   *n_cu = v;
+  return MK_OK;
+}
+
+extern "C" mk_status mk_expert_tile(const mk_model_desc* m, const mk_weights* w, void* out, void* stream) {
+  if (!m || !w || !out) return fail(MK_EINVAL, "mk_expert_tile: NULL argument");
+  if (!w->gate || !w->up || !w->down) return fail(MK_EINVAL, "mk_expert_tile: missing weight pointer");
+  const bool moe = m->n_experts > 0;
+  const int L = m->n_layers, H = m->hidden, E = moe ? m->n_experts : 1, F = moe ? m->expert_ffn : m->ffn_dim;
+  if (L <= 0 || H <= 0 || F <= 0 || E <= 0) return fail(MK_EINVAL, "mk_expert_tile: bad shape");
+  if (H % 32 || F % 32) return fail(MK_EUNSUPPORTED, "mk_expert_tile: hidden and FFN widths must be multiples of 32");
+  if (((uintptr_t)out | (uintptr_t)w->gate | (uintptr_t)w->up | (uintptr_t)w->down) & 15)
+    return fail(MK_EINVAL, "mk_expert_tile: pointers must be 16-byte aligned");
+  hipLaunchKernelGGL(mk::dev::mk_expert_tile_kernel, dim3(4096), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)w->gate, (const uint16_t*)w->up, (const uint16_t*)w->down, (uint4*)out,
+                     L * E, H, F);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "mk_expert_tile");
   return MK_OK;
 }
 
@@ -3030,6 +3101,9 @@ static mk_status launch_step(const mk_plan_t* p, const mk_weights* w, const mk_k
   a.gate = (const uint16_t*)w->gate; a.up = (const uint16_t*)w->up; a.down = (const uint16_t*)w->down;
   a.final_norm = (const uint16_t*)w->final_norm; a.lm = (const uint16_t*)w->lm_head;
   a.rfold = w->router_fold;
+  a.etile = (const uint16_t*)w->expert_tiles;
+  if (a.etile && ((uintptr_t)a.etile & 15))
+    return fail(MK_EINVAL, "mk_decode_step: expert tiles not 16-byte aligned");
   if (p->router_fold && !w->router_fold)
     return fail(MK_EINVAL, "mk_decode_step: this plan reads the folded router (mk_router_fold) and it is NULL");
   a.pool = (uint16_t*)kv->pool;

@@ -238,6 +238,7 @@ struct KArgs {
   const uint16_t *embed, *attn_norm, *wqkv, *wo, *ffn_norm, *router, *gate, *up, *down,
       *final_norm, *lm;
   const float* rfold;  // [L][E][Hq D] W_r diag(g) W_o (folded router), or NULL
+  const uint16_t* etile;  // batch expert weights in MFMA tile order (mk_expert_tile), or NULL
   // KV cache
   uint16_t* pool;
   int64_t page_stride, layer_stride;  // bf16 elements

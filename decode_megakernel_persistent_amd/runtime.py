@@ -15,7 +15,7 @@ from . import (
     MK_PLAN_ATTN_QUEUE, MK_PLAN_NO_ROUTER_FOLD, MK_PLAN_CHANGED_COUNTERS, MK_PLAN_CHANGED_IMAGE, MK_PLAN_CHANGED_WORKSPACE,
     MkError, MK_OK, mk_decode_step, mk_decode_step_static, mk_io, mk_kv, mk_kv_pool_elems, mk_plan,
     mk_plan_buffer, mk_plan_counter_bytes, mk_plan_device_bytes, mk_plan_free, mk_plan_n_tasks,
-    mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_stream_copy, mk_router_fold,
+    mk_plan_update, mk_plan_upload, mk_plan_workspace_bytes, mk_rope_table, mk_step_buffers, mk_stream_copy, mk_router_fold, mk_expert_tile,
     mk_sampling, mk_step_status, mk_weights, model_desc,
 )
 
@@ -65,7 +65,7 @@ class Decoder:
 
     def __init__(self, model, weights, pool, n_pages, seq_lens, page_table, max_pages, bound,
                  n_cu=0, attn_split_pages=0, device="cuda", trace=False, plan_flags=0,
-                 ctx_bounds=None):
+                 ctx_bounds=None, expert_tiles=True):
         self.m = dict(model)
         self.device = torch.device(device)
         self.B = len(seq_lens)
@@ -100,7 +100,20 @@ class Decoder:
             w0 = mk_weights(*[_ptr(weights.get(k)) for k, _ in mk_weights._fields_])
             mk_router_fold(self.desc, w0, fold.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
             weights["router_fold"] = fold
-        self._w = mk_weights(*[_ptr(weights.get(k)) for k, _ in mk_weights._fields_])
+        # batch plans' expert GEMMs read the expert weights in MFMA tile order
+        # (mk_expert_tile): made once per weight set and kept in the weights dict
+        self.expert_tiled = self.B > 1 and expert_tiles
+        if self.expert_tiled and weights.get("expert_tiles") is None:
+            m = self.m
+            moe = m["n_experts"] > 0
+            E = m["n_experts"] if moe else 1
+            F = m["expert_ffn"] if moe else m["ffn_dim"]
+            tiles = torch.empty(m["n_layers"] * E * 3 * F * m["hidden"], dtype=torch.bfloat16, device=dev)
+            w0 = mk_weights(*[_ptr(weights.get(k)) for k, _ in mk_weights._fields_])
+            mk_expert_tile(self.desc, w0, tiles.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+            weights["expert_tiles"] = tiles
+        self._w = mk_weights(*[_ptr(weights.get(k)) if (k != "expert_tiles" or self.expert_tiled) else None
+                               for k, _ in mk_weights._fields_])
         self._set_rope(bound)
         self.trace = None
         if trace:

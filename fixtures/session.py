@@ -39,7 +39,7 @@ def lease_pages(w, seed=0):
 
 
 def gpu_session(w, seed=0, device="cuda", weights=None, n_cu=0, attn_split_pages=0, trace=False,
-                plan_flags=0):
+                plan_flags=0, expert_tiles=True):
     """A Decoder for workload w with its KV filled; returns (decoder, pool handle, weights)."""
     import decode_megakernel_persistent_amd as mk
     from decode_megakernel_persistent_amd.runtime import Decoder, alloc_kv_pool
@@ -52,7 +52,8 @@ def gpu_session(w, seed=0, device="cuda", weights=None, n_cu=0, attn_split_pages
     ctx_bounds = [c + w["steps"] for c in w["ctx"]] if B > 1 else None
     dec = Decoder(m, W, kvpool, w["pool_pages"], w["ctx"], rows, max_pages, bound,
                   n_cu=n_cu, attn_split_pages=attn_split_pages, device=device, trace=trace,
-                  plan_flags=plan_flags, ctx_bounds=ctx_bounds)
+                  plan_flags=plan_flags, ctx_bounds=ctx_bounds,
+                  **({} if expert_tiles else {"expert_tiles": False}))
     for b in range(B):
         fxd.fill_kv(kvpool, dec.page_table[b], m, seed, b, w["ctx"][b])
     torch.cuda.synchronize(device)

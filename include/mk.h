@@ -152,6 +152,10 @@ typedef struct mk_weights {
                                [W_r diag(ffn_norm) | W_r diag(ffn_norm) W_o], made by
                                mk_router_fold from the weights above; read by batch-1 MoE plans
                                (unless MK_PLAN_NO_ROUTER_FOLD), NULL otherwise */
+  const void* expert_tiles; /* bf16 [L][E][3 F hidden] (dense FFN: E = 1, F = ffn): the gate, up
+                               and down rows in MFMA tile order, made by mk_expert_tile; read by
+                               batch plans' expert tasks when not NULL (else they read gate, up
+                               and down), 16-byte aligned */
 } mk_weights;
 
 /* KV cache and positions. */
@@ -253,6 +257,23 @@ mk_status mk_rope_table(float theta, int32_t head_dim, int32_t n_pos, float* cos
  * dense model or a missing pointer; MK_EUNSUPPORTED if hidden + Hq d is not a
  * multiple of 4 or exceeds 8192. */
 mk_status mk_router_fold(const mk_model_desc* m, const mk_weights* w, float* out, void* hip_stream);
+
+/* Expert weights in MFMA tile order, for the batch path's expert GEMMs (the
+ * article's point that a decode step is bound by streaming the weights from
+ * HBM, "Inside the megakernel serving engine for North Mini Code",
+ * introduction: the batch GEMMs read their A operand 16 rows x 32 columns at
+ * a time, and row-major rows give each wave load 16 runs of 64 bytes; the
+ * tile order gives it one contiguous kilobyte). Fills out (device, 16-byte
+ * aligned, L x E x 3 F x hidden bf16, E = 1 and F = ffn for a dense FFN)
+ * from w->gate, w->up and w->down, enqueued on hip_stream: per layer and
+ * expert the gate/up rows interleaved (row 2f = gate row f, 2f + 1 = up row
+ * f) in 2F/16 blocks of 16 rows, then the down rows in hidden/16 blocks;
+ * block rb's k-step s (columns 32 s .. 32 s + 31) is 64 x 16 bytes, entry t
+ * holding row 16 rb + t % 16, columns 32 s + 8 (t / 16) .. + 7. The caller
+ * owns out and passes it as mk_weights.expert_tiles. Errors: MK_EINVAL (NULL
+ * or misaligned pointers, bad shape), MK_EUNSUPPORTED (hidden or FFN width
+ * not a multiple of 32), MK_EDEVICE (launch failure). */
+mk_status mk_expert_tile(const mk_model_desc* m, const mk_weights* w, void* out, void* hip_stream);
 /* Elements (bf16) of a KV pool of n_pages pages. */
 int64_t mk_kv_pool_elems(const mk_model_desc* m, int64_t n_pages);
 /* Algorithmic bytes of one step: weights read once (selected experts only:

@@ -43,6 +43,44 @@ def test_small_moe_batch5_fixed_expert_parts():
     run_step_parity("small_moe_b5", plan_flags=mk.MK_PLAN_NO_EXPERT_SHARE)
 
 
+def test_small_moe_batch5_row_major_experts():
+    # the expert GEMMs on the row-major gate, up and down rows (no tile copy)
+    run_step_parity("small_moe_b5", expert_tiles=False)
+
+
+@pytest.mark.parametrize("name", ["small_moe", "tiny_dense"])
+def test_expert_tile_order(name):
+    # mk_expert_tile against the tile order written out with tensor reshapes:
+    # per layer and expert, gate/up rows interleaved then the down rows, in
+    # 16-row blocks of 32-column k-steps, entry t = row t % 16, columns
+    # 8 (t / 16) .. + 7; bit-exact
+    import torch
+    import decode_megakernel_persistent_amd as mk
+    from fixtures import device as fxd
+    from fixtures.session import spec
+    m = spec(name, 0)["model"]
+    W = fxd.weights(m, 0, "cuda")
+    moe = m["n_experts"] > 0
+    L, H = m["n_layers"], m["hidden"]
+    E = m["n_experts"] if moe else 1
+    F = m["expert_ffn"] if moe else m["ffn_dim"]
+    out = torch.empty(L * E * 3 * F * H, dtype=torch.bfloat16, device="cuda")
+    w0 = mk.mk_weights(*[None if W.get(k) is None else W[k].data_ptr() for k, _ in mk.mk_weights._fields_])
+    mk.mk_expert_tile(mk.model_desc(m), w0, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    g = W["gate"].view(L, E, F, H).cpu().view(torch.int16)
+    u = W["up"].view(L, E, F, H).cpu().view(torch.int16)
+    d = W["down"].view(L, E, H, F).cpu().view(torch.int16)
+    gu = torch.stack([g, u], dim=3).reshape(L, E, 2 * F, H)
+
+    def tiles(x, R, K):
+        # [L][E][R][K] -> [L][E][R/16][K/32][kq][r16][8]
+        t = x.reshape(L, E, R // 16, 16, K // 32, 4, 8).permute(0, 1, 2, 4, 5, 3, 6)
+        return t.reshape(L, E, R * K)
+    want = torch.cat([tiles(gu, 2 * F, H), tiles(d, H, F)], dim=2).reshape(-1)
+    assert torch.equal(out.cpu().view(torch.int16), want)
+
+
 def test_batch_attention_split_queue():
     # the batch's attention splits pulled from one shared queue (longest
     # first, from the plan's split table) instead of dealt to fixed units

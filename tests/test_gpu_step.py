@@ -36,7 +36,7 @@ def _pool_slot(dec, m, b, l, g, pos):
     return blk[ko], blk[vo]
 
 
-def run_step_parity(name, seed=0, plan_flags=0, n_cu=0, **over):
+def run_step_parity(name, seed=0, plan_flags=0, n_cu=0, expert_tiles=True, **over):
     w = spec(name, seed, **over)
     m, B = w["model"], w["batch"]
     L, V = m["n_layers"], m["vocab"]
@@ -44,7 +44,7 @@ def run_step_parity(name, seed=0, plan_flags=0, n_cu=0, **over):
     K = m["top_k"] if moe else 1
     flush(f"[step parity] {name} seed={seed} over={over} flags={plan_flags} n_cu={n_cu or 'all'} B={B} "
           f"ctx={w['ctx']}")
-    dec, pool, W = gpu_session(w, seed, plan_flags=plan_flags, n_cu=n_cu)
+    dec, pool, W = gpu_session(w, seed, plan_flags=plan_flags, n_cu=n_cu, expert_tiles=expert_tiles)
     dev = dec.device
     tok_in = torch.tensor(w["tokens"], dtype=torch.int32, device=dev)
     tok_out = torch.full((B,), -1, dtype=torch.int32, device=dev)
